@@ -1,0 +1,185 @@
+"""CPU oracle for low-bit KV decode attention -- TEST INFRASTRUCTURE ONLY.
+
+Only tests, the smoke check and the benchmark's CPU-baseline leg may import
+this package.  The GPU library never calls it, and it shares no code with the
+GPU library (the seeded input generator in ``synth`` is the only module both
+sides use, and it holds none of the attention arithmetic).
+
+What it computes (fp64 throughout):
+
+* ``dequantize``: value = s*q + z with one (s, z) per group -- FOSCAR explainer
+  ("FOSCAR speeds up 2-bit KV decode", learnaivisually), encoding paragraph;
+  groups token-wise or channel-wise -- same page, fold-placement table.
+* ``attend``: one query row against the dequantised keys and values with a
+  two-pass softmax.  This is the "dequantized attention output" that the
+  FOSCAR abstract (arXiv 2611.09722) says folding preserves in exact
+  arithmetic; the oracle computes it directly, with no folding and no online
+  softmax.
+* ``decode`` / ``decode_rows``: every (sequence, query head) of a decode step;
+  query head i reads KV head i // (Hq / Hkv) (GQA: "4 query heads per KV head",
+  explainer, issue-budget paragraph).
+* ``pack_k`` / ``pack_v`` / ``unpack_k`` / ``unpack_v``: the packed code layout
+  of the C interface, written from its specification (keys packed along
+  channels, values packed along tokens, element 0 in the lowest bits).
+
+Parity pins: every function here is pinned by ``tests/test_oracle_pins.py``
+(worked receipt, exact fold-vs-unfold, closed forms, invariants, a textbook
+special case, golden packed words).
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+TOKEN = "token"
+CHANNEL = "channel"
+
+
+def dequantize(codes, scale, zero, layout: str, group: int) -> np.ndarray:
+    """Dequantised cache slice [T, D] in fp64: x = s*q + z.
+
+    codes: [T, D] integer codes; scale, zero: fp16, [T, D/g] (token-wise:
+    group = g consecutive channels of one token) or [T/g, D] (channel-wise:
+    group = g consecutive tokens of one channel).  Every product is exact in
+    fp64 (an 11-bit significand times a 4-bit integer plus an fp16 value).
+    """
+    q = np.asarray(codes, dtype=np.float64)
+    s = np.asarray(scale, dtype=np.float64)
+    z = np.asarray(zero, dtype=np.float64)
+    T, D = q.shape
+    if layout == TOKEN:
+        s_full = np.repeat(s, group, axis=1)[:T, :D]
+        z_full = np.repeat(z, group, axis=1)[:T, :D]
+    elif layout == CHANNEL:
+        s_full = np.repeat(s, group, axis=0)[:T, :D]
+        z_full = np.repeat(z, group, axis=0)[:T, :D]
+    else:
+        raise ValueError(layout)
+    return s_full * q + z_full
+
+
+def attend(q_row, k_hat, v_hat, sm_scale: float):
+    """Softmax attention of one query row over T dequantised tokens.
+
+    Returns (o [D] fp64, lse fp64) with lse = ln sum_t exp(sm_scale * q.k_t).
+    Two passes: the max first, then the exponentials.  T = 0 gives o = 0 and
+    lse = -inf.
+    """
+    q = np.asarray(q_row, dtype=np.float64)
+    T = k_hat.shape[0]
+    if T == 0:
+        return np.zeros(v_hat.shape[1]), -math.inf
+    scores = sm_scale * (k_hat @ q)
+    m = scores.max()
+    w = np.exp(scores - m)
+    l = w.sum()
+    p = w / l
+    assert abs(p.sum() - 1.0) < 1e-9
+    o = p @ v_hat
+    return o, m + math.log(l)
+
+
+def _head(w: dict, b: int, h: int, t: int, k_layout: str, v_layout: str, group: int):
+    k_hat = dequantize(w["k_codes"][b, h, :t], _scale_rows(w["k_scale"][b, h], k_layout, group, t),
+                       _scale_rows(w["k_zero"][b, h], k_layout, group, t), k_layout, group)
+    v_hat = dequantize(w["v_codes"][b, h, :t], _scale_rows(w["v_scale"][b, h], v_layout, group, t),
+                       _scale_rows(w["v_zero"][b, h], v_layout, group, t), v_layout, group)
+    return k_hat, v_hat
+
+
+def _scale_rows(s, layout: str, group: int, t: int):
+    """The (s, z) rows that cover the first t tokens."""
+    if layout == TOKEN:
+        return s[:t]
+    return s[: -(-t // group)]
+
+
+def decode(w: dict, *, k_layout: str, v_layout: str, group: int, sm_scale: float,
+           num_kv_heads: int | None = None):
+    """Whole decode step.  ``w`` holds q [B,Hq,D], k_codes / v_codes
+    [B,Hkv,Tcap,D], k_scale / k_zero / v_scale / v_zero in the layouts of
+    ``dequantize`` (with leading [B,Hkv]) and seq_lens [B] (clamped to
+    [0, Tcap]).  Returns (out [B,Hq,D] fp64, lse [B,Hq] fp64)."""
+    q = np.asarray(w["q"], dtype=np.float64)
+    B, Hq, D = q.shape
+    rows = [(b, i) for b in range(B) for i in range(Hq)]
+    o, l = decode_rows(w, rows, k_layout=k_layout, v_layout=v_layout, group=group, sm_scale=sm_scale)
+    return o.reshape(B, Hq, D), l.reshape(B, Hq)
+
+
+def decode_rows(w: dict, rows, *, k_layout: str, v_layout: str, group: int, sm_scale: float):
+    """Like ``decode`` for a list of (b, query head) pairs only."""
+    q = np.asarray(w["q"], dtype=np.float64)
+    B, Hq, D = q.shape
+    Hkv = w["k_codes"].shape[1]
+    Tcap = w["k_codes"].shape[2]
+    G = Hq // Hkv
+    out = np.zeros((len(rows), D))
+    lse = np.zeros(len(rows))
+    cache = {}
+    for n, (b, i) in enumerate(rows):
+        h = i // G
+        t = int(min(max(int(w["seq_lens"][b]), 0), Tcap))
+        if (b, h) not in cache:
+            cache = {(b, h): _head(w, b, h, t, k_layout, v_layout, group)}
+        k_hat, v_hat = cache[(b, h)]
+        out[n], lse[n] = attend(q[b, i], k_hat, v_hat, sm_scale)
+    return out, lse
+
+
+# ---------------------------------------------------------------------------
+# Packed code layout of the C interface, written from its specification.
+#   keys:   word [t][c // E], channel c at bits [bits*(c % E), +bits)
+#   values: word [t // E][c], token t at bits [bits*(t % E), +bits)
+# with E = 32 / bits codes per 32-bit word, element 0 in the lowest bits.
+# ---------------------------------------------------------------------------
+
+def _per_word(bits: int) -> int:
+    if bits not in (2, 4):
+        raise ValueError("bits must be 2 or 4")
+    return 32 // bits
+
+
+def pack_k(codes, bits: int) -> np.ndarray:
+    """codes [..., T, D] -> uint32 [..., T, D*bits/32], packed along channels."""
+    E = _per_word(bits)
+    c = np.asarray(codes, dtype=np.uint32)
+    *lead, T, D = c.shape
+    c = c.reshape(*lead, T, D // E, E)
+    word = np.zeros((*lead, T, D // E), dtype=np.uint32)
+    for e in range(E):
+        word |= (c[..., e] & ((1 << bits) - 1)) << np.uint32(bits * e)
+    return word
+
+
+def unpack_k(words, bits: int, head_dim: int) -> np.ndarray:
+    E = _per_word(bits)
+    wv = np.asarray(words, dtype=np.uint32)
+    *lead, T, W = wv.shape
+    out = np.zeros((*lead, T, W, E), dtype=np.uint8)
+    for e in range(E):
+        out[..., e] = (wv >> np.uint32(bits * e)) & ((1 << bits) - 1)
+    return out.reshape(*lead, T, W * E)[..., :head_dim]
+
+
+def pack_v(codes, bits: int) -> np.ndarray:
+    """codes [..., T, D] -> uint32 [..., T/E, D], packed along tokens."""
+    E = _per_word(bits)
+    c = np.asarray(codes, dtype=np.uint32)
+    *lead, T, D = c.shape
+    c = c.reshape(*lead, T // E, E, D)
+    word = np.zeros((*lead, T // E, D), dtype=np.uint32)
+    for e in range(E):
+        word |= (c[..., e, :] & ((1 << bits) - 1)) << np.uint32(bits * e)
+    return word
+
+
+def unpack_v(words, bits: int) -> np.ndarray:
+    E = _per_word(bits)
+    wv = np.asarray(words, dtype=np.uint32)
+    *lead, W, D = wv.shape
+    out = np.zeros((*lead, W, E, D), dtype=np.uint8)
+    for e in range(E):
+        out[..., e, :] = (wv >> np.uint32(bits * e)) & ((1 << bits) - 1)
+    return out.reshape(*lead, W * E, D)

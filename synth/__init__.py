@@ -1,0 +1,280 @@
+"""Seeded synthetic decode-attention workloads (inputs only).
+
+This module draws the query, the full-precision keys and values, and turns
+the keys and values into a low-bit cache with one scale ``s`` and one
+offset ``z`` per group (value = s*q + z).  It holds none of the attention
+arithmetic: both the CPU oracle and the GPU path consume what it returns.
+
+Sources (the FOSCAR pages):
+  * explainer page "FOSCAR speeds up 2-bit KV decode -- Affine folding of
+    KV dequantization", paragraph on the encoding: a 2- or 4-bit code q,
+    a group of codes shares one scale and one offset, value = s*q + z;
+  * the same page, fold-placement table: groups run token-wise (along the
+    channels of one token) or channel-wise (along the tokens of one channel);
+  * the same page, results paragraph: 32 query heads, 8 KV heads, head
+    dimension 128, token-wise groups of 128.
+
+Readings where the pages are silent (each one is listed in the design notes):
+  * codes are unsigned, 0 .. 2**bits - 1;
+  * min-max quantiser: s = (max - min) / (2**bits - 1) computed in fp32 and
+    rounded to fp16, z = fp16(min), q = round-half-even((x - z16) / s16)
+    clamped to the code range; a constant group gets s = 0 and q = 0;
+  * a channel-wise group whose tokens run past the sequence length is
+    quantised over its valid tokens only;
+  * every random stream is ``numpy.random.default_rng([seed, workload id,
+    tensor id, b, h])`` so any (sequence, KV head) slice can be regenerated
+    on its own.
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+import os
+from concurrent.futures import ThreadPoolExecutor
+from typing import Optional
+
+import numpy as np
+
+TOKEN = "token"
+CHANNEL = "channel"
+
+# tensor ids for the random streams
+_T_K, _T_V, _T_Q, _T_OUTLIER, _T_STD, _T_LENS, _T_POISON = range(7)
+
+
+@dataclasses.dataclass(frozen=True)
+class Spec:
+    """Shape and value recipe of one synthetic workload."""
+
+    name: str
+    wid: int                  # workload id, part of every random stream key
+    bits: int                 # 2 or 4
+    k_layout: str             # TOKEN or CHANNEL
+    v_layout: str
+    group: int                # g: channels per group (token-wise) or tokens per group (channel-wise)
+    batch: int
+    num_q_heads: int
+    num_kv_heads: int
+    head_dim: int
+    max_seq_len: int          # Tcap: allocated tokens per sequence
+    ragged: bool = False      # lengths log-uniform in [ragged_lo, max_seq_len]
+    ragged_lo: int = 1024
+    seq_len: Optional[int] = None   # fixed length when not ragged (default Tcap)
+    k_outlier_frac: float = 0.0     # fraction of K channels per KV head scaled by k_outlier_scale
+    k_outlier_scale: float = 10.0
+    channel_std_logu: Optional[tuple] = None  # (lo, hi) per-(head, channel) std, log-uniform
+    seed: int = 0
+
+    @property
+    def sm_scale(self) -> float:
+        return 1.0 / math.sqrt(self.head_dim)
+
+    def replace(self, **kw) -> "Spec":
+        return dataclasses.replace(self, **kw)
+
+    def seq_lens(self) -> np.ndarray:
+        if self.ragged:
+            rng = np.random.default_rng([self.seed, self.wid, _T_LENS])
+            u = rng.uniform(math.log(self.ragged_lo), math.log(self.max_seq_len), size=self.batch)
+            lens = np.floor(np.exp(u)).astype(np.int64)
+            return np.clip(lens, self.ragged_lo, self.max_seq_len).astype(np.int32)
+        t = self.max_seq_len if self.seq_len is None else self.seq_len
+        return np.full(self.batch, t, dtype=np.int32)
+
+
+def _base_specs():
+    s = {}
+    s["c1_tiny_int2"] = Spec("c1_tiny_int2", 1, 2, TOKEN, TOKEN, 128, 1, 4, 1, 128, 1024)
+    for bits in (2, 4):
+        s[f"c2_paper_int{bits}"] = Spec(f"c2_paper_int{bits}", 2, bits, TOKEN, TOKEN, 128, 16, 32, 8, 128, 8192,
+                                        k_outlier_frac=0.05)
+    s["c3_long_int2"] = Spec("c3_long_int2", 3, 2, TOKEN, TOKEN, 128, 4, 32, 8, 128, 131072)
+    for bits in (2, 4):
+        s[f"c4_channel_int{bits}"] = Spec(f"c4_channel_int{bits}", 4, bits, CHANNEL, CHANNEL, 128, 8, 32, 8, 128,
+                                          32768, channel_std_logu=(0.1, 10.0))
+    for bits in (2, 4):
+        for g in (32, 64, 128):
+            s[f"c5_ragged_int{bits}_g{g}"] = Spec(f"c5_ragged_int{bits}_g{g}", 5, bits, TOKEN, CHANNEL, g, 64, 32, 8,
+                                                  128, 65536, ragged=True)
+    return s
+
+
+SPECS = _base_specs()
+
+
+def bf16_round(x: np.ndarray) -> np.ndarray:
+    """Round fp32 values to the nearest bf16 (ties to even); returns fp32 holding bf16 values."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    u = (u + 0x7FFF + ((u >> 16) & 1)) & 0xFFFF0000
+    return u.astype(np.uint32).view(np.float32)
+
+
+def bf16_bits(x: np.ndarray) -> np.ndarray:
+    """The uint16 bit patterns of fp32 values that are already bf16-representable."""
+    return (np.ascontiguousarray(x, dtype=np.float32).view(np.uint32) >> 16).astype(np.uint16)
+
+
+def quantize_minmax(x: np.ndarray, bits: int, axis: int, valid: Optional[np.ndarray] = None):
+    """Min-max asymmetric quantisation of ``x`` along ``axis`` (the group axis).
+
+    Returns (codes uint8, s fp16, z fp16); s and z have ``axis`` reduced.
+    ``valid`` (bool, same shape as x) excludes entries from min/max; excluded
+    entries get code 0.
+    """
+    levels = (1 << bits) - 1
+    xf = x.astype(np.float32)
+    if valid is None:
+        mn = xf.min(axis=axis)
+        mx = xf.max(axis=axis)
+    else:
+        mn = np.where(valid, xf, np.inf).min(axis=axis)
+        mx = np.where(valid, xf, -np.inf).max(axis=axis)
+        empty = ~np.isfinite(mn)
+        mn = np.where(empty, 0.0, mn).astype(np.float32)
+        mx = np.where(empty, 0.0, mx).astype(np.float32)
+    s16 = ((mx - mn) / np.float32(levels)).astype(np.float32).astype(np.float16)
+    z16 = mn.astype(np.float16)
+    s64 = np.expand_dims(s16.astype(np.float64), axis)
+    z64 = np.expand_dims(z16.astype(np.float64), axis)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        q = np.rint((xf.astype(np.float64) - z64) / s64)
+    q = np.where(s64 == 0.0, 0.0, q)
+    q = np.clip(np.nan_to_num(q, nan=0.0), 0, levels).astype(np.uint8)
+    if valid is not None:
+        q = np.where(valid, q, 0).astype(np.uint8)
+    return q, s16, z16
+
+
+def _outlier_channels(spec: Spec, h: int) -> np.ndarray:
+    n = int(round(spec.k_outlier_frac * spec.head_dim))
+    rng = np.random.default_rng([spec.seed, spec.wid, _T_OUTLIER, h])
+    return rng.choice(spec.head_dim, size=n, replace=False)
+
+
+def _channel_std(spec: Spec, tensor: int, h: int) -> np.ndarray:
+    lo, hi = spec.channel_std_logu
+    rng = np.random.default_rng([spec.seed, spec.wid, _T_STD, tensor, h])
+    return np.exp(rng.uniform(math.log(lo), math.log(hi), size=spec.head_dim)).astype(np.float32)
+
+
+def _quantize_head(spec: Spec, x: np.ndarray, layout: str, t_valid: int):
+    """Quantise one (T, D) head slice; returns codes [T, D] and (s, z) in the boundary layout."""
+    T, D = x.shape
+    g = spec.group
+    valid_tok = (np.arange(T) < t_valid)
+    if layout == TOKEN:
+        xg = x.reshape(T, D // g, g)
+        q, s, z = quantize_minmax(xg, spec.bits, axis=2)
+        q = q.reshape(T, D)
+        q[~valid_tok] = 0
+        s[~valid_tok] = 0
+        z[~valid_tok] = 0
+        return q, s, z                                # s, z: [T, D/g]
+    xg = x.reshape(T // g, g, D)
+    valid = np.broadcast_to(valid_tok.reshape(T // g, g, 1), xg.shape)
+    q, s, z = quantize_minmax(xg, spec.bits, axis=1, valid=valid)
+    return q.reshape(T, D), s, z                      # s, z: [T/g, D]
+
+
+def make_head(spec: Spec, b: int, h: int, seq_len: Optional[int] = None, poison: bool = False) -> dict:
+    """Cache slice of one (sequence b, KV head h): codes and (s, z) for K and V.
+
+    With ``poison`` the tokens past the sequence length get random codes and
+    NaN scales/offsets, to show that nothing past the length reaches the result.
+    """
+    T, D = spec.max_seq_len, spec.head_dim
+    t_valid = int(spec.seq_lens()[b] if seq_len is None else seq_len)
+    out = {}
+    for tensor, name, layout in ((_T_K, "k", spec.k_layout), (_T_V, "v", spec.v_layout)):
+        rng = np.random.default_rng([spec.seed, spec.wid, tensor, b, h])
+        x = rng.standard_normal((T, D), dtype=np.float32)
+        if spec.channel_std_logu is not None:
+            x *= _channel_std(spec, tensor, h)[None, :]
+        if tensor == _T_K and spec.k_outlier_frac > 0:
+            x[:, _outlier_channels(spec, h)] *= np.float32(spec.k_outlier_scale)
+        q, s, z = _quantize_head(spec, x, layout, t_valid)
+        if poison and t_valid < T:
+            prng = np.random.default_rng([spec.seed, spec.wid, _T_POISON, tensor, b, h])
+            q[t_valid:] = prng.integers(0, 1 << spec.bits, size=(T - t_valid, D), dtype=np.uint8)
+            if layout == TOKEN:
+                s[t_valid:] = np.float16(np.nan)
+                z[t_valid:] = np.float16(np.nan)
+            else:
+                first_dead = -(-t_valid // spec.group)
+                s[first_dead:] = np.float16(np.nan)
+                z[first_dead:] = np.float16(np.nan)
+        out[name + "_codes"] = q
+        out[name + "_scale"] = s
+        out[name + "_zero"] = z
+    return out
+
+
+def make_query(spec: Spec) -> np.ndarray:
+    """Query of the decode step: N(0,1) drawn in fp32, rounded to bf16; fp32 array [B, Hq, D]."""
+    rng = np.random.default_rng([spec.seed, spec.wid, _T_Q])
+    q = rng.standard_normal((spec.batch, spec.num_q_heads, spec.head_dim), dtype=np.float32)
+    return bf16_round(q)
+
+
+def scale_shape(spec: Spec, layout: str):
+    T, D, g = spec.max_seq_len, spec.head_dim, spec.group
+    return (T, D // g) if layout == TOKEN else (T // g, D)
+
+
+def make_workload(spec: Spec, threads: Optional[int] = None, poison: bool = False) -> dict:
+    """All inputs of one decode step, as numpy arrays in the boundary layouts.
+
+    Keys: q (fp32 holding bf16 values, [B,Hq,D]), k_codes / v_codes (uint8
+    [B,Hkv,Tcap,D]), k_scale / k_zero / v_scale / v_zero (fp16, token-wise
+    [B,Hkv,Tcap,D/g], channel-wise [B,Hkv,Tcap/g,D]), seq_lens (int32 [B]).
+    """
+    B, H, T, D = spec.batch, spec.num_kv_heads, spec.max_seq_len, spec.head_dim
+    lens = spec.seq_lens()
+    w = {
+        "q": make_query(spec),
+        "seq_lens": lens,
+        "k_codes": np.empty((B, H, T, D), np.uint8),
+        "v_codes": np.empty((B, H, T, D), np.uint8),
+        "k_scale": np.empty((B, H) + scale_shape(spec, spec.k_layout), np.float16),
+        "k_zero": np.empty((B, H) + scale_shape(spec, spec.k_layout), np.float16),
+        "v_scale": np.empty((B, H) + scale_shape(spec, spec.v_layout), np.float16),
+        "v_zero": np.empty((B, H) + scale_shape(spec, spec.v_layout), np.float16),
+    }
+
+    def one(bh):
+        b, h = bh
+        head = make_head(spec, b, h, seq_len=int(lens[b]), poison=poison)
+        for k, v in head.items():
+            w[k][b, h] = v
+
+    n = threads or min(16, os.cpu_count() or 1)
+    jobs = [(b, h) for b in range(B) for h in range(H)]
+    if n <= 1 or len(jobs) == 1:
+        for j in jobs:
+            one(j)
+    else:
+        with ThreadPoolExecutor(n) as ex:
+            list(ex.map(one, jobs))
+    return w
+
+
+def algorithmic_bytes(spec: Spec, lens: Optional[np.ndarray] = None) -> int:
+    """Bytes one decode step must move at least: packed K and V codes and their
+    fp16 (s, z) for the valid tokens, the bf16 query, the bf16 output, the fp32
+    lse and the int32 lengths."""
+    if lens is None:
+        lens = spec.seq_lens()
+    D, H, g = spec.head_dim, spec.num_kv_heads, spec.group
+    total = 0
+    for t in lens.astype(np.int64):
+        codes = 2 * t * D * spec.bits // 8
+        sz = 0
+        for layout in (spec.k_layout, spec.v_layout):
+            if layout == TOKEN:
+                sz += 2 * 2 * t * (D // g)
+            else:
+                sz += 2 * 2 * (-(-t // g)) * D
+        total += H * (codes + sz)
+    B, Hq = spec.batch, spec.num_q_heads
+    total += 2 * B * Hq * D + 2 * B * Hq * D + 4 * B * Hq + 4 * B
+    return int(total)
