@@ -20,7 +20,8 @@ What it computes (fp64 throughout):
   explainer, issue-budget paragraph).
 * ``pack_k`` / ``pack_v`` / ``unpack_k`` / ``unpack_v``: the packed code layout
   of the C interface, written from its specification (keys packed along
-  channels, values packed along tokens, element 0 in the lowest bits).
+  channels, values packed along tokens; even elements of a word in its low
+  half-word, odd elements in its high half-word).
 
 Parity pins: every function here is pinned by ``tests/test_oracle_pins.py``
 (worked receipt, exact fold-vs-unfold, closed forms, invariants, a textbook
@@ -130,15 +131,25 @@ def decode_rows(w: dict, rows, *, k_layout: str, v_layout: str, group: int, sm_s
 
 # ---------------------------------------------------------------------------
 # Packed code layout of the C interface, written from its specification.
-#   keys:   word [t][c // E], channel c at bits [bits*(c % E), +bits)
-#   values: word [t // E][c], token t at bits [bits*(t % E), +bits)
-# with E = 32 / bits codes per 32-bit word, element 0 in the lowest bits.
+# E = 32 / bits codes per 32-bit word, packed along the axis the consuming
+# product sums over:
+#   keys:   word [t][c // E] holds channels E*(c // E) .. + E-1 of token t
+#   values: word [t // E][c] holds tokens   E*(t // E) .. + E-1 of channel c
+# Inside a word, element e (0 .. E-1) occupies bits
+#   [bits*(e // 2) + 16*(e % 2), + bits)
+# i.e. even elements fill the low half-word and odd elements the high
+# half-word, each half in increasing order from bit 0 (resp. bit 16).
 # ---------------------------------------------------------------------------
 
 def _per_word(bits: int) -> int:
     if bits not in (2, 4):
         raise ValueError("bits must be 2 or 4")
     return 32 // bits
+
+
+def element_shift(bits: int, e: int) -> int:
+    """Bit offset of element e inside its word."""
+    return bits * (e // 2) + 16 * (e % 2)
 
 
 def pack_k(codes, bits: int) -> np.ndarray:
@@ -149,7 +160,7 @@ def pack_k(codes, bits: int) -> np.ndarray:
     c = c.reshape(*lead, T, D // E, E)
     word = np.zeros((*lead, T, D // E), dtype=np.uint32)
     for e in range(E):
-        word |= (c[..., e] & ((1 << bits) - 1)) << np.uint32(bits * e)
+        word |= (c[..., e] & ((1 << bits) - 1)) << np.uint32(element_shift(bits, e))
     return word
 
 
@@ -159,7 +170,7 @@ def unpack_k(words, bits: int, head_dim: int) -> np.ndarray:
     *lead, T, W = wv.shape
     out = np.zeros((*lead, T, W, E), dtype=np.uint8)
     for e in range(E):
-        out[..., e] = (wv >> np.uint32(bits * e)) & ((1 << bits) - 1)
+        out[..., e] = (wv >> np.uint32(element_shift(bits, e))) & ((1 << bits) - 1)
     return out.reshape(*lead, T, W * E)[..., :head_dim]
 
 
@@ -171,7 +182,7 @@ def pack_v(codes, bits: int) -> np.ndarray:
     c = c.reshape(*lead, T // E, E, D)
     word = np.zeros((*lead, T // E, D), dtype=np.uint32)
     for e in range(E):
-        word |= (c[..., e, :] & ((1 << bits) - 1)) << np.uint32(bits * e)
+        word |= (c[..., e, :] & ((1 << bits) - 1)) << np.uint32(element_shift(bits, e))
     return word
 
 
@@ -181,5 +192,5 @@ def unpack_v(words, bits: int) -> np.ndarray:
     *lead, W, D = wv.shape
     out = np.zeros((*lead, W, E, D), dtype=np.uint8)
     for e in range(E):
-        out[..., e, :] = (wv >> np.uint32(bits * e)) & ((1 << bits) - 1)
+        out[..., e, :] = (wv >> np.uint32(element_shift(bits, e))) & ((1 << bits) - 1)
     return out.reshape(*lead, W * E, D)

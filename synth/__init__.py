@@ -64,6 +64,7 @@ class Spec:
     k_outlier_scale: float = 10.0
     channel_std_logu: Optional[tuple] = None  # (lo, hi) per-(head, channel) std, log-uniform
     seed: int = 0
+    lens: Optional[tuple] = None    # explicit per-sequence lengths (edge-case tests)
 
     @property
     def sm_scale(self) -> float:
@@ -73,6 +74,8 @@ class Spec:
         return dataclasses.replace(self, **kw)
 
     def seq_lens(self) -> np.ndarray:
+        if self.lens is not None:
+            return np.array(self.lens, dtype=np.int32)
         if self.ragged:
             rng = np.random.default_rng([self.seed, self.wid, _T_LENS])
             u = rng.uniform(math.log(self.ragged_lo), math.log(self.max_seq_len), size=self.batch)
@@ -187,7 +190,9 @@ def make_head(spec: Spec, b: int, h: int, seq_len: Optional[int] = None, poison:
     out = {}
     for tensor, name, layout in ((_T_K, "k", spec.k_layout), (_T_V, "v", spec.v_layout)):
         rng = np.random.default_rng([spec.seed, spec.wid, tensor, b, h])
-        x = rng.standard_normal((T, D), dtype=np.float32)
+        # only the valid tokens are drawn (a prefix of the stream); padding is zero
+        x = np.zeros((T, D), dtype=np.float32)
+        x[:t_valid] = rng.standard_normal((t_valid, D), dtype=np.float32)
         if spec.channel_std_logu is not None:
             x *= _channel_std(spec, tensor, h)[None, :]
         if tensor == _T_K and spec.k_outlier_frac > 0:
@@ -278,3 +283,23 @@ def algorithmic_bytes(spec: Spec, lens: Optional[np.ndarray] = None) -> int:
     B, Hq = spec.batch, spec.num_q_heads
     total += 2 * B * Hq * D + 2 * B * Hq * D + 4 * B * Hq + 4 * B
     return int(total)
+
+
+def make_sequence(spec: Spec, b: int, threads: Optional[int] = None, poison: bool = False) -> dict:
+    """All KV heads of sequence b, stacked: codes [Hkv, Tcap, D], (s, z) [Hkv, ...]."""
+    H = spec.num_kv_heads
+    t = int(spec.seq_lens()[b])
+    n = threads or min(16, os.cpu_count() or 1)
+    if n > 1 and H > 1:
+        with ThreadPoolExecutor(min(n, H)) as ex:
+            heads = list(ex.map(lambda h: make_head(spec, b, h, seq_len=t, poison=poison), range(H)))
+    else:
+        heads = [make_head(spec, b, h, seq_len=t, poison=poison) for h in range(H)]
+    return {k: np.stack([hd[k] for hd in heads]) for k in heads[0]}
+
+
+def full_scale_shapes(spec: Spec) -> dict:
+    B, H = spec.batch, spec.num_kv_heads
+    ks = (B, H) + scale_shape(spec, spec.k_layout)
+    vs = (B, H) + scale_shape(spec, spec.v_layout)
+    return {"k_scale": ks, "k_zero": ks, "v_scale": vs, "v_zero": vs}
