@@ -1,0 +1,206 @@
+"""Python binding of libfoscar: decode attention over a 2-/4-bit KV cache on MI355X.
+
+Thin marshalling over the C interface of include/foscar.h; every function of
+that header is available here under the same name, taking torch tensors (used
+only as device memory) instead of raw pointers, plus ``decode`` / ``pack`` /
+``unpack`` conveniences.  All computation runs in the HIP kernels of
+libfoscar.so; if the library is not built, importing the entry points raises.
+
+Layout constants and shapes are those of the C header.
+"""
+import ctypes
+import math
+
+from . import _lib
+
+FOSCAR_OK = 0
+FOSCAR_EINVAL = -1
+FOSCAR_EUNSUPPORTED = -2
+FOSCAR_EHIP = -3
+FOSCAR_ENOMEM = -4
+FOSCAR_K_TOKEN = 0
+FOSCAR_K_CHANNEL = 1
+FOSCAR_V_TOKEN = 0
+FOSCAR_V_CHANNEL = 2
+FOSCAR_SIDE_K = 0
+FOSCAR_SIDE_V = 1
+
+FoscarDims = _lib.FoscarDims
+
+
+class FoscarError(RuntimeError):
+    def __init__(self, code, where):
+        lib = _lib.load()
+        msg = lib.foscar_strerror(code).decode()
+        hip = lib.foscar_last_hip_error() if code == FOSCAR_EHIP else 0
+        super().__init__(f"{where}: {msg} (code {code}{', hip error ' + str(hip) if hip else ''})")
+        self.code = code
+
+
+def _check(rc, where):
+    if rc != FOSCAR_OK:
+        if rc in (FOSCAR_EINVAL, FOSCAR_EUNSUPPORTED):
+            raise ValueError(f"{where}: {_lib.load().foscar_strerror(rc).decode()} (code {rc})")
+        raise FoscarError(rc, where)
+
+
+def layout_bits(k_layout: str, v_layout: str) -> int:
+    return (FOSCAR_K_CHANNEL if k_layout == "channel" else 0) | (FOSCAR_V_CHANNEL if v_layout == "channel" else 0)
+
+
+def make_dims(batch, num_q_heads, num_kv_heads, head_dim, max_seq_len, sm_scale=0.0):
+    return FoscarDims(int(batch), int(num_q_heads), int(num_kv_heads), int(head_dim), int(max_seq_len),
+                      float(sm_scale))
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else None
+
+
+def _stream(stream):
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _require(t, name, dtype, device):
+    import torch
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.device != device:
+        raise ValueError(f"{name} must be on {device}, got {t.device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _decode(bits, q, packed_k, packed_v, k_scale, k_zero, v_scale, v_zero, seq_lens, layout, group,
+            out=None, lse=None, sm_scale=0.0, stream=None):
+    import torch
+    lib = _lib.load()
+    dev = q.device
+    _require(q, "q", torch.bfloat16, dev)
+    for name, t in (("packed_k", packed_k), ("packed_v", packed_v)):
+        _require(t, name, torch.int32, dev)
+    for name, t in (("k_scale", k_scale), ("k_zero", k_zero), ("v_scale", v_scale), ("v_zero", v_zero)):
+        _require(t, name, torch.float16, dev)
+    _require(seq_lens, "seq_lens", torch.int32, dev)
+    B, Hq, D = q.shape
+    Hkv, Tcap = packed_k.shape[1], packed_k.shape[2]
+    if out is None:
+        out = torch.empty((B, Hq, D), dtype=torch.bfloat16, device=dev)
+    if lse is None:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=dev)
+    _require(out, "out", torch.bfloat16, dev)
+    _require(lse, "lse", torch.float32, dev)
+    dims = make_dims(B, Hq, Hkv, D, Tcap, sm_scale)
+    fn = lib.foscar_decode_int2 if bits == 2 else lib.foscar_decode_int4
+    with torch.cuda.device(dev):
+        rc = fn(ctypes.byref(dims), _ptr(q), _ptr(packed_k), _ptr(packed_v), _ptr(k_scale), _ptr(k_zero),
+                _ptr(v_scale), _ptr(v_zero), _ptr(seq_lens), int(layout), int(group), _ptr(out), _ptr(lse),
+                _stream(stream))
+    _check(rc, f"foscar_decode_int{bits}")
+    return out, lse
+
+
+def foscar_decode_int2(q, packed_k, packed_v, k_scale, k_zero, v_scale, v_zero, seq_lens, layout, group,
+                       out=None, lse=None, sm_scale=0.0, stream=None):
+    """2-bit decode step; tensors as in include/foscar.h (packed words as int32). Returns (out, lse)."""
+    return _decode(2, q, packed_k, packed_v, k_scale, k_zero, v_scale, v_zero, seq_lens, layout, group,
+                   out, lse, sm_scale, stream)
+
+
+def foscar_decode_int4(q, packed_k, packed_v, k_scale, k_zero, v_scale, v_zero, seq_lens, layout, group,
+                       out=None, lse=None, sm_scale=0.0, stream=None):
+    """4-bit decode step; tensors as in include/foscar.h (packed words as int32). Returns (out, lse)."""
+    return _decode(4, q, packed_k, packed_v, k_scale, k_zero, v_scale, v_zero, seq_lens, layout, group,
+                   out, lse, sm_scale, stream)
+
+
+def decode(q, packed_k, packed_v, k_scale, k_zero, v_scale, v_zero, seq_lens, *, bits, k_layout="token",
+           v_layout="token", group=128, sm_scale=0.0, out=None, lse=None, stream=None):
+    fn = foscar_decode_int2 if bits == 2 else foscar_decode_int4
+    return fn(q, packed_k, packed_v, k_scale, k_zero, v_scale, v_zero, seq_lens, layout_bits(k_layout, v_layout),
+              group, out, lse, sm_scale, stream)
+
+
+def _pack_dims(codes_shape):
+    B, Hkv, T, D = codes_shape
+    return make_dims(B, Hkv, Hkv, D, T)
+
+
+def packed_shape(bits, side, B, Hkv, T, D):
+    E = 32 // bits
+    return (B, Hkv, T, D // E) if side == FOSCAR_SIDE_K else (B, Hkv, T // E, D)
+
+
+def foscar_pack(bits, side, codes, packed=None, stream=None):
+    """codes uint8 [B, Hkv, Tcap, D] on the GPU -> packed int32 words (layout of include/foscar.h)."""
+    import torch
+    lib = _lib.load()
+    _require(codes, "codes", torch.uint8, codes.device)
+    dims = _pack_dims(codes.shape)
+    if packed is None:
+        packed = torch.empty(packed_shape(bits, side, *codes.shape), dtype=torch.int32, device=codes.device)
+    _require(packed, "packed", torch.int32, codes.device)
+    with torch.cuda.device(codes.device):
+        rc = lib.foscar_pack(int(bits), int(side), ctypes.byref(dims), _ptr(codes), _ptr(packed), _stream(stream))
+    _check(rc, "foscar_pack")
+    return packed
+
+
+def foscar_unpack(bits, side, packed, shape, codes=None, stream=None):
+    """packed int32 words -> codes uint8 of ``shape`` = [B, Hkv, Tcap, D]."""
+    import torch
+    lib = _lib.load()
+    _require(packed, "packed", torch.int32, packed.device)
+    dims = _pack_dims(shape)
+    if codes is None:
+        codes = torch.empty(tuple(shape), dtype=torch.uint8, device=packed.device)
+    _require(codes, "codes", torch.uint8, packed.device)
+    with torch.cuda.device(packed.device):
+        rc = lib.foscar_unpack(int(bits), int(side), ctypes.byref(dims), _ptr(packed), _ptr(codes), _stream(stream))
+    _check(rc, "foscar_unpack")
+    return codes
+
+
+pack = foscar_pack
+unpack = foscar_unpack
+
+
+def foscar_packed_bytes(bits, side, dims):
+    return int(_lib.load().foscar_packed_bytes(int(bits), int(side), ctypes.byref(dims)))
+
+
+def foscar_scale_count(side, side_layout, group, dims):
+    return int(_lib.load().foscar_scale_count(int(side), int(side_layout), int(group), ctypes.byref(dims)))
+
+
+def foscar_workspace_reserve(dims, layout, group, stream=None):
+    _check(_lib.load().foscar_workspace_reserve(ctypes.byref(dims), int(layout), int(group), _stream(stream)),
+           "foscar_workspace_reserve")
+
+
+def foscar_release():
+    _lib.load().foscar_release()
+
+
+def foscar_split_plan(dims, layout, group):
+    s, c = ctypes.c_int32(0), ctypes.c_int32(0)
+    _check(_lib.load().foscar_split_plan(ctypes.byref(dims), int(layout), int(group), ctypes.byref(s),
+                                         ctypes.byref(c)), "foscar_split_plan")
+    return s.value, c.value
+
+
+def foscar_strerror(code):
+    return _lib.load().foscar_strerror(int(code)).decode()
+
+
+def foscar_version():
+    return int(_lib.load().foscar_version())
+
+
+def foscar_last_hip_error():
+    return int(_lib.load().foscar_last_hip_error())

@@ -1,0 +1,305 @@
+// Host side of libfoscar: the C interface declared in include/foscar.h.
+// Every argument is checked before the first HIP call; errors are returned as
+// codes, never thrown.  The only memory the library owns is the grow-only
+// split workspace, one per (device, stream).
+#include <math.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include <map>
+#include <mutex>
+#include <utility>
+
+#include "../../include/foscar.h"
+#include "foscar_internal.h"
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+struct Workspace {
+  void* ptr = nullptr;
+  size_t bytes = 0;
+};
+
+std::mutex g_ws_mutex;
+std::map<std::pair<int, void*>, Workspace> g_ws;  // (device, stream) -> workspace
+std::map<int, int> g_cus;                           // device -> compute units
+
+int hip_fail(hipError_t e) {
+  g_last_hip_error = (int)e;
+  return (e == hipErrorOutOfMemory || e == hipErrorMemoryAllocation) ? FOSCAR_ENOMEM : FOSCAR_EHIP;
+}
+
+bool valid_group(int g) { return g == 32 || g == 64 || g == 128; }
+
+// Shape checks shared by every entry point that takes dims.
+int check_dims(const foscar_dims* d, bool need_heads_ratio) {
+  if (!d) return FOSCAR_EINVAL;
+  if (d->batch < 0 || d->num_q_heads < 1 || d->num_kv_heads < 1 || d->head_dim < 1 || d->max_seq_len < 0)
+    return FOSCAR_EINVAL;
+  if (d->head_dim != foscar::kHeadDim) return FOSCAR_EUNSUPPORTED;
+  if (need_heads_ratio) {
+    if (d->num_q_heads % d->num_kv_heads != 0) return FOSCAR_EINVAL;
+    if (d->num_q_heads / d->num_kv_heads > foscar::kMaxG) return FOSCAR_EUNSUPPORTED;
+  }
+  return FOSCAR_OK;
+}
+
+int check_decode_shape(const foscar_dims* d, int layout, int group) {
+  int rc = check_dims(d, true);
+  if (rc) return rc;
+  if (layout < 0 || layout > 3) return FOSCAR_EINVAL;
+  if (!valid_group(group)) return FOSCAR_EUNSUPPORTED;
+  if (d->max_seq_len % foscar::kTile != 0) return FOSCAR_EUNSUPPORTED;
+  if (layout != 0 && d->max_seq_len % group != 0) return FOSCAR_EUNSUPPORTED;
+  return FOSCAR_OK;
+}
+
+// tokens one wave takes at a time
+int unit_tokens(int layout, int group) { return (layout != 0 && group > foscar::kTile) ? group : foscar::kTile; }
+
+int compute_units(int device) {
+  std::lock_guard<std::mutex> lk(g_ws_mutex);
+  auto it = g_cus.find(device);
+  if (it != g_cus.end()) return it->second;
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device) != hipSuccess || cus <= 0) cus = 256;
+  g_cus[device] = cus;
+  return cus;
+}
+
+// Split plan: enough work-groups to fill the chip, ranges of at most 4096
+// tokens so ragged batches balance, every range a multiple of the wave unit.
+void plan(const foscar_dims* d, int layout, int group, int cus, int32_t* splits, int32_t* chunk) {
+  const int unit = unit_tokens(layout, group);
+  const int tcap = d->max_seq_len;
+  const int units = tcap / unit;
+  if (units == 0) {
+    *splits = 1;
+    *chunk = unit;
+    return;
+  }
+  const long long bh = (long long)d->batch * d->num_kv_heads;
+  long long s = 1;
+  const char* env = getenv("FOSCAR_SPLITS");
+  if (env && atoi(env) > 0) {
+    s = atoi(env);
+  } else {
+    const long long target = 4LL * cus;  // work-groups in flight wanted
+    if (bh > 0) s = (target + bh - 1) / bh;
+    const long long by_len = (tcap + 4095) / 4096;
+    if (s < by_len) s = by_len;
+  }
+  if (s > units) s = units;
+  if (s < 1) s = 1;
+  const long long per = (units + s - 1) / s;
+  *chunk = (int32_t)(per * unit);
+  *splits = (int32_t)((units + per - 1) / per);
+}
+
+size_t workspace_bytes(const foscar_dims* d, int32_t splits) {
+  const size_t rows = (size_t)d->batch * d->num_q_heads * splits;
+  return rows * (foscar::kHeadDim + 1) * sizeof(float);
+}
+
+// Grow-only workspace of (current device, stream).  Growing frees the old
+// buffer after synchronising the device, so no running call still uses it.
+int get_workspace(size_t bytes, hipStream_t stream, void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e);
+  std::lock_guard<std::mutex> lk(g_ws_mutex);
+  Workspace& ws = g_ws[std::make_pair(dev, (void*)stream)];
+  if (ws.bytes < bytes) {
+    if (ws.ptr) {
+      e = hipDeviceSynchronize();
+      if (e != hipSuccess) return hip_fail(e);
+      (void)hipFree(ws.ptr);
+      ws.ptr = nullptr;
+      ws.bytes = 0;
+    }
+    e = hipMalloc(&ws.ptr, bytes);
+    if (e != hipSuccess) {
+      ws.ptr = nullptr;
+      return hip_fail(e);
+    }
+    ws.bytes = bytes;
+  }
+  *out = ws.ptr;
+  return FOSCAR_OK;
+}
+
+int decode_common(int bits, const foscar_dims* d, const void* q, const void* pk, const void* pv, const void* ks,
+                  const void* kz, const void* vs, const void* vz, const int32_t* seq_lens, int layout, int group,
+                  void* out, float* lse, void* stream) {
+  int rc = check_decode_shape(d, layout, group);
+  if (rc) return rc;
+  if (d->batch == 0) return FOSCAR_OK;
+  if (!q || !pk || !pv || !ks || !kz || !vs || !vz || !seq_lens || !out) return FOSCAR_EINVAL;
+
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e);
+  int32_t splits = 1, chunk = foscar::kTile;
+  plan(d, layout, group, compute_units(dev), &splits, &chunk);
+  void* ws = nullptr;
+  rc = get_workspace(workspace_bytes(d, splits), (hipStream_t)stream, &ws);
+  if (rc) return rc;
+
+  const float sm = d->sm_scale > 0.f ? d->sm_scale : 1.0f / sqrtf((float)d->head_dim);
+  foscar::SplitArgs sa;
+  sa.q = (const uint16_t*)q;
+  sa.pk = (const uint32_t*)pk;
+  sa.pv = (const uint32_t*)pv;
+  sa.ks = (const uint16_t*)ks;
+  sa.kz = (const uint16_t*)kz;
+  sa.vs = (const uint16_t*)vs;
+  sa.vz = (const uint16_t*)vz;
+  sa.seq_lens = seq_lens;
+  sa.o_part = (float*)ws;
+  sa.lse_part = (float*)ws + (size_t)d->batch * d->num_q_heads * splits * foscar::kHeadDim;
+  sa.hq = d->num_q_heads;
+  sa.hkv = d->num_kv_heads;
+  sa.g_heads = d->num_q_heads / d->num_kv_heads;
+  sa.tcap = d->max_seq_len;
+  sa.splits = splits;
+  sa.chunk = chunk;
+  sa.sm_log2 = sm * 1.4426950408889634f;
+
+  foscar::MergeArgs ma;
+  ma.o_part = sa.o_part;
+  ma.lse_part = sa.lse_part;
+  ma.seq_lens = seq_lens;
+  ma.out = (uint16_t*)out;
+  ma.lse = lse;
+  ma.hq = d->num_q_heads;
+  ma.tcap = d->max_seq_len;
+  ma.splits = splits;
+  ma.chunk = chunk;
+
+  e = foscar::launch_decode(bits, (layout & FOSCAR_K_CHANNEL) != 0, (layout & FOSCAR_V_CHANNEL) != 0, group,
+                            d->batch, d->num_kv_heads, sa, ma, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e);
+  return FOSCAR_OK;
+}
+
+int check_pack(int bits, int side, const foscar_dims* d) {
+  if (bits != 2 && bits != 4) return FOSCAR_EINVAL;
+  if (side != FOSCAR_SIDE_K && side != FOSCAR_SIDE_V) return FOSCAR_EINVAL;
+  int rc = check_dims(d, false);
+  if (rc) return rc;
+  if (side == FOSCAR_SIDE_V && d->max_seq_len % (32 / bits) != 0) return FOSCAR_EUNSUPPORTED;
+  return FOSCAR_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int foscar_decode_int2(const foscar_dims* dims, const void* q, const void* packed_k, const void* packed_v,
+                       const void* k_scale, const void* k_zero, const void* v_scale, const void* v_zero,
+                       const int32_t* seq_lens, int layout, int group, void* out, float* lse, void* stream) {
+  return decode_common(2, dims, q, packed_k, packed_v, k_scale, k_zero, v_scale, v_zero, seq_lens, layout, group,
+                       out, lse, stream);
+}
+
+int foscar_decode_int4(const foscar_dims* dims, const void* q, const void* packed_k, const void* packed_v,
+                       const void* k_scale, const void* k_zero, const void* v_scale, const void* v_zero,
+                       const int32_t* seq_lens, int layout, int group, void* out, float* lse, void* stream) {
+  return decode_common(4, dims, q, packed_k, packed_v, k_scale, k_zero, v_scale, v_zero, seq_lens, layout, group,
+                       out, lse, stream);
+}
+
+int foscar_pack(int bits, int side, const foscar_dims* dims, const uint8_t* codes, void* packed, void* stream) {
+  int rc = check_pack(bits, side, dims);
+  if (rc) return rc;
+  if ((size_t)dims->batch * dims->num_kv_heads * dims->max_seq_len == 0) return FOSCAR_OK;
+  if (!codes || !packed) return FOSCAR_EINVAL;
+  hipError_t e = foscar::launch_pack(bits, side, dims->batch, dims->num_kv_heads, dims->max_seq_len, codes,
+                                     (uint32_t*)packed, (hipStream_t)stream);
+  return e == hipSuccess ? FOSCAR_OK : hip_fail(e);
+}
+
+int foscar_unpack(int bits, int side, const foscar_dims* dims, const void* packed, uint8_t* codes, void* stream) {
+  int rc = check_pack(bits, side, dims);
+  if (rc) return rc;
+  if ((size_t)dims->batch * dims->num_kv_heads * dims->max_seq_len == 0) return FOSCAR_OK;
+  if (!codes || !packed) return FOSCAR_EINVAL;
+  hipError_t e = foscar::launch_unpack(bits, side, dims->batch, dims->num_kv_heads, dims->max_seq_len,
+                                       (const uint32_t*)packed, codes, (hipStream_t)stream);
+  return e == hipSuccess ? FOSCAR_OK : hip_fail(e);
+}
+
+size_t foscar_packed_bytes(int bits, int side, const foscar_dims* dims) {
+  if (check_pack(bits, side, dims)) return 0;
+  return (size_t)dims->batch * dims->num_kv_heads * dims->max_seq_len * dims->head_dim * bits / 8;
+}
+
+size_t foscar_scale_count(int side, int side_layout, int group, const foscar_dims* dims) {
+  if (check_dims(dims, false) || !valid_group(group)) return 0;
+  if (side != FOSCAR_SIDE_K && side != FOSCAR_SIDE_V) return 0;
+  const int channel_bit = side == FOSCAR_SIDE_K ? FOSCAR_K_CHANNEL : FOSCAR_V_CHANNEL;
+  if (side_layout != 0 && side_layout != channel_bit) return 0;
+  const size_t bh = (size_t)dims->batch * dims->num_kv_heads;
+  if (side_layout == 0) return bh * dims->max_seq_len * (dims->head_dim / group);
+  if (dims->max_seq_len % group) return 0;
+  return bh * (dims->max_seq_len / group) * dims->head_dim;
+}
+
+int foscar_split_plan(const foscar_dims* dims, int layout, int group, int32_t* splits, int32_t* chunk) {
+  int rc = check_decode_shape(dims, layout, group);
+  if (rc) return rc;
+  if (!splits || !chunk) return FOSCAR_EINVAL;
+  int dev = 0;
+  int cus = 256;
+  if (hipGetDevice(&dev) == hipSuccess) cus = compute_units(dev);
+  plan(dims, layout, group, cus, splits, chunk);
+  return FOSCAR_OK;
+}
+
+int foscar_workspace_reserve(const foscar_dims* dims, int layout, int group, void* stream) {
+  int rc = check_decode_shape(dims, layout, group);
+  if (rc) return rc;
+  if (dims->batch == 0) return FOSCAR_OK;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e);
+  int32_t splits = 1, chunk = 0;
+  plan(dims, layout, group, compute_units(dev), &splits, &chunk);
+  void* ws = nullptr;
+  return get_workspace(workspace_bytes(dims, splits), (hipStream_t)stream, &ws);
+}
+
+void foscar_release(void) {
+  std::lock_guard<std::mutex> lk(g_ws_mutex);
+  if (g_ws.empty()) return;
+  int cur = 0;
+  bool have_cur = hipGetDevice(&cur) == hipSuccess;
+  for (auto& kv : g_ws) {
+    if (!kv.second.ptr) continue;
+    if (hipSetDevice(kv.first.first) == hipSuccess) {
+      (void)hipDeviceSynchronize();
+      (void)hipFree(kv.second.ptr);
+    }
+  }
+  g_ws.clear();
+  if (have_cur) (void)hipSetDevice(cur);
+}
+
+const char* foscar_strerror(int code) {
+  switch (code) {
+    case FOSCAR_OK: return "ok";
+    case FOSCAR_EINVAL: return "invalid argument";
+    case FOSCAR_EUNSUPPORTED: return "unsupported shape or parameter";
+    case FOSCAR_EHIP: return "HIP runtime error";
+    case FOSCAR_ENOMEM: return "out of device memory";
+  }
+  return "unknown error";
+}
+
+int foscar_version(void) { return FOSCAR_VERSION; }
+
+int foscar_last_hip_error(void) { return g_last_hip_error; }
+
+}  // extern "C"

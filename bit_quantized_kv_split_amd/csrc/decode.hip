@@ -1,0 +1,646 @@
+// Split-KV decode attention over a 2-/4-bit quantised KV cache, gfx950.
+//
+// Method: FOSCAR ("Accelerating Decode Attention over 2- and 4-Bit KV Caches
+// through Affine Folding", arXiv 2611.09722, abstract) as explained on
+// "FOSCAR speeds up 2-bit KV decode -- Affine folding of KV dequantization"
+// (learnaivisually): value = s*q + z per group (encoding paragraph); fold rule
+// and fold-placement table: token-wise K and channel-wise V take acc-fold
+// (scale the finished partial sum of a group once), channel-wise K and
+// token-wise V take operand-fold (pre-scale Q or the softmax weights P); each
+// offset becomes a correction z * (sum of the other operand); key-side
+// corrections land before the softmax and value-side ones before the final
+// division; an unscaled partial sum never crosses a group boundary.
+//
+// Work decomposition (MI355X-native; the pages' Hopper/Blackwell pipelines
+// are not used):
+//   * grid = (ranges S, KV heads, sequences); a work-group of 4 waves owns one
+//     token range of one (sequence, KV head); waves take 64-token tiles (or
+//     g-token units when a channel-wise group is longer than a tile) in turn;
+//   * per tile, lane l streams token l's packed key row and the packed value
+//     words of channels 2l, 2l+1 straight from HBM into registers (dwordx4 /
+//     dwordx2, one tile of prefetch in flight);
+//   * codes become matrix-core operands by one AND-OR per fp16 pair: a code
+//     dropped into the mantissa under a fixed exponent reads as C + q (C a
+//     power of two), and the C*sum(other operand) it adds is removed once per
+//     row together with the offset correction -- no per-value convert or FMA;
+//   * QK^T: v_mfma_f32_4x4x4_16b_f16, block = 4 tokens x 4 query heads, so
+//     each lane ends with 4 dense scores (4 tokens of its quad, one query head)
+//     and the key-side fold, mask and online softmax run on dense registers;
+//   * P V: the same instruction with blocks over channels; the 4x4 P block of
+//     every quad is shared through LDS (one 8-byte store, eight 16-byte loads
+//     per lane per tile);
+//   * online softmax with the exact running max of each query head (DPP,
+//     ds_swizzle and ds_bpermute reductions across the 16 lanes of a head; the
+//     accumulators are rescaled only when a max rises);
+//   * the range's partial (O, lse) goes to a workspace and a second kernel
+//     merges the ranges by log-sum-exp.
+#include <math.h>
+
+#include "foscar_internal.h"
+
+namespace foscar {
+namespace {
+
+typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+typedef float f4 __attribute__((ext_vector_type(4)));
+
+constexpr float kLn2 = 0.69314718055994530942f;
+
+__device__ __forceinline__ uint32_t and_or(uint32_t x, uint32_t m, uint32_t e) { return (x & m) | e; }
+__device__ __forceinline__ h4 cat4(uint32_t lo, uint32_t hi) {
+  return __builtin_bit_cast(h4, (unsigned long long)lo | ((unsigned long long)hi << 32));
+}
+__device__ __forceinline__ h2 as_h2(uint32_t u) { return __builtin_bit_cast(h2, u); }
+__device__ __forceinline__ uint32_t as_u32(h2 v) { return __builtin_bit_cast(uint32_t, v); }
+__device__ __forceinline__ float half_lo(uint32_t u) { return (float)__builtin_bit_cast(h2, u)[0]; }
+__device__ __forceinline__ float half_hi(uint32_t u) { return (float)__builtin_bit_cast(h2, u)[1]; }
+__device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2(as_h2(a), as_h2(b), c, false);
+}
+__device__ __forceinline__ uint32_t pack_f16(float lo, float hi) {
+  h2 v = {(_Float16)lo, (_Float16)hi};
+  return as_u32(v);
+}
+__device__ __forceinline__ uint32_t splat_f16(float c) { return pack_f16(c, c); }
+
+// ---------------------------------------------------------------------------
+// Code -> fp16 operand construction.  A packed word holds E codes; element e
+// sits at bit bits*(e/2) + 16*(e%2), so pair k = elements (2k, 2k+1) occupies
+// the same bit position p_k in both half-words.  AND with the pair's 2-bit
+// (4-bit) mask after an optional shift that brings it to position p, OR with
+// the fp16 exponent that gives mantissa bit p the weight 1: each half then
+// reads exactly C + code with C = 2^(10 - p).
+// ---------------------------------------------------------------------------
+template <int BITS>
+struct Codec;
+
+template <>
+struct Codec<2> {
+  static constexpr int E = 16;      // codes per word
+  static constexpr int PAIRS = 8;   // fp16 pairs per word
+  // C of pair k (positions 4, 6, 8 -> 64, 16, 4)
+  __host__ __device__ static constexpr float bias(int k) {
+    return (k == 4 || k == 7) ? 4.0f : ((k == 1 || k == 3 || k == 6) ? 16.0f : 64.0f);
+  }
+  __device__ static __forceinline__ void extract(uint32_t w, uint32_t (&p)[8]) {
+    const uint32_t l = w << 4, r = w >> 6;
+    p[0] = and_or(l, 0x00300030u, 0x54005400u);  // bits 0-1   -> 4-5
+    p[1] = and_or(l, 0x00C000C0u, 0x4C004C00u);  // bits 2-3   -> 6-7
+    p[2] = and_or(w, 0x00300030u, 0x54005400u);  // bits 4-5
+    p[3] = and_or(w, 0x00C000C0u, 0x4C004C00u);  // bits 6-7
+    p[4] = and_or(w, 0x03000300u, 0x44004400u);  // bits 8-9
+    p[5] = and_or(r, 0x00300030u, 0x54005400u);  // bits 10-11 -> 4-5
+    p[6] = and_or(r, 0x00C000C0u, 0x4C004C00u);  // bits 12-13 -> 6-7
+    p[7] = and_or(r, 0x03000300u, 0x44004400u);  // bits 14-15 -> 8-9
+  }
+};
+
+template <>
+struct Codec<4> {
+  static constexpr int E = 8;
+  static constexpr int PAIRS = 4;
+  __host__ __device__ static constexpr float bias(int) { return 64.0f; }
+  __device__ static __forceinline__ void extract(uint32_t w, uint32_t (&p)[4]) {
+    p[0] = and_or(w << 4, 0x00F000F0u, 0x54005400u);  // bits 0-3   -> 4-7
+    p[1] = and_or(w, 0x00F000F0u, 0x54005400u);       // bits 4-7
+    p[2] = and_or(w >> 4, 0x00F000F0u, 0x54005400u);  // bits 8-11  -> 4-7
+    p[3] = and_or(w >> 8, 0x00F000F0u, 0x54005400u);  // bits 12-15 -> 4-7
+  }
+};
+
+// Cross-lane helpers.  Lane l holds query head (l & 3) of quad (l >> 2); the
+// lanes of one query head are l, l^4, l^8, ... (stride 4).
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xf, 0xf, false));
+}
+// value of lane (l & ~3) | I, i.e. query head I of this lane's quad
+template <int I>
+__device__ __forceinline__ float quad_bcast(float v) {
+  return dpp<(I | (I << 2) | (I << 4) | (I << 6))>(v);
+}
+// v of lane l ^ 16 (ds_swizzle bit-mask mode inside each 32-lane half)
+__device__ __forceinline__ float xor16(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, v), 0x401F));
+}
+// v of lane l ^ 32
+__device__ __forceinline__ float xor32(float v) { return __shfl_xor(v, 32); }
+// {v of this lane's counterpart in half-wave 0, in half-wave 1}
+__device__ __forceinline__ void halves(float v, float& h0, float& h1) {
+  const float o = xor32(v);
+  const bool lo = (threadIdx.x & 63) < 32;
+  h0 = lo ? v : o;
+  h1 = lo ? o : v;
+}
+__device__ __forceinline__ float wave_max_same_query(float v) {
+  v = fmaxf(v, dpp<0x124>(v));  // row_ror:4
+  v = fmaxf(v, dpp<0x128>(v));  // row_ror:8
+  v = fmaxf(v, xor16(v));
+  return fmaxf(v, xor32(v));
+}
+template <int SPAN>  // sum over the lanes of one query head within SPAN lanes (32: half-wave, 64: wave)
+__device__ __forceinline__ float sum_same_query(float v) {
+  v += dpp<0x124>(v);
+  v += dpp<0x128>(v);
+  v += xor16(v);
+  if (SPAN == 64) v += xor32(v);
+  return v;
+}
+
+template <int N>
+__device__ __forceinline__ void load_u2(uint2 (&dst)[N], const uint16_t* p) {
+  const uint2* q = reinterpret_cast<const uint2*>(p);
+#pragma unroll
+  for (int i = 0; i < N; ++i) dst[i] = q[i];
+}
+
+// ---------------------------------------------------------------------------
+// Split kernel.
+// BITS: 2 or 4; KCH / VCH: channel-wise key / value groups; GRP: g.
+// ---------------------------------------------------------------------------
+template <int BITS, bool KCH, bool VCH, int GRP>
+__global__ __launch_bounds__(256) void split_decode(const SplitArgs a) {
+  using C = Codec<BITS>;
+  constexpr int D = kHeadDim;
+  constexpr int E = C::E;
+  constexpr int PAIRS = C::PAIRS;
+  constexpr int KPW = PAIRS / 2;           // k-steps (of 4 channels / 4 tokens) per word
+  constexpr int KW = D / E;                // key words per token
+  constexpr int VW = kTile / E;            // value token-words per tile
+  constexpr int NGK = KCH ? 1 : D / GRP;   // key groups per token
+  constexpr int NGV = VCH ? 1 : D / GRP;   // value groups per token
+  constexpr int UNIT = ((KCH || VCH) && GRP > kTile) ? GRP : kTile;
+  constexpr int TPU = UNIT / kTile;
+
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int split = blockIdx.x;
+  const int h = blockIdx.y;
+  const int b = blockIdx.z;
+  const int T = min(max(a.seq_lens[b], 0), a.tcap);
+  const int r0 = split * a.chunk;
+  if (r0 >= T) return;  // the merge never reads ranges at or past T
+  const int r1 = min(r0 + a.chunk, T);
+  const int nunits = (r1 - r0 + UNIT - 1) / UNIT;
+
+  __shared__ uint2 s_p[kWaves][NGV][4][16];   // P operand of (group, query, quad)
+  __shared__ float s_o[kWaves][4][D];         // epilogue: per-wave partial output
+  __shared__ float s_ml[kWaves][2][4];        // epilogue: per-wave (m, l) per query
+
+  const int qd = lane >> 2;   // quad: QK block (tokens 4qd..4qd+3); PV block (channels 8qd..8qd+7)
+  const int qn = lane & 3;    // QK output column / PV A-operand row = query head within the KV group
+  const bool qvalid = qn < a.g_heads;
+  const size_t bh = (size_t)b * a.hkv + h;
+  const float sl2 = a.sm_log2;
+
+  // ---- query prologue: bf16 -> fp16 pairs (channels 2j, 2j+1); exact for values in the fp16 range
+  const uint4* qrow = reinterpret_cast<const uint4*>(a.q + ((size_t)b * a.hq + h * a.g_heads + (qvalid ? qn : 0)) * D);
+  uint32_t q16[KCH ? 1 : D / 2];
+  // token-wise K: per group, sigma' * sum(Q) and sigma' * sum(Q * C)  (C = operand bias of each channel)
+  float kq_sum[NGK], kq_bias[NGK];
+#pragma unroll
+  for (int j = 0; j < NGK; ++j) kq_sum[j] = kq_bias[j] = 0.f;
+  if constexpr (!KCH) {
+#pragma unroll
+    for (int i = 0; i < D / 8; ++i) {
+      uint4 v = qrow[i];
+      if (!qvalid) v = make_uint4(0, 0, 0, 0);
+      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        q16[4 * i + j] = pack_f16(__builtin_bit_cast(float, w[j] << 16), __builtin_bit_cast(float, w[j] & 0xFFFF0000u));
+    }
+#pragma unroll
+    for (int j = 0; j < D / 2; ++j) {
+      const float s2 = half_lo(q16[j]) + half_hi(q16[j]);
+      kq_sum[(2 * j) / GRP] += s2;
+      kq_bias[(2 * j) / GRP] += C::bias(j % PAIRS) * s2;
+    }
+#pragma unroll
+    for (int j = 0; j < NGK; ++j) {
+      kq_sum[j] *= sl2;
+      kq_bias[j] *= sl2;
+    }
+  }
+  // channel-wise K (operand-fold on Q): Q~ = Q * s_tau carried exactly as an fp16 pair hi + lo
+  // (the fp32 product of a bf16 and an fp16 value is exact), and sigma' * (sum Q z - sum Q~ C)
+  uint32_t qt_hi[KCH ? D / 2 : 1], qt_lo[KCH ? D / 2 : 1];
+  float kconst = 0.f;
+  int k_tau = -1;
+
+  // ---- running state
+  float m_ref = -INFINITY;                 // reference max of this lane's query (log2 units)
+  float l_part = 0.f;                      // sum of p over this lane's quad tokens
+  float vz_part[NGV], vb_part[NGV];        // token-wise V: sum p*z, sum P~ * C (per value group)
+#pragma unroll
+  for (int j = 0; j < NGV; ++j) vz_part[j] = vb_part[j] = 0.f;
+  float ps_part = 0.f, pb_part = 0.f;      // channel-wise V: sum P16, sum P16 * C over the current group
+  f4 o_acc[2];                             // PV accumulators: [channel 2l+h][query]
+  f4 o_tot[2];                             // channel-wise V: folded output
+#pragma unroll
+  for (int hh = 0; hh < 2; ++hh) {
+    o_acc[hh] = f4{0.f, 0.f, 0.f, 0.f};
+    o_tot[hh] = f4{0.f, 0.f, 0.f, 0.f};
+  }
+
+  // value-operand bias of this lane's quad (pairs 2*(qd % KPW), +1)
+  const float cv0 = C::bias(2 * (qd % KPW)), cv1 = C::bias(2 * (qd % KPW) + 1);
+  const uint32_t cv0h = splat_f16(cv0), cv1h = splat_f16(cv1), oneh = splat_f16(1.f);
+
+  const uint32_t* kbase = a.pk + bh * (size_t)a.tcap * KW;
+  const uint32_t* vbase = a.pv + bh * (size_t)(a.tcap / E) * D;
+  const uint16_t* ksb = a.ks + bh * (size_t)(KCH ? (a.tcap / GRP) * D : a.tcap * NGK);
+  const uint16_t* kzb = a.kz + bh * (size_t)(KCH ? (a.tcap / GRP) * D : a.tcap * NGK);
+  const uint16_t* vsb = a.vs + bh * (size_t)(VCH ? (a.tcap / GRP) * D : a.tcap * NGV);
+  const uint16_t* vzb = a.vz + bh * (size_t)(VCH ? (a.tcap / GRP) * D : a.tcap * NGV);
+
+  // rescale every accumulator of this wave after the reference max of a query moved
+  auto rescale = [&](float alpha) {
+    l_part *= alpha;
+#pragma unroll
+    for (int j = 0; j < NGV; ++j) {
+      vz_part[j] *= alpha;
+      vb_part[j] *= alpha;
+    }
+    ps_part *= alpha;
+    pb_part *= alpha;
+    const float ai[4] = {quad_bcast<0>(alpha), quad_bcast<1>(alpha), quad_bcast<2>(alpha), quad_bcast<3>(alpha)};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        o_acc[hh][i] *= ai[i];  // row i of the PV accumulators is query head i
+        o_tot[hh][i] *= ai[i];
+      }
+    }
+  };
+
+  // channel-wise V: fold the finished group tau into o_tot.  `span` = lanes whose quads form the group.
+  auto fold_value_group = [&](int tau, int src_half) {
+    // sums of the group per query, then broadcast query i's sums to every lane
+    float ps, pb;
+    if (GRP == 32) {  // the group's quads are the lanes of half-wave src_half
+      float a0, a1, b0, b1;
+      halves(sum_same_query<32>(ps_part), a0, a1);
+      halves(sum_same_query<32>(pb_part), b0, b1);
+      ps = src_half ? a1 : a0;
+      pb = src_half ? b1 : b0;
+    } else {
+      ps = sum_same_query<64>(ps_part);
+      pb = sum_same_query<64>(pb_part);
+    }
+    const float psq[4] = {quad_bcast<0>(ps), quad_bcast<1>(ps), quad_bcast<2>(ps), quad_bcast<3>(ps)};
+    const float pbq[4] = {quad_bcast<0>(pb), quad_bcast<1>(pb), quad_bcast<2>(pb), quad_bcast<3>(pb)};
+    const uint32_t s2 = *reinterpret_cast<const uint32_t*>(vsb + (size_t)tau * D + 2 * lane);
+    const uint32_t z2 = *reinterpret_cast<const uint32_t*>(vzb + (size_t)tau * D + 2 * lane);
+    const float sv[2] = {half_lo(s2), half_hi(s2)};
+    const float zv[2] = {half_lo(z2), half_hi(z2)};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh)
+        o_tot[hh][i] += sv[hh] * o_acc[hh][i] + (zv[hh] * psq[i] - sv[hh] * pbq[i]);
+    }
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) o_acc[hh] = f4{0.f, 0.f, 0.f, 0.f};
+  };
+
+  for (int u = wave; u < nunits; u += kWaves) {
+    const int ustart = r0 + u * UNIT;
+#pragma unroll 1
+    for (int tt = 0; tt < TPU; ++tt) {
+      const int t0 = ustart + tt * kTile;
+      if (t0 >= r1) break;
+      const bool tail = t0 + kTile > T;
+
+      // ---------------- loads
+      uint4 kw4[KW / 4];
+      {
+        const uint4* kp = reinterpret_cast<const uint4*>(kbase + (size_t)(t0 + lane) * KW);
+#pragma unroll
+        for (int i = 0; i < KW / 4; ++i) kw4[i] = kp[i];
+      }
+      uint2 vw2[VW];
+#pragma unroll
+      for (int w = 0; w < VW; ++w)
+        vw2[w] = *reinterpret_cast<const uint2*>(vbase + (size_t)(t0 / E + w) * D + 2 * lane);
+      uint2 ks2[NGK], kz2[NGK];
+      if constexpr (!KCH) {
+        load_u2(ks2, ksb + (size_t)(t0 + 4 * qd) * NGK);
+        load_u2(kz2, kzb + (size_t)(t0 + 4 * qd) * NGK);
+      }
+      uint2 vs2[NGV], vz2[NGV];
+      if constexpr (!VCH) {
+        load_u2(vs2, vsb + (size_t)(t0 + 4 * qd) * NGV);
+        load_u2(vz2, vzb + (size_t)(t0 + 4 * qd) * NGV);
+      }
+
+      // ---------------- channel-wise K: operand Q~ for the group of this lane's quad
+      if constexpr (KCH) {
+        const int tau = (t0 + 4 * qd) / GRP;
+        if (tau != k_tau) {  // uniform for g >= 64; per half-wave for g = 32
+          k_tau = tau;
+          const uint4* sp = reinterpret_cast<const uint4*>(ksb + (size_t)tau * D);
+          const uint4* zp = reinterpret_cast<const uint4*>(kzb + (size_t)tau * D);
+          float bq = 0.f, zq = 0.f;
+#pragma unroll
+          for (int i = 0; i < D / 8; ++i) {
+            uint4 q4 = qrow[i];
+            if (!qvalid) q4 = make_uint4(0, 0, 0, 0);
+            const uint4 s4 = sp[i], z4 = zp[i];
+            const uint32_t qw[4] = {q4.x, q4.y, q4.z, q4.w};
+            const uint32_t sw[4] = {s4.x, s4.y, s4.z, s4.w};
+            const uint32_t zw[4] = {z4.x, z4.y, z4.z, z4.w};
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              const int jj = 4 * i + j;
+              const float q0 = __builtin_bit_cast(float, qw[j] << 16);
+              const float q1 = __builtin_bit_cast(float, qw[j] & 0xFFFF0000u);
+              const float pr0 = q0 * half_lo(sw[j]), pr1 = q1 * half_hi(sw[j]);  // exact
+              const _Float16 h0 = (_Float16)pr0, h1 = (_Float16)pr1;
+              const h2 hi = {h0, h1};
+              const h2 lo = {(_Float16)(pr0 - (float)h0), (_Float16)(pr1 - (float)h1)};
+              qt_hi[jj] = as_u32(hi);
+              qt_lo[jj] = as_u32(lo);
+              bq = fmaf(C::bias(jj % PAIRS), pr0 + pr1, bq);
+              zq = fmaf(q0, half_lo(zw[j]), fmaf(q1, half_hi(zw[j]), zq));
+            }
+          }
+          kconst = (zq - bq) * sl2;
+        }
+      }
+
+      // ---------------- QK^T on the matrix cores
+      f4 sacc[NGK];
+#pragma unroll
+      for (int j = 0; j < NGK; ++j) sacc[j] = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int d = 0; d < KW; ++d) {
+        const uint32_t wrd = (d % 4 == 0) ? kw4[d / 4].x : (d % 4 == 1) ? kw4[d / 4].y : (d % 4 == 2) ? kw4[d / 4].z : kw4[d / 4].w;
+        uint32_t p[PAIRS];
+        C::extract(wrd, p);
+#pragma unroll
+        for (int sg = 0; sg < KPW; ++sg) {
+          const int j = d * KPW + sg;  // k-step: channels 4j .. 4j+3
+          const h4 av = cat4(p[2 * sg], p[2 * sg + 1]);
+          if constexpr (KCH) {
+            sacc[0] = __builtin_amdgcn_mfma_f32_4x4x4f16(av, cat4(qt_hi[2 * j], qt_hi[2 * j + 1]), sacc[0], 0, 0, 0);
+            sacc[0] = __builtin_amdgcn_mfma_f32_4x4x4f16(av, cat4(qt_lo[2 * j], qt_lo[2 * j + 1]), sacc[0], 0, 0, 0);
+          } else {
+            const int grp = (4 * j) / GRP;
+            sacc[grp] = __builtin_amdgcn_mfma_f32_4x4x4f16(av, cat4(q16[2 * j], q16[2 * j + 1]), sacc[grp], 0, 0, 0);
+          }
+        }
+      }
+
+      // ---------------- key-side fold (before the softmax) -> scores in log2 units
+      float sc[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        if constexpr (KCH) {
+          sc[r] = fmaf(sacc[0][r], sl2, kconst);
+        } else {
+          float acc = 0.f;
+#pragma unroll
+          for (int j = 0; j < NGK; ++j) {
+            const int idx = r * NGK + j;  // fp16 index inside the quad's (token, group) block
+            const uint2 sv = ks2[idx / 4];
+            const uint2 zv = kz2[idx / 4];
+            const uint32_t s32 = ((idx % 4) < 2) ? sv.x : sv.y;
+            const uint32_t z32 = ((idx % 4) < 2) ? zv.x : zv.y;
+            const float s = (idx % 2 == 0) ? half_lo(s32) : half_hi(s32);
+            const float z = (idx % 2 == 0) ? half_lo(z32) : half_hi(z32);
+            acc = fmaf(s, fmaf(sacc[j][r], sl2, -kq_bias[j]), acc);
+            acc = fmaf(z, kq_sum[j], acc);
+          }
+          sc[r] = acc;
+        }
+        if (tail && (t0 + 4 * qd + r >= T)) sc[r] = -INFINITY;
+      }
+
+      // ---------------- online softmax: exact running max per query head.  The
+      // largest weight seen so far is exactly 1, so the operand-folded weight of
+      // the dominant token (p * s) is its fp16 scale itself, with no rounding.
+      const float m_new = fmaxf(m_ref, wave_max_same_query(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]))));
+      if (__any(m_new > m_ref)) {
+        const float alpha = __builtin_amdgcn_exp2f(m_ref - m_new);  // 0 on the first tile
+        m_ref = m_new;
+        rescale(alpha);
+      }
+      float p[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) p[r] = __builtin_amdgcn_exp2f(sc[r] - m_ref);
+      l_part += (p[0] + p[1]) + (p[2] + p[3]);
+
+      // ---------------- P operands (value-side operand-fold for token-wise V)
+      if constexpr (!VCH) {
+#pragma unroll
+        for (int j = 0; j < NGV; ++j) {
+          float s[4], z[4];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int idx = r * NGV + j;
+            const uint2 sv = vs2[idx / 4];
+            const uint2 zv = vz2[idx / 4];
+            const uint32_t s32 = ((idx % 4) < 2) ? sv.x : sv.y;
+            const uint32_t z32 = ((idx % 4) < 2) ? zv.x : zv.y;
+            s[r] = (idx % 2 == 0) ? half_lo(s32) : half_hi(s32);
+            z[r] = (idx % 2 == 0) ? half_lo(z32) : half_hi(z32);
+            if (tail && (t0 + 4 * qd + r >= T)) s[r] = z[r] = 0.f;  // padding may hold NaN
+          }
+          const uint32_t p01 = pack_f16(p[0] * s[0], p[1] * s[1]);
+          const uint32_t p23 = pack_f16(p[2] * s[2], p[3] * s[3]);
+          s_p[wave][j][qn][qd] = make_uint2(p01, p23);
+          vb_part[j] = dot2(p23, cv1h, dot2(p01, cv0h, vb_part[j]));
+          vz_part[j] = fmaf(p[0], z[0], fmaf(p[1], z[1], fmaf(p[2], z[2], fmaf(p[3], z[3], vz_part[j]))));
+        }
+      } else {
+        const uint32_t p01 = pack_f16(p[0], p[1]);
+        const uint32_t p23 = pack_f16(p[2], p[3]);
+        s_p[wave][0][qn][qd] = make_uint2(p01, p23);
+        ps_part = dot2(p23, oneh, dot2(p01, oneh, ps_part));
+        pb_part = dot2(p23, cv1h, dot2(p01, cv0h, pb_part));
+      }
+      __builtin_amdgcn_wave_barrier();
+      // gathered A operands: P of query qn for all 16 quads (value group of this lane's channels)
+      uint2 pa[16];
+      {
+        const int jv = VCH ? 0 : (8 * qd) / GRP;
+        const uint4* src = reinterpret_cast<const uint4*>(&s_p[wave][jv][qn][0]);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const uint4 v = src[i];
+          pa[2 * i] = make_uint2(v.x, v.y);
+          pa[2 * i + 1] = make_uint2(v.z, v.w);
+        }
+      }
+      __builtin_amdgcn_wave_barrier();
+
+      // ---------------- P V on the matrix cores (+ acc-fold of channel-wise value groups)
+#pragma unroll
+      for (int w = 0; w < VW; ++w) {
+        uint32_t p0[PAIRS], p1[PAIRS];
+        C::extract(vw2[w].x, p0);  // channel 2*lane
+        C::extract(vw2[w].y, p1);  // channel 2*lane + 1
+#pragma unroll
+        for (int sg = 0; sg < KPW; ++sg) {
+          const int bq = w * KPW + sg;  // quad: tokens 4bq .. 4bq+3 of the tile
+          const h4 av = cat4(pa[bq].x, pa[bq].y);
+          o_acc[0] = __builtin_amdgcn_mfma_f32_4x4x4f16(av, cat4(p0[2 * sg], p0[2 * sg + 1]), o_acc[0], 0, 0, 0);
+          o_acc[1] = __builtin_amdgcn_mfma_f32_4x4x4f16(av, cat4(p1[2 * sg], p1[2 * sg + 1]), o_acc[1], 0, 0, 0);
+          if constexpr (VCH && GRP == 32) {
+            if (bq == 7) {  // first 32-token group of the tile is complete
+              if (t0 < T) fold_value_group(t0 / GRP, 0);
+            }
+          }
+        }
+      }
+      if constexpr (VCH) {
+        if (GRP == 32) {
+          if (t0 + 32 < T) fold_value_group(t0 / GRP + 1, 1);
+          else {
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh) o_acc[hh] = f4{0.f, 0.f, 0.f, 0.f};
+          }
+          ps_part = pb_part = 0.f;
+        } else if ((t0 + kTile) % GRP == 0 || t0 + kTile >= r1) {
+          fold_value_group(t0 / GRP, 0);
+          ps_part = pb_part = 0.f;
+        }
+      }
+    }
+  }
+
+  // ---------------- wave epilogue: totals per query, value-side corrections
+  const float l_tot = sum_same_query<64>(l_part);
+  f4 o_fin[2];
+  if constexpr (VCH) {
+    o_fin[0] = o_tot[0];
+    o_fin[1] = o_tot[1];
+  } else {
+    float zc[NGV], bc[NGV];
+#pragma unroll
+    for (int j = 0; j < NGV; ++j) {
+      zc[j] = sum_same_query<64>(vz_part[j]);
+      bc[j] = sum_same_query<64>(vb_part[j]);
+    }
+    const int jv = (8 * qd) / GRP;  // value group of channels 2l, 2l+1
+    float cg = 0.f;  // correction of this lane's value group, per this lane's query head
+#pragma unroll
+    for (int j = 0; j < NGV; ++j) cg = (j == jv) ? zc[j] - bc[j] : cg;
+    const float cq[4] = {quad_bcast<0>(cg), quad_bcast<1>(cg), quad_bcast<2>(cg), quad_bcast<3>(cg)};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float corr = cq[i];
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) o_fin[hh][i] = o_acc[hh][i] + corr;
+    }
+  }
+  if (lane < 4) {
+    s_ml[wave][0][lane] = m_ref;
+    s_ml[wave][1][lane] = l_tot;
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    s_o[wave][i][2 * lane] = o_fin[0][i];
+    s_o[wave][i][2 * lane + 1] = o_fin[1][i];
+  }
+  __syncthreads();
+
+  // ---------------- work-group merge of the 4 waves -> partial of this range
+  for (int idx = threadIdx.x; idx < 4 * D; idx += blockDim.x) {
+    const int i = idx / D, c = idx % D;
+    if (i >= a.g_heads) continue;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, s_ml[w][0][i]);
+    float num = 0.f, den = 0.f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      const float l = s_ml[w][1][i];
+      const float f = (l > 0.f) ? __builtin_amdgcn_exp2f(s_ml[w][0][i] - M) : 0.f;
+      num = fmaf(f, s_o[w][i][c], num);
+      den = fmaf(f, l, den);
+    }
+    const size_t row = (size_t)b * a.hq + h * a.g_heads + i;
+    a.o_part[(row * a.splits + split) * D + c] = num / den;
+    if (c == 0) a.lse_part[row * a.splits + split] = (M + __log2f(den)) * kLn2;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Log-sum-exp merge of the ranges of one (sequence, query head).
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint16_t to_bf16_rne(float f) {
+  uint32_t u = __builtin_bit_cast(uint32_t, f);
+  if ((u & 0x7F800000u) == 0x7F800000u && (u & 0x007FFFFFu)) return 0x7FC0;  // NaN
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+__global__ __launch_bounds__(128) void merge_ranges(const MergeArgs a) {
+  const int row = blockIdx.x;  // b * Hq + head
+  const int b = row / a.hq;
+  const int c = threadIdx.x;
+  const int T = min(max(a.seq_lens[b], 0), a.tcap);
+  const int ns = (T + a.chunk - 1) / a.chunk;
+  if (ns == 0) {
+    a.out[(size_t)row * kHeadDim + c] = 0;
+    if (c == 0 && a.lse) a.lse[row] = -INFINITY;
+    return;
+  }
+  const float* lp = a.lse_part + (size_t)row * a.splits;
+  const float* op = a.o_part + (size_t)row * a.splits * kHeadDim + c;
+  float M = -INFINITY;
+  for (int s = 0; s < ns; ++s) M = fmaxf(M, lp[s]);
+  float num = 0.f, den = 0.f;
+  for (int s = 0; s < ns; ++s) {
+    const float w = __expf(lp[s] - M);
+    num = fmaf(w, op[(size_t)s * kHeadDim], num);
+    den += w;
+  }
+  a.out[(size_t)row * kHeadDim + c] = to_bf16_rne(num / den);
+  if (c == 0 && a.lse) a.lse[row] = M + __logf(den);
+}
+
+template <int BITS, bool KCH, bool VCH, int GRP>
+hipError_t launch_one(int batch, int hkv, const SplitArgs& sa, const MergeArgs& ma, hipStream_t stream) {
+  dim3 grid(sa.splits, hkv, batch);
+  hipLaunchKernelGGL((split_decode<BITS, KCH, VCH, GRP>), grid, dim3(kWaves * 64), 0, stream, sa);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(merge_ranges, dim3(batch * sa.hq), dim3(kHeadDim), 0, stream, ma);
+  return hipGetLastError();
+}
+
+template <int BITS, bool KCH, bool VCH>
+hipError_t launch_g(int group, int batch, int hkv, const SplitArgs& sa, const MergeArgs& ma, hipStream_t stream) {
+  switch (group) {
+    case 32: return launch_one<BITS, KCH, VCH, 32>(batch, hkv, sa, ma, stream);
+    case 64: return launch_one<BITS, KCH, VCH, 64>(batch, hkv, sa, ma, stream);
+    case 128: return launch_one<BITS, KCH, VCH, 128>(batch, hkv, sa, ma, stream);
+  }
+  return hipErrorInvalidValue;
+}
+
+template <int BITS>
+hipError_t launch_bits(bool kch, bool vch, int group, int batch, int hkv, const SplitArgs& sa, const MergeArgs& ma,
+                       hipStream_t stream) {
+  if (kch) {
+    return vch ? launch_g<BITS, true, true>(group, batch, hkv, sa, ma, stream)
+               : launch_g<BITS, true, false>(group, batch, hkv, sa, ma, stream);
+  }
+  return vch ? launch_g<BITS, false, true>(group, batch, hkv, sa, ma, stream)
+             : launch_g<BITS, false, false>(group, batch, hkv, sa, ma, stream);
+}
+
+}  // namespace
+
+hipError_t launch_decode(int bits, bool k_channel, bool v_channel, int group, int batch, int hkv,
+                         const SplitArgs& sa, const MergeArgs& ma, hipStream_t stream) {
+  if (bits == 2) return launch_bits<2>(k_channel, v_channel, group, batch, hkv, sa, ma, stream);
+  return launch_bits<4>(k_channel, v_channel, group, batch, hkv, sa, ma, stream);
+}
+
+}  // namespace foscar

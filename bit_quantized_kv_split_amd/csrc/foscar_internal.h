@@ -1,0 +1,51 @@
+// Internal declarations shared by the host interface and the kernels of
+// libfoscar (decode attention over a 2-/4-bit quantised KV cache, gfx950).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace foscar {
+
+constexpr int kHeadDim = 128;   // D
+constexpr int kTile = 64;       // tokens per wave tile (16 quads of 4)
+constexpr int kWaves = 4;       // waves per work-group
+constexpr int kMaxG = 4;        // query heads per KV head served by one wave
+
+// Arguments of the split kernel (one work-group per (range, KV head, sequence)).
+struct SplitArgs {
+  const uint16_t* q;         // bf16 [B][Hq][D]
+  const uint32_t* pk;        // [B][Hkv][Tcap][D*bits/32]
+  const uint32_t* pv;        // [B][Hkv][Tcap*bits/32][D]
+  const uint16_t* ks;        // fp16 key scales   (token-wise [B][Hkv][Tcap][D/g], channel-wise [B][Hkv][Tcap/g][D])
+  const uint16_t* kz;        // fp16 key offsets
+  const uint16_t* vs;        // fp16 value scales
+  const uint16_t* vz;        // fp16 value offsets
+  const int32_t* seq_lens;   // [B]
+  float* o_part;             // fp32 [B][Hq][S][D]   normalised partial output of each range
+  float* lse_part;           // fp32 [B][Hq][S]      natural-log lse of each range
+  int32_t hq, hkv, g_heads;  // Hq, Hkv, G = Hq / Hkv
+  int32_t tcap;              // Tcap
+  int32_t splits;            // S
+  int32_t chunk;             // tokens per range (multiple of the wave unit)
+  float sm_log2;             // sm_scale * log2(e)
+};
+
+// Arguments of the merge kernel (one work-group per (sequence, query head)).
+struct MergeArgs {
+  const float* o_part;
+  const float* lse_part;
+  const int32_t* seq_lens;
+  uint16_t* out;             // bf16 [B][Hq][D]
+  float* lse;                // fp32 [B][Hq] or null
+  int32_t hq, tcap, splits, chunk;
+};
+
+hipError_t launch_decode(int bits, bool k_channel, bool v_channel, int group, int batch, int hkv,
+                         const SplitArgs& sa, const MergeArgs& ma, hipStream_t stream);
+
+hipError_t launch_pack(int bits, int side, int batch, int hkv, int tcap, const uint8_t* codes, uint32_t* packed,
+                       hipStream_t stream);
+hipError_t launch_unpack(int bits, int side, int batch, int hkv, int tcap, const uint32_t* packed, uint8_t* codes,
+                         hipStream_t stream);
+
+}  // namespace foscar

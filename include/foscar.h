@@ -1,0 +1,164 @@
+/*
+ * foscar.h -- decode attention over a 2-bit or 4-bit quantised KV cache on
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The method is the one of "FOSCAR: Accelerating Decode Attention over 2- and
+ * 4-Bit KV Caches through Affine Folding" (arXiv 2611.09722; abstract) and of
+ * its explainer "FOSCAR speeds up 2-bit KV decode -- Affine folding of KV
+ * dequantization" (learnaivisually):
+ *   - the cache holds codes q with one scale s and one offset z per group,
+ *     value = s*q + z (explainer, encoding paragraph);
+ *   - groups run token-wise (g channels of one token) or channel-wise (g
+ *     tokens of one channel) (explainer, fold-placement table);
+ *   - no value is dequantised one by one: token-wise K and channel-wise V scale
+ *     each group's partial sum once (acc-fold), channel-wise K and token-wise V
+ *     pre-scale the other operand (operand-fold); each offset becomes one
+ *     correction z * (sum of the other operand) (explainer, fold rule and
+ *     table); key-side corrections land before the softmax, value-side ones
+ *     before the final division (explainer, fold rule).
+ * The result equals softmax attention over the dequantised cache, up to
+ * floating-point rounding (abstract: exact in exact arithmetic).
+ *
+ * One decode step = one new query token per sequence, grouped-query
+ * attention: query head i reads KV head i / (Hq / Hkv).
+ *
+ * Conventions for every entry point:
+ *   - all tensor pointers are DEVICE memory owned by the caller; inputs are
+ *     only read; the library never frees or keeps them;
+ *   - `stream` is a hipStream_t (NULL = the null stream of the current
+ *     device); calls are asynchronous on it: no host synchronisation and no
+ *     host read of device data; buffers must stay alive until the stream has
+ *     passed the call;
+ *   - arguments are validated on the host BEFORE any HIP call; an invalid
+ *     call returns an error code and launches nothing;
+ *   - return value: FOSCAR_OK (0) or a negative FOSCAR_E* code; no exception
+ *     or abort crosses this interface.
+ */
+#ifndef FOSCAR_H
+#define FOSCAR_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define FOSCAR_VERSION 100 /* 1.0.0 */
+
+/* Return codes. */
+#define FOSCAR_OK 0
+#define FOSCAR_EINVAL (-1)       /* null pointer, negative size, bad layout/side/bits value, Hq % Hkv != 0 */
+#define FOSCAR_EUNSUPPORTED (-2) /* head_dim != 128, group not in {32,64,128}, Hq/Hkv > 4,
+                                    max_seq_len not a multiple of 64 (and of group for a
+                                    channel-wise side) */
+#define FOSCAR_EHIP (-3)         /* a HIP call failed; foscar_last_hip_error() has its code */
+#define FOSCAR_ENOMEM (-4)       /* workspace allocation failed */
+
+/* Layout bits (OR one K value with one V value).
+ * Token-wise group: g consecutive channels of one token share (s, z).
+ * Channel-wise group: g consecutive tokens (from token 0) of one channel share (s, z). */
+#define FOSCAR_K_TOKEN 0
+#define FOSCAR_K_CHANNEL 1
+#define FOSCAR_V_TOKEN 0
+#define FOSCAR_V_CHANNEL 2
+
+/* Sides for pack / unpack / sizing. */
+#define FOSCAR_SIDE_K 0
+#define FOSCAR_SIDE_V 1
+
+typedef struct foscar_dims {
+  int32_t batch;        /* B >= 0 sequences (B = 0: nothing to do) */
+  int32_t num_q_heads;  /* Hq >= 1 */
+  int32_t num_kv_heads; /* Hkv >= 1, Hq % Hkv == 0, Hq / Hkv <= 4 */
+  int32_t head_dim;     /* D; must be 128 */
+  int32_t max_seq_len;  /* Tcap: tokens allocated per sequence; multiple of 64, and of
+                           `group` when a side is channel-wise */
+  float sm_scale;       /* softmax scale applied to q.k; <= 0 selects 1/sqrt(head_dim) */
+} foscar_dims;
+
+/*
+ * Decode step, 2-bit (foscar_decode_int2) or 4-bit (foscar_decode_int4) codes.
+ *
+ * q         bf16  [B][Hq][D]
+ * packed_k  u32   [B][Hkv][Tcap][D*bits/32]   keys packed along channels
+ * packed_v  u32   [B][Hkv][Tcap*bits/32][D]   values packed along tokens
+ *           E = 32/bits codes per word; word holds E consecutive elements of the
+ *           packed axis; element e of a word sits at bits
+ *           [bits*(e/2) + 16*(e%2), +bits): even elements in the low half-word,
+ *           odd elements in the high half-word (little-endian, lowest bits first).
+ *           Codes are unsigned, 0 .. 2^bits - 1.
+ * k_scale, k_zero  fp16, token-wise [B][Hkv][Tcap][D/g], channel-wise [B][Hkv][Tcap/g][D]
+ * v_scale, v_zero  fp16, same two shapes for the value side
+ * seq_lens  int32 [B]; T_b is clamped on the device to [0, Tcap].  Tokens at or
+ *           past T_b (codes, scales, offsets) may hold anything, NaN included,
+ *           and do not affect the result.  A channel-wise group that reaches
+ *           past T_b covers only its tokens below T_b.
+ * layout    FOSCAR_K_* | FOSCAR_V_*
+ * group     g in {32, 64, 128} (channels for a token-wise side, tokens for a
+ *           channel-wise side; the same g for both sides)
+ * out       bf16  [B][Hq][D]  softmax(sm_scale * q K^T) V over the dequantised
+ *           cache, rounded to nearest even; 0 for a row with T_b = 0
+ * lse       fp32  [B][Hq]     ln sum_t exp(sm_scale * q.k_t); -inf when T_b = 0
+ *           (may be NULL)
+ * stream    hipStream_t
+ *
+ * Precision: fp16 matrix-core products with fp32 accumulation; query values
+ * must lie in the fp16 range; value scales of a token-wise value side must
+ * satisfy |s| < 256.  The first call on a (device, stream) pair may allocate the
+ * split workspace (see foscar_workspace_reserve); later calls of the same or
+ * smaller size do not allocate.  Calls on different streams do not share
+ * workspace.
+ */
+int foscar_decode_int2(const foscar_dims* dims, const void* q, const void* packed_k, const void* packed_v,
+                       const void* k_scale, const void* k_zero, const void* v_scale, const void* v_zero,
+                       const int32_t* seq_lens, int layout, int group, void* out, float* lse, void* stream);
+int foscar_decode_int4(const foscar_dims* dims, const void* q, const void* packed_k, const void* packed_v,
+                       const void* k_scale, const void* k_zero, const void* v_scale, const void* v_zero,
+                       const int32_t* seq_lens, int layout, int group, void* out, float* lse, void* stream);
+
+/*
+ * Pack logical codes into the layout above (bit-exact with any packer written
+ * from the same specification), or unpack it.
+ * codes   u8 [B][Hkv][Tcap][D], values 0 .. 2^bits - 1 (higher bits are dropped)
+ * packed  u32, FOSCAR_SIDE_K: [B][Hkv][Tcap][D*bits/32]; FOSCAR_SIDE_V: [B][Hkv][Tcap*bits/32][D]
+ * bits    2 or 4;  side  FOSCAR_SIDE_K or FOSCAR_SIDE_V
+ * Only batch, num_kv_heads, head_dim and max_seq_len of dims are used
+ * (head_dim must be 128, max_seq_len a multiple of 32/bits for FOSCAR_SIDE_V).
+ */
+int foscar_pack(int bits, int side, const foscar_dims* dims, const uint8_t* codes, void* packed, void* stream);
+int foscar_unpack(int bits, int side, const foscar_dims* dims, const void* packed, uint8_t* codes, void* stream);
+
+/* Bytes of one packed side (pure host arithmetic; 0 on invalid arguments). */
+size_t foscar_packed_bytes(int bits, int side, const foscar_dims* dims);
+
+/* Number of fp16 scales (equally offsets) of one side:
+ * side_layout is FOSCAR_K_TOKEN/FOSCAR_K_CHANNEL for side K (pass side = FOSCAR_SIDE_K)
+ * or FOSCAR_V_TOKEN/FOSCAR_V_CHANNEL for side V; 0 on invalid arguments. */
+size_t foscar_scale_count(int side, int side_layout, int group, const foscar_dims* dims);
+
+/*
+ * Allocate (grow-only) the split workspace that decode calls with these dims,
+ * layout and group use on `stream` of the current device, so that no later
+ * call of that size allocates.  Synchronous.  FOSCAR_ENOMEM on failure.
+ */
+int foscar_workspace_reserve(const foscar_dims* dims, int layout, int group, void* stream);
+
+/* Free every workspace of the library (all devices and streams).  The caller
+ * must make sure no decode call is still running.  Synchronous. */
+void foscar_release(void);
+
+/* Split plan the decode entry points use for these arguments: *splits = number
+ * of key/value ranges per (sequence, KV head), *chunk = tokens per range.
+ * FOSCAR_SPLITS=<n> in the environment forces n ranges (tuning and tests). */
+int foscar_split_plan(const foscar_dims* dims, int layout, int group, int32_t* splits, int32_t* chunk);
+
+const char* foscar_strerror(int code);
+int foscar_version(void);
+/* hipError_t of the last failed HIP call on this host thread (0 if none). */
+int foscar_last_hip_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* FOSCAR_H */

@@ -1,0 +1,107 @@
+"""The C interface on the host: the library loads, exports every function that
+include/foscar.h declares, and rejects invalid arguments with error codes
+before touching the GPU (these calls run without a GPU)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER_DIR = os.path.join(ROOT, "include")
+
+
+def _declared_functions():
+    names = []
+    for fn in sorted(os.listdir(HEADER_DIR)):
+        if not fn.endswith(".h"):
+            continue
+        text = open(os.path.join(HEADER_DIR, fn)).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        names += re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\*?\s*(foscar_[a-z0-9_]+)\s*\(", text, flags=re.M)
+    return sorted(set(names))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from bit_quantized_kv_split_amd import _lib
+    if not os.path.exists(_lib.LIB_PATH):
+        pytest.skip("libfoscar.so not built")
+    return _lib.load()
+
+
+def test_header_declares_the_expected_entry_points():
+    names = _declared_functions()
+    assert "foscar_decode_int2" in names and "foscar_decode_int4" in names
+    from bit_quantized_kv_split_amd import _lib
+    assert sorted(_lib.EXPORTS) == names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for name in _declared_functions():
+        assert hasattr(lib, name), name
+
+
+def _dims(**kw):
+    import bit_quantized_kv_split_amd as fos
+    d = dict(batch=1, num_q_heads=4, num_kv_heads=1, head_dim=128, max_seq_len=1024, sm_scale=0.0)
+    d.update(kw)
+    return fos.make_dims(**d)
+
+
+def _decode(lib, dims, layout=0, group=128, ptr=1):
+    p = ctypes.c_void_p(ptr) if ptr else None
+    return lib.foscar_decode_int2(ctypes.byref(dims) if dims is not None else None, p, p, p, p, p, p, p, p,
+                                  layout, group, p, p, None)
+
+
+@pytest.mark.parametrize("kw,layout,group,code", [
+    (dict(head_dim=64), 0, 128, -2),
+    (dict(num_q_heads=6, num_kv_heads=4), 0, 128, -1),
+    (dict(num_q_heads=16, num_kv_heads=2), 0, 128, -2),     # 8 query heads per KV head
+    (dict(max_seq_len=1000), 0, 128, -2),                    # not a multiple of 64
+    (dict(max_seq_len=192), 2, 128, -2),                     # channel-wise group of 128 does not divide 192
+    (dict(batch=-1), 0, 128, -1),
+    (dict(), 4, 128, -1),                                    # bad layout bits
+    (dict(), 0, 48, -2),                                     # bad group
+])
+def test_invalid_arguments_return_codes_before_any_gpu_call(lib, kw, layout, group, code):
+    assert _decode(lib, _dims(**kw), layout, group) == code
+
+
+def test_null_pointers_and_dims(lib):
+    assert _decode(lib, None) == -1
+    assert _decode(lib, _dims(), ptr=0) == -1
+    assert _decode(lib, _dims(batch=0), ptr=0) == 0   # nothing to do
+
+
+def test_sizes_and_strings(lib):
+    import bit_quantized_kv_split_amd as fos
+    d = _dims(batch=2, num_kv_heads=3, num_q_heads=6, max_seq_len=256)
+    assert fos.foscar_packed_bytes(2, fos.FOSCAR_SIDE_K, d) == 2 * 3 * 256 * 128 * 2 // 8
+    assert fos.foscar_packed_bytes(4, fos.FOSCAR_SIDE_V, d) == 2 * 3 * 256 * 128 * 4 // 8
+    assert fos.foscar_packed_bytes(3, fos.FOSCAR_SIDE_V, d) == 0
+    assert fos.foscar_scale_count(fos.FOSCAR_SIDE_K, fos.FOSCAR_K_TOKEN, 32, d) == 2 * 3 * 256 * 4
+    assert fos.foscar_scale_count(fos.FOSCAR_SIDE_V, fos.FOSCAR_V_CHANNEL, 64, d) == 2 * 3 * 4 * 128
+    assert fos.foscar_scale_count(fos.FOSCAR_SIDE_V, fos.FOSCAR_K_CHANNEL, 64, d) == 0
+    assert fos.foscar_version() == 100
+    for c, s in [(0, "ok"), (-1, "invalid argument"), (-2, "unsupported"), (-3, "HIP"), (-4, "memory")]:
+        assert s in fos.foscar_strerror(c)
+    with pytest.raises(ValueError):
+        fos.foscar_split_plan(_dims(head_dim=96), 0, 128)
+
+
+def test_split_plan_covers_the_cache(lib, monkeypatch):
+    import bit_quantized_kv_split_amd as fos
+    monkeypatch.delenv("FOSCAR_SPLITS", raising=False)
+    for kw, layout, g in [(dict(batch=4, num_q_heads=32, num_kv_heads=8, max_seq_len=131072), 0, 128),
+                          (dict(batch=64, num_q_heads=32, num_kv_heads=8, max_seq_len=65536), 2, 32),
+                          (dict(batch=8, num_q_heads=32, num_kv_heads=8, max_seq_len=32768), 3, 128),
+                          (dict(), 0, 128)]:
+        d = _dims(**kw)
+        s, c = fos.foscar_split_plan(d, layout, g)
+        unit = g if (layout and g > 64) else 64
+        assert c % unit == 0 and s * c >= d.max_seq_len and (s - 1) * c < d.max_seq_len
+    monkeypatch.setenv("FOSCAR_SPLITS", "3")
+    s, c = fos.foscar_split_plan(_dims(), 0, 128)
+    assert s == 3 and c == 384

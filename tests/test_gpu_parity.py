@@ -1,0 +1,122 @@
+"""GPU parity: the HIP decode path (through the C interface) against the fp64
+oracle, element by element, on seeded synthetic workloads.
+
+Bar (written in gpu_util): |out - O| <= 2e-3 + 2^-8 |O| per element (bf16
+output), |lse - lse_ref| <= 2e-3.
+"""
+import os
+
+import numpy as np
+import pytest
+
+import synth
+from gpu_util import check, oracle_all, oracle_rows, run, stage_spec
+
+pytestmark = pytest.mark.gpu
+
+
+def _spec(name, **kw):
+    return synth.SPECS[name].replace(**kw)
+
+
+def test_c1_tiny_full_size():
+    spec = synth.SPECS["c1_tiny_int2"]
+    dev, q, lens = stage_spec(spec)
+    out, lse = run(spec, dev)
+    ro, rl, vsc = oracle_all(spec, q, lens)
+    check(out, lse, ro, rl, "c1", vsc)
+
+
+MATRIX = [(bits, kl, vl, g) for bits in (2, 4) for kl in ("token", "channel") for vl in ("token", "channel")
+          for g in (32, 64, 128)]
+
+
+@pytest.mark.parametrize("bits,kl,vl,g", MATRIX)
+def test_layout_matrix(bits, kl, vl, g):
+    """Every kernel instance: 3 ragged sequences spanning several tiles with tails."""
+    std = (0.1, 10.0) if "channel" in (kl, vl) else None
+    spec = synth.Spec(f"matrix_{bits}_{kl}_{vl}_{g}", 11, bits, kl, vl, g, 3, 8, 2, 128, 768,
+                      lens=(768, 517, 130), channel_std_logu=std)
+    dev, q, lens = stage_spec(spec)
+    out, lse = run(spec, dev)
+    ro, rl, vsc = oracle_all(spec, q, lens)
+    check(out, lse, ro, rl, spec.name, vsc)
+
+
+SCALED = [
+    _spec("c2_paper_int2", batch=2, num_q_heads=8, num_kv_heads=2, max_seq_len=2048),
+    _spec("c2_paper_int4", batch=2, num_q_heads=8, num_kv_heads=2, max_seq_len=2048),
+    _spec("c3_long_int2", batch=1, num_q_heads=4, num_kv_heads=1, max_seq_len=16384),
+    _spec("c4_channel_int2", batch=2, num_q_heads=8, num_kv_heads=2, max_seq_len=2048),
+    _spec("c4_channel_int4", batch=2, num_q_heads=8, num_kv_heads=2, max_seq_len=2048),
+] + [_spec(f"c5_ragged_int{b}_g{g}", batch=6, num_q_heads=8, num_kv_heads=2, max_seq_len=4096, ragged_lo=64)
+     for b in (2, 4) for g in (32, 64, 128)]
+
+
+@pytest.mark.parametrize("spec", SCALED, ids=[s.name for s in SCALED])
+def test_scaled_workloads(spec):
+    """The five workloads' value recipes at sizes the oracle finishes in seconds."""
+    dev, q, lens = stage_spec(spec)
+    out, lse = run(spec, dev)
+    ro, rl, vsc = oracle_all(spec, q, lens)
+    check(out, lse, ro, rl, spec.name, vsc)
+
+
+EDGE_LENS = (0, 1, 2, 63, 64, 65, 127, 128, 129, 255, 256)
+
+
+@pytest.mark.parametrize("bits", [2, 4])
+@pytest.mark.parametrize("kl,vl,g", [("token", "token", 128), ("channel", "channel", 128), ("token", "channel", 32),
+                                     ("channel", "token", 64)])
+def test_edge_lengths_and_poisoned_padding(bits, kl, vl, g):
+    """Empty, single-token, tile-boundary and group-boundary lengths; padding
+    past each length holds random codes and NaN scales/offsets."""
+    spec = synth.Spec(f"edge_{bits}_{kl}_{vl}_{g}", 12, bits, kl, vl, g, len(EDGE_LENS), 4, 1, 128, 256,
+                      lens=EDGE_LENS)
+    dev, q, lens = stage_spec(spec, poison=True)
+    out, lse = run(spec, dev)
+    ro, rl, vsc = oracle_all(spec, q, lens, poison=True)
+    check(out, lse, ro, rl, spec.name, vsc)
+    assert np.all(out[0] == 0) and np.all(np.isneginf(lse[0]))
+
+
+@pytest.mark.parametrize("G", [1, 2, 3, 4])
+def test_gqa_ratios(G):
+    spec = synth.Spec(f"gqa_{G}", 13, 2, "token", "channel", 64, 2, 3 * G, 3, 128, 512, lens=(512, 300))
+    dev, q, lens = stage_spec(spec)
+    out, lse = run(spec, dev)
+    ro, rl, vsc = oracle_all(spec, q, lens)
+    check(out, lse, ro, rl, spec.name, vsc)
+
+
+@pytest.mark.parametrize("splits", ["1", "2", "7", "auto"])
+def test_split_count_invariance(splits, monkeypatch):
+    spec = _spec("c5_ragged_int2_g64", batch=4, num_q_heads=8, num_kv_heads=2, max_seq_len=2048, ragged_lo=100)
+    if splits != "auto":
+        monkeypatch.setenv("FOSCAR_SPLITS", splits)
+    else:
+        monkeypatch.delenv("FOSCAR_SPLITS", raising=False)
+    dev, q, lens = stage_spec(spec)
+    out, lse = run(spec, dev)
+    ro, rl, vsc = oracle_all(spec, q, lens)
+    check(out, lse, ro, rl, f"splits={splits}", vsc)
+
+
+FULL = ["c2_paper_int2", "c2_paper_int4", "c3_long_int2", "c4_channel_int2", "c4_channel_int4",
+        "c5_ragged_int2_g32", "c5_ragged_int4_g128"]
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_full_size_sampled_rows(name):
+    """Full workload size, default launch configuration; sampled rows against
+    the oracle computed one (sequence, query head) at a time."""
+    spec = synth.SPECS[name]
+    dev, q, lens = stage_spec(spec)
+    out, lse = run(spec, dev)
+    rng = np.random.default_rng(7)
+    rows = [(0, 0), (spec.batch - 1, spec.num_q_heads - 1)]
+    rows += [(int(rng.integers(spec.batch)), int(rng.integers(spec.num_q_heads))) for _ in range(4)]
+    ro, rl, vsc = oracle_rows(spec, rows, q, lens, with_scale=True)
+    for n, (b, i) in enumerate(rows):
+        check(out[b, i][None], lse[b, i][None], ro[n][None], rl[n][None], f"{name} row {(b, i)}", vsc[n][None])
+    assert np.all(np.isfinite(out))
