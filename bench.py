@@ -1,0 +1,200 @@
+"""Benchmark: one decode step of the long-context INT2 workload on one MI355X.
+
+Workload (default): batch 4, 32 query heads / 8 KV heads (GQA 4), head_dim
+128, 131072 tokens per sequence, 2-bit codes, token-wise K and V groups of
+128, K/V ~ N(0,1) min-max quantised, bf16 query -- one layer's decode step.
+
+A step is one call of foscar_decode_int2 (one kernel launch: split-KV over
+the whole chip plus the log-sum-exp merge).  Inputs are staged in HBM before
+the timed region; steps rotate over --copies independent copies of the cache
+so that every step streams its cache from HBM rather than from the 256 MB
+Infinity Cache.
+
+Prints one JSON line: metric/value (achieved HBM GB/s of algorithmic bytes per
+step), ms_per_step, a roofline object for the decode kernel (HIP events on
+the launch stream; rocprofv3 summaries of the same command are committed
+under profiles/), and the CPU oracle timed on a bounded sample.
+"""
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "INT2/INT4 decode-attn achieved HBM GB/s (% of 8 TB/s) and µs/step"
+PEAK_HBM_GBS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="c3_long_int2")
+    ap.add_argument("--copies", type=int, default=2, help="independent cache copies rotated over the steps")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the oracle sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    return ap.parse_args()
+
+
+def kernel_sha():
+    h = hashlib.sha256()
+    with open(os.path.join(ROOT, "bit_quantized_kv_split_amd", "csrc", "decode.hip"), "rb") as f:
+        h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_per_launch(workload):
+    """HBM bytes per launch from the committed rocprofv3 counter runs, if they
+    were taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", f"decode_{workload}_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    if t.get("kernel_source_sha") != kernel_sha():
+        return None
+    return t.get("bytes_per_launch")
+
+
+def cpu_baseline(spec, q, lens, target_s):
+    """The fp64 oracle (single-threaded numpy) on the first (sequence, KV head)
+    slices of the same workload until about target_s seconds of CPU work."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+
+    import oracle
+    import synth
+
+    G = spec.num_q_heads // spec.num_kv_heads
+    done_bytes, spent, slices = 0, 0.0, 0
+    D = spec.head_dim
+    for b in range(spec.batch):
+        for h in range(spec.num_kv_heads):
+            head = synth.make_head(spec, b, h, seq_len=int(lens[b]))  # not timed
+            w = {k: v[None, None] for k, v in head.items()}
+            w["q"] = q[b:b + 1, h * G:(h + 1) * G]
+            w["seq_lens"] = np.array([lens[b]], np.int32)
+            with threadpool_limits(1):
+                t0 = time.perf_counter()
+                oracle.decode_rows(w, [(0, i) for i in range(G)], k_layout=spec.k_layout, v_layout=spec.v_layout,
+                                   group=spec.group, sm_scale=spec.sm_scale)
+                spent += time.perf_counter() - t0
+            t = int(lens[b])
+            sz = 0
+            for layout in (spec.k_layout, spec.v_layout):
+                sz += 2 * 2 * (t * (D // spec.group) if layout == "token" else -(-t // spec.group) * D)
+            done_bytes += 2 * t * D * spec.bits // 8 + sz + 2 * 2 * G * D + 4 * G
+            slices += 1
+            if spent >= target_s:
+                break
+        if spent >= target_s:
+            break
+    return {"value": round(done_bytes / spent / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"{slices} of {spec.batch * spec.num_kv_heads} (sequence, KV head) slices, "
+                      f"{slices * G} query heads, fp64 numpy, BLAS limited to 1 thread; {spent:.1f} s",
+            "seconds_per_step_extrapolated": round(spent / slices * spec.batch * spec.num_kv_heads, 2)}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for --gpus {args.gpus}).",
+              file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    import bit_quantized_kv_split_amd as fos
+    import bit_quantized_kv_split_amd.staging as staging
+    import synth
+
+    spec = synth.SPECS[args.workload]
+    dev_name = "cuda:0"
+    torch.cuda.set_device(0)
+    q = synth.make_query(spec)
+    lens = spec.seq_lens()
+    t_stage = time.perf_counter()
+    base = staging.stage((spec.batch, spec.num_q_heads, spec.num_kv_heads, spec.max_seq_len, spec.head_dim),
+                         spec.bits, q, lens, lambda b: synth.make_sequence(spec, b), synth.full_scale_shapes(spec),
+                         device=dev_name)
+    copies = [base] + [{k: v.clone() for k, v in base.items()} for _ in range(max(1, args.copies) - 1)]
+    torch.cuda.synchronize()
+    stage_s = time.perf_counter() - t_stage
+    layout = fos.layout_bits(spec.k_layout, spec.v_layout)
+    dims = fos.make_dims(spec.batch, spec.num_q_heads, spec.num_kv_heads, spec.head_dim, spec.max_seq_len)
+    fos.foscar_workspace_reserve(dims, layout, spec.group)
+    splits, chunk = fos.foscar_split_plan(dims, layout, spec.group)
+    outs = [(torch.empty((spec.batch, spec.num_q_heads, spec.head_dim), dtype=torch.bfloat16, device=dev_name),
+             torch.empty((spec.batch, spec.num_q_heads), dtype=torch.float32, device=dev_name)) for _ in copies]
+    fn = fos.foscar_decode_int2 if spec.bits == 2 else fos.foscar_decode_int4
+
+    def step(k):
+        c = copies[k % len(copies)]
+        o, l = outs[k % len(copies)]
+        fn(c["q"], c["packed_k"], c["packed_v"], c["k_scale"], c["k_zero"], c["v_scale"], c["v_zero"],
+           c["seq_lens"], layout, spec.group, out=o, lse=l)
+
+    for k in range(args.warmup):
+        step(k)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        ev[k][0].record(stream)
+        step(k)
+        ev[k][1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kernel_ms = [a.elapsed_time(b) for a, b in ev]
+    ms_per_step = wall * 1e3 / args.steps
+    alg = synth.algorithmic_bytes(spec, lens)
+    value = alg / (ms_per_step * 1e-3) / 1e9
+    k_avg = sum(kernel_ms) / len(kernel_ms)
+    achieved = alg / (k_avg * 1e-3) / 1e9
+    assert torch.isfinite(outs[0][0].float()).all(), "non-finite output"
+
+    line = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "us_per_step": round(ms_per_step * 1e3, 2),
+        "pct_of_peak_hbm": round(100 * value / PEAK_HBM_GBS, 2),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "arith": "2-bit codes -> fp16 matrix-core operands (magic-exponent AND-OR), fp32 accumulation, bf16 out",
+        "data": "synthetic",
+        "config": {"workload": f"{spec.name}: batch {spec.batch}, {spec.num_q_heads} query heads / "
+                               f"{spec.num_kv_heads} KV heads, head_dim {spec.head_dim}, {spec.max_seq_len} tokens, "
+                               f"INT{spec.bits}, K {spec.k_layout}-wise / V {spec.v_layout}-wise, group {spec.group}",
+                   "global_batch": spec.batch, "seq_len": spec.max_seq_len, "bits": spec.bits,
+                   "k_layout": spec.k_layout, "v_layout": spec.v_layout, "group": spec.group,
+                   "splits": splits, "chunk": chunk, "cache_copies": len(copies),
+                   "algorithmic_bytes_per_step": alg},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic_per_launch(spec.name),
+                     "kernel": "split_decode (one launch per step)", "kernel_us_avg": round(k_avg * 1e3, 2),
+                     "kernel_us_min": round(min(kernel_ms) * 1e3, 2)},
+        "staging_s": round(stage_s, 1),
+        "kernel_source_sha": kernel_sha(),
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(spec, q, lens, args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

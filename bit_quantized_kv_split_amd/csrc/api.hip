@@ -69,7 +69,7 @@ int compute_units(int device) {
   return cus;
 }
 
-// Split plan: enough work-groups to fill the chip, ranges of at most 4096
+// Split plan: enough work-groups to fill the chip once, ranges of at most 8192
 // tokens so ragged batches balance, every range a multiple of the wave unit.
 void plan(const foscar_dims* d, int layout, int group, int cus, int32_t* splits, int32_t* chunk) {
   const int unit = unit_tokens(layout, group);
@@ -86,9 +86,9 @@ void plan(const foscar_dims* d, int layout, int group, int cus, int32_t* splits,
   if (env && atoi(env) > 0) {
     s = atoi(env);
   } else {
-    const long long target = 4LL * cus;  // work-groups in flight wanted
+    const long long target = 2LL * cus;  // one round of work-groups (two resident per CU)
     if (bh > 0) s = (target + bh - 1) / bh;
-    const long long by_len = (tcap + 4095) / 4096;
+    const long long by_len = (tcap + 8191) / 8192;  // ranges of at most 8192 tokens
     if (s < by_len) s = by_len;
   }
   if (s > units) s = units;
@@ -98,9 +98,13 @@ void plan(const foscar_dims* d, int layout, int group, int cus, int32_t* splits,
   *splits = (int32_t)((units + per - 1) / per);
 }
 
+// Workspace: [counters int32 B*Hkv (padded to 256 B)][o_part fp32 B*Hq*S*D][lse_part fp32 B*Hq*S]
+size_t counter_bytes(const foscar_dims* d) {
+  return (((size_t)d->batch * d->num_kv_heads * sizeof(int32_t)) + 255) / 256 * 256;
+}
 size_t workspace_bytes(const foscar_dims* d, int32_t splits) {
   const size_t rows = (size_t)d->batch * d->num_q_heads * splits;
-  return rows * (foscar::kHeadDim + 1) * sizeof(float);
+  return counter_bytes(d) + rows * (foscar::kHeadDim + 1) * sizeof(float);
 }
 
 // Grow-only workspace of (current device, stream).  Growing frees the old
@@ -121,6 +125,14 @@ int get_workspace(size_t bytes, hipStream_t stream, void** out) {
     }
     e = hipMalloc(&ws.ptr, bytes);
     if (e != hipSuccess) {
+      ws.ptr = nullptr;
+      return hip_fail(e);
+    }
+    // range counters must start at zero; every call leaves them at zero
+    e = hipMemset(ws.ptr, 0, bytes);
+    if (e == hipSuccess) e = hipDeviceSynchronize();
+    if (e != hipSuccess) {
+      (void)hipFree(ws.ptr);
       ws.ptr = nullptr;
       return hip_fail(e);
     }
@@ -157,8 +169,11 @@ int decode_common(int bits, const foscar_dims* d, const void* q, const void* pk,
   sa.vs = (const uint16_t*)vs;
   sa.vz = (const uint16_t*)vz;
   sa.seq_lens = seq_lens;
-  sa.o_part = (float*)ws;
-  sa.lse_part = (float*)ws + (size_t)d->batch * d->num_q_heads * splits * foscar::kHeadDim;
+  sa.out = (uint16_t*)out;
+  sa.lse = lse;
+  sa.counters = (int32_t*)ws;
+  sa.o_part = (float*)((char*)ws + counter_bytes(d));
+  sa.lse_part = sa.o_part + (size_t)d->batch * d->num_q_heads * splits * foscar::kHeadDim;
   sa.hq = d->num_q_heads;
   sa.hkv = d->num_kv_heads;
   sa.g_heads = d->num_q_heads / d->num_kv_heads;
@@ -167,19 +182,8 @@ int decode_common(int bits, const foscar_dims* d, const void* q, const void* pk,
   sa.chunk = chunk;
   sa.sm_log2 = sm * 1.4426950408889634f;
 
-  foscar::MergeArgs ma;
-  ma.o_part = sa.o_part;
-  ma.lse_part = sa.lse_part;
-  ma.seq_lens = seq_lens;
-  ma.out = (uint16_t*)out;
-  ma.lse = lse;
-  ma.hq = d->num_q_heads;
-  ma.tcap = d->max_seq_len;
-  ma.splits = splits;
-  ma.chunk = chunk;
-
   e = foscar::launch_decode(bits, (layout & FOSCAR_K_CHANNEL) != 0, (layout & FOSCAR_V_CHANNEL) != 0, group,
-                            d->batch, d->num_kv_heads, sa, ma, (hipStream_t)stream);
+                            d->batch, d->num_kv_heads, sa, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e);
   return FOSCAR_OK;
 }

@@ -18,7 +18,7 @@
 //     g-token units when a channel-wise group is longer than a tile) in turn;
 //   * per tile, lane l streams token l's packed key row and the packed value
 //     words of channels 2l, 2l+1 straight from HBM into registers (dwordx4 /
-//     dwordx2, one tile of prefetch in flight);
+//     dwordx2); the next tile's loads are issued before the current tile's math;
 //   * codes become matrix-core operands by one AND-OR per fp16 pair: a code
 //     dropped into the mantissa under a fixed exponent reads as C + q (C a
 //     power of two), and the C*sum(other operand) it adds is removed once per
@@ -32,8 +32,9 @@
 //   * online softmax with the exact running max of each query head (DPP,
 //     ds_swizzle and ds_bpermute reductions across the 16 lanes of a head; the
 //     accumulators are rescaled only when a max rises);
-//   * the range's partial (O, lse) goes to a workspace and a second kernel
-//     merges the ranges by log-sum-exp.
+//   * a range's partial (O, lse) goes to a workspace; the last work-group to
+//     finish a (sequence, KV head) merges its ranges by log-sum-exp (agent-scope
+//     release/acquire counter), so one decode step is one kernel launch.
 #include <math.h>
 
 #include "foscar_internal.h"
@@ -63,6 +64,12 @@ __device__ __forceinline__ uint32_t pack_f16(float lo, float hi) {
   return as_u32(v);
 }
 __device__ __forceinline__ uint32_t splat_f16(float c) { return pack_f16(c, c); }
+__device__ __forceinline__ uint16_t to_bf16_rne(float f) {
+  uint32_t u = __builtin_bit_cast(uint32_t, f);
+  if ((u & 0x7F800000u) == 0x7F800000u && (u & 0x007FFFFFu)) return 0x7FC0;  // NaN
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
 
 // ---------------------------------------------------------------------------
 // Code -> fp16 operand construction.  A packed word holds E codes; element e
@@ -79,20 +86,24 @@ template <>
 struct Codec<2> {
   static constexpr int E = 16;      // codes per word
   static constexpr int PAIRS = 8;   // fp16 pairs per word
+  static constexpr int NCONST = 6;
   // C of pair k (positions 4, 6, 8 -> 64, 16, 4)
   __host__ __device__ static constexpr float bias(int k) {
     return (k == 4 || k == 7) ? 4.0f : ((k == 1 || k == 3 || k == 6) ? 16.0f : 64.0f);
   }
-  __device__ static __forceinline__ void extract(uint32_t w, uint32_t (&p)[8]) {
+  // masks and exponent words; kept in registers so that each pair is one v_and_or_b32
+  static constexpr uint32_t kConst[NCONST] = {0x00300030u, 0x00C000C0u, 0x03000300u,
+                                              0x54005400u, 0x4C004C00u, 0x44004400u};
+  __device__ static __forceinline__ void extract(uint32_t w, const uint32_t (&k)[NCONST], uint32_t (&p)[8]) {
     const uint32_t l = w << 4, r = w >> 6;
-    p[0] = and_or(l, 0x00300030u, 0x54005400u);  // bits 0-1   -> 4-5
-    p[1] = and_or(l, 0x00C000C0u, 0x4C004C00u);  // bits 2-3   -> 6-7
-    p[2] = and_or(w, 0x00300030u, 0x54005400u);  // bits 4-5
-    p[3] = and_or(w, 0x00C000C0u, 0x4C004C00u);  // bits 6-7
-    p[4] = and_or(w, 0x03000300u, 0x44004400u);  // bits 8-9
-    p[5] = and_or(r, 0x00300030u, 0x54005400u);  // bits 10-11 -> 4-5
-    p[6] = and_or(r, 0x00C000C0u, 0x4C004C00u);  // bits 12-13 -> 6-7
-    p[7] = and_or(r, 0x03000300u, 0x44004400u);  // bits 14-15 -> 8-9
+    p[0] = and_or(l, k[0], k[3]);  // bits 0-1   -> 4-5, C = 64
+    p[1] = and_or(l, k[1], k[4]);  // bits 2-3   -> 6-7, C = 16
+    p[2] = and_or(w, k[0], k[3]);  // bits 4-5
+    p[3] = and_or(w, k[1], k[4]);  // bits 6-7
+    p[4] = and_or(w, k[2], k[5]);  // bits 8-9,        C = 4
+    p[5] = and_or(r, k[0], k[3]);  // bits 10-11 -> 4-5
+    p[6] = and_or(r, k[1], k[4]);  // bits 12-13 -> 6-7
+    p[7] = and_or(r, k[2], k[5]);  // bits 14-15 -> 8-9
   }
 };
 
@@ -100,14 +111,22 @@ template <>
 struct Codec<4> {
   static constexpr int E = 8;
   static constexpr int PAIRS = 4;
+  static constexpr int NCONST = 2;
   __host__ __device__ static constexpr float bias(int) { return 64.0f; }
-  __device__ static __forceinline__ void extract(uint32_t w, uint32_t (&p)[4]) {
-    p[0] = and_or(w << 4, 0x00F000F0u, 0x54005400u);  // bits 0-3   -> 4-7
-    p[1] = and_or(w, 0x00F000F0u, 0x54005400u);       // bits 4-7
-    p[2] = and_or(w >> 4, 0x00F000F0u, 0x54005400u);  // bits 8-11  -> 4-7
-    p[3] = and_or(w >> 8, 0x00F000F0u, 0x54005400u);  // bits 12-15 -> 4-7
+  static constexpr uint32_t kConst[NCONST] = {0x00F000F0u, 0x54005400u};
+  __device__ static __forceinline__ void extract(uint32_t w, const uint32_t (&k)[NCONST], uint32_t (&p)[4]) {
+    p[0] = and_or(w << 4, k[0], k[1]);  // bits 0-3   -> 4-7, C = 64
+    p[1] = and_or(w, k[0], k[1]);       // bits 4-7
+    p[2] = and_or(w >> 4, k[0], k[1]);  // bits 8-11  -> 4-7
+    p[3] = and_or(w >> 8, k[0], k[1]);  // bits 12-15 -> 4-7
   }
 };
+
+// A value the compiler must keep in a VGPR (no literal folding).
+__device__ __forceinline__ uint32_t in_vgpr(uint32_t v) {
+  asm volatile("" : "+v"(v));
+  return v;
+}
 
 // Cross-lane helpers.  Lane l holds query head (l & 3) of quad (l >> 2); the
 // lanes of one query head are l, l^4, l^8, ... (stride 4).
@@ -180,9 +199,17 @@ __global__ __launch_bounds__(256) void split_decode(const SplitArgs a) {
   const int b = blockIdx.z;
   const int T = min(max(a.seq_lens[b], 0), a.tcap);
   const int r0 = split * a.chunk;
-  if (r0 >= T) return;  // the merge never reads ranges at or past T
+  if (r0 >= T) {  // ranges at or past T hold no token; an empty sequence is written by range 0
+    if (T == 0 && split == 0) {
+      for (int idx = threadIdx.x; idx < a.g_heads * kHeadDim; idx += blockDim.x) {
+        const size_t row = (size_t)b * a.hq + h * a.g_heads + idx / kHeadDim;
+        a.out[row * kHeadDim + idx % kHeadDim] = 0;
+        if (idx % kHeadDim == 0 && a.lse) a.lse[row] = -INFINITY;
+      }
+    }
+    return;
+  }
   const int r1 = min(r0 + a.chunk, T);
-  const int nunits = (r1 - r0 + UNIT - 1) / UNIT;
 
   __shared__ uint2 s_p[kWaves][NGV][4][16];   // P operand of (group, query, quad)
   __shared__ float s_o[kWaves][4][D];         // epilogue: per-wave partial output
@@ -236,13 +263,16 @@ __global__ __launch_bounds__(256) void split_decode(const SplitArgs a) {
 #pragma unroll
   for (int j = 0; j < NGV; ++j) vz_part[j] = vb_part[j] = 0.f;
   float ps_part = 0.f, pb_part = 0.f;      // channel-wise V: sum P16, sum P16 * C over the current group
-  f4 o_acc[2];                             // PV accumulators: [channel 2l+h][query]
+  f4 o_acc[2][2];                          // PV accumulators [channel 2l+h][quad parity]: rows = query heads
   f4 o_tot[2];                             // channel-wise V: folded output
 #pragma unroll
   for (int hh = 0; hh < 2; ++hh) {
-    o_acc[hh] = f4{0.f, 0.f, 0.f, 0.f};
+    o_acc[hh][0] = o_acc[hh][1] = f4{0.f, 0.f, 0.f, 0.f};
     o_tot[hh] = f4{0.f, 0.f, 0.f, 0.f};
   }
+  uint32_t kc[C::NCONST];                  // operand-construction masks / exponents
+#pragma unroll
+  for (int i = 0; i < C::NCONST; ++i) kc[i] = in_vgpr(C::kConst[i]);
 
   // value-operand bias of this lane's quad (pairs 2*(qd % KPW), +1)
   const float cv0 = C::bias(2 * (qd % KPW)), cv1 = C::bias(2 * (qd % KPW) + 1);
@@ -270,7 +300,8 @@ __global__ __launch_bounds__(256) void split_decode(const SplitArgs a) {
     for (int i = 0; i < 4; ++i) {
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh) {
-        o_acc[hh][i] *= ai[i];  // row i of the PV accumulators is query head i
+        o_acc[hh][0][i] *= ai[i];  // row i of the PV accumulators is query head i
+        o_acc[hh][1][i] *= ai[i];
         o_tot[hh][i] *= ai[i];
       }
     }
@@ -300,216 +331,235 @@ __global__ __launch_bounds__(256) void split_decode(const SplitArgs a) {
     for (int i = 0; i < 4; ++i) {
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh)
-        o_tot[hh][i] += sv[hh] * o_acc[hh][i] + (zv[hh] * psq[i] - sv[hh] * pbq[i]);
+        o_tot[hh][i] += sv[hh] * (o_acc[hh][0][i] + o_acc[hh][1][i]) + (zv[hh] * psq[i] - sv[hh] * pbq[i]);
     }
 #pragma unroll
-    for (int hh = 0; hh < 2; ++hh) o_acc[hh] = f4{0.f, 0.f, 0.f, 0.f};
+    for (int hh = 0; hh < 2; ++hh) o_acc[hh][0] = o_acc[hh][1] = f4{0.f, 0.f, 0.f, 0.f};
   };
 
-  for (int u = wave; u < nunits; u += kWaves) {
-    const int ustart = r0 + u * UNIT;
-#pragma unroll 1
-    for (int tt = 0; tt < TPU; ++tt) {
-      const int t0 = ustart + tt * kTile;
-      if (t0 >= r1) break;
-      const bool tail = t0 + kTile > T;
+  // ---------------- tile registers, prefetched one tile ahead
+  struct Tile {
+    uint4 k[KW / 4];           // key row of token t0 + lane
+    uint2 v[VW];               // value words of channels 2 lane, 2 lane + 1
+    uint2 ks[NGK], kz[NGK];    // token-wise key (s, z) of the quad's tokens
+    uint2 vs[NGV], vz[NGV];    // token-wise value (s, z) of the quad's tokens
+  };
+  auto load_tile = [&](Tile& tl, int t0) {
+    const uint4* kp = reinterpret_cast<const uint4*>(kbase + (size_t)(t0 + lane) * KW);
+#pragma unroll
+    for (int i = 0; i < KW / 4; ++i) tl.k[i] = kp[i];
+#pragma unroll
+    for (int w = 0; w < VW; ++w)
+      tl.v[w] = *reinterpret_cast<const uint2*>(vbase + (size_t)(t0 / E + w) * D + 2 * lane);
+    if constexpr (!KCH) {
+      load_u2(tl.ks, ksb + (size_t)(t0 + 4 * qd) * NGK);
+      load_u2(tl.kz, kzb + (size_t)(t0 + 4 * qd) * NGK);
+    }
+    if constexpr (!VCH) {
+      load_u2(tl.vs, vsb + (size_t)(t0 + 4 * qd) * NGV);
+      load_u2(tl.vz, vzb + (size_t)(t0 + 4 * qd) * NGV);
+    }
+  };
 
-      // ---------------- loads
-      uint4 kw4[KW / 4];
-      {
-        const uint4* kp = reinterpret_cast<const uint4*>(kbase + (size_t)(t0 + lane) * KW);
+  auto process = [&](const Tile& tl, const int t0) {
+    const bool tail = t0 + kTile > T;
+    // ---------------- channel-wise K: operand Q~ for the group of this lane's quad
+    if constexpr (KCH) {
+      const int tau = (t0 + 4 * qd) / GRP;
+      if (tau != k_tau) {  // uniform for g >= 64; per half-wave for g = 32
+        k_tau = tau;
+        const uint4* sp = reinterpret_cast<const uint4*>(ksb + (size_t)tau * D);
+        const uint4* zp = reinterpret_cast<const uint4*>(kzb + (size_t)tau * D);
+        float bq = 0.f, zq = 0.f;
 #pragma unroll
-        for (int i = 0; i < KW / 4; ++i) kw4[i] = kp[i];
-      }
-      uint2 vw2[VW];
+        for (int i = 0; i < D / 8; ++i) {
+          uint4 q4 = qrow[i];
+          if (!qvalid) q4 = make_uint4(0, 0, 0, 0);
+          const uint4 s4 = sp[i], z4 = zp[i];
+          const uint32_t qw[4] = {q4.x, q4.y, q4.z, q4.w};
+          const uint32_t sw[4] = {s4.x, s4.y, s4.z, s4.w};
+          const uint32_t zw[4] = {z4.x, z4.y, z4.z, z4.w};
 #pragma unroll
-      for (int w = 0; w < VW; ++w)
-        vw2[w] = *reinterpret_cast<const uint2*>(vbase + (size_t)(t0 / E + w) * D + 2 * lane);
-      uint2 ks2[NGK], kz2[NGK];
-      if constexpr (!KCH) {
-        load_u2(ks2, ksb + (size_t)(t0 + 4 * qd) * NGK);
-        load_u2(kz2, kzb + (size_t)(t0 + 4 * qd) * NGK);
-      }
-      uint2 vs2[NGV], vz2[NGV];
-      if constexpr (!VCH) {
-        load_u2(vs2, vsb + (size_t)(t0 + 4 * qd) * NGV);
-        load_u2(vz2, vzb + (size_t)(t0 + 4 * qd) * NGV);
-      }
-
-      // ---------------- channel-wise K: operand Q~ for the group of this lane's quad
-      if constexpr (KCH) {
-        const int tau = (t0 + 4 * qd) / GRP;
-        if (tau != k_tau) {  // uniform for g >= 64; per half-wave for g = 32
-          k_tau = tau;
-          const uint4* sp = reinterpret_cast<const uint4*>(ksb + (size_t)tau * D);
-          const uint4* zp = reinterpret_cast<const uint4*>(kzb + (size_t)tau * D);
-          float bq = 0.f, zq = 0.f;
-#pragma unroll
-          for (int i = 0; i < D / 8; ++i) {
-            uint4 q4 = qrow[i];
-            if (!qvalid) q4 = make_uint4(0, 0, 0, 0);
-            const uint4 s4 = sp[i], z4 = zp[i];
-            const uint32_t qw[4] = {q4.x, q4.y, q4.z, q4.w};
-            const uint32_t sw[4] = {s4.x, s4.y, s4.z, s4.w};
-            const uint32_t zw[4] = {z4.x, z4.y, z4.z, z4.w};
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-              const int jj = 4 * i + j;
-              const float q0 = __builtin_bit_cast(float, qw[j] << 16);
-              const float q1 = __builtin_bit_cast(float, qw[j] & 0xFFFF0000u);
-              const float pr0 = q0 * half_lo(sw[j]), pr1 = q1 * half_hi(sw[j]);  // exact
-              const _Float16 h0 = (_Float16)pr0, h1 = (_Float16)pr1;
-              const h2 hi = {h0, h1};
-              const h2 lo = {(_Float16)(pr0 - (float)h0), (_Float16)(pr1 - (float)h1)};
-              qt_hi[jj] = as_u32(hi);
-              qt_lo[jj] = as_u32(lo);
-              bq = fmaf(C::bias(jj % PAIRS), pr0 + pr1, bq);
-              zq = fmaf(q0, half_lo(zw[j]), fmaf(q1, half_hi(zw[j]), zq));
-            }
-          }
-          kconst = (zq - bq) * sl2;
-        }
-      }
-
-      // ---------------- QK^T on the matrix cores
-      f4 sacc[NGK];
-#pragma unroll
-      for (int j = 0; j < NGK; ++j) sacc[j] = f4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int d = 0; d < KW; ++d) {
-        const uint32_t wrd = (d % 4 == 0) ? kw4[d / 4].x : (d % 4 == 1) ? kw4[d / 4].y : (d % 4 == 2) ? kw4[d / 4].z : kw4[d / 4].w;
-        uint32_t p[PAIRS];
-        C::extract(wrd, p);
-#pragma unroll
-        for (int sg = 0; sg < KPW; ++sg) {
-          const int j = d * KPW + sg;  // k-step: channels 4j .. 4j+3
-          const h4 av = cat4(p[2 * sg], p[2 * sg + 1]);
-          if constexpr (KCH) {
-            sacc[0] = __builtin_amdgcn_mfma_f32_4x4x4f16(av, cat4(qt_hi[2 * j], qt_hi[2 * j + 1]), sacc[0], 0, 0, 0);
-            sacc[0] = __builtin_amdgcn_mfma_f32_4x4x4f16(av, cat4(qt_lo[2 * j], qt_lo[2 * j + 1]), sacc[0], 0, 0, 0);
-          } else {
-            const int grp = (4 * j) / GRP;
-            sacc[grp] = __builtin_amdgcn_mfma_f32_4x4x4f16(av, cat4(q16[2 * j], q16[2 * j + 1]), sacc[grp], 0, 0, 0);
+          for (int j = 0; j < 4; ++j) {
+            const int jj = 4 * i + j;
+            const float q0 = __builtin_bit_cast(float, qw[j] << 16);
+            const float q1 = __builtin_bit_cast(float, qw[j] & 0xFFFF0000u);
+            const float pr0 = q0 * half_lo(sw[j]), pr1 = q1 * half_hi(sw[j]);  // exact
+            const _Float16 h0 = (_Float16)pr0, h1 = (_Float16)pr1;
+            const h2 hi = {h0, h1};
+            const h2 lo = {(_Float16)(pr0 - (float)h0), (_Float16)(pr1 - (float)h1)};
+            qt_hi[jj] = as_u32(hi);
+            qt_lo[jj] = as_u32(lo);
+            bq = fmaf(C::bias(jj % PAIRS), pr0 + pr1, bq);
+            zq = fmaf(q0, half_lo(zw[j]), fmaf(q1, half_hi(zw[j]), zq));
           }
         }
+        kconst = (zq - bq) * sl2;
       }
+    }
 
-      // ---------------- key-side fold (before the softmax) -> scores in log2 units
-      float sc[4];
+    // ---------------- QK^T on the matrix cores
+    constexpr int NCH = (NGK == 1) ? 2 : NGK;  // independent accumulation chains
+    f4 sacc[NCH];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
+    for (int j = 0; j < NCH; ++j) sacc[j] = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int d = 0; d < KW; ++d) {
+      const uint32_t wrd = (d % 4 == 0) ? tl.k[d / 4].x : (d % 4 == 1) ? tl.k[d / 4].y : (d % 4 == 2) ? tl.k[d / 4].z : tl.k[d / 4].w;
+      uint32_t p[PAIRS];
+      C::extract(wrd, kc, p);
+#pragma unroll
+      for (int sg = 0; sg < KPW; ++sg) {
+        const int j = d * KPW + sg;  // k-step: channels 4j .. 4j+3
+        const h4 av = cat4(p[2 * sg], p[2 * sg + 1]);
         if constexpr (KCH) {
-          sc[r] = fmaf(sacc[0][r], sl2, kconst);
+          sacc[0] = __builtin_amdgcn_mfma_f32_4x4x4f16(av, cat4(qt_hi[2 * j], qt_hi[2 * j + 1]), sacc[0], 0, 0, 0);
+          sacc[1] = __builtin_amdgcn_mfma_f32_4x4x4f16(av, cat4(qt_lo[2 * j], qt_lo[2 * j + 1]), sacc[1], 0, 0, 0);
         } else {
-          float acc = 0.f;
-#pragma unroll
-          for (int j = 0; j < NGK; ++j) {
-            const int idx = r * NGK + j;  // fp16 index inside the quad's (token, group) block
-            const uint2 sv = ks2[idx / 4];
-            const uint2 zv = kz2[idx / 4];
-            const uint32_t s32 = ((idx % 4) < 2) ? sv.x : sv.y;
-            const uint32_t z32 = ((idx % 4) < 2) ? zv.x : zv.y;
-            const float s = (idx % 2 == 0) ? half_lo(s32) : half_hi(s32);
-            const float z = (idx % 2 == 0) ? half_lo(z32) : half_hi(z32);
-            acc = fmaf(s, fmaf(sacc[j][r], sl2, -kq_bias[j]), acc);
-            acc = fmaf(z, kq_sum[j], acc);
-          }
-          sc[r] = acc;
-        }
-        if (tail && (t0 + 4 * qd + r >= T)) sc[r] = -INFINITY;
-      }
-
-      // ---------------- online softmax: exact running max per query head.  The
-      // largest weight seen so far is exactly 1, so the operand-folded weight of
-      // the dominant token (p * s) is its fp16 scale itself, with no rounding.
-      const float m_new = fmaxf(m_ref, wave_max_same_query(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]))));
-      if (__any(m_new > m_ref)) {
-        const float alpha = __builtin_amdgcn_exp2f(m_ref - m_new);  // 0 on the first tile
-        m_ref = m_new;
-        rescale(alpha);
-      }
-      float p[4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) p[r] = __builtin_amdgcn_exp2f(sc[r] - m_ref);
-      l_part += (p[0] + p[1]) + (p[2] + p[3]);
-
-      // ---------------- P operands (value-side operand-fold for token-wise V)
-      if constexpr (!VCH) {
-#pragma unroll
-        for (int j = 0; j < NGV; ++j) {
-          float s[4], z[4];
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int idx = r * NGV + j;
-            const uint2 sv = vs2[idx / 4];
-            const uint2 zv = vz2[idx / 4];
-            const uint32_t s32 = ((idx % 4) < 2) ? sv.x : sv.y;
-            const uint32_t z32 = ((idx % 4) < 2) ? zv.x : zv.y;
-            s[r] = (idx % 2 == 0) ? half_lo(s32) : half_hi(s32);
-            z[r] = (idx % 2 == 0) ? half_lo(z32) : half_hi(z32);
-            if (tail && (t0 + 4 * qd + r >= T)) s[r] = z[r] = 0.f;  // padding may hold NaN
-          }
-          const uint32_t p01 = pack_f16(p[0] * s[0], p[1] * s[1]);
-          const uint32_t p23 = pack_f16(p[2] * s[2], p[3] * s[3]);
-          s_p[wave][j][qn][qd] = make_uint2(p01, p23);
-          vb_part[j] = dot2(p23, cv1h, dot2(p01, cv0h, vb_part[j]));
-          vz_part[j] = fmaf(p[0], z[0], fmaf(p[1], z[1], fmaf(p[2], z[2], fmaf(p[3], z[3], vz_part[j]))));
-        }
-      } else {
-        const uint32_t p01 = pack_f16(p[0], p[1]);
-        const uint32_t p23 = pack_f16(p[2], p[3]);
-        s_p[wave][0][qn][qd] = make_uint2(p01, p23);
-        ps_part = dot2(p23, oneh, dot2(p01, oneh, ps_part));
-        pb_part = dot2(p23, cv1h, dot2(p01, cv0h, pb_part));
-      }
-      __builtin_amdgcn_wave_barrier();
-      // gathered A operands: P of query qn for all 16 quads (value group of this lane's channels)
-      uint2 pa[16];
-      {
-        const int jv = VCH ? 0 : (8 * qd) / GRP;
-        const uint4* src = reinterpret_cast<const uint4*>(&s_p[wave][jv][qn][0]);
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const uint4 v = src[i];
-          pa[2 * i] = make_uint2(v.x, v.y);
-          pa[2 * i + 1] = make_uint2(v.z, v.w);
-        }
-      }
-      __builtin_amdgcn_wave_barrier();
-
-      // ---------------- P V on the matrix cores (+ acc-fold of channel-wise value groups)
-#pragma unroll
-      for (int w = 0; w < VW; ++w) {
-        uint32_t p0[PAIRS], p1[PAIRS];
-        C::extract(vw2[w].x, p0);  // channel 2*lane
-        C::extract(vw2[w].y, p1);  // channel 2*lane + 1
-#pragma unroll
-        for (int sg = 0; sg < KPW; ++sg) {
-          const int bq = w * KPW + sg;  // quad: tokens 4bq .. 4bq+3 of the tile
-          const h4 av = cat4(pa[bq].x, pa[bq].y);
-          o_acc[0] = __builtin_amdgcn_mfma_f32_4x4x4f16(av, cat4(p0[2 * sg], p0[2 * sg + 1]), o_acc[0], 0, 0, 0);
-          o_acc[1] = __builtin_amdgcn_mfma_f32_4x4x4f16(av, cat4(p1[2 * sg], p1[2 * sg + 1]), o_acc[1], 0, 0, 0);
-          if constexpr (VCH && GRP == 32) {
-            if (bq == 7) {  // first 32-token group of the tile is complete
-              if (t0 < T) fold_value_group(t0 / GRP, 0);
-            }
-          }
-        }
-      }
-      if constexpr (VCH) {
-        if (GRP == 32) {
-          if (t0 + 32 < T) fold_value_group(t0 / GRP + 1, 1);
-          else {
-#pragma unroll
-            for (int hh = 0; hh < 2; ++hh) o_acc[hh] = f4{0.f, 0.f, 0.f, 0.f};
-          }
-          ps_part = pb_part = 0.f;
-        } else if ((t0 + kTile) % GRP == 0 || t0 + kTile >= r1) {
-          fold_value_group(t0 / GRP, 0);
-          ps_part = pb_part = 0.f;
+          const int ch = (NGK == 1) ? (j & 1) : (4 * j) / GRP;
+          sacc[ch] = __builtin_amdgcn_mfma_f32_4x4x4f16(av, cat4(q16[2 * j], q16[2 * j + 1]), sacc[ch], 0, 0, 0);
         }
       }
     }
+
+    // ---------------- key-side fold (before the softmax) -> scores in log2 units
+    float sc[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      if constexpr (KCH) {
+        sc[r] = fmaf(sacc[0][r] + sacc[1][r], sl2, kconst);
+      } else {
+        float acc = 0.f;
+#pragma unroll
+        for (int j = 0; j < NGK; ++j) {
+          const int idx = r * NGK + j;  // fp16 index inside the quad's (token, group) block
+          const uint2 sv = tl.ks[idx / 4];
+          const uint2 zv = tl.kz[idx / 4];
+          const uint32_t s32 = ((idx % 4) < 2) ? sv.x : sv.y;
+          const uint32_t z32 = ((idx % 4) < 2) ? zv.x : zv.y;
+          const float s = (idx % 2 == 0) ? half_lo(s32) : half_hi(s32);
+          const float z = (idx % 2 == 0) ? half_lo(z32) : half_hi(z32);
+          const float raw = (NGK == 1) ? sacc[0][r] + sacc[1][r] : sacc[j][r];
+          acc = fmaf(s, fmaf(raw, sl2, -kq_bias[j]), acc);
+          acc = fmaf(z, kq_sum[j], acc);
+        }
+        sc[r] = acc;
+      }
+      if (tail && (t0 + 4 * qd + r >= T)) sc[r] = -INFINITY;
+    }
+
+    // ---------------- online softmax: exact running max per query head.  The
+    // largest weight seen so far is exactly 1, so the operand-folded weight of
+    // the dominant token (p * s) is its fp16 scale itself, with no rounding.
+    const float m_new = fmaxf(m_ref, wave_max_same_query(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]))));
+    if (__any(m_new > m_ref)) {
+      const float alpha = __builtin_amdgcn_exp2f(m_ref - m_new);  // 0 on the first tile
+      m_ref = m_new;
+      rescale(alpha);
+    }
+    float p[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) p[r] = __builtin_amdgcn_exp2f(sc[r] - m_ref);
+    l_part += (p[0] + p[1]) + (p[2] + p[3]);
+
+    // ---------------- P operands (value-side operand-fold for token-wise V)
+    if constexpr (!VCH) {
+#pragma unroll
+      for (int j = 0; j < NGV; ++j) {
+        float s[4], z[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int idx = r * NGV + j;
+          const uint2 sv = tl.vs[idx / 4];
+          const uint2 zv = tl.vz[idx / 4];
+          const uint32_t s32 = ((idx % 4) < 2) ? sv.x : sv.y;
+          const uint32_t z32 = ((idx % 4) < 2) ? zv.x : zv.y;
+          s[r] = (idx % 2 == 0) ? half_lo(s32) : half_hi(s32);
+          z[r] = (idx % 2 == 0) ? half_lo(z32) : half_hi(z32);
+          if (tail && (t0 + 4 * qd + r >= T)) s[r] = z[r] = 0.f;  // padding may hold NaN
+        }
+        const uint32_t p01 = pack_f16(p[0] * s[0], p[1] * s[1]);
+        const uint32_t p23 = pack_f16(p[2] * s[2], p[3] * s[3]);
+        s_p[wave][j][qn][qd] = make_uint2(p01, p23);
+        vb_part[j] = dot2(p23, cv1h, dot2(p01, cv0h, vb_part[j]));
+        vz_part[j] = fmaf(p[0], z[0], fmaf(p[1], z[1], fmaf(p[2], z[2], fmaf(p[3], z[3], vz_part[j]))));
+      }
+    } else {
+      const uint32_t p01 = pack_f16(p[0], p[1]);
+      const uint32_t p23 = pack_f16(p[2], p[3]);
+      s_p[wave][0][qn][qd] = make_uint2(p01, p23);
+      ps_part = dot2(p23, oneh, dot2(p01, oneh, ps_part));
+      pb_part = dot2(p23, cv1h, dot2(p01, cv0h, pb_part));
+    }
+    __builtin_amdgcn_wave_barrier();
+    // gathered A operands: P of query qn for all 16 quads (value group of this lane's channels)
+    uint2 pa[16];
+    {
+      const int jv = VCH ? 0 : (8 * qd) / GRP;
+      const uint4* src = reinterpret_cast<const uint4*>(&s_p[wave][jv][qn][0]);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const uint4 v = src[i];
+        pa[2 * i] = make_uint2(v.x, v.y);
+        pa[2 * i + 1] = make_uint2(v.z, v.w);
+      }
+    }
+    __builtin_amdgcn_wave_barrier();
+
+    // ---------------- P V on the matrix cores (+ acc-fold of channel-wise value groups)
+#pragma unroll
+    for (int w = 0; w < VW; ++w) {
+      uint32_t p0[PAIRS], p1[PAIRS];
+      C::extract(tl.v[w].x, kc, p0);  // channel 2*lane
+      C::extract(tl.v[w].y, kc, p1);  // channel 2*lane + 1
+#pragma unroll
+      for (int sg = 0; sg < KPW; ++sg) {
+        const int bq = w * KPW + sg;  // quad: tokens 4bq .. 4bq+3 of the tile
+        const h4 av = cat4(pa[bq].x, pa[bq].y);
+        f4& a0 = o_acc[0][bq & 1];
+        f4& a1 = o_acc[1][bq & 1];
+        a0 = __builtin_amdgcn_mfma_f32_4x4x4f16(av, cat4(p0[2 * sg], p0[2 * sg + 1]), a0, 0, 0, 0);
+        a1 = __builtin_amdgcn_mfma_f32_4x4x4f16(av, cat4(p1[2 * sg], p1[2 * sg + 1]), a1, 0, 0, 0);
+        if constexpr (VCH && GRP == 32) {
+          if (bq == 7) {  // first 32-token group of the tile is complete
+            if (t0 < T) fold_value_group(t0 / GRP, 0);
+          }
+        }
+      }
+    }
+    if constexpr (VCH) {
+      if (GRP == 32) {
+        if (t0 + 32 < T) fold_value_group(t0 / GRP + 1, 1);
+        else {
+#pragma unroll
+          for (int hh = 0; hh < 2; ++hh) o_acc[hh][0] = o_acc[hh][1] = f4{0.f, 0.f, 0.f, 0.f};
+        }
+        ps_part = pb_part = 0.f;
+      } else if ((t0 + kTile) % GRP == 0 || t0 + kTile >= r1) {
+        fold_value_group(t0 / GRP, 0);
+        ps_part = pb_part = 0.f;
+      }
+    }
+  };
+
+  // the wave's tiles in order: unit wave, wave + kWaves, ...; TPU tiles per unit
+  auto tile_start = [&](int k) { return r0 + (wave + kWaves * (k / TPU)) * UNIT + (k % TPU) * kTile; };
+  Tile ta, tb;
+  int kt = 0;
+  int t0 = tile_start(0);
+  if (t0 < r1) load_tile(ta, t0);
+  while (t0 < r1) {
+    int t1 = tile_start(kt + 1);
+    if (t1 < r1) load_tile(tb, t1);
+    process(ta, t0);
+    t0 = t1;
+    ++kt;
+    if (t0 >= r1) break;
+    t1 = tile_start(kt + 1);
+    if (t1 < r1) load_tile(ta, t1);
+    process(tb, t0);
+    t0 = t1;
+    ++kt;
   }
 
   // ---------------- wave epilogue: totals per query, value-side corrections
@@ -534,7 +584,7 @@ __global__ __launch_bounds__(256) void split_decode(const SplitArgs a) {
     for (int i = 0; i < 4; ++i) {
       const float corr = cq[i];
 #pragma unroll
-      for (int hh = 0; hh < 2; ++hh) o_fin[hh][i] = o_acc[hh][i] + corr;
+      for (int hh = 0; hh < 2; ++hh) o_fin[hh][i] = (o_acc[hh][0][i] + o_acc[hh][1][i]) + corr;
     }
   }
   if (lane < 4) {
@@ -548,7 +598,8 @@ __global__ __launch_bounds__(256) void split_decode(const SplitArgs a) {
   }
   __syncthreads();
 
-  // ---------------- work-group merge of the 4 waves -> partial of this range
+  // ---------------- work-group merge of the 4 waves -> this range's (O, lse)
+  const int ns = (T + a.chunk - 1) / a.chunk;  // ranges holding tokens of this sequence
   for (int idx = threadIdx.x; idx < 4 * D; idx += blockDim.x) {
     const int i = idx / D, c = idx % D;
     if (i >= a.g_heads) continue;
@@ -564,83 +615,80 @@ __global__ __launch_bounds__(256) void split_decode(const SplitArgs a) {
       den = fmaf(f, l, den);
     }
     const size_t row = (size_t)b * a.hq + h * a.g_heads + i;
-    a.o_part[(row * a.splits + split) * D + c] = num / den;
-    if (c == 0) a.lse_part[row * a.splits + split] = (M + __log2f(den)) * kLn2;
+    const float o = num / den, l_nat = (M + __log2f(den)) * kLn2;
+    if (ns == 1) {  // the only range: final output
+      a.out[row * D + c] = to_bf16_rne(o);
+      if (c == 0 && a.lse) a.lse[row] = l_nat;
+    } else {
+      a.o_part[(row * a.splits + split) * D + c] = o;
+      if (c == 0) a.lse_part[row * a.splits + split] = l_nat;
+    }
   }
-}
+  if (ns == 1) return;
 
-// ---------------------------------------------------------------------------
-// Log-sum-exp merge of the ranges of one (sequence, query head).
-// ---------------------------------------------------------------------------
-__device__ __forceinline__ uint16_t to_bf16_rne(float f) {
-  uint32_t u = __builtin_bit_cast(uint32_t, f);
-  if ((u & 0x7F800000u) == 0x7F800000u && (u & 0x007FFFFFu)) return 0x7FC0;  // NaN
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
-}
-
-__global__ __launch_bounds__(128) void merge_ranges(const MergeArgs a) {
-  const int row = blockIdx.x;  // b * Hq + head
-  const int b = row / a.hq;
-  const int c = threadIdx.x;
-  const int T = min(max(a.seq_lens[b], 0), a.tcap);
-  const int ns = (T + a.chunk - 1) / a.chunk;
-  if (ns == 0) {
-    a.out[(size_t)row * kHeadDim + c] = 0;
-    if (c == 0 && a.lse) a.lse[row] = -INFINITY;
-    return;
+  // ---------------- the last range of this (sequence, KV head) merges all ranges
+  __shared__ int s_last;
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const int done = __hip_atomic_fetch_add(a.counters + bh, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+    s_last = (done == ns - 1);
   }
-  const float* lp = a.lse_part + (size_t)row * a.splits;
-  const float* op = a.o_part + (size_t)row * a.splits * kHeadDim + c;
-  float M = -INFINITY;
-  for (int s = 0; s < ns; ++s) M = fmaxf(M, lp[s]);
-  float num = 0.f, den = 0.f;
-  for (int s = 0; s < ns; ++s) {
-    const float w = __expf(lp[s] - M);
-    num = fmaf(w, op[(size_t)s * kHeadDim], num);
-    den += w;
+  __syncthreads();
+  if (!s_last) return;
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  for (int idx = threadIdx.x; idx < a.g_heads * D; idx += blockDim.x) {
+    const int i = idx / D, c = idx % D;
+    const size_t row = (size_t)b * a.hq + h * a.g_heads + i;
+    const float* lp = a.lse_part + row * a.splits;
+    const float* op = a.o_part + row * a.splits * D + c;
+    float M = -INFINITY;
+    for (int s2 = 0; s2 < ns; ++s2) M = fmaxf(M, lp[s2]);
+    float num = 0.f, den = 0.f;
+    for (int s2 = 0; s2 < ns; ++s2) {
+      const float w = __expf(lp[s2] - M);
+      num = fmaf(w, op[(size_t)s2 * D], num);
+      den += w;
+    }
+    a.out[row * D + c] = to_bf16_rne(num / den);
+    if (c == 0 && a.lse) a.lse[row] = M + __logf(den);
   }
-  a.out[(size_t)row * kHeadDim + c] = to_bf16_rne(num / den);
-  if (c == 0 && a.lse) a.lse[row] = M + __logf(den);
+  if (threadIdx.x == 0) a.counters[bh] = 0;  // ready for the next call on this workspace
 }
 
 template <int BITS, bool KCH, bool VCH, int GRP>
-hipError_t launch_one(int batch, int hkv, const SplitArgs& sa, const MergeArgs& ma, hipStream_t stream) {
+hipError_t launch_one(int batch, int hkv, const SplitArgs& sa, hipStream_t stream) {
   dim3 grid(sa.splits, hkv, batch);
   hipLaunchKernelGGL((split_decode<BITS, KCH, VCH, GRP>), grid, dim3(kWaves * 64), 0, stream, sa);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(merge_ranges, dim3(batch * sa.hq), dim3(kHeadDim), 0, stream, ma);
   return hipGetLastError();
 }
 
 template <int BITS, bool KCH, bool VCH>
-hipError_t launch_g(int group, int batch, int hkv, const SplitArgs& sa, const MergeArgs& ma, hipStream_t stream) {
+hipError_t launch_g(int group, int batch, int hkv, const SplitArgs& sa, hipStream_t stream) {
   switch (group) {
-    case 32: return launch_one<BITS, KCH, VCH, 32>(batch, hkv, sa, ma, stream);
-    case 64: return launch_one<BITS, KCH, VCH, 64>(batch, hkv, sa, ma, stream);
-    case 128: return launch_one<BITS, KCH, VCH, 128>(batch, hkv, sa, ma, stream);
+    case 32: return launch_one<BITS, KCH, VCH, 32>(batch, hkv, sa, stream);
+    case 64: return launch_one<BITS, KCH, VCH, 64>(batch, hkv, sa, stream);
+    case 128: return launch_one<BITS, KCH, VCH, 128>(batch, hkv, sa, stream);
   }
   return hipErrorInvalidValue;
 }
 
 template <int BITS>
-hipError_t launch_bits(bool kch, bool vch, int group, int batch, int hkv, const SplitArgs& sa, const MergeArgs& ma,
-                       hipStream_t stream) {
+hipError_t launch_bits(bool kch, bool vch, int group, int batch, int hkv, const SplitArgs& sa, hipStream_t stream) {
   if (kch) {
-    return vch ? launch_g<BITS, true, true>(group, batch, hkv, sa, ma, stream)
-               : launch_g<BITS, true, false>(group, batch, hkv, sa, ma, stream);
+    return vch ? launch_g<BITS, true, true>(group, batch, hkv, sa, stream)
+               : launch_g<BITS, true, false>(group, batch, hkv, sa, stream);
   }
-  return vch ? launch_g<BITS, false, true>(group, batch, hkv, sa, ma, stream)
-             : launch_g<BITS, false, false>(group, batch, hkv, sa, ma, stream);
+  return vch ? launch_g<BITS, false, true>(group, batch, hkv, sa, stream)
+             : launch_g<BITS, false, false>(group, batch, hkv, sa, stream);
 }
 
 }  // namespace
 
 hipError_t launch_decode(int bits, bool k_channel, bool v_channel, int group, int batch, int hkv,
-                         const SplitArgs& sa, const MergeArgs& ma, hipStream_t stream) {
-  if (bits == 2) return launch_bits<2>(k_channel, v_channel, group, batch, hkv, sa, ma, stream);
-  return launch_bits<4>(k_channel, v_channel, group, batch, hkv, sa, ma, stream);
+                         const SplitArgs& sa, hipStream_t stream) {
+  if (bits == 2) return launch_bits<2>(k_channel, v_channel, group, batch, hkv, sa, stream);
+  return launch_bits<4>(k_channel, v_channel, group, batch, hkv, sa, stream);
 }
 
 }  // namespace foscar

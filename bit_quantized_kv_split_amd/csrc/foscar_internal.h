@@ -11,7 +11,8 @@ constexpr int kTile = 64;       // tokens per wave tile (16 quads of 4)
 constexpr int kWaves = 4;       // waves per work-group
 constexpr int kMaxG = 4;        // query heads per KV head served by one wave
 
-// Arguments of the split kernel (one work-group per (range, KV head, sequence)).
+// Arguments of the decode kernel (one work-group per (range, KV head, sequence)).
+// The last work-group to finish the ranges of a (sequence, KV head) merges them.
 struct SplitArgs {
   const uint16_t* q;         // bf16 [B][Hq][D]
   const uint32_t* pk;        // [B][Hkv][Tcap][D*bits/32]
@@ -21,8 +22,11 @@ struct SplitArgs {
   const uint16_t* vs;        // fp16 value scales
   const uint16_t* vz;        // fp16 value offsets
   const int32_t* seq_lens;   // [B]
+  uint16_t* out;             // bf16 [B][Hq][D]
+  float* lse;                // fp32 [B][Hq] or null
   float* o_part;             // fp32 [B][Hq][S][D]   normalised partial output of each range
   float* lse_part;           // fp32 [B][Hq][S]      natural-log lse of each range
+  int32_t* counters;         // [B][Hkv] ranges finished; zero between calls
   int32_t hq, hkv, g_heads;  // Hq, Hkv, G = Hq / Hkv
   int32_t tcap;              // Tcap
   int32_t splits;            // S
@@ -30,18 +34,8 @@ struct SplitArgs {
   float sm_log2;             // sm_scale * log2(e)
 };
 
-// Arguments of the merge kernel (one work-group per (sequence, query head)).
-struct MergeArgs {
-  const float* o_part;
-  const float* lse_part;
-  const int32_t* seq_lens;
-  uint16_t* out;             // bf16 [B][Hq][D]
-  float* lse;                // fp32 [B][Hq] or null
-  int32_t hq, tcap, splits, chunk;
-};
-
 hipError_t launch_decode(int bits, bool k_channel, bool v_channel, int group, int batch, int hkv,
-                         const SplitArgs& sa, const MergeArgs& ma, hipStream_t stream);
+                         const SplitArgs& sa, hipStream_t stream);
 
 hipError_t launch_pack(int bits, int side, int batch, int hkv, int tcap, const uint8_t* codes, uint32_t* packed,
                        hipStream_t stream);

@@ -125,7 +125,7 @@ def quantize_minmax(x: np.ndarray, bits: int, axis: int, valid: Optional[np.ndar
     entries get code 0.
     """
     levels = (1 << bits) - 1
-    xf = x.astype(np.float32)
+    xf = np.asarray(x, dtype=np.float32)
     if valid is None:
         mn = xf.min(axis=axis)
         mx = xf.max(axis=axis)
@@ -139,12 +139,16 @@ def quantize_minmax(x: np.ndarray, bits: int, axis: int, valid: Optional[np.ndar
     z16 = mn.astype(np.float16)
     s64 = np.expand_dims(s16.astype(np.float64), axis)
     z64 = np.expand_dims(z16.astype(np.float64), axis)
-    with np.errstate(divide="ignore", invalid="ignore"):
-        q = np.rint((xf.astype(np.float64) - z64) / s64)
-    q = np.where(s64 == 0.0, 0.0, q)
-    q = np.clip(np.nan_to_num(q, nan=0.0), 0, levels).astype(np.uint8)
+    q = xf.astype(np.float64)
+    q -= z64
+    q /= np.where(s64 == 0.0, 1.0, s64)      # a constant group (s = 0) keeps code 0 below
+    np.rint(q, out=q)
+    np.maximum(q, 0.0, out=q)
+    np.minimum(q, float(levels), out=q)
+    q = q.astype(np.uint8)
+    q *= (s64 != 0.0).astype(np.uint8)
     if valid is not None:
-        q = np.where(valid, q, 0).astype(np.uint8)
+        q *= valid.astype(np.uint8)
     return q, s16, z16
 
 
@@ -160,44 +164,46 @@ def _channel_std(spec: Spec, tensor: int, h: int) -> np.ndarray:
     return np.exp(rng.uniform(math.log(lo), math.log(hi), size=spec.head_dim)).astype(np.float32)
 
 
-def _quantize_head(spec: Spec, x: np.ndarray, layout: str, t_valid: int):
-    """Quantise one (T, D) head slice; returns codes [T, D] and (s, z) in the boundary layout."""
-    T, D = x.shape
-    g = spec.group
-    valid_tok = (np.arange(T) < t_valid)
-    if layout == TOKEN:
-        xg = x.reshape(T, D // g, g)
-        q, s, z = quantize_minmax(xg, spec.bits, axis=2)
-        q = q.reshape(T, D)
-        q[~valid_tok] = 0
-        s[~valid_tok] = 0
-        z[~valid_tok] = 0
-        return q, s, z                                # s, z: [T, D/g]
-    xg = x.reshape(T // g, g, D)
-    valid = np.broadcast_to(valid_tok.reshape(T // g, g, 1), xg.shape)
-    q, s, z = quantize_minmax(xg, spec.bits, axis=1, valid=valid)
-    return q.reshape(T, D), s, z                      # s, z: [T/g, D]
+_CHUNK = 65536  # tokens per generation step (a multiple of every group size)
 
 
 def make_head(spec: Spec, b: int, h: int, seq_len: Optional[int] = None, poison: bool = False) -> dict:
     """Cache slice of one (sequence b, KV head h): codes and (s, z) for K and V.
 
+    Values are drawn token by token from one stream per (b, h, tensor); only
+    the valid tokens are drawn, in chunks (the same values as one draw).
     With ``poison`` the tokens past the sequence length get random codes and
     NaN scales/offsets, to show that nothing past the length reaches the result.
     """
-    T, D = spec.max_seq_len, spec.head_dim
+    T, D, g = spec.max_seq_len, spec.head_dim, spec.group
     t_valid = int(spec.seq_lens()[b] if seq_len is None else seq_len)
     out = {}
     for tensor, name, layout in ((_T_K, "k", spec.k_layout), (_T_V, "v", spec.v_layout)):
         rng = np.random.default_rng([spec.seed, spec.wid, tensor, b, h])
-        # only the valid tokens are drawn (a prefix of the stream); padding is zero
-        x = np.zeros((T, D), dtype=np.float32)
-        x[:t_valid] = rng.standard_normal((t_valid, D), dtype=np.float32)
-        if spec.channel_std_logu is not None:
-            x *= _channel_std(spec, tensor, h)[None, :]
-        if tensor == _T_K and spec.k_outlier_frac > 0:
-            x[:, _outlier_channels(spec, h)] *= np.float32(spec.k_outlier_scale)
-        q, s, z = _quantize_head(spec, x, layout, t_valid)
+        std = _channel_std(spec, tensor, h) if spec.channel_std_logu is not None else None
+        outl = _outlier_channels(spec, h) if (tensor == _T_K and spec.k_outlier_frac > 0) else None
+        q = np.zeros((T, D), np.uint8)
+        sshape = (T, D // g) if layout == TOKEN else (T // g, D)
+        s = np.zeros(sshape, np.float16)
+        z = np.zeros(sshape, np.float16)
+        for c0 in range(0, t_valid, _CHUNK):
+            c1 = min(c0 + _CHUNK, t_valid)
+            rows = -(-(c1 - c0) // g) * g if layout == CHANNEL else c1 - c0
+            x = np.zeros((rows, D), np.float32)
+            x[: c1 - c0] = rng.standard_normal((c1 - c0, D), dtype=np.float32)
+            if std is not None:
+                x *= std[None, :]
+            if outl is not None:
+                x[:, outl] *= np.float32(spec.k_outlier_scale)
+            if layout == TOKEN:
+                qc, sc, zc = quantize_minmax(x.reshape(rows, D // g, g), spec.bits, axis=2)
+                q[c0:c1] = qc.reshape(rows, D)
+                s[c0:c1], z[c0:c1] = sc, zc
+            else:
+                valid = np.broadcast_to((np.arange(rows) < c1 - c0).reshape(rows // g, g, 1), (rows // g, g, D))
+                qc, sc, zc = quantize_minmax(x.reshape(rows // g, g, D), spec.bits, axis=1, valid=valid)
+                q[c0:c0 + rows] = qc.reshape(rows, D)
+                s[c0 // g: (c0 + rows) // g], z[c0 // g: (c0 + rows) // g] = sc, zc
         if poison and t_valid < T:
             prng = np.random.default_rng([spec.seed, spec.wid, _T_POISON, tensor, b, h])
             q[t_valid:] = prng.integers(0, 1 << spec.bits, size=(T - t_valid, D), dtype=np.uint8)
@@ -205,7 +211,7 @@ def make_head(spec: Spec, b: int, h: int, seq_len: Optional[int] = None, poison:
                 s[t_valid:] = np.float16(np.nan)
                 z[t_valid:] = np.float16(np.nan)
             else:
-                first_dead = -(-t_valid // spec.group)
+                first_dead = -(-t_valid // g)
                 s[first_dead:] = np.float16(np.nan)
                 z[first_dead:] = np.float16(np.nan)
         out[name + "_codes"] = q
