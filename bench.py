@@ -39,6 +39,8 @@ def parse():
     ap.add_argument("--copies", type=int, default=2, help="independent cache copies rotated over the steps")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy-mib", type=int, default=0,
+                    help="run one plain device copy of this many MiB before warm-up (counter calibration)")
     return ap.parse_args()
 
 
@@ -140,6 +142,14 @@ def main():
         fn(c["q"], c["packed_k"], c["packed_v"], c["k_scale"], c["k_zero"], c["v_scale"], c["v_zero"],
            c["seq_lens"], layout, spec.group, out=o, lse=l)
 
+    if args.calibrate_copy_mib > 0:  # a plain copy of known size, for HBM byte counters
+        n = args.calibrate_copy_mib << 20
+        src = torch.empty(n, dtype=torch.uint8, device=dev_name).fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     for k in range(args.warmup):
         step(k)
     torch.cuda.synchronize()

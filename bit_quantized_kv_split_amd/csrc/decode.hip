@@ -16,9 +16,10 @@
 //   * grid = (ranges S, KV heads, sequences); a work-group of 4 waves owns one
 //     token range of one (sequence, KV head); waves take 64-token tiles (or
 //     g-token units when a channel-wise group is longer than a tile) in turn;
-//   * per tile, lane l streams token l's packed key row and the packed value
-//     words of channels 2l, 2l+1 straight from HBM into registers (dwordx4 /
-//     dwordx2); the next tile's loads are issued before the current tile's math;
+//   * each wave streams its tiles HBM -> LDS with global_load_lds (dwordx4),
+//     NS tiles deep in a per-wave ring, then reads lane l's data (token l's
+//     packed key row, the value words of channels 2l, 2l+1, the quad's scales)
+//     into registers; no registers are held by loads in flight;
 //   * codes become matrix-core operands by one AND-OR per fp16 pair: a code
 //     dropped into the mantissa under a fixed exponent reads as C + q (C a
 //     power of two), and the C*sum(other operand) it adds is removed once per
@@ -122,6 +123,71 @@ struct Codec<4> {
   }
 };
 
+// ---------------------------------------------------------------------------
+// LDS staging.  Tiles arrive in LDS by global_load_lds (direct HBM -> LDS, no
+// registers held while in flight).  The compiler cannot tell the stages of the
+// ring apart and would wait for every such load before any LDS read, so the
+// reads of a staged tile are inline asm and this code places the waits itself:
+// vmcnt(n) for "all but the last n loads issued have landed", then
+// lgkmcnt(0) before the registers are used (touch() makes every later use
+// depend on that wait).
+// ---------------------------------------------------------------------------
+typedef __attribute__((address_space(3))) unsigned char lds_u8;
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const lds_u8*)p;
+}
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+__device__ __forceinline__ void wait_lgkm0() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+template <int OFF>
+__device__ __forceinline__ uint4 lds_b128(uint32_t a) {
+  u32x4 v;
+  asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(v) : "v"(a), "i"(OFF) : "memory");
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
+template <int OFF>
+__device__ __forceinline__ uint2 lds_b64(uint32_t a) {
+  u32x2 v;
+  asm volatile("ds_read_b64 %0, %1 offset:%2" : "=v"(v) : "v"(a), "i"(OFF) : "memory");
+  return make_uint2(v[0], v[1]);
+}
+__device__ __forceinline__ void touch(uint32_t& v) { asm volatile("" : "+v"(v)); }
+__device__ __forceinline__ void touch(uint4& v) { touch(v.x); touch(v.y); touch(v.z); touch(v.w); }
+__device__ __forceinline__ void touch(uint2& v) { touch(v.x); touch(v.y); }
+__device__ __forceinline__ void dma16(const void* g, void* l) {
+  __builtin_amdgcn_global_load_lds(g, (lds_u8*)l, 16, 0, 0);
+}
+__device__ __forceinline__ void dma4(const void* g, void* l) {
+  __builtin_amdgcn_global_load_lds(g, (lds_u8*)l, 4, 0, 0);
+}
+
+// Bytes of one staged tile and its layout: [K rows | V words | token-wise (s, z)].
+template <int BITS, bool KCH, bool VCH, int GRP>
+struct Stage {
+  static constexpr int E = 32 / BITS;
+  static constexpr int KW = kHeadDim / E;            // key words per token
+  static constexpr int VW = kTile / E;               // value token-words per tile
+  static constexpr int NGK = KCH ? 0 : kHeadDim / GRP;
+  static constexpr int NGV = VCH ? 0 : kHeadDim / GRP;
+  static constexpr int KBYTES = KW * 4 * kTile;      // KW/4 chunks of 1 KB
+  static constexpr int VOFF = KBYTES;
+  static constexpr int VBYTES = VW * kHeadDim * 4;   // VW/2 chunks of 1 KB
+  static constexpr int SOFF = VOFF + VBYTES;
+  static constexpr int KSB = 128 * NGK;              // bytes of ks (equally kz) per tile
+  static constexpr int VSOFF = SOFF + 2 * KSB;
+  static constexpr int VSB = 128 * NGV;
+  static constexpr int BYTES = VSOFF + 2 * VSB;
+  static constexpr int LOADS = KW / 4 + VW / 2 + (2 * KSB) / 256 + (2 * VSB) / 256;  // load instructions per tile
+  // ring depth: two work-groups of four waves per CU within 160 KB of LDS
+  static constexpr int NS = (4 * BYTES * 4 <= 76 * 1024) ? 4 : (3 * BYTES * 4 <= 76 * 1024) ? 3 : 2;
+};
+
 // A value the compiler must keep in a VGPR (no literal folding).
 __device__ __forceinline__ uint32_t in_vgpr(uint32_t v) {
   asm volatile("" : "+v"(v));
@@ -211,9 +277,12 @@ __global__ __launch_bounds__(256) void split_decode(const SplitArgs a) {
   }
   const int r1 = min(r0 + a.chunk, T);
 
+  using ST = Stage<BITS, KCH, VCH, GRP>;
+  constexpr int NS = ST::NS;
+  extern __shared__ __align__(16) unsigned char smem[];  // kWaves rings of NS staged tiles
   __shared__ uint2 s_p[kWaves][NGV][4][16];   // P operand of (group, query, quad)
-  __shared__ float s_o[kWaves][4][D];         // epilogue: per-wave partial output
   __shared__ float s_ml[kWaves][2][4];        // epilogue: per-wave (m, l) per query
+  float (*s_o)[4][D] = reinterpret_cast<float (*)[4][D]>(smem);  // epilogue, reuses the rings
 
   const int qd = lane >> 2;   // quad: QK block (tokens 4qd..4qd+3); PV block (channels 8qd..8qd+7)
   const int qn = lane & 3;    // QK output column / PV A-operand row = query head within the KV group
@@ -337,27 +406,112 @@ __global__ __launch_bounds__(256) void split_decode(const SplitArgs a) {
     for (int hh = 0; hh < 2; ++hh) o_acc[hh][0] = o_acc[hh][1] = f4{0.f, 0.f, 0.f, 0.f};
   };
 
-  // ---------------- tile registers, prefetched one tile ahead
+  // ---------------- tiles: staged in a per-wave LDS ring NS deep, read into registers
   struct Tile {
     uint4 k[KW / 4];           // key row of token t0 + lane
     uint2 v[VW];               // value words of channels 2 lane, 2 lane + 1
     uint2 ks[NGK], kz[NGK];    // token-wise key (s, z) of the quad's tokens
     uint2 vs[NGV], vz[NGV];    // token-wise value (s, z) of the quad's tokens
   };
-  auto load_tile = [&](Tile& tl, int t0) {
-    const uint4* kp = reinterpret_cast<const uint4*>(kbase + (size_t)(t0 + lane) * KW);
+  unsigned char* ring = smem + wave * NS * ST::BYTES;
+  const uint32_t ring_lds = lds_addr(ring);
+  // the wave's tiles in order: unit wave, wave + kWaves, ...; TPU tiles per unit
+  auto tile_start = [&](int k) { return r0 + (wave + kWaves * (k / TPU)) * UNIT + (k % TPU) * kTile; };
+  auto issue = [&](int k) {  // HBM -> LDS slot k % NS
+    const int t0 = tile_start(k);
+    unsigned char* st = ring + (k % NS) * ST::BYTES;
 #pragma unroll
-    for (int i = 0; i < KW / 4; ++i) tl.k[i] = kp[i];
+    for (int i = 0; i < KW / 4; ++i)
+      dma16(kbase + (size_t)(t0 + lane) * KW + 4 * i, st + i * 1024);
 #pragma unroll
-    for (int w = 0; w < VW; ++w)
-      tl.v[w] = *reinterpret_cast<const uint2*>(vbase + (size_t)(t0 / E + w) * D + 2 * lane);
+    for (int i = 0; i < VW / 2; ++i)
+      dma16(vbase + (size_t)(t0 / E + 2 * i + (lane >> 5)) * D + 4 * (lane & 31), st + ST::VOFF + i * 1024);
     if constexpr (!KCH) {
-      load_u2(tl.ks, ksb + (size_t)(t0 + 4 * qd) * NGK);
-      load_u2(tl.kz, kzb + (size_t)(t0 + 4 * qd) * NGK);
+#pragma unroll
+      for (int m = 0; m < (2 * ST::KSB) / 256; ++m) {
+        const int o = m * 256 + lane * 4;
+        const unsigned char* src = (o < ST::KSB) ? (const unsigned char*)(ksb + (size_t)t0 * NGK) + o
+                                                 : (const unsigned char*)(kzb + (size_t)t0 * NGK) + (o - ST::KSB);
+        dma4(src, st + ST::SOFF + m * 256);
+      }
     }
     if constexpr (!VCH) {
-      load_u2(tl.vs, vsb + (size_t)(t0 + 4 * qd) * NGV);
-      load_u2(tl.vz, vzb + (size_t)(t0 + 4 * qd) * NGV);
+#pragma unroll
+      for (int m = 0; m < (2 * ST::VSB) / 256; ++m) {
+        const int o = m * 256 + lane * 4;
+        const unsigned char* src = (o < ST::VSB) ? (const unsigned char*)(vsb + (size_t)t0 * NGV) + o
+                                                 : (const unsigned char*)(vzb + (size_t)t0 * NGV) + (o - ST::VSB);
+        dma4(src, st + ST::VSOFF + m * 256);
+      }
+    }
+  };
+  auto read = [&](Tile& tl, int k, int ahead) {  // wait for slot k % NS, LDS -> registers
+    switch (ahead) {  // loads issued after this tile's that may still be in flight
+      case 0: wait_vmcnt<0>(); break;
+      case 1: wait_vmcnt<ST::LOADS>(); break;
+      case 2: wait_vmcnt<(NS > 2 ? 2 : 1) * ST::LOADS>(); break;
+      default: wait_vmcnt<(NS - 1) * ST::LOADS>(); break;
+    }
+    const uint32_t st = ring_lds + (k % NS) * ST::BYTES;
+    const uint32_t ak = st + lane * 16, av = st + ST::VOFF + lane * 8;
+    tl.k[0] = lds_b128<0>(ak);
+    tl.k[1] = lds_b128<1024>(ak);
+    if constexpr (KW / 4 > 2) {
+      tl.k[2 % (KW / 4)] = lds_b128<2048>(ak);
+      tl.k[3 % (KW / 4)] = lds_b128<3072>(ak);
+    }
+    tl.v[0] = lds_b64<0>(av);
+    tl.v[1] = lds_b64<512>(av);
+    tl.v[2] = lds_b64<1024>(av);
+    tl.v[3] = lds_b64<1536>(av);
+    if constexpr (VW > 4) {
+      tl.v[4 % VW] = lds_b64<2048>(av);
+      tl.v[5 % VW] = lds_b64<2560>(av);
+      tl.v[6 % VW] = lds_b64<3072>(av);
+      tl.v[7 % VW] = lds_b64<3584>(av);
+    }
+    if constexpr (!KCH) {
+      const uint32_t as = st + ST::SOFF + qd * 8 * NGK;
+      tl.ks[0] = lds_b64<0>(as);
+      tl.kz[0] = lds_b64<ST::KSB>(as);
+      if constexpr (NGK > 1) {
+        tl.ks[1 % NGK] = lds_b64<8>(as);
+        tl.kz[1 % NGK] = lds_b64<ST::KSB + 8>(as);
+      }
+      if constexpr (NGK > 2) {
+        tl.ks[2 % NGK] = lds_b64<16>(as);
+        tl.kz[2 % NGK] = lds_b64<ST::KSB + 16>(as);
+        tl.ks[3 % NGK] = lds_b64<24>(as);
+        tl.kz[3 % NGK] = lds_b64<ST::KSB + 24>(as);
+      }
+    }
+    if constexpr (!VCH) {
+      const uint32_t as = st + ST::VSOFF + qd * 8 * NGV;
+      tl.vs[0] = lds_b64<0>(as);
+      tl.vz[0] = lds_b64<ST::VSB>(as);
+      if constexpr (NGV > 1) {
+        tl.vs[1 % NGV] = lds_b64<8>(as);
+        tl.vz[1 % NGV] = lds_b64<ST::VSB + 8>(as);
+      }
+      if constexpr (NGV > 2) {
+        tl.vs[2 % NGV] = lds_b64<16>(as);
+        tl.vz[2 % NGV] = lds_b64<ST::VSB + 16>(as);
+        tl.vs[3 % NGV] = lds_b64<24>(as);
+        tl.vz[3 % NGV] = lds_b64<ST::VSB + 24>(as);
+      }
+    }
+    wait_lgkm0();
+#pragma unroll
+    for (int i = 0; i < KW / 4; ++i) touch(tl.k[i]);
+#pragma unroll
+    for (int w = 0; w < VW; ++w) touch(tl.v[w]);
+    if constexpr (!KCH) {
+#pragma unroll
+      for (int j = 0; j < NGK; ++j) { touch(tl.ks[j]); touch(tl.kz[j]); }
+    }
+    if constexpr (!VCH) {
+#pragma unroll
+      for (int j = 0; j < NGV; ++j) { touch(tl.vs[j]); touch(tl.vz[j]); }
     }
   };
 
@@ -542,24 +696,16 @@ __global__ __launch_bounds__(256) void split_decode(const SplitArgs a) {
     }
   };
 
-  // the wave's tiles in order: unit wave, wave + kWaves, ...; TPU tiles per unit
-  auto tile_start = [&](int k) { return r0 + (wave + kWaves * (k / TPU)) * UNIT + (k % TPU) * kTile; };
-  Tile ta, tb;
-  int kt = 0;
-  int t0 = tile_start(0);
-  if (t0 < r1) load_tile(ta, t0);
-  while (t0 < r1) {
-    int t1 = tile_start(kt + 1);
-    if (t1 < r1) load_tile(tb, t1);
-    process(ta, t0);
-    t0 = t1;
-    ++kt;
-    if (t0 >= r1) break;
-    t1 = tile_start(kt + 1);
-    if (t1 < r1) load_tile(ta, t1);
-    process(tb, t0);
-    t0 = t1;
-    ++kt;
+  int nt = 0;  // tiles of this wave
+  while (tile_start(nt) < r1) ++nt;
+#pragma unroll
+  for (int k = 0; k < NS - 1; ++k)
+    if (k < nt) issue(k);
+  for (int k = 0; k < nt; ++k) {
+    if (k + NS - 1 < nt) issue(k + NS - 1);
+    Tile tl;
+    read(tl, k, min(NS - 1, nt - 1 - k));
+    process(tl, tile_start(k));
   }
 
   // ---------------- wave epilogue: totals per query, value-side corrections
@@ -587,6 +733,7 @@ __global__ __launch_bounds__(256) void split_decode(const SplitArgs a) {
       for (int hh = 0; hh < 2; ++hh) o_fin[hh][i] = (o_acc[hh][0][i] + o_acc[hh][1][i]) + corr;
     }
   }
+  __syncthreads();  // every wave is done with its ring before the rings hold s_o
   if (lane < 4) {
     s_ml[wave][0][lane] = m_ref;
     s_ml[wave][1][lane] = l_tot;
@@ -658,8 +805,11 @@ __global__ __launch_bounds__(256) void split_decode(const SplitArgs a) {
 
 template <int BITS, bool KCH, bool VCH, int GRP>
 hipError_t launch_one(int batch, int hkv, const SplitArgs& sa, hipStream_t stream) {
+  using ST = Stage<BITS, KCH, VCH, GRP>;
+  constexpr size_t lds = (size_t)kWaves * ST::NS * ST::BYTES;
+  static_assert(lds >= sizeof(float) * kWaves * 4 * kHeadDim, "rings must hold the epilogue buffer");
   dim3 grid(sa.splits, hkv, batch);
-  hipLaunchKernelGGL((split_decode<BITS, KCH, VCH, GRP>), grid, dim3(kWaves * 64), 0, stream, sa);
+  hipLaunchKernelGGL((split_decode<BITS, KCH, VCH, GRP>), grid, dim3(kWaves * 64), lds, stream, sa);
   return hipGetLastError();
 }
 
