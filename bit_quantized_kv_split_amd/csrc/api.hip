@@ -7,6 +7,7 @@
 #include <string.h>
 
 #include <map>
+#include <algorithm>
 #include <mutex>
 #include <utility>
 
@@ -17,9 +18,13 @@ namespace {
 
 thread_local int g_last_hip_error = 0;
 
+// [counters: counter_bytes][partials: bytes - counter_bytes].  The counter
+// region keeps its place and size until the buffer grows, and holds nothing
+// but counters, so counters that every call leaves at zero stay zero.
 struct Workspace {
   void* ptr = nullptr;
   size_t bytes = 0;
+  size_t counter_bytes = 0;
 };
 
 std::mutex g_ws_mutex;
@@ -91,6 +96,7 @@ void plan(const foscar_dims* d, int layout, int group, int cus, int32_t* splits,
     const long long by_len = (tcap + 8191) / 8192;  // ranges of at most 8192 tokens
     if (s < by_len) s = by_len;
   }
+  if (s > foscar::kMaxSplits) s = foscar::kMaxSplits;
   if (s > units) s = units;
   if (s < 1) s = 1;
   const long long per = (units + s - 1) / s;
@@ -98,30 +104,36 @@ void plan(const foscar_dims* d, int layout, int group, int cus, int32_t* splits,
   *splits = (int32_t)((units + per - 1) / per);
 }
 
-// Workspace: [counters int32 B*Hkv (padded to 256 B)][o_part fp32 B*Hq*S*D][lse_part fp32 B*Hq*S]
+// A call needs one int32 counter per (sequence, KV head), padded to 256 B,
+// and partials o_part fp32 [B*Hq*S*D] then lse_part fp32 [B*Hq*S].
 size_t counter_bytes(const foscar_dims* d) {
   return (((size_t)d->batch * d->num_kv_heads * sizeof(int32_t)) + 255) / 256 * 256;
 }
-size_t workspace_bytes(const foscar_dims* d, int32_t splits) {
+size_t partial_bytes(const foscar_dims* d, int32_t splits) {
   const size_t rows = (size_t)d->batch * d->num_q_heads * splits;
-  return counter_bytes(d) + rows * (foscar::kHeadDim + 1) * sizeof(float);
+  return rows * (foscar::kHeadDim + 1) * sizeof(float);
 }
 
 // Grow-only workspace of (current device, stream).  Growing frees the old
-// buffer after synchronising the device, so no running call still uses it.
-int get_workspace(size_t bytes, hipStream_t stream, void** out) {
+// buffer after synchronising the device, so no running call still uses it,
+// and zeroes the new one.  *counters / *partials point into it.
+int get_workspace(size_t cbytes, size_t pbytes, hipStream_t stream, int32_t** counters, float** partials) {
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return hip_fail(e);
   std::lock_guard<std::mutex> lk(g_ws_mutex);
   Workspace& ws = g_ws[std::make_pair(dev, (void*)stream)];
-  if (ws.bytes < bytes) {
+  if (ws.counter_bytes < cbytes || ws.bytes - ws.counter_bytes < pbytes) {
+    cbytes = std::max(cbytes, ws.counter_bytes);
+    pbytes = std::max(pbytes, ws.bytes - ws.counter_bytes);
+    const size_t bytes = cbytes + pbytes;
     if (ws.ptr) {
       e = hipDeviceSynchronize();
       if (e != hipSuccess) return hip_fail(e);
       (void)hipFree(ws.ptr);
       ws.ptr = nullptr;
       ws.bytes = 0;
+      ws.counter_bytes = 0;
     }
     e = hipMalloc(&ws.ptr, bytes);
     if (e != hipSuccess) {
@@ -137,8 +149,10 @@ int get_workspace(size_t bytes, hipStream_t stream, void** out) {
       return hip_fail(e);
     }
     ws.bytes = bytes;
+    ws.counter_bytes = cbytes;
   }
-  *out = ws.ptr;
+  if (counters) *counters = (int32_t*)ws.ptr;
+  if (partials) *partials = (float*)((char*)ws.ptr + ws.counter_bytes);
   return FOSCAR_OK;
 }
 
@@ -155,8 +169,9 @@ int decode_common(int bits, const foscar_dims* d, const void* q, const void* pk,
   if (e != hipSuccess) return hip_fail(e);
   int32_t splits = 1, chunk = foscar::kTile;
   plan(d, layout, group, compute_units(dev), &splits, &chunk);
-  void* ws = nullptr;
-  rc = get_workspace(workspace_bytes(d, splits), (hipStream_t)stream, &ws);
+  int32_t* counters = nullptr;
+  float* partials = nullptr;
+  rc = get_workspace(counter_bytes(d), partial_bytes(d, splits), (hipStream_t)stream, &counters, &partials);
   if (rc) return rc;
 
   const float sm = d->sm_scale > 0.f ? d->sm_scale : 1.0f / sqrtf((float)d->head_dim);
@@ -171,8 +186,8 @@ int decode_common(int bits, const foscar_dims* d, const void* q, const void* pk,
   sa.seq_lens = seq_lens;
   sa.out = (uint16_t*)out;
   sa.lse = lse;
-  sa.counters = (int32_t*)ws;
-  sa.o_part = (float*)((char*)ws + counter_bytes(d));
+  sa.counters = counters;
+  sa.o_part = partials;
   sa.lse_part = sa.o_part + (size_t)d->batch * d->num_q_heads * splits * foscar::kHeadDim;
   sa.hq = d->num_q_heads;
   sa.hkv = d->num_kv_heads;
@@ -271,8 +286,7 @@ int foscar_workspace_reserve(const foscar_dims* dims, int layout, int group, voi
   if (e != hipSuccess) return hip_fail(e);
   int32_t splits = 1, chunk = 0;
   plan(dims, layout, group, compute_units(dev), &splits, &chunk);
-  void* ws = nullptr;
-  return get_workspace(workspace_bytes(dims, splits), (hipStream_t)stream, &ws);
+  return get_workspace(counter_bytes(dims), partial_bytes(dims, splits), (hipStream_t)stream, nullptr, nullptr);
 }
 
 void foscar_release(void) {

@@ -184,8 +184,13 @@ struct Stage {
   static constexpr int VSB = 128 * NGV;
   static constexpr int BYTES = VSOFF + 2 * VSB;
   static constexpr int LOADS = KW / 4 + VW / 2 + (2 * KSB) / 256 + (2 * VSB) / 256;  // load instructions per tile
-  // ring depth: two work-groups of four waves per CU within 160 KB of LDS
-  static constexpr int NS = (4 * BYTES * 4 <= 76 * 1024) ? 4 : (3 * BYTES * 4 <= 76 * 1024) ? 3 : 2;
+  // ring depth: two work-groups of four waves per CU within 160 KB of LDS;
+  // measured: three tiles in flight per wave hide HBM latency as well as four
+#ifdef FOSCAR_RING_DEPTH
+  static constexpr int NS = FOSCAR_RING_DEPTH;
+#else
+  static constexpr int NS = (3 * BYTES * 4 <= 76 * 1024) ? 3 : 2;
+#endif
 };
 
 // A value the compiler must keep in a VGPR (no literal folding).
@@ -244,6 +249,108 @@ __device__ __forceinline__ void load_u2(uint2 (&dst)[N], const uint16_t* p) {
 // Split kernel.
 // BITS: 2 or 4; KCH / VCH: channel-wise key / value groups; GRP: g.
 // ---------------------------------------------------------------------------
+// Block-wide max / sum of four values per thread (one per query head); every
+// thread receives the result.  s_red holds kWaves x 4 floats.
+template <bool MAX>
+__device__ __forceinline__ void block_reduce4(float (&v)[4], float (*s_red)[4]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) {
+      const float o = __shfl_xor(v[i], m);
+      v[i] = MAX ? fmaxf(v[i], o) : v[i] + o;
+    }
+  const int wave = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) s_red[wave][i] = v[i];
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    float r = s_red[0][i];
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w) r = MAX ? fmaxf(r, s_red[w][i]) : r + s_red[w][i];
+    v[i] = r;
+  }
+  __syncthreads();
+}
+
+__device__ __forceinline__ float coherent_load(const float* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Log-sum-exp merge of the ns ranges of one (sequence, KV head), run by the
+// work-group that finished last: O = sum_s exp(lse_s - M) O_s / sum_s exp(lse_s - M),
+// lse = M + log(sum_s exp(lse_s - M)).  The partials were written by other
+// work-groups, so they are read with device-coherent loads, all issued in
+// parallel (weights first, then 16 partial outputs in flight per thread).
+// s_w: ns * 4 floats of LDS.
+__device__ __forceinline__ void merge_ranges(const SplitArgs& a, int b, int h, int ns, float* s_w) {
+  constexpr int D = kHeadDim;
+  __shared__ float s_red[kWaves][4];
+  const int G = a.g_heads;
+  const size_t row0 = (size_t)b * a.hq + (size_t)h * G;
+  float mx[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+  for (int s2 = threadIdx.x; s2 < ns; s2 += blockDim.x) {
+    float v[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] = (i < G) ? coherent_load(a.lse_part + (row0 + i) * a.splits + s2) : -INFINITY;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      s_w[i * ns + s2] = v[i];
+      mx[i] = fmaxf(mx[i], v[i]);
+    }
+  }
+  block_reduce4<true>(mx, s_red);
+  float den[4] = {0.f, 0.f, 0.f, 0.f};
+  for (int s2 = threadIdx.x; s2 < ns; s2 += blockDim.x)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float w = (i < G) ? __expf(s_w[i * ns + s2] - mx[i]) : 0.f;
+      s_w[i * ns + s2] = w;
+      den[i] += w;
+    }
+  block_reduce4<false>(den, s_red);  // also orders the weight writes before the reads below
+
+  const int c = threadIdx.x & (D - 1);
+  const int i0 = threadIdx.x / D;  // rows i0 and i0 + 2 (blockDim.x == 2 * D)
+  const bool two = i0 + 2 < G;
+  if (i0 >= G) return;
+  const float* op0 = a.o_part + ((row0 + i0) * a.splits) * D + c;
+  const float* op1 = a.o_part + ((row0 + (two ? i0 + 2 : i0)) * a.splits) * D + c;
+  const float* w0 = s_w + i0 * ns;
+  const float* w1 = s_w + (two ? i0 + 2 : i0) * ns;
+  float n0 = 0.f, n1 = 0.f;
+  int s2 = 0;
+  for (; s2 + 8 <= ns; s2 += 8) {
+    float v0[8], v1[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      v0[u] = coherent_load(op0 + (size_t)(s2 + u) * D);
+      v1[u] = two ? coherent_load(op1 + (size_t)(s2 + u) * D) : 0.f;
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      n0 = fmaf(w0[s2 + u], v0[u], n0);
+      n1 = fmaf(w1[s2 + u], v1[u], n1);
+    }
+  }
+  for (; s2 < ns; ++s2) {
+    n0 = fmaf(w0[s2], coherent_load(op0 + (size_t)s2 * D), n0);
+    if (two) n1 = fmaf(w1[s2], coherent_load(op1 + (size_t)s2 * D), n1);
+  }
+  float d0 = den[0], d1 = den[2], m0 = mx[0], m1 = mx[2];
+  if (i0 == 1) {
+    d0 = den[1]; d1 = den[3]; m0 = mx[1]; m1 = mx[3];
+  }
+  a.out[(row0 + i0) * D + c] = to_bf16_rne(n0 / d0);
+  if (c == 0 && a.lse) a.lse[row0 + i0] = m0 + __logf(d0);
+  if (two) {
+    a.out[(row0 + i0 + 2) * D + c] = to_bf16_rne(n1 / d1);
+    if (c == 0 && a.lse) a.lse[row0 + i0 + 2] = m1 + __logf(d1);
+  }
+}
+
 template <int BITS, bool KCH, bool VCH, int GRP>
 __global__ __launch_bounds__(256) void split_decode(const SplitArgs a) {
   using C = Codec<BITS>;
@@ -767,39 +874,31 @@ __global__ __launch_bounds__(256) void split_decode(const SplitArgs a) {
       a.out[row * D + c] = to_bf16_rne(o);
       if (c == 0 && a.lse) a.lse[row] = l_nat;
     } else {
-      a.o_part[(row * a.splits + split) * D + c] = o;
-      if (c == 0) a.lse_part[row * a.splits + split] = l_nat;
+      // device-coherent stores (they bypass this XCD's L2 for the merging work-group)
+      __hip_atomic_store(a.o_part + (row * a.splits + split) * D + c, o, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (c == 0)
+        __hip_atomic_store(a.lse_part + row * a.splits + split, l_nat, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   }
   if (ns == 1) return;
 
   // ---------------- the last range of this (sequence, KV head) merges all ranges
+  // Hand-off without agent-scope fences: those write back and invalidate the
+  // whole L2 of the XCD, once per work-group, and serialise the grid's tail.
+  // Every value that crosses work-groups is a device-coherent atomic access,
+  // so ordering only needs this work-group's stores to have completed
+  // (vmcnt 0 in every wave, then the barrier) before the counter increment,
+  // and the merging work-group's loads to be issued after it read the count.
   __shared__ int s_last;
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
   if (threadIdx.x == 0) {
-    const int done = __hip_atomic_fetch_add(a.counters + bh, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+    const int done = __hip_atomic_fetch_add(a.counters + bh, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     s_last = (done == ns - 1);
   }
   __syncthreads();
   if (!s_last) return;
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-  for (int idx = threadIdx.x; idx < a.g_heads * D; idx += blockDim.x) {
-    const int i = idx / D, c = idx % D;
-    const size_t row = (size_t)b * a.hq + h * a.g_heads + i;
-    const float* lp = a.lse_part + row * a.splits;
-    const float* op = a.o_part + row * a.splits * D + c;
-    float M = -INFINITY;
-    for (int s2 = 0; s2 < ns; ++s2) M = fmaxf(M, lp[s2]);
-    float num = 0.f, den = 0.f;
-    for (int s2 = 0; s2 < ns; ++s2) {
-      const float w = __expf(lp[s2] - M);
-      num = fmaf(w, op[(size_t)s2 * D], num);
-      den += w;
-    }
-    a.out[row * D + c] = to_bf16_rne(num / den);
-    if (c == 0 && a.lse) a.lse[row] = M + __logf(den);
-  }
+  merge_ranges(a, b, h, ns, reinterpret_cast<float*>(smem));
   if (threadIdx.x == 0) a.counters[bh] = 0;  // ready for the next call on this workspace
 }
 
@@ -808,6 +907,7 @@ hipError_t launch_one(int batch, int hkv, const SplitArgs& sa, hipStream_t strea
   using ST = Stage<BITS, KCH, VCH, GRP>;
   constexpr size_t lds = (size_t)kWaves * ST::NS * ST::BYTES;
   static_assert(lds >= sizeof(float) * kWaves * 4 * kHeadDim, "rings must hold the epilogue buffer");
+  static_assert(lds >= sizeof(float) * 4 * kMaxSplits, "rings must hold the merge weights");
   dim3 grid(sa.splits, hkv, batch);
   hipLaunchKernelGGL((split_decode<BITS, KCH, VCH, GRP>), grid, dim3(kWaves * 64), lds, stream, sa);
   return hipGetLastError();

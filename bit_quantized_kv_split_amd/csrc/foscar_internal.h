@@ -10,6 +10,7 @@ constexpr int kHeadDim = 128;   // D
 constexpr int kTile = 64;       // tokens per wave tile (16 quads of 4)
 constexpr int kWaves = 4;       // waves per work-group
 constexpr int kMaxG = 4;        // query heads per KV head served by one wave
+constexpr int kMaxSplits = 512;  // ranges per sequence (the merge keeps 4 weights per range in LDS)
 
 // Arguments of the decode kernel (one work-group per (range, KV head, sequence)).
 // The last work-group to finish the ranges of a (sequence, KV head) merges them.

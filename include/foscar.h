@@ -150,7 +150,8 @@ void foscar_release(void);
 
 /* Split plan the decode entry points use for these arguments: *splits = number
  * of key/value ranges per (sequence, KV head), *chunk = tokens per range.
- * FOSCAR_SPLITS=<n> in the environment forces n ranges (tuning and tests). */
+ * FOSCAR_SPLITS=<n> in the environment forces n ranges (tuning and tests);
+ * the count is capped at 512 ranges and at one range per 64-token unit. */
 int foscar_split_plan(const foscar_dims* dims, int layout, int group, int32_t* splits, int32_t* chunk);
 
 const char* foscar_strerror(int code);

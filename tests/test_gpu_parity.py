@@ -89,7 +89,7 @@ def test_gqa_ratios(G):
     check(out, lse, ro, rl, spec.name, vsc)
 
 
-@pytest.mark.parametrize("splits", ["1", "2", "7", "auto"])
+@pytest.mark.parametrize("splits", ["1", "2", "7", "17", "32", "auto"])
 def test_split_count_invariance(splits, monkeypatch):
     spec = _spec("c5_ragged_int2_g64", batch=4, num_q_heads=8, num_kv_heads=2, max_seq_len=2048, ragged_lo=100)
     if splits != "auto":
@@ -100,6 +100,41 @@ def test_split_count_invariance(splits, monkeypatch):
     out, lse = run(spec, dev)
     ro, rl, vsc = oracle_all(spec, q, lens)
     check(out, lse, ro, rl, f"splits={splits}", vsc)
+
+
+def test_many_ranges(monkeypatch):
+    """More ranges than the merge handles in one batch of loads, up to the
+    512-range cap (asking for 600 gives 512 ranges of 128 tokens)."""
+    spec = _spec("c5_ragged_int2_g64", batch=2, num_q_heads=8, num_kv_heads=2, max_seq_len=65536, ragged_lo=20000)
+    monkeypatch.setenv("FOSCAR_SPLITS", "600")
+    dev, q, lens = stage_spec(spec)
+    import bit_quantized_kv_split_amd as fos
+    dims = fos.make_dims(spec.batch, spec.num_q_heads, spec.num_kv_heads, spec.head_dim, spec.max_seq_len)
+    assert fos.foscar_split_plan(dims, fos.layout_bits(spec.k_layout, spec.v_layout), spec.group) == (512, 128)
+    out, lse = run(spec, dev)
+    ro, rl, vsc = oracle_all(spec, q, lens)
+    check(out, lse, ro, rl, "512 ranges", vsc)
+
+
+def test_workspace_reuse_across_shapes(monkeypatch):
+    """A call with few (sequence, KV head) pairs and many ranges, then one with
+    many pairs and few ranges on the same workspace: the second call's range
+    counters must not land on the first call's partial results."""
+    import bit_quantized_kv_split_amd as fos
+    fos.foscar_release()
+    first = _spec("c5_ragged_int2_g64", batch=1, num_q_heads=4, num_kv_heads=1, max_seq_len=16384, ragged_lo=16384)
+    monkeypatch.setenv("FOSCAR_SPLITS", "256")
+    dev, q, lens = stage_spec(first)
+    out, lse = run(first, dev)
+    ro, rl, vsc = oracle_all(first, q, lens)
+    check(out, lse, ro, rl, "many ranges", vsc)
+    second = _spec("c2_paper_int2", batch=16, num_q_heads=32, num_kv_heads=8, max_seq_len=512)
+    monkeypatch.setenv("FOSCAR_SPLITS", "2")
+    dev, q, lens = stage_spec(second)
+    for _ in range(2):
+        out, lse = run(second, dev)
+        ro, rl, vsc = oracle_all(second, q, lens)
+        check(out, lse, ro, rl, "many pairs after many ranges", vsc)
 
 
 FULL = ["c2_paper_int2", "c2_paper_int4", "c3_long_int2", "c4_channel_int2", "c4_channel_int4",
