@@ -91,7 +91,7 @@ void plan(const foscar_dims* d, int layout, int group, int cus, int32_t* splits,
   if (env && atoi(env) > 0) {
     s = atoi(env);
   } else {
-    const long long target = 2LL * cus;  // one round of work-groups (two resident per CU)
+    const long long target = 4LL * cus;  // one round of work-groups at four resident per CU
     if (bh > 0) s = (target + bh - 1) / bh;
     const long long by_len = (tcap + 8191) / 8192;  // ranges of at most 8192 tokens
     if (s < by_len) s = by_len;

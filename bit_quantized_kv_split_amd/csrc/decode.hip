@@ -38,6 +38,8 @@
 //     release/acquire counter), so one decode step is one kernel launch.
 #include <math.h>
 
+#include <type_traits>
+
 #include "foscar_internal.h"
 
 namespace foscar {
@@ -160,14 +162,26 @@ __device__ __forceinline__ uint2 lds_b64(uint32_t a) {
 __device__ __forceinline__ void touch(uint32_t& v) { asm volatile("" : "+v"(v)); }
 __device__ __forceinline__ void touch(uint4& v) { touch(v.x); touch(v.y); touch(v.z); touch(v.w); }
 __device__ __forceinline__ void touch(uint2& v) { touch(v.x); touch(v.y); }
-__device__ __forceinline__ void dma16(const void* g, void* l) {
-  __builtin_amdgcn_global_load_lds(g, (lds_u8*)l, 16, 0, 0);
+// Buffer resource over `bytes` bytes at p (raw, unswizzled).  Loads past the
+// end read zero, so a tile that runs past the cache capacity stays in bounds.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, (int)bytes, 0x00020000);
 }
-__device__ __forceinline__ void dma4(const void* g, void* l) {
-  __builtin_amdgcn_global_load_lds(g, (lds_u8*)l, 4, 0, 0);
+// HBM -> LDS: each lane's 16 (4) bytes at voff + soff land at l + 16 (4) * lane.
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff, void* l) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_u8*)l, 16, voff, soff, 0, 0);
+}
+__device__ __forceinline__ void dma4(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff, void* l) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_u8*)l, 4, voff, soff, 0, 0);
 }
 
-// Bytes of one staged tile and its layout: [K rows | V words | token-wise (s, z)].
+// Bytes of one staged tile and its layout:
+//   [ks | kz | vs | vz (token-wise sides only)][K rows][V words].
+// Scales are loaded in 256-byte blocks (one dword per lane).  A side with one
+// group per token has 128 bytes per tile, so the upper half of its block lands
+// on the next region; loads into one wave's LDS complete in issue order, so
+// issuing the scale blocks first and the K rows after them leaves every region
+// holding its own data.
 template <int BITS, bool KCH, bool VCH, int GRP>
 struct Stage {
   static constexpr int E = 32 / BITS;
@@ -175,21 +189,25 @@ struct Stage {
   static constexpr int VW = kTile / E;               // value token-words per tile
   static constexpr int NGK = KCH ? 0 : kHeadDim / GRP;
   static constexpr int NGV = VCH ? 0 : kHeadDim / GRP;
-  static constexpr int KBYTES = KW * 4 * kTile;      // KW/4 chunks of 1 KB
-  static constexpr int VOFF = KBYTES;
-  static constexpr int VBYTES = VW * kHeadDim * 4;   // VW/2 chunks of 1 KB
-  static constexpr int SOFF = VOFF + VBYTES;
   static constexpr int KSB = 128 * NGK;              // bytes of ks (equally kz) per tile
-  static constexpr int VSOFF = SOFF + 2 * KSB;
   static constexpr int VSB = 128 * NGV;
-  static constexpr int BYTES = VSOFF + 2 * VSB;
-  static constexpr int LOADS = KW / 4 + VW / 2 + (2 * KSB) / 256 + (2 * VSB) / 256;  // load instructions per tile
-  // ring depth: two work-groups of four waves per CU within 160 KB of LDS;
-  // measured: three tiles in flight per wave hide HBM latency as well as four
+  static constexpr int SOFF = 0;
+  static constexpr int VSOFF = SOFF + 2 * KSB;
+  static constexpr int KOFF = VSOFF + 2 * VSB;
+  static constexpr int KBYTES = KW * 4 * kTile;      // KW/4 chunks of 1 KB
+  static constexpr int VOFF = KOFF + KBYTES;
+  static constexpr int VBYTES = VW * kHeadDim * 4;   // VW/2 chunks of 1 KB
+  static constexpr int BYTES = VOFF + VBYTES;
+  static constexpr int KSL = (KSB + 255) / 256;      // 256-byte scale loads per array
+  static constexpr int VSL = (VSB + 255) / 256;
+  static constexpr int LOADS = KW / 4 + VW / 2 + 2 * KSL + 2 * VSL;  // load instructions per tile
+  static_assert(KOFF % 16 == 0, "K rows need 16-byte alignment");
+  // ring depth: two tiles in flight per wave; with four waves per work-group
+  // and four work-groups per CU the INT2 rings fit the 160 KB of LDS
 #ifdef FOSCAR_RING_DEPTH
   static constexpr int NS = FOSCAR_RING_DEPTH;
 #else
-  static constexpr int NS = (3 * BYTES * 4 <= 76 * 1024) ? 3 : 2;
+  static constexpr int NS = 2;
 #endif
 };
 
@@ -223,11 +241,26 @@ __device__ __forceinline__ void halves(float v, float& h0, float& h1) {
   h0 = lo ? v : o;
   h1 = lo ? o : v;
 }
+// max over rows (0,1) and (2,3) of 16 lanes: v_permlane16_swap trades the odd
+// rows of its first operand with the even rows of its second.  Like DPP, a
+// cross-lane read needs two wait states after the VALU write of its operands,
+// which the compiler cannot see through inline asm.
+__device__ __forceinline__ float max_row_pairs(float v) {
+  float a = v, b = v;
+  asm volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1" : "+v"(a), "+v"(b));
+  return fmaxf(a, b);
+}
+// max over the two half-waves: v_permlane32_swap trades the upper half of its
+// first operand with the lower half of its second
+__device__ __forceinline__ float max_halves(float v) {
+  float a = v, b = v;
+  asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(a), "+v"(b));
+  return fmaxf(a, b);
+}
 __device__ __forceinline__ float wave_max_same_query(float v) {
   v = fmaxf(v, dpp<0x124>(v));  // row_ror:4
   v = fmaxf(v, dpp<0x128>(v));  // row_ror:8
-  v = fmaxf(v, xor16(v));
-  return fmaxf(v, xor32(v));
+  return max_halves(max_row_pairs(v));
 }
 template <int SPAN>  // sum over the lanes of one query head within SPAN lanes (32: half-wave, 64: wave)
 __device__ __forceinline__ float sum_same_query(float v) {
@@ -358,6 +391,7 @@ __global__ __launch_bounds__(256) void split_decode(const SplitArgs a) {
   constexpr int E = C::E;
   constexpr int PAIRS = C::PAIRS;
   constexpr int KPW = PAIRS / 2;           // k-steps (of 4 channels / 4 tokens) per word
+  constexpr int QPW = KPW / 2;             // 16-byte operand reads per word (two k-steps each)
   constexpr int KW = D / E;                // key words per token
   constexpr int VW = kTile / E;            // value token-words per tile
   constexpr int NGK = KCH ? 1 : D / GRP;   // key groups per token
@@ -366,7 +400,7 @@ __global__ __launch_bounds__(256) void split_decode(const SplitArgs a) {
   constexpr int TPU = UNIT / kTile;
 
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int split = blockIdx.x;
   const int h = blockIdx.y;
   const int b = blockIdx.z;
@@ -399,31 +433,36 @@ __global__ __launch_bounds__(256) void split_decode(const SplitArgs a) {
 
   // ---- query prologue: bf16 -> fp16 pairs (channels 2j, 2j+1); exact for values in the fp16 range
   const uint4* qrow = reinterpret_cast<const uint4*>(a.q + ((size_t)b * a.hq + h * a.g_heads + (qvalid ? qn : 0)) * D);
-  uint32_t q16[KCH ? 1 : D / 2];
-  // token-wise K: per group, sigma' * sum(Q) and sigma' * sum(Q * C)  (C = operand bias of each channel)
+  // token-wise K: the work-group's query block as the QK^T B operand in LDS (row = query head;
+  // rows padded by 16 B so the four rows of one read fall in different banks), and per group
+  // sigma' * sum(Q) and sigma' * sum(Q * C)  (C = operand bias of each channel)
+  __shared__ __align__(16) uint32_t s_q[KCH ? 1 : 4][KCH ? 4 : D / 2 + 4];
+  __shared__ float s_kq[2][4][NGK];
   float kq_sum[NGK], kq_bias[NGK];
-#pragma unroll
-  for (int j = 0; j < NGK; ++j) kq_sum[j] = kq_bias[j] = 0.f;
   if constexpr (!KCH) {
+    {  // wave i converts query head i, lane j its channel pair j
+      const int qi = wave, pj = lane;
+      uint32_t w = 0;
+      if (qi < a.g_heads) w = reinterpret_cast<const uint32_t*>(a.q + ((size_t)b * a.hq + h * a.g_heads + qi) * D)[pj];
+      const uint32_t q2 = pack_f16(__builtin_bit_cast(float, w << 16), __builtin_bit_cast(float, w & 0xFFFF0000u));
+      s_q[qi][pj] = q2;
+      float s2 = half_lo(q2) + half_hi(q2);
+      float c2 = C::bias(pj % PAIRS) * s2;
 #pragma unroll
-    for (int i = 0; i < D / 8; ++i) {
-      uint4 v = qrow[i];
-      if (!qvalid) v = make_uint4(0, 0, 0, 0);
-      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        q16[4 * i + j] = pack_f16(__builtin_bit_cast(float, w[j] << 16), __builtin_bit_cast(float, w[j] & 0xFFFF0000u));
+      for (int m = 1; m < GRP / 2; m <<= 1) {  // sum over the GRP/2 pairs of the group
+        s2 += __shfl_xor(s2, m);
+        c2 += __shfl_xor(c2, m);
+      }
+      if (pj % (GRP / 2) == 0) {
+        s_kq[0][qi][pj / (GRP / 2)] = s2 * sl2;
+        s_kq[1][qi][pj / (GRP / 2)] = c2 * sl2;
+      }
     }
-#pragma unroll
-    for (int j = 0; j < D / 2; ++j) {
-      const float s2 = half_lo(q16[j]) + half_hi(q16[j]);
-      kq_sum[(2 * j) / GRP] += s2;
-      kq_bias[(2 * j) / GRP] += C::bias(j % PAIRS) * s2;
-    }
+    __syncthreads();
 #pragma unroll
     for (int j = 0; j < NGK; ++j) {
-      kq_sum[j] *= sl2;
-      kq_bias[j] *= sl2;
+      kq_sum[j] = s_kq[0][qn][j];
+      kq_bias[j] = s_kq[1][qn][j];
     }
   }
   // channel-wise K (operand-fold on Q): Q~ = Q * s_tau carried exactly as an fp16 pair hi + lo
@@ -456,10 +495,16 @@ __global__ __launch_bounds__(256) void split_decode(const SplitArgs a) {
 
   const uint32_t* kbase = a.pk + bh * (size_t)a.tcap * KW;
   const uint32_t* vbase = a.pv + bh * (size_t)(a.tcap / E) * D;
+  const __amdgpu_buffer_rsrc_t rk = rsrc(kbase, (uint32_t)a.tcap * KW * 4);
+  const __amdgpu_buffer_rsrc_t rv = rsrc(vbase, (uint32_t)(a.tcap / E) * D * 4);
   const uint16_t* ksb = a.ks + bh * (size_t)(KCH ? (a.tcap / GRP) * D : a.tcap * NGK);
   const uint16_t* kzb = a.kz + bh * (size_t)(KCH ? (a.tcap / GRP) * D : a.tcap * NGK);
   const uint16_t* vsb = a.vs + bh * (size_t)(VCH ? (a.tcap / GRP) * D : a.tcap * NGV);
   const uint16_t* vzb = a.vz + bh * (size_t)(VCH ? (a.tcap / GRP) * D : a.tcap * NGV);
+  const __amdgpu_buffer_rsrc_t rks = rsrc(ksb, KCH ? 0u : (uint32_t)a.tcap * NGK * 2);
+  const __amdgpu_buffer_rsrc_t rkz = rsrc(kzb, KCH ? 0u : (uint32_t)a.tcap * NGK * 2);
+  const __amdgpu_buffer_rsrc_t rvs = rsrc(vsb, VCH ? 0u : (uint32_t)a.tcap * NGV * 2);
+  const __amdgpu_buffer_rsrc_t rvz = rsrc(vzb, VCH ? 0u : (uint32_t)a.tcap * NGV * 2);
 
   // rescale every accumulator of this wave after the reference max of a query moved
   auto rescale = [&](float alpha) {
@@ -524,33 +569,26 @@ __global__ __launch_bounds__(256) void split_decode(const SplitArgs a) {
   const uint32_t ring_lds = lds_addr(ring);
   // the wave's tiles in order: unit wave, wave + kWaves, ...; TPU tiles per unit
   auto tile_start = [&](int k) { return r0 + (wave + kWaves * (k / TPU)) * UNIT + (k % TPU) * kTile; };
-  auto issue = [&](int k) {  // HBM -> LDS slot k % NS
-    const int t0 = tile_start(k);
+  auto issue = [&](int k) {  // HBM -> LDS slot k % NS (per-lane offsets fixed, per-tile offset scalar)
+    const uint32_t t0 = (uint32_t)tile_start(k);
     unsigned char* st = ring + (k % NS) * ST::BYTES;
-#pragma unroll
-    for (int i = 0; i < KW / 4; ++i)
-      dma16(kbase + (size_t)(t0 + lane) * KW + 4 * i, st + i * 1024);
-#pragma unroll
-    for (int i = 0; i < VW / 2; ++i)
-      dma16(vbase + (size_t)(t0 / E + 2 * i + (lane >> 5)) * D + 4 * (lane & 31), st + ST::VOFF + i * 1024);
+    // scale blocks first, in layout order (see Stage), then K rows and V words
     if constexpr (!KCH) {
 #pragma unroll
-      for (int m = 0; m < (2 * ST::KSB) / 256; ++m) {
-        const int o = m * 256 + lane * 4;
-        const unsigned char* src = (o < ST::KSB) ? (const unsigned char*)(ksb + (size_t)t0 * NGK) + o
-                                                 : (const unsigned char*)(kzb + (size_t)t0 * NGK) + (o - ST::KSB);
-        dma4(src, st + ST::SOFF + m * 256);
-      }
+      for (int m = 0; m < ST::KSL; ++m) dma4(rks, 4 * lane + 256 * m, t0 * NGK * 2, st + ST::SOFF + m * 256);
+#pragma unroll
+      for (int m = 0; m < ST::KSL; ++m) dma4(rkz, 4 * lane + 256 * m, t0 * NGK * 2, st + ST::SOFF + ST::KSB + m * 256);
     }
     if constexpr (!VCH) {
 #pragma unroll
-      for (int m = 0; m < (2 * ST::VSB) / 256; ++m) {
-        const int o = m * 256 + lane * 4;
-        const unsigned char* src = (o < ST::VSB) ? (const unsigned char*)(vsb + (size_t)t0 * NGV) + o
-                                                 : (const unsigned char*)(vzb + (size_t)t0 * NGV) + (o - ST::VSB);
-        dma4(src, st + ST::VSOFF + m * 256);
-      }
+      for (int m = 0; m < ST::VSL; ++m) dma4(rvs, 4 * lane + 256 * m, t0 * NGV * 2, st + ST::VSOFF + m * 256);
+#pragma unroll
+      for (int m = 0; m < ST::VSL; ++m) dma4(rvz, 4 * lane + 256 * m, t0 * NGV * 2, st + ST::VSOFF + ST::VSB + m * 256);
     }
+#pragma unroll
+    for (int i = 0; i < KW / 4; ++i) dma16(rk, lane * KW * 4 + 16 * i, t0 * KW * 4, st + ST::KOFF + i * 1024);
+#pragma unroll
+    for (int i = 0; i < VW / 2; ++i) dma16(rv, 16 * lane + 1024 * i, (t0 / E) * D * 4, st + ST::VOFF + i * 1024);
   };
   auto read = [&](Tile& tl, int k, int ahead) {  // wait for slot k % NS, LDS -> registers
     switch (ahead) {  // loads issued after this tile's that may still be in flight
@@ -560,7 +598,7 @@ __global__ __launch_bounds__(256) void split_decode(const SplitArgs a) {
       default: wait_vmcnt<(NS - 1) * ST::LOADS>(); break;
     }
     const uint32_t st = ring_lds + (k % NS) * ST::BYTES;
-    const uint32_t ak = st + lane * 16, av = st + ST::VOFF + lane * 8;
+    const uint32_t ak = st + ST::KOFF + lane * 16, av = st + ST::VOFF + lane * 8;
     tl.k[0] = lds_b128<0>(ak);
     tl.k[1] = lds_b128<1024>(ak);
     if constexpr (KW / 4 > 2) {
@@ -622,8 +660,8 @@ __global__ __launch_bounds__(256) void split_decode(const SplitArgs a) {
     }
   };
 
-  auto process = [&](const Tile& tl, const int t0) {
-    const bool tail = t0 + kTile > T;
+  auto process = [&](const Tile& tl, const int t0, auto tail_c) {
+    constexpr bool tail = decltype(tail_c)::value;  // the tile reaches past T: mask its last tokens
     // ---------------- channel-wise K: operand Q~ for the group of this lane's quad
     if constexpr (KCH) {
       const int tau = (t0 + 4 * qd) / GRP;
@@ -664,9 +702,27 @@ __global__ __launch_bounds__(256) void split_decode(const SplitArgs a) {
     f4 sacc[NCH];
 #pragma unroll
     for (int j = 0; j < NCH; ++j) sacc[j] = f4{0.f, 0.f, 0.f, 0.f};
+    // B operand rows from LDS, re-read every tile (an opaque zero offset keeps
+    // the compiler from hoisting them into 64 live registers)
+    // One segment per key word (its KPW k-steps); the compiler may not move work
+    // across segments, which bounds the live operands, and each segment reads
+    // the next one's B operands from LDS ahead of use.
+    const uint4* qsrc = reinterpret_cast<const uint4*>(&s_q[KCH ? 0 : qn][0]) + (int)in_vgpr(0u);
+    uint4 qcur[QPW], qnxt[QPW];
+    if constexpr (!KCH) {
+#pragma unroll
+      for (int i = 0; i < QPW; ++i) qcur[i] = qsrc[i];
+    }
 #pragma unroll
     for (int d = 0; d < KW; ++d) {
-      const uint32_t wrd = (d % 4 == 0) ? tl.k[d / 4].x : (d % 4 == 1) ? tl.k[d / 4].y : (d % 4 == 2) ? tl.k[d / 4].z : tl.k[d / 4].w;
+      if constexpr (!KCH) {
+        if (d + 1 < KW) {
+#pragma unroll
+          for (int i = 0; i < QPW; ++i) qnxt[i] = qsrc[(d + 1) * QPW + i];
+        }
+      }
+      uint32_t wrd = (d % 4 == 0) ? tl.k[d / 4].x : (d % 4 == 1) ? tl.k[d / 4].y : (d % 4 == 2) ? tl.k[d / 4].z : tl.k[d / 4].w;
+      touch(wrd);  // ties the unpacking to this segment
       uint32_t p[PAIRS];
       C::extract(wrd, kc, p);
 #pragma unroll
@@ -678,9 +734,16 @@ __global__ __launch_bounds__(256) void split_decode(const SplitArgs a) {
           sacc[1] = __builtin_amdgcn_mfma_f32_4x4x4f16(av, cat4(qt_lo[2 * j], qt_lo[2 * j + 1]), sacc[1], 0, 0, 0);
         } else {
           const int ch = (NGK == 1) ? (j & 1) : (4 * j) / GRP;
-          sacc[ch] = __builtin_amdgcn_mfma_f32_4x4x4f16(av, cat4(q16[2 * j], q16[2 * j + 1]), sacc[ch], 0, 0, 0);
+          const uint4 qq = qcur[sg / 2];
+          const h4 bv = (sg & 1) ? cat4(qq.z, qq.w) : cat4(qq.x, qq.y);
+          sacc[ch] = __builtin_amdgcn_mfma_f32_4x4x4f16(av, bv, sacc[ch], 0, 0, 0);
         }
       }
+      if constexpr (!KCH) {
+#pragma unroll
+        for (int i = 0; i < QPW; ++i) qcur[i] = qnxt[i];
+      }
+      __builtin_amdgcn_sched_barrier(0);
     }
 
     // ---------------- key-side fold (before the softmax) -> scores in log2 units
@@ -753,30 +816,33 @@ __global__ __launch_bounds__(256) void split_decode(const SplitArgs a) {
       pb_part = dot2(p23, cv1h, dot2(p01, cv0h, pb_part));
     }
     __builtin_amdgcn_wave_barrier();
-    // gathered A operands: P of query qn for all 16 quads (value group of this lane's channels)
-    uint2 pa[16];
-    {
-      const int jv = VCH ? 0 : (8 * qd) / GRP;
-      const uint4* src = reinterpret_cast<const uint4*>(&s_p[wave][jv][qn][0]);
+    __builtin_amdgcn_sched_barrier(0);
+    // A operands: P of query qn for the 16 quads (value group of this lane's
+    // channels), gathered from LDS one segment ahead of use
+    const int jv = VCH ? 0 : (8 * qd) / GRP;
+    const uint4* psrc = reinterpret_cast<const uint4*>(&s_p[wave][jv][qn][0]);
+    uint4 pcur[QPW], pnxt[QPW];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const uint4 v = src[i];
-        pa[2 * i] = make_uint2(v.x, v.y);
-        pa[2 * i + 1] = make_uint2(v.z, v.w);
-      }
-    }
-    __builtin_amdgcn_wave_barrier();
+    for (int i = 0; i < QPW; ++i) pcur[i] = psrc[i];
 
     // ---------------- P V on the matrix cores (+ acc-fold of channel-wise value groups)
 #pragma unroll
     for (int w = 0; w < VW; ++w) {
+      if (w + 1 < VW) {
+#pragma unroll
+        for (int i = 0; i < QPW; ++i) pnxt[i] = psrc[(w + 1) * QPW + i];
+      }
+      uint32_t vx = tl.v[w].x, vy = tl.v[w].y;
+      touch(vx);  // ties the unpacking to this segment
+      touch(vy);
       uint32_t p0[PAIRS], p1[PAIRS];
-      C::extract(tl.v[w].x, kc, p0);  // channel 2*lane
-      C::extract(tl.v[w].y, kc, p1);  // channel 2*lane + 1
+      C::extract(vx, kc, p0);  // channel 2*lane
+      C::extract(vy, kc, p1);  // channel 2*lane + 1
 #pragma unroll
       for (int sg = 0; sg < KPW; ++sg) {
         const int bq = w * KPW + sg;  // quad: tokens 4bq .. 4bq+3 of the tile
-        const h4 av = cat4(pa[bq].x, pa[bq].y);
+        const uint4 pp = pcur[sg / 2];
+        const h4 av = (sg & 1) ? cat4(pp.z, pp.w) : cat4(pp.x, pp.y);
         f4& a0 = o_acc[0][bq & 1];
         f4& a1 = o_acc[1][bq & 1];
         a0 = __builtin_amdgcn_mfma_f32_4x4x4f16(av, cat4(p0[2 * sg], p0[2 * sg + 1]), a0, 0, 0, 0);
@@ -787,7 +853,11 @@ __global__ __launch_bounds__(256) void split_decode(const SplitArgs a) {
           }
         }
       }
+#pragma unroll
+      for (int i = 0; i < QPW; ++i) pcur[i] = pnxt[i];
+      __builtin_amdgcn_sched_barrier(0);
     }
+    __builtin_amdgcn_wave_barrier();
     if constexpr (VCH) {
       if (GRP == 32) {
         if (t0 + 32 < T) fold_value_group(t0 / GRP + 1, 1);
@@ -812,7 +882,11 @@ __global__ __launch_bounds__(256) void split_decode(const SplitArgs a) {
     if (k + NS - 1 < nt) issue(k + NS - 1);
     Tile tl;
     read(tl, k, min(NS - 1, nt - 1 - k));
-    process(tl, tile_start(k));
+    const int t0k = tile_start(k);
+    if (t0k + kTile > T)
+      process(tl, t0k, std::true_type{});
+    else
+      process(tl, t0k, std::false_type{});
   }
 
   // ---------------- wave epilogue: totals per query, value-side corrections
