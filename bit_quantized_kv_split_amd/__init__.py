@@ -76,9 +76,35 @@ def _require(t, name, dtype, device):
         raise ValueError(f"{name} must be contiguous")
 
 
-def _decode(bits, q, packed_k, packed_v, k_scale, k_zero, v_scale, v_zero, seq_lens, layout, group,
-            out=None, lse=None, sm_scale=0.0, stream=None):
+class DecodeCall:
+    """One decode step with its arguments checked and marshalled once.
+
+    Calling the object launches the step again on the stream it was prepared
+    for and returns (out, lse); the tensors it was built from must keep their
+    storage (they are referenced, not copied), and their contents may change
+    between calls.  This is the path for a serving loop: a call is one C call.
+    """
+
+    __slots__ = ("_fn", "_args", "_name", "_dev", "out", "lse", "_keep")
+
+    def __call__(self):
+        import torch
+        if torch.cuda.current_device() != self._dev:
+            with torch.cuda.device(self._dev):
+                rc = self._fn(*self._args)
+        else:
+            rc = self._fn(*self._args)
+        if rc != FOSCAR_OK:
+            _check(rc, self._name)
+        return self.out, self.lse
+
+
+def prepare_decode(bits, q, packed_k, packed_v, k_scale, k_zero, v_scale, v_zero, seq_lens, layout, group,
+                   out=None, lse=None, sm_scale=0.0, stream=None):
+    """Check and marshal a decode step (arguments as foscar_decode_int2/4); returns a DecodeCall."""
     import torch
+    if bits not in (2, 4):
+        raise ValueError(f"bits must be 2 or 4, got {bits}")
     lib = _lib.load()
     dev = q.device
     _require(q, "q", torch.bfloat16, dev)
@@ -96,13 +122,23 @@ def _decode(bits, q, packed_k, packed_v, k_scale, k_zero, v_scale, v_zero, seq_l
     _require(out, "out", torch.bfloat16, dev)
     _require(lse, "lse", torch.float32, dev)
     dims = make_dims(B, Hq, Hkv, D, Tcap, sm_scale)
-    fn = lib.foscar_decode_int2 if bits == 2 else lib.foscar_decode_int4
+    call = DecodeCall()
+    call._fn = lib.foscar_decode_int2 if bits == 2 else lib.foscar_decode_int4
     with torch.cuda.device(dev):
-        rc = fn(ctypes.byref(dims), _ptr(q), _ptr(packed_k), _ptr(packed_v), _ptr(k_scale), _ptr(k_zero),
-                _ptr(v_scale), _ptr(v_zero), _ptr(seq_lens), int(layout), int(group), _ptr(out), _ptr(lse),
-                _stream(stream))
-    _check(rc, f"foscar_decode_int{bits}")
-    return out, lse
+        st = _stream(stream)
+    call._args = (ctypes.byref(dims), _ptr(q), _ptr(packed_k), _ptr(packed_v), _ptr(k_scale), _ptr(k_zero),
+                  _ptr(v_scale), _ptr(v_zero), _ptr(seq_lens), int(layout), int(group), _ptr(out), _ptr(lse), st)
+    call._name = f"foscar_decode_int{bits}"
+    call._dev = dev.index if dev.index is not None else torch.cuda.current_device()
+    call.out, call.lse = out, lse
+    call._keep = (dims, q, packed_k, packed_v, k_scale, k_zero, v_scale, v_zero, seq_lens)
+    return call
+
+
+def _decode(bits, q, packed_k, packed_v, k_scale, k_zero, v_scale, v_zero, seq_lens, layout, group,
+            out=None, lse=None, sm_scale=0.0, stream=None):
+    return prepare_decode(bits, q, packed_k, packed_v, k_scale, k_zero, v_scale, v_zero, seq_lens, layout, group,
+                          out, lse, sm_scale, stream)()
 
 
 def foscar_decode_int2(q, packed_k, packed_v, k_scale, k_zero, v_scale, v_zero, seq_lens, layout, group,
@@ -192,6 +228,13 @@ def foscar_split_plan(dims, layout, group):
     _check(_lib.load().foscar_split_plan(ctypes.byref(dims), int(layout), int(group), ctypes.byref(s),
                                          ctypes.byref(c)), "foscar_split_plan")
     return s.value, c.value
+
+
+def foscar_occupancy(bits, layout, group):
+    """Work-groups of the decode kernel one compute unit holds at once."""
+    n = ctypes.c_int32(0)
+    _check(_lib.load().foscar_occupancy(int(bits), int(layout), int(group), ctypes.byref(n)), "foscar_occupancy")
+    return int(n.value)
 
 
 def foscar_strerror(code):

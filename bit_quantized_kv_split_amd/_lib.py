@@ -12,7 +12,7 @@ LIB_PATH = os.path.join(HERE, "libfoscar.so")
 # Names declared in include/foscar.h, in order.
 EXPORTS = [
     "foscar_decode_int2", "foscar_decode_int4", "foscar_pack", "foscar_unpack", "foscar_packed_bytes",
-    "foscar_scale_count", "foscar_workspace_reserve", "foscar_release", "foscar_split_plan",
+    "foscar_scale_count", "foscar_workspace_reserve", "foscar_release", "foscar_split_plan", "foscar_occupancy",
     "foscar_strerror", "foscar_version", "foscar_last_hip_error",
 ]
 
@@ -53,6 +53,8 @@ def load():
     lib.foscar_release.restype = None
     lib.foscar_split_plan.argtypes = [D, I, I, ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int32)]
     lib.foscar_split_plan.restype = I
+    lib.foscar_occupancy.argtypes = [I, I, I, ctypes.POINTER(ctypes.c_int32)]
+    lib.foscar_occupancy.restype = I
     lib.foscar_strerror.argtypes = [I]
     lib.foscar_strerror.restype = ctypes.c_char_p
     lib.foscar_version.argtypes = []

@@ -277,6 +277,18 @@ int foscar_split_plan(const foscar_dims* dims, int layout, int group, int32_t* s
   return FOSCAR_OK;
 }
 
+int foscar_occupancy(int bits, int layout, int group, int32_t* wgs_per_cu) {
+  if (!wgs_per_cu) return FOSCAR_EINVAL;
+  if (layout < 0 || layout > 3) return FOSCAR_EINVAL;
+  if ((bits != 2 && bits != 4) || !valid_group(group)) return FOSCAR_EUNSUPPORTED;
+  int n = 0;
+  const hipError_t e = foscar::decode_occupancy(bits, (layout & FOSCAR_K_CHANNEL) != 0, (layout & FOSCAR_V_CHANNEL) != 0,
+                                                group, &n);
+  if (e != hipSuccess) return hip_fail(e);
+  *wgs_per_cu = n;
+  return FOSCAR_OK;
+}
+
 int foscar_workspace_reserve(const foscar_dims* dims, int layout, int group, void* stream) {
   int rc = check_decode_shape(dims, layout, group);
   if (rc) return rc;

@@ -282,32 +282,6 @@ __device__ __forceinline__ void load_u2(uint2 (&dst)[N], const uint16_t* p) {
 // Split kernel.
 // BITS: 2 or 4; KCH / VCH: channel-wise key / value groups; GRP: g.
 // ---------------------------------------------------------------------------
-// Block-wide max / sum of four values per thread (one per query head); every
-// thread receives the result.  s_red holds kWaves x 4 floats.
-template <bool MAX>
-__device__ __forceinline__ void block_reduce4(float (&v)[4], float (*s_red)[4]) {
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) {
-      const float o = __shfl_xor(v[i], m);
-      v[i] = MAX ? fmaxf(v[i], o) : v[i] + o;
-    }
-  const int wave = threadIdx.x >> 6;
-  if ((threadIdx.x & 63) == 0)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) s_red[wave][i] = v[i];
-  __syncthreads();
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    float r = s_red[0][i];
-#pragma unroll
-    for (int w = 1; w < kWaves; ++w) r = MAX ? fmaxf(r, s_red[w][i]) : r + s_red[w][i];
-    v[i] = r;
-  }
-  __syncthreads();
-}
-
 __device__ __forceinline__ float coherent_load(const float* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -315,77 +289,82 @@ __device__ __forceinline__ float coherent_load(const float* p) {
 // Log-sum-exp merge of the ns ranges of one (sequence, KV head), run by the
 // work-group that finished last: O = sum_s exp(lse_s - M) O_s / sum_s exp(lse_s - M),
 // lse = M + log(sum_s exp(lse_s - M)).  The partials were written by other
-// work-groups, so they are read with device-coherent loads, all issued in
-// parallel (weights first, then 16 partial outputs in flight per thread).
-// s_w: ns * 4 floats of LDS.
-__device__ __forceinline__ void merge_ranges(const SplitArgs& a, int b, int h, int ns, float* s_w) {
-  constexpr int D = kHeadDim;
-  __shared__ float s_red[kWaves][4];
+// work-groups, so they are read with device-coherent loads.  Thread t owns
+// channel t % 128 of query rows t / 128 and t / 128 + 2 and streams the
+// ranges in blocks of 16: each block's lse and partial outputs are loaded
+// together (one memory round trip per block), then folded into a running max.
+__device__ __forceinline__ void merge_ranges(const SplitArgs& a, int b, int h, int ns) {
+  constexpr int D = kHeadDim, BLK = 16;
   const int G = a.g_heads;
-  const size_t row0 = (size_t)b * a.hq + (size_t)h * G;
-  float mx[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
-  for (int s2 = threadIdx.x; s2 < ns; s2 += blockDim.x) {
-    float v[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) v[i] = (i < G) ? coherent_load(a.lse_part + (row0 + i) * a.splits + s2) : -INFINITY;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      s_w[i * ns + s2] = v[i];
-      mx[i] = fmaxf(mx[i], v[i]);
-    }
-  }
-  block_reduce4<true>(mx, s_red);
-  float den[4] = {0.f, 0.f, 0.f, 0.f};
-  for (int s2 = threadIdx.x; s2 < ns; s2 += blockDim.x)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float w = (i < G) ? __expf(s_w[i * ns + s2] - mx[i]) : 0.f;
-      s_w[i * ns + s2] = w;
-      den[i] += w;
-    }
-  block_reduce4<false>(den, s_red);  // also orders the weight writes before the reads below
-
   const int c = threadIdx.x & (D - 1);
-  const int i0 = threadIdx.x / D;  // rows i0 and i0 + 2 (blockDim.x == 2 * D)
-  const bool two = i0 + 2 < G;
+  const int i0 = threadIdx.x / D;  // blockDim.x == 2 * D
   if (i0 >= G) return;
-  const float* op0 = a.o_part + ((row0 + i0) * a.splits) * D + c;
-  const float* op1 = a.o_part + ((row0 + (two ? i0 + 2 : i0)) * a.splits) * D + c;
-  const float* w0 = s_w + i0 * ns;
-  const float* w1 = s_w + (two ? i0 + 2 : i0) * ns;
-  float n0 = 0.f, n1 = 0.f;
-  int s2 = 0;
-  for (; s2 + 8 <= ns; s2 += 8) {
-    float v0[8], v1[8];
+  const bool two = i0 + 2 < G;
+  const size_t row0 = (size_t)b * a.hq + (size_t)h * G + i0;
+  const size_t row1 = two ? row0 + 2 : row0;
+  const float* lp0 = a.lse_part + row0 * a.splits;
+  const float* lp1 = a.lse_part + row1 * a.splits;
+  const float* op0 = a.o_part + row0 * a.splits * D + c;
+  const float* op1 = a.o_part + row1 * a.splits * D + c;
+  float m0 = -INFINITY, m1 = -INFINITY, n0 = 0.f, n1 = 0.f, d0 = 0.f, d1 = 0.f;
+  for (int s0 = 0; s0 < ns; s0 += BLK) {
+    float l0[BLK], l1[BLK], v0[BLK], v1[BLK];
+    // unconditional loads (an atomic load under a branch is not speculated, and
+    // the branches would serialise the round trips): ranges past ns re-read
+    // range ns - 1 and are masked afterwards
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      v0[u] = coherent_load(op0 + (size_t)(s2 + u) * D);
-      v1[u] = two ? coherent_load(op1 + (size_t)(s2 + u) * D) : 0.f;
+    for (int u = 0; u < BLK; ++u) {
+      const int si = min(s0 + u, ns - 1);
+      l0[u] = coherent_load(lp0 + si);
+      v0[u] = coherent_load(op0 + (size_t)si * D);
+      l1[u] = coherent_load(lp1 + si);
+      v1[u] = coherent_load(op1 + (size_t)si * D);
     }
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      n0 = fmaf(w0[s2 + u], v0[u], n0);
-      n1 = fmaf(w1[s2 + u], v1[u], n1);
+    for (int u = 0; u < BLK; ++u) {
+      if (s0 + u >= ns) {
+        l0[u] = l1[u] = -INFINITY;
+        v0[u] = v1[u] = 0.f;
+      }
     }
+    float b0 = m0, b1 = m1;  // every range below ns holds a token, so its lse is finite
+#pragma unroll
+    for (int u = 0; u < BLK; ++u) {
+      b0 = fmaxf(b0, l0[u]);
+      b1 = fmaxf(b1, l1[u]);
+    }
+    const float r0 = __expf(m0 - b0), r1 = __expf(m1 - b1);  // 0 on the first block
+    n0 *= r0;
+    d0 *= r0;
+    n1 *= r1;
+    d1 *= r1;
+#pragma unroll
+    for (int u = 0; u < BLK; ++u) {
+      const float w0 = __expf(l0[u] - b0), w1 = __expf(l1[u] - b1);
+      n0 = fmaf(w0, v0[u], n0);
+      d0 += w0;
+      n1 = fmaf(w1, v1[u], n1);
+      d1 += w1;
+    }
+    m0 = b0;
+    m1 = b1;
   }
-  for (; s2 < ns; ++s2) {
-    n0 = fmaf(w0[s2], coherent_load(op0 + (size_t)s2 * D), n0);
-    if (two) n1 = fmaf(w1[s2], coherent_load(op1 + (size_t)s2 * D), n1);
-  }
-  float d0 = den[0], d1 = den[2], m0 = mx[0], m1 = mx[2];
-  if (i0 == 1) {
-    d0 = den[1]; d1 = den[3]; m0 = mx[1]; m1 = mx[3];
-  }
-  a.out[(row0 + i0) * D + c] = to_bf16_rne(n0 / d0);
-  if (c == 0 && a.lse) a.lse[row0 + i0] = m0 + __logf(d0);
+  a.out[row0 * D + c] = to_bf16_rne(n0 / d0);
+  if (c == 0 && a.lse) a.lse[row0] = m0 + __logf(d0);
   if (two) {
-    a.out[(row0 + i0 + 2) * D + c] = to_bf16_rne(n1 / d1);
-    if (c == 0 && a.lse) a.lse[row0 + i0 + 2] = m1 + __logf(d1);
+    a.out[row1 * D + c] = to_bf16_rne(n1 / d1);
+    if (c == 0 && a.lse) a.lse[row1] = m1 + __logf(d1);
   }
 }
 
 template <int BITS, bool KCH, bool VCH, int GRP>
-__global__ __launch_bounds__(256) void split_decode(const SplitArgs a) {
+constexpr int waves_per_simd() {
+  return (BITS == 2 && !KCH && !VCH && GRP == 128) ? 4 : 1;
+}
+
+template <int BITS, bool KCH, bool VCH, int GRP>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(waves_per_simd<BITS, KCH, VCH, GRP>())))
+void split_decode(const SplitArgs a) {
   using C = Codec<BITS>;
   constexpr int D = kHeadDim;
   constexpr int E = C::E;
@@ -439,7 +418,8 @@ __global__ __launch_bounds__(256) void split_decode(const SplitArgs a) {
   __shared__ __align__(16) uint32_t s_q[KCH ? 1 : 4][KCH ? 4 : D / 2 + 4];
   __shared__ float s_kq[2][4][NGK];
   float kq_sum[NGK], kq_bias[NGK];
-  if constexpr (!KCH) {
+  auto query_prologue = [&]() {  // run after the first tiles are in flight, so the two HBM latencies overlap
+   if constexpr (!KCH) {
     {  // wave i converts query head i, lane j its channel pair j
       const int qi = wave, pj = lane;
       uint32_t w = 0;
@@ -464,7 +444,8 @@ __global__ __launch_bounds__(256) void split_decode(const SplitArgs a) {
       kq_sum[j] = s_kq[0][qn][j];
       kq_bias[j] = s_kq[1][qn][j];
     }
-  }
+   }
+  };
   // channel-wise K (operand-fold on Q): Q~ = Q * s_tau carried exactly as an fp16 pair hi + lo
   // (the fp32 product of a bf16 and an fp16 value is exact), and sigma' * (sum Q z - sum Q~ C)
   uint32_t qt_hi[KCH ? D / 2 : 1], qt_lo[KCH ? D / 2 : 1];
@@ -878,7 +859,17 @@ __global__ __launch_bounds__(256) void split_decode(const SplitArgs a) {
 #pragma unroll
   for (int k = 0; k < NS - 1; ++k)
     if (k < nt) issue(k);
+  query_prologue();
+  // The SIMD issues from the oldest ready wave first, so the work-groups
+  // dispatched first would race ahead and the last ones would finish alone.
+  // Each wave lowers its priority at every quarter of its tiles: waves that
+  // are behind win the arbitration and all of them finish together.
+  const int q1 = nt / 4, q2 = nt / 2, q3 = (3 * nt) / 4;
+  __builtin_amdgcn_s_setprio(3);
   for (int k = 0; k < nt; ++k) {
+    if (k == q1) __builtin_amdgcn_s_setprio(2);
+    if (k == q2) __builtin_amdgcn_s_setprio(1);
+    if (k == q3) __builtin_amdgcn_s_setprio(0);
     if (k + NS - 1 < nt) issue(k + NS - 1);
     Tile tl;
     read(tl, k, min(NS - 1, nt - 1 - k));
@@ -888,6 +879,8 @@ __global__ __launch_bounds__(256) void split_decode(const SplitArgs a) {
     else
       process(tl, t0k, std::false_type{});
   }
+
+  __builtin_amdgcn_s_setprio(3);  // the epilogue and the merge are the tail of the launch
 
   // ---------------- wave epilogue: totals per query, value-side corrections
   const float l_tot = sum_same_query<64>(l_part);
@@ -972,47 +965,57 @@ __global__ __launch_bounds__(256) void split_decode(const SplitArgs a) {
   }
   __syncthreads();
   if (!s_last) return;
-  merge_ranges(a, b, h, ns, reinterpret_cast<float*>(smem));
+  merge_ranges(a, b, h, ns);
   if (threadIdx.x == 0) a.counters[bh] = 0;  // ready for the next call on this workspace
 }
 
+// Launch the instantiation on `stream`, or (per_cu != nullptr) report how many
+// of its work-groups one CU holds at once instead.
 template <int BITS, bool KCH, bool VCH, int GRP>
-hipError_t launch_one(int batch, int hkv, const SplitArgs& sa, hipStream_t stream) {
+hipError_t launch_one(int batch, int hkv, const SplitArgs& sa, hipStream_t stream, int* per_cu) {
   using ST = Stage<BITS, KCH, VCH, GRP>;
   constexpr size_t lds = (size_t)kWaves * ST::NS * ST::BYTES;
   static_assert(lds >= sizeof(float) * kWaves * 4 * kHeadDim, "rings must hold the epilogue buffer");
-  static_assert(lds >= sizeof(float) * 4 * kMaxSplits, "rings must hold the merge weights");
+  if (per_cu)
+    return hipOccupancyMaxActiveBlocksPerMultiprocessor(per_cu, split_decode<BITS, KCH, VCH, GRP>, kWaves * 64, lds);
   dim3 grid(sa.splits, hkv, batch);
   hipLaunchKernelGGL((split_decode<BITS, KCH, VCH, GRP>), grid, dim3(kWaves * 64), lds, stream, sa);
   return hipGetLastError();
 }
 
 template <int BITS, bool KCH, bool VCH>
-hipError_t launch_g(int group, int batch, int hkv, const SplitArgs& sa, hipStream_t stream) {
+hipError_t launch_g(int group, int batch, int hkv, const SplitArgs& sa, hipStream_t stream, int* per_cu) {
   switch (group) {
-    case 32: return launch_one<BITS, KCH, VCH, 32>(batch, hkv, sa, stream);
-    case 64: return launch_one<BITS, KCH, VCH, 64>(batch, hkv, sa, stream);
-    case 128: return launch_one<BITS, KCH, VCH, 128>(batch, hkv, sa, stream);
+    case 32: return launch_one<BITS, KCH, VCH, 32>(batch, hkv, sa, stream, per_cu);
+    case 64: return launch_one<BITS, KCH, VCH, 64>(batch, hkv, sa, stream, per_cu);
+    case 128: return launch_one<BITS, KCH, VCH, 128>(batch, hkv, sa, stream, per_cu);
   }
   return hipErrorInvalidValue;
 }
 
 template <int BITS>
-hipError_t launch_bits(bool kch, bool vch, int group, int batch, int hkv, const SplitArgs& sa, hipStream_t stream) {
+hipError_t launch_bits(bool kch, bool vch, int group, int batch, int hkv, const SplitArgs& sa, hipStream_t stream,
+                       int* per_cu) {
   if (kch) {
-    return vch ? launch_g<BITS, true, true>(group, batch, hkv, sa, stream)
-               : launch_g<BITS, true, false>(group, batch, hkv, sa, stream);
+    return vch ? launch_g<BITS, true, true>(group, batch, hkv, sa, stream, per_cu)
+               : launch_g<BITS, true, false>(group, batch, hkv, sa, stream, per_cu);
   }
-  return vch ? launch_g<BITS, false, true>(group, batch, hkv, sa, stream)
-             : launch_g<BITS, false, false>(group, batch, hkv, sa, stream);
+  return vch ? launch_g<BITS, false, true>(group, batch, hkv, sa, stream, per_cu)
+             : launch_g<BITS, false, false>(group, batch, hkv, sa, stream, per_cu);
 }
 
 }  // namespace
 
 hipError_t launch_decode(int bits, bool k_channel, bool v_channel, int group, int batch, int hkv,
                          const SplitArgs& sa, hipStream_t stream) {
-  if (bits == 2) return launch_bits<2>(k_channel, v_channel, group, batch, hkv, sa, stream);
-  return launch_bits<4>(k_channel, v_channel, group, batch, hkv, sa, stream);
+  if (bits == 2) return launch_bits<2>(k_channel, v_channel, group, batch, hkv, sa, stream, nullptr);
+  return launch_bits<4>(k_channel, v_channel, group, batch, hkv, sa, stream, nullptr);
+}
+
+hipError_t decode_occupancy(int bits, bool k_channel, bool v_channel, int group, int* per_cu) {
+  SplitArgs sa{};
+  if (bits == 2) return launch_bits<2>(k_channel, v_channel, group, 0, 0, sa, nullptr, per_cu);
+  return launch_bits<4>(k_channel, v_channel, group, 0, 0, sa, nullptr, per_cu);
 }
 
 }  // namespace foscar

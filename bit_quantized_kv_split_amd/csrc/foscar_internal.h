@@ -10,7 +10,7 @@ constexpr int kHeadDim = 128;   // D
 constexpr int kTile = 64;       // tokens per wave tile (16 quads of 4)
 constexpr int kWaves = 4;       // waves per work-group
 constexpr int kMaxG = 4;        // query heads per KV head served by one wave
-constexpr int kMaxSplits = 512;  // ranges per sequence (the merge keeps 4 weights per range in LDS)
+constexpr int kMaxSplits = 512;  // ranges per sequence (bounds the workspace and the merge passes)
 
 // Arguments of the decode kernel (one work-group per (range, KV head, sequence)).
 // The last work-group to finish the ranges of a (sequence, KV head) merges them.
@@ -38,6 +38,8 @@ struct SplitArgs {
 hipError_t launch_decode(int bits, bool k_channel, bool v_channel, int group, int batch, int hkv,
                          const SplitArgs& sa, hipStream_t stream);
 
+// Work-groups of the decode kernel for (bits, layout sides, group) one CU holds at once.
+hipError_t decode_occupancy(int bits, bool k_channel, bool v_channel, int group, int* per_cu);
 hipError_t launch_pack(int bits, int side, int batch, int hkv, int tcap, const uint8_t* codes, uint32_t* packed,
                        hipStream_t stream);
 hipError_t launch_unpack(int bits, int side, int batch, int hkv, int tcap, const uint32_t* packed, uint8_t* codes,

@@ -154,6 +154,12 @@ void foscar_release(void);
  * the count is capped at 512 ranges and at one range per 64-token unit. */
 int foscar_split_plan(const foscar_dims* dims, int layout, int group, int32_t* splits, int32_t* chunk);
 
+/* Work-groups of the decode kernel for (bits, layout, group) that one compute
+ * unit of the current device holds at once (registers and LDS permitting).
+ * Reporting only; FOSCAR_EUNSUPPORTED for bits/group outside the supported
+ * set, FOSCAR_EHIP if the runtime query fails. */
+int foscar_occupancy(int bits, int layout, int group, int32_t* wgs_per_cu);
+
 const char* foscar_strerror(int code);
 int foscar_version(void);
 /* hipError_t of the last failed HIP call on this host thread (0 if none). */

@@ -105,3 +105,18 @@ def test_split_plan_covers_the_cache(lib, monkeypatch):
     monkeypatch.setenv("FOSCAR_SPLITS", "3")
     s, c = fos.foscar_split_plan(_dims(), 0, 128)
     assert s == 3 and c == 384
+
+
+def test_occupancy_rejects_bad_arguments(lib):
+    n = ctypes.c_int32(0)
+    assert lib.foscar_occupancy(3, 0, 128, ctypes.byref(n)) == -2
+    assert lib.foscar_occupancy(2, 0, 48, ctypes.byref(n)) == -2
+    assert lib.foscar_occupancy(2, 4, 128, ctypes.byref(n)) == -1
+    assert lib.foscar_occupancy(2, 0, 128, None) == -1
+
+
+def test_split_plan_caps_the_range_count(lib, monkeypatch):
+    import bit_quantized_kv_split_amd as fos
+    monkeypatch.setenv("FOSCAR_SPLITS", "100000")
+    s, c = fos.foscar_split_plan(_dims(max_seq_len=1 << 20), 0, 128)
+    assert s == 512 and c == 2048

@@ -216,3 +216,15 @@ def test_zero_query_gives_exact_mean_value(bits, kl, vl, g):
                 assert np.all(err <= 1e-4 * scale + 2.0 ** -8 * np.abs(mean)), (
                     f"seq {b} head {i}: max err {err.max():.3e} at ch {np.argmax(err)}; mean {mean[np.argmax(err)]:.4f}")
             np.testing.assert_allclose(lse[b, 4 * h:4 * h + 4], math.log(T), atol=1e-5)
+
+
+@pytest.mark.gpu
+def test_occupancy_query_reports_resident_work_groups():
+    """Every instantiation fits at least one work-group per CU; the INT2
+    token-wise kernel of the long-context workload fits four."""
+    import bit_quantized_kv_split_amd as fos
+    for bits in (2, 4):
+        for layout in range(4):
+            for g in (32, 64, 128):
+                assert fos.foscar_occupancy(bits, layout, g) >= 1
+    print("INT2 token-wise g=128 work-groups per CU:", fos.foscar_occupancy(2, 0, 128))
