@@ -154,6 +154,12 @@ __device__ __forceinline__ uint4 lds_b128(uint32_t a) {
   return make_uint4(v[0], v[1], v[2], v[3]);
 }
 template <int OFF>
+__device__ __forceinline__ uint32_t lds_b32(uint32_t a) {
+  uint32_t v;
+  asm volatile("ds_read_b32 %0, %1 offset:%2" : "=v"(v) : "v"(a), "i"(OFF) : "memory");
+  return v;
+}
+template <int OFF>
 __device__ __forceinline__ uint2 lds_b64(uint32_t a) {
   u32x2 v;
   asm volatile("ds_read_b64 %0, %1 offset:%2" : "=v"(v) : "v"(a), "i"(OFF) : "memory");
@@ -176,7 +182,9 @@ __device__ __forceinline__ void dma4(__amdgpu_buffer_rsrc_t r, uint32_t voff, ui
 }
 
 // Bytes of one staged tile and its layout:
-//   [ks | kz | vs | vz (token-wise sides only)][K rows][V words].
+//   [ks | kz | vs | vz (token-wise sides)][K (s | z) rows | V (s | z) rows (channel-wise sides)][K rows][V words].
+// A channel-wise side stages the (s, z) rows (256 B each) of the groups the
+// tile touches (two for g = 32; for g = 128 both tiles of a unit carry them).
 // Scales are loaded in 256-byte blocks (one dword per lane).  A side with one
 // group per token has 128 bytes per tile, so the upper half of its block lands
 // on the next region; loads into one wave's LDS complete in issue order, so
@@ -191,16 +199,21 @@ struct Stage {
   static constexpr int NGV = VCH ? 0 : kHeadDim / GRP;
   static constexpr int KSB = 128 * NGK;              // bytes of ks (equally kz) per tile
   static constexpr int VSB = 128 * NGV;
+  static constexpr int NGT = (GRP < kTile) ? kTile / GRP : 1;  // channel-wise groups one tile touches
+  static constexpr int KCB = KCH ? 512 * NGT : 0;    // channel-wise K: s rows then z rows
+  static constexpr int VCB = VCH ? 512 * NGT : 0;
   static constexpr int SOFF = 0;
   static constexpr int VSOFF = SOFF + 2 * KSB;
-  static constexpr int KOFF = VSOFF + 2 * VSB;
+  static constexpr int KCOFF = VSOFF + 2 * VSB;
+  static constexpr int VCOFF = KCOFF + KCB;
+  static constexpr int KOFF = VCOFF + VCB;
   static constexpr int KBYTES = KW * 4 * kTile;      // KW/4 chunks of 1 KB
   static constexpr int VOFF = KOFF + KBYTES;
   static constexpr int VBYTES = VW * kHeadDim * 4;   // VW/2 chunks of 1 KB
   static constexpr int BYTES = VOFF + VBYTES;
   static constexpr int KSL = (KSB + 255) / 256;      // 256-byte scale loads per array
   static constexpr int VSL = (VSB + 255) / 256;
-  static constexpr int LOADS = KW / 4 + VW / 2 + 2 * KSL + 2 * VSL;  // load instructions per tile
+  static constexpr int LOADS = KW / 4 + VW / 2 + 2 * KSL + 2 * VSL + (KCB + VCB) / 256;  // loads per tile
   static_assert(KOFF % 16 == 0, "K rows need 16-byte alignment");
   // ring depth: two tiles in flight per wave; with four waves per work-group
   // and four work-groups per CU the INT2 rings fit the 160 KB of LDS
@@ -256,6 +269,20 @@ __device__ __forceinline__ float max_halves(float v) {
   float a = v, b = v;
   asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(a), "+v"(b));
   return fmaxf(a, b);
+}
+// sum over all 64 lanes, in every lane
+__device__ __forceinline__ float wave_sum(float v) {
+  v += dpp<0x121>(v);  // row_ror:1
+  v += dpp<0x122>(v);  // row_ror:2
+  v += dpp<0x124>(v);  // row_ror:4
+  v += dpp<0x128>(v);  // row_ror:8
+  float a = v, b = v;
+  asm volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1" : "+v"(a), "+v"(b));
+  v = a + b;
+  a = v;
+  b = v;
+  asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(a), "+v"(b));
+  return a + b;
 }
 __device__ __forceinline__ float wave_max_same_query(float v) {
   v = fmaxf(v, dpp<0x124>(v));  // row_ror:4
@@ -411,15 +438,23 @@ void split_decode(const SplitArgs a) {
   const float sl2 = a.sm_log2;
 
   // ---- query prologue: bf16 -> fp16 pairs (channels 2j, 2j+1); exact for values in the fp16 range
-  const uint4* qrow = reinterpret_cast<const uint4*>(a.q + ((size_t)b * a.hq + h * a.g_heads + (qvalid ? qn : 0)) * D);
   // token-wise K: the work-group's query block as the QK^T B operand in LDS (row = query head;
   // rows padded by 16 B so the four rows of one read fall in different banks), and per group
   // sigma' * sum(Q) and sigma' * sum(Q * C)  (C = operand bias of each channel)
   __shared__ __align__(16) uint32_t s_q[KCH ? 1 : 4][KCH ? 4 : D / 2 + 4];
   __shared__ float s_kq[2][4][NGK];
+  // channel-wise K: the bf16 query pairs (row = query head) from which each
+  // wave builds Q~ = Q * s_tau for its tile's groups, hi and lo fp16 parts
+  __shared__ uint32_t s_qb[KCH ? 4 : 1][KCH ? D / 2 : 1];
+  constexpr int NGT = Stage<BITS, KCH, VCH, GRP>::NGT;
+  __shared__ __align__(16) uint32_t s_qt[KCH ? kWaves : 1][KCH ? NGT : 1][2][4][KCH ? D / 2 + 4 : 4];
   float kq_sum[NGK], kq_bias[NGK];
   auto query_prologue = [&]() {  // run after the first tiles are in flight, so the two HBM latencies overlap
-   if constexpr (!KCH) {
+   if constexpr (KCH) {
+    s_qb[wave][lane] = (wave < a.g_heads)
+        ? reinterpret_cast<const uint32_t*>(a.q + ((size_t)b * a.hq + h * a.g_heads + wave) * D)[lane] : 0u;
+    __syncthreads();
+   } else {
     {  // wave i converts query head i, lane j its channel pair j
       const int qi = wave, pj = lane;
       uint32_t w = 0;
@@ -448,9 +483,7 @@ void split_decode(const SplitArgs a) {
   };
   // channel-wise K (operand-fold on Q): Q~ = Q * s_tau carried exactly as an fp16 pair hi + lo
   // (the fp32 product of a bf16 and an fp16 value is exact), and sigma' * (sum Q z - sum Q~ C)
-  uint32_t qt_hi[KCH ? D / 2 : 1], qt_lo[KCH ? D / 2 : 1];
   float kconst = 0.f;
-  int k_tau = -1;
 
   // ---- running state
   float m_ref = -INFINITY;                 // reference max of this lane's query (log2 units)
@@ -482,10 +515,12 @@ void split_decode(const SplitArgs a) {
   const uint16_t* kzb = a.kz + bh * (size_t)(KCH ? (a.tcap / GRP) * D : a.tcap * NGK);
   const uint16_t* vsb = a.vs + bh * (size_t)(VCH ? (a.tcap / GRP) * D : a.tcap * NGV);
   const uint16_t* vzb = a.vz + bh * (size_t)(VCH ? (a.tcap / GRP) * D : a.tcap * NGV);
-  const __amdgpu_buffer_rsrc_t rks = rsrc(ksb, KCH ? 0u : (uint32_t)a.tcap * NGK * 2);
-  const __amdgpu_buffer_rsrc_t rkz = rsrc(kzb, KCH ? 0u : (uint32_t)a.tcap * NGK * 2);
-  const __amdgpu_buffer_rsrc_t rvs = rsrc(vsb, VCH ? 0u : (uint32_t)a.tcap * NGV * 2);
-  const __amdgpu_buffer_rsrc_t rvz = rsrc(vzb, VCH ? 0u : (uint32_t)a.tcap * NGV * 2);
+  const uint32_t kscale_bytes = KCH ? (uint32_t)(a.tcap / GRP) * D * 2 : (uint32_t)a.tcap * NGK * 2;
+  const uint32_t vscale_bytes = VCH ? (uint32_t)(a.tcap / GRP) * D * 2 : (uint32_t)a.tcap * NGV * 2;
+  const __amdgpu_buffer_rsrc_t rks = rsrc(ksb, kscale_bytes);
+  const __amdgpu_buffer_rsrc_t rkz = rsrc(kzb, kscale_bytes);
+  const __amdgpu_buffer_rsrc_t rvs = rsrc(vsb, vscale_bytes);
+  const __amdgpu_buffer_rsrc_t rvz = rsrc(vzb, vscale_bytes);
 
   // rescale every accumulator of this wave after the reference max of a query moved
   auto rescale = [&](float alpha) {
@@ -510,7 +545,7 @@ void split_decode(const SplitArgs a) {
   };
 
   // channel-wise V: fold the finished group tau into o_tot.  `span` = lanes whose quads form the group.
-  auto fold_value_group = [&](int tau, int src_half) {
+  auto fold_value_group = [&](uint32_t s2, uint32_t z2, int src_half) {
     // sums of the group per query, then broadcast query i's sums to every lane
     float ps, pb;
     if (GRP == 32) {  // the group's quads are the lanes of half-wave src_half
@@ -525,8 +560,6 @@ void split_decode(const SplitArgs a) {
     }
     const float psq[4] = {quad_bcast<0>(ps), quad_bcast<1>(ps), quad_bcast<2>(ps), quad_bcast<3>(ps)};
     const float pbq[4] = {quad_bcast<0>(pb), quad_bcast<1>(pb), quad_bcast<2>(pb), quad_bcast<3>(pb)};
-    const uint32_t s2 = *reinterpret_cast<const uint32_t*>(vsb + (size_t)tau * D + 2 * lane);
-    const uint32_t z2 = *reinterpret_cast<const uint32_t*>(vzb + (size_t)tau * D + 2 * lane);
     const float sv[2] = {half_lo(s2), half_hi(s2)};
     const float zv[2] = {half_lo(z2), half_hi(z2)};
 #pragma unroll
@@ -545,6 +578,8 @@ void split_decode(const SplitArgs a) {
     uint2 v[VW];               // value words of channels 2 lane, 2 lane + 1
     uint2 ks[NGK], kz[NGK];    // token-wise key (s, z) of the quad's tokens
     uint2 vs[NGV], vz[NGV];    // token-wise value (s, z) of the quad's tokens
+    uint32_t kcs[NGT], kcz[NGT];  // channel-wise key (s, z) of channels 2 lane, 2 lane + 1, per group
+    uint32_t vcs[NGT], vcz[NGT];  // channel-wise value (s, z), likewise
   };
   unsigned char* ring = smem + wave * NS * ST::BYTES;
   const uint32_t ring_lds = lds_addr(ring);
@@ -565,6 +600,20 @@ void split_decode(const SplitArgs a) {
       for (int m = 0; m < ST::VSL; ++m) dma4(rvs, 4 * lane + 256 * m, t0 * NGV * 2, st + ST::VSOFF + m * 256);
 #pragma unroll
       for (int m = 0; m < ST::VSL; ++m) dma4(rvz, 4 * lane + 256 * m, t0 * NGV * 2, st + ST::VSOFF + ST::VSB + m * 256);
+    }
+    if constexpr (KCH) {
+#pragma unroll
+      for (int g2 = 0; g2 < NGT; ++g2) dma4(rks, 4 * lane, (t0 / GRP + g2) * D * 2, st + ST::KCOFF + g2 * 256);
+#pragma unroll
+      for (int g2 = 0; g2 < NGT; ++g2)
+        dma4(rkz, 4 * lane, (t0 / GRP + g2) * D * 2, st + ST::KCOFF + (NGT + g2) * 256);
+    }
+    if constexpr (VCH) {
+#pragma unroll
+      for (int g2 = 0; g2 < NGT; ++g2) dma4(rvs, 4 * lane, (t0 / GRP + g2) * D * 2, st + ST::VCOFF + g2 * 256);
+#pragma unroll
+      for (int g2 = 0; g2 < NGT; ++g2)
+        dma4(rvz, 4 * lane, (t0 / GRP + g2) * D * 2, st + ST::VCOFF + (NGT + g2) * 256);
     }
 #pragma unroll
     for (int i = 0; i < KW / 4; ++i) dma16(rk, lane * KW * 4 + 16 * i, t0 * KW * 4, st + ST::KOFF + i * 1024);
@@ -626,6 +675,24 @@ void split_decode(const SplitArgs a) {
         tl.vz[3 % NGV] = lds_b64<ST::VSB + 24>(as);
       }
     }
+    if constexpr (KCH) {
+      const uint32_t ac = st + ST::KCOFF + lane * 4;
+      tl.kcs[0] = lds_b32<0>(ac);
+      tl.kcz[0] = lds_b32<NGT * 256>(ac);
+      if constexpr (NGT > 1) {
+        tl.kcs[1 % NGT] = lds_b32<256>(ac);
+        tl.kcz[1 % NGT] = lds_b32<(NGT + 1) * 256>(ac);
+      }
+    }
+    if constexpr (VCH) {
+      const uint32_t ac = st + ST::VCOFF + lane * 4;
+      tl.vcs[0] = lds_b32<0>(ac);
+      tl.vcz[0] = lds_b32<NGT * 256>(ac);
+      if constexpr (NGT > 1) {
+        tl.vcs[1 % NGT] = lds_b32<256>(ac);
+        tl.vcz[1 % NGT] = lds_b32<(NGT + 1) * 256>(ac);
+      }
+    }
     wait_lgkm0();
 #pragma unroll
     for (int i = 0; i < KW / 4; ++i) touch(tl.k[i]);
@@ -639,42 +706,45 @@ void split_decode(const SplitArgs a) {
 #pragma unroll
       for (int j = 0; j < NGV; ++j) { touch(tl.vs[j]); touch(tl.vz[j]); }
     }
+#pragma unroll
+    for (int g2 = 0; g2 < NGT; ++g2) {
+      if constexpr (KCH) { touch(tl.kcs[g2]); touch(tl.kcz[g2]); }
+      if constexpr (VCH) { touch(tl.vcs[g2]); touch(tl.vcz[g2]); }
+    }
   };
 
   auto process = [&](const Tile& tl, const int t0, auto tail_c) {
     constexpr bool tail = decltype(tail_c)::value;  // the tile reaches past T: mask its last tokens
-    // ---------------- channel-wise K: operand Q~ for the group of this lane's quad
+    // ---------------- channel-wise K: the wave builds Q~ = Q * s_tau (hi, lo) for the tile's
+    // groups in LDS, lane l taking channel pair l of every query head, and the score constant
+    // sigma' * (sum_c Q z - sum_c Q~ C) of each (group, query head)
     if constexpr (KCH) {
-      const int tau = (t0 + 4 * qd) / GRP;
-      if (tau != k_tau) {  // uniform for g >= 64; per half-wave for g = 32
-        k_tau = tau;
-        const uint4* sp = reinterpret_cast<const uint4*>(ksb + (size_t)tau * D);
-        const uint4* zp = reinterpret_cast<const uint4*>(kzb + (size_t)tau * D);
-        float bq = 0.f, zq = 0.f;
+      if (GRP <= kTile || t0 % GRP == 0) {
+        const float cb = C::bias(lane % PAIRS);
+        float kc[NGT];
 #pragma unroll
-        for (int i = 0; i < D / 8; ++i) {
-          uint4 q4 = qrow[i];
-          if (!qvalid) q4 = make_uint4(0, 0, 0, 0);
-          const uint4 s4 = sp[i], z4 = zp[i];
-          const uint32_t qw[4] = {q4.x, q4.y, q4.z, q4.w};
-          const uint32_t sw[4] = {s4.x, s4.y, s4.z, s4.w};
-          const uint32_t zw[4] = {z4.x, z4.y, z4.z, z4.w};
+        for (int g2 = 0; g2 < NGT; ++g2) {
+          const uint32_t s2 = tl.kcs[g2], z2 = tl.kcz[g2];
+          const float s0 = half_lo(s2), s1 = half_hi(s2), z0 = half_lo(z2), z1 = half_hi(z2);
+          float part[4];
 #pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const int jj = 4 * i + j;
-            const float q0 = __builtin_bit_cast(float, qw[j] << 16);
-            const float q1 = __builtin_bit_cast(float, qw[j] & 0xFFFF0000u);
-            const float pr0 = q0 * half_lo(sw[j]), pr1 = q1 * half_hi(sw[j]);  // exact
+          for (int i = 0; i < 4; ++i) {
+            const uint32_t w = s_qb[i][lane];
+            const float q0 = __builtin_bit_cast(float, w << 16), q1 = __builtin_bit_cast(float, w & 0xFFFF0000u);
+            const float pr0 = q0 * s0, pr1 = q1 * s1;  // exact
             const _Float16 h0 = (_Float16)pr0, h1 = (_Float16)pr1;
             const h2 hi = {h0, h1};
             const h2 lo = {(_Float16)(pr0 - (float)h0), (_Float16)(pr1 - (float)h1)};
-            qt_hi[jj] = as_u32(hi);
-            qt_lo[jj] = as_u32(lo);
-            bq = fmaf(C::bias(jj % PAIRS), pr0 + pr1, bq);
-            zq = fmaf(q0, half_lo(zw[j]), fmaf(q1, half_hi(zw[j]), zq));
+            s_qt[wave][g2][0][i][lane] = as_u32(hi);
+            s_qt[wave][g2][1][i][lane] = as_u32(lo);
+            part[i] = fmaf(q0, z0, q1 * z1) - cb * (pr0 + pr1);
           }
+#pragma unroll
+          for (int i = 0; i < 4; ++i) part[i] = wave_sum(part[i]);
+          kc[g2] = (qn == 0) ? part[0] : (qn == 1) ? part[1] : (qn == 2) ? part[2] : part[3];
         }
-        kconst = (zq - bq) * sl2;
+        kconst = ((NGT > 1 && qd >= 8) ? kc[NGT - 1] : kc[0]) * sl2;
+        __builtin_amdgcn_wave_barrier();
       }
     }
 
@@ -688,18 +758,27 @@ void split_decode(const SplitArgs a) {
     // One segment per key word (its KPW k-steps); the compiler may not move work
     // across segments, which bounds the live operands, and each segment reads
     // the next one's B operands from LDS ahead of use.
-    const uint4* qsrc = reinterpret_cast<const uint4*>(&s_q[KCH ? 0 : qn][0]) + (int)in_vgpr(0u);
-    uint4 qcur[QPW], qnxt[QPW];
-    if constexpr (!KCH) {
+    // channel-wise K: hi parts (chain 0) and lo parts (chain 1) of Q~ for this lane's group
+    const int opq = (int)in_vgpr(0u);
+    const int g2l = (KCH && NGT > 1 && qd >= 8) ? 1 : 0;
+    const uint4* qsrc = KCH ? reinterpret_cast<const uint4*>(&s_qt[KCH ? wave : 0][g2l][0][qn][0]) + opq
+                            : reinterpret_cast<const uint4*>(&s_q[KCH ? 0 : qn][0]) + opq;
+    const uint4* qlsrc = reinterpret_cast<const uint4*>(&s_qt[KCH ? wave : 0][g2l][1][qn][0]) + opq;
+    uint4 qcur[QPW], qnxt[QPW], lcur[KCH ? QPW : 1], lnxt[KCH ? QPW : 1];
 #pragma unroll
-      for (int i = 0; i < QPW; ++i) qcur[i] = qsrc[i];
+    for (int i = 0; i < QPW; ++i) qcur[i] = qsrc[i];
+    if constexpr (KCH) {
+#pragma unroll
+      for (int i = 0; i < QPW; ++i) lcur[i] = qlsrc[i];
     }
 #pragma unroll
     for (int d = 0; d < KW; ++d) {
-      if constexpr (!KCH) {
-        if (d + 1 < KW) {
+      if (d + 1 < KW) {
 #pragma unroll
-          for (int i = 0; i < QPW; ++i) qnxt[i] = qsrc[(d + 1) * QPW + i];
+        for (int i = 0; i < QPW; ++i) qnxt[i] = qsrc[(d + 1) * QPW + i];
+        if constexpr (KCH) {
+#pragma unroll
+          for (int i = 0; i < QPW; ++i) lnxt[i] = qlsrc[(d + 1) * QPW + i];
         }
       }
       uint32_t wrd = (d % 4 == 0) ? tl.k[d / 4].x : (d % 4 == 1) ? tl.k[d / 4].y : (d % 4 == 2) ? tl.k[d / 4].z : tl.k[d / 4].w;
@@ -711,8 +790,11 @@ void split_decode(const SplitArgs a) {
         const int j = d * KPW + sg;  // k-step: channels 4j .. 4j+3
         const h4 av = cat4(p[2 * sg], p[2 * sg + 1]);
         if constexpr (KCH) {
-          sacc[0] = __builtin_amdgcn_mfma_f32_4x4x4f16(av, cat4(qt_hi[2 * j], qt_hi[2 * j + 1]), sacc[0], 0, 0, 0);
-          sacc[1] = __builtin_amdgcn_mfma_f32_4x4x4f16(av, cat4(qt_lo[2 * j], qt_lo[2 * j + 1]), sacc[1], 0, 0, 0);
+          const uint4 qh = qcur[sg / 2], ql = lcur[sg / 2];
+          const h4 bh = (sg & 1) ? cat4(qh.z, qh.w) : cat4(qh.x, qh.y);
+          const h4 bl = (sg & 1) ? cat4(ql.z, ql.w) : cat4(ql.x, ql.y);
+          sacc[0] = __builtin_amdgcn_mfma_f32_4x4x4f16(av, bh, sacc[0], 0, 0, 0);
+          sacc[1] = __builtin_amdgcn_mfma_f32_4x4x4f16(av, bl, sacc[1], 0, 0, 0);
         } else {
           const int ch = (NGK == 1) ? (j & 1) : (4 * j) / GRP;
           const uint4 qq = qcur[sg / 2];
@@ -720,9 +802,11 @@ void split_decode(const SplitArgs a) {
           sacc[ch] = __builtin_amdgcn_mfma_f32_4x4x4f16(av, bv, sacc[ch], 0, 0, 0);
         }
       }
-      if constexpr (!KCH) {
 #pragma unroll
-        for (int i = 0; i < QPW; ++i) qcur[i] = qnxt[i];
+      for (int i = 0; i < QPW; ++i) qcur[i] = qnxt[i];
+      if constexpr (KCH) {
+#pragma unroll
+        for (int i = 0; i < QPW; ++i) lcur[i] = lnxt[i];
       }
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -830,7 +914,7 @@ void split_decode(const SplitArgs a) {
         a1 = __builtin_amdgcn_mfma_f32_4x4x4f16(av, cat4(p1[2 * sg], p1[2 * sg + 1]), a1, 0, 0, 0);
         if constexpr (VCH && GRP == 32) {
           if (bq == 7) {  // first 32-token group of the tile is complete
-            if (t0 < T) fold_value_group(t0 / GRP, 0);
+            if (t0 < T) fold_value_group(tl.vcs[0], tl.vcz[0], 0);
           }
         }
       }
@@ -841,14 +925,14 @@ void split_decode(const SplitArgs a) {
     __builtin_amdgcn_wave_barrier();
     if constexpr (VCH) {
       if (GRP == 32) {
-        if (t0 + 32 < T) fold_value_group(t0 / GRP + 1, 1);
+        if (t0 + 32 < T) fold_value_group(tl.vcs[NGT - 1], tl.vcz[NGT - 1], 1);
         else {
 #pragma unroll
           for (int hh = 0; hh < 2; ++hh) o_acc[hh][0] = o_acc[hh][1] = f4{0.f, 0.f, 0.f, 0.f};
         }
         ps_part = pb_part = 0.f;
       } else if ((t0 + kTile) % GRP == 0 || t0 + kTile >= r1) {
-        fold_value_group(t0 / GRP, 0);
+        fold_value_group(tl.vcs[0], tl.vcz[0], 0);
         ps_part = pb_part = 0.f;
       }
     }
