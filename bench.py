@@ -45,9 +45,12 @@ def parse():
 
 
 def kernel_sha():
+    """Hash of the library sources (kernels, launch and split plan)."""
     h = hashlib.sha256()
-    with open(os.path.join(ROOT, "bit_quantized_kv_split_amd", "csrc", "decode.hip"), "rb") as f:
-        h.update(f.read())
+    csrc = os.path.join(ROOT, "bit_quantized_kv_split_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
     return h.hexdigest()[:16]
 
 
@@ -154,13 +157,17 @@ def main():
         step(k)
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
+    # kernel durations: events recorded by each decode dispatch itself (hipExtLaunchKernel), the
+    # same span rocprofv3's kernel trace reports; recorded once first so that they exist
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    for a, b in ev:
+        a.record(stream)
+        b.record(stream)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for k in range(args.steps):
-        ev[k][0].record(stream)
+        fos.foscar_record_next_launch(ev[k][0], ev[k][1])
         step(k)
-        ev[k][1].record(stream)
     enqueued = time.perf_counter() - t0
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -198,6 +205,7 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic_per_launch(spec.name),
                      "kernel": "split_decode (one launch per step)", "kernel_us_avg": round(k_avg * 1e3, 2),
+                     "kernel_us_median": round(sorted(kernel_ms)[len(kernel_ms) // 2] * 1e3, 2),
                      "kernel_us_min": round(min(kernel_ms) * 1e3, 2),
                      "host_enqueue_us_per_step": round(enqueued * 1e6 / args.steps, 2)},
         "staging_s": round(stage_s, 1),

@@ -230,6 +230,17 @@ def foscar_split_plan(dims, layout, group):
     return s.value, c.value
 
 
+def foscar_record_next_launch(start, stop):
+    """Have the next decode call on this thread record `start`/`stop` with its
+    kernel dispatch.  Events are torch.cuda.Event objects that have been
+    recorded once (so that they exist) or raw hipEvent_t handles."""
+    def handle(e):
+        if e is None:
+            return None
+        return ctypes.c_void_p(e.cuda_event if hasattr(e, "cuda_event") else int(e))
+    _lib.load().foscar_record_next_launch(handle(start), handle(stop))
+
+
 def foscar_occupancy(bits, layout, group):
     """Work-groups of the decode kernel one compute unit holds at once."""
     n = ctypes.c_int32(0)

@@ -13,6 +13,7 @@ LIB_PATH = os.path.join(HERE, "libfoscar.so")
 EXPORTS = [
     "foscar_decode_int2", "foscar_decode_int4", "foscar_pack", "foscar_unpack", "foscar_packed_bytes",
     "foscar_scale_count", "foscar_workspace_reserve", "foscar_release", "foscar_split_plan", "foscar_occupancy",
+    "foscar_record_next_launch",
     "foscar_strerror", "foscar_version", "foscar_last_hip_error",
 ]
 
@@ -55,6 +56,8 @@ def load():
     lib.foscar_split_plan.restype = I
     lib.foscar_occupancy.argtypes = [I, I, I, ctypes.POINTER(ctypes.c_int32)]
     lib.foscar_occupancy.restype = I
+    lib.foscar_record_next_launch.argtypes = [P, P]
+    lib.foscar_record_next_launch.restype = I
     lib.foscar_strerror.argtypes = [I]
     lib.foscar_strerror.restype = ctypes.c_char_p
     lib.foscar_version.argtypes = []

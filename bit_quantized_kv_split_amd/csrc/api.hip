@@ -17,6 +17,7 @@
 namespace {
 
 thread_local int g_last_hip_error = 0;
+thread_local foscar::LaunchEvents g_next_events;  // armed by foscar_record_next_launch
 
 // [counters: counter_bytes][partials: bytes - counter_bytes].  The counter
 // region keeps its place and size until the buffer grows, and holds nothing
@@ -159,6 +160,8 @@ int get_workspace(size_t cbytes, size_t pbytes, hipStream_t stream, int32_t** co
 int decode_common(int bits, const foscar_dims* d, const void* q, const void* pk, const void* pv, const void* ks,
                   const void* kz, const void* vs, const void* vz, const int32_t* seq_lens, int layout, int group,
                   void* out, float* lse, void* stream) {
+  const foscar::LaunchEvents ev = g_next_events;  // consumed by this call whether or not it launches
+  g_next_events = foscar::LaunchEvents{};
   int rc = check_decode_shape(d, layout, group);
   if (rc) return rc;
   if (d->batch == 0) return FOSCAR_OK;
@@ -198,7 +201,7 @@ int decode_common(int bits, const foscar_dims* d, const void* q, const void* pk,
   sa.sm_log2 = sm * 1.4426950408889634f;
 
   e = foscar::launch_decode(bits, (layout & FOSCAR_K_CHANNEL) != 0, (layout & FOSCAR_V_CHANNEL) != 0, group,
-                            d->batch, d->num_kv_heads, sa, (hipStream_t)stream);
+                            d->batch, d->num_kv_heads, sa, (hipStream_t)stream, ev);
   if (e != hipSuccess) return hip_fail(e);
   return FOSCAR_OK;
 }
@@ -274,6 +277,12 @@ int foscar_split_plan(const foscar_dims* dims, int layout, int group, int32_t* s
   int cus = 256;
   if (hipGetDevice(&dev) == hipSuccess) cus = compute_units(dev);
   plan(dims, layout, group, cus, splits, chunk);
+  return FOSCAR_OK;
+}
+
+int foscar_record_next_launch(void* start_event, void* stop_event) {
+  g_next_events.start = (hipEvent_t)start_event;
+  g_next_events.stop = (hipEvent_t)stop_event;
   return FOSCAR_OK;
 }
 

@@ -38,6 +38,8 @@
 //     release/acquire counter), so one decode step is one kernel launch.
 #include <math.h>
 
+#include <hip/hip_ext.h>
+
 #include <type_traits>
 
 #include "foscar_internal.h"
@@ -1056,50 +1058,56 @@ void split_decode(const SplitArgs a) {
 // Launch the instantiation on `stream`, or (per_cu != nullptr) report how many
 // of its work-groups one CU holds at once instead.
 template <int BITS, bool KCH, bool VCH, int GRP>
-hipError_t launch_one(int batch, int hkv, const SplitArgs& sa, hipStream_t stream, int* per_cu) {
+hipError_t launch_one(int batch, int hkv, const SplitArgs& sa, hipStream_t stream, int* per_cu, const LaunchEvents& ev) {
   using ST = Stage<BITS, KCH, VCH, GRP>;
   constexpr size_t lds = (size_t)kWaves * ST::NS * ST::BYTES;
   static_assert(lds >= sizeof(float) * kWaves * 4 * kHeadDim, "rings must hold the epilogue buffer");
   if (per_cu)
     return hipOccupancyMaxActiveBlocksPerMultiprocessor(per_cu, split_decode<BITS, KCH, VCH, GRP>, kWaves * 64, lds);
   dim3 grid(sa.splits, hkv, batch);
-  hipLaunchKernelGGL((split_decode<BITS, KCH, VCH, GRP>), grid, dim3(kWaves * 64), lds, stream, sa);
+  if (ev.start || ev.stop)  // timing events recorded by the dispatch itself
+    hipExtLaunchKernelGGL((split_decode<BITS, KCH, VCH, GRP>), grid, dim3(kWaves * 64), lds, stream, ev.start, ev.stop,
+                          0, sa);
+  else
+    hipLaunchKernelGGL((split_decode<BITS, KCH, VCH, GRP>), grid, dim3(kWaves * 64), lds, stream, sa);
   return hipGetLastError();
 }
 
 template <int BITS, bool KCH, bool VCH>
-hipError_t launch_g(int group, int batch, int hkv, const SplitArgs& sa, hipStream_t stream, int* per_cu) {
+hipError_t launch_g(int group, int batch, int hkv, const SplitArgs& sa, hipStream_t stream, int* per_cu,
+                    const LaunchEvents& ev) {
   switch (group) {
-    case 32: return launch_one<BITS, KCH, VCH, 32>(batch, hkv, sa, stream, per_cu);
-    case 64: return launch_one<BITS, KCH, VCH, 64>(batch, hkv, sa, stream, per_cu);
-    case 128: return launch_one<BITS, KCH, VCH, 128>(batch, hkv, sa, stream, per_cu);
+    case 32: return launch_one<BITS, KCH, VCH, 32>(batch, hkv, sa, stream, per_cu, ev);
+    case 64: return launch_one<BITS, KCH, VCH, 64>(batch, hkv, sa, stream, per_cu, ev);
+    case 128: return launch_one<BITS, KCH, VCH, 128>(batch, hkv, sa, stream, per_cu, ev);
   }
   return hipErrorInvalidValue;
 }
 
 template <int BITS>
 hipError_t launch_bits(bool kch, bool vch, int group, int batch, int hkv, const SplitArgs& sa, hipStream_t stream,
-                       int* per_cu) {
+                       int* per_cu, const LaunchEvents& ev) {
   if (kch) {
-    return vch ? launch_g<BITS, true, true>(group, batch, hkv, sa, stream, per_cu)
-               : launch_g<BITS, true, false>(group, batch, hkv, sa, stream, per_cu);
+    return vch ? launch_g<BITS, true, true>(group, batch, hkv, sa, stream, per_cu, ev)
+               : launch_g<BITS, true, false>(group, batch, hkv, sa, stream, per_cu, ev);
   }
-  return vch ? launch_g<BITS, false, true>(group, batch, hkv, sa, stream, per_cu)
-             : launch_g<BITS, false, false>(group, batch, hkv, sa, stream, per_cu);
+  return vch ? launch_g<BITS, false, true>(group, batch, hkv, sa, stream, per_cu, ev)
+             : launch_g<BITS, false, false>(group, batch, hkv, sa, stream, per_cu, ev);
 }
 
 }  // namespace
 
 hipError_t launch_decode(int bits, bool k_channel, bool v_channel, int group, int batch, int hkv,
-                         const SplitArgs& sa, hipStream_t stream) {
-  if (bits == 2) return launch_bits<2>(k_channel, v_channel, group, batch, hkv, sa, stream, nullptr);
-  return launch_bits<4>(k_channel, v_channel, group, batch, hkv, sa, stream, nullptr);
+                         const SplitArgs& sa, hipStream_t stream, const LaunchEvents& ev) {
+  if (bits == 2) return launch_bits<2>(k_channel, v_channel, group, batch, hkv, sa, stream, nullptr, ev);
+  return launch_bits<4>(k_channel, v_channel, group, batch, hkv, sa, stream, nullptr, ev);
 }
 
 hipError_t decode_occupancy(int bits, bool k_channel, bool v_channel, int group, int* per_cu) {
   SplitArgs sa{};
-  if (bits == 2) return launch_bits<2>(k_channel, v_channel, group, 0, 0, sa, nullptr, per_cu);
-  return launch_bits<4>(k_channel, v_channel, group, 0, 0, sa, nullptr, per_cu);
+  const LaunchEvents none{};
+  if (bits == 2) return launch_bits<2>(k_channel, v_channel, group, 0, 0, sa, nullptr, per_cu, none);
+  return launch_bits<4>(k_channel, v_channel, group, 0, 0, sa, nullptr, per_cu, none);
 }
 
 }  // namespace foscar

@@ -35,8 +35,13 @@ struct SplitArgs {
   float sm_log2;             // sm_scale * log2(e)
 };
 
+// Events the dispatch records around the kernel (either may be null).
+struct LaunchEvents {
+  hipEvent_t start = nullptr;
+  hipEvent_t stop = nullptr;
+};
 hipError_t launch_decode(int bits, bool k_channel, bool v_channel, int group, int batch, int hkv,
-                         const SplitArgs& sa, hipStream_t stream);
+                         const SplitArgs& sa, hipStream_t stream, const LaunchEvents& ev);
 
 // Work-groups of the decode kernel for (bits, layout sides, group) one CU holds at once.
 hipError_t decode_occupancy(int bits, bool k_channel, bool v_channel, int group, int* per_cu);

@@ -154,6 +154,14 @@ void foscar_release(void);
  * the count is capped at 512 ranges and at one range per 64-token unit. */
 int foscar_split_plan(const foscar_dims* dims, int layout, int group, int32_t* splits, int32_t* chunk);
 
+/* Timing: the next foscar_decode_int2/int4 call on this host thread records
+ * start_event / stop_event (hipEvent_t created by the caller; either may be
+ * NULL) as part of its kernel dispatch, so their elapsed time is the decode
+ * kernel's own duration, without the queue's gaps around it.  The request is
+ * consumed by that call whether or not it launches (an empty batch or an
+ * argument error launches nothing).  Always FOSCAR_OK. */
+int foscar_record_next_launch(void* start_event, void* stop_event);
+
 /* Work-groups of the decode kernel for (bits, layout, group) that one compute
  * unit of the current device holds at once (registers and LDS permitting).
  * Reporting only; FOSCAR_EUNSUPPORTED for bits/group outside the supported
