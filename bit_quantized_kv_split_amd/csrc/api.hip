@@ -57,6 +57,8 @@ int check_decode_shape(const foscar_dims* d, int layout, int group) {
   if (rc) return rc;
   if (layout < 0 || layout > 3) return FOSCAR_EINVAL;
   if (!valid_group(group)) return FOSCAR_EUNSUPPORTED;
+  // one grid row of work-groups per (sequence, KV head); per-head byte offsets are 32-bit
+  if ((int64_t)d->batch * d->num_kv_heads > (1 << 22) || d->max_seq_len > (1 << 24)) return FOSCAR_EUNSUPPORTED;
   if (d->max_seq_len % foscar::kTile != 0) return FOSCAR_EUNSUPPORTED;
   if (layout != 0 && d->max_seq_len % group != 0) return FOSCAR_EUNSUPPORTED;
   return FOSCAR_OK;

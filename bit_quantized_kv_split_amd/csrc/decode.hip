@@ -409,9 +409,12 @@ void split_decode(const SplitArgs a) {
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int split = blockIdx.x;
-  const int h = blockIdx.y;
-  const int b = blockIdx.z;
+  // grid x = (sequence, KV head) pairs, y = ranges: consecutive work-groups go
+  // to different XCDs, so each XCD gets whole (sequence, KV head) columns of
+  // ranges and a ragged batch's first ranges do not all land on one XCD
+  const int split = blockIdx.y;
+  const int h = blockIdx.x % a.hkv;
+  const int b = blockIdx.x / a.hkv;
   const int T = min(max(a.seq_lens[b], 0), a.tcap);
   const int r0 = split * a.chunk;
   if (r0 >= T) {  // ranges at or past T hold no token; an empty sequence is written by range 0
@@ -1064,7 +1067,7 @@ hipError_t launch_one(int batch, int hkv, const SplitArgs& sa, hipStream_t strea
   static_assert(lds >= sizeof(float) * kWaves * 4 * kHeadDim, "rings must hold the epilogue buffer");
   if (per_cu)
     return hipOccupancyMaxActiveBlocksPerMultiprocessor(per_cu, split_decode<BITS, KCH, VCH, GRP>, kWaves * 64, lds);
-  dim3 grid(sa.splits, hkv, batch);
+  dim3 grid(batch * hkv, sa.splits);
   if (ev.start || ev.stop)  // timing events recorded by the dispatch itself
     hipExtLaunchKernelGGL((split_decode<BITS, KCH, VCH, GRP>), grid, dim3(kWaves * 64), lds, stream, ev.start, ev.stop,
                           0, sa);

@@ -51,7 +51,8 @@ extern "C" {
 #define FOSCAR_EINVAL (-1)       /* null pointer, negative size, bad layout/side/bits value, Hq % Hkv != 0 */
 #define FOSCAR_EUNSUPPORTED (-2) /* head_dim != 128, group not in {32,64,128}, Hq/Hkv > 4,
                                     max_seq_len not a multiple of 64 (and of group for a
-                                    channel-wise side) */
+                                    channel-wise side), max_seq_len > 2^24,
+                                    batch * num_kv_heads > 2^22 */
 #define FOSCAR_EHIP (-3)         /* a HIP call failed; foscar_last_hip_error() has its code */
 #define FOSCAR_ENOMEM (-4)       /* workspace allocation failed */
 

@@ -56,6 +56,8 @@ def _decode(lib, dims, layout=0, group=128, ptr=1):
 
 
 @pytest.mark.parametrize("kw,layout,group,code", [
+    (dict(batch=1 << 20, num_q_heads=8, num_kv_heads=8), 0, 128, -2),
+    (dict(max_seq_len=1 << 25), 0, 128, -2),
     (dict(head_dim=64), 0, 128, -2),
     (dict(num_q_heads=6, num_kv_heads=4), 0, 128, -1),
     (dict(num_q_heads=16, num_kv_heads=2), 0, 128, -2),     # 8 query heads per KV head
