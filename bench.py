@@ -133,8 +133,8 @@ def main():
     stage_s = time.perf_counter() - t_stage
     layout = fos.layout_bits(spec.k_layout, spec.v_layout)
     dims = fos.make_dims(spec.batch, spec.num_q_heads, spec.num_kv_heads, spec.head_dim, spec.max_seq_len)
-    fos.foscar_workspace_reserve(dims, layout, spec.group)
-    splits, chunk = fos.foscar_split_plan(dims, layout, spec.group)
+    fos.foscar_workspace_reserve(dims, spec.bits, layout, spec.group)
+    splits, chunk = fos.foscar_split_plan(dims, spec.bits, layout, spec.group)
     outs = [(torch.empty((spec.batch, spec.num_q_heads, spec.head_dim), dtype=torch.bfloat16, device=dev_name),
              torch.empty((spec.batch, spec.num_q_heads), dtype=torch.float32, device=dev_name)) for _ in copies]
     # one prepared call per cache copy: arguments checked and marshalled once, a step is one C call

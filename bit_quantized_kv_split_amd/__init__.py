@@ -214,18 +214,18 @@ def foscar_scale_count(side, side_layout, group, dims):
     return int(_lib.load().foscar_scale_count(int(side), int(side_layout), int(group), ctypes.byref(dims)))
 
 
-def foscar_workspace_reserve(dims, layout, group, stream=None):
-    _check(_lib.load().foscar_workspace_reserve(ctypes.byref(dims), int(layout), int(group), _stream(stream)),
-           "foscar_workspace_reserve")
+def foscar_workspace_reserve(dims, bits, layout, group, stream=None):
+    _check(_lib.load().foscar_workspace_reserve(ctypes.byref(dims), int(bits), int(layout), int(group),
+                                                _stream(stream)), "foscar_workspace_reserve")
 
 
 def foscar_release():
     _lib.load().foscar_release()
 
 
-def foscar_split_plan(dims, layout, group):
+def foscar_split_plan(dims, bits, layout, group):
     s, c = ctypes.c_int32(0), ctypes.c_int32(0)
-    _check(_lib.load().foscar_split_plan(ctypes.byref(dims), int(layout), int(group), ctypes.byref(s),
+    _check(_lib.load().foscar_split_plan(ctypes.byref(dims), int(bits), int(layout), int(group), ctypes.byref(s),
                                          ctypes.byref(c)), "foscar_split_plan")
     return s.value, c.value
 

@@ -48,11 +48,11 @@ def load():
     lib.foscar_packed_bytes.restype = SZ
     lib.foscar_scale_count.argtypes = [I, I, I, D]
     lib.foscar_scale_count.restype = SZ
-    lib.foscar_workspace_reserve.argtypes = [D, I, I, P]
+    lib.foscar_workspace_reserve.argtypes = [D, I, I, I, P]
     lib.foscar_workspace_reserve.restype = I
     lib.foscar_release.argtypes = []
     lib.foscar_release.restype = None
-    lib.foscar_split_plan.argtypes = [D, I, I, ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int32)]
+    lib.foscar_split_plan.argtypes = [D, I, I, I, ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int32)]
     lib.foscar_split_plan.restype = I
     lib.foscar_occupancy.argtypes = [I, I, I, ctypes.POINTER(ctypes.c_int32)]
     lib.foscar_occupancy.restype = I

@@ -31,6 +31,7 @@ struct Workspace {
 std::mutex g_ws_mutex;
 std::map<std::pair<int, void*>, Workspace> g_ws;  // (device, stream) -> workspace
 std::map<int, int> g_cus;                           // device -> compute units
+std::map<long long, int> g_occ;                     // (device, bits, layout, group) -> resident work-groups per CU
 
 int hip_fail(hipError_t e) {
   g_last_hip_error = (int)e;
@@ -77,9 +78,29 @@ int compute_units(int device) {
   return cus;
 }
 
-// Split plan: enough work-groups to fill the chip once, ranges of at most 8192
-// tokens so ragged batches balance, every range a multiple of the wave unit.
-void plan(const foscar_dims* d, int layout, int group, int cus, int32_t* splits, int32_t* chunk) {
+// Work-groups of the (bits, layout, group) kernel one CU of `device` holds at
+// once (cached; 4 when the runtime cannot say, e.g. without a GPU).
+int resident_per_cu(int device, int bits, int layout, int group) {
+  const long long key = (((long long)device * 8 + bits) * 4 + layout) * 256 + group;
+  {
+    std::lock_guard<std::mutex> lk(g_ws_mutex);
+    auto it = g_occ.find(key);
+    if (it != g_occ.end()) return it->second;
+  }
+  int n = 0;
+  if (foscar::decode_occupancy(bits, (layout & FOSCAR_K_CHANNEL) != 0, (layout & FOSCAR_V_CHANNEL) != 0, group, &n) !=
+          hipSuccess || n <= 0)
+    return 4;
+  std::lock_guard<std::mutex> lk(g_ws_mutex);
+  g_occ[key] = n;
+  return n;
+}
+
+// Split plan: one round of work-groups at the kernel's residency (more ranges
+// only add per-range prologue, hand-off and merge work; measured), ranges of
+// at most 4096 tokens so ragged batches balance, every range a multiple of the
+// wave unit.
+void plan(const foscar_dims* d, int layout, int group, int cus, int per_cu, int32_t* splits, int32_t* chunk) {
   const int unit = unit_tokens(layout, group);
   const int tcap = d->max_seq_len;
   const int units = tcap / unit;
@@ -94,9 +115,11 @@ void plan(const foscar_dims* d, int layout, int group, int cus, int32_t* splits,
   if (env && atoi(env) > 0) {
     s = atoi(env);
   } else {
-    const long long target = 4LL * cus;  // one round of work-groups at four resident per CU
+    const long long target = (long long)per_cu * cus;  // one round of resident work-groups
     if (bh > 0) s = (target + bh - 1) / bh;
-    const long long by_len = (tcap + 8191) / 8192;  // ranges of at most 8192 tokens
+    // ranges of at most 4096 tokens: on ragged batches (lengths unknown to the host) shorter
+    // ranges keep the last work-groups short; measured best for long and ragged caches
+    const long long by_len = (tcap + 4095) / 4096;
     if (s < by_len) s = by_len;
   }
   if (s > foscar::kMaxSplits) s = foscar::kMaxSplits;
@@ -173,7 +196,7 @@ int decode_common(int bits, const foscar_dims* d, const void* q, const void* pk,
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return hip_fail(e);
   int32_t splits = 1, chunk = foscar::kTile;
-  plan(d, layout, group, compute_units(dev), &splits, &chunk);
+  plan(d, layout, group, compute_units(dev), resident_per_cu(dev, bits, layout, group), &splits, &chunk);
   int32_t* counters = nullptr;
   float* partials = nullptr;
   rc = get_workspace(counter_bytes(d), partial_bytes(d, splits), (hipStream_t)stream, &counters, &partials);
@@ -271,14 +294,17 @@ size_t foscar_scale_count(int side, int side_layout, int group, const foscar_dim
   return bh * (dims->max_seq_len / group) * dims->head_dim;
 }
 
-int foscar_split_plan(const foscar_dims* dims, int layout, int group, int32_t* splits, int32_t* chunk) {
+int foscar_split_plan(const foscar_dims* dims, int bits, int layout, int group, int32_t* splits, int32_t* chunk) {
   int rc = check_decode_shape(dims, layout, group);
   if (rc) return rc;
+  if (bits != 2 && bits != 4) return FOSCAR_EINVAL;
   if (!splits || !chunk) return FOSCAR_EINVAL;
-  int dev = 0;
-  int cus = 256;
-  if (hipGetDevice(&dev) == hipSuccess) cus = compute_units(dev);
-  plan(dims, layout, group, cus, splits, chunk);
+  int dev = 0, cus = 256, per_cu = 4;
+  if (hipGetDevice(&dev) == hipSuccess) {
+    cus = compute_units(dev);
+    per_cu = resident_per_cu(dev, bits, layout, group);
+  }
+  plan(dims, layout, group, cus, per_cu, splits, chunk);
   return FOSCAR_OK;
 }
 
@@ -300,15 +326,16 @@ int foscar_occupancy(int bits, int layout, int group, int32_t* wgs_per_cu) {
   return FOSCAR_OK;
 }
 
-int foscar_workspace_reserve(const foscar_dims* dims, int layout, int group, void* stream) {
+int foscar_workspace_reserve(const foscar_dims* dims, int bits, int layout, int group, void* stream) {
   int rc = check_decode_shape(dims, layout, group);
   if (rc) return rc;
+  if (bits != 2 && bits != 4) return FOSCAR_EINVAL;
   if (dims->batch == 0) return FOSCAR_OK;
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return hip_fail(e);
   int32_t splits = 1, chunk = 0;
-  plan(dims, layout, group, compute_units(dev), &splits, &chunk);
+  plan(dims, layout, group, compute_units(dev), resident_per_cu(dev, bits, layout, group), &splits, &chunk);
   return get_workspace(counter_bytes(dims), partial_bytes(dims, splits), (hipStream_t)stream, nullptr, nullptr);
 }
 

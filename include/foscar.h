@@ -140,20 +140,23 @@ size_t foscar_scale_count(int side, int side_layout, int group, const foscar_dim
 
 /*
  * Allocate (grow-only) the split workspace that decode calls with these dims,
- * layout and group use on `stream` of the current device, so that no later
- * call of that size allocates.  Synchronous.  FOSCAR_ENOMEM on failure.
+ * bits (2 or 4), layout and group use on `stream` of the current device, so
+ * that no later call of that size allocates.  Synchronous.  FOSCAR_ENOMEM on
+ * failure.
  */
-int foscar_workspace_reserve(const foscar_dims* dims, int layout, int group, void* stream);
+int foscar_workspace_reserve(const foscar_dims* dims, int bits, int layout, int group, void* stream);
 
 /* Free every workspace of the library (all devices and streams).  The caller
  * must make sure no decode call is still running.  Synchronous. */
 void foscar_release(void);
 
-/* Split plan the decode entry points use for these arguments: *splits = number
- * of key/value ranges per (sequence, KV head), *chunk = tokens per range.
+/* Split plan the decode entry points use for these arguments (bits 2 or 4):
+ * *splits = number of key/value ranges per (sequence, KV head), *chunk =
+ * tokens per range.  The plan fills the device once at the kernel's
+ * residency (foscar_occupancy) with ranges of at most 4096 tokens.
  * FOSCAR_SPLITS=<n> in the environment forces n ranges (tuning and tests);
  * the count is capped at 512 ranges and at one range per 64-token unit. */
-int foscar_split_plan(const foscar_dims* dims, int layout, int group, int32_t* splits, int32_t* chunk);
+int foscar_split_plan(const foscar_dims* dims, int bits, int layout, int group, int32_t* splits, int32_t* chunk);
 
 /* Timing: the next foscar_decode_int2/int4 call on this host thread records
  * start_event / stop_event (hipEvent_t created by the caller; either may be

@@ -90,7 +90,7 @@ def test_sizes_and_strings(lib):
     for c, s in [(0, "ok"), (-1, "invalid argument"), (-2, "unsupported"), (-3, "HIP"), (-4, "memory")]:
         assert s in fos.foscar_strerror(c)
     with pytest.raises(ValueError):
-        fos.foscar_split_plan(_dims(head_dim=96), 0, 128)
+        fos.foscar_split_plan(_dims(head_dim=96), 2, 0, 128)
 
 
 def test_split_plan_covers_the_cache(lib, monkeypatch):
@@ -101,11 +101,11 @@ def test_split_plan_covers_the_cache(lib, monkeypatch):
                           (dict(batch=8, num_q_heads=32, num_kv_heads=8, max_seq_len=32768), 3, 128),
                           (dict(), 0, 128)]:
         d = _dims(**kw)
-        s, c = fos.foscar_split_plan(d, layout, g)
+        s, c = fos.foscar_split_plan(d, 2, layout, g)
         unit = g if (layout and g > 64) else 64
         assert c % unit == 0 and s * c >= d.max_seq_len and (s - 1) * c < d.max_seq_len
     monkeypatch.setenv("FOSCAR_SPLITS", "3")
-    s, c = fos.foscar_split_plan(_dims(), 0, 128)
+    s, c = fos.foscar_split_plan(_dims(), 2, 0, 128)
     assert s == 3 and c == 384
 
 
@@ -120,5 +120,12 @@ def test_occupancy_rejects_bad_arguments(lib):
 def test_split_plan_caps_the_range_count(lib, monkeypatch):
     import bit_quantized_kv_split_amd as fos
     monkeypatch.setenv("FOSCAR_SPLITS", "100000")
-    s, c = fos.foscar_split_plan(_dims(max_seq_len=1 << 20), 0, 128)
+    s, c = fos.foscar_split_plan(_dims(max_seq_len=1 << 20), 2, 0, 128)
     assert s == 512 and c == 2048
+
+
+def test_plan_and_reserve_reject_bad_bits(lib):
+    import bit_quantized_kv_split_amd as fos
+    with pytest.raises(ValueError):
+        fos.foscar_split_plan(_dims(), 3, 0, 128)
+    assert lib.foscar_workspace_reserve(ctypes.byref(_dims()), 8, 0, 128, None) == -1

@@ -110,7 +110,7 @@ def test_many_ranges(monkeypatch):
     dev, q, lens = stage_spec(spec)
     import bit_quantized_kv_split_amd as fos
     dims = fos.make_dims(spec.batch, spec.num_q_heads, spec.num_kv_heads, spec.head_dim, spec.max_seq_len)
-    assert fos.foscar_split_plan(dims, fos.layout_bits(spec.k_layout, spec.v_layout), spec.group) == (512, 128)
+    assert fos.foscar_split_plan(dims, spec.bits, fos.layout_bits(spec.k_layout, spec.v_layout), spec.group) == (512, 128)
     out, lse = run(spec, dev)
     ro, rl, vsc = oracle_all(spec, q, lens)
     check(out, lse, ro, rl, "512 ranges", vsc)
