@@ -196,7 +196,8 @@ int decode_common(int bits, const foscar_dims* d, const void* q, const void* pk,
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return hip_fail(e);
   int32_t splits = 1, chunk = foscar::kTile;
-  plan(d, layout, group, compute_units(dev), resident_per_cu(dev, bits, layout, group), &splits, &chunk);
+  const int cus = compute_units(dev), per_cu = resident_per_cu(dev, bits, layout, group);
+  plan(d, layout, group, cus, per_cu, &splits, &chunk);
   int32_t* counters = nullptr;
   float* partials = nullptr;
   rc = get_workspace(counter_bytes(d), partial_bytes(d, splits), (hipStream_t)stream, &counters, &partials);
@@ -224,6 +225,8 @@ int decode_common(int bits, const foscar_dims* d, const void* q, const void* pk,
   sa.splits = splits;
   sa.chunk = chunk;
   sa.sm_log2 = sm * 1.4426950408889634f;
+  // work order only matters when not every work-group is resident at once
+  sa.ordered = ((long long)splits * d->batch * d->num_kv_heads > (long long)cus * per_cu) ? 1 : 0;
 
   e = foscar::launch_decode(bits, (layout & FOSCAR_K_CHANNEL) != 0, (layout & FOSCAR_V_CHANNEL) != 0, group,
                             d->batch, d->num_kv_heads, sa, (hipStream_t)stream, ev);

@@ -386,6 +386,95 @@ __device__ __forceinline__ void merge_ranges(const SplitArgs& a, int b, int h, i
   }
 }
 
+// ---------------------------------------------------------------------------
+// Work order.  The dispatcher starts work-groups in index order, so the index
+// -> (sequence, KV head, range) map decides which work runs last.  With the
+// sequence lengths known only on the device, wave 0 of every work-group maps
+// its index to a work item, longest first: every full range (all of the same
+// length), then the sequences' last partial ranges of more than half a range,
+// then the shorter ones, then one item per (empty sequence, KV head) that
+// writes out = 0 and lse = -inf.  Work-group indices past the items exit.
+// Consecutive indices are different KV heads of one range, which land on
+// different XCDs.  Batches above kMapMaxB sequences, and grids that fit the
+// device in one round (where the order does not matter), keep the grid's own
+// map.
+// ---------------------------------------------------------------------------
+constexpr int kMapMaxB = 1024;  // 64 lanes x 16 sequences
+enum : int { kItemRange = 0, kItemEmpty = 1, kItemNone = 2 };
+
+__device__ __forceinline__ int wave_incl_scan(int v) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int o = __shfl_up(v, d);
+    if (lane >= d) v += o;
+  }
+  return v;
+}
+
+// Run by all 64 lanes of one wave; writes {b, h, range, kind} to item.
+template <int UNIT>
+__device__ __forceinline__ void map_work(const SplitArgs& a, int L, int B, int* item) {
+  const int lane = threadIdx.x & 63;
+  const int K = (B + 63) / 64;  // sequences per lane, <= 16
+  const int hkv = a.hkv, chunk = a.chunk;
+  const int nb = chunk / UNIT;  // units per full range
+  int tl[16];
+  int cnt[4] = {0, 0, 0, 0};  // items of this lane's sequences: full ranges, long / short partials, empty
+#pragma unroll
+  for (int k = 0; k < 16; ++k) {
+    const int bb = lane * K + k;
+    tl[k] = (k < K && bb < B) ? min(max(a.seq_lens[bb], 0), a.tcap) : -1;
+  }
+#pragma unroll
+  for (int k = 0; k < 16; ++k) {
+    const int t = tl[k];
+    if (t < 0) continue;
+    const int pu = (t % chunk + UNIT - 1) / UNIT;
+    cnt[0] += (t / chunk) * hkv;
+    cnt[1] += (pu > 0 && 2 * pu > nb) ? hkv : 0;
+    cnt[2] += (pu > 0 && 2 * pu <= nb) ? hkv : 0;
+    cnt[3] += (t == 0) ? hkv : 0;
+  }
+  int pre[4], base = 0, cls = -1, lc = 0;
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    const int inc = wave_incl_scan(cnt[c]);
+    pre[c] = inc - cnt[c];
+    const int tot = __shfl(inc, 63);
+    if (cls < 0 && L < base + tot) {
+      cls = c;
+      lc = L - base;
+    }
+    base += tot;
+  }
+  if (lane == 0) item[3] = kItemNone;
+  if (cls < 0) return;  // uniform: L is past every item
+  int sel = 0;
+#pragma unroll
+  for (int c = 0; c < 4; ++c) sel = (c == cls) ? pre[c] : sel;
+  int run = sel;  // first item index of this lane's next matching sequence
+#pragma unroll
+  for (int k = 0; k < 16; ++k) {
+    const int t = tl[k];
+    if (t < 0) continue;
+    const int pu = (t % chunk + UNIT - 1) / UNIT;
+    int n = 0;  // items of sequence lane * K + k in class cls
+    if (cls == 0) n = (t / chunk) * hkv;
+    else if (cls == 1) n = (pu > 0 && 2 * pu > nb) ? hkv : 0;
+    else if (cls == 2) n = (pu > 0 && 2 * pu <= nb) ? hkv : 0;
+    else n = (t == 0) ? hkv : 0;
+    if (lc >= run && lc < run + n) {
+      const int o = lc - run;
+      item[0] = lane * K + k;
+      item[1] = o % hkv;
+      item[2] = (cls == 0) ? o / hkv : (cls == 3 ? 0 : t / chunk);
+      item[3] = (cls == 3) ? kItemEmpty : kItemRange;
+    }
+    run += n;
+  }
+}
+
 template <int BITS, bool KCH, bool VCH, int GRP>
 constexpr int waves_per_simd() {
   return (BITS == 2 && !KCH && !VCH && GRP == 128) ? 4 : 1;
@@ -409,15 +498,29 @@ void split_decode(const SplitArgs a) {
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  // grid x = (sequence, KV head) pairs, y = ranges: consecutive work-groups go
-  // to different XCDs, so each XCD gets whole (sequence, KV head) columns of
-  // ranges and a ragged batch's first ranges do not all land on one XCD
-  const int split = blockIdx.y;
-  const int h = blockIdx.x % a.hkv;
-  const int b = blockIdx.x / a.hkv;
+  // work item of this work-group (see map_work); for batches above kMapMaxB
+  // sequences the grid's own map: x = (sequence, KV head) pair, y = range
+  int split, h, b, kind = kItemRange;
+  {
+    __shared__ int s_item[4];
+    const int B = gridDim.x / a.hkv;
+    if (a.ordered && B <= kMapMaxB) {
+      if (wave == 0) map_work<UNIT>(a, blockIdx.x + gridDim.x * blockIdx.y, B, s_item);
+      __syncthreads();
+      kind = __builtin_amdgcn_readfirstlane(s_item[3]);
+      if (kind == kItemNone) return;
+      b = __builtin_amdgcn_readfirstlane(s_item[0]);
+      h = __builtin_amdgcn_readfirstlane(s_item[1]);
+      split = __builtin_amdgcn_readfirstlane(s_item[2]);
+    } else {
+      split = blockIdx.y;
+      h = blockIdx.x % a.hkv;
+      b = blockIdx.x / a.hkv;
+    }
+  }
   const int T = min(max(a.seq_lens[b], 0), a.tcap);
   const int r0 = split * a.chunk;
-  if (r0 >= T) {  // ranges at or past T hold no token; an empty sequence is written by range 0
+  if (r0 >= T) {  // no token in this range; an empty sequence's rows are written once
     if (T == 0 && split == 0) {
       for (int idx = threadIdx.x; idx < a.g_heads * kHeadDim; idx += blockDim.x) {
         const size_t row = (size_t)b * a.hq + h * a.g_heads + idx / kHeadDim;

@@ -33,6 +33,7 @@ struct SplitArgs {
   int32_t splits;            // S
   int32_t chunk;             // tokens per range (multiple of the wave unit)
   float sm_log2;             // sm_scale * log2(e)
+  int32_t ordered;           // 1: map work-groups to work longest first (the grid is more than one round)
 };
 
 // Events the dispatch records around the kernel (either may be null).
