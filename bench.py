@@ -39,6 +39,7 @@ def parse():
     ap.add_argument("--copies", type=int, default=2, help="independent cache copies rotated over the steps")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--dump-steps", action="store_true", help="print each step's kernel microseconds to stderr")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="run one plain device copy of this many MiB before warm-up (counter calibration)")
     return ap.parse_args()
@@ -172,6 +173,8 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     kernel_ms = [a.elapsed_time(b) for a, b in ev]
+    if args.dump_steps:
+        print("kernel us per step:", " ".join(f"{x * 1e3:.1f}" for x in kernel_ms), file=sys.stderr)
     ms_per_step = wall * 1e3 / args.steps
     alg = synth.algorithmic_bytes(spec, lens)
     value = alg / (ms_per_step * 1e-3) / 1e9
