@@ -132,8 +132,8 @@ void plan(const foscar_dims* d, int layout, int group, int cus, int per_cu, int3
 
 // A call needs one int32 counter per (sequence, KV head), padded to 256 B,
 // and partials o_part fp32 [B*Hq*S*D] then lse_part fp32 [B*Hq*S].
-size_t counter_bytes(const foscar_dims* d) {
-  return (((size_t)d->batch * d->num_kv_heads * sizeof(int32_t)) + 255) / 256 * 256;
+size_t counter_bytes(const foscar_dims* d) {  // B*Hkv range counters, then the 2 work counters
+  return (((size_t)d->batch * d->num_kv_heads + 2) * sizeof(int32_t) + 255) / 256 * 256;
 }
 size_t partial_bytes(const foscar_dims* d, int32_t splits) {
   const size_t rows = (size_t)d->batch * d->num_q_heads * splits;
@@ -225,8 +225,12 @@ int decode_common(int bits, const foscar_dims* d, const void* q, const void* pk,
   sa.splits = splits;
   sa.chunk = chunk;
   sa.sm_log2 = sm * 1.4426950408889634f;
-  // work order only matters when not every work-group is resident at once
-  sa.ordered = ((long long)splits * d->batch * d->num_kv_heads > (long long)cus * per_cu) ? 1 : 0;
+  // more work-groups than one round: a persistent round takes work items longest first
+  sa.batch = d->batch;
+  sa.grid_wgs = cus * per_cu;
+  sa.persistent = ((long long)splits * d->batch * d->num_kv_heads > (long long)sa.grid_wgs &&
+                   d->batch <= foscar::kMapMaxB) ? 1 : 0;
+  sa.work_ctr = counters + (size_t)d->batch * d->num_kv_heads;
 
   e = foscar::launch_decode(bits, (layout & FOSCAR_K_CHANNEL) != 0, (layout & FOSCAR_V_CHANNEL) != 0, group,
                             d->batch, d->num_kv_heads, sa, (hipStream_t)stream, ev);

@@ -243,18 +243,14 @@ template <int I>
 __device__ __forceinline__ float quad_bcast(float v) {
   return dpp<(I | (I << 2) | (I << 4) | (I << 6))>(v);
 }
-// v of lane l ^ 16 (ds_swizzle bit-mask mode inside each 32-lane half)
-__device__ __forceinline__ float xor16(float v) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, v), 0x401F));
-}
-// v of lane l ^ 32
-__device__ __forceinline__ float xor32(float v) { return __shfl_xor(v, 32); }
-// {v of this lane's counterpart in half-wave 0, in half-wave 1}
+// {v of this lane's counterpart in half-wave 0, in half-wave 1}: v_permlane32_swap
+// leaves the lower half's values in every lane of its first operand and the
+// upper half's in every lane of its second
 __device__ __forceinline__ void halves(float v, float& h0, float& h1) {
-  const float o = xor32(v);
-  const bool lo = (threadIdx.x & 63) < 32;
-  h0 = lo ? v : o;
-  h1 = lo ? o : v;
+  float a = v, b = v;
+  asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(a), "+v"(b));
+  h0 = a;
+  h1 = b;
 }
 // max over rows (0,1) and (2,3) of 16 lanes: v_permlane16_swap trades the odd
 // rows of its first operand with the even rows of its second.  Like DPP, a
@@ -291,12 +287,21 @@ __device__ __forceinline__ float wave_max_same_query(float v) {
   v = fmaxf(v, dpp<0x128>(v));  // row_ror:8
   return max_halves(max_row_pairs(v));
 }
-template <int SPAN>  // sum over the lanes of one query head within SPAN lanes (32: half-wave, 64: wave)
+// sum over the lanes of one query head within SPAN lanes (32: half-wave, 64: wave),
+// with DPP row rotations and v_permlane16/32_swap (no LDS round trip)
+template <int SPAN>
 __device__ __forceinline__ float sum_same_query(float v) {
-  v += dpp<0x124>(v);
-  v += dpp<0x128>(v);
-  v += xor16(v);
-  if (SPAN == 64) v += xor32(v);
+  v += dpp<0x124>(v);  // row_ror:4
+  v += dpp<0x128>(v);  // row_ror:8
+  float a = v, b = v;
+  asm volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1" : "+v"(a), "+v"(b));
+  v = a + b;
+  if (SPAN == 64) {
+    a = v;
+    b = v;
+    asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(a), "+v"(b));
+    v = a + b;
+  }
   return v;
 }
 
@@ -325,8 +330,9 @@ __device__ __forceinline__ float coherent_load(const float* p) {
 __device__ __forceinline__ void merge_ranges(const SplitArgs& a, int b, int h, int ns) {
   constexpr int D = kHeadDim, BLK = 16;
   const int G = a.g_heads;
-  const int c = threadIdx.x & (D - 1);
-  const int i0 = threadIdx.x / D;  // blockDim.x == 2 * D
+  const uint32_t tid = in_vgpr(threadIdx.x);  // opaque: not hoisted out of a work loop
+  const int c = tid & (D - 1);
+  const int i0 = tid / D;  // blockDim.x == 2 * D
   if (i0 >= G) return;
   const bool two = i0 + 2 < G;
   const size_t row0 = (size_t)b * a.hq + (size_t)h * G + i0;
@@ -395,15 +401,12 @@ __device__ __forceinline__ void merge_ranges(const SplitArgs& a, int b, int h, i
 // then the shorter ones, then one item per (empty sequence, KV head) that
 // writes out = 0 and lse = -inf.  Work-group indices past the items exit.
 // Consecutive indices are different KV heads of one range, which land on
-// different XCDs.  Batches above kMapMaxB sequences, and grids that fit the
-// device in one round (where the order does not matter), keep the grid's own
-// map.
+// different XCDs.
 // ---------------------------------------------------------------------------
-constexpr int kMapMaxB = 1024;  // 64 lanes x 16 sequences
 enum : int { kItemRange = 0, kItemEmpty = 1, kItemNone = 2 };
 
 __device__ __forceinline__ int wave_incl_scan(int v) {
-  const int lane = threadIdx.x & 63;
+  const int lane = in_vgpr(threadIdx.x) & 63;
 #pragma unroll
   for (int d = 1; d < 64; d <<= 1) {
     const int o = __shfl_up(v, d);
@@ -415,7 +418,7 @@ __device__ __forceinline__ int wave_incl_scan(int v) {
 // Run by all 64 lanes of one wave; writes {b, h, range, kind} to item.
 template <int UNIT>
 __device__ __forceinline__ void map_work(const SplitArgs& a, int L, int B, int* item) {
-  const int lane = threadIdx.x & 63;
+  const int lane = in_vgpr(threadIdx.x) & 63;  // opaque: nothing here is hoisted out of a work loop
   const int K = (B + 63) / 64;  // sequences per lane, <= 16
   const int hkv = a.hkv, chunk = a.chunk;
   const int nb = chunk / UNIT;  // units per full range
@@ -480,9 +483,10 @@ constexpr int waves_per_simd() {
   return (BITS == 2 && !KCH && !VCH && GRP == 128) ? 4 : 1;
 }
 
+// One work item: range `split` of KV head h of sequence b (T = 0 and split = 0:
+// the empty sequence's rows).  Every return is uniform over the work-group.
 template <int BITS, bool KCH, bool VCH, int GRP>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(waves_per_simd<BITS, KCH, VCH, GRP>())))
-void split_decode(const SplitArgs a) {
+__device__ __forceinline__ void run_item(const SplitArgs& a, const int b, const int h, const int split) {
   using C = Codec<BITS>;
   constexpr int D = kHeadDim;
   constexpr int E = C::E;
@@ -496,33 +500,17 @@ void split_decode(const SplitArgs a) {
   constexpr int UNIT = ((KCH || VCH) && GRP > kTile) ? GRP : kTile;
   constexpr int TPU = UNIT / kTile;
 
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  // work item of this work-group (see map_work); for batches above kMapMaxB
-  // sequences the grid's own map: x = (sequence, KV head) pair, y = range
-  int split, h, b, kind = kItemRange;
-  {
-    __shared__ int s_item[4];
-    const int B = gridDim.x / a.hkv;
-    if (a.ordered && B <= kMapMaxB) {
-      if (wave == 0) map_work<UNIT>(a, blockIdx.x + gridDim.x * blockIdx.y, B, s_item);
-      __syncthreads();
-      kind = __builtin_amdgcn_readfirstlane(s_item[3]);
-      if (kind == kItemNone) return;
-      b = __builtin_amdgcn_readfirstlane(s_item[0]);
-      h = __builtin_amdgcn_readfirstlane(s_item[1]);
-      split = __builtin_amdgcn_readfirstlane(s_item[2]);
-    } else {
-      split = blockIdx.y;
-      h = blockIdx.x % a.hkv;
-      b = blockIdx.x / a.hkv;
-    }
-  }
+  // lane and wave pass through an opaque register: in a persistent loop the
+  // compiler would otherwise hoist every per-lane address and constant of the
+  // item out of the loop and keep them live through the tile loop
+  const uint32_t tid = in_vgpr(threadIdx.x);
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int T = min(max(a.seq_lens[b], 0), a.tcap);
   const int r0 = split * a.chunk;
   if (r0 >= T) {  // no token in this range; an empty sequence's rows are written once
     if (T == 0 && split == 0) {
-      for (int idx = threadIdx.x; idx < a.g_heads * kHeadDim; idx += blockDim.x) {
+      for (int idx = (int)tid; idx < a.g_heads * kHeadDim; idx += blockDim.x) {
         const size_t row = (size_t)b * a.hq + h * a.g_heads + idx / kHeadDim;
         a.out[row * kHeadDim + idx % kHeadDim] = 0;
         if (idx % kHeadDim == 0 && a.lse) a.lse[row] = -INFINITY;
@@ -1113,7 +1101,7 @@ void split_decode(const SplitArgs a) {
 
   // ---------------- work-group merge of the 4 waves -> this range's (O, lse)
   const int ns = (T + a.chunk - 1) / a.chunk;  // ranges holding tokens of this sequence
-  for (int idx = threadIdx.x; idx < 4 * D; idx += blockDim.x) {
+  for (int idx = (int)tid; idx < 4 * D; idx += blockDim.x) {
     const int i = idx / D, c = idx % D;
     if (i >= a.g_heads) continue;
     float M = -INFINITY;
@@ -1151,14 +1139,56 @@ void split_decode(const SplitArgs a) {
   __shared__ int s_last;
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
-  if (threadIdx.x == 0) {
+  if (tid == 0) {
     const int done = __hip_atomic_fetch_add(a.counters + bh, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     s_last = (done == ns - 1);
   }
   __syncthreads();
   if (!s_last) return;
   merge_ranges(a, b, h, ns);
-  if (threadIdx.x == 0) a.counters[bh] = 0;  // ready for the next call on this workspace
+  if (tid == 0) a.counters[bh] = 0;  // ready for the next call on this workspace
+}
+
+// Grids that fit the device in one round: the grid's own map (x = (sequence,
+// KV head) pair, y = range; consecutive work-groups land on different XCDs).
+// Larger grids (ragged batches of at most kMapMaxB sequences) run persistent:
+// one round of work-groups takes work items from a device-wide counter, longest
+// first (map_work), until the items run out; the last work-group to leave
+// resets the counters for the next call.
+template <int BITS, bool KCH, bool VCH, int GRP>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(waves_per_simd<BITS, KCH, VCH, GRP>())))
+void split_decode(const SplitArgs a) {
+  constexpr int UNIT = ((KCH || VCH) && GRP > kTile) ? GRP : kTile;
+  if (!a.persistent) {
+    run_item<BITS, KCH, VCH, GRP>(a, blockIdx.x / a.hkv, blockIdx.x % a.hkv, blockIdx.y);
+    return;
+  }
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  __shared__ int s_idx;
+  __shared__ int s_item[4];
+  for (;;) {
+    if (threadIdx.x == 0)
+      s_idx = __hip_atomic_fetch_add(a.work_ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    const int idx = __builtin_amdgcn_readfirstlane(s_idx);
+    if (wave == 0) map_work<UNIT>(a, idx, a.batch, s_item);
+    __syncthreads();
+    const int kind = __builtin_amdgcn_readfirstlane(s_item[3]);
+    const int b = __builtin_amdgcn_readfirstlane(s_item[0]);
+    const int h = __builtin_amdgcn_readfirstlane(s_item[1]);
+    const int split = __builtin_amdgcn_readfirstlane(s_item[2]);
+    __syncthreads();  // s_idx and s_item are read before the next item rewrites them
+    if (kind == kItemNone) break;
+    run_item<BITS, KCH, VCH, GRP>(a, b, h, split);
+    __syncthreads();  // the item's LDS is free
+  }
+  if (threadIdx.x == 0) {
+    const int left = __hip_atomic_fetch_add(a.work_ctr + 1, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (left == (int)(gridDim.x * gridDim.y) - 1) {  // every other work-group has left: no more grabs
+      __hip_atomic_store(a.work_ctr, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(a.work_ctr + 1, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
 }
 
 // Launch the instantiation on `stream`, or (per_cu != nullptr) report how many
@@ -1170,7 +1200,7 @@ hipError_t launch_one(int batch, int hkv, const SplitArgs& sa, hipStream_t strea
   static_assert(lds >= sizeof(float) * kWaves * 4 * kHeadDim, "rings must hold the epilogue buffer");
   if (per_cu)
     return hipOccupancyMaxActiveBlocksPerMultiprocessor(per_cu, split_decode<BITS, KCH, VCH, GRP>, kWaves * 64, lds);
-  dim3 grid(batch * hkv, sa.splits);
+  const dim3 grid = sa.persistent ? dim3(sa.grid_wgs) : dim3(batch * hkv, sa.splits);
   if (ev.start || ev.stop)  // timing events recorded by the dispatch itself
     hipExtLaunchKernelGGL((split_decode<BITS, KCH, VCH, GRP>), grid, dim3(kWaves * 64), lds, stream, ev.start, ev.stop,
                           0, sa);

@@ -10,6 +10,7 @@ constexpr int kHeadDim = 128;   // D
 constexpr int kTile = 64;       // tokens per wave tile (16 quads of 4)
 constexpr int kWaves = 4;       // waves per work-group
 constexpr int kMaxG = 4;        // query heads per KV head served by one wave
+constexpr int kMapMaxB = 1024;   // largest batch the device-side work order handles (64 lanes x 16)
 constexpr int kMaxSplits = 512;  // ranges per sequence (bounds the workspace and the merge passes)
 
 // Arguments of the decode kernel (one work-group per (range, KV head, sequence)).
@@ -33,7 +34,10 @@ struct SplitArgs {
   int32_t splits;            // S
   int32_t chunk;             // tokens per range (multiple of the wave unit)
   float sm_log2;             // sm_scale * log2(e)
-  int32_t ordered;           // 1: map work-groups to work longest first (the grid is more than one round)
+  int32_t persistent;        // 1: grid_wgs work-groups take work items from work_ctr (see split_decode)
+  int32_t grid_wgs;          // persistent grid size (one round of resident work-groups)
+  int32_t batch;             // B
+  int32_t* work_ctr;         // [2] items taken, work-groups left; zero between calls
 };
 
 // Events the dispatch records around the kernel (either may be null).

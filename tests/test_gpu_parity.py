@@ -10,7 +10,7 @@ import numpy as np
 import pytest
 
 import synth
-from gpu_util import check, oracle_all, oracle_rows, run, stage_spec
+from gpu_util import check, oracle_all, oracle_rows, run, stage_spec, value_rms
 
 pytestmark = pytest.mark.gpu
 
@@ -155,3 +155,39 @@ def test_full_size_sampled_rows(name):
     for n, (b, i) in enumerate(rows):
         check(out[b, i][None], lse[b, i][None], ro[n][None], rl[n][None], f"{name} row {(b, i)}", vsc[n][None])
     assert np.all(np.isfinite(out))
+
+
+def test_persistent_work_order_ragged_with_empty_sequences():
+    """A batch whose plan needs more work-groups than one round runs the
+    persistent, longest-first path: every row (including empty sequences and
+    sequences of a few tokens) must match the oracle, on two calls in a row."""
+    import bit_quantized_kv_split_amd as fos
+    import oracle
+    import torch
+    lens = [0, 3, 32768, 1, 20000, 0, 4096, 4097, 12000, 64, 65, 30000, 0, 8191, 100, 32767] * 4
+    spec = _spec("c5_ragged_int2_g64", batch=len(lens), num_q_heads=8, num_kv_heads=2, max_seq_len=32768,
+                 lens=tuple(lens))
+    dims = fos.make_dims(spec.batch, spec.num_q_heads, spec.num_kv_heads, spec.head_dim, spec.max_seq_len)
+    layout = fos.layout_bits(spec.k_layout, spec.v_layout)
+    s, c = fos.foscar_split_plan(dims, spec.bits, layout, spec.group)
+    per_cu = fos.foscar_occupancy(spec.bits, layout, spec.group)
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    assert s * spec.batch * spec.num_kv_heads > per_cu * cus, "the plan must need more than one round"
+    dev, q, lens_np = stage_spec(spec, poison=True)
+    G = spec.num_q_heads // spec.num_kv_heads
+    ro = np.zeros((spec.batch, spec.num_q_heads, spec.head_dim))
+    rl = np.zeros((spec.batch, spec.num_q_heads))
+    vsc = np.zeros_like(ro)
+    for b in range(spec.batch):
+        for h in range(spec.num_kv_heads):
+            head = synth.make_head(spec, b, h, seq_len=int(lens_np[b]), poison=True)
+            w = {k: v[None, None] for k, v in head.items()}
+            w["q"] = q[b:b + 1, h * G:(h + 1) * G]
+            w["seq_lens"] = np.array([lens_np[b]], np.int32)
+            o, l = oracle.decode_rows(w, [(0, i) for i in range(G)], k_layout=spec.k_layout, v_layout=spec.v_layout,
+                                      group=spec.group, sm_scale=spec.sm_scale)
+            ro[b, h * G:(h + 1) * G], rl[b, h * G:(h + 1) * G] = o, l
+            vsc[b, h * G:(h + 1) * G] = value_rms(spec, head, int(lens_np[b]))
+    for k in range(2):
+        out, lse = run(spec, dev)
+        check(out, lse, ro, rl, f"persistent ragged call {k}", vsc)
