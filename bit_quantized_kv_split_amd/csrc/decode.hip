@@ -324,17 +324,20 @@ __device__ __forceinline__ float coherent_load(const float* p) {
 // work-group that finished last: O = sum_s exp(lse_s - M) O_s / sum_s exp(lse_s - M),
 // lse = M + log(sum_s exp(lse_s - M)).  The partials were written by other
 // work-groups, so they are read with device-coherent loads.  Thread t owns
-// channel t % 128 of query rows t / 128 and t / 128 + 2 and streams the
-// ranges in blocks of 16: each block's lse and partial outputs are loaded
-// together (one memory round trip per block), then folded into a running max.
+// channel t % 128 of query row t / 128 (and of row t / 128 + 2 with 256
+// threads) and streams the ranges in blocks of 16: each block's lse and
+// partial outputs are loaded together (one memory round trip per block), then
+// folded into a running max.
 __device__ __forceinline__ void merge_ranges(const SplitArgs& a, int b, int h, int ns) {
   constexpr int D = kHeadDim, BLK = 16;
   const int G = a.g_heads;
   const uint32_t tid = in_vgpr(threadIdx.x);  // opaque: not hoisted out of a work loop
   const int c = tid & (D - 1);
-  const int i0 = tid / D;  // blockDim.x == 2 * D
+  constexpr int RS = kWaves * 64 / D;  // rows one pass of the work-group covers
+  static_assert(RS == 2 || RS == 4, "two or four rows per pass");
+  const int i0 = tid / D;
   if (i0 >= G) return;
-  const bool two = i0 + 2 < G;
+  const bool two = RS == 2 && i0 + 2 < G;
   const size_t row0 = (size_t)b * a.hq + (size_t)h * G + i0;
   const size_t row1 = two ? row0 + 2 : row0;
   const float* lp0 = a.lse_part + row0 * a.splits;
@@ -547,11 +550,12 @@ __device__ __forceinline__ void run_item(const SplitArgs& a, const int b, const 
   float kq_sum[NGK], kq_bias[NGK];
   auto query_prologue = [&]() {  // run after the first tiles are in flight, so the two HBM latencies overlap
    if constexpr (KCH) {
-    s_qb[wave][lane] = (wave < a.g_heads)
-        ? reinterpret_cast<const uint32_t*>(a.q + ((size_t)b * a.hq + h * a.g_heads + wave) * D)[lane] : 0u;
+    if (wave < 4)
+      s_qb[wave][lane] = (wave < a.g_heads)
+          ? reinterpret_cast<const uint32_t*>(a.q + ((size_t)b * a.hq + h * a.g_heads + wave) * D)[lane] : 0u;
     __syncthreads();
    } else {
-    {  // wave i converts query head i, lane j its channel pair j
+    if (wave < 4) {  // wave i converts query head i, lane j its channel pair j
       const int qi = wave, pj = lane;
       uint32_t w = 0;
       if (qi < a.g_heads) w = reinterpret_cast<const uint32_t*>(a.q + ((size_t)b * a.hq + h * a.g_heads + qi) * D)[pj];
@@ -1156,7 +1160,7 @@ __device__ __forceinline__ void run_item(const SplitArgs& a, const int b, const 
 // first (map_work), until the items run out; the last work-group to leave
 // resets the counters for the next call.
 template <int BITS, bool KCH, bool VCH, int GRP>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(waves_per_simd<BITS, KCH, VCH, GRP>())))
+__global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(waves_per_simd<BITS, KCH, VCH, GRP>())))
 void split_decode(const SplitArgs a) {
   constexpr int UNIT = ((KCH || VCH) && GRP > kTile) ? GRP : kTile;
   if (!a.persistent) {
@@ -1198,6 +1202,19 @@ hipError_t launch_one(int batch, int hkv, const SplitArgs& sa, hipStream_t strea
   using ST = Stage<BITS, KCH, VCH, GRP>;
   constexpr size_t lds = (size_t)kWaves * ST::NS * ST::BYTES;
   static_assert(lds >= sizeof(float) * kWaves * 4 * kHeadDim, "rings must hold the epilogue buffer");
+  // the work-group's LDS (static + rings) must fit one CU, or the dispatch
+  // would be rejected on the device and abort the queue: refuse it here
+  static int lds_ok = -1;  // per instantiation: -1 unknown, 0 too big, 1 fits
+  if (lds_ok < 0) {
+    hipFuncAttributes fa;
+    int dev = 0, cu_lds = 0;
+    if (hipFuncGetAttributes(&fa, reinterpret_cast<const void*>(split_decode<BITS, KCH, VCH, GRP>)) != hipSuccess ||
+        hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cu_lds, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor, dev) != hipSuccess)
+      return hipErrorInvalidDeviceFunction;
+    lds_ok = (fa.sharedSizeBytes + lds <= (size_t)cu_lds) ? 1 : 0;
+  }
+  if (!lds_ok) return hipErrorInvalidConfiguration;
   if (per_cu)
     return hipOccupancyMaxActiveBlocksPerMultiprocessor(per_cu, split_decode<BITS, KCH, VCH, GRP>, kWaves * 64, lds);
   const dim3 grid = sa.persistent ? dim3(sa.grid_wgs) : dim3(batch * hkv, sa.splits);
