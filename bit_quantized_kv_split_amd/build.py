@@ -3,7 +3,11 @@
     python -m bit_quantized_kv_split_amd.build        # or build() from Python
 
 Every source is compiled with packed fp32 arithmetic disabled
-(-Xclang -target-feature -Xclang -packed-fp32-ops).
+(-Xclang -target-feature -Xclang -packed-fp32-ops) and without the compiler's
+wave-level atomic rewrite (-amdgpu-atomic-optimizer-strategy=None): every
+atomic here runs in one lane, and the rewrite makes the issuing wave wait for
+the result right away, where the kernels issue a work-counter increment early
+and read it much later.
 """
 import os
 import shutil
@@ -20,6 +24,7 @@ ARCH = os.environ.get("FOSCAR_ARCH", "gfx950")
 
 FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+         "-mllvm", "-amdgpu-atomic-optimizer-strategy=None",
          "-Wno-unused-command-line-argument"]
 
 

@@ -400,84 +400,123 @@ __device__ __forceinline__ void merge_ranges(const SplitArgs& a, int b, int h, i
 // -> (sequence, KV head, range) map decides which work runs last.  With the
 // sequence lengths known only on the device, wave 0 of every work-group maps
 // its index to a work item, longest first: every full range (all of the same
-// length), then the sequences' last partial ranges of more than half a range,
-// then the shorter ones, then one item per (empty sequence, KV head) that
-// writes out = 0 and lse = -inf.  Work-group indices past the items exit.
+// length), then the sequences' last partial ranges in eight length buckets,
+// longest first, then one item per (empty sequence, KV head) that writes
+// out = 0 and lse = -inf.  Work-group indices past the items exit.
 // Consecutive indices are different KV heads of one range, which land on
 // different XCDs.
 // ---------------------------------------------------------------------------
 enum : int { kItemRange = 0, kItemEmpty = 1, kItemNone = 2 };
 
+// Inclusive prefix sum over the 64 lanes: Hillis-Steele inside each row of 16
+// (DPP row_shr 1, 2, 4, 8 with zero fill), then row_bcast:15 carries row 0's
+// total into row 1 and row 2's into row 3, and row_bcast:31 carries the total
+// of rows 0-1 into rows 2-3.
+template <int CTRL, int ROWS>
+__device__ __forceinline__ int dpp_in(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, CTRL, ROWS, 0xf, CTRL < 0x140);
+}
 __device__ __forceinline__ int wave_incl_scan(int v) {
-  const int lane = in_vgpr(threadIdx.x) & 63;
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const int o = __shfl_up(v, d);
-    if (lane >= d) v += o;
-  }
+  v += dpp_in<0x111, 0xf>(v);
+  v += dpp_in<0x112, 0xf>(v);
+  v += dpp_in<0x114, 0xf>(v);
+  v += dpp_in<0x118, 0xf>(v);
+  v += dpp_in<0x142, 0xa>(v);
+  v += dpp_in<0x143, 0xc>(v);
   return v;
 }
 
-// Run by all 64 lanes of one wave; writes {b, h, range, kind} to item.
-template <int UNIT>
-__device__ __forceinline__ void map_work(const SplitArgs& a, int L, int B, int* item) {
+// Work classes in dispatch order: full ranges, then each sequence's last
+// partial range by length (kPartBuckets buckets, longest first), then empty
+// sequences.
+constexpr int kPartBuckets = 8;
+constexpr int kClasses = 2 + kPartBuckets;
+
+// x / d for 0 <= x <= 2^24 and d >= 1, given r = 1/d rounded to float: the
+// float product is within one of x / d, so one correction each way makes the
+// truncated quotient exact (d = 1 and 2 have exact reciprocals).
+__device__ __forceinline__ int div_u24(int x, int d, float r) {
+  int q = (int)((float)x * r);
+  const int m = x - q * d;
+  q += (m >= d) ? 1 : 0;
+  q -= (m < 0) ? 1 : 0;
+  return q;
+}
+
+// Length granule of the work classes: the tile, or the channel-wise group
+// when that is longer (ranges hold whole groups).
+template <bool KCH, bool VCH, int GRP>
+constexpr int work_unit() { return ((KCH || VCH) && GRP > kTile) ? GRP : kTile; }
+
+struct NextLoad {
+  int idx;     // lane 0: the work index
+  int tl[16];  // raw lengths of sequences lane * K + k (K = ceil(B / 64)) below B
+};
+__device__ __forceinline__ void next_load(const SplitArgs& a, NextLoad& n) {
   const int lane = in_vgpr(threadIdx.x) & 63;  // opaque: nothing here is hoisted out of a work loop
-  const int K = (B + 63) / 64;  // sequences per lane, <= 16
-  const int hkv = a.hkv, chunk = a.chunk;
-  const int nb = chunk / UNIT;  // units per full range
-  int tl[16];
-  int cnt[4] = {0, 0, 0, 0};  // items of this lane's sequences: full ranges, long / short partials, empty
+  const int B = a.batch, K = (B + 63) / 64;    // sequences per lane, <= 16
+  n.idx = 0;
+  if (lane == 0) n.idx = __hip_atomic_fetch_add(a.work_ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 #pragma unroll
   for (int k = 0; k < 16; ++k) {
     const int bb = lane * K + k;
-    tl[k] = (k < K && bb < B) ? min(max(a.seq_lens[bb], 0), a.tcap) : -1;
+    n.tl[k] = (k < K && bb < B) ? a.seq_lens[bb] : 0;
   }
+}
+
+template <int UNIT>
+__device__ __forceinline__ void map_select(const SplitArgs& a, const NextLoad& n, int* item) {
+  const int lane = in_vgpr(threadIdx.x) & 63;
+  const int K = (a.batch + 63) / 64;
+  const int hkv = a.hkv, chunk = a.chunk;
+  const int nb = chunk / UNIT;  // units per full range
+  const float rc = 1.0f / (float)chunk, rn = 1.0f / (float)nb;
+  const int L = __builtin_amdgcn_readfirstlane(n.idx);
+  int nf[16], pc[16];  // per sequence: full ranges; class of the last partial range (-1: none, -2: no sequence)
+  int cnt[kClasses];   // items of this lane's sequences per class
+#pragma unroll
+  for (int c = 0; c < kClasses; ++c) cnt[c] = 0;
 #pragma unroll
   for (int k = 0; k < 16; ++k) {
-    const int t = tl[k];
-    if (t < 0) continue;
-    const int pu = (t % chunk + UNIT - 1) / UNIT;
-    cnt[0] += (t / chunk) * hkv;
-    cnt[1] += (pu > 0 && 2 * pu > nb) ? hkv : 0;
-    cnt[2] += (pu > 0 && 2 * pu <= nb) ? hkv : 0;
-    cnt[3] += (t == 0) ? hkv : 0;
-  }
-  int pre[4], base = 0, cls = -1, lc = 0;
+    nf[k] = 0;
+    pc[k] = -2;
+    if (!(k < K && lane * K + k < a.batch)) continue;
+    const int t = min(max(n.tl[k], 0), a.tcap);
+    nf[k] = div_u24(t, chunk, rc);
+    const int pu = (t - nf[k] * chunk + UNIT - 1) / UNIT;  // units of the partial range
+    pc[k] = (t == 0) ? kClasses - 1 : (pu == 0) ? -1 : kPartBuckets - div_u24((pu - 1) * kPartBuckets, nb, rn);
+    cnt[0] += nf[k] * hkv;
 #pragma unroll
-  for (int c = 0; c < 4; ++c) {
+    for (int c = 1; c < kClasses; ++c) cnt[c] += (pc[k] == c) ? hkv : 0;
+  }
+  int base = 0, cls = -1, lc = 0, sel = 0;
+#pragma unroll
+  for (int c = 0; c < kClasses; ++c) {
     const int inc = wave_incl_scan(cnt[c]);
-    pre[c] = inc - cnt[c];
     const int tot = __shfl(inc, 63);
     if (cls < 0 && L < base + tot) {
       cls = c;
       lc = L - base;
+      sel = inc - cnt[c];  // this lane's first item in the class
     }
     base += tot;
   }
   if (lane == 0) item[3] = kItemNone;
   if (cls < 0) return;  // uniform: L is past every item
-  int sel = 0;
-#pragma unroll
-  for (int c = 0; c < 4; ++c) sel = (c == cls) ? pre[c] : sel;
-  int run = sel;  // first item index of this lane's next matching sequence
+  int run = sel;
 #pragma unroll
   for (int k = 0; k < 16; ++k) {
-    const int t = tl[k];
-    if (t < 0) continue;
-    const int pu = (t % chunk + UNIT - 1) / UNIT;
-    int n = 0;  // items of sequence lane * K + k in class cls
-    if (cls == 0) n = (t / chunk) * hkv;
-    else if (cls == 1) n = (pu > 0 && 2 * pu > nb) ? hkv : 0;
-    else if (cls == 2) n = (pu > 0 && 2 * pu <= nb) ? hkv : 0;
-    else n = (t == 0) ? hkv : 0;
-    if (lc >= run && lc < run + n) {
+    if (pc[k] == -2) continue;
+    const int m = (cls == 0) ? nf[k] * hkv : (pc[k] == cls) ? hkv : 0;  // items of this sequence in class cls
+    if (lc >= run && lc < run + m) {
       const int o = lc - run;
       item[0] = lane * K + k;
       item[1] = o % hkv;
-      item[2] = (cls == 0) ? o / hkv : (cls == 3 ? 0 : t / chunk);
-      item[3] = (cls == 3) ? kItemEmpty : kItemRange;
+      item[2] = (cls == 0) ? o / hkv : (cls == kClasses - 1) ? 0 : nf[k];
+      item[3] = (cls == kClasses - 1) ? kItemEmpty : kItemRange;
+      item[4] = min(max(n.tl[k], 0), a.tcap);
     }
-    run += n;
+    run += m;
   }
 }
 
@@ -489,7 +528,8 @@ constexpr int waves_per_simd() {
 // One work item: range `split` of KV head h of sequence b (T = 0 and split = 0:
 // the empty sequence's rows).  Every return is uniform over the work-group.
 template <int BITS, bool KCH, bool VCH, int GRP>
-__device__ __forceinline__ void run_item(const SplitArgs& a, const int b, const int h, const int split) {
+__device__ __forceinline__ void run_item(const SplitArgs& a, const int b, const int h, const int split, const int T,
+                                         int* next) {
   using C = Codec<BITS>;
   constexpr int D = kHeadDim;
   constexpr int E = C::E;
@@ -500,7 +540,7 @@ __device__ __forceinline__ void run_item(const SplitArgs& a, const int b, const 
   constexpr int VW = kTile / E;            // value token-words per tile
   constexpr int NGK = KCH ? 1 : D / GRP;   // key groups per token
   constexpr int NGV = VCH ? 1 : D / GRP;   // value groups per token
-  constexpr int UNIT = ((KCH || VCH) && GRP > kTile) ? GRP : kTile;
+  constexpr int UNIT = work_unit<KCH, VCH, GRP>();  // tiles of a range come in whole units
   constexpr int TPU = UNIT / kTile;
 
   // lane and wave pass through an opaque register: in a persistent loop the
@@ -509,7 +549,6 @@ __device__ __forceinline__ void run_item(const SplitArgs& a, const int b, const 
   const uint32_t tid = in_vgpr(threadIdx.x);
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int T = min(max(a.seq_lens[b], 0), a.tcap);
   const int r0 = split * a.chunk;
   if (r0 >= T) {  // no token in this range; an empty sequence's rows are written once
     if (T == 0 && split == 0) {
@@ -518,6 +557,11 @@ __device__ __forceinline__ void run_item(const SplitArgs& a, const int b, const 
         a.out[row * kHeadDim + idx % kHeadDim] = 0;
         if (idx % kHeadDim == 0 && a.lse) a.lse[row] = -INFINITY;
       }
+    }
+    if (next && wave == 0) {
+      NextLoad nx;
+      next_load(a, nx);
+      map_select<UNIT>(a, nx, next);
     }
     return;
   }
@@ -1065,6 +1109,9 @@ __device__ __forceinline__ void run_item(const SplitArgs& a, const int b, const 
   }
 
   __builtin_amdgcn_s_setprio(3);  // the epilogue and the merge are the tail of the launch
+  // persistent work-groups: the next item's index and lengths load during the epilogue
+  NextLoad nx;
+  if (next && wave == 0) next_load(a, nx);
 
   // ---------------- wave epilogue: totals per query, value-side corrections
   const float l_tot = sum_same_query<64>(l_part);
@@ -1131,7 +1178,10 @@ __device__ __forceinline__ void run_item(const SplitArgs& a, const int b, const 
         __hip_atomic_store(a.lse_part + row * a.splits + split, l_nat, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   }
-  if (ns == 1) return;
+  if (ns == 1) {
+    if (next && wave == 0) map_select<UNIT>(a, nx, next);
+    return;
+  }
 
   // ---------------- the last range of this (sequence, KV head) merges all ranges
   // Hand-off without agent-scope fences: those write back and invalidate the
@@ -1143,10 +1193,10 @@ __device__ __forceinline__ void run_item(const SplitArgs& a, const int b, const 
   __shared__ int s_last;
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
-  if (tid == 0) {
-    const int done = __hip_atomic_fetch_add(a.counters + bh, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    s_last = (done == ns - 1);
-  }
+  int done = 0;
+  if (tid == 0) done = __hip_atomic_fetch_add(a.counters + bh, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (next && wave == 0) map_select<UNIT>(a, nx, next);  // while the count is in flight
+  if (tid == 0) s_last = (done == ns - 1);
   __syncthreads();
   if (!s_last) return;
   merge_ranges(a, b, h, ns);
@@ -1157,34 +1207,34 @@ __device__ __forceinline__ void run_item(const SplitArgs& a, const int b, const 
 // KV head) pair, y = range; consecutive work-groups land on different XCDs).
 // Larger grids (ragged batches of at most kMapMaxB sequences) run persistent:
 // one round of work-groups takes work items from a device-wide counter, longest
-// first (map_work), until the items run out; the last work-group to leave
+// first (map_select), until the items run out; the last work-group to leave
 // resets the counters for the next call.
 template <int BITS, bool KCH, bool VCH, int GRP>
 __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(waves_per_simd<BITS, KCH, VCH, GRP>())))
 void split_decode(const SplitArgs a) {
-  constexpr int UNIT = ((KCH || VCH) && GRP > kTile) ? GRP : kTile;
   if (!a.persistent) {
-    run_item<BITS, KCH, VCH, GRP>(a, blockIdx.x / a.hkv, blockIdx.x % a.hkv, blockIdx.y);
+    const int b = blockIdx.x / a.hkv;
+    run_item<BITS, KCH, VCH, GRP>(a, b, blockIdx.x % a.hkv, blockIdx.y, min(max(a.seq_lens[b], 0), a.tcap), nullptr);
     return;
   }
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  __shared__ int s_idx;
-  __shared__ int s_item[4];
+  __shared__ int s_item[5];  // the next item: {b, h, range, kind, T}
+  if (wave == 0) {
+    NextLoad nx;
+    next_load(a, nx);
+    map_select<work_unit<KCH, VCH, GRP>()>(a, nx, s_item);
+  }
+  __syncthreads();
   for (;;) {
-    if (threadIdx.x == 0)
-      s_idx = __hip_atomic_fetch_add(a.work_ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __syncthreads();
-    const int idx = __builtin_amdgcn_readfirstlane(s_idx);
-    if (wave == 0) map_work<UNIT>(a, idx, a.batch, s_item);
-    __syncthreads();
     const int kind = __builtin_amdgcn_readfirstlane(s_item[3]);
     const int b = __builtin_amdgcn_readfirstlane(s_item[0]);
     const int h = __builtin_amdgcn_readfirstlane(s_item[1]);
     const int split = __builtin_amdgcn_readfirstlane(s_item[2]);
-    __syncthreads();  // s_idx and s_item are read before the next item rewrites them
+    const int T = __builtin_amdgcn_readfirstlane(s_item[4]);
+    __syncthreads();  // s_item is read before wave 0 maps the item after this one into it
     if (kind == kItemNone) break;
-    run_item<BITS, KCH, VCH, GRP>(a, b, h, split);
-    __syncthreads();  // the item's LDS is free
+    run_item<BITS, KCH, VCH, GRP>(a, b, h, split, T, s_item);
+    __syncthreads();  // the item's LDS is free and s_item holds the next item
   }
   if (threadIdx.x == 0) {
     const int left = __hip_atomic_fetch_add(a.work_ctr + 1, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
