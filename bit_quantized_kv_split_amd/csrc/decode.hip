@@ -168,8 +168,17 @@ __device__ __forceinline__ uint2 lds_b64(uint32_t a) {
   return make_uint2(v[0], v[1]);
 }
 __device__ __forceinline__ void touch(uint32_t& v) { asm volatile("" : "+v"(v)); }
-__device__ __forceinline__ void touch(uint4& v) { touch(v.x); touch(v.y); touch(v.z); touch(v.w); }
-__device__ __forceinline__ void touch(uint2& v) { touch(v.x); touch(v.y); }
+// whole register tuples: a 32-bit asm operand taken from a live tuple costs a copy
+__device__ __forceinline__ void touch(uint4& v) {
+  u32x4 t = {v.x, v.y, v.z, v.w};
+  asm volatile("" : "+v"(t));
+  v = make_uint4(t[0], t[1], t[2], t[3]);
+}
+__device__ __forceinline__ void touch(uint2& v) {
+  u32x2 t = {v.x, v.y};
+  asm volatile("" : "+v"(t));
+  v = make_uint2(t[0], t[1]);
+}
 // Buffer resource over `bytes` bytes at p (raw, unswizzled).  Loads past the
 // end read zero, so a tile that runs past the cache capacity stays in bounds.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* p, uint32_t bytes) {
@@ -915,8 +924,10 @@ __device__ __forceinline__ void run_item(const SplitArgs& a, const int b, const 
 #pragma unroll
       for (int i = 0; i < QPW; ++i) lcur[i] = qlsrc[i];
     }
+    uint4 kseg;
 #pragma unroll
     for (int d = 0; d < KW; ++d) {
+      if (d % 4 == 0) kseg = tl.k[d / 4];
       if (d + 1 < KW) {
 #pragma unroll
         for (int i = 0; i < QPW; ++i) qnxt[i] = qsrc[(d + 1) * QPW + i];
@@ -925,8 +936,8 @@ __device__ __forceinline__ void run_item(const SplitArgs& a, const int b, const 
           for (int i = 0; i < QPW; ++i) lnxt[i] = qlsrc[(d + 1) * QPW + i];
         }
       }
-      uint32_t wrd = (d % 4 == 0) ? tl.k[d / 4].x : (d % 4 == 1) ? tl.k[d / 4].y : (d % 4 == 2) ? tl.k[d / 4].z : tl.k[d / 4].w;
-      touch(wrd);  // ties the unpacking to this segment
+      if (d % 4 == 0) touch(kseg);  // ties the unpacking of these four words to this segment onwards
+      const uint32_t wrd = (d % 4 == 0) ? kseg.x : (d % 4 == 1) ? kseg.y : (d % 4 == 2) ? kseg.z : kseg.w;
       uint32_t p[PAIRS];
       C::extract(wrd, kc, p);
 #pragma unroll
@@ -1041,9 +1052,9 @@ __device__ __forceinline__ void run_item(const SplitArgs& a, const int b, const 
 #pragma unroll
         for (int i = 0; i < QPW; ++i) pnxt[i] = psrc[(w + 1) * QPW + i];
       }
-      uint32_t vx = tl.v[w].x, vy = tl.v[w].y;
-      touch(vx);  // ties the unpacking to this segment
-      touch(vy);
+      uint2 vw = tl.v[w];
+      touch(vw);  // ties the unpacking to this segment
+      const uint32_t vx = vw.x, vy = vw.y;
       uint32_t p0[PAIRS], p1[PAIRS];
       C::extract(vx, kc, p0);  // channel 2*lane
       C::extract(vy, kc, p1);  // channel 2*lane + 1
@@ -1094,14 +1105,25 @@ __device__ __forceinline__ void run_item(const SplitArgs& a, const int b, const 
   // are behind win the arbitration and all of them finish together.
   const int q1 = nt / 4, q2 = nt / 2, q3 = (3 * nt) / 4;
   __builtin_amdgcn_s_setprio(3);
-  for (int k = 0; k < nt; ++k) {
+  // Tiles start in increasing order and stop below T, so only the wave's last
+  // tile can reach past T.  It is peeled off the loop: a loop body with one
+  // instance of the tile code keeps its accumulators in the same registers
+  // from one iteration to the next (two instances merging in the loop made
+  // the compiler copy them back at every iteration).
+  for (int k = 0; k < nt - 1; ++k) {
     if (k == q1) __builtin_amdgcn_s_setprio(2);
     if (k == q2) __builtin_amdgcn_s_setprio(1);
     if (k == q3) __builtin_amdgcn_s_setprio(0);
     if (k + NS - 1 < nt) issue(k + NS - 1);
     Tile tl;
     read(tl, k, min(NS - 1, nt - 1 - k));
-    const int t0k = tile_start(k);
+    process(tl, tile_start(k), std::false_type{});
+  }
+  if (nt > 0) {
+    __builtin_amdgcn_s_setprio(0);  // q3 <= nt - 1: the last tile always ran at the lowest priority
+    Tile tl;
+    read(tl, nt - 1, 0);
+    const int t0k = tile_start(nt - 1);
     if (t0k + kTile > T)
       process(tl, t0k, std::true_type{});
     else
