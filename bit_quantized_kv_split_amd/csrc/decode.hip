@@ -277,6 +277,44 @@ __device__ __forceinline__ float max_halves(float v) {
   asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(a), "+v"(b));
   return fmaxf(a, b);
 }
+// max over the lanes of one query head (l, l^4, ..., across the wave), and m:
+// the DPP row rotations fused into the max, then the permlane swaps, in one
+// block.  Scores are never NaN (masked ones are -inf), so the canonicalising
+// max the compiler puts before each cross-lane result is not needed.  Each
+// DPP or permlane read of a VGPR follows its VALU write by two wait states.
+__device__ __forceinline__ float wave_max_same_query_and(float v, float m) {
+  float a, r;
+  asm volatile(
+      "s_nop 1\n\t"
+      "v_max_f32_dpp %0, %0, %0 row_ror:4 row_mask:0xf bank_mask:0xf\n\t"
+      "s_nop 1\n\t"
+      "v_max_f32_dpp %0, %0, %0 row_ror:8 row_mask:0xf bank_mask:0xf\n\t"
+      "v_mov_b32 %1, %0\n\t"
+      "s_nop 1\n\t"
+      "v_permlane16_swap_b32 %0, %1\n\t"
+      "v_max_f32 %0, %0, %1\n\t"
+      "v_mov_b32 %1, %0\n\t"
+      "s_nop 1\n\t"
+      "v_permlane32_swap_b32 %0, %1\n\t"
+      "v_max3_f32 %2, %0, %1, %3"
+      : "+v"(v), "=&v"(a), "=v"(r)
+      : "v"(m));
+  return r;
+}
+// The fp16 pair {fp16(pa * a), fp16(pb * b)}, each product rounded once, where
+// a and b are fp16 halves (high when ha / hb) of the words wa and wb.
+__device__ __forceinline__ uint32_t mul_f16x2(float pa, uint32_t wa, bool ha, float pb, uint32_t wb, bool hb) {
+  uint32_t r;
+  if (ha)
+    asm("v_fma_mixlo_f16 %0, %1, %2, 0 op_sel:[0,1,0] op_sel_hi:[0,1,0]" : "=v"(r) : "v"(pa), "v"(wa));
+  else
+    asm("v_fma_mixlo_f16 %0, %1, %2, 0 op_sel_hi:[0,1,0]" : "=v"(r) : "v"(pa), "v"(wa));
+  if (hb)
+    asm("v_fma_mixhi_f16 %0, %1, %2, 0 op_sel:[0,1,0] op_sel_hi:[0,1,0]" : "+v"(r) : "v"(pb), "v"(wb));
+  else
+    asm("v_fma_mixhi_f16 %0, %1, %2, 0 op_sel_hi:[0,1,0]" : "+v"(r) : "v"(pb), "v"(wb));
+  return r;
+}
 // sum over all 64 lanes, in every lane
 __device__ __forceinline__ float wave_sum(float v) {
   v += dpp<0x121>(v);  // row_ror:1
@@ -995,7 +1033,7 @@ __device__ __forceinline__ void run_item(const SplitArgs& a, const int b, const 
     // ---------------- online softmax: exact running max per query head.  The
     // largest weight seen so far is exactly 1, so the operand-folded weight of
     // the dominant token (p * s) is its fp16 scale itself, with no rounding.
-    const float m_new = fmaxf(m_ref, wave_max_same_query(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]))));
+    const float m_new = wave_max_same_query_and(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])), m_ref);
     if (__any(m_new > m_ref)) {
       const float alpha = __builtin_amdgcn_exp2f(m_ref - m_new);  // 0 on the first tile
       m_ref = m_new;
@@ -1011,6 +1049,7 @@ __device__ __forceinline__ void run_item(const SplitArgs& a, const int b, const 
 #pragma unroll
       for (int j = 0; j < NGV; ++j) {
         float s[4], z[4];
+        uint32_t sw[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int idx = r * NGV + j;
@@ -1018,12 +1057,19 @@ __device__ __forceinline__ void run_item(const SplitArgs& a, const int b, const 
           const uint2 zv = tl.vz[idx / 4];
           const uint32_t s32 = ((idx % 4) < 2) ? sv.x : sv.y;
           const uint32_t z32 = ((idx % 4) < 2) ? zv.x : zv.y;
+          sw[r] = s32;
           s[r] = (idx % 2 == 0) ? half_lo(s32) : half_hi(s32);
           z[r] = (idx % 2 == 0) ? half_lo(z32) : half_hi(z32);
           if (tail && (t0 + 4 * qd + r >= T)) s[r] = z[r] = 0.f;  // padding may hold NaN
         }
-        const uint32_t p01 = pack_f16(p[0] * s[0], p[1] * s[1]);
-        const uint32_t p23 = pack_f16(p[2] * s[2], p[3] * s[3]);
+        uint32_t p01, p23;
+        if constexpr (tail) {
+          p01 = pack_f16(p[0] * s[0], p[1] * s[1]);
+          p23 = pack_f16(p[2] * s[2], p[3] * s[3]);
+        } else {  // straight from the fp16 scales, one rounding per product
+          p01 = mul_f16x2(p[0], sw[0], (0 * NGV + j) % 2, p[1], sw[1], (1 * NGV + j) % 2);
+          p23 = mul_f16x2(p[2], sw[2], (2 * NGV + j) % 2, p[3], sw[3], (3 * NGV + j) % 2);
+        }
         s_p[wave][j][qn][qd] = make_uint2(p01, p23);
         vb_part[j] = dot2(p23, cv1h, dot2(p01, cv0h, vb_part[j]));
         vz_part[j] = fmaf(p[0], z[0], fmaf(p[1], z[1], fmaf(p[2], z[2], fmaf(p[3], z[3], vz_part[j]))));
