@@ -162,6 +162,48 @@ def decode(q, packed_k, packed_v, k_scale, k_zero, v_scale, v_zero, seq_lens, *,
               group, out, lse, sm_scale, stream)
 
 
+def _quantize(bits, k_src, v_src, start, count, packed_k, packed_v, k_scale, k_zero, v_scale, v_zero, layout, group,
+              stream=None):
+    import torch
+    lib = _lib.load()
+    dev = k_src.device
+    _require(k_src, "k_src", torch.bfloat16, dev)
+    _require(v_src, "v_src", torch.bfloat16, dev)
+    if tuple(k_src.shape) != tuple(v_src.shape) or k_src.dim() != 4:
+        raise ValueError("k_src and v_src must both be [B, Hkv, N, D]")
+    for name, t in (("start", start), ("count", count)):
+        _require(t, name, torch.int32, dev)
+    for name, t in (("packed_k", packed_k), ("packed_v", packed_v)):
+        _require(t, name, torch.int32, dev)
+    for name, t in (("k_scale", k_scale), ("k_zero", k_zero), ("v_scale", v_scale), ("v_zero", v_zero)):
+        _require(t, name, torch.float16, dev)
+    B, Hkv, N, D = k_src.shape
+    Tcap = packed_k.shape[2]
+    if packed_k.shape[:2] != (B, Hkv) or start.numel() != B or count.numel() != B:
+        raise ValueError("cache, sources, start and count disagree on [B, Hkv]")
+    dims = make_dims(B, Hkv, Hkv, D, Tcap)
+    fn = lib.foscar_quantize_int2 if bits == 2 else lib.foscar_quantize_int4
+    with torch.cuda.device(dev):
+        rc = fn(ctypes.byref(dims), _ptr(k_src), _ptr(v_src), int(N), _ptr(start), _ptr(count), int(layout),
+                int(group), _ptr(packed_k), _ptr(packed_v), _ptr(k_scale), _ptr(k_zero), _ptr(v_scale),
+                _ptr(v_zero), _stream(stream))
+    _check(rc, f"foscar_quantize_int{bits}")
+
+
+def foscar_quantize_int2(k_src, v_src, start, count, packed_k, packed_v, k_scale, k_zero, v_scale, v_zero, layout,
+                         group, stream=None):
+    """Quantise bf16 keys / values [B, Hkv, N, D] into a 2-bit cache in place (include/foscar.h)."""
+    _quantize(2, k_src, v_src, start, count, packed_k, packed_v, k_scale, k_zero, v_scale, v_zero, layout, group,
+              stream)
+
+
+def foscar_quantize_int4(k_src, v_src, start, count, packed_k, packed_v, k_scale, k_zero, v_scale, v_zero, layout,
+                         group, stream=None):
+    """Quantise bf16 keys / values [B, Hkv, N, D] into a 4-bit cache in place (include/foscar.h)."""
+    _quantize(4, k_src, v_src, start, count, packed_k, packed_v, k_scale, k_zero, v_scale, v_zero, layout, group,
+              stream)
+
+
 def _pack_dims(codes_shape):
     B, Hkv, T, D = codes_shape
     return make_dims(B, Hkv, Hkv, D, T)

@@ -238,6 +238,24 @@ int decode_common(int bits, const foscar_dims* d, const void* q, const void* pk,
   return FOSCAR_OK;
 }
 
+int quantize_common(int bits, const foscar_dims* d, const void* k_src, const void* v_src, int32_t src_tokens,
+                    const int32_t* start, const int32_t* count, int layout, int group, void* pk, void* pv, void* ks,
+                    void* kz, void* vs, void* vz, void* stream) {
+  int rc = check_dims(d, false);
+  if (rc) return rc;
+  if (layout < 0 || layout > 3 || src_tokens < 0) return FOSCAR_EINVAL;
+  if (!valid_group(group)) return FOSCAR_EUNSUPPORTED;
+  if (d->max_seq_len % foscar::kTile != 0 || d->max_seq_len > (1 << 24)) return FOSCAR_EUNSUPPORTED;
+  if (layout != 0 && d->max_seq_len % group != 0) return FOSCAR_EUNSUPPORTED;
+  if (d->batch > 65535 || d->num_kv_heads > 65535) return FOSCAR_EUNSUPPORTED;  // grid z / y
+  if (d->batch == 0 || src_tokens == 0) return FOSCAR_OK;
+  if (!k_src || !v_src || !start || !count || !pk || !pv || !ks || !kz || !vs || !vz) return FOSCAR_EINVAL;
+  const hipError_t e = foscar::launch_quantize(bits, (layout & FOSCAR_K_CHANNEL) != 0, (layout & FOSCAR_V_CHANNEL) != 0,
+                                               group, d->batch, d->num_kv_heads, d->max_seq_len, src_tokens, k_src,
+                                               v_src, start, count, pk, pv, ks, kz, vs, vz, (hipStream_t)stream);
+  return e == hipSuccess ? FOSCAR_OK : hip_fail(e);
+}
+
 int check_pack(int bits, int side, const foscar_dims* d) {
   if (bits != 2 && bits != 4) return FOSCAR_EINVAL;
   if (side != FOSCAR_SIDE_K && side != FOSCAR_SIDE_V) return FOSCAR_EINVAL;
@@ -263,6 +281,20 @@ int foscar_decode_int4(const foscar_dims* dims, const void* q, const void* packe
                        const int32_t* seq_lens, int layout, int group, void* out, float* lse, void* stream) {
   return decode_common(4, dims, q, packed_k, packed_v, k_scale, k_zero, v_scale, v_zero, seq_lens, layout, group,
                        out, lse, stream);
+}
+
+int foscar_quantize_int2(const foscar_dims* dims, const void* k_src, const void* v_src, int32_t src_tokens,
+                         const int32_t* start, const int32_t* count, int layout, int group, void* packed_k,
+                         void* packed_v, void* k_scale, void* k_zero, void* v_scale, void* v_zero, void* stream) {
+  return quantize_common(2, dims, k_src, v_src, src_tokens, start, count, layout, group, packed_k, packed_v, k_scale,
+                         k_zero, v_scale, v_zero, stream);
+}
+
+int foscar_quantize_int4(const foscar_dims* dims, const void* k_src, const void* v_src, int32_t src_tokens,
+                         const int32_t* start, const int32_t* count, int layout, int group, void* packed_k,
+                         void* packed_v, void* k_scale, void* k_zero, void* v_scale, void* v_zero, void* stream) {
+  return quantize_common(4, dims, k_src, v_src, src_tokens, start, count, layout, group, packed_k, packed_v, k_scale,
+                         k_zero, v_scale, v_zero, stream);
 }
 
 int foscar_pack(int bits, int side, const foscar_dims* dims, const uint8_t* codes, void* packed, void* stream) {

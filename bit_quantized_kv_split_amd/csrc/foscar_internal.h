@@ -50,6 +50,10 @@ hipError_t launch_decode(int bits, bool k_channel, bool v_channel, int group, in
 
 // Work-groups of the decode kernel for (bits, layout sides, group) one CU holds at once.
 hipError_t decode_occupancy(int bits, bool k_channel, bool v_channel, int group, int* per_cu);
+// Quantise tokens [start_b, start_b + count_b) of new keys / values into the cache (quant.hip).
+hipError_t launch_quantize(int bits, bool k_channel, bool v_channel, int group, int batch, int hkv, int tcap,
+                           int n_src, const void* k_src, const void* v_src, const int32_t* start, const int32_t* count,
+                           void* pk, void* pv, void* ks, void* kz, void* vs, void* vz, hipStream_t stream);
 hipError_t launch_pack(int bits, int side, int batch, int hkv, int tcap, const uint8_t* codes, uint32_t* packed,
                        hipStream_t stream);
 hipError_t launch_unpack(int bits, int side, int batch, int hkv, int tcap, const uint32_t* packed, uint8_t* codes,

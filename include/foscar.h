@@ -119,6 +119,47 @@ int foscar_decode_int4(const foscar_dims* dims, const void* q, const void* packe
                        const int32_t* seq_lens, int layout, int group, void* out, float* lse, void* stream);
 
 /*
+ * Quantise new keys and values into the cache (2-bit: foscar_quantize_int2,
+ * 4-bit: foscar_quantize_int4), in the layouts the decode entry points read.
+ *
+ * Encoding value = s*q + z, one (s, z) per group (explainer, encoding
+ * paragraph); groups token-wise or channel-wise as in `layout` (explainer,
+ * fold-placement table).  The pages give no quantiser; this one is min-max
+ * asymmetric with every decision in fp32:
+ *   s = fp16_rne(fp32(max - min) / (2^bits - 1)),  z = fp16_rne(min),
+ *   q = clamp(rint_half_even(fp32(x - z) / s), 0, 2^bits - 1), q = 0 if s = 0.
+ *
+ * k_src, v_src  bf16 [B][Hkv][src_tokens][D]: row r of sequence b is token
+ *               start[b] + r; finite values with |x| < 65504
+ * start, count  int32 [B] (device): sequence b receives tokens
+ *               [start[b], start[b] + n_b), n_b = count[b] clamped to
+ *               [0, min(src_tokens, Tcap - start[b])]; start[b] outside
+ *               [0, Tcap] leaves the sequence untouched
+ * layout, group as for decode.  A token-wise side quantises each token's
+ *               groups of g channels.  A channel-wise side needs start[b] to
+ *               be a multiple of g (otherwise sequence b is left untouched);
+ *               each group g*tau .. g*tau + g - 1 the range reaches is
+ *               quantised over the tokens of the range it holds (a partly
+ *               filled last group is quantised over its tokens so far and is
+ *               re-quantised whole by a later call that starts at g*tau).
+ * packed_k, packed_v, k_scale, k_zero, v_scale, v_zero
+ *               the cache, in the layouts of the decode entry points; only
+ *               the written tokens' codes and their groups' (s, z) change:
+ *               codes of other tokens in a shared value word are kept.
+ * Only batch, num_kv_heads, head_dim and max_seq_len of dims are used
+ * (head_dim 128; max_seq_len a multiple of 64, and of g for a channel-wise
+ * side; batch and num_kv_heads at most 65535).
+ * Asynchronous on `stream`; the caller keeps the buffers alive.  Calls that
+ * write the same sequences must be ordered on one stream.
+ */
+int foscar_quantize_int2(const foscar_dims* dims, const void* k_src, const void* v_src, int32_t src_tokens,
+                         const int32_t* start, const int32_t* count, int layout, int group, void* packed_k,
+                         void* packed_v, void* k_scale, void* k_zero, void* v_scale, void* v_zero, void* stream);
+int foscar_quantize_int4(const foscar_dims* dims, const void* k_src, const void* v_src, int32_t src_tokens,
+                         const int32_t* start, const int32_t* count, int layout, int group, void* packed_k,
+                         void* packed_v, void* k_scale, void* k_zero, void* v_scale, void* v_zero, void* stream);
+
+/*
  * Pack logical codes into the layout above (bit-exact with any packer written
  * from the same specification), or unpack it.
  * codes   u8 [B][Hkv][Tcap][D], values 0 .. 2^bits - 1 (higher bits are dropped)

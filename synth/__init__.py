@@ -309,3 +309,43 @@ def full_scale_shapes(spec: Spec) -> dict:
     ks = (B, H) + scale_shape(spec, spec.k_layout)
     vs = (B, H) + scale_shape(spec, spec.v_layout)
     return {"k_scale": ks, "k_zero": ks, "v_scale": vs, "v_zero": vs}
+
+
+def make_append_case(seed: int, batch: int, num_kv_heads: int, max_seq_len: int, src_tokens: int, bits: int,
+                     starts, counts, head_dim: int = 128, channel_std_logu=(0.1, 10.0)) -> dict:
+    """Inputs of a quantise-and-append call (values only, no quantiser arithmetic).
+
+    * k_src / v_src: fp32 arrays of bf16 values [B][Hkv][N][D], N(0,1) times a
+      per-(head, channel) std drawn log-uniform in ``channel_std_logu``;
+    * a cache that already holds arbitrary content: random packed words
+      (uint32, the layouts of the C interface) and random fp16 bit patterns,
+      NaN patterns included, for the scales and offsets of both layouts;
+    * start / count: int32 [B] as given.
+    """
+    B, H, T, D, N = batch, num_kv_heads, max_seq_len, head_dim, src_tokens
+    E = 32 // bits
+    rng = np.random.default_rng([seed, 900, bits, B, H, T, N])
+    lo, hi = channel_std_logu
+    std = np.exp(rng.uniform(math.log(lo), math.log(hi), size=(2, 1, H, 1, D))).astype(np.float32)
+    k = bf16_round(rng.standard_normal((B, H, N, D), dtype=np.float32) * std[0])
+    v = bf16_round(rng.standard_normal((B, H, N, D), dtype=np.float32) * std[1])
+    case = {
+        "k_src": k, "v_src": v,
+        "packed_k": rng.integers(0, 1 << 32, (B, H, T, D // E), dtype=np.uint64).astype(np.uint32),
+        "packed_v": rng.integers(0, 1 << 32, (B, H, T // E, D), dtype=np.uint64).astype(np.uint32),
+        "start": np.asarray(starts, np.int32), "count": np.asarray(counts, np.int32),
+    }
+    for side in ("k", "v"):
+        for part in ("scale", "zero"):
+            for layout in (TOKEN, CHANNEL):
+                shp = (B, H, T, D // 32) if layout == TOKEN else (B, H, T // 32, D)  # sliced per g by the caller
+                case[f"{side}_{part}_{layout}"] = rng.integers(0, 1 << 16, shp, dtype=np.uint32).astype(np.uint16)
+    return case
+
+
+def device_normal_bf16(shape, seed: int, device="cuda"):
+    """N(0,1) values rounded to bf16, drawn on the device by a seeded torch
+    generator (inputs too large to draw on the host in a test's time)."""
+    import torch
+    gen = torch.Generator(device=device).manual_seed(seed)
+    return torch.randn(tuple(shape), generator=gen, device=device).to(torch.bfloat16)
