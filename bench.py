@@ -40,6 +40,8 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--dump-steps", action="store_true", help="print each step's kernel microseconds to stderr")
+    ap.add_argument("--op", choices=["decode", "quantize"], default="decode",
+                    help="decode: the decode step (default); quantize: quantise-and-append of the workload's cache")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="run one plain device copy of this many MiB before warm-up (counter calibration)")
     return ap.parse_args()
@@ -107,6 +109,67 @@ def cpu_baseline(spec, q, lens, target_s):
             "seconds_per_step_extrapolated": round(spent / slices * spec.batch * spec.num_kv_heads, 2)}
 
 
+def quantize_bytes(spec, tokens_per_head):
+    """Algorithmic bytes of quantising tokens_per_head tokens of every (sequence,
+    KV head): bf16 keys and values read, codes and (s, z) of both sides
+    written (token-wise groups), plus start/count."""
+    D = spec.head_dim
+    per_token = 2 * 2 * D + 2 * D * spec.bits // 8 + 2 * 2 * 2 * (D // spec.group)
+    return spec.batch * spec.num_kv_heads * tokens_per_head * per_token + 8 * spec.batch
+
+
+def bench_quantize(args, spec):
+    """Quantise-and-append of the whole cache (a prefill: every token of every
+    sequence in one call) and of one token per sequence (a decode-time append),
+    timed with events on the launch stream."""
+    import numpy as np
+    import torch
+
+    import bit_quantized_kv_split_amd as fos
+    import synth
+
+    if spec.k_layout != "token" or spec.v_layout != "token":
+        raise SystemExit("--op quantize measures token-wise workloads")
+    B, H, T, D, E = spec.batch, spec.num_kv_heads, spec.max_seq_len, spec.head_dim, 32 // spec.bits
+    dev = "cuda"
+    k_src = synth.device_normal_bf16((B, H, T, D), 1234)
+    v_src = synth.device_normal_bf16((B, H, T, D), 1235)
+    pk = torch.zeros((B, H, T, D // E), dtype=torch.int32, device=dev)
+    pv = torch.zeros((B, H, T // E, D), dtype=torch.int32, device=dev)
+    sc = [torch.zeros((B, H, T, D // spec.group), dtype=torch.float16, device=dev) for _ in range(4)]
+    fn = fos.foscar_quantize_int2 if spec.bits == 2 else fos.foscar_quantize_int4
+    layout = fos.layout_bits("token", "token")
+    zero = torch.zeros(B, dtype=torch.int32, device=dev)
+    full = torch.full((B,), T, dtype=torch.int32, device=dev)
+    one = torch.ones(B, dtype=torch.int32, device=dev)
+    k1, v1 = k_src[:, :, :1].contiguous(), v_src[:, :, :1].contiguous()
+    at = torch.full((B,), T // 2 + 3, dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream()
+    lines = []
+    for name, call, toks in (("prefill", lambda: fn(k_src, v_src, zero, full, pk, pv, *sc, layout, spec.group), T),
+                             ("append", lambda: fn(k1, v1, at, one, pk, pv, *sc, layout, spec.group), 1)):
+        for _ in range(args.warmup):
+            call()
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+        for a, b in ev:
+            a.record(stream)
+            call()
+            b.record(stream)
+        torch.cuda.synchronize()
+        ms = [a.elapsed_time(b) for a, b in ev]
+        avg = sum(ms) / len(ms)
+        alg = quantize_bytes(spec, toks)
+        lines.append({"op": f"quantize_{name}", "workload": spec.name, "tokens_per_head": toks,
+                      "us_avg": round(avg * 1e3, 2), "us_median": round(sorted(ms)[len(ms) // 2] * 1e3, 2),
+                      "us_min": round(min(ms) * 1e3, 2), "algorithmic_bytes": alg,
+                      "roofline": {"bound": "hbm", "achieved": round(alg / (avg * 1e-3) / 1e9, 2),
+                                   "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                                   "frac": round(alg / (avg * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}})
+    for line in lines:
+        print(json.dumps(line), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -123,6 +186,8 @@ def main():
     spec = synth.SPECS[args.workload]
     dev_name = "cuda:0"
     torch.cuda.set_device(0)
+    if args.op == "quantize":
+        return bench_quantize(args, spec)
     q = synth.make_query(spec)
     lens = spec.seq_lens()
     t_stage = time.perf_counter()

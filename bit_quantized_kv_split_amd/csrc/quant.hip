@@ -56,12 +56,59 @@ struct GroupQ {
     s = (float)s16;
     z = (float)z16;
   }
-  __device__ __forceinline__ uint32_t code(float x) const {
+  // rint(RN(d / s)) for d = x - z: with r = rcp(s) (1 ulp), d * r lies within
+  // 3 ulp of the correctly rounded quotient, so its nearest integer is the same
+  // unless it sits within that distance of a half-integer; |quotient| < 16
+  // there, where 2^-16 is many ulps.  Only those rare lanes take the exact
+  // division.
+  __device__ __forceinline__ uint32_t code(float x, float r) const {
     if (s == 0.f) return 0u;
-    const float q = rintf(__fdiv_rn(x - z, s));  // round half to even
+    const float d = x - z;
+    float q = d * r;
+    const float f = q - floorf(q);
+    if (fabsf(f - 0.5f) < 0x1p-16f) q = __fdiv_rn(d, s);
+    q = rintf(q);  // round half to even
     return (uint32_t)fminf(fmaxf(q, 0.f), (float)((1 << BITS) - 1));
   }
+  __device__ __forceinline__ float rcp() const { return s == 0.f ? 0.f : __builtin_amdgcn_rcpf(s); }
 };
+
+// Cross-lane reductions with DPP and permlane swaps (inline asm: each
+// cross-lane read of a VGPR follows its VALU write by two wait states).  Every
+// step pairs lanes symmetrically (quad xor 1 and 2, half-row and row mirrors,
+// row-pair and half-wave swaps), so every lane ends with the result.
+#define FOSCAR_DPP_MINMAX(mn, mx, ctrl)                                               \
+  asm volatile("s_nop 1\n\t"                                                        \
+               "v_min_f32_dpp %0, %0, %0 " ctrl " row_mask:0xf bank_mask:0xf\n\t"   \
+               "v_max_f32_dpp %1, %1, %1 " ctrl " row_mask:0xf bank_mask:0xf"         \
+               : "+v"(mn), "+v"(mx))
+#define FOSCAR_DPP_OR(v, ctrl) \
+  asm volatile("s_nop 1\n\tv_or_b32_dpp %0, %0, %0 " ctrl " row_mask:0xf bank_mask:0xf" : "+v"(v))
+
+// min and max over each aligned group of LANES lanes (16, 32 or 64)
+template <int LANES>
+__device__ __forceinline__ void group_minmax(float& mn, float& mx) {
+  FOSCAR_DPP_MINMAX(mn, mx, "quad_perm:[1,0,3,2]");
+  FOSCAR_DPP_MINMAX(mn, mx, "quad_perm:[2,3,0,1]");
+  FOSCAR_DPP_MINMAX(mn, mx, "row_half_mirror");
+  FOSCAR_DPP_MINMAX(mn, mx, "row_mirror");
+  if constexpr (LANES >= 32) {
+    float a, b;
+    asm volatile(
+        "v_mov_b32 %2, %0\n\tv_mov_b32 %3, %1\n\ts_nop 1\n\t"
+        "v_permlane16_swap_b32 %0, %2\n\tv_permlane16_swap_b32 %1, %3\n\t"
+        "v_min_f32 %0, %0, %2\n\tv_max_f32 %1, %1, %3"
+        : "+v"(mn), "+v"(mx), "=&v"(a), "=&v"(b));
+  }
+  if constexpr (LANES == 64) {
+    float a, b;
+    asm volatile(
+        "v_mov_b32 %2, %0\n\tv_mov_b32 %3, %1\n\ts_nop 1\n\t"
+        "v_permlane32_swap_b32 %0, %2\n\tv_permlane32_swap_b32 %1, %3\n\t"
+        "v_min_f32 %0, %0, %2\n\tv_max_f32 %1, %1, %3"
+        : "+v"(mn), "+v"(mx), "=&v"(a), "=&v"(b));
+  }
+}
 
 struct QuantArgs {
   const uint32_t* ksrc;    // bf16 pairs [B][Hkv][N][D/2]
@@ -77,12 +124,12 @@ struct QuantArgs {
   int32_t hkv, tcap, n_src;
 };
 
-// OR of `v` over the E/2 lanes that share one key word
+// OR of `v` over the E/2 lanes (4 or 8, aligned) that share one key word
 template <int BITS>
 __device__ __forceinline__ uint32_t or_word_lanes(uint32_t v) {
-  constexpr int E = 32 / BITS;
-#pragma unroll
-  for (int m = 1; m < E / 2; m <<= 1) v |= (uint32_t)__shfl_xor((int)v, m);
+  FOSCAR_DPP_OR(v, "quad_perm:[1,0,3,2]");
+  FOSCAR_DPP_OR(v, "quad_perm:[2,3,0,1]");
+  if constexpr (BITS == 2) FOSCAR_DPP_OR(v, "row_half_mirror");
   return v;
 }
 
@@ -113,26 +160,36 @@ __device__ __forceinline__ void quant_side(const uint32_t* src, uint32_t* packed
     if (lane % (E / 2) == 0) packed[(bh * tcap + t) * KW + (2 * lane) / E] = w;
   };
   uint32_t* vrow = packed + bh * (size_t)(tcap / E) * D + 2 * lane;  // value word row r at vrow[r * D]
+  // Rows are loaded U at a time ahead of their processing: the cross-lane asm
+  // of the processing keeps the compiler from moving later loads above it,
+  // which would leave one row load in flight per wave.
+  constexpr int U = 16;
+  auto load_batch = [&](uint32_t(&w)[U], int t, int t_end) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) w[u] = (t + u < t_end) ? load_row(t + u) : 0u;
+  };
 
   if constexpr (!CH) {
     uint32_t acc0 = 0, acc1 = 0, msk = 0;
-#pragma unroll 4
-    for (int t = t_lo; t < t_hi; ++t) {
-      const uint32_t w = load_row(t);
+    for (int tb = t_lo; tb < t_hi; tb += U) {
+     uint32_t wb[U];
+     load_batch(wb, tb, t_hi);
+#pragma unroll
+     for (int u = 0; u < U; ++u) {
+      const int t = tb + u;
+      if (t >= t_hi) break;
+      const uint32_t w = wb[u];
       const float x0 = bf16_lo(w), x1 = bf16_hi(w);
       float mn = fminf(x0, x1), mx = fmaxf(x0, x1);
-#pragma unroll
-      for (int m = 1; m < GRP / 2; m <<= 1) {  // the g/2 lanes of this lane's group
-        mn = fminf(mn, __shfl_xor(mn, m));
-        mx = fmaxf(mx, __shfl_xor(mx, m));
-      }
+      group_minmax<GRP / 2>(mn, mx);  // the g/2 lanes of this lane's group
       const GroupQ<BITS> gq(mn, mx);
+      const float rq = gq.rcp();
       if ((2 * lane) % GRP == 0) {
         const size_t si = (bh * tcap + t) * (D / GRP) + (2 * lane) / GRP;
         sc[si] = h_bits(gq.s16);
         zr[si] = h_bits(gq.z16);
       }
-      const uint32_t c0 = gq.code(x0), c1 = gq.code(x1);
+      const uint32_t c0 = gq.code(x0, rq), c1 = gq.code(x1, rq);
       if constexpr (!VALUE) {
         store_key(t, c0, c1);
       } else {
@@ -145,6 +202,7 @@ __device__ __forceinline__ void quant_side(const uint32_t* src, uint32_t* packed
           acc0 = acc1 = msk = 0;
         }
       }
+     }
     }
   } else {
     // channel-wise groups: [g0, g0 + GRP) from token 0; t_lo is a group start
@@ -161,14 +219,20 @@ __device__ __forceinline__ void quant_side(const uint32_t* src, uint32_t* packed
         mx1 = fmaxf(mx1, x1);
       }
       const GroupQ<BITS> q0(mn0, mx0), q1(mn1, mx1);
+      const float r0 = q0.rcp(), r1 = q1.rcp();
       const size_t si = (bh * (size_t)(tcap / GRP) + g0 / GRP) * D + 2 * lane;
       *reinterpret_cast<uint32_t*>(sc + si) = (uint32_t)h_bits(q0.s16) | ((uint32_t)h_bits(q1.s16) << 16);
       *reinterpret_cast<uint32_t*>(zr + si) = (uint32_t)h_bits(q0.z16) | ((uint32_t)h_bits(q1.z16) << 16);
       uint32_t acc0 = 0, acc1 = 0, msk = 0;
-#pragma unroll 4
-      for (int t = g0; t < g1; ++t) {
-        const uint32_t w = load_row(t);
-        const uint32_t c0 = q0.code(bf16_lo(w)), c1 = q1.code(bf16_hi(w));
+      for (int tb = g0; tb < g1; tb += U) {
+       uint32_t wb[U];
+       load_batch(wb, tb, g1);
+#pragma unroll
+       for (int u = 0; u < U; ++u) {
+        const int t = tb + u;
+        if (t >= g1) break;
+        const uint32_t w = wb[u];
+        const uint32_t c0 = q0.code(bf16_lo(w), r0), c1 = q1.code(bf16_hi(w), r1);
         if constexpr (!VALUE) {
           store_key(t, c0, c1);
         } else {
@@ -181,6 +245,7 @@ __device__ __forceinline__ void quant_side(const uint32_t* src, uint32_t* packed
             acc0 = acc1 = msk = 0;
           }
         }
+       }
       }
     }
   }
