@@ -223,20 +223,25 @@ def main():
         step(k)
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
-    # kernel durations: events recorded by each decode dispatch itself (hipExtLaunchKernel), the
-    # same span rocprofv3's kernel trace reports; recorded once first so that they exist
+    # whole-job throughput: exactly `steps` steps back to back, nothing else on the stream
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        step(k)
+    enqueued = time.perf_counter() - t0
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    # kernel durations, in a second pass of as many steps: events recorded by each decode
+    # dispatch itself (hipExtLaunchKernel), the span rocprofv3's kernel trace reports;
+    # recorded once first so that they exist
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
     for a, b in ev:
         a.record(stream)
         b.record(stream)
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
     for k in range(args.steps):
         fos.foscar_record_next_launch(ev[k][0], ev[k][1])
         step(k)
-    enqueued = time.perf_counter() - t0
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
     kernel_ms = [a.elapsed_time(b) for a, b in ev]
     if args.dump_steps:
         print("kernel us per step:", " ".join(f"{x * 1e3:.1f}" for x in kernel_ms), file=sys.stderr)
