@@ -10,20 +10,26 @@
 // fp32: s = fp16((max - min) / (2^bits - 1)), z = fp16(min),
 // q = rint((x - z) / s) clamped to the code range (q = 0 when s = 0).
 //
-// Work decomposition: one wave per (128-token block, KV head, sequence).
-// Lane l owns channels 2l and 2l+1 of each token row (one 4-byte bf16 pair
-// per row, so a row is one 256-byte coalesced load).
-//   * token-wise group (g channels of a token = g/2 lanes): min / max by
-//     xor-shuffles inside the g/2 lanes;
-//   * channel-wise group (g tokens of a channel): each lane folds the group's
-//     tokens into its two channels' min / max, then codes them on a second
-//     pass (the group's rows are re-read, from L2);
-//   * keys are packed along channels: the E/2 lanes of a word OR their codes
-//     together by xor-shuffles and one lane stores the word;
-//   * values are packed along tokens: each lane gathers the E tokens of its
-//     two channels' words in registers and stores them as one 8-byte write;
-//     a word that the written range covers only in part is read, merged and
-//     written back, so tokens outside the range keep their codes.
+// Work decomposition: one wave per (128-token block, KV head, sequence),
+// stepping four tokens at a time.  Lane l takes token slot l / 16 of the step
+// and channels 8 (l % 16) .. +7: one 16-byte load per lane, four consecutive
+// 256-byte rows per wave-instruction.
+//   * token-wise group (g channels of a token = g/8 lanes of one slot):
+//     min / max inside the lane, then DPP quad swaps and row mirrors;
+//   * channel-wise group (g tokens of a channel): each lane folds its slot's
+//     tokens of the group into min / max of its 8 channels, the four slots are
+//     combined by permlane swaps, then the group's rows are read again (from
+//     L2) to code them;
+//   * codes: rint((x - z) * rcp(s)); a lane whose product lies within 2^-16 of
+//     a half-integer takes the correctly rounded division instead, so every
+//     code equals rint of the fp32 quotient;
+//   * keys are packed along channels: a lane's 8 codes fill half an INT2 word
+//     (one DPP OR with the neighbour octet) or a whole INT4 word;
+//   * values are packed along tokens: each lane ORs its slot's codes into the
+//     words of its 8 channels, the four slots are combined by permlane swaps
+//     when a word row is complete, and one slot stores the row (32 bytes per
+//     lane); a word row the written range covers only in part is read, merged
+//     and written back, so tokens outside the range keep their codes.
 // Blocks are 128-token aligned, a multiple of every g and of E = 32/bits, so
 // no group and no packed value word is shared by two work-groups.
 #include <hip/hip_runtime.h>
@@ -49,6 +55,7 @@ template <int BITS>
 struct GroupQ {
   _Float16 s16, z16;
   float s, z;  // fp32 values of s16, z16
+  GroupQ() = default;
   __device__ __forceinline__ GroupQ(float mn, float mx) {
     constexpr float L = (float)((1 << BITS) - 1);
     s16 = (_Float16)__fdiv_rn(mx - mn, L);  // fp32 quotient rounded once, then to fp16 (RNE)
@@ -56,19 +63,10 @@ struct GroupQ {
     s = (float)s16;
     z = (float)z16;
   }
-  // rint(RN(d / s)) for d = x - z: with r = rcp(s) (1 ulp), d * r lies within
-  // 3 ulp of the correctly rounded quotient, so its nearest integer is the same
-  // unless it sits within that distance of a half-integer; |quotient| < 16
-  // there, where 2^-16 is many ulps.  Only those rare lanes take the exact
-  // division.
-  __device__ __forceinline__ uint32_t code(float x, float r) const {
+  // rint(RN((x - z) / s)), clamped: the correctly rounded division
+  __device__ __forceinline__ uint32_t code_exact(float x) const {
     if (s == 0.f) return 0u;
-    const float d = x - z;
-    float q = d * r;
-    const float f = q - floorf(q);
-    if (fabsf(f - 0.5f) < 0x1p-16f) q = __fdiv_rn(d, s);
-    q = rintf(q);  // round half to even
-    return (uint32_t)fminf(fmaxf(q, 0.f), (float)((1 << BITS) - 1));
+    return (uint32_t)__builtin_amdgcn_fmed3f(rintf(__fdiv_rn(x - z, s)), 0.f, (float)((1 << BITS) - 1));
   }
   __device__ __forceinline__ float rcp() const { return s == 0.f ? 0.f : __builtin_amdgcn_rcpf(s); }
 };
@@ -85,31 +83,6 @@ struct GroupQ {
 #define FOSCAR_DPP_OR(v, ctrl) \
   asm volatile("s_nop 1\n\tv_or_b32_dpp %0, %0, %0 " ctrl " row_mask:0xf bank_mask:0xf" : "+v"(v))
 
-// min and max over each aligned group of LANES lanes (16, 32 or 64)
-template <int LANES>
-__device__ __forceinline__ void group_minmax(float& mn, float& mx) {
-  FOSCAR_DPP_MINMAX(mn, mx, "quad_perm:[1,0,3,2]");
-  FOSCAR_DPP_MINMAX(mn, mx, "quad_perm:[2,3,0,1]");
-  FOSCAR_DPP_MINMAX(mn, mx, "row_half_mirror");
-  FOSCAR_DPP_MINMAX(mn, mx, "row_mirror");
-  if constexpr (LANES >= 32) {
-    float a, b;
-    asm volatile(
-        "v_mov_b32 %2, %0\n\tv_mov_b32 %3, %1\n\ts_nop 1\n\t"
-        "v_permlane16_swap_b32 %0, %2\n\tv_permlane16_swap_b32 %1, %3\n\t"
-        "v_min_f32 %0, %0, %2\n\tv_max_f32 %1, %1, %3"
-        : "+v"(mn), "+v"(mx), "=&v"(a), "=&v"(b));
-  }
-  if constexpr (LANES == 64) {
-    float a, b;
-    asm volatile(
-        "v_mov_b32 %2, %0\n\tv_mov_b32 %3, %1\n\ts_nop 1\n\t"
-        "v_permlane32_swap_b32 %0, %2\n\tv_permlane32_swap_b32 %1, %3\n\t"
-        "v_min_f32 %0, %0, %2\n\tv_max_f32 %1, %1, %3"
-        : "+v"(mn), "+v"(mx), "=&v"(a), "=&v"(b));
-  }
-}
-
 struct QuantArgs {
   const uint32_t* ksrc;    // bf16 pairs [B][Hkv][N][D/2]
   const uint32_t* vsrc;
@@ -124,128 +97,247 @@ struct QuantArgs {
   int32_t hkv, tcap, n_src;
 };
 
-// OR of `v` over the E/2 lanes (4 or 8, aligned) that share one key word
+// Codes of 8 values with scales s[j], offsets z[j] and r[j] = rcp(s[j]) (0
+// when s[j] = 0).  rint((x - z) * r) equals rint of the correctly rounded
+// quotient RN((x - z) / s) unless the product lies within 2^-16 of a
+// half-integer: rcp is within 1 ulp, so the product is within 3 ulp (< 2^-18
+// for quotients below 16) of that quotient.  If any lane of the wave has such
+// a value, the whole wave recomputes its 8 codes with the correctly rounded
+// division (a uniform branch, rarely taken; a per-value select would make the
+// compiler run the division every time).
 template <int BITS>
-__device__ __forceinline__ uint32_t or_word_lanes(uint32_t v) {
-  FOSCAR_DPP_OR(v, "quad_perm:[1,0,3,2]");
-  FOSCAR_DPP_OR(v, "quad_perm:[2,3,0,1]");
-  if constexpr (BITS == 2) FOSCAR_DPP_OR(v, "row_half_mirror");
-  return v;
+__device__ __forceinline__ void code8(const float (&x)[8], const GroupQ<BITS> (&g)[8], const float (&r)[8],
+                                      uint32_t (&c)[8]) {
+  constexpr float L = (float)((1 << BITS) - 1);
+  bool near = false;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const float q = (x[j] - g[j].z) * r[j];
+    const float k = rintf(q);
+    near |= fabsf(q - k) > 0.5f - 0x1p-16f;
+    c[j] = (uint32_t)__builtin_amdgcn_fmed3f(k, 0.f, L);
+  }
+  if (__builtin_expect(__any(near), 0)) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) c[j] = g[j].code_exact(x[j]);
+  }
 }
 
-// Store the value words of channels 2*lane, 2*lane+1 for the tokens of `mask`
-// (word row `row`), keeping the other tokens' codes.
-__device__ __forceinline__ void store_value_words(uint32_t* pv_row, uint32_t acc0, uint32_t acc1, uint32_t mask) {
-  uint2* p = reinterpret_cast<uint2*>(pv_row);
-  if (mask != 0xFFFFFFFFu) {
-    const uint2 old = *p;
-    acc0 |= old.x & ~mask;
-    acc1 |= old.y & ~mask;
+// OR / min / max of a value over the four token slots (lanes l, l^16, l^32,
+// l^48): v_permlane16_swap pairs rows 0-1 and 2-3, v_permlane32_swap the two
+// halves; every lane ends with the result.
+__device__ __forceinline__ uint32_t or_slots(uint32_t v) {
+  uint32_t a;
+  asm volatile(
+      "v_mov_b32 %1, %0\n\ts_nop 1\n\tv_permlane16_swap_b32 %0, %1\n\tv_or_b32 %0, %0, %1\n\t"
+      "v_mov_b32 %1, %0\n\ts_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\tv_or_b32 %0, %0, %1"
+      : "+v"(v), "=&v"(a));
+  return v;
+}
+__device__ __forceinline__ void minmax_slots(float& mn, float& mx) {
+  float a, b;
+  asm volatile(
+      "v_mov_b32 %2, %0\n\tv_mov_b32 %3, %1\n\ts_nop 1\n\t"
+      "v_permlane16_swap_b32 %0, %2\n\tv_permlane16_swap_b32 %1, %3\n\t"
+      "v_min_f32 %0, %0, %2\n\tv_max_f32 %1, %1, %3\n\t"
+      "v_mov_b32 %2, %0\n\tv_mov_b32 %3, %1\n\ts_nop 1\n\t"
+      "v_permlane32_swap_b32 %0, %2\n\tv_permlane32_swap_b32 %1, %3\n\t"
+      "v_min_f32 %0, %0, %2\n\tv_max_f32 %1, %1, %3"
+      : "+v"(mn), "+v"(mx), "=&v"(a), "=&v"(b));
+}
+// min / max over the aligned groups of LANES (1, 4, 8 or 16) lanes of one token slot
+template <int LANES>
+__device__ __forceinline__ void octet_group_minmax(float& mn, float& mx) {
+  if constexpr (LANES >= 4) {
+    FOSCAR_DPP_MINMAX(mn, mx, "quad_perm:[1,0,3,2]");
+    FOSCAR_DPP_MINMAX(mn, mx, "quad_perm:[2,3,0,1]");
   }
-  *p = make_uint2(acc0, acc1);
+  if constexpr (LANES >= 8) FOSCAR_DPP_MINMAX(mn, mx, "row_half_mirror");
+  if constexpr (LANES >= 16) FOSCAR_DPP_MINMAX(mn, mx, "row_mirror");
+}
+
+// Store the value words of channels 8o .. 8o+7 of one word row for the tokens
+// of `mask`, keeping the other tokens' codes.
+__device__ __forceinline__ void store_value_octet(uint32_t* row, const uint32_t (&acc)[8], uint32_t mask) {
+  uint4* p = reinterpret_cast<uint4*>(row);
+  uint4 a = make_uint4(acc[0], acc[1], acc[2], acc[3]), b = make_uint4(acc[4], acc[5], acc[6], acc[7]);
+  if (mask != 0xFFFFFFFFu) {
+    const uint4 oa = p[0], ob = p[1];
+    a.x |= oa.x & ~mask; a.y |= oa.y & ~mask; a.z |= oa.z & ~mask; a.w |= oa.w & ~mask;
+    b.x |= ob.x & ~mask; b.y |= ob.y & ~mask; b.z |= ob.z & ~mask; b.w |= ob.w & ~mask;
+  }
+  p[0] = a;
+  p[1] = b;
+}
+
+__device__ __forceinline__ void unpack_bf16x8(const uint4& w, float (&x)[8]) {
+  x[0] = bf16_lo(w.x); x[1] = bf16_hi(w.x); x[2] = bf16_lo(w.y); x[3] = bf16_hi(w.y);
+  x[4] = bf16_lo(w.z); x[5] = bf16_hi(w.z); x[6] = bf16_lo(w.w); x[7] = bf16_hi(w.w);
 }
 
 // One side (keys or values) of tokens [t_lo, t_hi) of one (sequence, KV head).
+// Lane l works on token slot r = l / 16 of each step of four tokens and on the
+// channel octet o = l % 16 (channels 8o .. 8o+7): one 16-byte load per lane
+// and row, four consecutive 256-byte rows per wave-instruction.
 template <int BITS, bool CH, int GRP, bool VALUE>
 __device__ __forceinline__ void quant_side(const uint32_t* src, uint32_t* packed, uint16_t* sc, uint16_t* zr,
                                            size_t bh, int tcap, int n_src, int s0, int t_lo, int t_hi) {
   constexpr int D = kHeadDim, E = 32 / BITS, KW = D / E;
+  constexpr int L = (1 << BITS) - 1;
   const int lane = threadIdx.x;
-  const uint32_t* src_bh = src + bh * (size_t)n_src * (D / 2) + lane;  // token t is source row t - s0
-  auto load_row = [&](int t) { return src_bh[(size_t)(t - s0) * (D / 2)]; };
-  const uint32_t cmask = (1u << BITS) - 1u;
-  const int e0 = (2 * lane) % E;  // element of channel 2*lane inside its key word (even)
-  auto store_key = [&](int t, uint32_t c0, uint32_t c1) {
-    const uint32_t w = or_word_lanes<BITS>((c0 << elem_shift<BITS>(e0)) | (c1 << elem_shift<BITS>(e0 + 1)));
-    if (lane % (E / 2) == 0) packed[(bh * tcap + t) * KW + (2 * lane) / E] = w;
-  };
-  uint32_t* vrow = packed + bh * (size_t)(tcap / E) * D + 2 * lane;  // value word row r at vrow[r * D]
-  // Rows are loaded U at a time ahead of their processing: the cross-lane asm
-  // of the processing keeps the compiler from moving later loads above it,
-  // which would leave one row load in flight per wave.
-  constexpr int U = 16;
-  auto load_batch = [&](uint32_t(&w)[U], int t, int t_end) {
+  const int r = lane >> 4, o = lane & 15;
+  const uint4* src_bh = reinterpret_cast<const uint4*>(src + bh * (size_t)n_src * (D / 2)) + o;  // row t - s0: [(t - s0) * 16]
+  uint32_t* vrow = packed + bh * (size_t)(tcap / E) * D + 8 * o;  // value word row w at vrow[w * D]
+  const uint32_t cmask = (uint32_t)L;
+  // key words: element e of channel 8o + j inside its word
+  auto key_word = [&](const uint32_t (&c)[8]) {
+    uint32_t part = 0;
 #pragma unroll
-    for (int u = 0; u < U; ++u) w[u] = (t + u < t_end) ? load_row(t + u) : 0u;
+    for (int j = 0; j < 8; ++j) {
+      const int e = (8 * o + j) % E;
+      part |= c[j] << elem_shift<BITS>(e);
+    }
+    return part;
+  };
+  auto store_key = [&](int t, bool act, const uint32_t (&c)[8]) {
+    uint32_t w = key_word(c);
+    if constexpr (BITS == 2) {  // a word is 16 channels: octets 2m and 2m+1
+      FOSCAR_DPP_OR(w, "quad_perm:[1,0,3,2]");
+      if (act && (o & 1) == 0) packed[(bh * tcap + t) * KW + o / 2] = w;
+    } else {  // a word is 8 channels: one octet
+      if (act) packed[(bh * tcap + t) * KW + o] = w;
+    }
+  };
+  // value words: token slots of a step share a word row (E is a multiple of 4)
+  uint32_t acc[8], msk = 0;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) acc[j] = 0;
+  auto add_value = [&](int t, bool act, const uint32_t (&c)[8]) {
+    const int sh = elem_shift<BITS>(t % E);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[j] |= c[j] << sh;
+    msk |= act ? (cmask << sh) : 0u;
+  };
+  auto flush_value = [&](int tb) {  // word row of the step starting at tb
+    // slots past the range were coded from zero rows: keep the written tokens' bits only
+    msk = or_slots(msk);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[j] = or_slots(acc[j]) & msk;
+    if (r == 0 && msk != 0) store_value_octet(vrow + (size_t)(tb / E) * D, acc, msk);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[j] = 0;
+    msk = 0;
+  };
+  // Steps of four tokens from t_lo rounded down to 4; rows are loaded U steps
+  // ahead (the cross-lane asm keeps the compiler from hoisting later loads).
+  constexpr int U = 4;
+  auto load_steps = [&](uint4 (&w)[U], int tb, int t_a, int t_b) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int t = tb + 4 * u + r;
+      w[u] = (t >= t_a && t < t_b) ? src_bh[(size_t)(t - s0) * 16] : make_uint4(0, 0, 0, 0);
+    }
   };
 
   if constexpr (!CH) {
-    uint32_t acc0 = 0, acc1 = 0, msk = 0;
-    for (int tb = t_lo; tb < t_hi; tb += U) {
-     uint32_t wb[U];
-     load_batch(wb, tb, t_hi);
+    const int t_first = t_lo & ~3;
+    for (int tb0 = t_first; tb0 < t_hi; tb0 += 4 * U) {
+      uint4 wb[U];
+      load_steps(wb, tb0, t_lo, t_hi);
 #pragma unroll
-     for (int u = 0; u < U; ++u) {
-      const int t = tb + u;
-      if (t >= t_hi) break;
-      const uint32_t w = wb[u];
-      const float x0 = bf16_lo(w), x1 = bf16_hi(w);
-      float mn = fminf(x0, x1), mx = fmaxf(x0, x1);
-      group_minmax<GRP / 2>(mn, mx);  // the g/2 lanes of this lane's group
-      const GroupQ<BITS> gq(mn, mx);
-      const float rq = gq.rcp();
-      if ((2 * lane) % GRP == 0) {
-        const size_t si = (bh * tcap + t) * (D / GRP) + (2 * lane) / GRP;
-        sc[si] = h_bits(gq.s16);
-        zr[si] = h_bits(gq.z16);
-      }
-      const uint32_t c0 = gq.code(x0, rq), c1 = gq.code(x1, rq);
-      if constexpr (!VALUE) {
-        store_key(t, c0, c1);
-      } else {
-        const int sh = elem_shift<BITS>(t % E);
-        acc0 |= c0 << sh;
-        acc1 |= c1 << sh;
-        msk |= cmask << sh;
-        if (t % E == E - 1 || t == t_hi - 1) {
-          store_value_words(vrow + (size_t)(t / E) * D, acc0, acc1, msk);
-          acc0 = acc1 = msk = 0;
+      for (int u = 0; u < U; ++u) {
+        const int tb = tb0 + 4 * u;
+        if (tb >= t_hi) break;
+        const int t = tb + r;
+        const bool act = t >= t_lo && t < t_hi;
+        float x[8];
+        unpack_bf16x8(wb[u], x);
+        float mn = fminf(fminf(fminf(x[0], x[1]), fminf(x[2], x[3])), fminf(fminf(x[4], x[5]), fminf(x[6], x[7])));
+        float mx = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])), fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
+        octet_group_minmax<GRP / 8>(mn, mx);  // the g/8 lanes of this lane's group
+        const GroupQ<BITS> gq(mn, mx);
+        const float rq = gq.rcp();
+        if (act && (8 * o) % GRP == 0) {
+          const size_t si = (bh * tcap + t) * (D / GRP) + (8 * o) / GRP;
+          sc[si] = h_bits(gq.s16);
+          zr[si] = h_bits(gq.z16);
+        }
+        const GroupQ<BITS> gs[8] = {gq, gq, gq, gq, gq, gq, gq, gq};
+        const float rs[8] = {rq, rq, rq, rq, rq, rq, rq, rq};
+        uint32_t c[8];
+        code8<BITS>(x, gs, rs, c);
+        if constexpr (!VALUE) {
+          store_key(t, act, c);
+        } else {
+          add_value(t, act, c);
+          if ((tb + 4) % E == 0 || tb + 4 >= t_hi) flush_value(tb);
         }
       }
-     }
     }
   } else {
-    // channel-wise groups: [g0, g0 + GRP) from token 0; t_lo is a group start
+    // channel-wise groups: [g0, g0 + GRP) from token 0; t_lo is a group start (a multiple of 4)
     for (int g0 = t_lo; g0 < t_hi; g0 += GRP) {
       const int g1 = min(g0 + GRP, t_hi);
-      float mn0 = INFINITY, mx0 = -INFINITY, mn1 = INFINITY, mx1 = -INFINITY;
-#pragma unroll 8
-      for (int t = g0; t < g1; ++t) {
-        const uint32_t w = load_row(t);
-        const float x0 = bf16_lo(w), x1 = bf16_hi(w);
-        mn0 = fminf(mn0, x0);
-        mx0 = fmaxf(mx0, x0);
-        mn1 = fminf(mn1, x1);
-        mx1 = fmaxf(mx1, x1);
-      }
-      const GroupQ<BITS> q0(mn0, mx0), q1(mn1, mx1);
-      const float r0 = q0.rcp(), r1 = q1.rcp();
-      const size_t si = (bh * (size_t)(tcap / GRP) + g0 / GRP) * D + 2 * lane;
-      *reinterpret_cast<uint32_t*>(sc + si) = (uint32_t)h_bits(q0.s16) | ((uint32_t)h_bits(q1.s16) << 16);
-      *reinterpret_cast<uint32_t*>(zr + si) = (uint32_t)h_bits(q0.z16) | ((uint32_t)h_bits(q1.z16) << 16);
-      uint32_t acc0 = 0, acc1 = 0, msk = 0;
-      for (int tb = g0; tb < g1; tb += U) {
-       uint32_t wb[U];
-       load_batch(wb, tb, g1);
+      float mn[8], mx[8];
 #pragma unroll
-       for (int u = 0; u < U; ++u) {
-        const int t = tb + u;
-        if (t >= g1) break;
-        const uint32_t w = wb[u];
-        const uint32_t c0 = q0.code(bf16_lo(w), r0), c1 = q1.code(bf16_hi(w), r1);
-        if constexpr (!VALUE) {
-          store_key(t, c0, c1);
-        } else {
-          const int sh = elem_shift<BITS>(t % E);
-          acc0 |= c0 << sh;
-          acc1 |= c1 << sh;
-          msk |= cmask << sh;
-          if (t % E == E - 1 || t == g1 - 1) {
-            store_value_words(vrow + (size_t)(t / E) * D, acc0, acc1, msk);
-            acc0 = acc1 = msk = 0;
+      for (int j = 0; j < 8; ++j) {
+        mn[j] = INFINITY;
+        mx[j] = -INFINITY;
+      }
+      for (int tb0 = g0; tb0 < g1; tb0 += 4 * U) {
+        uint4 wb[U];
+        load_steps(wb, tb0, g0, g1);
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          if (tb0 + 4 * u + r >= g1) continue;  // this slot's token is past the group (lane-local)
+          float x[8];
+          unpack_bf16x8(wb[u], x);
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            mn[j] = fminf(mn[j], x[j]);
+            mx[j] = fmaxf(mx[j], x[j]);
           }
         }
-       }
+      }
+      GroupQ<BITS> gq[8];
+      float rc[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        minmax_slots(mn[j], mx[j]);
+        gq[j] = GroupQ<BITS>(mn[j], mx[j]);
+        rc[j] = gq[j].rcp();
+      }
+      if (r == 0) {
+        const size_t si = (bh * (size_t)(tcap / GRP) + g0 / GRP) * D + 8 * o;
+        uint4 sv, zv;
+        auto pair = [&](const _Float16& a, const _Float16& b) { return (uint32_t)h_bits(a) | ((uint32_t)h_bits(b) << 16); };
+        sv = make_uint4(pair(gq[0].s16, gq[1].s16), pair(gq[2].s16, gq[3].s16), pair(gq[4].s16, gq[5].s16),
+                        pair(gq[6].s16, gq[7].s16));
+        zv = make_uint4(pair(gq[0].z16, gq[1].z16), pair(gq[2].z16, gq[3].z16), pair(gq[4].z16, gq[5].z16),
+                        pair(gq[6].z16, gq[7].z16));
+        *reinterpret_cast<uint4*>(sc + si) = sv;
+        *reinterpret_cast<uint4*>(zr + si) = zv;
+      }
+      for (int tb0 = g0; tb0 < g1; tb0 += 4 * U) {
+        uint4 wb[U];
+        load_steps(wb, tb0, g0, g1);
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const int tb = tb0 + 4 * u;
+          if (tb >= g1) break;
+          const int t = tb + r;
+          const bool act = t < g1;
+          float x[8];
+          unpack_bf16x8(wb[u], x);
+          uint32_t c[8];
+          code8<BITS>(x, gq, rc, c);
+          if constexpr (!VALUE) {
+            store_key(t, act, c);
+          } else {
+            add_value(t, act, c);
+            if ((tb + 4) % E == 0 || tb + 4 >= g1) flush_value(tb);
+          }
+        }
       }
     }
   }
