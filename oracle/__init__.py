@@ -18,6 +18,11 @@ What it computes (fp64 throughout):
 * ``decode`` / ``decode_rows``: every (sequence, query head) of a decode step;
   query head i reads KV head i // (Hq / Hkv) (GQA: "4 query heads per KV head",
   explainer, issue-budget paragraph).
+* ``decode_window_rows``: the same decode step with a window of recent tokens
+  kept in full precision beside the quantised cache (the accuracy recipe the
+  explainer's accuracy paragraph names: "full-precision windows of recent
+  tokens"); attention is over the union of the T_b dequantised cache tokens
+  and the window's tokens, computed by ``attend`` on the concatenation.
 * ``pack_k`` / ``pack_v`` / ``unpack_k`` / ``unpack_v``: the packed code layout
   of the C interface, written from its specification (keys packed along
   channels, values packed along tokens; even elements of a word in its low
@@ -126,6 +131,30 @@ def decode_rows(w: dict, rows, *, k_layout: str, v_layout: str, group: int, sm_s
             cache = {(b, h): _head(w, b, h, t, k_layout, v_layout, group)}
         k_hat, v_hat = cache[(b, h)]
         out[n], lse[n] = attend(q[b, i], k_hat, v_hat, sm_scale)
+    return out, lse
+
+
+def decode_window_rows(w: dict, win: dict, rows, *, k_layout: str, v_layout: str, group: int, sm_scale: float):
+    """``decode_rows`` over the quantised cache of ``w`` plus a full-precision
+    window: win["k"], win["v"] [B][Hkv][W][D] (bf16 values, any float dtype),
+    win["lens"] [B] (clamped to [0, W]).  Returns (out [n, D], lse [n]) in
+    fp64; a row with no token at all gives out = 0, lse = -inf."""
+    q = np.asarray(w["q"], dtype=np.float64)
+    B, Hq, D = q.shape
+    Hkv = w["k_codes"].shape[1]
+    Tcap = w["k_codes"].shape[2]
+    W = np.asarray(win["k"]).shape[2]
+    G = Hq // Hkv
+    out = np.zeros((len(rows), D))
+    lse = np.zeros(len(rows))
+    for n, (b, i) in enumerate(rows):
+        h = i // G
+        t = int(min(max(int(w["seq_lens"][b]), 0), Tcap))
+        wl = int(min(max(int(win["lens"][b]), 0), W))
+        k_hat, v_hat = _head(w, b, h, t, k_layout, v_layout, group)
+        k_all = np.concatenate([k_hat, np.asarray(win["k"], np.float64)[b, h, :wl]], axis=0)
+        v_all = np.concatenate([v_hat, np.asarray(win["v"], np.float64)[b, h, :wl]], axis=0)
+        out[n], lse[n] = attend(q[b, i], k_all, v_all, sm_scale)
     return out, lse
 
 

@@ -44,3 +44,46 @@ def test_dispatch_recorded_events_time_the_kernel():
     assert torch.equal(out, ref[0]) and torch.equal(lse, ref[1])
     ms = a.elapsed_time(b)
     assert 0.0 < ms < 100.0, ms
+
+
+@pytest.mark.parametrize("name", ["c2_paper_int2", "c5_ragged_int4_g64"])
+def test_graph_capture_replays_match_eager(name):
+    """Decode steps captured in a HIP graph (after the workspace of the capture
+    stream is reserved, a call allocates nothing and records no memset):
+    every replay, with eager work and synchronisation between replays, equals
+    the eager result bit for bit (the merge order is fixed, so the output is
+    deterministic).  The ragged workload takes the persistent work order,
+    whose counters the kernel itself resets for the next call."""
+    import bit_quantized_kv_split_amd as fos
+    spec = synth.SPECS[name].replace(batch=6, max_seq_len=4096, ragged_lo=64) if "ragged" in name else \
+        synth.SPECS[name].replace(batch=3, max_seq_len=4096)
+    dev, q, lens = stage_spec(spec)
+    layout = fos.layout_bits(spec.k_layout, spec.v_layout)
+    args = (dev["q"], dev["packed_k"], dev["packed_v"], dev["k_scale"], dev["k_zero"], dev["v_scale"], dev["v_zero"],
+            dev["seq_lens"], layout, spec.group)
+    ref_out, ref_lse = fos.prepare_decode(spec.bits, *args)()
+    torch.cuda.synchronize()
+    ref_out, ref_lse = ref_out.clone(), ref_lse.clone()
+    B, Hq, D = dev["q"].shape
+    dims = fos.make_dims(B, Hq, dev["packed_k"].shape[1], D, dev["packed_k"].shape[2])
+    side = torch.cuda.Stream()
+    fos.foscar_workspace_reserve(dims, spec.bits, layout, spec.group, stream=side)
+    out = torch.empty_like(ref_out)
+    lse = torch.empty_like(ref_lse)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(side):
+        call = fos.prepare_decode(spec.bits, *args, out=out, lse=lse, stream=side)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(graph, stream=side):
+            for _ in range(3):
+                call()
+    for k in range(4):
+        out.fill_(float("nan"))
+        lse.fill_(0.0)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref_out) and torch.equal(lse, ref_lse), f"replay {k}"
+        eager_out, eager_lse = fos.prepare_decode(spec.bits, *args)()  # eager work between replays
+        torch.cuda.synchronize()
+        assert torch.equal(eager_out, ref_out) and torch.equal(eager_lse, ref_lse), f"eager after replay {k}"

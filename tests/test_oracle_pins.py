@@ -485,3 +485,59 @@ def test_pack_roundtrip_and_positions(bits):
         sv = bits * ((t % E) // 2) + 16 * (t % 2)
         assert (int(pk[b, h, t, c // E]) >> sk) & ((1 << bits) - 1) == codes[b, h, t, c]
         assert (int(pv[b, h, t // E, c]) >> sv) & ((1 << bits) - 1) == codes[b, h, t, c]
+
+
+# ---------------------------------------------------------------- full-precision window
+
+def _window_case(rng, T, W, wl, D=16, g=8):
+    w = _one_head(rng.standard_normal((2, D)), rng.integers(0, 4, (T, D), dtype=np.uint8),
+                  rng.integers(0, 4, (T, D), dtype=np.uint8), rng.integers(1, 64, (T, D // g)) / 32.0,
+                  rng.integers(-64, 64, (T, D // g)) / 32.0, rng.integers(1, 64, (T, D // g)) / 32.0,
+                  rng.integers(-64, 64, (T, D // g)) / 32.0)
+    win = {"k": rng.standard_normal((1, 1, W, D)), "v": rng.standard_normal((1, 1, W, D)), "lens": np.array([wl])}
+    return w, win
+
+
+def test_window_only_is_plain_attention():
+    """No cache token (T = 0): the window alone is textbook softmax attention."""
+    rng = np.random.default_rng(21)
+    w, win = _window_case(rng, 4, 12, 9)
+    w["seq_lens"] = np.array([0], np.int32)
+    out, lse = oracle.decode_window_rows(w, win, [(0, 0), (0, 1)], k_layout="token", v_layout="token", group=8,
+                                         sm_scale=0.3)
+    for n in range(2):
+        q = w["q"][0, n]
+        k, v = win["k"][0, 0, :9], win["v"][0, 0, :9]
+        s = 0.3 * (k @ q)
+        p = np.exp(s - s.max())
+        assert np.allclose(out[n], (p / p.sum()) @ v, atol=1e-13)
+        assert abs(lse[n] - (s.max() + np.log(p.sum()))) < 1e-13
+
+
+def test_moving_tokens_between_cache_and_window_changes_nothing():
+    """A window token whose value equals a cache token's dequantised value can
+    move from the cache to the window (or back) without changing the output:
+    attention is over the union of both token sets."""
+    rng = np.random.default_rng(22)
+    T, D, g = 10, 16, 8
+    w, win = _window_case(rng, T, 6, 3, D, g)
+    k_hat = oracle.dequantize(w["k_codes"][0, 0], w["k_scale"][0, 0], w["k_zero"][0, 0], "token", g)
+    v_hat = oracle.dequantize(w["v_codes"][0, 0], w["v_scale"][0, 0], w["v_zero"][0, 0], "token", g)
+    full, lse_full = oracle.decode_window_rows(w, win, [(0, 0)], k_layout="token", v_layout="token", group=g,
+                                               sm_scale=0.25)
+    # the last 4 cache tokens move into the window
+    w2 = dict(w, seq_lens=np.array([T - 4], np.int32))
+    win2 = {"k": np.concatenate([k_hat[None, None, T - 4:], win["k"][:, :, :3]], axis=2),
+            "v": np.concatenate([v_hat[None, None, T - 4:], win["v"][:, :, :3]], axis=2), "lens": np.array([7])}
+    moved, lse_moved = oracle.decode_window_rows(w2, win2, [(0, 0)], k_layout="token", v_layout="token", group=g,
+                                                 sm_scale=0.25)
+    assert np.allclose(full, moved, atol=1e-13) and abs(lse_full[0] - lse_moved[0]) < 1e-13
+    # an empty window is the plain decode step
+    none = dict(win, lens=np.array([0]))
+    o1, l1 = oracle.decode_window_rows(w, none, [(0, 0)], k_layout="token", v_layout="token", group=g, sm_scale=0.25)
+    o2, l2 = oracle.decode_rows(w, [(0, 0)], k_layout="token", v_layout="token", group=g, sm_scale=0.25)
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+    # nothing at all: out 0, lse -inf
+    o3, l3 = oracle.decode_window_rows(dict(w, seq_lens=np.array([0], np.int32)), none, [(0, 0)], k_layout="token",
+                                       v_layout="token", group=g, sm_scale=0.25)
+    assert not o3.any() and l3[0] == -np.inf
