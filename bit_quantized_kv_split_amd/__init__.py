@@ -155,11 +155,51 @@ def foscar_decode_int4(q, packed_k, packed_v, k_scale, k_zero, v_scale, v_zero, 
                    out, lse, sm_scale, stream)
 
 
+def _decode_window(bits, q, packed_k, packed_v, k_scale, k_zero, v_scale, v_zero, seq_lens, layout, group, win_k,
+                   win_v, win_lens, out=None, lse=None, sm_scale=0.0, stream=None):
+    import torch
+    call = prepare_decode(bits, q, packed_k, packed_v, k_scale, k_zero, v_scale, v_zero, seq_lens, layout, group, out,
+                          lse, sm_scale, stream)
+    dev = q.device
+    _require(win_k, "win_k", torch.bfloat16, dev)
+    _require(win_v, "win_v", torch.bfloat16, dev)
+    _require(win_lens, "win_lens", torch.int32, dev)
+    B, Hq, D = q.shape
+    if win_k.dim() != 4 or tuple(win_k.shape) != tuple(win_v.shape) or win_k.shape[0] != B or win_k.shape[3] != D \
+            or win_k.shape[1] != packed_k.shape[1] or win_lens.numel() != B:
+        raise ValueError("win_k / win_v must be [B, Hkv, W, D] and win_lens [B]")
+    fn = _lib.load().foscar_decode_window_int2 if bits == 2 else _lib.load().foscar_decode_window_int4
+    a = call._args
+    with torch.cuda.device(dev):
+        rc = fn(*a[:11], _ptr(win_k), _ptr(win_v), _ptr(win_lens), int(win_k.shape[2]), *a[11:])
+    _check(rc, f"foscar_decode_window_int{bits}")
+    return call.out, call.lse
+
+
+def foscar_decode_window_int2(q, packed_k, packed_v, k_scale, k_zero, v_scale, v_zero, seq_lens, layout, group, win_k,
+                              win_v, win_lens, out=None, lse=None, sm_scale=0.0, stream=None):
+    """2-bit decode step plus a bf16 window of recent tokens [B, Hkv, W, D] (include/foscar.h)."""
+    return _decode_window(2, q, packed_k, packed_v, k_scale, k_zero, v_scale, v_zero, seq_lens, layout, group, win_k,
+                          win_v, win_lens, out, lse, sm_scale, stream)
+
+
+def foscar_decode_window_int4(q, packed_k, packed_v, k_scale, k_zero, v_scale, v_zero, seq_lens, layout, group, win_k,
+                              win_v, win_lens, out=None, lse=None, sm_scale=0.0, stream=None):
+    """4-bit decode step plus a bf16 window of recent tokens [B, Hkv, W, D] (include/foscar.h)."""
+    return _decode_window(4, q, packed_k, packed_v, k_scale, k_zero, v_scale, v_zero, seq_lens, layout, group, win_k,
+                          win_v, win_lens, out, lse, sm_scale, stream)
+
+
 def decode(q, packed_k, packed_v, k_scale, k_zero, v_scale, v_zero, seq_lens, *, bits, k_layout="token",
-           v_layout="token", group=128, sm_scale=0.0, out=None, lse=None, stream=None):
+           v_layout="token", group=128, sm_scale=0.0, out=None, lse=None, stream=None, window=None):
+    """Decode step; ``window`` = (win_k, win_v, win_lens) adds a bf16 window of recent tokens."""
+    layout = layout_bits(k_layout, v_layout)
+    if window is not None:
+        return _decode_window(bits, q, packed_k, packed_v, k_scale, k_zero, v_scale, v_zero, seq_lens, layout, group,
+                              *window, out, lse, sm_scale, stream)
     fn = foscar_decode_int2 if bits == 2 else foscar_decode_int4
-    return fn(q, packed_k, packed_v, k_scale, k_zero, v_scale, v_zero, seq_lens, layout_bits(k_layout, v_layout),
-              group, out, lse, sm_scale, stream)
+    return fn(q, packed_k, packed_v, k_scale, k_zero, v_scale, v_zero, seq_lens, layout, group, out, lse, sm_scale,
+              stream)
 
 
 def _quantize(bits, k_src, v_src, start, count, packed_k, packed_v, k_scale, k_zero, v_scale, v_zero, layout, group,

@@ -135,8 +135,8 @@ void plan(const foscar_dims* d, int layout, int group, int cus, int per_cu, int3
 size_t counter_bytes(const foscar_dims* d) {  // B*Hkv range counters, then the 2 work counters
   return (((size_t)d->batch * d->num_kv_heads + 2) * sizeof(int32_t) + 255) / 256 * 256;
 }
-size_t partial_bytes(const foscar_dims* d, int32_t splits) {
-  const size_t rows = (size_t)d->batch * d->num_q_heads * splits;
+size_t partial_bytes(const foscar_dims* d, int32_t splits) {  // range partials, then one window partial per row
+  const size_t rows = (size_t)d->batch * d->num_q_heads * (splits + 1);
   return rows * (foscar::kHeadDim + 1) * sizeof(float);
 }
 
@@ -182,15 +182,23 @@ int get_workspace(size_t cbytes, size_t pbytes, hipStream_t stream, int32_t** co
   return FOSCAR_OK;
 }
 
+// win_k == nullptr: no window.  Otherwise win_k, win_v bf16 [B][Hkv][win_cap][D] and win_lens [B].
 int decode_common(int bits, const foscar_dims* d, const void* q, const void* pk, const void* pv, const void* ks,
                   const void* kz, const void* vs, const void* vz, const int32_t* seq_lens, int layout, int group,
-                  void* out, float* lse, void* stream) {
+                  void* out, float* lse, void* stream, bool windowed = false, const void* win_k = nullptr,
+                  const void* win_v = nullptr, const int32_t* win_lens = nullptr, int32_t win_cap = 0) {
   const foscar::LaunchEvents ev = g_next_events;  // consumed by this call whether or not it launches
   g_next_events = foscar::LaunchEvents{};
   int rc = check_decode_shape(d, layout, group);
   if (rc) return rc;
+  if (windowed) {
+    if (win_cap < 0) return FOSCAR_EINVAL;
+    if (win_cap > foscar::kMaxWindow || d->batch > 65535) return FOSCAR_EUNSUPPORTED;
+  }
   if (d->batch == 0) return FOSCAR_OK;
   if (!q || !pk || !pv || !ks || !kz || !vs || !vz || !seq_lens || !out) return FOSCAR_EINVAL;
+  if (windowed && win_cap > 0 && (!win_k || !win_v || !win_lens)) return FOSCAR_EINVAL;
+  if (windowed && !win_lens) return FOSCAR_EINVAL;
 
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
@@ -231,6 +239,28 @@ int decode_common(int bits, const foscar_dims* d, const void* q, const void* pk,
   sa.persistent = ((long long)splits * d->batch * d->num_kv_heads > (long long)sa.grid_wgs &&
                    d->batch <= foscar::kMapMaxB) ? 1 : 0;
   sa.work_ctr = counters + (size_t)d->batch * d->num_kv_heads;
+  sa.win_o = nullptr;
+  sa.win_lse = nullptr;
+  if (windowed) {  // the window's partial first, into the last slot of the workspace; then the merge takes it in
+    const size_t rows = (size_t)d->batch * d->num_q_heads;
+    float* wo = sa.lse_part + rows * splits;
+    foscar::WindowArgs wa;
+    wa.q = (const uint16_t*)q;
+    wa.wk = (const uint16_t*)win_k;
+    wa.wv = (const uint16_t*)win_v;
+    wa.wlens = win_lens;
+    wa.o = wo;
+    wa.lse = wo + rows * foscar::kHeadDim;
+    wa.hq = d->num_q_heads;
+    wa.hkv = d->num_kv_heads;
+    wa.g_heads = sa.g_heads;
+    wa.wcap = win_cap;
+    wa.sm = sm;
+    e = foscar::launch_window(wa, d->batch, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e);
+    sa.win_o = wa.o;
+    sa.win_lse = wa.lse;
+  }
 
   e = foscar::launch_decode(bits, (layout & FOSCAR_K_CHANNEL) != 0, (layout & FOSCAR_V_CHANNEL) != 0, group,
                             d->batch, d->num_kv_heads, sa, (hipStream_t)stream, ev);
@@ -281,6 +311,22 @@ int foscar_decode_int4(const foscar_dims* dims, const void* q, const void* packe
                        const int32_t* seq_lens, int layout, int group, void* out, float* lse, void* stream) {
   return decode_common(4, dims, q, packed_k, packed_v, k_scale, k_zero, v_scale, v_zero, seq_lens, layout, group,
                        out, lse, stream);
+}
+
+int foscar_decode_window_int2(const foscar_dims* dims, const void* q, const void* packed_k, const void* packed_v,
+                              const void* k_scale, const void* k_zero, const void* v_scale, const void* v_zero,
+                              const int32_t* seq_lens, int layout, int group, const void* win_k, const void* win_v,
+                              const int32_t* win_lens, int32_t win_cap, void* out, float* lse, void* stream) {
+  return decode_common(2, dims, q, packed_k, packed_v, k_scale, k_zero, v_scale, v_zero, seq_lens, layout, group,
+                       out, lse, stream, true, win_k, win_v, win_lens, win_cap);
+}
+
+int foscar_decode_window_int4(const foscar_dims* dims, const void* q, const void* packed_k, const void* packed_v,
+                              const void* k_scale, const void* k_zero, const void* v_scale, const void* v_zero,
+                              const int32_t* seq_lens, int layout, int group, const void* win_k, const void* win_v,
+                              const int32_t* win_lens, int32_t win_cap, void* out, float* lse, void* stream) {
+  return decode_common(4, dims, q, packed_k, packed_v, k_scale, k_zero, v_scale, v_zero, seq_lens, layout, group,
+                       out, lse, stream, true, win_k, win_v, win_lens, win_cap);
 }
 
 int foscar_quantize_int2(const foscar_dims* dims, const void* k_src, const void* v_src, int32_t src_tokens,

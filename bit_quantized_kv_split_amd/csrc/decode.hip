@@ -434,6 +434,17 @@ __device__ __forceinline__ void merge_ranges(const SplitArgs& a, int b, int h, i
     m0 = b0;
     m1 = b1;
   }
+  if (a.win_o) {  // the full-precision window's partial is one more term of the same merge
+    const float wl0 = a.win_lse[row0], wl1 = a.win_lse[row1];
+    const float b0 = fmaxf(m0, wl0), b1 = fmaxf(m1, wl1);  // m0, m1 finite: the cache has tokens
+    const float r0 = __expf(m0 - b0), r1 = __expf(m1 - b1), w0 = __expf(wl0 - b0), w1 = __expf(wl1 - b1);
+    n0 = fmaf(w0, a.win_o[row0 * D + c], n0 * r0);
+    d0 = fmaf(d0, r0, w0);
+    n1 = fmaf(w1, a.win_o[row1 * D + c], n1 * r1);
+    d1 = fmaf(d1, r1, w1);
+    m0 = b0;
+    m1 = b1;
+  }
   a.out[row0 * D + c] = to_bf16_rne(n0 / d0);
   if (c == 0 && a.lse) a.lse[row0] = m0 + __logf(d0);
   if (two) {
@@ -601,8 +612,9 @@ __device__ __forceinline__ void run_item(const SplitArgs& a, const int b, const 
     if (T == 0 && split == 0) {
       for (int idx = (int)tid; idx < a.g_heads * kHeadDim; idx += blockDim.x) {
         const size_t row = (size_t)b * a.hq + h * a.g_heads + idx / kHeadDim;
-        a.out[row * kHeadDim + idx % kHeadDim] = 0;
-        if (idx % kHeadDim == 0 && a.lse) a.lse[row] = -INFINITY;
+        // no cache token: the window's result as it is (0 and -inf for an empty window too)
+        a.out[row * kHeadDim + idx % kHeadDim] = a.win_o ? to_bf16_rne(a.win_o[row * kHeadDim + idx % kHeadDim]) : 0;
+        if (idx % kHeadDim == 0 && a.lse) a.lse[row] = a.win_o ? a.win_lse[row] : -INFINITY;
       }
     }
     if (next && wave == 0) {
@@ -1237,8 +1249,15 @@ __device__ __forceinline__ void run_item(const SplitArgs& a, const int b, const 
     const size_t row = (size_t)b * a.hq + h * a.g_heads + i;
     const float o = num / den, l_nat = (M + __log2f(den)) * kLn2;
     if (ns == 1) {  // the only range: final output
-      a.out[row * D + c] = to_bf16_rne(o);
-      if (c == 0 && a.lse) a.lse[row] = l_nat;
+      float of = o, lf = l_nat;
+      if (a.win_o) {  // merged with the full-precision window's partial
+        const float wl = a.win_lse[row];
+        const float mm = fmaxf(l_nat, wl), w1 = __expf(l_nat - mm), w2 = __expf(wl - mm);
+        of = fmaf(w1, o, w2 * a.win_o[row * D + c]) / (w1 + w2);
+        lf = mm + __logf(w1 + w2);
+      }
+      a.out[row * D + c] = to_bf16_rne(of);
+      if (c == 0 && a.lse) a.lse[row] = lf;
     } else {
       // device-coherent stores (they bypass this XCD's L2 for the merging work-group)
       __hip_atomic_store(a.o_part + (row * a.splits + split) * D + c, o, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);

@@ -38,7 +38,25 @@ struct SplitArgs {
   int32_t grid_wgs;          // persistent grid size (one round of resident work-groups)
   int32_t batch;             // B
   int32_t* work_ctr;         // [2] items taken, work-groups left; zero between calls
+  const float* win_o;        // fp32 [B][Hq][D] normalised output over a full-precision window, or null
+  const float* win_lse;      // fp32 [B][Hq] its natural-log lse (-inf: empty window)
 };
+
+// Attention over a full-precision (bf16) window of recent tokens (window.hip):
+// per (sequence, KV head) the window's normalised output and lse, merged into
+// the decode result by the decode kernel.
+struct WindowArgs {
+  const uint16_t* q;         // bf16 [B][Hq][D]
+  const uint16_t* wk;        // bf16 [B][Hkv][wcap][D]
+  const uint16_t* wv;        // bf16 [B][Hkv][wcap][D]
+  const int32_t* wlens;      // [B] window tokens, clamped to [0, wcap]
+  float* o;                  // fp32 [B][Hq][D]
+  float* lse;                // fp32 [B][Hq]
+  int32_t hq, hkv, g_heads, wcap;
+  float sm;                  // softmax scale
+};
+constexpr int kMaxWindow = 4096;  // tokens of a window (LDS score table of the window kernel)
+hipError_t launch_window(const WindowArgs& a, int batch, hipStream_t stream);
 
 // Events the dispatch records around the kernel (either may be null).
 struct LaunchEvents {

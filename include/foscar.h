@@ -119,6 +119,35 @@ int foscar_decode_int4(const foscar_dims* dims, const void* q, const void* packe
                        const int32_t* seq_lens, int layout, int group, void* out, float* lse, void* stream);
 
 /*
+ * Decode step over the quantised cache plus a full-precision window of recent
+ * tokens (2-bit: foscar_decode_window_int2, 4-bit: foscar_decode_window_int4).
+ *
+ * The FOSCAR explainer's accuracy paragraph names full-precision windows of
+ * recent tokens as part of the accuracy recipe a 2-bit cache needs.  The
+ * window's tokens are further keys and values of the same softmax: out and lse
+ * are those of attention over the T_b cache tokens and the window's tokens
+ * together.  The window is attended by its own kernel, in fp32 from bf16, and
+ * merged with the cache's ranges by log-sum-exp inside the decode kernel.
+ *
+ * Arguments as foscar_decode_int2/int4, plus:
+ * win_k, win_v  bf16 [B][Hkv][win_cap][D]: window keys and values
+ * win_lens      int32 [B] (device): window tokens of each sequence, clamped to
+ *               [0, win_cap]; rows past them may hold anything
+ * win_cap       0 .. 4096 tokens (win_k / win_v may be NULL when 0)
+ * A sequence with no cache token and no window token gives out = 0,
+ * lse = -inf.  The window uses a slot of the split workspace (see
+ * foscar_workspace_reserve, which reserves it).
+ */
+int foscar_decode_window_int2(const foscar_dims* dims, const void* q, const void* packed_k, const void* packed_v,
+                              const void* k_scale, const void* k_zero, const void* v_scale, const void* v_zero,
+                              const int32_t* seq_lens, int layout, int group, const void* win_k, const void* win_v,
+                              const int32_t* win_lens, int32_t win_cap, void* out, float* lse, void* stream);
+int foscar_decode_window_int4(const foscar_dims* dims, const void* q, const void* packed_k, const void* packed_v,
+                              const void* k_scale, const void* k_zero, const void* v_scale, const void* v_zero,
+                              const int32_t* seq_lens, int layout, int group, const void* win_k, const void* win_v,
+                              const int32_t* win_lens, int32_t win_cap, void* out, float* lse, void* stream);
+
+/*
  * Quantise new keys and values into the cache (2-bit: foscar_quantize_int2,
  * 4-bit: foscar_quantize_int4), in the layouts the decode entry points read.
  *

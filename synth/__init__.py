@@ -349,3 +349,12 @@ def device_normal_bf16(shape, seed: int, device="cuda"):
     import torch
     gen = torch.Generator(device=device).manual_seed(seed)
     return torch.randn(tuple(shape), generator=gen, device=device).to(torch.bfloat16)
+
+
+def make_window(seed: int, batch: int, num_kv_heads: int, cap: int, lens, head_dim: int = 128, std: float = 1.0):
+    """Full-precision window of recent tokens: keys and values N(0, std^2)
+    rounded to bf16, fp32 arrays [B][Hkv][cap][D], and int32 lengths."""
+    rng = np.random.default_rng([seed, 901, batch, num_kv_heads, cap])
+    k = bf16_round((rng.standard_normal((batch, num_kv_heads, cap, head_dim)) * std).astype(np.float32))
+    v = bf16_round((rng.standard_normal((batch, num_kv_heads, cap, head_dim)) * std).astype(np.float32))
+    return {"k": k, "v": v, "lens": np.asarray(lens, np.int32)}

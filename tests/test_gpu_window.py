@@ -1,0 +1,99 @@
+"""GPU parity of decode with a full-precision window of recent tokens
+(foscar_decode_window_int2/int4, through the C interface) against the
+oracle's attention over the union of dequantised cache tokens and window
+tokens, with the decode bar of gpu_util: single-range and multi-range
+sequences, the persistent work order, empty caches with a window, empty
+windows, and nothing at all."""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from gpu_util import check, stage_spec, value_rms
+
+pytestmark = pytest.mark.gpu
+
+
+def _oracle(spec, q, lens, win):
+    G = spec.num_q_heads // spec.num_kv_heads
+    B, Hq, D = spec.batch, spec.num_q_heads, spec.head_dim
+    out, lse, vsc = np.zeros((B, Hq, D)), np.zeros((B, Hq)), np.zeros((B, Hq, D))
+    for b in range(B):
+        for h in range(spec.num_kv_heads):
+            head = synth.make_head(spec, b, h, seq_len=int(lens[b]))
+            w = {k: v[None, None] for k, v in head.items()}
+            w["q"] = q[b:b + 1, h * G:(h + 1) * G]
+            w["seq_lens"] = np.array([lens[b]], np.int32)
+            wl = int(win["lens"][b])
+            ws = {"k": win["k"][b:b + 1, h:h + 1], "v": win["v"][b:b + 1, h:h + 1], "lens": np.array([wl])}
+            o, l = oracle.decode_window_rows(w, ws, [(0, i) for i in range(G)], k_layout=spec.k_layout,
+                                             v_layout=spec.v_layout, group=spec.group, sm_scale=spec.sm_scale)
+            out[b, h * G:(h + 1) * G], lse[b, h * G:(h + 1) * G] = o, l
+            # magnitude of the values averaged: cache channels and window channels
+            t = int(lens[b])
+            r = value_rms(spec, head, t) if t else np.zeros(D)
+            wv = win["v"][b, h, :wl].astype(np.float64)
+            rw = np.sqrt(np.mean(wv * wv, axis=0)) if wl else np.zeros(D)
+            vsc[b, h * G:(h + 1) * G] = np.maximum(r, rw)
+    return out, lse, vsc
+
+
+def _run(spec, dev, win):
+    import torch
+    import bit_quantized_kv_split_amd as fos
+    wk = torch.from_numpy(win["k"]).to(torch.bfloat16).cuda()
+    wv = torch.from_numpy(win["v"]).to(torch.bfloat16).cuda()
+    wl = torch.from_numpy(win["lens"]).cuda()
+    out, lse = fos.decode(dev["q"], dev["packed_k"], dev["packed_v"], dev["k_scale"], dev["k_zero"], dev["v_scale"],
+                          dev["v_zero"], dev["seq_lens"], bits=spec.bits, k_layout=spec.k_layout,
+                          v_layout=spec.v_layout, group=spec.group, window=(wk, wv, wl))
+    torch.cuda.synchronize()
+    return out.float().cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64)
+
+
+CASES = [(2, "token", "token", 128), (4, "token", "token", 64), (2, "channel", "channel", 32),
+         (4, "channel", "channel", 128), (2, "token", "channel", 64), (4, "channel", "token", 32)]
+
+
+@pytest.mark.parametrize("bits,kl,vl,g", CASES)
+def test_window_matrix(bits, kl, vl, g):
+    """Ragged cache lengths (one empty) and ragged windows (one empty, one on
+    the empty cache, one sequence with neither)."""
+    std = (0.1, 10.0) if "channel" in (kl, vl) else None
+    spec = synth.Spec(f"win_{bits}_{kl}_{vl}_{g}", 12, bits, kl, vl, g, 5, 8, 2, 128, 768,
+                      lens=(768, 517, 130, 0, 0), channel_std_logu=std)
+    dev, q, lens = stage_spec(spec)
+    win = synth.make_window(1, spec.batch, spec.num_kv_heads, 200, [200, 0, 37, 64, 0])
+    out, lse = _run(spec, dev, win)
+    ro, rl, vsc = _oracle(spec, q, lens, win)
+    check(out, lse, ro, rl, spec.name, vsc)
+
+
+@pytest.mark.parametrize("name,cap", [("c3_long_int2", 1024), ("c5_ragged_int2_g64", 4096)])
+def test_window_multi_range_and_persistent(name, cap):
+    """Many ranges per sequence (merge path) and the persistent work order
+    (ragged batch), with windows up to the largest supported."""
+    base = synth.SPECS[name]
+    spec = base.replace(batch=1, num_q_heads=4, num_kv_heads=1, max_seq_len=16384) if "long" in name else \
+        base.replace(batch=6, num_q_heads=8, num_kv_heads=2, max_seq_len=4096, ragged_lo=64)
+    dev, q, lens = stage_spec(spec)
+    wl = [cap - 7 * b for b in range(spec.batch)]
+    win = synth.make_window(2, spec.batch, spec.num_kv_heads, cap, wl)
+    out, lse = _run(spec, dev, win)
+    ro, rl, vsc = _oracle(spec, q, lens, win)
+    check(out, lse, ro, rl, spec.name, vsc)
+
+
+def test_window_dominates_when_its_scores_are_larger():
+    """A window whose keys align with the query takes almost all the weight:
+    the output approaches the window's own attention output (a property of
+    the merge, not only agreement with the oracle)."""
+    spec = synth.SPECS["c1_tiny_int2"]
+    dev, q, lens = stage_spec(spec)
+    win = synth.make_window(3, 1, 1, 8, [8])
+    win["k"][0, 0] = synth.bf16_round((q[0, 0] * 4.0).astype(np.float32))[None].repeat(8, 0)
+    out, lse = _run(spec, dev, win)
+    ro, rl, vsc = _oracle(spec, q, lens, win)
+    check(out, lse, ro, rl, "dominant window", vsc)
+    mean_v = win["v"][0, 0].astype(np.float64).mean(0)
+    assert np.abs(out[0, 0] - mean_v).max() < 0.05
