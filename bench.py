@@ -40,6 +40,8 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--dump-steps", action="store_true", help="print each step's kernel microseconds to stderr")
+    ap.add_argument("--window", type=int, default=0,
+                    help="decode with a bf16 window of this many recent tokens per sequence beside the cache")
     ap.add_argument("--op", choices=["decode", "quantize"], default="decode",
                     help="decode: the decode step (default); quantize: quantise-and-append of the workload's cache")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
@@ -204,9 +206,20 @@ def main():
     outs = [(torch.empty((spec.batch, spec.num_q_heads, spec.head_dim), dtype=torch.bfloat16, device=dev_name),
              torch.empty((spec.batch, spec.num_q_heads), dtype=torch.float32, device=dev_name)) for _ in copies]
     # one prepared call per cache copy: arguments checked and marshalled once, a step is one C call
-    calls = [fos.prepare_decode(spec.bits, c["q"], c["packed_k"], c["packed_v"], c["k_scale"], c["k_zero"],
-                                c["v_scale"], c["v_zero"], c["seq_lens"], layout, spec.group, out=o, lse=l)
-             for c, (o, l) in zip(copies, outs)]
+    if args.window > 0:  # decode with a full-precision window: one call = window kernel + decode kernel
+        win = synth.make_window(0, spec.batch, spec.num_kv_heads, args.window, [args.window] * spec.batch,
+                                spec.head_dim)
+        wins = [(torch.from_numpy(win["k"]).to(torch.bfloat16).to(dev_name),
+                 torch.from_numpy(win["v"]).to(torch.bfloat16).to(dev_name),
+                 torch.from_numpy(win["lens"]).to(dev_name)) for _ in copies]
+        calls = [fos.prepare_decode(spec.bits, c["q"], c["packed_k"], c["packed_v"], c["k_scale"], c["k_zero"],
+                                    c["v_scale"], c["v_zero"], c["seq_lens"], layout, spec.group, out=o, lse=l,
+                                    window=w)
+                 for c, (o, l), w in zip(copies, outs, wins)]
+    else:
+        calls = [fos.prepare_decode(spec.bits, c["q"], c["packed_k"], c["packed_v"], c["k_scale"], c["k_zero"],
+                                    c["v_scale"], c["v_zero"], c["seq_lens"], layout, spec.group, out=o, lse=l)
+                 for c, (o, l) in zip(copies, outs)]
 
     def step(k):
         calls[k % len(calls)]()
@@ -239,14 +252,19 @@ def main():
         b.record(stream)
     torch.cuda.synchronize()
     for k in range(args.steps):
-        fos.foscar_record_next_launch(ev[k][0], ev[k][1])
-        step(k)
+        if args.window > 0:  # two kernels per step: stream events around both
+            ev[k][0].record(stream)
+            step(k)
+            ev[k][1].record(stream)
+        else:
+            fos.foscar_record_next_launch(ev[k][0], ev[k][1])
+            step(k)
     torch.cuda.synchronize()
     kernel_ms = [a.elapsed_time(b) for a, b in ev]
     if args.dump_steps:
         print("kernel us per step:", " ".join(f"{x * 1e3:.1f}" for x in kernel_ms), file=sys.stderr)
     ms_per_step = wall * 1e3 / args.steps
-    alg = synth.algorithmic_bytes(spec, lens)
+    alg = synth.algorithmic_bytes(spec, lens) + 2 * 2 * spec.batch * spec.num_kv_heads * args.window * spec.head_dim
     value = alg / (ms_per_step * 1e-3) / 1e9
     k_avg = sum(kernel_ms) / len(kernel_ms)
     achieved = alg / (k_avg * 1e-3) / 1e9
@@ -273,7 +291,7 @@ def main():
                                f"INT{spec.bits}, K {spec.k_layout}-wise / V {spec.v_layout}-wise, group {spec.group}",
                    "global_batch": spec.batch, "seq_len": spec.max_seq_len, "bits": spec.bits,
                    "k_layout": spec.k_layout, "v_layout": spec.v_layout, "group": spec.group,
-                   "splits": splits, "chunk": chunk, "cache_copies": len(copies),
+                   "splits": splits, "chunk": chunk, "cache_copies": len(copies), "window_tokens": args.window,
                    "algorithmic_bytes_per_step": alg},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic_per_launch(spec.name),

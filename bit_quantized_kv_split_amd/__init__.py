@@ -100,8 +100,9 @@ class DecodeCall:
 
 
 def prepare_decode(bits, q, packed_k, packed_v, k_scale, k_zero, v_scale, v_zero, seq_lens, layout, group,
-                   out=None, lse=None, sm_scale=0.0, stream=None):
-    """Check and marshal a decode step (arguments as foscar_decode_int2/4); returns a DecodeCall."""
+                   out=None, lse=None, sm_scale=0.0, stream=None, window=None):
+    """Check and marshal a decode step (arguments as foscar_decode_int2/4); returns a DecodeCall.
+    ``window`` = (win_k, win_v, win_lens) marshals foscar_decode_window_int2/4 instead."""
     import torch
     if bits not in (2, 4):
         raise ValueError(f"bits must be 2 or 4, got {bits}")
@@ -132,6 +133,18 @@ def prepare_decode(bits, q, packed_k, packed_v, k_scale, k_zero, v_scale, v_zero
     call._dev = dev.index if dev.index is not None else torch.cuda.current_device()
     call.out, call.lse = out, lse
     call._keep = (dims, q, packed_k, packed_v, k_scale, k_zero, v_scale, v_zero, seq_lens)
+    if window is not None:
+        win_k, win_v, win_lens = window
+        _require(win_k, "win_k", torch.bfloat16, dev)
+        _require(win_v, "win_v", torch.bfloat16, dev)
+        _require(win_lens, "win_lens", torch.int32, dev)
+        if win_k.dim() != 4 or tuple(win_k.shape) != tuple(win_v.shape) or win_k.shape[0] != B \
+                or win_k.shape[1] != Hkv or win_k.shape[3] != D or win_lens.numel() != B:
+            raise ValueError("win_k / win_v must be [B, Hkv, W, D] and win_lens [B]")
+        call._fn = lib.foscar_decode_window_int2 if bits == 2 else lib.foscar_decode_window_int4
+        call._args = call._args[:11] + (_ptr(win_k), _ptr(win_v), _ptr(win_lens), int(win_k.shape[2])) + call._args[11:]
+        call._name = f"foscar_decode_window_int{bits}"
+        call._keep = call._keep + (win_k, win_v, win_lens)
     return call
 
 
@@ -157,23 +170,8 @@ def foscar_decode_int4(q, packed_k, packed_v, k_scale, k_zero, v_scale, v_zero, 
 
 def _decode_window(bits, q, packed_k, packed_v, k_scale, k_zero, v_scale, v_zero, seq_lens, layout, group, win_k,
                    win_v, win_lens, out=None, lse=None, sm_scale=0.0, stream=None):
-    import torch
-    call = prepare_decode(bits, q, packed_k, packed_v, k_scale, k_zero, v_scale, v_zero, seq_lens, layout, group, out,
-                          lse, sm_scale, stream)
-    dev = q.device
-    _require(win_k, "win_k", torch.bfloat16, dev)
-    _require(win_v, "win_v", torch.bfloat16, dev)
-    _require(win_lens, "win_lens", torch.int32, dev)
-    B, Hq, D = q.shape
-    if win_k.dim() != 4 or tuple(win_k.shape) != tuple(win_v.shape) or win_k.shape[0] != B or win_k.shape[3] != D \
-            or win_k.shape[1] != packed_k.shape[1] or win_lens.numel() != B:
-        raise ValueError("win_k / win_v must be [B, Hkv, W, D] and win_lens [B]")
-    fn = _lib.load().foscar_decode_window_int2 if bits == 2 else _lib.load().foscar_decode_window_int4
-    a = call._args
-    with torch.cuda.device(dev):
-        rc = fn(*a[:11], _ptr(win_k), _ptr(win_v), _ptr(win_lens), int(win_k.shape[2]), *a[11:])
-    _check(rc, f"foscar_decode_window_int{bits}")
-    return call.out, call.lse
+    return prepare_decode(bits, q, packed_k, packed_v, k_scale, k_zero, v_scale, v_zero, seq_lens, layout, group, out,
+                          lse, sm_scale, stream, window=(win_k, win_v, win_lens))()
 
 
 def foscar_decode_window_int2(q, packed_k, packed_v, k_scale, k_zero, v_scale, v_zero, seq_lens, layout, group, win_k,
