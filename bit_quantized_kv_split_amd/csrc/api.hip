@@ -100,7 +100,8 @@ int resident_per_cu(int device, int bits, int layout, int group) {
 // only add per-range prologue, hand-off and merge work; measured), ranges of
 // at most 4096 tokens so ragged batches balance, every range a multiple of the
 // wave unit.
-void plan(const foscar_dims* d, int layout, int group, int cus, int per_cu, int32_t* splits, int32_t* chunk) {
+void plan(const foscar_dims* d, int layout, int group, int cus, int per_cu, int32_t* splits, int32_t* chunk,
+          int extra_per_pair = 0) {
   const int unit = unit_tokens(layout, group);
   const int tcap = d->max_seq_len;
   const int units = tcap / unit;
@@ -115,8 +116,9 @@ void plan(const foscar_dims* d, int layout, int group, int cus, int per_cu, int3
   if (env && atoi(env) > 0) {
     s = atoi(env);
   } else {
-    const long long target = (long long)per_cu * cus;  // one round of resident work-groups
-    if (bh > 0) s = (target + bh - 1) / bh;
+    // one round of resident work-groups, less the pairs' other work-groups (a fused window)
+    const long long target = (long long)per_cu * cus - bh * extra_per_pair;
+    if (bh > 0) s = std::max(1LL, (target + bh - 1) / bh);
     // ranges of at most 4096 tokens: on ragged batches (lengths unknown to the host) shorter
     // ranges keep the last work-groups short; measured best for long and ragged caches
     const long long by_len = (tcap + 4095) / 4096;
@@ -206,6 +208,12 @@ int decode_common(int bits, const foscar_dims* d, const void* q, const void* pk,
   int32_t splits = 1, chunk = foscar::kTile;
   const int cus = compute_units(dev), per_cu = resident_per_cu(dev, bits, layout, group);
   plan(d, layout, group, cus, per_cu, &splits, &chunk);
+  // a small window is attended inside the launch when the grid runs in one round: one work-group
+  // per pair, so the ranges are planned for one slot fewer per pair
+  const bool one_round = (long long)splits * d->batch * d->num_kv_heads <= (long long)cus * per_cu ||
+                         d->batch > foscar::kMapMaxB;
+  const bool fuse_window = windowed && win_cap <= foscar::kFusedWindowMax && one_round;
+  if (fuse_window) plan(d, layout, group, cus, per_cu, &splits, &chunk, 1);
   int32_t* counters = nullptr;
   float* partials = nullptr;
   rc = get_workspace(counter_bytes(d), partial_bytes(d, splits), (hipStream_t)stream, &counters, &partials);
@@ -241,7 +249,22 @@ int decode_common(int bits, const foscar_dims* d, const void* q, const void* pk,
   sa.work_ctr = counters + (size_t)d->batch * d->num_kv_heads;
   sa.win_o = nullptr;
   sa.win_lse = nullptr;
-  if (windowed) {  // the window's partial first, into the last slot of the workspace; then the merge takes it in
+  sa.win_fused = 0;
+  sa.win_k = sa.win_v = nullptr;
+  sa.win_lens = nullptr;
+  sa.win_cap = 0;
+  sa.win_sm = sm;
+  if (fuse_window && !sa.persistent) {
+    // attended inside the decode launch by one more work-group per pair, concurrently with the ranges
+    const size_t rows = (size_t)d->batch * d->num_q_heads;
+    sa.win_o = sa.lse_part + rows * splits;
+    sa.win_lse = sa.win_o + rows * foscar::kHeadDim;
+    sa.win_fused = 1;
+    sa.win_k = (const uint16_t*)win_k;
+    sa.win_v = (const uint16_t*)win_v;
+    sa.win_lens = win_lens;
+    sa.win_cap = win_cap;
+  } else if (windowed) {  // the window's partial first, into the last slot of the workspace; then the merge takes it in
     const size_t rows = (size_t)d->batch * d->num_q_heads;
     float* wo = sa.lse_part + rows * splits;
     foscar::WindowArgs wa;

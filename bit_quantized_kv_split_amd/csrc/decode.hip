@@ -435,12 +435,14 @@ __device__ __forceinline__ void merge_ranges(const SplitArgs& a, int b, int h, i
     m1 = b1;
   }
   if (a.win_o) {  // the full-precision window's partial is one more term of the same merge
-    const float wl0 = a.win_lse[row0], wl1 = a.win_lse[row1];
+    // device-coherent loads: in a fused launch another work-group wrote the slot
+    const float wl0 = coherent_load(a.win_lse + row0), wl1 = coherent_load(a.win_lse + row1);
+    const float wo0 = coherent_load(a.win_o + row0 * D + c), wo1 = coherent_load(a.win_o + row1 * D + c);
     const float b0 = fmaxf(m0, wl0), b1 = fmaxf(m1, wl1);  // m0, m1 finite: the cache has tokens
     const float r0 = __expf(m0 - b0), r1 = __expf(m1 - b1), w0 = __expf(wl0 - b0), w1 = __expf(wl1 - b1);
-    n0 = fmaf(w0, a.win_o[row0 * D + c], n0 * r0);
+    n0 = fmaf(w0, wo0, n0 * r0);
     d0 = fmaf(d0, r0, w0);
-    n1 = fmaf(w1, a.win_o[row1 * D + c], n1 * r1);
+    n1 = fmaf(w1, wo1, n1 * r1);
     d1 = fmaf(d1, r1, w1);
     m0 = b0;
     m1 = b1;
@@ -609,7 +611,7 @@ __device__ __forceinline__ void run_item(const SplitArgs& a, const int b, const 
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r0 = split * a.chunk;
   if (r0 >= T) {  // no token in this range; an empty sequence's rows are written once
-    if (T == 0 && split == 0) {
+    if (T == 0 && split == 0 && !a.win_fused) {  // (a fused window's work-group writes them itself)
       for (int idx = (int)tid; idx < a.g_heads * kHeadDim; idx += blockDim.x) {
         const size_t row = (size_t)b * a.hq + h * a.g_heads + idx / kHeadDim;
         // no cache token: the window's result as it is (0 and -inf for an empty window too)
@@ -1232,6 +1234,7 @@ __device__ __forceinline__ void run_item(const SplitArgs& a, const int b, const 
 
   // ---------------- work-group merge of the 4 waves -> this range's (O, lse)
   const int ns = (T + a.chunk - 1) / a.chunk;  // ranges holding tokens of this sequence
+  const bool direct = ns == 1 && !a.win_fused;  // the only partial: write the final output
   for (int idx = (int)tid; idx < 4 * D; idx += blockDim.x) {
     const int i = idx / D, c = idx % D;
     if (i >= a.g_heads) continue;
@@ -1248,7 +1251,7 @@ __device__ __forceinline__ void run_item(const SplitArgs& a, const int b, const 
     }
     const size_t row = (size_t)b * a.hq + h * a.g_heads + i;
     const float o = num / den, l_nat = (M + __log2f(den)) * kLn2;
-    if (ns == 1) {  // the only range: final output
+    if (direct) {  // the only range: final output
       float of = o, lf = l_nat;
       if (a.win_o) {  // merged with the full-precision window's partial
         const float wl = a.win_lse[row];
@@ -1265,7 +1268,7 @@ __device__ __forceinline__ void run_item(const SplitArgs& a, const int b, const 
         __hip_atomic_store(a.lse_part + row * a.splits + split, l_nat, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   }
-  if (ns == 1) {
+  if (direct) {
     if (next && wave == 0) map_select<UNIT>(a, nx, next);
     return;
   }
@@ -1283,11 +1286,151 @@ __device__ __forceinline__ void run_item(const SplitArgs& a, const int b, const 
   int done = 0;
   if (tid == 0) done = __hip_atomic_fetch_add(a.counters + bh, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   if (next && wave == 0) map_select<UNIT>(a, nx, next);  // while the count is in flight
-  if (tid == 0) s_last = (done == ns - 1);
+  if (tid == 0) s_last = (done == ns - 1 + a.win_fused);  // a fused window arrives like a range
   __syncthreads();
   if (!s_last) return;
   merge_ranges(a, b, h, ns);
   if (tid == 0) a.counters[bh] = 0;  // ready for the next call on this workspace
+}
+
+// A full-precision window of recent tokens attended by one more work-group of
+// the pair (grid row y = 0, dispatched first), concurrently with the pair's
+// cache ranges (rows 1 .. splits; the plan leaves one slot per pair for it):
+// the window's keys and values are further tokens of the same softmax.  The
+// work-group writes the window's normalised partial and lse to the window slot
+// with device-coherent stores and arrives at the pair's counter like a range;
+// the last arrival merges (merge_ranges folds the slot in).  A sequence with no
+// cache token has no range arriving: the window's result is its output.
+// Scores come from bf16 x bf16 products in fp32.  LDS: the query rows, the
+// score table and the waves' partial sums reuse the tile rings.
+__device__ __forceinline__ float wg_reduce(float v, float* red, bool is_max) {
+  for (int m = 32; m >= 1; m >>= 1) {
+    const float o = __shfl_xor(v, m);
+    v = is_max ? fmaxf(v, o) : v + o;
+  }
+  __syncthreads();  // red is free
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  float r = red[0];
+#pragma unroll
+  for (int w = 1; w < kWaves; ++w) r = is_max ? fmaxf(r, red[w]) : r + red[w];
+  return r;
+}
+
+__device__ __forceinline__ void window_item(const SplitArgs& a, const int b, const int h, const int T) {
+  constexpr int D = kHeadDim;
+  extern __shared__ __align__(16) unsigned char smem[];
+  __shared__ float s_wred[kWaves];
+  float* s_qf = reinterpret_cast<float*>(smem);  // [kMaxG][D]
+  float* s_p = s_qf + kMaxG * D;                 // [kMaxG][win_cap]
+  float* s_ow = s_p + kMaxG * a.win_cap;         // [kWaves][kMaxG][D]
+  const int G = a.g_heads;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int W = min(max(a.win_lens[b], 0), a.win_cap);
+  const int chunk = (W + kWaves - 1) / kWaves;
+  const int t0 = wave * chunk, t1 = min(t0 + chunk, W);
+  const size_t row0 = (size_t)b * a.hq + (size_t)h * G;
+  const size_t bh = (size_t)b * a.hkv + h;
+  for (int idx = tid; idx < kMaxG * D; idx += kWaves * 64) {
+    const int i = idx / D, c = idx % D;
+    s_qf[idx] = (i < G) ? __uint_as_float((uint32_t)a.q[(row0 + i) * D + c] << 16) : 0.f;
+  }
+  __syncthreads();
+  const size_t kv0 = bh * (size_t)a.win_cap * D;
+  const uint4* wk = reinterpret_cast<const uint4*>(a.win_k + kv0);
+  for (int t = t0 + lane; t < t1; t += 64) {
+    float acc[kMaxG] = {0.f, 0.f, 0.f, 0.f};
+    const uint4* kr = wk + (size_t)t * (D / 8);
+#pragma unroll 2
+    for (int k = 0; k < D / 8; ++k) {
+      const uint4 w = kr[k];
+      const float x[8] = {__uint_as_float(w.x << 16), __uint_as_float(w.x & 0xFFFF0000u),
+                          __uint_as_float(w.y << 16), __uint_as_float(w.y & 0xFFFF0000u),
+                          __uint_as_float(w.z << 16), __uint_as_float(w.z & 0xFFFF0000u),
+                          __uint_as_float(w.w << 16), __uint_as_float(w.w & 0xFFFF0000u)};
+#pragma unroll
+      for (int i = 0; i < kMaxG; ++i) {
+        const float4 qa = *reinterpret_cast<const float4*>(s_qf + i * D + 8 * k);
+        const float4 qb = *reinterpret_cast<const float4*>(s_qf + i * D + 8 * k + 4);
+        float v = acc[i];
+        v = fmaf(qa.x, x[0], v); v = fmaf(qa.y, x[1], v); v = fmaf(qa.z, x[2], v); v = fmaf(qa.w, x[3], v);
+        v = fmaf(qb.x, x[4], v); v = fmaf(qb.y, x[5], v); v = fmaf(qb.z, x[6], v); v = fmaf(qb.w, x[7], v);
+        acc[i] = v;
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < kMaxG; ++i) s_p[i * a.win_cap + t] = acc[i] * a.win_sm;
+  }
+  __syncthreads();
+  float m[kMaxG], l[kMaxG];
+#pragma unroll
+  for (int i = 0; i < kMaxG; ++i) {
+    float v = -INFINITY;
+    for (int t = tid; t < W; t += kWaves * 64) v = fmaxf(v, s_p[i * a.win_cap + t]);
+    m[i] = wg_reduce(v, s_wred, true);
+    float sum = 0.f;
+    for (int t = tid; t < W; t += kWaves * 64) {
+      const float p = __expf(s_p[i * a.win_cap + t] - m[i]);
+      s_p[i * a.win_cap + t] = p;
+      sum += p;
+    }
+    l[i] = wg_reduce(sum, s_wred, false);
+  }
+  __syncthreads();
+  const uint32_t* wv = reinterpret_cast<const uint32_t*>(a.win_v + kv0) + lane;
+  float o[kMaxG][2] = {{0.f, 0.f}, {0.f, 0.f}, {0.f, 0.f}, {0.f, 0.f}};
+  for (int tb = t0; tb < t1; tb += 16) {
+    uint32_t vr[16];
+#pragma unroll
+    for (int u = 0; u < 16; ++u) vr[u] = (tb + u < t1) ? wv[(size_t)(tb + u) * (D / 2)] : 0u;
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      if (tb + u >= t1) break;
+      const float v0 = __uint_as_float(vr[u] << 16), v1 = __uint_as_float(vr[u] & 0xFFFF0000u);
+#pragma unroll
+      for (int i = 0; i < kMaxG; ++i) {
+        const float p = s_p[i * a.win_cap + tb + u];
+        o[i][0] = fmaf(p, v0, o[i][0]);
+        o[i][1] = fmaf(p, v1, o[i][1]);
+      }
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < kMaxG; ++i) {
+    s_ow[(wave * kMaxG + i) * D + 2 * lane] = o[i][0];
+    s_ow[(wave * kMaxG + i) * D + 2 * lane + 1] = o[i][1];
+  }
+  __syncthreads();
+  for (int idx = tid; idx < G * D; idx += kWaves * 64) {
+    const int i = idx / D, c = idx % D;
+    float sum = 0.f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) sum += s_ow[(w * kMaxG + i) * D + c];
+    const float li = (i == 0) ? l[0] : (i == 1) ? l[1] : (i == 2) ? l[2] : l[3];
+    const float mi = (i == 0) ? m[0] : (i == 1) ? m[1] : (i == 2) ? m[2] : m[3];
+    const float ow = (W == 0) ? 0.f : sum / li, lw = (W == 0) ? -INFINITY : mi + __logf(li);
+    const size_t row = row0 + i;
+    if (T == 0) {  // no cache range: the window's result is the output
+      a.out[row * D + c] = to_bf16_rne(ow);
+      if (c == 0 && a.lse) a.lse[row] = lw;
+    } else {
+      __hip_atomic_store(a.win_o + row * D + c, ow, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (c == 0) __hip_atomic_store(a.win_lse + row, lw, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+  if (T == 0) return;
+  const int ns = (T + a.chunk - 1) / a.chunk;
+  __shared__ int s_wlast;
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  if (tid == 0) {
+    const int done = __hip_atomic_fetch_add(a.counters + bh, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    s_wlast = (done == ns);  // ns ranges and this work-group arrive
+  }
+  __syncthreads();
+  if (!s_wlast) return;
+  merge_ranges(a, b, h, ns);
+  if (tid == 0) a.counters[bh] = 0;
 }
 
 // Grids that fit the device in one round: the grid's own map (x = (sequence,
@@ -1301,7 +1444,12 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(wav
 void split_decode(const SplitArgs a) {
   if (!a.persistent) {
     const int b = blockIdx.x / a.hkv;
-    run_item<BITS, KCH, VCH, GRP>(a, b, blockIdx.x % a.hkv, blockIdx.y, min(max(a.seq_lens[b], 0), a.tcap), nullptr);
+    const int T = min(max(a.seq_lens[b], 0), a.tcap);
+    if (a.win_fused && blockIdx.y == 0) {  // dispatched first: runs beside the ranges, not after them
+      window_item(a, b, blockIdx.x % a.hkv, T);
+      return;
+    }
+    run_item<BITS, KCH, VCH, GRP>(a, b, blockIdx.x % a.hkv, (int)blockIdx.y - a.win_fused, T, nullptr);
     return;
   }
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -1354,7 +1502,9 @@ hipError_t launch_one(int batch, int hkv, const SplitArgs& sa, hipStream_t strea
   if (!lds_ok) return hipErrorInvalidConfiguration;
   if (per_cu)
     return hipOccupancyMaxActiveBlocksPerMultiprocessor(per_cu, split_decode<BITS, KCH, VCH, GRP>, kWaves * 64, lds);
-  const dim3 grid = sa.persistent ? dim3(sa.grid_wgs) : dim3(batch * hkv, sa.splits);
+  static_assert(lds >= sizeof(float) * (kMaxG * kHeadDim * (1 + kWaves) + kMaxG * kFusedWindowMax),
+                "rings must hold a fused window's query rows, scores and partial sums");
+  const dim3 grid = sa.persistent ? dim3(sa.grid_wgs) : dim3(batch * hkv, sa.splits + (sa.win_fused ? 1 : 0));
   if (ev.start || ev.stop)  // timing events recorded by the dispatch itself
     hipExtLaunchKernelGGL((split_decode<BITS, KCH, VCH, GRP>), grid, dim3(kWaves * 64), lds, stream, ev.start, ev.stop,
                           0, sa);

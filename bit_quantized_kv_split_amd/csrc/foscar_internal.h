@@ -38,9 +38,17 @@ struct SplitArgs {
   int32_t grid_wgs;          // persistent grid size (one round of resident work-groups)
   int32_t batch;             // B
   int32_t* work_ctr;         // [2] items taken, work-groups left; zero between calls
-  const float* win_o;        // fp32 [B][Hq][D] normalised output over a full-precision window, or null
-  const float* win_lse;      // fp32 [B][Hq] its natural-log lse (-inf: empty window)
+  float* win_o;              // fp32 [B][Hq][D] normalised output over a full-precision window, or null
+  float* win_lse;            // fp32 [B][Hq] its natural-log lse (-inf: empty window)
+  // window attended inside this launch (one more work-group per pair, grid row y = 0; ranges in rows 1 .. splits)
+  int32_t win_fused;
+  const uint16_t* win_k;     // bf16 [B][Hkv][win_cap][D]
+  const uint16_t* win_v;
+  const int32_t* win_lens;   // [B]
+  int32_t win_cap;           // <= kFusedWindowMax
+  float win_sm;              // softmax scale (natural units)
 };
+constexpr int kFusedWindowMax = 512;  // largest window attended inside the decode launch
 
 // Attention over a full-precision (bf16) window of recent tokens (window.hip):
 // per (sequence, KV head) the window's normalised output and lse, merged into

@@ -69,10 +69,12 @@ def test_window_matrix(bits, kl, vl, g):
     check(out, lse, ro, rl, spec.name, vsc)
 
 
-@pytest.mark.parametrize("name,cap", [("c3_long_int2", 1024), ("c5_ragged_int2_g64", 4096)])
+@pytest.mark.parametrize("name,cap", [("c3_long_int2", 300), ("c3_long_int2", 512), ("c3_long_int2", 1024),
+                                      ("c5_ragged_int2_g64", 512), ("c5_ragged_int2_g64", 4096)])
 def test_window_multi_range_and_persistent(name, cap):
-    """Many ranges per sequence (merge path) and the persistent work order
-    (ragged batch), with windows up to the largest supported."""
+    """Many ranges per sequence (merge path) with the window attended inside the
+    decode launch (up to 512 tokens) or by its own kernel (larger windows), and
+    the persistent work order (ragged batch, always its own kernel)."""
     base = synth.SPECS[name]
     spec = base.replace(batch=1, num_q_heads=4, num_kv_heads=1, max_seq_len=16384) if "long" in name else \
         base.replace(batch=6, num_q_heads=8, num_kv_heads=2, max_seq_len=4096, ragged_lo=64)
