@@ -129,3 +129,48 @@ def test_plan_and_reserve_reject_bad_bits(lib):
     with pytest.raises(ValueError):
         fos.foscar_split_plan(_dims(), 3, 0, 128)
     assert lib.foscar_workspace_reserve(ctypes.byref(_dims()), 8, 0, 128, None) == -1
+
+
+def _quantize(lib, dims, layout=0, group=128, src_tokens=16, ptr=1, bits=2):
+    p = ctypes.c_void_p(ptr) if ptr else None
+    fn = lib.foscar_quantize_int2 if bits == 2 else lib.foscar_quantize_int4
+    return fn(ctypes.byref(dims) if dims is not None else None, p, p, src_tokens, p, p, layout, group,
+              p, p, p, p, p, p, None)
+
+
+@pytest.mark.parametrize("kw,layout,group,src,code", [
+    (dict(head_dim=64), 0, 128, 16, -2),
+    (dict(max_seq_len=1000), 0, 128, 16, -2),                 # not a multiple of 64
+    (dict(max_seq_len=192), 1, 128, 16, -2),                  # channel-wise group of 128 does not divide 192
+    (dict(batch=70000), 0, 128, 16, -2),                      # grid z
+    (dict(), 5, 128, 16, -1),                                 # bad layout bits
+    (dict(), 0, 16, 16, -2),                                  # bad group
+    (dict(), 0, 128, -1, -1),                                 # negative source length
+])
+def test_quantize_rejects_bad_arguments_before_any_gpu_call(lib, kw, layout, group, src, code):
+    assert _quantize(lib, _dims(**kw), layout, group, src) == code
+    assert _quantize(lib, _dims(**kw), layout, group, src, bits=4) == code
+
+
+def test_quantize_null_pointers_and_empty_calls(lib):
+    assert _quantize(lib, None) == -1
+    assert _quantize(lib, _dims(), ptr=0) == -1
+    assert _quantize(lib, _dims(batch=0), ptr=0) == 0     # nothing to do
+    assert _quantize(lib, _dims(), src_tokens=0, ptr=0) == 0
+
+
+def _decode_window(lib, dims, win_cap=128, ptr=1, win_ptr=1, layout=0, group=128):
+    p = ctypes.c_void_p(ptr) if ptr else None
+    w = ctypes.c_void_p(win_ptr) if win_ptr else None
+    return lib.foscar_decode_window_int2(ctypes.byref(dims) if dims is not None else None, p, p, p, p, p, p, p, p,
+                                         layout, group, w, w, w, win_cap, p, p, None)
+
+
+def test_decode_window_rejects_bad_arguments_before_any_gpu_call(lib):
+    assert _decode_window(lib, _dims(), win_cap=-1) == -1
+    assert _decode_window(lib, _dims(), win_cap=4097) == -2          # largest window: 4096 tokens
+    assert _decode_window(lib, _dims(), win_ptr=0) == -1             # window pointers missing
+    assert _decode_window(lib, _dims(head_dim=64)) == -2
+    assert _decode_window(lib, _dims(), layout=4) == -1
+    assert _decode_window(lib, None) == -1
+    assert _decode_window(lib, _dims(batch=0), ptr=0, win_ptr=0) == 0
