@@ -40,6 +40,10 @@ int hip_fail(hipError_t e) {
 
 bool valid_group(int g) { return g == 32 || g == 64 || g == 128; }
 
+// The kernels move packed words, scales and bf16 rows 16 bytes at a time and
+// read the query, lengths and outputs 4 bytes at a time.
+bool aligned(const void* p, uintptr_t n) { return ((uintptr_t)p % n) == 0; }
+
 // Shape checks shared by every entry point that takes dims.
 int check_dims(const foscar_dims* d, bool need_heads_ratio) {
   if (!d) return FOSCAR_EINVAL;
@@ -201,6 +205,10 @@ int decode_common(int bits, const foscar_dims* d, const void* q, const void* pk,
   if (!q || !pk || !pv || !ks || !kz || !vs || !vz || !seq_lens || !out) return FOSCAR_EINVAL;
   if (windowed && win_cap > 0 && (!win_k || !win_v || !win_lens)) return FOSCAR_EINVAL;
   if (windowed && !win_lens) return FOSCAR_EINVAL;
+  if (!aligned(pk, 16) || !aligned(pv, 16) || !aligned(ks, 16) || !aligned(kz, 16) || !aligned(vs, 16) ||
+      !aligned(vz, 16) || !aligned(q, 4) || !aligned(seq_lens, 4) || !aligned(out, 4) || !aligned(lse, 4))
+    return FOSCAR_EINVAL;
+  if (windowed && (!aligned(win_k, 16) || !aligned(win_v, 16) || !aligned(win_lens, 4))) return FOSCAR_EINVAL;
 
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
@@ -303,6 +311,9 @@ int quantize_common(int bits, const foscar_dims* d, const void* k_src, const voi
   if (d->batch > 65535 || d->num_kv_heads > 65535) return FOSCAR_EUNSUPPORTED;  // grid z / y
   if (d->batch == 0 || src_tokens == 0) return FOSCAR_OK;
   if (!k_src || !v_src || !start || !count || !pk || !pv || !ks || !kz || !vs || !vz) return FOSCAR_EINVAL;
+  if (!aligned(k_src, 16) || !aligned(v_src, 16) || !aligned(pk, 16) || !aligned(pv, 16) || !aligned(ks, 16) ||
+      !aligned(kz, 16) || !aligned(vs, 16) || !aligned(vz, 16) || !aligned(start, 4) || !aligned(count, 4))
+    return FOSCAR_EINVAL;
   const hipError_t e = foscar::launch_quantize(bits, (layout & FOSCAR_K_CHANNEL) != 0, (layout & FOSCAR_V_CHANNEL) != 0,
                                                group, d->batch, d->num_kv_heads, d->max_seq_len, src_tokens, k_src,
                                                v_src, start, count, pk, pv, ks, kz, vs, vz, (hipStream_t)stream);

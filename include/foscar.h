@@ -25,6 +25,9 @@
  * Conventions for every entry point:
  *   - all tensor pointers are DEVICE memory owned by the caller; inputs are
  *     only read; the library never frees or keeps them;
+ *   - packed codes, scales, offsets, bf16 key/value sources and windows must
+ *     be 16-byte aligned, every other tensor 4-byte aligned (FOSCAR_EINVAL
+ *     otherwise); fresh allocations are;
  *   - `stream` is a hipStream_t (NULL = the null stream of the current
  *     device); calls are asynchronous on it: no host synchronisation and no
  *     host read of device data; buffers must stay alive until the stream has
@@ -48,7 +51,8 @@ extern "C" {
 
 /* Return codes. */
 #define FOSCAR_OK 0
-#define FOSCAR_EINVAL (-1)       /* null pointer, negative size, bad layout/side/bits value, Hq % Hkv != 0 */
+#define FOSCAR_EINVAL (-1)       /* null or misaligned pointer, negative size, bad layout/side/bits value,
+                                    Hq % Hkv != 0 */
 #define FOSCAR_EUNSUPPORTED (-2) /* head_dim != 128, group not in {32,64,128}, Hq/Hkv > 4,
                                     max_seq_len not a multiple of 64 (and of group for a
                                     channel-wise side), max_seq_len > 2^24,

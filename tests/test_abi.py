@@ -174,3 +174,16 @@ def test_decode_window_rejects_bad_arguments_before_any_gpu_call(lib):
     assert _decode_window(lib, _dims(), layout=4) == -1
     assert _decode_window(lib, None) == -1
     assert _decode_window(lib, _dims(batch=0), ptr=0, win_ptr=0) == 0
+
+
+def test_misaligned_pointers_are_rejected_before_any_gpu_call(lib):
+    """16-byte loads and stores need 16-byte aligned packed arrays, scales and
+    sources: a misaligned pointer is an argument error, never a launch.  The
+    pointers are not real allocations, so this runs only where no GPU is
+    visible (a broken check must not be able to launch on them)."""
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("host-only check: the pointers are fabricated")
+    assert _decode(lib, _dims(), ptr=0x1008) == -1          # 8-byte aligned only
+    assert _quantize(lib, _dims(), ptr=0x1004) == -1
+    assert _decode_window(lib, _dims(), ptr=0x1000, win_ptr=0x1002) == -1
