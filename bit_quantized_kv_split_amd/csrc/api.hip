@@ -141,8 +141,8 @@ void plan(const foscar_dims* d, int layout, int group, int cus, int per_cu, int3
 size_t counter_bytes(const foscar_dims* d) {  // B*Hkv range counters, then the 2 work counters
   return (((size_t)d->batch * d->num_kv_heads + 2) * sizeof(int32_t) + 255) / 256 * 256;
 }
-size_t partial_bytes(const foscar_dims* d, int32_t splits) {  // range partials, then one window partial per row
-  const size_t rows = (size_t)d->batch * d->num_q_heads * (splits + 1);
+size_t partial_bytes(const foscar_dims* d, int32_t splits) {  // range partials, then the window partials of each row
+  const size_t rows = (size_t)d->batch * d->num_q_heads * (splits + foscar::kMaxWindowWgs);
   return rows * (foscar::kHeadDim + 1) * sizeof(float);
 }
 
@@ -220,8 +220,13 @@ int decode_common(int bits, const foscar_dims* d, const void* q, const void* pk,
   // per pair, so the ranges are planned for one slot fewer per pair
   const bool one_round = (long long)splits * d->batch * d->num_kv_heads <= (long long)cus * per_cu ||
                          d->batch > foscar::kMapMaxB;
-  const bool fuse_window = windowed && win_cap <= foscar::kFusedWindowMax && one_round;
-  if (fuse_window) plan(d, layout, group, cus, per_cu, &splits, &chunk, 1);
+  const bool fuse_window = windowed && one_round;
+  // window work-groups per pair: 1, 2, 4 or 8, chunks of at most 128 tokens where 8 allow it
+  // (chunks of at most 4096 / 8 = 512 = kFusedWindowMax tokens)
+  int win_wgs = 1;
+  while (win_wgs < foscar::kMaxWindowWgs && win_wgs * 128 < win_cap) win_wgs *= 2;
+  const int win_chunk = (win_cap + win_wgs - 1) / win_wgs;
+  if (fuse_window) plan(d, layout, group, cus, per_cu, &splits, &chunk, win_wgs);
   int32_t* counters = nullptr;
   float* partials = nullptr;
   rc = get_workspace(counter_bytes(d), partial_bytes(d, splits), (hipStream_t)stream, &counters, &partials);
@@ -257,17 +262,21 @@ int decode_common(int bits, const foscar_dims* d, const void* q, const void* pk,
   sa.work_ctr = counters + (size_t)d->batch * d->num_kv_heads;
   sa.win_o = nullptr;
   sa.win_lse = nullptr;
-  sa.win_fused = 0;
+  sa.win_slots = 0;
+  sa.win_wgs = 0;
+  sa.win_chunk = 0;
   sa.win_k = sa.win_v = nullptr;
   sa.win_lens = nullptr;
   sa.win_cap = 0;
   sa.win_sm = sm;
   if (fuse_window && !sa.persistent) {
-    // attended inside the decode launch by one more work-group per pair, concurrently with the ranges
+    // attended inside the decode launch by win_wgs more work-groups per pair, beside the ranges
     const size_t rows = (size_t)d->batch * d->num_q_heads;
     sa.win_o = sa.lse_part + rows * splits;
-    sa.win_lse = sa.win_o + rows * foscar::kHeadDim;
-    sa.win_fused = 1;
+    sa.win_lse = sa.win_o + rows * win_wgs * foscar::kHeadDim;
+    sa.win_slots = win_wgs;
+    sa.win_wgs = win_wgs;
+    sa.win_chunk = win_chunk;
     sa.win_k = (const uint16_t*)win_k;
     sa.win_v = (const uint16_t*)win_v;
     sa.win_lens = win_lens;
@@ -291,6 +300,7 @@ int decode_common(int bits, const foscar_dims* d, const void* q, const void* pk,
     if (e != hipSuccess) return hip_fail(e);
     sa.win_o = wa.o;
     sa.win_lse = wa.lse;
+    sa.win_slots = 1;
   }
 
   e = foscar::launch_decode(bits, (layout & FOSCAR_K_CHANNEL) != 0, (layout & FOSCAR_V_CHANNEL) != 0, group,

@@ -367,6 +367,38 @@ __device__ __forceinline__ float coherent_load(const float* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// Fold the S window partials of rows row0 and row1 (channel c) into a running
+// log-sum-exp merge (max m, weighted sum n, weight sum d).  Device-coherent
+// loads (in a fused launch other work-groups wrote the slots), all issued
+// before any is used.  An empty term (lse -inf) adds nothing, and a running
+// max of -inf has nothing to rescale.
+template <int S>
+__device__ __forceinline__ void fold_window_slots(const SplitArgs& a, size_t row0, size_t row1, int c, float& m0,
+                                                  float& n0, float& d0, float& m1, float& n1, float& d1) {
+  constexpr int D = kHeadDim;
+  float wl0[S], wl1[S], wo0[S], wo1[S];
+#pragma unroll
+  for (int j = 0; j < S; ++j) {
+    wl0[j] = coherent_load(a.win_lse + row0 * S + j);
+    wl1[j] = coherent_load(a.win_lse + row1 * S + j);
+    wo0[j] = coherent_load(a.win_o + (row0 * S + j) * D + c);
+    wo1[j] = coherent_load(a.win_o + (row1 * S + j) * D + c);
+  }
+#pragma unroll
+  for (int j = 0; j < S; ++j) {
+    const float b0 = fmaxf(m0, wl0[j]), b1 = fmaxf(m1, wl1[j]);
+    const float r0 = (b0 == -INFINITY) ? 1.f : __expf(m0 - b0), r1 = (b1 == -INFINITY) ? 1.f : __expf(m1 - b1);
+    const float w0 = (wl0[j] == -INFINITY) ? 0.f : __expf(wl0[j] - b0);
+    const float w1 = (wl1[j] == -INFINITY) ? 0.f : __expf(wl1[j] - b1);
+    n0 = fmaf(w0, wo0[j], n0 * r0);
+    d0 = fmaf(d0, r0, w0);
+    n1 = fmaf(w1, wo1[j], n1 * r1);
+    d1 = fmaf(d1, r1, w1);
+    m0 = b0;
+    m1 = b1;
+  }
+}
+
 // Log-sum-exp merge of the ns ranges of one (sequence, KV head), run by the
 // work-group that finished last: O = sum_s exp(lse_s - M) O_s / sum_s exp(lse_s - M),
 // lse = M + log(sum_s exp(lse_s - M)).  The partials were written by other
@@ -434,18 +466,23 @@ __device__ __forceinline__ void merge_ranges(const SplitArgs& a, int b, int h, i
     m0 = b0;
     m1 = b1;
   }
-  if (a.win_o) {  // the full-precision window's partial is one more term of the same merge
-    // device-coherent loads: in a fused launch another work-group wrote the slot
-    const float wl0 = coherent_load(a.win_lse + row0), wl1 = coherent_load(a.win_lse + row1);
-    const float wo0 = coherent_load(a.win_o + row0 * D + c), wo1 = coherent_load(a.win_o + row1 * D + c);
-    const float b0 = fmaxf(m0, wl0), b1 = fmaxf(m1, wl1);  // m0, m1 finite: the cache has tokens
-    const float r0 = __expf(m0 - b0), r1 = __expf(m1 - b1), w0 = __expf(wl0 - b0), w1 = __expf(wl1 - b1);
-    n0 = fmaf(w0, wo0, n0 * r0);
-    d0 = fmaf(d0, r0, w0);
-    n1 = fmaf(w1, wo1, n1 * r1);
-    d1 = fmaf(d1, r1, w1);
-    m0 = b0;
-    m1 = b1;
+  // the full-precision window's partials are further terms of the same merge (1, 2, 4 or 8 slots)
+  switch (a.win_slots) {
+    case 1: fold_window_slots<1>(a, row0, row1, c, m0, n0, d0, m1, n1, d1); break;
+    case 2: fold_window_slots<2>(a, row0, row1, c, m0, n0, d0, m1, n1, d1); break;
+    case 4: fold_window_slots<4>(a, row0, row1, c, m0, n0, d0, m1, n1, d1); break;
+    case 8: fold_window_slots<8>(a, row0, row1, c, m0, n0, d0, m1, n1, d1); break;
+    default: break;
+  }
+  if (!(d0 > 0.f)) {  // no token at all (no cache range and empty window slots)
+    n0 = 0.f;
+    d0 = 1.f;
+    m0 = -INFINITY;
+  }
+  if (!(d1 > 0.f)) {
+    n1 = 0.f;
+    d1 = 1.f;
+    m1 = -INFINITY;
   }
   a.out[row0 * D + c] = to_bf16_rne(n0 / d0);
   if (c == 0 && a.lse) a.lse[row0] = m0 + __logf(d0);
@@ -611,7 +648,7 @@ __device__ __forceinline__ void run_item(const SplitArgs& a, const int b, const 
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r0 = split * a.chunk;
   if (r0 >= T) {  // no token in this range; an empty sequence's rows are written once
-    if (T == 0 && split == 0 && !a.win_fused) {  // (a fused window's work-group writes them itself)
+    if (T == 0 && split == 0 && !a.win_wgs) {  // (fused window work-groups write them themselves)
       for (int idx = (int)tid; idx < a.g_heads * kHeadDim; idx += blockDim.x) {
         const size_t row = (size_t)b * a.hq + h * a.g_heads + idx / kHeadDim;
         // no cache token: the window's result as it is (0 and -inf for an empty window too)
@@ -1234,7 +1271,7 @@ __device__ __forceinline__ void run_item(const SplitArgs& a, const int b, const 
 
   // ---------------- work-group merge of the 4 waves -> this range's (O, lse)
   const int ns = (T + a.chunk - 1) / a.chunk;  // ranges holding tokens of this sequence
-  const bool direct = ns == 1 && !a.win_fused;  // the only partial: write the final output
+  const bool direct = ns == 1 && !a.win_wgs;  // the only range partial: write the final output
   for (int idx = (int)tid; idx < 4 * D; idx += blockDim.x) {
     const int i = idx / D, c = idx % D;
     if (i >= a.g_heads) continue;
@@ -1286,21 +1323,22 @@ __device__ __forceinline__ void run_item(const SplitArgs& a, const int b, const 
   int done = 0;
   if (tid == 0) done = __hip_atomic_fetch_add(a.counters + bh, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   if (next && wave == 0) map_select<UNIT>(a, nx, next);  // while the count is in flight
-  if (tid == 0) s_last = (done == ns - 1 + a.win_fused);  // a fused window arrives like a range
+  if (tid == 0) s_last = (done == ns - 1 + a.win_wgs);  // fused window work-groups arrive like ranges
   __syncthreads();
   if (!s_last) return;
   merge_ranges(a, b, h, ns);
   if (tid == 0) a.counters[bh] = 0;  // ready for the next call on this workspace
 }
 
-// A full-precision window of recent tokens attended by one more work-group of
-// the pair (grid row y = 0, dispatched first), concurrently with the pair's
-// cache ranges (rows 1 .. splits; the plan leaves one slot per pair for it):
+// A full-precision window of recent tokens attended by S more work-groups of
+// the pair (grid rows 0 .. S-1, dispatched first, work-group j taking window
+// tokens [j * chunk, +chunk)), concurrently with the pair's cache ranges (the
+// rows after them; the plan leaves S slots per pair for them):
 // the window's keys and values are further tokens of the same softmax.  The
-// work-group writes the window's normalised partial and lse to the window slot
-// with device-coherent stores and arrives at the pair's counter like a range;
-// the last arrival merges (merge_ranges folds the slot in).  A sequence with no
-// cache token has no range arriving: the window's result is its output.
+// work-group writes its normalised partial and lse to its window slot with
+// device-coherent stores and arrives at the pair's counter like a range; the
+// last arrival merges (merge_ranges folds the slots in).  A sequence with no
+// cache token and a single window work-group takes that partial as output.
 // Scores come from bf16 x bf16 products in fp32.  LDS: the query rows, the
 // score table and the waves' partial sums reuse the tile rings.
 __device__ __forceinline__ float wg_reduce(float v, float* red, bool is_max) {
@@ -1317,16 +1355,19 @@ __device__ __forceinline__ float wg_reduce(float v, float* red, bool is_max) {
   return r;
 }
 
-__device__ __forceinline__ void window_item(const SplitArgs& a, const int b, const int h, const int T) {
+__device__ __forceinline__ void window_item(const SplitArgs& a, const int b, const int h, const int T, const int j) {
   constexpr int D = kHeadDim;
   extern __shared__ __align__(16) unsigned char smem[];
   __shared__ float s_wred[kWaves];
+  const int CW = a.win_chunk;                    // window tokens of one work-group
   float* s_qf = reinterpret_cast<float*>(smem);  // [kMaxG][D]
-  float* s_p = s_qf + kMaxG * D;                 // [kMaxG][win_cap]
-  float* s_ow = s_p + kMaxG * a.win_cap;         // [kWaves][kMaxG][D]
+  float* s_p = s_qf + kMaxG * D;                 // [kMaxG][CW]
+  float* s_ow = s_p + kMaxG * CW;                // [kWaves][kMaxG][D]
   const int G = a.g_heads;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int W = min(max(a.win_lens[b], 0), a.win_cap);
+  const int S = a.win_wgs;
+  // this work-group's window tokens: [j * CW, j * CW + W)
+  const int W = min(max(min(max(a.win_lens[b], 0), a.win_cap) - j * CW, 0), CW);
   const int chunk = (W + kWaves - 1) / kWaves;
   const int t0 = wave * chunk, t1 = min(t0 + chunk, W);
   const size_t row0 = (size_t)b * a.hq + (size_t)h * G;
@@ -1336,7 +1377,7 @@ __device__ __forceinline__ void window_item(const SplitArgs& a, const int b, con
     s_qf[idx] = (i < G) ? __uint_as_float((uint32_t)a.q[(row0 + i) * D + c] << 16) : 0.f;
   }
   __syncthreads();
-  const size_t kv0 = bh * (size_t)a.win_cap * D;
+  const size_t kv0 = (bh * (size_t)a.win_cap + (size_t)j * CW) * D;
   const uint4* wk = reinterpret_cast<const uint4*>(a.win_k + kv0);
   for (int t = t0 + lane; t < t1; t += 64) {
     float acc[kMaxG] = {0.f, 0.f, 0.f, 0.f};
@@ -1359,19 +1400,19 @@ __device__ __forceinline__ void window_item(const SplitArgs& a, const int b, con
       }
     }
 #pragma unroll
-    for (int i = 0; i < kMaxG; ++i) s_p[i * a.win_cap + t] = acc[i] * a.win_sm;
+    for (int i = 0; i < kMaxG; ++i) s_p[i * CW + t] = acc[i] * a.win_sm;
   }
   __syncthreads();
   float m[kMaxG], l[kMaxG];
 #pragma unroll
   for (int i = 0; i < kMaxG; ++i) {
     float v = -INFINITY;
-    for (int t = tid; t < W; t += kWaves * 64) v = fmaxf(v, s_p[i * a.win_cap + t]);
+    for (int t = tid; t < W; t += kWaves * 64) v = fmaxf(v, s_p[i * CW + t]);
     m[i] = wg_reduce(v, s_wred, true);
     float sum = 0.f;
     for (int t = tid; t < W; t += kWaves * 64) {
-      const float p = __expf(s_p[i * a.win_cap + t] - m[i]);
-      s_p[i * a.win_cap + t] = p;
+      const float p = __expf(s_p[i * CW + t] - m[i]);
+      s_p[i * CW + t] = p;
       sum += p;
     }
     l[i] = wg_reduce(sum, s_wred, false);
@@ -1389,7 +1430,7 @@ __device__ __forceinline__ void window_item(const SplitArgs& a, const int b, con
       const float v0 = __uint_as_float(vr[u] << 16), v1 = __uint_as_float(vr[u] & 0xFFFF0000u);
 #pragma unroll
       for (int i = 0; i < kMaxG; ++i) {
-        const float p = s_p[i * a.win_cap + tb + u];
+        const float p = s_p[i * CW + tb + u];
         o[i][0] = fmaf(p, v0, o[i][0]);
         o[i][1] = fmaf(p, v1, o[i][1]);
       }
@@ -1410,22 +1451,22 @@ __device__ __forceinline__ void window_item(const SplitArgs& a, const int b, con
     const float mi = (i == 0) ? m[0] : (i == 1) ? m[1] : (i == 2) ? m[2] : m[3];
     const float ow = (W == 0) ? 0.f : sum / li, lw = (W == 0) ? -INFINITY : mi + __logf(li);
     const size_t row = row0 + i;
-    if (T == 0) {  // no cache range: the window's result is the output
+    if (T == 0 && S == 1) {  // no cache range and one window partial: it is the output
       a.out[row * D + c] = to_bf16_rne(ow);
       if (c == 0 && a.lse) a.lse[row] = lw;
     } else {
-      __hip_atomic_store(a.win_o + row * D + c, ow, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      if (c == 0) __hip_atomic_store(a.win_lse + row, lw, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(a.win_o + (row * S + j) * D + c, ow, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (c == 0) __hip_atomic_store(a.win_lse + row * S + j, lw, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   }
-  if (T == 0) return;
+  if (T == 0 && S == 1) return;
   const int ns = (T + a.chunk - 1) / a.chunk;
   __shared__ int s_wlast;
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
   if (tid == 0) {
     const int done = __hip_atomic_fetch_add(a.counters + bh, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    s_wlast = (done == ns);  // ns ranges and this work-group arrive
+    s_wlast = (done == ns + S - 1);  // ns ranges and S window work-groups arrive
   }
   __syncthreads();
   if (!s_wlast) return;
@@ -1445,11 +1486,11 @@ void split_decode(const SplitArgs a) {
   if (!a.persistent) {
     const int b = blockIdx.x / a.hkv;
     const int T = min(max(a.seq_lens[b], 0), a.tcap);
-    if (a.win_fused && blockIdx.y == 0) {  // dispatched first: runs beside the ranges, not after them
-      window_item(a, b, blockIdx.x % a.hkv, T);
+    if ((int)blockIdx.y < a.win_wgs) {  // dispatched first: run beside the ranges, not after them
+      window_item(a, b, blockIdx.x % a.hkv, T, blockIdx.y);
       return;
     }
-    run_item<BITS, KCH, VCH, GRP>(a, b, blockIdx.x % a.hkv, (int)blockIdx.y - a.win_fused, T, nullptr);
+    run_item<BITS, KCH, VCH, GRP>(a, b, blockIdx.x % a.hkv, (int)blockIdx.y - a.win_wgs, T, nullptr);
     return;
   }
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -1504,7 +1545,7 @@ hipError_t launch_one(int batch, int hkv, const SplitArgs& sa, hipStream_t strea
     return hipOccupancyMaxActiveBlocksPerMultiprocessor(per_cu, split_decode<BITS, KCH, VCH, GRP>, kWaves * 64, lds);
   static_assert(lds >= sizeof(float) * (kMaxG * kHeadDim * (1 + kWaves) + kMaxG * kFusedWindowMax),
                 "rings must hold a fused window's query rows, scores and partial sums");
-  const dim3 grid = sa.persistent ? dim3(sa.grid_wgs) : dim3(batch * hkv, sa.splits + (sa.win_fused ? 1 : 0));
+  const dim3 grid = sa.persistent ? dim3(sa.grid_wgs) : dim3(batch * hkv, sa.splits + sa.win_wgs);
   if (ev.start || ev.stop)  // timing events recorded by the dispatch itself
     hipExtLaunchKernelGGL((split_decode<BITS, KCH, VCH, GRP>), grid, dim3(kWaves * 64), lds, stream, ev.start, ev.stop,
                           0, sa);

@@ -38,17 +38,21 @@ struct SplitArgs {
   int32_t grid_wgs;          // persistent grid size (one round of resident work-groups)
   int32_t batch;             // B
   int32_t* work_ctr;         // [2] items taken, work-groups left; zero between calls
-  float* win_o;              // fp32 [B][Hq][D] normalised output over a full-precision window, or null
-  float* win_lse;            // fp32 [B][Hq] its natural-log lse (-inf: empty window)
-  // window attended inside this launch (one more work-group per pair, grid row y = 0; ranges in rows 1 .. splits)
-  int32_t win_fused;
+  float* win_o;              // fp32 [B][Hq][win_slots][D] normalised outputs over a full-precision window, or null
+  float* win_lse;            // fp32 [B][Hq][win_slots] their natural-log lse (-inf: no window token)
+  int32_t win_slots;         // window partials per row (0: no window)
+  // window attended inside this launch: win_wgs more work-groups per pair (grid rows 0 .. win_wgs-1,
+  // ranges in the rows after them), work-group j taking window tokens [j * win_chunk, +win_chunk)
+  int32_t win_wgs;
+  int32_t win_chunk;         // <= kFusedWindowMax
   const uint16_t* win_k;     // bf16 [B][Hkv][win_cap][D]
   const uint16_t* win_v;
   const int32_t* win_lens;   // [B]
-  int32_t win_cap;           // <= kFusedWindowMax
+  int32_t win_cap;
   float win_sm;              // softmax scale (natural units)
 };
-constexpr int kFusedWindowMax = 512;  // largest window attended inside the decode launch
+constexpr int kMaxWindowWgs = 8;      // window work-groups per pair inside the decode launch
+constexpr int kFusedWindowMax = 512;  // window tokens of one work-group inside the decode launch
 
 // Attention over a full-precision (bf16) window of recent tokens (window.hip):
 // per (sequence, KV head) the window's normalised output and lse, merged into
