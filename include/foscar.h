@@ -130,8 +130,10 @@ int foscar_decode_int4(const foscar_dims* dims, const void* q, const void* packe
  * recent tokens as part of the accuracy recipe a 2-bit cache needs.  The
  * window's tokens are further keys and values of the same softmax: out and lse
  * are those of attention over the T_b cache tokens and the window's tokens
- * together.  The window is attended by its own kernel, in fp32 from bf16, and
- * merged with the cache's ranges by log-sum-exp inside the decode kernel.
+ * together.  The window is attended in fp32 from bf16, by 1-8 extra
+ * work-groups per (sequence, KV head) of the decode launch when its grid runs
+ * in one round, else by a kernel of its own before it, and merged with the
+ * cache's ranges by log-sum-exp inside the decode kernel.
  *
  * Arguments as foscar_decode_int2/int4, plus:
  * win_k, win_v  bf16 [B][Hkv][win_cap][D]: window keys and values
