@@ -68,3 +68,22 @@ def test_outliers_and_channel_std():
     spec4 = synth.SPECS["c4_channel_int2"]
     std = synth._channel_std(spec4, 0, 0)
     assert std.min() >= 0.1 and std.max() <= 10.0
+
+
+def test_append_case_and_window_generators_are_seeded_and_shaped():
+    """The quantise-and-append and window inputs regenerate bit for bit from
+    their seed, hold bf16 values, and have the interface's shapes."""
+    a = synth.make_append_case(3, 2, 2, 256, 100, 2, [0, 64], [100, 10])
+    b = synth.make_append_case(3, 2, 2, 256, 100, 2, [0, 64], [100, 10])
+    for k in a:
+        assert np.array_equal(a[k], b[k]), k
+    assert a["k_src"].shape == (2, 2, 100, 128) and a["packed_k"].shape == (2, 2, 256, 8)
+    assert a["packed_v"].shape == (2, 2, 16, 128) and a["k_scale_channel"].shape == (2, 2, 8, 128)
+    assert np.array_equal(synth.bf16_round(a["k_src"]), a["k_src"])
+    c = synth.make_append_case(4, 2, 2, 256, 100, 2, [0, 64], [100, 10])
+    assert not np.array_equal(a["k_src"], c["k_src"])
+    w1 = synth.make_window(5, 3, 2, 40, [40, 0, 7])
+    w2 = synth.make_window(5, 3, 2, 40, [40, 0, 7])
+    assert all(np.array_equal(w1[k], w2[k]) for k in w1)
+    assert w1["k"].shape == (3, 2, 40, 128) and w1["lens"].dtype == np.int32
+    assert np.array_equal(synth.bf16_round(w1["v"]), w1["v"])
