@@ -123,6 +123,9 @@ void plan(const foscar_dims* d, int layout, int group, int cus, int per_cu, int3
     // one round of resident work-groups, less the pairs' other work-groups (a fused window)
     const long long target = (long long)per_cu * cus - bh * extra_per_pair;
     if (bh > 0) s = std::max(1LL, (target + bh - 1) / bh);
+    // but at least 8 tiles per wave: shorter ranges spend more on ramp-up, hand-off and merge
+    // than they gain in parallel work (16 x 8192 tokens, INT2: 4 ranges 20.0 us, 8 ranges 22.1)
+    s = std::min(s, std::max(1LL, (long long)tcap / (foscar::kTile * foscar::kWaves * 8)));
     // ranges of at most 4096 tokens: on ragged batches (lengths unknown to the host) shorter
     // ranges keep the last work-groups short; measured best for long and ragged caches
     const long long by_len = (tcap + 4095) / 4096;
