@@ -226,10 +226,13 @@ int foscar_workspace_reserve(const foscar_dims* dims, int bits, int layout, int 
  * must make sure no decode call is still running.  Synchronous. */
 void foscar_release(void);
 
-/* Split plan the decode entry points use for these arguments (bits 2 or 4):
- * *splits = number of key/value ranges per (sequence, KV head), *chunk =
- * tokens per range.  The plan fills the device once at the kernel's
- * residency (foscar_occupancy) with ranges of at most 4096 tokens.
+/* Split plan the decode entry points use for these arguments (bits 2 or 4),
+ * without a window: *splits = number of key/value ranges per (sequence, KV
+ * head), *chunk = tokens per range.  The plan fills the device once at the
+ * kernel's residency (foscar_occupancy), keeps at least 8 tiles of 64 tokens
+ * per wave and makes ranges of at most 4096 tokens.  A windowed call attended
+ * inside the decode launch plans its ranges for the slots its window
+ * work-groups leave.
  * FOSCAR_SPLITS=<n> in the environment forces n ranges (tuning and tests);
  * the count is capped at 512 ranges and at one range per 64-token unit. */
 int foscar_split_plan(const foscar_dims* dims, int bits, int layout, int group, int32_t* splits, int32_t* chunk);
