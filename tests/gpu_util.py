@@ -98,3 +98,25 @@ def check(out, lse, ref_out, ref_lse, what="", vscale=None):
         lerr = np.abs(lse[fin] - ref_lse[fin]).max()
         assert lerr <= LSE_ATOL, f"{what}: lse error {lerr:.3e}"
     return float(err.max())
+
+
+# A ragged batch whose plan needs more work-groups than one round (the persistent,
+# longest-first work order), with empty sequences and sequences of a few tokens.
+PERSISTENT_LENS = (0, 3, 32768, 1, 20000, 0, 4096, 4097, 12000, 64, 65, 30000, 0, 8191, 100, 32767) * 4
+
+
+def persistent_spec():
+    return synth.SPECS["c5_ragged_int2_g64"].replace(batch=len(PERSISTENT_LENS), num_q_heads=8, num_kv_heads=2,
+                                                     max_seq_len=32768, lens=PERSISTENT_LENS)
+
+
+def assert_persistent(spec):
+    """The plan of this spec needs more than one round of resident work-groups."""
+    import bit_quantized_kv_split_amd as fos
+    import torch
+    dims = fos.make_dims(spec.batch, spec.num_q_heads, spec.num_kv_heads, spec.head_dim, spec.max_seq_len)
+    layout = fos.layout_bits(spec.k_layout, spec.v_layout)
+    s, c = fos.foscar_split_plan(dims, spec.bits, layout, spec.group)
+    per_cu = fos.foscar_occupancy(spec.bits, layout, spec.group)
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    assert s * spec.batch * spec.num_kv_heads > per_cu * cus, "the plan must need more than one round"

@@ -10,7 +10,7 @@ import numpy as np
 import pytest
 
 import synth
-from gpu_util import check, oracle_all, oracle_rows, run, stage_spec, value_rms
+from gpu_util import assert_persistent, check, oracle_all, oracle_rows, persistent_spec, run, stage_spec, value_rms
 
 pytestmark = pytest.mark.gpu
 
@@ -164,15 +164,8 @@ def test_persistent_work_order_ragged_with_empty_sequences():
     import bit_quantized_kv_split_amd as fos
     import oracle
     import torch
-    lens = [0, 3, 32768, 1, 20000, 0, 4096, 4097, 12000, 64, 65, 30000, 0, 8191, 100, 32767] * 4
-    spec = _spec("c5_ragged_int2_g64", batch=len(lens), num_q_heads=8, num_kv_heads=2, max_seq_len=32768,
-                 lens=tuple(lens))
-    dims = fos.make_dims(spec.batch, spec.num_q_heads, spec.num_kv_heads, spec.head_dim, spec.max_seq_len)
-    layout = fos.layout_bits(spec.k_layout, spec.v_layout)
-    s, c = fos.foscar_split_plan(dims, spec.bits, layout, spec.group)
-    per_cu = fos.foscar_occupancy(spec.bits, layout, spec.group)
-    cus = torch.cuda.get_device_properties(0).multi_processor_count
-    assert s * spec.batch * spec.num_kv_heads > per_cu * cus, "the plan must need more than one round"
+    spec = persistent_spec()
+    assert_persistent(spec)
     dev, q, lens_np = stage_spec(spec, poison=True)
     G = spec.num_q_heads // spec.num_kv_heads
     ro = np.zeros((spec.batch, spec.num_q_heads, spec.head_dim))

@@ -4,7 +4,7 @@ import pytest
 import torch
 
 import synth
-from gpu_util import stage_spec
+from gpu_util import assert_persistent, persistent_spec, stage_spec
 
 pytestmark = pytest.mark.gpu
 
@@ -46,7 +46,7 @@ def test_dispatch_recorded_events_time_the_kernel():
     assert 0.0 < ms < 100.0, ms
 
 
-@pytest.mark.parametrize("name", ["c2_paper_int2", "c5_ragged_int4_g64"])
+@pytest.mark.parametrize("name", ["c2_paper_int2", "persistent"])
 def test_graph_capture_replays_match_eager(name):
     """Decode steps captured in a HIP graph (after the workspace of the capture
     stream is reserved, a call allocates nothing and records no memset):
@@ -55,8 +55,11 @@ def test_graph_capture_replays_match_eager(name):
     deterministic).  The ragged workload takes the persistent work order,
     whose counters the kernel itself resets for the next call."""
     import bit_quantized_kv_split_amd as fos
-    spec = synth.SPECS[name].replace(batch=6, max_seq_len=4096, ragged_lo=64) if "ragged" in name else \
-        synth.SPECS[name].replace(batch=3, max_seq_len=4096)
+    if name == "persistent":
+        spec = persistent_spec()
+        assert_persistent(spec)
+    else:
+        spec = synth.SPECS[name].replace(batch=3, max_seq_len=4096)
     dev, q, lens = stage_spec(spec)
     layout = fos.layout_bits(spec.k_layout, spec.v_layout)
     args = (dev["q"], dev["packed_k"], dev["packed_v"], dev["k_scale"], dev["k_zero"], dev["v_scale"], dev["v_zero"],

@@ -9,7 +9,7 @@ import pytest
 
 import oracle
 import synth
-from gpu_util import check, stage_spec, value_rms
+from gpu_util import assert_persistent, check, persistent_spec, stage_spec, value_rms
 
 pytestmark = pytest.mark.gpu
 
@@ -70,14 +70,16 @@ def test_window_matrix(bits, kl, vl, g):
 
 
 @pytest.mark.parametrize("name,cap", [("c3_long_int2", 300), ("c3_long_int2", 512), ("c3_long_int2", 1024),
-                                      ("c5_ragged_int2_g64", 512), ("c5_ragged_int2_g64", 4096)])
+                                      ("c3_long_int2", 4096), ("persistent", 512), ("persistent", 4096)])
 def test_window_multi_range_and_persistent(name, cap):
     """Many ranges per sequence (merge path) with the window attended inside the
-    decode launch (up to 512 tokens) or by its own kernel (larger windows), and
-    the persistent work order (ragged batch, always its own kernel)."""
-    base = synth.SPECS[name]
-    spec = base.replace(batch=1, num_q_heads=4, num_kv_heads=1, max_seq_len=16384) if "long" in name else \
-        base.replace(batch=6, num_q_heads=8, num_kv_heads=2, max_seq_len=4096, ragged_lo=64)
+    decode launch by 1-8 work-groups per pair, and the persistent work order
+    (ragged batch with empty sequences; the window by its own kernel)."""
+    if name == "persistent":
+        spec = persistent_spec()
+        assert_persistent(spec)
+    else:
+        spec = synth.SPECS[name].replace(batch=1, num_q_heads=4, num_kv_heads=1, max_seq_len=16384)
     dev, q, lens = stage_spec(spec)
     wl = [cap - 7 * b for b in range(spec.batch)]
     win = synth.make_window(2, spec.batch, spec.num_kv_heads, cap, wl)
