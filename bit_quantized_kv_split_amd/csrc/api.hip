@@ -219,17 +219,16 @@ int decode_common(int bits, const foscar_dims* d, const void* q, const void* pk,
   int32_t splits = 1, chunk = foscar::kTile;
   const int cus = compute_units(dev), per_cu = resident_per_cu(dev, bits, layout, group);
   plan(d, layout, group, cus, per_cu, &splits, &chunk);
-  // a small window is attended inside the launch when the grid runs in one round: one work-group
-  // per pair, so the ranges are planned for one slot fewer per pair
+  // the window is attended inside the decode launch by win_wgs more work-groups per pair: 1, 2, 4
+  // or 8, chunks of at most 128 tokens where 8 allow it (at most 4096 / 8 = 512 = kFusedWindowMax),
+  // beside the ranges of a one-round grid (planned for win_wgs slots fewer per pair) or ahead of a
+  // persistent round
   const bool one_round = (long long)splits * d->batch * d->num_kv_heads <= (long long)cus * per_cu ||
                          d->batch > foscar::kMapMaxB;
-  const bool fuse_window = windowed && one_round;
-  // window work-groups per pair: 1, 2, 4 or 8, chunks of at most 128 tokens where 8 allow it
-  // (chunks of at most 4096 / 8 = 512 = kFusedWindowMax tokens)
   int win_wgs = 1;
   while (win_wgs < foscar::kMaxWindowWgs && win_wgs * 128 < win_cap) win_wgs *= 2;
   const int win_chunk = (win_cap + win_wgs - 1) / win_wgs;
-  if (fuse_window) plan(d, layout, group, cus, per_cu, &splits, &chunk, win_wgs);
+  if (windowed && one_round) plan(d, layout, group, cus, per_cu, &splits, &chunk, win_wgs);
   int32_t* counters = nullptr;
   float* partials = nullptr;
   rc = get_workspace(counter_bytes(d), partial_bytes(d, splits), (hipStream_t)stream, &counters, &partials);
@@ -272,8 +271,7 @@ int decode_common(int bits, const foscar_dims* d, const void* q, const void* pk,
   sa.win_lens = nullptr;
   sa.win_cap = 0;
   sa.win_sm = sm;
-  if (fuse_window && !sa.persistent) {
-    // attended inside the decode launch by win_wgs more work-groups per pair, beside the ranges
+  if (windowed) {  // beside the ranges (one round) or before the persistent round in the same grid
     const size_t rows = (size_t)d->batch * d->num_q_heads;
     sa.win_o = sa.lse_part + rows * splits;
     sa.win_lse = sa.win_o + rows * win_wgs * foscar::kHeadDim;
@@ -284,26 +282,6 @@ int decode_common(int bits, const foscar_dims* d, const void* q, const void* pk,
     sa.win_v = (const uint16_t*)win_v;
     sa.win_lens = win_lens;
     sa.win_cap = win_cap;
-  } else if (windowed) {  // the window's partial first, into the last slot of the workspace; then the merge takes it in
-    const size_t rows = (size_t)d->batch * d->num_q_heads;
-    float* wo = sa.lse_part + rows * splits;
-    foscar::WindowArgs wa;
-    wa.q = (const uint16_t*)q;
-    wa.wk = (const uint16_t*)win_k;
-    wa.wv = (const uint16_t*)win_v;
-    wa.wlens = win_lens;
-    wa.o = wo;
-    wa.lse = wo + rows * foscar::kHeadDim;
-    wa.hq = d->num_q_heads;
-    wa.hkv = d->num_kv_heads;
-    wa.g_heads = sa.g_heads;
-    wa.wcap = win_cap;
-    wa.sm = sm;
-    e = foscar::launch_window(wa, d->batch, (hipStream_t)stream);
-    if (e != hipSuccess) return hip_fail(e);
-    sa.win_o = wa.o;
-    sa.win_lse = wa.lse;
-    sa.win_slots = 1;
   }
 
   e = foscar::launch_decode(bits, (layout & FOSCAR_K_CHANNEL) != 0, (layout & FOSCAR_V_CHANNEL) != 0, group,

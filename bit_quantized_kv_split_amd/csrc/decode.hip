@@ -648,12 +648,11 @@ __device__ __forceinline__ void run_item(const SplitArgs& a, const int b, const 
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r0 = split * a.chunk;
   if (r0 >= T) {  // no token in this range; an empty sequence's rows are written once
-    if (T == 0 && split == 0 && !a.win_wgs) {  // (fused window work-groups write them themselves)
+    if (T == 0 && split == 0 && !a.win_wgs) {  // (with a window, its work-groups write them)
       for (int idx = (int)tid; idx < a.g_heads * kHeadDim; idx += blockDim.x) {
         const size_t row = (size_t)b * a.hq + h * a.g_heads + idx / kHeadDim;
-        // no cache token: the window's result as it is (0 and -inf for an empty window too)
-        a.out[row * kHeadDim + idx % kHeadDim] = a.win_o ? to_bf16_rne(a.win_o[row * kHeadDim + idx % kHeadDim]) : 0;
-        if (idx % kHeadDim == 0 && a.lse) a.lse[row] = a.win_o ? a.win_lse[row] : -INFINITY;
+        a.out[row * kHeadDim + idx % kHeadDim] = 0;  // no token at all: out = 0, lse = -inf
+        if (idx % kHeadDim == 0 && a.lse) a.lse[row] = -INFINITY;
       }
     }
     if (next && wave == 0) {
@@ -1479,7 +1478,9 @@ __device__ __forceinline__ void window_item(const SplitArgs& a, const int b, con
 // Larger grids (ragged batches of at most kMapMaxB sequences) run persistent:
 // one round of work-groups takes work items from a device-wide counter, longest
 // first (map_select), until the items run out; the last work-group to leave
-// resets the counters for the next call.
+// resets the counters for the next call.  A window's work-groups come before
+// that round in the grid, one item each; no work-group ever waits for another
+// (every hand-off is an arrival count), so their order cannot stall the grid.
 template <int BITS, bool KCH, bool VCH, int GRP>
 __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(waves_per_simd<BITS, KCH, VCH, GRP>())))
 void split_decode(const SplitArgs a) {
@@ -1491,6 +1492,16 @@ void split_decode(const SplitArgs a) {
       return;
     }
     run_item<BITS, KCH, VCH, GRP>(a, b, blockIdx.x % a.hkv, (int)blockIdx.y - a.win_wgs, T, nullptr);
+    return;
+  }
+  // window work-groups take the first blocks (dispatched first) and leave
+  // after their one item; they never take an item from the counter
+  const int pairs = a.batch * a.hkv;
+  const int nwin = pairs * a.win_wgs;
+  if ((int)blockIdx.x < nwin) {
+    const int pair = (int)blockIdx.x % pairs;  // consecutive blocks: different pairs
+    const int b = pair / a.hkv;
+    window_item(a, b, pair % a.hkv, min(max(a.seq_lens[b], 0), a.tcap), (int)blockIdx.x / pairs);
     return;
   }
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -1514,7 +1525,7 @@ void split_decode(const SplitArgs a) {
   }
   if (threadIdx.x == 0) {
     const int left = __hip_atomic_fetch_add(a.work_ctr + 1, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (left == (int)(gridDim.x * gridDim.y) - 1) {  // every other work-group has left: no more grabs
+    if (left == (int)gridDim.x - nwin - 1) {  // every other item-taking work-group has left: no more grabs
       __hip_atomic_store(a.work_ctr, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       __hip_atomic_store(a.work_ctr + 1, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
@@ -1545,7 +1556,7 @@ hipError_t launch_one(int batch, int hkv, const SplitArgs& sa, hipStream_t strea
     return hipOccupancyMaxActiveBlocksPerMultiprocessor(per_cu, split_decode<BITS, KCH, VCH, GRP>, kWaves * 64, lds);
   static_assert(lds >= sizeof(float) * (kMaxG * kHeadDim * (1 + kWaves) + kMaxG * kFusedWindowMax),
                 "rings must hold a fused window's query rows, scores and partial sums");
-  const dim3 grid = sa.persistent ? dim3(sa.grid_wgs) : dim3(batch * hkv, sa.splits + sa.win_wgs);
+  const dim3 grid = sa.persistent ? dim3(sa.grid_wgs + batch * hkv * sa.win_wgs) : dim3(batch * hkv, sa.splits + sa.win_wgs);
   if (ev.start || ev.stop)  // timing events recorded by the dispatch itself
     hipExtLaunchKernelGGL((split_decode<BITS, KCH, VCH, GRP>), grid, dim3(kWaves * 64), lds, stream, ev.start, ev.stop,
                           0, sa);

@@ -41,8 +41,9 @@ struct SplitArgs {
   float* win_o;              // fp32 [B][Hq][win_slots][D] normalised outputs over a full-precision window, or null
   float* win_lse;            // fp32 [B][Hq][win_slots] their natural-log lse (-inf: no window token)
   int32_t win_slots;         // window partials per row (0: no window)
-  // window attended inside this launch: win_wgs more work-groups per pair (grid rows 0 .. win_wgs-1,
-  // ranges in the rows after them), work-group j taking window tokens [j * win_chunk, +win_chunk)
+  // window attended inside this launch: win_wgs more work-groups per pair (grid rows 0 .. win_wgs-1
+  // with the ranges in the rows after them, or the first B * Hkv * win_wgs blocks of a persistent
+  // grid), work-group j taking window tokens [j * win_chunk, +win_chunk)
   int32_t win_wgs;
   int32_t win_chunk;         // <= kFusedWindowMax
   const uint16_t* win_k;     // bf16 [B][Hkv][win_cap][D]
@@ -53,22 +54,7 @@ struct SplitArgs {
 };
 constexpr int kMaxWindowWgs = 8;      // window work-groups per pair inside the decode launch
 constexpr int kFusedWindowMax = 512;  // window tokens of one work-group inside the decode launch
-
-// Attention over a full-precision (bf16) window of recent tokens (window.hip):
-// per (sequence, KV head) the window's normalised output and lse, merged into
-// the decode result by the decode kernel.
-struct WindowArgs {
-  const uint16_t* q;         // bf16 [B][Hq][D]
-  const uint16_t* wk;        // bf16 [B][Hkv][wcap][D]
-  const uint16_t* wv;        // bf16 [B][Hkv][wcap][D]
-  const int32_t* wlens;      // [B] window tokens, clamped to [0, wcap]
-  float* o;                  // fp32 [B][Hq][D]
-  float* lse;                // fp32 [B][Hq]
-  int32_t hq, hkv, g_heads, wcap;
-  float sm;                  // softmax scale
-};
-constexpr int kMaxWindow = 4096;  // tokens of a window (LDS score table of the window kernel)
-hipError_t launch_window(const WindowArgs& a, int batch, hipStream_t stream);
+constexpr int kMaxWindow = kMaxWindowWgs * kFusedWindowMax;  // tokens of a window: 4096
 
 // Events the dispatch records around the kernel (either may be null).
 struct LaunchEvents {

@@ -73,8 +73,8 @@ def test_window_matrix(bits, kl, vl, g):
                                       ("c3_long_int2", 4096), ("persistent", 512), ("persistent", 4096)])
 def test_window_multi_range_and_persistent(name, cap):
     """Many ranges per sequence (merge path) with the window attended inside the
-    decode launch by 1-8 work-groups per pair, and the persistent work order
-    (ragged batch with empty sequences; the window by its own kernel)."""
+    decode launch by 1-8 work-groups per pair, beside the ranges or ahead of
+    the persistent round (ragged batch with empty sequences)."""
     if name == "persistent":
         spec = persistent_spec()
         assert_persistent(spec)
