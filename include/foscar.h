@@ -130,10 +130,10 @@ int foscar_decode_int4(const foscar_dims* dims, const void* q, const void* packe
  * recent tokens as part of the accuracy recipe a 2-bit cache needs.  The
  * window's tokens are further keys and values of the same softmax: out and lse
  * are those of attention over the T_b cache tokens and the window's tokens
- * together.  The window is attended in fp32 from bf16, by 1-8 extra
- * work-groups per (sequence, KV head) of the decode launch when its grid runs
- * in one round, else by a kernel of its own before it, and merged with the
- * cache's ranges by log-sum-exp inside the decode kernel.
+ * together.  The window is attended in fp32 from bf16 by 1-8 extra
+ * work-groups per (sequence, KV head) of the decode launch itself, and merged
+ * with the cache's ranges by log-sum-exp inside the same kernel: one launch per
+ * call.
  *
  * Arguments as foscar_decode_int2/int4, plus:
  * win_k, win_v  bf16 [B][Hkv][win_cap][D]: window keys and values
@@ -141,8 +141,8 @@ int foscar_decode_int4(const foscar_dims* dims, const void* q, const void* packe
  *               [0, win_cap]; rows past them may hold anything
  * win_cap       0 .. 4096 tokens (win_k / win_v may be NULL when 0)
  * A sequence with no cache token and no window token gives out = 0,
- * lse = -inf.  The window uses a slot of the split workspace (see
- * foscar_workspace_reserve, which reserves it).
+ * lse = -inf.  The window uses slots of the split workspace (see
+ * foscar_workspace_reserve, which reserves them).
  */
 int foscar_decode_window_int2(const foscar_dims* dims, const void* q, const void* packed_k, const void* packed_v,
                               const void* k_scale, const void* k_zero, const void* v_scale, const void* v_zero,
@@ -230,8 +230,8 @@ void foscar_release(void);
  * without a window: *splits = number of key/value ranges per (sequence, KV
  * head), *chunk = tokens per range.  The plan fills the device once at the
  * kernel's residency (foscar_occupancy), keeps at least 8 tiles of 64 tokens
- * per wave and makes ranges of at most 4096 tokens.  A windowed call attended
- * inside the decode launch plans its ranges for the slots its window
+ * per wave and makes ranges of at most 4096 tokens.  A windowed call whose
+ * grid runs in one round plans its ranges for the slots its window
  * work-groups leave.
  * FOSCAR_SPLITS=<n> in the environment forces n ranges (tuning and tests);
  * the count is capped at 512 ranges and at one range per 64-token unit. */
