@@ -367,22 +367,22 @@ __device__ __forceinline__ float coherent_load(const float* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Fold the S window partials of rows row0 and row1 (channel c) into a running
-// log-sum-exp merge (max m, weighted sum n, weight sum d).  Device-coherent
-// loads (in a fused launch other work-groups wrote the slots), all issued
-// before any is used.  An empty term (lse -inf) adds nothing, and a running
-// max of -inf has nothing to rescale.
+// Fold the S window partials of (row0, channel c0) and (row1, channel c1) into
+// running log-sum-exp merges (max m, weighted sum n, weight sum d).
+// Device-coherent loads (other work-groups wrote the slots), all issued before
+// any is used.  An empty term (lse -inf) adds nothing, and a running max of
+// -inf has nothing to rescale.
 template <int S>
-__device__ __forceinline__ void fold_window_slots(const SplitArgs& a, size_t row0, size_t row1, int c, float& m0,
-                                                  float& n0, float& d0, float& m1, float& n1, float& d1) {
+__device__ __forceinline__ void fold_window_slots(const SplitArgs& a, size_t row0, int c0, size_t row1, int c1,
+                                                  float& m0, float& n0, float& d0, float& m1, float& n1, float& d1) {
   constexpr int D = kHeadDim;
   float wl0[S], wl1[S], wo0[S], wo1[S];
 #pragma unroll
   for (int j = 0; j < S; ++j) {
     wl0[j] = coherent_load(a.win_lse + row0 * S + j);
     wl1[j] = coherent_load(a.win_lse + row1 * S + j);
-    wo0[j] = coherent_load(a.win_o + (row0 * S + j) * D + c);
-    wo1[j] = coherent_load(a.win_o + (row1 * S + j) * D + c);
+    wo0[j] = coherent_load(a.win_o + (row0 * S + j) * D + c0);
+    wo1[j] = coherent_load(a.win_o + (row1 * S + j) * D + c1);
   }
 #pragma unroll
   for (int j = 0; j < S; ++j) {
@@ -402,94 +402,87 @@ __device__ __forceinline__ void fold_window_slots(const SplitArgs& a, size_t row
 // Log-sum-exp merge of the ns ranges of one (sequence, KV head), run by the
 // work-group that finished last: O = sum_s exp(lse_s - M) O_s / sum_s exp(lse_s - M),
 // lse = M + log(sum_s exp(lse_s - M)).  The partials were written by other
-// work-groups, so they are read with device-coherent loads.  Thread t owns
-// channel t % 128 of query row t / 128 (and of row t / 128 + 2 with 256
-// threads) and streams the ranges in blocks of 16: each block's lse and
-// partial outputs are loaded together (one memory round trip per block), then
-// folded into a running max.
+// work-groups, so they are read with device-coherent loads.  Wave i owns query
+// row i, lane l its channels 2l and 2l + 1, and the ranges stream in blocks of
+// 32 (all of them at the long-context plan): each block's partial outputs
+// (64-bit loads, the range in a scalar offset) and lse values (lane u: range
+// u) are issued together, one memory round trip per block.  The block's max,
+// weights and weight sum are wave reductions, and each weight reaches the
+// multiply-adds as a scalar operand (readlane), so the merge needs no LDS and
+// no barrier.
+// max over all 64 lanes, in every lane (the pattern of wave_sum)
+__device__ __forceinline__ float wave_max(float v) {
+  v = fmaxf(v, dpp<0x121>(v));  // row_ror:1
+  v = fmaxf(v, dpp<0x122>(v));  // row_ror:2
+  v = fmaxf(v, dpp<0x124>(v));  // row_ror:4
+  v = fmaxf(v, dpp<0x128>(v));  // row_ror:8
+  float a = v, b = v;
+  asm volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1" : "+v"(a), "+v"(b));
+  v = fmaxf(a, b);
+  a = v;
+  b = v;
+  asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(a), "+v"(b));
+  return fmaxf(a, b);
+}
 __device__ __forceinline__ void merge_ranges(const SplitArgs& a, int b, int h, int ns) {
-  constexpr int D = kHeadDim, BLK = 16;
+  constexpr int D = kHeadDim, BLK = 32;
+  static_assert(kWaves == kMaxG && D == 128, "one wave per query row, two channels per lane");
   const int G = a.g_heads;
   const uint32_t tid = in_vgpr(threadIdx.x);  // opaque: not hoisted out of a work loop
-  const int c = tid & (D - 1);
-  constexpr int RS = kWaves * 64 / D;  // rows one pass of the work-group covers
-  static_assert(RS == 2 || RS == 4, "two or four rows per pass");
-  const int i0 = tid / D;
-  if (i0 >= G) return;
-  const bool two = RS == 2 && i0 + 2 < G;
-  const size_t row0 = (size_t)b * a.hq + (size_t)h * G + i0;
-  const size_t row1 = two ? row0 + 2 : row0;
-  const float* lp0 = a.lse_part + row0 * a.splits;
-  const float* lp1 = a.lse_part + row1 * a.splits;
-  const float* op0 = a.o_part + row0 * a.splits * D + c;
-  const float* op1 = a.o_part + row1 * a.splits * D + c;
-  float m0 = -INFINITY, m1 = -INFINITY, n0 = 0.f, n1 = 0.f, d0 = 0.f, d1 = 0.f;
+  const int lane = tid & 63;
+  const int i = __builtin_amdgcn_readfirstlane(tid >> 6);
+  if (i >= G) return;
+  const size_t row = (size_t)b * a.hq + (size_t)h * G + i;
+  const __amdgpu_buffer_rsrc_t ro = rsrc(a.o_part + row * a.splits * D, (uint32_t)(a.splits * D * 4));
+  const uint32_t vo = (uint32_t)lane * 8;
+  const float* lp = a.lse_part + row * a.splits;
+  float m = -INFINITY, n0 = 0.f, n1 = 0.f, d = 0.f;
   for (int s0 = 0; s0 < ns; s0 += BLK) {
-    float l0[BLK], l1[BLK], v0[BLK], v1[BLK];
     // unconditional loads (an atomic load under a branch is not speculated, and
     // the branches would serialise the round trips): ranges past ns re-read
-    // range ns - 1 and are masked afterwards
+    // range ns - 1 and are masked afterwards.  sc1 (cache policy 16): device-
+    // coherent, like the relaxed agent-scope atomic loads of the hand-off
+    uint2 v[BLK];
 #pragma unroll
     for (int u = 0; u < BLK; ++u) {
-      const int si = min(s0 + u, ns - 1);
-      l0[u] = coherent_load(lp0 + si);
-      v0[u] = coherent_load(op0 + (size_t)si * D);
-      l1[u] = coherent_load(lp1 + si);
-      v1[u] = coherent_load(op1 + (size_t)si * D);
+      const uint32_t so = (uint32_t)(min(s0 + u, ns - 1) * D * 4);
+      v[u] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(ro, vo, so, 16));
     }
+    const int su = s0 + (lane & (BLK - 1));
+    const float l0 = coherent_load(lp + min(su, ns - 1));
+    const float l = (lane < BLK && su < ns) ? l0 : -INFINITY;  // every range below ns has a finite lse
+    const float bm = fmaxf(m, wave_max(l));
+    const float w = __expf(l - bm);  // 0 for masked lanes
+    const float r = __expf(m - bm);  // 0 on the first block
+    n0 *= r;
+    n1 *= r;
+    d = fmaf(d, r, wave_sum(w));
 #pragma unroll
     for (int u = 0; u < BLK; ++u) {
-      if (s0 + u >= ns) {
-        l0[u] = l1[u] = -INFINITY;
-        v0[u] = v1[u] = 0.f;
-      }
+      const float wu = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), u));
+      n0 = fmaf(wu, __uint_as_float(v[u].x), n0);  // masked ranges: wu = 0 and a finite re-read
+      n1 = fmaf(wu, __uint_as_float(v[u].y), n1);
     }
-    float b0 = m0, b1 = m1;  // every range below ns holds a token, so its lse is finite
-#pragma unroll
-    for (int u = 0; u < BLK; ++u) {
-      b0 = fmaxf(b0, l0[u]);
-      b1 = fmaxf(b1, l1[u]);
-    }
-    const float r0 = __expf(m0 - b0), r1 = __expf(m1 - b1);  // 0 on the first block
-    n0 *= r0;
-    d0 *= r0;
-    n1 *= r1;
-    d1 *= r1;
-#pragma unroll
-    for (int u = 0; u < BLK; ++u) {
-      const float w0 = __expf(l0[u] - b0), w1 = __expf(l1[u] - b1);
-      n0 = fmaf(w0, v0[u], n0);
-      d0 += w0;
-      n1 = fmaf(w1, v1[u], n1);
-      d1 += w1;
-    }
-    m0 = b0;
-    m1 = b1;
+    m = bm;
   }
   // the full-precision window's partials are further terms of the same merge (1, 2, 4 or 8 slots)
+  float m1 = m, d1 = d;
+  const int c = 2 * lane;
   switch (a.win_slots) {
-    case 1: fold_window_slots<1>(a, row0, row1, c, m0, n0, d0, m1, n1, d1); break;
-    case 2: fold_window_slots<2>(a, row0, row1, c, m0, n0, d0, m1, n1, d1); break;
-    case 4: fold_window_slots<4>(a, row0, row1, c, m0, n0, d0, m1, n1, d1); break;
-    case 8: fold_window_slots<8>(a, row0, row1, c, m0, n0, d0, m1, n1, d1); break;
+    case 1: fold_window_slots<1>(a, row, c, row, c + 1, m, n0, d, m1, n1, d1); break;
+    case 2: fold_window_slots<2>(a, row, c, row, c + 1, m, n0, d, m1, n1, d1); break;
+    case 4: fold_window_slots<4>(a, row, c, row, c + 1, m, n0, d, m1, n1, d1); break;
+    case 8: fold_window_slots<8>(a, row, c, row, c + 1, m, n0, d, m1, n1, d1); break;
     default: break;
   }
-  if (!(d0 > 0.f)) {  // no token at all (no cache range and empty window slots)
-    n0 = 0.f;
-    d0 = 1.f;
-    m0 = -INFINITY;
+  if (!(d > 0.f)) {  // no token at all (no cache range and empty window slots)
+    n0 = n1 = 0.f;
+    d = 1.f;
+    m = -INFINITY;
   }
-  if (!(d1 > 0.f)) {
-    n1 = 0.f;
-    d1 = 1.f;
-    m1 = -INFINITY;
-  }
-  a.out[row0 * D + c] = to_bf16_rne(n0 / d0);
-  if (c == 0 && a.lse) a.lse[row0] = m0 + __logf(d0);
-  if (two) {
-    a.out[row1 * D + c] = to_bf16_rne(n1 / d1);
-    if (c == 0 && a.lse) a.lse[row1] = m1 + __logf(d1);
-  }
+  const uint32_t packed = (uint32_t)to_bf16_rne(n0 / d) | ((uint32_t)to_bf16_rne(n1 / d) << 16);
+  reinterpret_cast<uint32_t*>(a.out + row * D)[lane] = packed;
+  if (lane == 0 && a.lse) a.lse[row] = m + __logf(d);
 }
 
 // ---------------------------------------------------------------------------
