@@ -1352,8 +1352,7 @@ __device__ __forceinline__ void window_item(const SplitArgs& a, const int b, con
   extern __shared__ __align__(16) unsigned char smem[];
   __shared__ float s_wred[kWaves];
   const int CW = a.win_chunk;                    // window tokens of one work-group
-  float* s_qf = reinterpret_cast<float*>(smem);  // [kMaxG][D]
-  float* s_p = s_qf + kMaxG * D;                 // [kMaxG][CW]
+  float* s_p = reinterpret_cast<float*>(smem) + kMaxG * D;  // [kMaxG][CW] (after a [kMaxG][D] area left free)
   float* s_ow = s_p + kMaxG * CW;                // [kWaves][kMaxG][D]
   const int G = a.g_heads;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -1364,35 +1363,46 @@ __device__ __forceinline__ void window_item(const SplitArgs& a, const int b, con
   const int t0 = wave * chunk, t1 = min(t0 + chunk, W);
   const size_t row0 = (size_t)b * a.hq + (size_t)h * G;
   const size_t bh = (size_t)b * a.hkv + h;
-  for (int idx = tid; idx < kMaxG * D; idx += kWaves * 64) {
-    const int i = idx / D, c = idx % D;
-    s_qf[idx] = (i < G) ? __uint_as_float((uint32_t)a.q[(row0 + i) * D + c] << 16) : 0.f;
-  }
-  __syncthreads();
   const size_t kv0 = (bh * (size_t)a.win_cap + (size_t)j * CW) * D;
-  const uint4* wk = reinterpret_cast<const uint4*>(a.win_k + kv0);
-  for (int t = t0 + lane; t < t1; t += 64) {
-    float acc[kMaxG] = {0.f, 0.f, 0.f, 0.f};
-    const uint4* kr = wk + (size_t)t * (D / 8);
-#pragma unroll 2
-    for (int k = 0; k < D / 8; ++k) {
-      const uint4 w = kr[k];
-      const float x[8] = {__uint_as_float(w.x << 16), __uint_as_float(w.x & 0xFFFF0000u),
-                          __uint_as_float(w.y << 16), __uint_as_float(w.y & 0xFFFF0000u),
-                          __uint_as_float(w.z << 16), __uint_as_float(w.z & 0xFFFF0000u),
-                          __uint_as_float(w.w << 16), __uint_as_float(w.w & 0xFFFF0000u)};
+  // scores on the matrix cores: v_mfma_f32_16x16x32_bf16 with A = 16 window keys (rows = tokens),
+  // B = the query rows (columns; G of 16 used), the contraction over channels in 4 steps of 32.
+  // Lane l holds token / query row l % 16 and, at step k, channels 32k + 8(l / 16) .. +7 of both
+  // operands (A and B take the same slot layout, so any assignment of channels to slots that both
+  // share gives the full dot product).  bf16 x bf16 products are exact in fp32.  C: lane l holds
+  // tokens 4(l / 16) .. +3 of the block for query row l % 16.
+  typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+  typedef float f32x4 __attribute__((ext_vector_type(4)));
+  const int mr = lane & 15, mg = lane >> 4;
+  bf16x8 qb[D / 32];
+  {
+    const uint32_t* qr = reinterpret_cast<const uint32_t*>(a.q + (row0 + (size_t)min(mr, G - 1)) * D);
 #pragma unroll
-      for (int i = 0; i < kMaxG; ++i) {
-        const float4 qa = *reinterpret_cast<const float4*>(s_qf + i * D + 8 * k);
-        const float4 qb = *reinterpret_cast<const float4*>(s_qf + i * D + 8 * k + 4);
-        float v = acc[i];
-        v = fmaf(qa.x, x[0], v); v = fmaf(qa.y, x[1], v); v = fmaf(qa.z, x[2], v); v = fmaf(qa.w, x[3], v);
-        v = fmaf(qb.x, x[4], v); v = fmaf(qb.y, x[5], v); v = fmaf(qb.z, x[6], v); v = fmaf(qb.w, x[7], v);
-        acc[i] = v;
-      }
+    for (int k = 0; k < D / 32; ++k) {
+      uint4 w;  // 4-byte loads: the query is only 4-byte aligned
+      w.x = qr[(32 * k + 8 * mg) / 2 + 0];
+      w.y = qr[(32 * k + 8 * mg) / 2 + 1];
+      w.z = qr[(32 * k + 8 * mg) / 2 + 2];
+      w.w = qr[(32 * k + 8 * mg) / 2 + 3];
+      if (mr >= G) w = make_uint4(0u, 0u, 0u, 0u);
+      qb[k] = __builtin_bit_cast(bf16x8, w);
     }
+  }
+  const uint4* wk = reinterpret_cast<const uint4*>(a.win_k + kv0);
+  for (int tb = t0; tb < t1; tb += 16) {  // wave-uniform: the matrix instructions run with every lane
+    const int t = tb + mr;
+    const uint4* kr = wk + (size_t)min(t, t1 - 1) * (D / 8) + mg;  // rows past t1 re-read row t1 - 1
+    uint4 kw[D / 32];
 #pragma unroll
-    for (int i = 0; i < kMaxG; ++i) s_p[i * CW + t] = acc[i] * a.win_sm;
+    for (int k = 0; k < D / 32; ++k) kw[k] = kr[4 * k];
+    f32x4 c = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int k = 0; k < D / 32; ++k)
+      c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kw[k]), qb[k], c, 0, 0, 0);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int tr = tb + 4 * mg + r;
+      if (mr < G && tr < t1) s_p[mr * CW + tr] = c[r] * a.win_sm;
+    }
   }
   __syncthreads();
   float m[kMaxG], l[kMaxG];
