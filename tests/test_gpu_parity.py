@@ -184,3 +184,18 @@ def test_persistent_work_order_ragged_with_empty_sequences():
     for k in range(2):
         out, lse = run(spec, dev)
         check(out, lse, ro, rl, f"persistent ragged call {k}", vsc)
+
+
+@pytest.mark.parametrize("G", [1, 2, 3])
+@pytest.mark.parametrize("splits", ["7", "64"])
+def test_gqa_ratios_through_the_merge(G, splits, monkeypatch):
+    """G = 1-3 query heads per KV head with several ranges per sequence: the
+    merge gives each query row its own wave, and waves past G leave early.  64
+    forced ranges give 4096 tokens two blocks of 32 ranges and 2500 tokens a
+    block plus a masked remainder."""
+    spec = synth.Spec(f"gqa_merge_{G}", 14, 2, "token", "channel", 64, 2, 3 * G, 3, 128, 4096, lens=(4096, 2500))
+    monkeypatch.setenv("FOSCAR_SPLITS", splits)
+    dev, q, lens = stage_spec(spec)
+    out, lse = run(spec, dev)
+    ro, rl, vsc = oracle_all(spec, q, lens)
+    check(out, lse, ro, rl, f"{spec.name} splits={splits}", vsc)

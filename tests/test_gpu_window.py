@@ -88,6 +88,20 @@ def test_window_multi_range_and_persistent(name, cap):
     check(out, lse, ro, rl, spec.name, vsc)
 
 
+@pytest.mark.parametrize("G", [1, 3])
+def test_window_gqa_ratios_through_the_merge(G, monkeypatch):
+    """G = 1 and 3 query heads per KV head, 64 forced ranges and a window:
+    window partials fold into the merge of every query row, including the
+    pairs whose sequence has no cache token."""
+    spec = synth.Spec(f"win_gqa_{G}", 15, 2, "token", "token", 128, 3, 3 * G, 3, 128, 4096, lens=(4096, 2500, 0))
+    monkeypatch.setenv("FOSCAR_SPLITS", "64")
+    dev, q, lens = stage_spec(spec)
+    win = synth.make_window(4, spec.batch, spec.num_kv_heads, 300, [300, 17, 150])
+    out, lse = _run(spec, dev, win)
+    ro, rl, vsc = _oracle(spec, q, lens, win)
+    check(out, lse, ro, rl, spec.name, vsc)
+
+
 def test_window_dominates_when_its_scores_are_larger():
     """A window whose keys align with the query takes almost all the weight:
     the output approaches the window's own attention output (a property of
