@@ -33,9 +33,13 @@
 //   * online softmax with the exact running max of each query head (DPP,
 //     ds_swizzle and ds_bpermute reductions across the 16 lanes of a head; the
 //     accumulators are rescaled only when a max rises);
-//   * a range's partial (O, lse) goes to a workspace; the last work-group to
-//     finish a (sequence, KV head) merges its ranges by log-sum-exp (agent-scope
-//     release/acquire counter), so one decode step is one kernel launch.
+//   * a range's partial (O, lse) goes to a workspace with device-coherent (sc1)
+//     relaxed stores; after its stores complete (vmcnt(0)) a work-group counts
+//     its arrival on the pair's counter, and the last to arrive merges the
+//     ranges by log-sum-exp, one memory round trip per 32 ranges: one decode
+//     step is one kernel launch;
+//   * a full-precision window of recent tokens is attended by extra work-groups
+//     of the same launch (window_item) whose partials join that merge.
 #include <math.h>
 
 #include <hip/hip_ext.h>
