@@ -27,6 +27,8 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "INT2/INT4 decode-attn achieved HBM GB/s (% of 8 TB/s) and µs/step"
+_ARITH = "f16"
+_ARITH_TEXT = "2-bit codes -> fp16 matrix-core operands (magic-exponent AND-OR), fp32 accumulation, bf16 out"
 PEAK_HBM_GBS = 8000.0
 
 
@@ -36,7 +38,10 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="c3_long_int2")
-    ap.add_argument("--copies", type=int, default=2, help="independent cache copies rotated over the steps")
+    ap.add_argument("--copies", type=int, default=0,
+                    help="cache copies rotated over the steps (default: enough for at least 1 GiB)")
+    ap.add_argument("--sustain", type=int, default=2000,
+                    help="steps of a second, sustained pass reported beside the timed one (0: none)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--dump-steps", action="store_true", help="print each step's kernel microseconds to stderr")
@@ -72,43 +77,108 @@ def traffic_per_launch(workload):
     return t.get("bytes_per_launch")
 
 
-def cpu_baseline(spec, q, lens, target_s):
-    """The fp64 oracle (single-threaded numpy) on the first (sequence, KV head)
-    slices of the same workload until about target_s seconds of CPU work."""
+def _cpu_info():
+    """Host CPU model, logical CPUs, and the CPUs this process may run on."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except AttributeError:
+        usable = os.cpu_count() or 1
+    return model, os.cpu_count() or 1, usable
+
+
+def _slice_bytes(spec, t, G):
+    D = spec.head_dim
+    sz = 0
+    for layout in (spec.k_layout, spec.v_layout):
+        sz += 2 * 2 * (t * (D // spec.group) if layout == "token" else -(-t // spec.group) * D)
+    return 2 * t * D * spec.bits // 8 + sz + 2 * 2 * G * D + 4 * G
+
+
+def _oracle_worker(args):
+    """One worker: build its (sequence, KV head) slices (not timed), wait for
+    every worker, then time the oracle over them; returns (start, end, bytes)."""
+    spec_name, spec_kw, q, lens, slices = args
     import numpy as np
     from threadpoolctl import threadpool_limits
 
     import oracle
     import synth
 
+    spec = synth.SPECS[spec_name].replace(**spec_kw) if spec_kw else synth.SPECS[spec_name]
     G = spec.num_q_heads // spec.num_kv_heads
-    done_bytes, spent, slices = 0, 0.0, 0
-    D = spec.head_dim
-    for b in range(spec.batch):
-        for h in range(spec.num_kv_heads):
-            head = synth.make_head(spec, b, h, seq_len=int(lens[b]))  # not timed
-            w = {k: v[None, None] for k, v in head.items()}
-            w["q"] = q[b:b + 1, h * G:(h + 1) * G]
-            w["seq_lens"] = np.array([lens[b]], np.int32)
-            with threadpool_limits(1):
-                t0 = time.perf_counter()
-                oracle.decode_rows(w, [(0, i) for i in range(G)], k_layout=spec.k_layout, v_layout=spec.v_layout,
-                                   group=spec.group, sm_scale=spec.sm_scale)
-                spent += time.perf_counter() - t0
-            t = int(lens[b])
-            sz = 0
-            for layout in (spec.k_layout, spec.v_layout):
-                sz += 2 * 2 * (t * (D // spec.group) if layout == "token" else -(-t // spec.group) * D)
-            done_bytes += 2 * t * D * spec.bits // 8 + sz + 2 * 2 * G * D + 4 * G
-            slices += 1
-            if spent >= target_s:
-                break
-        if spent >= target_s:
+    work = []
+    for b, h in slices:
+        head = synth.make_head(spec, b, h, seq_len=int(lens[b]))
+        w = {k: v[None, None] for k, v in head.items()}
+        w["q"] = q[b:b + 1, h * G:(h + 1) * G]
+        w["seq_lens"] = np.array([lens[b]], np.int32)
+        work.append((w, _slice_bytes(spec, int(lens[b]), G)))
+    _BARRIER[0].wait()
+    with threadpool_limits(1):
+        t0 = time.perf_counter()
+        done = 0
+        for w, nb in work:
+            oracle.decode_rows(w, [(0, i) for i in range(G)], k_layout=spec.k_layout, v_layout=spec.v_layout,
+                               group=spec.group, sm_scale=spec.sm_scale)
+            done += nb
+        t1 = time.perf_counter()
+    return t0, t1, done
+
+
+_BARRIER = [None]
+
+
+def _init_worker(barrier):
+    _BARRIER[0] = barrier
+
+
+def cpu_baseline(spec, q, lens, target_s, max_workers=16):
+    """The fp64 oracle (numpy, one BLAS thread per process) timed on the host
+    cores: one worker process per core (at most the box's 16-CPU share of one
+    GPU), the same workload's (sequence, KV head) slices dealt round-robin, all
+    workers started together after building their inputs; wall clock from the
+    first start to the last end.  The sample is the whole step when one core's
+    estimated share fits target_s, otherwise the first slices that do."""
+    import multiprocessing as mp
+
+    model, logical, usable = _cpu_info()
+    workers = max(1, min(max_workers, usable))
+    G = spec.num_q_heads // spec.num_kv_heads
+    pairs = [(b, h) for b in range(spec.batch) for h in range(spec.num_kv_heads) if int(lens[b]) > 0]
+    # one core runs the fp64 oracle at about 80 MB of cache per second (the long-context step: 3.8 s for 302 MB)
+    est = [_slice_bytes(spec, int(lens[b]), G) / 8e7 for b, h in pairs]
+    budget, take = target_s * workers, []
+    for p, e in zip(pairs, est):
+        if take and sum(est[:len(take)]) + e > budget:
             break
-    return {"value": round(done_bytes / spent / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"{slices} of {spec.batch * spec.num_kv_heads} (sequence, KV head) slices, "
-                      f"{slices * G} query heads, fp64 numpy, BLAS limited to 1 thread; {spent:.1f} s",
-            "seconds_per_step_extrapolated": round(spent / slices * spec.batch * spec.num_kv_heads, 2)}
+        take.append(p)
+    workers = min(workers, len(take))
+    # fresh interpreters (spawn): the workers hold nothing of this process's GPU state
+    ctx = mp.get_context("spawn")
+    barrier = ctx.Barrier(workers, timeout=600)
+    chunks = [take[i::workers] for i in range(workers)]
+    with ctx.Pool(workers, initializer=_init_worker, initargs=(barrier,)) as pool:
+        res = pool.map(_oracle_worker, [(spec.name, None, q, lens, c) for c in chunks], chunksize=1)
+    t0 = min(r[0] for r in res)
+    t1 = max(r[1] for r in res)
+    done = sum(r[2] for r in res)
+    wall = t1 - t0
+    whole = len(take) == len(pairs)
+    return {"value": round(done / wall / 1e9, 4), "unit": "GB/s", "cores": workers, "kind": "oracle",
+            "sample": f"{len(take)} of {len(pairs)} (sequence, KV head) slices ({'the whole step' if whole else 'first slices'}), "
+                      f"{len(take) * G} query heads, fp64 numpy, {workers} worker processes x 1 BLAS thread; "
+                      f"wall {wall:.2f} s",
+            "seconds_per_step": round(wall * len(pairs) / len(take), 3),
+            "host": {"cpu_model": model, "logical_cpus": logical, "usable_cpus": usable}}
 
 
 def quantize_bytes(spec, tokens_per_head):
@@ -192,11 +262,16 @@ def main():
         return bench_quantize(args, spec)
     q = synth.make_query(spec)
     lens = spec.seq_lens()
+    alg = synth.algorithmic_bytes(spec, lens) + 2 * 2 * spec.batch * spec.num_kv_heads * args.window * spec.head_dim
     t_stage = time.perf_counter()
     base = staging.stage((spec.batch, spec.num_q_heads, spec.num_kv_heads, spec.max_seq_len, spec.head_dim),
                          spec.bits, q, lens, lambda b: synth.make_sequence(spec, b), synth.full_scale_shapes(spec),
                          device=dev_name)
-    copies = [base] + [{k: v.clone() for k, v in base.items()} for _ in range(max(1, args.copies) - 1)]
+    # cold cache: the steps rotate over independent copies of the whole cache, at least 1 GiB of
+    # them, so a copy was last touched at least 1 GiB of reads ago (the Infinity Cache holds 256 MB)
+    cache_bytes = sum(v.numel() * v.element_size() for v in base.values())
+    n_copies = args.copies if args.copies > 0 else max(2, -(-(1 << 30) // cache_bytes))
+    copies = [base] + [{k: v.clone() for k, v in base.items()} for _ in range(n_copies - 1)]
     torch.cuda.synchronize()
     stage_s = time.perf_counter() - t_stage
     layout = fos.layout_bits(spec.k_layout, spec.v_layout)
@@ -206,23 +281,16 @@ def main():
     outs = [(torch.empty((spec.batch, spec.num_q_heads, spec.head_dim), dtype=torch.bfloat16, device=dev_name),
              torch.empty((spec.batch, spec.num_q_heads), dtype=torch.float32, device=dev_name)) for _ in copies]
     # one prepared call per cache copy: arguments checked and marshalled once, a step is one C call
-    if args.window > 0:  # decode with a full-precision window: one call = window kernel + decode kernel
+    window = [None] * len(copies)
+    if args.window > 0:  # decode beside a full-precision window: still one launch per step
         win = synth.make_window(0, spec.batch, spec.num_kv_heads, args.window, [args.window] * spec.batch,
                                 spec.head_dim)
-        wins = [(torch.from_numpy(win["k"]).to(torch.bfloat16).to(dev_name),
-                 torch.from_numpy(win["v"]).to(torch.bfloat16).to(dev_name),
-                 torch.from_numpy(win["lens"]).to(dev_name)) for _ in copies]
-        calls = [fos.prepare_decode(spec.bits, c["q"], c["packed_k"], c["packed_v"], c["k_scale"], c["k_zero"],
-                                    c["v_scale"], c["v_zero"], c["seq_lens"], layout, spec.group, out=o, lse=l,
-                                    window=w)
-                 for c, (o, l), w in zip(copies, outs, wins)]
-    else:
-        calls = [fos.prepare_decode(spec.bits, c["q"], c["packed_k"], c["packed_v"], c["k_scale"], c["k_zero"],
-                                    c["v_scale"], c["v_zero"], c["seq_lens"], layout, spec.group, out=o, lse=l)
-                 for c, (o, l) in zip(copies, outs)]
-
-    def step(k):
-        calls[k % len(calls)]()
+        window = [(torch.from_numpy(win["k"]).to(torch.bfloat16).to(dev_name),
+                   torch.from_numpy(win["v"]).to(torch.bfloat16).to(dev_name),
+                   torch.from_numpy(win["lens"]).to(dev_name)) for _ in copies]
+    calls = [fos.prepare_decode(spec.bits, c["q"], c["packed_k"], c["packed_v"], c["k_scale"], c["k_zero"],
+                                c["v_scale"], c["v_zero"], c["seq_lens"], layout, spec.group, out=o, lse=l, window=w)
+             for c, (o, l), w in zip(copies, outs, window)]
 
     if args.calibrate_copy_mib > 0:  # a plain copy of known size, for HBM byte counters
         n = args.calibrate_copy_mib << 20
@@ -232,43 +300,44 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
-    for k in range(args.warmup):
-        step(k)
-    torch.cuda.synchronize()
-    stream = torch.cuda.current_stream()
-    # whole-job throughput: exactly `steps` steps back to back, nothing else on the stream
-    t0 = time.perf_counter()
-    for k in range(args.steps):
-        step(k)
-    enqueued = time.perf_counter() - t0
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    # kernel durations, in a second pass of as many steps: events recorded by each decode
-    # dispatch itself (hipExtLaunchKernel), the span rocprofv3's kernel trace reports;
-    # recorded once first so that they exist
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
-    for a, b in ev:
-        a.record(stream)
-        b.record(stream)
-    torch.cuda.synchronize()
-    for k in range(args.steps):
-        if args.window > 0:  # two kernels per step: stream events around both
-            ev[k][0].record(stream)
-            step(k)
-            ev[k][1].record(stream)
-        else:
+
+    def timed_pass(steps, first):
+        """`steps` steps back to back; each decode dispatch records its own start
+        and stop events (hipExtLaunchKernel), the span rocprofv3's kernel trace
+        reports.  Returns (wall seconds between the two synchronisations, kernel ms)."""
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+        stream = torch.cuda.current_stream()
+        for a, b in ev:  # recorded once so that the events exist
+            a.record(stream)
+            b.record(stream)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for k in range(steps):
             fos.foscar_record_next_launch(ev[k][0], ev[k][1])
-            step(k)
+            calls[(first + k) % len(calls)]()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        return wall, [a.elapsed_time(b) for a, b in ev]
+
+    def pct(xs, p):
+        xs = sorted(xs)
+        return xs[min(len(xs) - 1, max(0, int(round(p / 100 * (len(xs) - 1)))))]
+
+    for k in range(args.warmup):
+        calls[k % len(calls)]()
     torch.cuda.synchronize()
-    kernel_ms = [a.elapsed_time(b) for a, b in ev]
+    # the reported pass: exactly `steps` steps; ms_per_step and the roofline both come from it
+    wall, kernel_ms = timed_pass(args.steps, args.warmup)
+    # a sustained pass right after it (clock and power settle under continuous HBM load)
+    sus_wall, sus_ms = timed_pass(args.sustain, args.warmup + args.steps) if args.sustain > 0 else (None, None)
     if args.dump_steps:
         print("kernel us per step:", " ".join(f"{x * 1e3:.1f}" for x in kernel_ms), file=sys.stderr)
     ms_per_step = wall * 1e3 / args.steps
-    alg = synth.algorithmic_bytes(spec, lens) + 2 * 2 * spec.batch * spec.num_kv_heads * args.window * spec.head_dim
     value = alg / (ms_per_step * 1e-3) / 1e9
     k_avg = sum(kernel_ms) / len(kernel_ms)
     achieved = alg / (k_avg * 1e-3) / 1e9
     assert torch.isfinite(outs[0][0].float()).all(), "non-finite output"
+    cold = n_copies * cache_bytes >= (1 << 30)
 
     line = {
         "metric": METRIC,
@@ -283,25 +352,38 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f16",
-        "arith": "2-bit codes -> fp16 matrix-core operands (magic-exponent AND-OR), fp32 accumulation, bf16 out",
+        "dtype": "f16" if _ARITH == "f16" else "fp8/fp4",
+        "arith": _ARITH_TEXT,
         "data": "synthetic",
+        "cache": ("cold: " if cold else "WARM (rotation under 1 GiB): ")
+                 + f"{n_copies} copies x {cache_bytes / 1e6:.1f} MB rotated over the steps",
         "config": {"workload": f"{spec.name}: batch {spec.batch}, {spec.num_q_heads} query heads / "
                                f"{spec.num_kv_heads} KV heads, head_dim {spec.head_dim}, {spec.max_seq_len} tokens, "
                                f"INT{spec.bits}, K {spec.k_layout}-wise / V {spec.v_layout}-wise, group {spec.group}",
                    "global_batch": spec.batch, "seq_len": spec.max_seq_len, "bits": spec.bits,
                    "k_layout": spec.k_layout, "v_layout": spec.v_layout, "group": spec.group,
-                   "splits": splits, "chunk": chunk, "cache_copies": len(copies), "window_tokens": args.window,
+                   "splits": splits, "chunk": chunk, "cache_copies": n_copies, "window_tokens": args.window,
                    "algorithmic_bytes_per_step": alg},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic_per_launch(spec.name),
                      "kernel": "split_decode (one launch per step)", "kernel_us_avg": round(k_avg * 1e3, 2),
-                     "kernel_us_median": round(sorted(kernel_ms)[len(kernel_ms) // 2] * 1e3, 2),
+                     "kernel_us_p10": round(pct(kernel_ms, 10) * 1e3, 2),
+                     "kernel_us_p50": round(pct(kernel_ms, 50) * 1e3, 2),
+                     "kernel_us_p90": round(pct(kernel_ms, 90) * 1e3, 2),
                      "kernel_us_min": round(min(kernel_ms) * 1e3, 2),
-                     "host_enqueue_us_per_step": round(enqueued * 1e6 / args.steps, 2)},
+                     "timing": "HIP events recorded by each timed decode dispatch of the same pass as ms_per_step"},
         "staging_s": round(stage_s, 1),
         "kernel_source_sha": kernel_sha(),
     }
+    if sus_wall is not None:
+        sus_ms_step = sus_wall * 1e3 / args.sustain
+        line["sustained"] = {"steps": args.sustain, "ms_per_step": round(sus_ms_step, 5),
+                             "value": round(alg / (sus_ms_step * 1e-3) / 1e9, 2),
+                             "kernel_us_avg": round(sum(sus_ms) / len(sus_ms) * 1e3, 2),
+                             "kernel_us_p10": round(pct(sus_ms, 10) * 1e3, 2),
+                             "kernel_us_p50": round(pct(sus_ms, 50) * 1e3, 2),
+                             "kernel_us_p90": round(pct(sus_ms, 90) * 1e3, 2),
+                             "ratio_to_reported": round(sus_ms_step / ms_per_step, 4)}
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(spec, q, lens, args.cpu_seconds)
     print(json.dumps(line), flush=True)

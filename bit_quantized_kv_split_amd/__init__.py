@@ -76,6 +76,44 @@ def _require(t, name, dtype, device):
         raise ValueError(f"{name} must be contiguous")
 
 
+def _shape(t, name, expect):
+    if tuple(t.shape) != tuple(expect):
+        raise ValueError(f"{name} must have shape {tuple(expect)}, got {tuple(t.shape)}")
+
+
+def _scale_shape(side_channel, B, Hkv, Tcap, D, group):
+    """Shape of one side's fp16 scales / offsets (include/foscar.h): token-wise
+    [B][Hkv][Tcap][D/g], channel-wise [B][Hkv][Tcap/g][D].  None when the
+    group does not divide the axis (the C interface rejects that call)."""
+    if group <= 0:
+        return None
+    if side_channel:
+        return (B, Hkv, Tcap // group, D) if Tcap % group == 0 else None
+    return (B, Hkv, Tcap, D // group) if D % group == 0 else None
+
+
+def _check_cache(bits, packed_k, packed_v, k_scale, k_zero, v_scale, v_zero, layout, group, B, D):
+    """Every cache tensor against the header's shapes for (bits, layout, group),
+    derived from packed_k's [B][Hkv][Tcap] and the head dimension D; a cache of
+    another bit width or layout fails here, before any launch."""
+    if packed_k.dim() != 4:
+        raise ValueError("packed_k must be [B, Hkv, Tcap, D*bits/32]")
+    Hkv, Tcap = int(packed_k.shape[1]), int(packed_k.shape[2])
+    E = 32 // bits
+    if D % E or Tcap % E:
+        raise ValueError(f"head_dim {D} and max_seq_len {Tcap} must be multiples of {E} for {bits}-bit codes")
+    _shape(packed_k, "packed_k", (B, Hkv, Tcap, D // E))
+    _shape(packed_v, "packed_v", (B, Hkv, Tcap // E, D))
+    for side_channel, names, ts in ((layout & FOSCAR_K_CHANNEL, ("k_scale", "k_zero"), (k_scale, k_zero)),
+                                    (layout & FOSCAR_V_CHANNEL, ("v_scale", "v_zero"), (v_scale, v_zero))):
+        expect = _scale_shape(bool(side_channel), B, Hkv, Tcap, D, int(group))
+        if expect is None:
+            raise ValueError(f"group {group} does not divide the grouped axis (max_seq_len {Tcap}, head_dim {D})")
+        for n, t in zip(names, ts):
+            _shape(t, n, expect)
+    return Hkv, Tcap
+
+
 class DecodeCall:
     """One decode step with its arguments checked and marshalled once.
 
@@ -114,14 +152,19 @@ def prepare_decode(bits, q, packed_k, packed_v, k_scale, k_zero, v_scale, v_zero
     for name, t in (("k_scale", k_scale), ("k_zero", k_zero), ("v_scale", v_scale), ("v_zero", v_zero)):
         _require(t, name, torch.float16, dev)
     _require(seq_lens, "seq_lens", torch.int32, dev)
-    B, Hq, D = q.shape
-    Hkv, Tcap = packed_k.shape[1], packed_k.shape[2]
+    if q.dim() != 3:
+        raise ValueError("q must be [B, Hq, D]")
+    B, Hq, D = (int(x) for x in q.shape)
+    Hkv, Tcap = _check_cache(bits, packed_k, packed_v, k_scale, k_zero, v_scale, v_zero, int(layout), group, B, D)
+    _shape(seq_lens, "seq_lens", (B,))
     if out is None:
         out = torch.empty((B, Hq, D), dtype=torch.bfloat16, device=dev)
     if lse is None:
         lse = torch.empty((B, Hq), dtype=torch.float32, device=dev)
     _require(out, "out", torch.bfloat16, dev)
     _require(lse, "lse", torch.float32, dev)
+    _shape(out, "out", (B, Hq, D))
+    _shape(lse, "lse", (B, Hq))
     dims = make_dims(B, Hq, Hkv, D, Tcap, sm_scale)
     call = DecodeCall()
     call._fn = lib.foscar_decode_int2 if bits == 2 else lib.foscar_decode_int4
@@ -215,10 +258,14 @@ def _quantize(bits, k_src, v_src, start, count, packed_k, packed_v, k_scale, k_z
         _require(t, name, torch.int32, dev)
     for name, t in (("k_scale", k_scale), ("k_zero", k_zero), ("v_scale", v_scale), ("v_zero", v_zero)):
         _require(t, name, torch.float16, dev)
-    B, Hkv, N, D = k_src.shape
-    Tcap = packed_k.shape[2]
-    if packed_k.shape[:2] != (B, Hkv) or start.numel() != B or count.numel() != B:
-        raise ValueError("cache, sources, start and count disagree on [B, Hkv]")
+    B, Hkv, N, D = (int(x) for x in k_src.shape)
+    if bits not in (2, 4):
+        raise ValueError(f"bits must be 2 or 4, got {bits}")
+    if packed_k.dim() != 4 or tuple(packed_k.shape[:2]) != (B, Hkv):
+        raise ValueError("cache and sources disagree on [B, Hkv]")
+    _, Tcap = _check_cache(bits, packed_k, packed_v, k_scale, k_zero, v_scale, v_zero, int(layout), group, B, D)
+    _shape(start, "start", (B,))
+    _shape(count, "count", (B,))
     dims = make_dims(B, Hkv, Hkv, D, Tcap)
     fn = lib.foscar_quantize_int2 if bits == 2 else lib.foscar_quantize_int4
     with torch.cuda.device(dev):

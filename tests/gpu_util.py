@@ -1,6 +1,5 @@
 """Helpers shared by the GPU tests: stage a synthetic workload on the device,
 run the HIP decode through the C interface, compute oracle rows, compare."""
-import math
 import os
 
 import numpy as np
@@ -8,13 +7,11 @@ import numpy as np
 import oracle
 import synth
 
-# Output bar, elementwise: |out - O| <= ATOL * max(1, rms_c) + RTOL_BF16 * |O|.
-# ATOL is the 2e-3 kernel-error scale for unit-scale values; rms_c is the RMS
-# of the dequantised value channel c over the sequence, so the bar keeps the
-# same relative meaning when channel scales reach 10 (a floating-point decode
-# kernel's error is proportional to the magnitude of the values it averages).
-# RTOL_BF16 = 2^-8 covers the round-to-nearest of the bf16 output (half an ulp
-# is at most 2^-9 relative) with a factor 2 margin.
+# Output bar, elementwise: |out - O| <= ATOL + RTOL_BF16 * |O|.  ATOL = 2e-3 is
+# the target's absolute kernel error; RTOL_BF16 = 2^-8 covers the
+# round-to-nearest of the bf16 output (half an ulp is at most 2^-9 relative)
+# with a factor 2 margin, since a bf16 output cannot hold 2e-3 absolute once
+# |O| > 0.5.
 ATOL = 2e-3
 RTOL_BF16 = 2.0 ** -8
 LSE_ATOL = 2e-3
@@ -39,22 +36,10 @@ def run(spec, dev, sm_scale=0.0):
     return out.float().cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64)
 
 
-def value_rms(spec, head, t):
-    """RMS over the first t tokens of each dequantised value channel."""
-    if t == 0:
-        return np.zeros(spec.head_dim)
-    if spec.v_layout == "token":
-        s, z = head["v_scale"][:t], head["v_zero"][:t]
-    else:
-        s, z = head["v_scale"][: -(-t // spec.group)], head["v_zero"][: -(-t // spec.group)]
-    v = oracle.dequantize(head["v_codes"][:t], s, z, spec.v_layout, spec.group)
-    return np.sqrt(np.mean(v * v, axis=0))
-
-
-def oracle_rows(spec, rows, q, lens, poison=False, with_scale=False):
+def oracle_rows(spec, rows, q, lens, poison=False):
     """Oracle output for (b, query head) rows, regenerating only the needed (b, KV head) slices."""
     G = spec.num_q_heads // spec.num_kv_heads
-    outs, lses, scales = [], [], []
+    outs, lses = [], []
     for (b, i) in rows:
         h = i // G
         head = synth.make_head(spec, b, h, seq_len=int(lens[b]), poison=poison)
@@ -65,29 +50,41 @@ def oracle_rows(spec, rows, q, lens, poison=False, with_scale=False):
                                   sm_scale=spec.sm_scale)
         outs.append(o[0])
         lses.append(l[0])
-        scales.append(value_rms(spec, head, int(lens[b])))
-    if with_scale:
-        return np.array(outs), np.array(lses), np.array(scales)
     return np.array(outs), np.array(lses)
 
 
 def oracle_all(spec, q, lens, poison=False):
-    """(out, lse, value rms) for every row; out and rms are [B, Hq, D]."""
+    """(out, lse) for every row: out [B, Hq, D], lse [B, Hq]."""
     rows = [(b, i) for b in range(spec.batch) for i in range(spec.num_q_heads)]
-    o, l, sc = oracle_rows(spec, rows, q, lens, poison, with_scale=True)
+    o, l = oracle_rows(spec, rows, q, lens, poison)
     B, Hq = spec.batch, spec.num_q_heads
-    return o.reshape(B, Hq, -1), l.reshape(B, Hq), sc.reshape(B, Hq, -1)
+    return o.reshape(B, Hq, -1), l.reshape(B, Hq)
 
 
-def check(out, lse, ref_out, ref_lse, what="", vscale=None):
-    err = np.abs(out - ref_out)
-    scale = 1.0 if vscale is None else np.maximum(1.0, vscale)
-    bound = ATOL * scale + RTOL_BF16 * np.abs(ref_out)
-    worst = np.unravel_index(np.argmax(err - bound), err.shape)
+def _log_parity(what, err, ref_out, bound, lse, ref_lse):
+    """Append one JSON line per comparison to $FOSCAR_PARITY_LOG: max error,
+    max |O| and max error/bound, so the suite's margin against the bar is on
+    record."""
     log = os.environ.get("FOSCAR_PARITY_LOG")
-    if log:
-        with open(log, "a") as f:
-            f.write(f"{what}: max|err| {err.max():.3e}  max err/bound {(err / bound).max():.3f}\n")
+    if not log:
+        return
+    import json
+    fin = np.isfinite(ref_lse)
+    lerr = float(np.abs(lse[fin] - ref_lse[fin]).max()) if fin.any() else 0.0
+    rec = {"test": os.environ.get("PYTEST_CURRENT_TEST", "").split(" ")[0], "what": what,
+           "max_err": float(err.max()) if err.size else 0.0,
+           "max_abs_out": float(np.abs(ref_out).max()) if ref_out.size else 0.0,
+           "ratio": float((err / bound).max()) if err.size else 0.0,
+           "lse_err": lerr}
+    with open(log, "a") as f:
+        f.write(json.dumps(rec) + "\n")
+
+
+def check(out, lse, ref_out, ref_lse, what=""):
+    err = np.abs(out - ref_out)
+    bound = ATOL + RTOL_BF16 * np.abs(ref_out)
+    worst = np.unravel_index(np.argmax(err - bound), err.shape)
+    _log_parity(what, err, ref_out, bound, lse, ref_lse)
     assert np.all(np.isfinite(out)), f"{what}: non-finite output"
     assert np.all(err <= bound), (f"{what}: out error {err[worst]:.3e} > bound {bound[worst]:.3e} at {worst} "
                                   f"(got {out[worst]:.6f}, oracle {ref_out[worst]:.6f}); max err {err.max():.3e}")

@@ -10,7 +10,7 @@ import numpy as np
 import pytest
 
 import synth
-from gpu_util import assert_persistent, check, oracle_all, oracle_rows, persistent_spec, run, stage_spec, value_rms
+from gpu_util import assert_persistent, check, oracle_all, oracle_rows, persistent_spec, run, stage_spec
 
 pytestmark = pytest.mark.gpu
 
@@ -23,8 +23,8 @@ def test_c1_tiny_full_size():
     spec = synth.SPECS["c1_tiny_int2"]
     dev, q, lens = stage_spec(spec)
     out, lse = run(spec, dev)
-    ro, rl, vsc = oracle_all(spec, q, lens)
-    check(out, lse, ro, rl, "c1", vsc)
+    ro, rl = oracle_all(spec, q, lens)
+    check(out, lse, ro, rl, "c1")
 
 
 MATRIX = [(bits, kl, vl, g) for bits in (2, 4) for kl in ("token", "channel") for vl in ("token", "channel")
@@ -39,8 +39,8 @@ def test_layout_matrix(bits, kl, vl, g):
                       lens=(768, 517, 130), channel_std_logu=std)
     dev, q, lens = stage_spec(spec)
     out, lse = run(spec, dev)
-    ro, rl, vsc = oracle_all(spec, q, lens)
-    check(out, lse, ro, rl, spec.name, vsc)
+    ro, rl = oracle_all(spec, q, lens)
+    check(out, lse, ro, rl, spec.name)
 
 
 SCALED = [
@@ -58,8 +58,8 @@ def test_scaled_workloads(spec):
     """The five workloads' value recipes at sizes the oracle finishes in seconds."""
     dev, q, lens = stage_spec(spec)
     out, lse = run(spec, dev)
-    ro, rl, vsc = oracle_all(spec, q, lens)
-    check(out, lse, ro, rl, spec.name, vsc)
+    ro, rl = oracle_all(spec, q, lens)
+    check(out, lse, ro, rl, spec.name)
 
 
 EDGE_LENS = (0, 1, 2, 63, 64, 65, 127, 128, 129, 255, 256)
@@ -67,7 +67,8 @@ EDGE_LENS = (0, 1, 2, 63, 64, 65, 127, 128, 129, 255, 256)
 
 @pytest.mark.parametrize("bits", [2, 4])
 @pytest.mark.parametrize("kl,vl,g", [("token", "token", 128), ("channel", "channel", 128), ("token", "channel", 32),
-                                     ("channel", "token", 64)])
+                                     ("channel", "token", 64), ("channel", "token", 32), ("channel", "channel", 32),
+                                     ("channel", "channel", 64)])
 def test_edge_lengths_and_poisoned_padding(bits, kl, vl, g):
     """Empty, single-token, tile-boundary and group-boundary lengths; padding
     past each length holds random codes and NaN scales/offsets."""
@@ -75,8 +76,8 @@ def test_edge_lengths_and_poisoned_padding(bits, kl, vl, g):
                       lens=EDGE_LENS)
     dev, q, lens = stage_spec(spec, poison=True)
     out, lse = run(spec, dev)
-    ro, rl, vsc = oracle_all(spec, q, lens, poison=True)
-    check(out, lse, ro, rl, spec.name, vsc)
+    ro, rl = oracle_all(spec, q, lens, poison=True)
+    check(out, lse, ro, rl, spec.name)
     assert np.all(out[0] == 0) and np.all(np.isneginf(lse[0]))
 
 
@@ -85,8 +86,8 @@ def test_gqa_ratios(G):
     spec = synth.Spec(f"gqa_{G}", 13, 2, "token", "channel", 64, 2, 3 * G, 3, 128, 512, lens=(512, 300))
     dev, q, lens = stage_spec(spec)
     out, lse = run(spec, dev)
-    ro, rl, vsc = oracle_all(spec, q, lens)
-    check(out, lse, ro, rl, spec.name, vsc)
+    ro, rl = oracle_all(spec, q, lens)
+    check(out, lse, ro, rl, spec.name)
 
 
 @pytest.mark.parametrize("splits", ["1", "2", "7", "17", "32", "auto"])
@@ -98,8 +99,8 @@ def test_split_count_invariance(splits, monkeypatch):
         monkeypatch.delenv("FOSCAR_SPLITS", raising=False)
     dev, q, lens = stage_spec(spec)
     out, lse = run(spec, dev)
-    ro, rl, vsc = oracle_all(spec, q, lens)
-    check(out, lse, ro, rl, f"splits={splits}", vsc)
+    ro, rl = oracle_all(spec, q, lens)
+    check(out, lse, ro, rl, f"splits={splits}")
 
 
 def test_many_ranges(monkeypatch):
@@ -112,8 +113,8 @@ def test_many_ranges(monkeypatch):
     dims = fos.make_dims(spec.batch, spec.num_q_heads, spec.num_kv_heads, spec.head_dim, spec.max_seq_len)
     assert fos.foscar_split_plan(dims, spec.bits, fos.layout_bits(spec.k_layout, spec.v_layout), spec.group) == (512, 128)
     out, lse = run(spec, dev)
-    ro, rl, vsc = oracle_all(spec, q, lens)
-    check(out, lse, ro, rl, "512 ranges", vsc)
+    ro, rl = oracle_all(spec, q, lens)
+    check(out, lse, ro, rl, "512 ranges")
 
 
 def test_workspace_reuse_across_shapes(monkeypatch):
@@ -126,15 +127,15 @@ def test_workspace_reuse_across_shapes(monkeypatch):
     monkeypatch.setenv("FOSCAR_SPLITS", "256")
     dev, q, lens = stage_spec(first)
     out, lse = run(first, dev)
-    ro, rl, vsc = oracle_all(first, q, lens)
-    check(out, lse, ro, rl, "many ranges", vsc)
+    ro, rl = oracle_all(first, q, lens)
+    check(out, lse, ro, rl, "many ranges")
     second = _spec("c2_paper_int2", batch=16, num_q_heads=32, num_kv_heads=8, max_seq_len=512)
     monkeypatch.setenv("FOSCAR_SPLITS", "2")
     dev, q, lens = stage_spec(second)
     for _ in range(2):
         out, lse = run(second, dev)
-        ro, rl, vsc = oracle_all(second, q, lens)
-        check(out, lse, ro, rl, "many pairs after many ranges", vsc)
+        ro, rl = oracle_all(second, q, lens)
+        check(out, lse, ro, rl, "many pairs after many ranges")
 
 
 FULL = ["c2_paper_int2", "c2_paper_int4", "c3_long_int2", "c4_channel_int2", "c4_channel_int4",
@@ -151,9 +152,9 @@ def test_full_size_sampled_rows(name):
     rng = np.random.default_rng(7)
     rows = [(0, 0), (spec.batch - 1, spec.num_q_heads - 1)]
     rows += [(int(rng.integers(spec.batch)), int(rng.integers(spec.num_q_heads))) for _ in range(4)]
-    ro, rl, vsc = oracle_rows(spec, rows, q, lens, with_scale=True)
+    ro, rl = oracle_rows(spec, rows, q, lens)
     for n, (b, i) in enumerate(rows):
-        check(out[b, i][None], lse[b, i][None], ro[n][None], rl[n][None], f"{name} row {(b, i)}", vsc[n][None])
+        check(out[b, i][None], lse[b, i][None], ro[n][None], rl[n][None], f"{name} row {(b, i)}")
     assert np.all(np.isfinite(out))
 
 
@@ -170,7 +171,6 @@ def test_persistent_work_order_ragged_with_empty_sequences():
     G = spec.num_q_heads // spec.num_kv_heads
     ro = np.zeros((spec.batch, spec.num_q_heads, spec.head_dim))
     rl = np.zeros((spec.batch, spec.num_q_heads))
-    vsc = np.zeros_like(ro)
     for b in range(spec.batch):
         for h in range(spec.num_kv_heads):
             head = synth.make_head(spec, b, h, seq_len=int(lens_np[b]), poison=True)
@@ -180,10 +180,9 @@ def test_persistent_work_order_ragged_with_empty_sequences():
             o, l = oracle.decode_rows(w, [(0, i) for i in range(G)], k_layout=spec.k_layout, v_layout=spec.v_layout,
                                       group=spec.group, sm_scale=spec.sm_scale)
             ro[b, h * G:(h + 1) * G], rl[b, h * G:(h + 1) * G] = o, l
-            vsc[b, h * G:(h + 1) * G] = value_rms(spec, head, int(lens_np[b]))
     for k in range(2):
         out, lse = run(spec, dev)
-        check(out, lse, ro, rl, f"persistent ragged call {k}", vsc)
+        check(out, lse, ro, rl, f"persistent ragged call {k}")
 
 
 @pytest.mark.parametrize("G", [1, 2, 3])
@@ -197,5 +196,5 @@ def test_gqa_ratios_through_the_merge(G, splits, monkeypatch):
     monkeypatch.setenv("FOSCAR_SPLITS", splits)
     dev, q, lens = stage_spec(spec)
     out, lse = run(spec, dev)
-    ro, rl, vsc = oracle_all(spec, q, lens)
-    check(out, lse, ro, rl, f"{spec.name} splits={splits}", vsc)
+    ro, rl = oracle_all(spec, q, lens)
+    check(out, lse, ro, rl, f"{spec.name} splits={splits}")

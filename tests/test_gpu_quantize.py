@@ -12,7 +12,7 @@ import pytest
 import oracle
 import oracle.quantize as oq
 import synth
-from gpu_util import check, value_rms
+from gpu_util import check
 
 pytestmark = pytest.mark.gpu
 
@@ -187,10 +187,5 @@ def test_quantize_then_decode(bits, kl, vl):
          "k_scale": exp["k_scale"], "k_zero": exp["k_zero"], "v_scale": exp["v_scale"], "v_zero": exp["v_zero"],
          "seq_lens": lens}
     ro, rl = oracle.decode(w, k_layout=kl, v_layout=vl, group=g, sm_scale=1 / np.sqrt(D))
-    spec = synth.SPECS["c1_tiny_int2"].replace(v_layout=vl, group=g)
-    G = Hq // H
-    vsc = np.stack([value_rms(spec, {"v_codes": w["v_codes"][b, i // G], "v_scale": w["v_scale"][b, i // G],
-                                     "v_zero": w["v_zero"][b, i // G]}, int(lens[b]))
-                    for b in range(B) for i in range(Hq)]).reshape(B, Hq, D)
     check(out.float().cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64), ro, rl,
-          f"quantise+decode int{bits} {kl}/{vl}", vsc)
+          f"quantise+decode int{bits} {kl}/{vl}")

@@ -56,7 +56,7 @@ def test_append_window_quantise_decode_loop(bits, kl, vl):
         rows = [(b, i) for b in range(B) for i in range(Hq)]
         ro, rl = oracle.decode_window_rows(w, win, rows, k_layout=kl, v_layout=vl, group=g, sm_scale=D ** -0.5)
         check(out.float().cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64),
-              ro.reshape(B, Hq, D), rl.reshape(B, Hq), f"step {t} (cache {T}, window {wl})", np.full((B, Hq, D), 2.0))
+              ro.reshape(B, Hq, D), rl.reshape(B, Hq), f"step {t} (cache {T}, window {wl})")
         if wl == g:  # the window holds a whole group: quantise it into the cache, empty the window
             start = torch.full((B,), T, dtype=torch.int32, device=dev)
             count = torch.full((B,), g, dtype=torch.int32, device=dev)
