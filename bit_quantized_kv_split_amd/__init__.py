@@ -18,6 +18,7 @@ FOSCAR_EINVAL = -1
 FOSCAR_EUNSUPPORTED = -2
 FOSCAR_EHIP = -3
 FOSCAR_ENOMEM = -4
+FOSCAR_ESCRATCH = -5
 FOSCAR_K_TOKEN = 0
 FOSCAR_K_CHANNEL = 1
 FOSCAR_V_TOKEN = 0
@@ -39,7 +40,7 @@ class FoscarError(RuntimeError):
 
 def _check(rc, where):
     if rc != FOSCAR_OK:
-        if rc in (FOSCAR_EINVAL, FOSCAR_EUNSUPPORTED):
+        if rc in (FOSCAR_EINVAL, FOSCAR_EUNSUPPORTED, FOSCAR_ESCRATCH):
             raise ValueError(f"{where}: {_lib.load().foscar_strerror(rc).decode()} (code {rc})")
         raise FoscarError(rc, where)
 
@@ -138,12 +139,15 @@ class DecodeCall:
 
 
 def prepare_decode(bits, q, packed_k, packed_v, k_scale, k_zero, v_scale, v_zero, seq_lens, layout, group,
-                   out=None, lse=None, sm_scale=0.0, stream=None, window=None):
+                   out=None, lse=None, sm_scale=0.0, stream=None, window=None, noalloc=False):
     """Check and marshal a decode step (arguments as foscar_decode_int2/4); returns a DecodeCall.
-    ``window`` = (win_k, win_v, win_lens) marshals foscar_decode_window_int2/4 instead."""
+    ``window`` = (win_k, win_v, win_lens) marshals foscar_decode_window_int2/4 instead;
+    ``noalloc`` marshals foscar_decode_noalloc (out and lse must then be given)."""
     import torch
     if bits not in (2, 4):
         raise ValueError(f"bits must be 2 or 4, got {bits}")
+    if noalloc and (out is None or lse is None or window is not None):
+        raise ValueError("foscar_decode_noalloc takes caller-provided out and lse, and no window")
     lib = _lib.load()
     dev = q.device
     _require(q, "q", torch.bfloat16, dev)
@@ -173,6 +177,10 @@ def prepare_decode(bits, q, packed_k, packed_v, k_scale, k_zero, v_scale, v_zero
     call._args = (ctypes.byref(dims), _ptr(q), _ptr(packed_k), _ptr(packed_v), _ptr(k_scale), _ptr(k_zero),
                   _ptr(v_scale), _ptr(v_zero), _ptr(seq_lens), int(layout), int(group), _ptr(out), _ptr(lse), st)
     call._name = f"foscar_decode_int{bits}"
+    if noalloc:
+        call._fn = lib.foscar_decode_noalloc
+        call._args = (int(bits),) + call._args
+        call._name = "foscar_decode_noalloc"
     call._dev = dev.index if dev.index is not None else torch.cuda.current_device()
     call.out, call.lse = out, lse
     call._keep = (dims, q, packed_k, packed_v, k_scale, k_zero, v_scale, v_zero, seq_lens)
@@ -209,6 +217,14 @@ def foscar_decode_int4(q, packed_k, packed_v, k_scale, k_zero, v_scale, v_zero, 
     """4-bit decode step; tensors as in include/foscar.h (packed words as int32). Returns (out, lse)."""
     return _decode(4, q, packed_k, packed_v, k_scale, k_zero, v_scale, v_zero, seq_lens, layout, group,
                    out, lse, sm_scale, stream)
+
+
+def foscar_decode_noalloc(bits, q, packed_k, packed_v, k_scale, k_zero, v_scale, v_zero, seq_lens, layout, group,
+                          out, lse, sm_scale=0.0, stream=None):
+    """Decode step that allocates nothing (include/foscar.h): the split workspace is the
+    library's static scratch; out [B, Hq, D] bf16 and lse [B, Hq] fp32 are the caller's."""
+    return prepare_decode(bits, q, packed_k, packed_v, k_scale, k_zero, v_scale, v_zero, seq_lens, layout, group,
+                          out, lse, sm_scale, stream, noalloc=True)()
 
 
 def _decode_window(bits, q, packed_k, packed_v, k_scale, k_zero, v_scale, v_zero, seq_lens, layout, group, win_k,

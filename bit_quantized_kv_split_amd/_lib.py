@@ -11,7 +11,8 @@ LIB_PATH = os.path.join(HERE, "libfoscar.so")
 
 # Names declared in include/foscar.h, in order.
 EXPORTS = [
-    "foscar_decode_int2", "foscar_decode_int4", "foscar_decode_window_int2", "foscar_decode_window_int4",
+    "foscar_decode_int2", "foscar_decode_int4", "foscar_decode_noalloc", "foscar_decode_window_int2",
+    "foscar_decode_window_int4",
     "foscar_quantize_int2", "foscar_quantize_int4", "foscar_pack", "foscar_unpack", "foscar_packed_bytes",
     "foscar_scale_count", "foscar_workspace_reserve", "foscar_release", "foscar_split_plan", "foscar_occupancy",
     "foscar_record_next_launch",
@@ -41,6 +42,8 @@ def load():
         f = getattr(lib, name)
         f.argtypes = [D, P, P, P, P, P, P, P, P, I, I, P, P, P]
         f.restype = I
+    lib.foscar_decode_noalloc.argtypes = [I, D, P, P, P, P, P, P, P, P, I, I, P, P, P]
+    lib.foscar_decode_noalloc.restype = I
     for name in ("foscar_decode_window_int2", "foscar_decode_window_int4"):
         f = getattr(lib, name)
         f.argtypes = [D, P, P, P, P, P, P, P, P, I, I, P, P, P, ctypes.c_int32, P, P, P]

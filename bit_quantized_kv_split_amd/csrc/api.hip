@@ -191,11 +191,21 @@ int get_workspace(size_t cbytes, size_t pbytes, hipStream_t stream, int32_t** co
   return FOSCAR_OK;
 }
 
+// A workspace the caller provides instead of the grow-only one: counters (zero
+// between calls, cbytes bytes at `base`) and partials (the rest, up to `bytes`).
+struct FixedWorkspace {
+  char* base = nullptr;
+  size_t cbytes = 0;
+  size_t bytes = 0;
+};
+
 // win_k == nullptr: no window.  Otherwise win_k, win_v bf16 [B][Hkv][win_cap][D] and win_lens [B].
+// fixed != nullptr: run in that workspace (FOSCAR_ESCRATCH if the call needs more), allocate nothing.
 int decode_common(int bits, const foscar_dims* d, const void* q, const void* pk, const void* pv, const void* ks,
                   const void* kz, const void* vs, const void* vz, const int32_t* seq_lens, int layout, int group,
                   void* out, float* lse, void* stream, bool windowed = false, const void* win_k = nullptr,
-                  const void* win_v = nullptr, const int32_t* win_lens = nullptr, int32_t win_cap = 0) {
+                  const void* win_v = nullptr, const int32_t* win_lens = nullptr, int32_t win_cap = 0,
+                  const FixedWorkspace* fixed = nullptr) {
   const foscar::LaunchEvents ev = g_next_events;  // consumed by this call whether or not it launches
   g_next_events = foscar::LaunchEvents{};
   int rc = check_decode_shape(d, layout, group);
@@ -235,8 +245,15 @@ int decode_common(int bits, const foscar_dims* d, const void* q, const void* pk,
   if (windowed && one_round) plan(d, layout, group, cus, per_cu, &splits, &chunk, win_wgs);
   int32_t* counters = nullptr;
   float* partials = nullptr;
-  rc = get_workspace(counter_bytes(d), partial_bytes(d, splits), (hipStream_t)stream, &counters, &partials);
-  if (rc) return rc;
+  if (fixed) {
+    if (counter_bytes(d) > fixed->cbytes || partial_bytes(d, splits) > fixed->bytes - fixed->cbytes)
+      return FOSCAR_ESCRATCH;
+    counters = (int32_t*)fixed->base;
+    partials = (float*)(fixed->base + fixed->cbytes);
+  } else {
+    rc = get_workspace(counter_bytes(d), partial_bytes(d, splits), (hipStream_t)stream, &counters, &partials);
+    if (rc) return rc;
+  }
 
   const float sm = d->sm_scale > 0.f ? d->sm_scale : 1.0f / sqrtf((float)d->head_dim);
   foscar::SplitArgs sa;
@@ -291,6 +308,49 @@ int decode_common(int bits, const foscar_dims* d, const void* q, const void* pk,
   e = foscar::launch_decode(bits, (layout & FOSCAR_K_CHANNEL) != 0, (layout & FOSCAR_V_CHANNEL) != 0, group,
                             d->batch, d->num_kv_heads, sa, (hipStream_t)stream, ev);
   if (e != hipSuccess) return hip_fail(e);
+  return FOSCAR_OK;
+}
+
+// ---------------------------------------------------------------------------
+// Static scratch of the no-allocation entry point: the split workspace of
+// foscar_decode_noalloc lives in this file-scope device array (one copy per
+// GPU, held until the process ends).  [counters: kScratchCounterBytes][partials].
+// Host code never passes the array's name to a kernel or a copy: it takes the
+// device address from hipGetSymbolAddress once per device (scratch_on).
+// ---------------------------------------------------------------------------
+constexpr size_t kScratchBytes = size_t(32) << 20;        // 32 MiB per GPU
+constexpr size_t kScratchCounterBytes = size_t(64) << 10;  // 16384 counters (B * Hkv + 2)
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+__global__ void zero_words(int32_t* p, int n) {
+  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) p[i] = 0;
+}
+
+std::mutex g_scratch_mutex;
+std::map<int, char*> g_scratch;  // device -> address of its copy of `scratch`
+
+// Address of the current device's scratch; the first call on a device looks it
+// up and clears its counter region with a fill kernel on `stream` (a kernel,
+// not a memset, so that the call may be captured into a graph).
+int scratch_on(hipStream_t stream, char** base) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e);
+  std::lock_guard<std::mutex> lk(g_scratch_mutex);
+  auto it = g_scratch.find(dev);
+  if (it != g_scratch.end()) {
+    *base = it->second;
+    return FOSCAR_OK;
+  }
+  void* ptr = nullptr;
+  e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+  if (e != hipSuccess || !ptr) return hip_fail(e != hipSuccess ? e : hipErrorInvalidSymbol);
+  const int n = (int)(kScratchCounterBytes / sizeof(int32_t));
+  hipLaunchKernelGGL(zero_words, dim3((n + 255) / 256), dim3(256), 0, stream, (int32_t*)ptr, n);
+  e = hipGetLastError();
+  if (e != hipSuccess) return hip_fail(e);
+  g_scratch[dev] = (char*)ptr;
+  *base = (char*)ptr;
   return FOSCAR_OK;
 }
 
@@ -356,6 +416,31 @@ int foscar_decode_window_int4(const foscar_dims* dims, const void* q, const void
                               const int32_t* win_lens, int32_t win_cap, void* out, float* lse, void* stream) {
   return decode_common(4, dims, q, packed_k, packed_v, k_scale, k_zero, v_scale, v_zero, seq_lens, layout, group,
                        out, lse, stream, true, win_k, win_v, win_lens, win_cap);
+}
+
+int foscar_decode_noalloc(int bits, const foscar_dims* dims, const void* q, const void* packed_k,
+                          const void* packed_v, const void* k_scale, const void* k_zero, const void* v_scale,
+                          const void* v_zero, const int32_t* seq_lens, int layout, int group, void* out, float* lse,
+                          void* stream) {
+  if (bits != 2 && bits != 4) return FOSCAR_EINVAL;
+  int rc = check_decode_shape(dims, layout, group);
+  if (rc) return rc;
+  if (dims->batch == 0) return FOSCAR_OK;
+  // sizes the static scratch cannot hold fail before any HIP call: the counters, and the
+  // partials of the smallest plan (one range per pair)
+  if (counter_bytes(dims) > kScratchCounterBytes || partial_bytes(dims, 1) > kScratchBytes - kScratchCounterBytes)
+    return FOSCAR_ESCRATCH;
+  if (!q || !packed_k || !packed_v || !k_scale || !k_zero || !v_scale || !v_zero || !seq_lens || !out)
+    return FOSCAR_EINVAL;
+  char* base = nullptr;
+  rc = scratch_on((hipStream_t)stream, &base);
+  if (rc) return rc;
+  FixedWorkspace ws;
+  ws.base = base;
+  ws.cbytes = kScratchCounterBytes;
+  ws.bytes = kScratchBytes;
+  return decode_common(bits, dims, q, packed_k, packed_v, k_scale, k_zero, v_scale, v_zero, seq_lens, layout, group,
+                       out, lse, stream, false, nullptr, nullptr, nullptr, 0, &ws);
 }
 
 int foscar_quantize_int2(const foscar_dims* dims, const void* k_src, const void* v_src, int32_t src_tokens,
@@ -476,6 +561,7 @@ const char* foscar_strerror(int code) {
     case FOSCAR_EUNSUPPORTED: return "unsupported shape or parameter";
     case FOSCAR_EHIP: return "HIP runtime error";
     case FOSCAR_ENOMEM: return "out of device memory";
+    case FOSCAR_ESCRATCH: return "call needs more than the static scratch of the no-allocation entry point";
   }
   return "unknown error";
 }

@@ -59,6 +59,8 @@ extern "C" {
                                     batch * num_kv_heads > 2^22 */
 #define FOSCAR_EHIP (-3)         /* a HIP call failed; foscar_last_hip_error() has its code */
 #define FOSCAR_ENOMEM (-4)       /* workspace allocation failed */
+#define FOSCAR_ESCRATCH (-5)     /* foscar_decode_noalloc: the call needs more split workspace than the
+                                    library's static scratch holds */
 
 /* Layout bits (OR one K value with one V value).
  * Token-wise group: g consecutive channels of one token share (s, z).
@@ -121,6 +123,31 @@ int foscar_decode_int2(const foscar_dims* dims, const void* q, const void* packe
 int foscar_decode_int4(const foscar_dims* dims, const void* q, const void* packed_k, const void* packed_v,
                        const void* k_scale, const void* k_zero, const void* v_scale, const void* v_zero,
                        const int32_t* seq_lens, int layout, int group, void* out, float* lse, void* stream);
+
+/*
+ * Decode step that allocates nothing, for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid allocation.  Arguments and results as foscar_decode_int2 (bits = 2)
+ * or foscar_decode_int4 (bits = 4), same kernels and split plan; the caller
+ * passes every input and output.
+ *
+ * The split workspace (range counters and partial results) is a static device
+ * array of 32 MiB inside the library, one copy per GPU, held until the process
+ * ends: 64 KiB of counters (batch * num_kv_heads + 2 of them) and the rest for
+ * partials, batch * num_q_heads * (splits + 8) * 129 floats.  A call that needs
+ * more returns FOSCAR_ESCRATCH: before any HIP call when even one range per
+ * (sequence, KV head) does not fit, otherwise after planning, still before
+ * any launch.  No call here allocates or frees device memory; the first call
+ * on a device looks up the array's address and clears its counters with a
+ * small kernel on `stream`.  Every call on a GPU shares that GPU's array:
+ * calls that overlap on one GPU (different streams, or different host
+ * threads) race and must be serialised by the caller; calls on one stream
+ * are ordered and never race.  Each call leaves the counters at zero.
+ */
+int foscar_decode_noalloc(int bits, const foscar_dims* dims, const void* q, const void* packed_k,
+                          const void* packed_v, const void* k_scale, const void* k_zero, const void* v_scale,
+                          const void* v_zero, const int32_t* seq_lens, int layout, int group, void* out, float* lse,
+                          void* stream);
 
 /*
  * Decode step over the quantised cache plus a full-precision window of recent

@@ -187,3 +187,22 @@ def test_misaligned_pointers_are_rejected_before_any_gpu_call(lib):
     assert _decode(lib, _dims(), ptr=0x1008) == -1          # 8-byte aligned only
     assert _quantize(lib, _dims(), ptr=0x1004) == -1
     assert _decode_window(lib, _dims(), ptr=0x1000, win_ptr=0x1002) == -1
+
+
+def _noalloc(lib, dims, bits=2, layout=0, group=128, ptr=1):
+    p = ctypes.c_void_p(ptr) if ptr else None
+    return lib.foscar_decode_noalloc(bits, ctypes.byref(dims) if dims is not None else None, p, p, p, p, p, p, p, p,
+                                     layout, group, p, p, None)
+
+
+def test_noalloc_rejects_before_any_gpu_call(lib):
+    """The no-allocation decode validates like the decode entry points and
+    rejects, before any HIP call, what its static scratch cannot hold."""
+    assert _noalloc(lib, _dims(), bits=3) == -1
+    assert _noalloc(lib, None) == -1
+    assert _noalloc(lib, _dims(head_dim=64)) == -2
+    assert _noalloc(lib, _dims(batch=0), ptr=0) == 0
+    assert _noalloc(lib, _dims(batch=20000, num_q_heads=1, num_kv_heads=1)) == -5   # range counters
+    assert _noalloc(lib, _dims(batch=1024, num_q_heads=32, num_kv_heads=8)) == -5   # partials of one range
+    assert _noalloc(lib, _dims(), ptr=0) == -1
+    assert "static scratch" in lib.foscar_strerror(-5).decode()
