@@ -27,8 +27,16 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "INT2/INT4 decode-attn achieved HBM GB/s (% of 8 TB/s) and µs/step"
-_ARITH = "f16"
-_ARITH_TEXT = "2-bit codes -> fp16 matrix-core operands (magic-exponent AND-OR), fp32 accumulation, bf16 out"
+# what the decode kernel computes in, by key layout
+_ARITH = {
+    "token": ("fp4/fp8 QK^T, f16 PV",
+              "QK^T on the block-scaled matrix cores: key codes as fp4 (INT2) / fp8 (INT4) operands, the query as "
+              "two exact e4m3 terms, fp32 accumulation; PV with value codes as fp16 matrix-core operands "
+              "(magic-exponent AND-OR), fp32 accumulation; bf16 out"),
+    "channel": ("f16",
+                "codes -> fp16 matrix-core operands (magic-exponent AND-OR) for QK^T and PV, fp32 accumulation, "
+                "bf16 out"),
+}
 PEAK_HBM_GBS = 8000.0
 
 
@@ -357,8 +365,8 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f16" if _ARITH == "f16" else "fp8/fp4",
-        "arith": _ARITH_TEXT,
+        "dtype": _ARITH[spec.k_layout][0],
+        "arith": _ARITH[spec.k_layout][1],
         "data": "synthetic",
         "cache": ("cold: " if cold else "WARM (rotation under 1 GiB): ")
                  + f"{n_copies} copies x {cache_bytes / 1e6:.1f} MB rotated over the steps",

@@ -132,6 +132,86 @@ struct Codec<4> {
 };
 
 // ---------------------------------------------------------------------------
+// Key operands of the block-scaled matrix cores (v_mfma_scale_f32_16x16x128_
+// f8f6f4) for token-wise keys.  Facts measured on gfx950 with in-bounds
+// probes (one-hot operands):
+//   * an INT2 code under the mask 0x33333333 is an fp4 (e2m1) nibble 00qq,
+//     exactly q/2; an INT4 code under 0x0F0F0F0F an fp8 (e4m3) byte, exactly
+//     q * 2^-9; the E8M0 operand scale 2 (2^9) restores q.  One AND per
+//     register, a shift for every other one: no per-value convert, no bias;
+//   * K slots: an fp4 operand's lane group g, nibble e meets lane group
+//     2(g%2) + e/16, byte 16(g/2) + e%16 of an 8-bit operand; two 8-bit
+//     operands meet at the same lane group and byte;
+//   * the E8M0 scale of 32-element block kb (supplied by lane group kb of the
+//     scale register) applies to byte b of lane group G of an 8-bit operand
+//     when kb = 2(b/16) + G/2, so per-row scales are the safe form;
+//   * products are summed with about 14 significant bits relative to the
+//     largest product of each group of 8 (and group sums likewise): fine for
+//     query x key code products, whose range is bounded, but not for softmax
+//     weights spanning more than 2^14, so P V stays on the fp16 path.
+// A key tile of 64 tokens is 4 blocks of 16: block j, column n is token
+// 4n + j, so each lane of the result holds one query head's scores for the
+// 4 tokens of one quad, as the fp16 P V path expects.
+// ---------------------------------------------------------------------------
+typedef int v8i __attribute__((ext_vector_type(8)));
+
+template <int BITS>
+struct MxKey;
+template <>
+struct MxKey<2> {
+  static constexpr int FMT = 4;           // fp4 e2m1 (cbsz / blgp code)
+  static constexpr int CODE_SCALE = 128;  // E8M0 2^1: q/2 -> q
+  static constexpr int WPL = 2;           // packed words per lane per block
+  __device__ static __forceinline__ v8i build(const uint32_t* w) {
+    const uint32_t M = 0x33333333u;
+    v8i r;
+    r[0] = (int)(w[0] & M);
+    r[1] = (int)((w[0] >> 2) & M);
+    r[2] = (int)(w[1] & M);
+    r[3] = (int)((w[1] >> 2) & M);
+    r[4] = r[5] = r[6] = r[7] = 0;
+    return r;
+  }
+  // key channel that byte b of lane group G of the query operand meets (lane
+  // group g of the key operand holds channels 32g .. 32g+31 in words 2g, 2g+1)
+  __host__ __device__ static constexpr int chan(int G, int b) {
+    return 64 * (b >> 4) + 16 * G + 4 * (b & 3) + ((b >> 2) & 3);
+  }
+  // lane group G's channels in local order l: 16G + l (l < 16), 64 + 16G + l - 16; byte b is
+  // local value local(b), and the 16-byte chunk i of the local values is chunk quad_index(G, i)
+  // of the query row
+  __host__ __device__ static constexpr int local(int b) { return 16 * (b >> 4) + 4 * (b & 3) + ((b >> 2) & 3); }
+  __host__ __device__ static constexpr int quad_index(int G, int i) { return 2 * G + (i < 2 ? i : 6 + i); }
+};
+template <>
+struct MxKey<4> {
+  static constexpr int FMT = 0;           // fp8 e4m3
+  static constexpr int CODE_SCALE = 136;  // E8M0 2^9: q * 2^-9 -> q
+  static constexpr int WPL = 4;
+  __device__ static __forceinline__ v8i build(const uint32_t* w) {
+    const uint32_t M = 0x0F0F0F0Fu;
+    v8i r;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      r[2 * i] = (int)(w[i] & M);
+      r[2 * i + 1] = (int)((w[i] >> 4) & M);
+    }
+    return r;
+  }
+  __host__ __device__ static constexpr int chan(int G, int b) {
+    return 32 * G + 8 * (b >> 3) + 4 * (b & 1) + ((b >> 1) & 3);
+  }
+  // lane group G's channels in local order l: 32G + l
+  __host__ __device__ static constexpr int local(int b) { return 8 * (b >> 3) + 4 * (b & 1) + ((b >> 1) & 3); }
+  __host__ __device__ static constexpr int quad_index(int G, int i) { return 4 * G + i; }
+};
+
+template <int AFMT, int BFMT>
+__device__ __forceinline__ f4 mx_mma(const v8i& a, const v8i& b, int sa, int sb) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, f4{0.f, 0.f, 0.f, 0.f}, AFMT, BFMT, 0, sa, 0, sb);
+}
+
+// ---------------------------------------------------------------------------
 // LDS staging.  Tiles arrive in LDS by global_load_lds (direct HBM -> LDS, no
 // registers held while in flight).  The compiler cannot tell the stages of the
 // ring apart and would wait for every such load before any LDS read, so the
@@ -261,35 +341,40 @@ __device__ __forceinline__ float quad_bcast(float v) {
 // upper half's in every lane of its second
 __device__ __forceinline__ void halves(float v, float& h0, float& h1) {
   float a = v, b = v;
-  asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(a), "+v"(b));
+  asm volatile("s_nop 2\n\tv_permlane32_swap_b32 %0, %1" : "+v"(a), "+v"(b));
   h0 = a;
   h1 = b;
 }
 // max over rows (0,1) and (2,3) of 16 lanes: v_permlane16_swap trades the odd
-// rows of its first operand with the even rows of its second.  Like DPP, a
-// cross-lane read needs two wait states after the VALU write of its operands,
-// which the compiler cannot see through inline asm.
+// rows of its first operand with the even rows of its second.
+//
+// Wait states of the inline-asm cross-lane reads.  A DPP or permlane read of a
+// VGPR needs two wait states after an ordinary VALU write of it and three
+// after a v_dot2 write (measured on gfx950: with two, a DPP read after
+// v_dot2c_f32_f16 returns the register's previous value).  The compiler does
+// not insert them before the operands of inline asm, so every block opens
+// with three (s_nop 2); reads inside a block follow a plain VALU write and
+// take two (s_nop 1).
 __device__ __forceinline__ float max_row_pairs(float v) {
   float a = v, b = v;
-  asm volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1" : "+v"(a), "+v"(b));
+  asm volatile("s_nop 2\n\tv_permlane16_swap_b32 %0, %1" : "+v"(a), "+v"(b));
   return fmaxf(a, b);
 }
 // max over the two half-waves: v_permlane32_swap trades the upper half of its
 // first operand with the lower half of its second
 __device__ __forceinline__ float max_halves(float v) {
   float a = v, b = v;
-  asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(a), "+v"(b));
+  asm volatile("s_nop 2\n\tv_permlane32_swap_b32 %0, %1" : "+v"(a), "+v"(b));
   return fmaxf(a, b);
 }
 // max over the lanes of one query head (l, l^4, ..., across the wave), and m:
 // the DPP row rotations fused into the max, then the permlane swaps, in one
 // block.  Scores are never NaN (masked ones are -inf), so the canonicalising
-// max the compiler puts before each cross-lane result is not needed.  Each
-// DPP or permlane read of a VGPR follows its VALU write by two wait states.
+// max the compiler puts before each cross-lane result is not needed.
 __device__ __forceinline__ float wave_max_same_query_and(float v, float m) {
   float a, r;
   asm volatile(
-      "s_nop 1\n\t"
+      "s_nop 2\n\t"
       "v_max_f32_dpp %0, %0, %0 row_ror:4 row_mask:0xf bank_mask:0xf\n\t"
       "s_nop 1\n\t"
       "v_max_f32_dpp %0, %0, %0 row_ror:8 row_mask:0xf bank_mask:0xf\n\t"
@@ -326,11 +411,11 @@ __device__ __forceinline__ float wave_sum(float v) {
   v += dpp<0x124>(v);  // row_ror:4
   v += dpp<0x128>(v);  // row_ror:8
   float a = v, b = v;
-  asm volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1" : "+v"(a), "+v"(b));
+  asm volatile("s_nop 2\n\tv_permlane16_swap_b32 %0, %1" : "+v"(a), "+v"(b));
   v = a + b;
   a = v;
   b = v;
-  asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(a), "+v"(b));
+  asm volatile("s_nop 2\n\tv_permlane32_swap_b32 %0, %1" : "+v"(a), "+v"(b));
   return a + b;
 }
 __device__ __forceinline__ float wave_max_same_query(float v) {
@@ -338,6 +423,46 @@ __device__ __forceinline__ float wave_max_same_query(float v) {
   v = fmaxf(v, dpp<0x128>(v));  // row_ror:8
   return max_halves(max_row_pairs(v));
 }
+// reductions over a row of 16 lanes (the lanes of one query head in the
+// block-scaled score layout), with the DPP rotations fused into the operation
+__device__ __forceinline__ float row_max16(float v) {
+  asm volatile(
+      "s_nop 2\n\t"
+      "v_max_f32_dpp %0, %0, %0 row_ror:8 row_mask:0xf bank_mask:0xf\n\t"
+      "s_nop 1\n\t"
+      "v_max_f32_dpp %0, %0, %0 row_ror:4 row_mask:0xf bank_mask:0xf\n\t"
+      "s_nop 1\n\t"
+      "v_max_f32_dpp %0, %0, %0 row_ror:2 row_mask:0xf bank_mask:0xf\n\t"
+      "s_nop 1\n\t"
+      "v_max_f32_dpp %0, %0, %0 row_ror:1 row_mask:0xf bank_mask:0xf"
+      : "+v"(v));
+  return v;
+}
+__device__ __forceinline__ float row_sum16(float v) {
+  asm volatile(
+      "s_nop 2\n\t"
+      "v_add_f32_dpp %0, %0, %0 row_ror:8 row_mask:0xf bank_mask:0xf\n\t"
+      "s_nop 1\n\t"
+      "v_add_f32_dpp %0, %0, %0 row_ror:4 row_mask:0xf bank_mask:0xf\n\t"
+      "s_nop 1\n\t"
+      "v_add_f32_dpp %0, %0, %0 row_ror:2 row_mask:0xf bank_mask:0xf\n\t"
+      "s_nop 1\n\t"
+      "v_add_f32_dpp %0, %0, %0 row_ror:1 row_mask:0xf bank_mask:0xf"
+      : "+v"(v));
+  return v;
+}
+// sum over each half-row of 8 lanes: quad swaps, then the half-row mirror
+__device__ __forceinline__ float half_row_sum8(float v) {
+  v += dpp<0xB1>(v);   // quad_perm [1,0,3,2]
+  v += dpp<0x4E>(v);   // quad_perm [2,3,0,1]
+  v += dpp<0x141>(v);  // row_half_mirror
+  return v;
+}
+// v of lane `src` (a wave-uniform lane index), as a scalar operand
+__device__ __forceinline__ float lane_value(float v, int src) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), src));
+}
+
 // sum over the lanes of one query head within SPAN lanes (32: half-wave, 64: wave),
 // with DPP row rotations and v_permlane16/32_swap (no LDS round trip)
 template <int SPAN>
@@ -345,12 +470,12 @@ __device__ __forceinline__ float sum_same_query(float v) {
   v += dpp<0x124>(v);  // row_ror:4
   v += dpp<0x128>(v);  // row_ror:8
   float a = v, b = v;
-  asm volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1" : "+v"(a), "+v"(b));
+  asm volatile("s_nop 2\n\tv_permlane16_swap_b32 %0, %1" : "+v"(a), "+v"(b));
   v = a + b;
   if (SPAN == 64) {
     a = v;
     b = v;
-    asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(a), "+v"(b));
+    asm volatile("s_nop 2\n\tv_permlane32_swap_b32 %0, %1" : "+v"(a), "+v"(b));
     v = a + b;
   }
   return v;
@@ -421,11 +546,11 @@ __device__ __forceinline__ float wave_max(float v) {
   v = fmaxf(v, dpp<0x124>(v));  // row_ror:4
   v = fmaxf(v, dpp<0x128>(v));  // row_ror:8
   float a = v, b = v;
-  asm volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1" : "+v"(a), "+v"(b));
+  asm volatile("s_nop 2\n\tv_permlane16_swap_b32 %0, %1" : "+v"(a), "+v"(b));
   v = fmaxf(a, b);
   a = v;
   b = v;
-  asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(a), "+v"(b));
+  asm volatile("s_nop 2\n\tv_permlane32_swap_b32 %0, %1" : "+v"(a), "+v"(b));
   return fmaxf(a, b);
 }
 __device__ __forceinline__ void merge_ranges(const SplitArgs& a, int b, int h, int ns) {
@@ -614,6 +739,80 @@ __device__ __forceinline__ void map_select(const SplitArgs& a, const NextLoad& n
   }
 }
 
+// The end of a work item: every wave has written its running max m (log2
+// units) and denominator l to s_ml and its un-normalised output rows to s_o.
+// The work-group merges its 4 waves into this range's (O, lse) and either
+// writes the final output (the only range) or stores the partial
+// device-coherently and counts its arrival; the last range of the (sequence,
+// KV head) merges them all.  Every return is uniform.
+template <int UNIT>
+__device__ __forceinline__ void finish_range(const SplitArgs& a, const int b, const int h, const int split,
+                                             const int T, float (*s_ml)[2][4], float (*s_o)[4][kHeadDim], int* next,
+                                             NextLoad& nx) {
+  constexpr int D = kHeadDim;
+  const uint32_t tid = in_vgpr(threadIdx.x);
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const size_t bh = (size_t)b * a.hkv + h;
+  const int ns = (T + a.chunk - 1) / a.chunk;  // ranges holding tokens of this sequence
+  const bool direct = ns == 1 && !a.win_wgs;  // the only range partial: write the final output
+  for (int idx = (int)tid; idx < 4 * D; idx += blockDim.x) {
+    const int i = idx / D, c = idx % D;
+    if (i >= a.g_heads) continue;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, s_ml[w][0][i]);
+    float num = 0.f, den = 0.f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      const float l = s_ml[w][1][i];
+      const float f = (l > 0.f) ? __builtin_amdgcn_exp2f(s_ml[w][0][i] - M) : 0.f;
+      num = fmaf(f, s_o[w][i][c], num);
+      den = fmaf(f, l, den);
+    }
+    const size_t row = (size_t)b * a.hq + h * a.g_heads + i;
+    const float o = num / den, l_nat = (M + __log2f(den)) * kLn2;
+    if (direct) {  // the only range: final output
+      float of = o, lf = l_nat;
+      if (a.win_o) {  // merged with the full-precision window's partial
+        const float wl = a.win_lse[row];
+        const float mm = fmaxf(l_nat, wl), w1 = __expf(l_nat - mm), w2 = __expf(wl - mm);
+        of = fmaf(w1, o, w2 * a.win_o[row * D + c]) / (w1 + w2);
+        lf = mm + __logf(w1 + w2);
+      }
+      a.out[row * D + c] = to_bf16_rne(of);
+      if (c == 0 && a.lse) a.lse[row] = lf;
+    } else {
+      // device-coherent stores (they bypass this XCD's L2 for the merging work-group)
+      __hip_atomic_store(a.o_part + (row * a.splits + split) * D + c, o, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (c == 0)
+        __hip_atomic_store(a.lse_part + row * a.splits + split, l_nat, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+  if (direct) {
+    if (next && wave == 0) map_select<UNIT>(a, nx, next);
+    return;
+  }
+
+  // ---------------- the last range of this (sequence, KV head) merges all ranges
+  // Hand-off without agent-scope fences: those write back and invalidate the
+  // whole L2 of the XCD, once per work-group, and serialise the grid's tail.
+  // Every value that crosses work-groups is a device-coherent atomic access,
+  // so ordering only needs this work-group's stores to have completed
+  // (vmcnt 0 in every wave, then the barrier) before the counter increment,
+  // and the merging work-group's loads to be issued after it read the count.
+  __shared__ int s_last;
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  int done = 0;
+  if (tid == 0) done = __hip_atomic_fetch_add(a.counters + bh, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (next && wave == 0) map_select<UNIT>(a, nx, next);  // while the count is in flight
+  if (tid == 0) s_last = (done == ns - 1 + a.win_wgs);  // fused window work-groups arrive like ranges
+  __syncthreads();
+  if (!s_last) return;
+  merge_ranges(a, b, h, ns);
+  if (tid == 0) a.counters[bh] = 0;  // ready for the next call on this workspace
+}
+
 template <int BITS, bool KCH, bool VCH, int GRP>
 constexpr int waves_per_simd() {
   return (BITS == 2 && !KCH && !VCH && GRP == 128) ? 4 : 1;
@@ -670,6 +869,12 @@ __device__ __forceinline__ void run_item(const SplitArgs& a, const int b, const 
 
   const int qd = lane >> 2;   // quad: QK block (tokens 4qd..4qd+3); PV block (channels 8qd..8qd+7)
   const int qn = lane & 3;    // QK output column / PV A-operand row = query head within the KV group
+  // token-wise keys (block-scaled QK^T): lane 16 rh + rq holds query head rh's scores of tile
+  // quad rq; channel-wise keys keep quad qd, head qn.  pq: the quad of this lane's scores
+  const int rh = lane >> 4, rq = lane & 15;
+  const int pq = KCH ? qd : rq;
+  using MK = MxKey<BITS>;
+  constexpr int NQM = (!KCH && NGK > 2) ? NGK / 2 : 1;  // block-scaled QK^T instructions per 16 tokens
   const bool qvalid = qn < a.g_heads;
   const size_t bh = (size_t)b * a.hkv + h;
   const float sl2 = a.sm_log2;
@@ -678,14 +883,14 @@ __device__ __forceinline__ void run_item(const SplitArgs& a, const int b, const 
   // token-wise K: the work-group's query block as the QK^T B operand in LDS (row = query head;
   // rows padded by 16 B so the four rows of one read fall in different banks), and per group
   // sigma' * sum(Q) and sigma' * sum(Q * C)  (C = operand bias of each channel)
-  __shared__ __align__(16) uint32_t s_q[KCH ? 1 : 4][KCH ? 4 : D / 2 + 4];
-  __shared__ float s_kq[2][4][NGK];
   // channel-wise K: the bf16 query pairs (row = query head) from which each
   // wave builds Q~ = Q * s_tau for its tile's groups, hi and lo fp16 parts
   __shared__ uint32_t s_qb[KCH ? 4 : 1][KCH ? D / 2 : 1];
   constexpr int NGT = Stage<BITS, KCH, VCH, GRP>::NGT;
   __shared__ __align__(16) uint32_t s_qt[KCH ? kWaves : 1][KCH ? NGT : 1][2][4][KCH ? D / 2 + 4 : 4];
-  float kq_sum[NGK], kq_bias[NGK];
+  float kq_sum[NGK];  // token-wise keys: sigma' * sum of head rh's query over each key group
+  v8i qa[NQM];        // token-wise keys: query operand (rows 4 h + t, e4m3 terms t = 0, 1)
+  int qsc[NQM];       // its E8M0 scale per row
   auto query_prologue = [&]() {  // run after the first tiles are in flight, so the two HBM latencies overlap
    if constexpr (KCH) {
     if (wave < 4)
@@ -693,29 +898,78 @@ __device__ __forceinline__ void run_item(const SplitArgs& a, const int b, const 
           ? reinterpret_cast<const uint32_t*>(a.q + ((size_t)b * a.hq + h * a.g_heads + wave) * D)[lane] : 0u;
     __syncthreads();
    } else {
-    if (wave < 4) {  // wave i converts query head i, lane j its channel pair j
-      const int qi = wave, pj = lane;
-      uint32_t w = 0;
-      if (qi < a.g_heads) w = reinterpret_cast<const uint32_t*>(a.q + ((size_t)b * a.hq + h * a.g_heads + qi) * D)[pj];
-      const uint32_t q2 = pack_f16(__builtin_bit_cast(float, w << 16), __builtin_bit_cast(float, w & 0xFFFF0000u));
-      s_q[qi][pj] = q2;
-      float s2 = half_lo(q2) + half_hi(q2);
-      float c2 = C::bias(pj % PAIRS) * s2;
+    // A operand of the block-scaled QK^T: lane (G = lane / 16, row m = lane % 16), row
+    // m = 4 h + (2 key group + term) (one key group: m = 4 h + t), bytes b = e4m3 term t of
+    // query value (h, channel MK::chan(G, b)) masked to the row's key group, with one E8M0
+    // scale per row from the row's largest value: two terms hold the 8 significant bits of
+    // a bf16 value exactly
+    {
+      const int m = lane & 15, hq = m >> 2, slot = m & 3, Gq = lane >> 4;
+      const bool hv = hq < a.g_heads;
+      const uint4* qr = reinterpret_cast<const uint4*>(
+          a.q + ((size_t)b * a.hq + (size_t)h * a.g_heads + (hv ? hq : 0)) * D);
+      // the lane's 32 query values (bf16 pairs, MxKey::local order): four 16-byte loads
+      uint32_t qw[16];
 #pragma unroll
-      for (int m = 1; m < GRP / 2; m <<= 1) {  // sum over the GRP/2 pairs of the group
-        s2 += __shfl_xor(s2, m);
-        c2 += __shfl_xor(c2, m);
+      for (int i = 0; i < 4; ++i) {
+        const uint4 u = qr[MK::quad_index(Gq, i)];
+        qw[4 * i] = u.x;
+        qw[4 * i + 1] = u.y;
+        qw[4 * i + 2] = u.z;
+        qw[4 * i + 3] = u.w;
       }
-      if (pj % (GRP / 2) == 0) {
-        s_kq[0][qi][pj / (GRP / 2)] = s2 * sl2;
-        s_kq[1][qi][pj / (GRP / 2)] = c2 * sl2;
+      float qv[32];
+#pragma unroll
+      for (int bb = 0; bb < 32; ++bb) {
+        const int l = MK::local(bb);
+        const uint32_t w = qw[l >> 1];
+        qv[bb] = __uint_as_float((l & 1) ? (w & 0xFFFF0000u) : (w << 16));
+      }
+#pragma unroll
+      for (int r = 0; r < NQM; ++r) {
+        const int jg = (NGK == 1) ? 0 : (NGK == 2) ? (slot >> 1) : 2 * r + (slot >> 1);
+        const int t = (NGK == 1) ? slot : (slot & 1);
+        const bool rv = hv && t < 2;
+        float x[32], mx = 0.f;
+#pragma unroll
+        for (int bb = 0; bb < 32; ++bb) {
+          x[bb] = (rv && MK::chan(Gq, bb) / GRP == jg) ? qv[bb] : 0.f;
+          mx = fmaxf(mx, fabsf(x[bb]));
+        }
+        mx = max_halves(max_row_pairs(mx));  // the row's largest value over all 4 lane groups
+        const int s0 = max((int)((__float_as_uint(mx) >> 23) & 0xFF) - 127, -100) - 7;  // largest in [128, 256)
+        // e4m3 terms by the hardware conversions (OCP e4m3, round to nearest even, with
+        // subnormals): term 0 of each value, and term 1 = 16 (value - term 0)
+        v8i v;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const float x0 = __builtin_ldexpf(x[4 * i], -s0), x1 = __builtin_ldexpf(x[4 * i + 1], -s0);
+          const float x2 = __builtin_ldexpf(x[4 * i + 2], -s0), x3 = __builtin_ldexpf(x[4 * i + 3], -s0);
+          const int w0 = __builtin_amdgcn_cvt_pk_fp8_f32(x2, x3, __builtin_amdgcn_cvt_pk_fp8_f32(x0, x1, 0, false), true);
+          const auto d01 = __builtin_amdgcn_cvt_pk_f32_fp8(w0, false);
+          const auto d23 = __builtin_amdgcn_cvt_pk_f32_fp8(w0, true);
+          const int w1 = __builtin_amdgcn_cvt_pk_fp8_f32(
+              (x2 - d23[0]) * 16.f, (x3 - d23[1]) * 16.f,
+              __builtin_amdgcn_cvt_pk_fp8_f32((x0 - d01[0]) * 16.f, (x1 - d01[1]) * 16.f, 0, false), true);
+          v[i] = (t == 1) ? w1 : w0;
+        }
+        qa[r] = v;
+        qsc[r] = rv ? min(max(127 + s0 - 4 * t, 1), 254) : 127;
       }
     }
-    __syncthreads();
+    // sigma' * sum of head rh's query over each key group: lane rq takes channels 8 rq .. 8 rq + 7
+    {
+      const bool hv = rh < a.g_heads;
+      const uint32_t* qg = reinterpret_cast<const uint32_t*>(
+          a.q + ((size_t)b * a.hq + (size_t)h * a.g_heads + (hv ? rh : 0)) * D);
+      float part = 0.f;
 #pragma unroll
-    for (int j = 0; j < NGK; ++j) {
-      kq_sum[j] = s_kq[0][qn][j];
-      kq_bias[j] = s_kq[1][qn][j];
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t w = hv ? qg[4 * rq + i] : 0u;
+        part += __uint_as_float(w << 16) + __uint_as_float(w & 0xFFFF0000u);
+      }
+#pragma unroll
+      for (int jg = 0; jg < NGK; ++jg) kq_sum[jg] = row_sum16((8 * rq) / GRP == jg ? part : 0.f) * sl2;
     }
    }
   };
@@ -742,7 +996,7 @@ __device__ __forceinline__ void run_item(const SplitArgs& a, const int b, const 
   for (int i = 0; i < C::NCONST; ++i) kc[i] = in_vgpr(C::kConst[i]);
 
   // value-operand bias of this lane's quad (pairs 2*(qd % KPW), +1)
-  const float cv0 = C::bias(2 * (qd % KPW)), cv1 = C::bias(2 * (qd % KPW) + 1);
+  const float cv0 = C::bias(2 * (pq % KPW)), cv1 = C::bias(2 * (pq % KPW) + 1);
   const uint32_t cv0h = splat_f16(cv0), cv1h = splat_f16(cv1), oneh = splat_f16(1.f);
 
   const uint32_t* kbase = a.pk + bh * (size_t)a.tcap * KW;
@@ -770,7 +1024,12 @@ __device__ __forceinline__ void run_item(const SplitArgs& a, const int b, const 
     }
     ps_part *= alpha;
     pb_part *= alpha;
-    const float ai[4] = {quad_bcast<0>(alpha), quad_bcast<1>(alpha), quad_bcast<2>(alpha), quad_bcast<3>(alpha)};
+    float ai[4];
+    if constexpr (KCH) {
+      ai[0] = quad_bcast<0>(alpha); ai[1] = quad_bcast<1>(alpha); ai[2] = quad_bcast<2>(alpha); ai[3] = quad_bcast<3>(alpha);
+    } else {  // head i's scores sit in row i
+      ai[0] = lane_value(alpha, 0); ai[1] = lane_value(alpha, 16); ai[2] = lane_value(alpha, 32); ai[3] = lane_value(alpha, 48);
+    }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
 #pragma unroll
@@ -785,19 +1044,31 @@ __device__ __forceinline__ void run_item(const SplitArgs& a, const int b, const 
   // channel-wise V: fold the finished group tau into o_tot.  `span` = lanes whose quads form the group.
   auto fold_value_group = [&](uint32_t s2, uint32_t z2, int src_half) {
     // sums of the group per query, then broadcast query i's sums to every lane
-    float ps, pb;
-    if (GRP == 32) {  // the group's quads are the lanes of half-wave src_half
-      float a0, a1, b0, b1;
-      halves(sum_same_query<32>(ps_part), a0, a1);
-      halves(sum_same_query<32>(pb_part), b0, b1);
-      ps = src_half ? a1 : a0;
-      pb = src_half ? b1 : b0;
-    } else {
-      ps = sum_same_query<64>(ps_part);
-      pb = sum_same_query<64>(pb_part);
+    float psq[4], pbq[4];
+    if constexpr (KCH) {
+      float ps, pb;
+      if (GRP == 32) {  // the group's quads are the lanes of half-wave src_half
+        float a0, a1, b0, b1;
+        halves(sum_same_query<32>(ps_part), a0, a1);
+        halves(sum_same_query<32>(pb_part), b0, b1);
+        ps = src_half ? a1 : a0;
+        pb = src_half ? b1 : b0;
+      } else {
+        ps = sum_same_query<64>(ps_part);
+        pb = sum_same_query<64>(pb_part);
+      }
+      psq[0] = quad_bcast<0>(ps); psq[1] = quad_bcast<1>(ps); psq[2] = quad_bcast<2>(ps); psq[3] = quad_bcast<3>(ps);
+      pbq[0] = quad_bcast<0>(pb); pbq[1] = quad_bcast<1>(pb); pbq[2] = quad_bcast<2>(pb); pbq[3] = quad_bcast<3>(pb);
+    } else {  // head i's quads are row i; a 32-token group is half a row (quads 0-7 or 8-15)
+      const float ps = (GRP == 32) ? half_row_sum8(ps_part) : row_sum16(ps_part);
+      const float pb = (GRP == 32) ? half_row_sum8(pb_part) : row_sum16(pb_part);
+      const int o = (GRP == 32 && src_half) ? 8 : 0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        psq[i] = lane_value(ps, 16 * i + o);
+        pbq[i] = lane_value(pb, 16 * i + o);
+      }
     }
-    const float psq[4] = {quad_bcast<0>(ps), quad_bcast<1>(ps), quad_bcast<2>(ps), quad_bcast<3>(ps)};
-    const float pbq[4] = {quad_bcast<0>(pb), quad_bcast<1>(pb), quad_bcast<2>(pb), quad_bcast<3>(pb)};
     const float sv[2] = {half_lo(s2), half_hi(s2)};
     const float zv[2] = {half_lo(z2), half_hi(z2)};
 #pragma unroll
@@ -812,7 +1083,8 @@ __device__ __forceinline__ void run_item(const SplitArgs& a, const int b, const 
 
   // ---------------- tiles: staged in a per-wave LDS ring NS deep, read into registers
   struct Tile {
-    uint4 k[KW / 4];           // key row of token t0 + lane
+    uint4 k[KCH ? KW / 4 : 1];  // channel-wise keys: key row of token t0 + lane
+    uint32_t kb[4][KCH ? 1 : MK::WPL];  // token-wise keys: packed words of block j's token 4 rq + j, lane group rh
     uint2 v[VW];               // value words of channels 2 lane, 2 lane + 1
     uint2 ks[NGK], kz[NGK];    // token-wise key (s, z) of the quad's tokens
     uint2 vs[NGV], vz[NGV];    // token-wise value (s, z) of the quad's tokens
@@ -866,12 +1138,37 @@ __device__ __forceinline__ void run_item(const SplitArgs& a, const int b, const 
       default: wait_vmcnt<(NS - 1) * ST::LOADS>(); break;
     }
     const uint32_t st = ring_lds + (k % NS) * ST::BYTES;
-    const uint32_t ak = st + ST::KOFF + lane * 16, av = st + ST::VOFF + lane * 8;
-    tl.k[0] = lds_b128<0>(ak);
-    tl.k[1] = lds_b128<1024>(ak);
-    if constexpr (KW / 4 > 2) {
-      tl.k[2 % (KW / 4)] = lds_b128<2048>(ak);
-      tl.k[3 % (KW / 4)] = lds_b128<3072>(ak);
+    const uint32_t av = st + ST::VOFF + lane * 8;
+    if constexpr (KCH) {
+      const uint32_t ak = st + ST::KOFF + lane * 16;
+      tl.k[0] = lds_b128<0>(ak);
+      tl.k[1 % (KCH ? KW / 4 : 1)] = lds_b128<1024>(ak);
+      if constexpr (KW / 4 > 2) {
+        tl.k[2 % (KW / 4)] = lds_b128<2048>(ak);
+        tl.k[3 % (KW / 4)] = lds_b128<3072>(ak);
+      }
+    } else {
+      // key rows sit as 16-byte chunks [chunk][token]: lane group rh's codes of token 4 rq + j are
+      // chunk rh / 2, bytes 8 (rh % 2) .. +7 (INT2), or chunk rh (INT4)
+      if constexpr (BITS == 2) {
+        const uint32_t ak = st + ST::KOFF + (rh >> 1) * 1024 + 64 * rq + 8 * (rh & 1);
+        const uint2 w0 = lds_b64<0>(ak), w1 = lds_b64<16>(ak), w2 = lds_b64<32>(ak), w3 = lds_b64<48>(ak);
+        tl.kb[0][0] = w0.x; tl.kb[0][1 % MK::WPL] = w0.y;
+        tl.kb[1][0] = w1.x; tl.kb[1][1 % MK::WPL] = w1.y;
+        tl.kb[2][0] = w2.x; tl.kb[2][1 % MK::WPL] = w2.y;
+        tl.kb[3][0] = w3.x; tl.kb[3][1 % MK::WPL] = w3.y;
+      } else {
+        const uint32_t ak = st + ST::KOFF + rh * 1024 + 64 * rq;
+        const uint4 w0 = lds_b128<0>(ak), w1 = lds_b128<16>(ak), w2 = lds_b128<32>(ak), w3 = lds_b128<48>(ak);
+        const uint4 w[4] = {w0, w1, w2, w3};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          tl.kb[j][0] = w[j].x;
+          tl.kb[j][1 % MK::WPL] = w[j].y;
+          tl.kb[j][2 % MK::WPL] = w[j].z;
+          tl.kb[j][3 % MK::WPL] = w[j].w;
+        }
+      }
     }
     tl.v[0] = lds_b64<0>(av);
     tl.v[1] = lds_b64<512>(av);
@@ -884,7 +1181,7 @@ __device__ __forceinline__ void run_item(const SplitArgs& a, const int b, const 
       tl.v[7 % VW] = lds_b64<3584>(av);
     }
     if constexpr (!KCH) {
-      const uint32_t as = st + ST::SOFF + qd * 8 * NGK;
+      const uint32_t as = st + ST::SOFF + pq * 8 * NGK;
       tl.ks[0] = lds_b64<0>(as);
       tl.kz[0] = lds_b64<ST::KSB>(as);
       if constexpr (NGK > 1) {
@@ -899,7 +1196,7 @@ __device__ __forceinline__ void run_item(const SplitArgs& a, const int b, const 
       }
     }
     if constexpr (!VCH) {
-      const uint32_t as = st + ST::VSOFF + qd * 8 * NGV;
+      const uint32_t as = st + ST::VSOFF + pq * 8 * NGV;
       tl.vs[0] = lds_b64<0>(as);
       tl.vz[0] = lds_b64<ST::VSB>(as);
       if constexpr (NGV > 1) {
@@ -932,8 +1229,15 @@ __device__ __forceinline__ void run_item(const SplitArgs& a, const int b, const 
       }
     }
     wait_lgkm0();
+    if constexpr (KCH) {
 #pragma unroll
-    for (int i = 0; i < KW / 4; ++i) touch(tl.k[i]);
+      for (int i = 0; i < KW / 4; ++i) touch(tl.k[i]);
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int w = 0; w < MK::WPL; ++w) touch(tl.kb[j][w]);
+    }
 #pragma unroll
     for (int w = 0; w < VW; ++w) touch(tl.v[w]);
     if constexpr (!KCH) {
@@ -987,100 +1291,106 @@ __device__ __forceinline__ void run_item(const SplitArgs& a, const int b, const 
     }
 
     // ---------------- QK^T on the matrix cores
-    constexpr int NCH = (NGK == 1) ? 2 : NGK;  // independent accumulation chains
-    f4 sacc[NCH];
-#pragma unroll
-    for (int j = 0; j < NCH; ++j) sacc[j] = f4{0.f, 0.f, 0.f, 0.f};
-    // B operand rows from LDS, re-read every tile (an opaque zero offset keeps
-    // the compiler from hoisting them into 64 live registers)
-    // One segment per key word (its KPW k-steps); the compiler may not move work
-    // across segments, which bounds the live operands, and each segment reads
-    // the next one's B operands from LDS ahead of use.
-    // channel-wise K: hi parts (chain 0) and lo parts (chain 1) of Q~ for this lane's group
-    const int opq = (int)in_vgpr(0u);
-    const int g2l = (KCH && NGT > 1 && qd >= 8) ? 1 : 0;
-    const uint4* qsrc = KCH ? reinterpret_cast<const uint4*>(&s_qt[KCH ? wave : 0][g2l][0][qn][0]) + opq
-                            : reinterpret_cast<const uint4*>(&s_q[KCH ? 0 : qn][0]) + opq;
-    const uint4* qlsrc = reinterpret_cast<const uint4*>(&s_qt[KCH ? wave : 0][g2l][1][qn][0]) + opq;
-    uint4 qcur[QPW], qnxt[QPW], lcur[KCH ? QPW : 1], lnxt[KCH ? QPW : 1];
-#pragma unroll
-    for (int i = 0; i < QPW; ++i) qcur[i] = qsrc[i];
-    if constexpr (KCH) {
-#pragma unroll
-      for (int i = 0; i < QPW; ++i) lcur[i] = qlsrc[i];
-    }
-    uint4 kseg;
-#pragma unroll
-    for (int d = 0; d < KW; ++d) {
-      if (d % 4 == 0) kseg = tl.k[d / 4];
-      if (d + 1 < KW) {
-#pragma unroll
-        for (int i = 0; i < QPW; ++i) qnxt[i] = qsrc[(d + 1) * QPW + i];
-        if constexpr (KCH) {
-#pragma unroll
-          for (int i = 0; i < QPW; ++i) lnxt[i] = qlsrc[(d + 1) * QPW + i];
-        }
-      }
-      if (d % 4 == 0) touch(kseg);  // ties the unpacking of these four words to this segment onwards
-      const uint32_t wrd = (d % 4 == 0) ? kseg.x : (d % 4 == 1) ? kseg.y : (d % 4 == 2) ? kseg.z : kseg.w;
-      uint32_t p[PAIRS];
-      C::extract(wrd, kc, p);
-#pragma unroll
-      for (int sg = 0; sg < KPW; ++sg) {
-        const int j = d * KPW + sg;  // k-step: channels 4j .. 4j+3
-        const h4 av = cat4(p[2 * sg], p[2 * sg + 1]);
-        if constexpr (KCH) {
-          const uint4 qh = qcur[sg / 2], ql = lcur[sg / 2];
-          const h4 bh = (sg & 1) ? cat4(qh.z, qh.w) : cat4(qh.x, qh.y);
-          const h4 bl = (sg & 1) ? cat4(ql.z, ql.w) : cat4(ql.x, ql.y);
-          sacc[0] = __builtin_amdgcn_mfma_f32_4x4x4f16(av, bh, sacc[0], 0, 0, 0);
-          sacc[1] = __builtin_amdgcn_mfma_f32_4x4x4f16(av, bl, sacc[1], 0, 0, 0);
-        } else {
-          const int ch = (NGK == 1) ? (j & 1) : (4 * j) / GRP;
-          const uint4 qq = qcur[sg / 2];
-          const h4 bv = (sg & 1) ? cat4(qq.z, qq.w) : cat4(qq.x, qq.y);
-          sacc[ch] = __builtin_amdgcn_mfma_f32_4x4x4f16(av, bv, sacc[ch], 0, 0, 0);
-        }
-      }
-#pragma unroll
-      for (int i = 0; i < QPW; ++i) qcur[i] = qnxt[i];
-      if constexpr (KCH) {
-#pragma unroll
-        for (int i = 0; i < QPW; ++i) lcur[i] = lnxt[i];
-      }
-      __builtin_amdgcn_sched_barrier(0);
-    }
-
-    // ---------------- key-side fold (before the softmax) -> scores in log2 units
     float sc[4];
+    if constexpr (!KCH) {
+      // token-wise keys: block j (16 tokens, column n = token 4n + j) per block-scaled instruction,
+      // key codes as fp4 / fp8 operands; lane 16 rh + rq receives head rh's raw scores of token
+      // 4 rq + j in its rows (key group, term); the key-side fold (acc-fold: each group's partial
+      // scaled once by s, plus z * sum(Q)) gives log2-unit scores before the softmax
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      if constexpr (KCH) {
-        sc[r] = fmaf(sacc[0][r] + sacc[1][r], sl2, kconst);
-      } else {
+      for (int j = 0; j < 4; ++j) {
+        const v8i bk = MK::build(tl.kb[j]);
+        f4 c[NQM];
+#pragma unroll
+        for (int r = 0; r < NQM; ++r) c[r] = mx_mma<0, MK::FMT>(qa[r], bk, qsc[r], MK::CODE_SCALE);
         float acc = 0.f;
 #pragma unroll
-        for (int j = 0; j < NGK; ++j) {
-          const int idx = r * NGK + j;  // fp16 index inside the quad's (token, group) block
+        for (int q = 0; q < NGK; ++q) {
+          const int idx = j * NGK + q;  // fp16 index inside the quad's (token, group) block
           const uint2 sv = tl.ks[idx / 4];
           const uint2 zv = tl.kz[idx / 4];
           const uint32_t s32 = ((idx % 4) < 2) ? sv.x : sv.y;
           const uint32_t z32 = ((idx % 4) < 2) ? zv.x : zv.y;
           const float s = (idx % 2 == 0) ? half_lo(s32) : half_hi(s32);
           const float z = (idx % 2 == 0) ? half_lo(z32) : half_hi(z32);
-          const float raw = (NGK == 1) ? sacc[0][r] + sacc[1][r] : sacc[j][r];
-          acc = fmaf(s, fmaf(raw, sl2, -kq_bias[j]), acc);
-          acc = fmaf(z, kq_sum[j], acc);
+          const f4& cq = c[(q / 2) % NQM];
+          const float raw = (NGK == 1) ? cq[0] + cq[1] : cq[2 * (q % 2)] + cq[2 * (q % 2) + 1];
+          acc = fmaf(s, raw * sl2, fmaf(z, kq_sum[q], acc));
         }
-        sc[r] = acc;
+        sc[j] = acc;
+        if (tail && (t0 + 4 * rq + j >= T)) sc[j] = -INFINITY;
       }
-      if (tail && (t0 + 4 * qd + r >= T)) sc[r] = -INFINITY;
+    } else {
+      constexpr int NCH = 2;  // independent accumulation chains (hi and lo parts of Q~)
+      f4 sacc[NCH];
+  #pragma unroll
+      for (int j = 0; j < NCH; ++j) sacc[j] = f4{0.f, 0.f, 0.f, 0.f};
+      // B operand rows from LDS, re-read every tile (an opaque zero offset keeps
+      // the compiler from hoisting them into 64 live registers)
+      // One segment per key word (its KPW k-steps); the compiler may not move work
+      // across segments, which bounds the live operands, and each segment reads
+      // the next one's B operands from LDS ahead of use.
+      // channel-wise K: hi parts (chain 0) and lo parts (chain 1) of Q~ for this lane's group
+      const int opq = (int)in_vgpr(0u);
+      const int g2l = (KCH && NGT > 1 && qd >= 8) ? 1 : 0;
+      const uint4* qsrc = reinterpret_cast<const uint4*>(&s_qt[KCH ? wave : 0][g2l][0][qn][0]) + opq;
+      const uint4* qlsrc = reinterpret_cast<const uint4*>(&s_qt[KCH ? wave : 0][g2l][1][qn][0]) + opq;
+      uint4 qcur[QPW], qnxt[QPW], lcur[KCH ? QPW : 1], lnxt[KCH ? QPW : 1];
+  #pragma unroll
+      for (int i = 0; i < QPW; ++i) qcur[i] = qsrc[i];
+      if constexpr (KCH) {
+  #pragma unroll
+        for (int i = 0; i < QPW; ++i) lcur[i] = qlsrc[i];
+      }
+      uint4 kseg;
+  #pragma unroll
+      for (int d = 0; d < KW; ++d) {
+        if (d % 4 == 0) kseg = tl.k[d / 4];
+        if (d + 1 < KW) {
+  #pragma unroll
+          for (int i = 0; i < QPW; ++i) qnxt[i] = qsrc[(d + 1) * QPW + i];
+          if constexpr (KCH) {
+  #pragma unroll
+            for (int i = 0; i < QPW; ++i) lnxt[i] = qlsrc[(d + 1) * QPW + i];
+          }
+        }
+        if (d % 4 == 0) touch(kseg);  // ties the unpacking of these four words to this segment onwards
+        const uint32_t wrd = (d % 4 == 0) ? kseg.x : (d % 4 == 1) ? kseg.y : (d % 4 == 2) ? kseg.z : kseg.w;
+        uint32_t p[PAIRS];
+        C::extract(wrd, kc, p);
+  #pragma unroll
+        for (int sg = 0; sg < KPW; ++sg) {
+          const int j = d * KPW + sg;  // k-step: channels 4j .. 4j+3
+          const h4 av = cat4(p[2 * sg], p[2 * sg + 1]);
+          (void)j;
+          const uint4 qh = qcur[sg / 2], ql = lcur[sg / 2];
+          const h4 bh = (sg & 1) ? cat4(qh.z, qh.w) : cat4(qh.x, qh.y);
+          const h4 bl = (sg & 1) ? cat4(ql.z, ql.w) : cat4(ql.x, ql.y);
+          sacc[0] = __builtin_amdgcn_mfma_f32_4x4x4f16(av, bh, sacc[0], 0, 0, 0);
+          sacc[1] = __builtin_amdgcn_mfma_f32_4x4x4f16(av, bl, sacc[1], 0, 0, 0);
+        }
+  #pragma unroll
+        for (int i = 0; i < QPW; ++i) qcur[i] = qnxt[i];
+        if constexpr (KCH) {
+  #pragma unroll
+          for (int i = 0; i < QPW; ++i) lcur[i] = lnxt[i];
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+
+      // ---------------- key-side fold (before the softmax) -> scores in log2 units
+  #pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        sc[r] = fmaf(sacc[0][r] + sacc[1][r], sl2, kconst);
+        if (tail && (t0 + 4 * qd + r >= T)) sc[r] = -INFINITY;
+      }
     }
 
     // ---------------- online softmax: exact running max per query head.  The
     // largest weight seen so far is exactly 1, so the operand-folded weight of
     // the dominant token (p * s) is its fp16 scale itself, with no rounding.
-    const float m_new = wave_max_same_query_and(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])), m_ref);
+    const float mt = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
+    const float m_new = KCH ? wave_max_same_query_and(mt, m_ref) : fmaxf(m_ref, row_max16(mt));
     if (__any(m_new > m_ref)) {
       const float alpha = __builtin_amdgcn_exp2f(m_ref - m_new);  // 0 on the first tile
       m_ref = m_new;
@@ -1107,7 +1417,7 @@ __device__ __forceinline__ void run_item(const SplitArgs& a, const int b, const 
           sw[r] = s32;
           s[r] = (idx % 2 == 0) ? half_lo(s32) : half_hi(s32);
           z[r] = (idx % 2 == 0) ? half_lo(z32) : half_hi(z32);
-          if (tail && (t0 + 4 * qd + r >= T)) s[r] = z[r] = 0.f;  // padding may hold NaN
+          if (tail && (t0 + 4 * pq + r >= T)) s[r] = z[r] = 0.f;  // padding may hold NaN
         }
         uint32_t p01, p23;
         if constexpr (tail) {
@@ -1117,14 +1427,14 @@ __device__ __forceinline__ void run_item(const SplitArgs& a, const int b, const 
           p01 = mul_f16x2(p[0], sw[0], (0 * NGV + j) % 2, p[1], sw[1], (1 * NGV + j) % 2);
           p23 = mul_f16x2(p[2], sw[2], (2 * NGV + j) % 2, p[3], sw[3], (3 * NGV + j) % 2);
         }
-        s_p[wave][j][qn][qd] = make_uint2(p01, p23);
+        s_p[wave][j][KCH ? qn : rh][pq] = make_uint2(p01, p23);
         vb_part[j] = dot2(p23, cv1h, dot2(p01, cv0h, vb_part[j]));
         vz_part[j] = fmaf(p[0], z[0], fmaf(p[1], z[1], fmaf(p[2], z[2], fmaf(p[3], z[3], vz_part[j]))));
       }
     } else {
       const uint32_t p01 = pack_f16(p[0], p[1]);
       const uint32_t p23 = pack_f16(p[2], p[3]);
-      s_p[wave][0][qn][qd] = make_uint2(p01, p23);
+      s_p[wave][0][KCH ? qn : rh][pq] = make_uint2(p01, p23);
       ps_part = dot2(p23, oneh, dot2(p01, oneh, ps_part));
       pb_part = dot2(p23, cv1h, dot2(p01, cv0h, pb_part));
     }
@@ -1229,23 +1539,36 @@ __device__ __forceinline__ void run_item(const SplitArgs& a, const int b, const 
   if (next && wave == 0) next_load(a, nx);
 
   // ---------------- wave epilogue: totals per query, value-side corrections
-  const float l_tot = sum_same_query<64>(l_part);
+  // (channel-wise keys: a query head's lanes are those of one l & 3; token-wise keys: one row)
+  const float l_tot = KCH ? sum_same_query<64>(l_part) : row_sum16(l_part);
   f4 o_fin[2];
   if constexpr (VCH) {
     o_fin[0] = o_tot[0];
     o_fin[1] = o_tot[1];
   } else {
-    float zc[NGV], bc[NGV];
-#pragma unroll
-    for (int j = 0; j < NGV; ++j) {
-      zc[j] = sum_same_query<64>(vz_part[j]);
-      bc[j] = sum_same_query<64>(vb_part[j]);
-    }
     const int jv = (8 * qd) / GRP;  // value group of channels 2l, 2l+1
-    float cg = 0.f;  // correction of this lane's value group, per this lane's query head
+    float cq[4];  // correction of this lane's value group for query head i
+    if constexpr (KCH) {
+      float zc[NGV], bc[NGV];
 #pragma unroll
-    for (int j = 0; j < NGV; ++j) cg = (j == jv) ? zc[j] - bc[j] : cg;
-    const float cq[4] = {quad_bcast<0>(cg), quad_bcast<1>(cg), quad_bcast<2>(cg), quad_bcast<3>(cg)};
+      for (int j = 0; j < NGV; ++j) {
+        zc[j] = sum_same_query<64>(vz_part[j]);
+        bc[j] = sum_same_query<64>(vb_part[j]);
+      }
+      float cg = 0.f;  // correction of this lane's value group, per this lane's query head
+#pragma unroll
+      for (int j = 0; j < NGV; ++j) cg = (j == jv) ? zc[j] - bc[j] : cg;
+      cq[0] = quad_bcast<0>(cg); cq[1] = quad_bcast<1>(cg); cq[2] = quad_bcast<2>(cg); cq[3] = quad_bcast<3>(cg);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) cq[i] = 0.f;
+#pragma unroll
+      for (int j = 0; j < NGV; ++j) {
+        const float dj = row_sum16(vz_part[j]) - row_sum16(vb_part[j]);  // head rh's correction of group j
+#pragma unroll
+        for (int i = 0; i < 4; ++i) cq[i] = (j == jv) ? lane_value(dj, 16 * i) : cq[i];
+      }
+    }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const float corr = cq[i];
@@ -1254,9 +1577,9 @@ __device__ __forceinline__ void run_item(const SplitArgs& a, const int b, const 
     }
   }
   __syncthreads();  // every wave is done with its ring before the rings hold s_o
-  if (lane < 4) {
-    s_ml[wave][0][lane] = m_ref;
-    s_ml[wave][1][lane] = l_tot;
+  if (KCH ? lane < 4 : rq == 0) {  // one lane per query head
+    s_ml[wave][0][KCH ? lane : rh] = m_ref;
+    s_ml[wave][1][KCH ? lane : rh] = l_tot;
   }
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -1265,65 +1588,7 @@ __device__ __forceinline__ void run_item(const SplitArgs& a, const int b, const 
   }
   __syncthreads();
 
-  // ---------------- work-group merge of the 4 waves -> this range's (O, lse)
-  const int ns = (T + a.chunk - 1) / a.chunk;  // ranges holding tokens of this sequence
-  const bool direct = ns == 1 && !a.win_wgs;  // the only range partial: write the final output
-  for (int idx = (int)tid; idx < 4 * D; idx += blockDim.x) {
-    const int i = idx / D, c = idx % D;
-    if (i >= a.g_heads) continue;
-    float M = -INFINITY;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, s_ml[w][0][i]);
-    float num = 0.f, den = 0.f;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
-      const float l = s_ml[w][1][i];
-      const float f = (l > 0.f) ? __builtin_amdgcn_exp2f(s_ml[w][0][i] - M) : 0.f;
-      num = fmaf(f, s_o[w][i][c], num);
-      den = fmaf(f, l, den);
-    }
-    const size_t row = (size_t)b * a.hq + h * a.g_heads + i;
-    const float o = num / den, l_nat = (M + __log2f(den)) * kLn2;
-    if (direct) {  // the only range: final output
-      float of = o, lf = l_nat;
-      if (a.win_o) {  // merged with the full-precision window's partial
-        const float wl = a.win_lse[row];
-        const float mm = fmaxf(l_nat, wl), w1 = __expf(l_nat - mm), w2 = __expf(wl - mm);
-        of = fmaf(w1, o, w2 * a.win_o[row * D + c]) / (w1 + w2);
-        lf = mm + __logf(w1 + w2);
-      }
-      a.out[row * D + c] = to_bf16_rne(of);
-      if (c == 0 && a.lse) a.lse[row] = lf;
-    } else {
-      // device-coherent stores (they bypass this XCD's L2 for the merging work-group)
-      __hip_atomic_store(a.o_part + (row * a.splits + split) * D + c, o, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      if (c == 0)
-        __hip_atomic_store(a.lse_part + row * a.splits + split, l_nat, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
-  }
-  if (direct) {
-    if (next && wave == 0) map_select<UNIT>(a, nx, next);
-    return;
-  }
-
-  // ---------------- the last range of this (sequence, KV head) merges all ranges
-  // Hand-off without agent-scope fences: those write back and invalidate the
-  // whole L2 of the XCD, once per work-group, and serialise the grid's tail.
-  // Every value that crosses work-groups is a device-coherent atomic access,
-  // so ordering only needs this work-group's stores to have completed
-  // (vmcnt 0 in every wave, then the barrier) before the counter increment,
-  // and the merging work-group's loads to be issued after it read the count.
-  __shared__ int s_last;
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __syncthreads();
-  int done = 0;
-  if (tid == 0) done = __hip_atomic_fetch_add(a.counters + bh, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  if (next && wave == 0) map_select<UNIT>(a, nx, next);  // while the count is in flight
-  if (tid == 0) s_last = (done == ns - 1 + a.win_wgs);  // fused window work-groups arrive like ranges
-  __syncthreads();
-  if (!s_last) return;
-  merge_ranges(a, b, h, ns);
-  if (tid == 0) a.counters[bh] = 0;  // ready for the next call on this workspace
+  finish_range<UNIT>(a, b, h, split, T, s_ml, s_o, next, nx);
 }
 
 // A full-precision window of recent tokens attended by S more work-groups of

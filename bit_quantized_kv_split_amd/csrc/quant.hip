@@ -71,17 +71,18 @@ struct GroupQ {
   __device__ __forceinline__ float rcp() const { return s == 0.f ? 0.f : __builtin_amdgcn_rcpf(s); }
 };
 
-// Cross-lane reductions with DPP and permlane swaps (inline asm: each
-// cross-lane read of a VGPR follows its VALU write by two wait states).  Every
+// Cross-lane reductions with DPP and permlane swaps (inline asm: a block opens
+// with three wait states, which covers a v_dot2 write of its operands as well
+// as an ordinary VALU write, and a read inside it follows its write by two).  Every
 // step pairs lanes symmetrically (quad xor 1 and 2, half-row and row mirrors,
 // row-pair and half-wave swaps), so every lane ends with the result.
 #define FOSCAR_DPP_MINMAX(mn, mx, ctrl)                                               \
-  asm volatile("s_nop 1\n\t"                                                        \
+  asm volatile("s_nop 2\n\t"                                                        \
                "v_min_f32_dpp %0, %0, %0 " ctrl " row_mask:0xf bank_mask:0xf\n\t"   \
                "v_max_f32_dpp %1, %1, %1 " ctrl " row_mask:0xf bank_mask:0xf"         \
                : "+v"(mn), "+v"(mx))
 #define FOSCAR_DPP_OR(v, ctrl) \
-  asm volatile("s_nop 1\n\tv_or_b32_dpp %0, %0, %0 " ctrl " row_mask:0xf bank_mask:0xf" : "+v"(v))
+  asm volatile("s_nop 2\n\tv_or_b32_dpp %0, %0, %0 " ctrl " row_mask:0xf bank_mask:0xf" : "+v"(v))
 
 struct QuantArgs {
   const uint32_t* ksrc;    // bf16 pairs [B][Hkv][N][D/2]
@@ -130,7 +131,7 @@ __device__ __forceinline__ void code8(const float (&x)[8], const GroupQ<BITS> (&
 __device__ __forceinline__ uint32_t or_slots(uint32_t v) {
   uint32_t a;
   asm volatile(
-      "v_mov_b32 %1, %0\n\ts_nop 1\n\tv_permlane16_swap_b32 %0, %1\n\tv_or_b32 %0, %0, %1\n\t"
+      "s_nop 2\n\tv_mov_b32 %1, %0\n\ts_nop 1\n\tv_permlane16_swap_b32 %0, %1\n\tv_or_b32 %0, %0, %1\n\t"
       "v_mov_b32 %1, %0\n\ts_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\tv_or_b32 %0, %0, %1"
       : "+v"(v), "=&v"(a));
   return v;
@@ -138,7 +139,7 @@ __device__ __forceinline__ uint32_t or_slots(uint32_t v) {
 __device__ __forceinline__ void minmax_slots(float& mn, float& mx) {
   float a, b;
   asm volatile(
-      "v_mov_b32 %2, %0\n\tv_mov_b32 %3, %1\n\ts_nop 1\n\t"
+      "s_nop 2\n\tv_mov_b32 %2, %0\n\tv_mov_b32 %3, %1\n\ts_nop 1\n\t"
       "v_permlane16_swap_b32 %0, %2\n\tv_permlane16_swap_b32 %1, %3\n\t"
       "v_min_f32 %0, %0, %2\n\tv_max_f32 %1, %1, %3\n\t"
       "v_mov_b32 %2, %0\n\tv_mov_b32 %3, %1\n\ts_nop 1\n\t"
