@@ -891,11 +891,35 @@ __device__ __forceinline__ void run_item(const SplitArgs& a, const int b, const 
   float kq_sum[NGK];  // token-wise keys: sigma' * sum of head rh's query over each key group
   v8i qa[NQM];        // token-wise keys: query operand (rows 4 h + t, e4m3 terms t = 0, 1)
   int qsc[NQM];       // its E8M0 scale per row
+  // query words, loaded before the first tiles are issued: the loads of one wave return in
+  // issue order, so query loads behind a tile's would wait for the whole tile
+  uint32_t qw[KCH ? 1 : 16];  // token-wise keys: the lane's 32 query values (MxKey::local order)
+  uint32_t qgw[KCH ? 1 : 4];  // token-wise keys: head rh's channels 8 rq .. 8 rq + 7
+  auto query_load = [&]() {
+   if constexpr (KCH) {
+    qw[0] = (wave < a.g_heads)
+        ? reinterpret_cast<const uint32_t*>(a.q + ((size_t)b * a.hq + h * a.g_heads + wave) * D)[lane] : 0u;
+   } else {
+    const int hq = (lane & 15) >> 2, Gq = lane >> 4;
+    const uint4* qr = reinterpret_cast<const uint4*>(
+        a.q + ((size_t)b * a.hq + (size_t)h * a.g_heads + (hq < a.g_heads ? hq : 0)) * D);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint4 u = qr[MK::quad_index(Gq, i)];
+      qw[4 * i] = u.x;
+      qw[4 * i + 1] = u.y;
+      qw[4 * i + 2] = u.z;
+      qw[4 * i + 3] = u.w;
+    }
+    const uint32_t* qg = reinterpret_cast<const uint32_t*>(
+        a.q + ((size_t)b * a.hq + (size_t)h * a.g_heads + (rh < a.g_heads ? rh : 0)) * D);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) qgw[i] = qg[4 * rq + i];
+   }
+  };
   auto query_prologue = [&]() {  // run after the first tiles are in flight, so the two HBM latencies overlap
    if constexpr (KCH) {
-    if (wave < 4)
-      s_qb[wave][lane] = (wave < a.g_heads)
-          ? reinterpret_cast<const uint32_t*>(a.q + ((size_t)b * a.hq + h * a.g_heads + wave) * D)[lane] : 0u;
+    if (wave < 4) s_qb[wave][lane] = qw[0];
     __syncthreads();
    } else {
     // A operand of the block-scaled QK^T: lane (G = lane / 16, row m = lane % 16), row
@@ -906,18 +930,6 @@ __device__ __forceinline__ void run_item(const SplitArgs& a, const int b, const 
     {
       const int m = lane & 15, hq = m >> 2, slot = m & 3, Gq = lane >> 4;
       const bool hv = hq < a.g_heads;
-      const uint4* qr = reinterpret_cast<const uint4*>(
-          a.q + ((size_t)b * a.hq + (size_t)h * a.g_heads + (hv ? hq : 0)) * D);
-      // the lane's 32 query values (bf16 pairs, MxKey::local order): four 16-byte loads
-      uint32_t qw[16];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const uint4 u = qr[MK::quad_index(Gq, i)];
-        qw[4 * i] = u.x;
-        qw[4 * i + 1] = u.y;
-        qw[4 * i + 2] = u.z;
-        qw[4 * i + 3] = u.w;
-      }
       float qv[32];
 #pragma unroll
       for (int bb = 0; bb < 32; ++bb) {
@@ -960,12 +972,10 @@ __device__ __forceinline__ void run_item(const SplitArgs& a, const int b, const 
     // sigma' * sum of head rh's query over each key group: lane rq takes channels 8 rq .. 8 rq + 7
     {
       const bool hv = rh < a.g_heads;
-      const uint32_t* qg = reinterpret_cast<const uint32_t*>(
-          a.q + ((size_t)b * a.hq + (size_t)h * a.g_heads + (hv ? rh : 0)) * D);
       float part = 0.f;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const uint32_t w = hv ? qg[4 * rq + i] : 0u;
+        const uint32_t w = hv ? qgw[i] : 0u;
         part += __uint_as_float(w << 16) + __uint_as_float(w & 0xFFFF0000u);
       }
 #pragma unroll
@@ -1095,40 +1105,54 @@ __device__ __forceinline__ void run_item(const SplitArgs& a, const int b, const 
   const uint32_t ring_lds = lds_addr(ring);
   // the wave's tiles in order: unit wave, wave + kWaves, ...; TPU tiles per unit
   auto tile_start = [&](int k) { return r0 + (wave + kWaves * (k / TPU)) * UNIT + (k % TPU) * kTile; };
-  auto issue = [&](int k) {  // HBM -> LDS slot k % NS (per-lane offsets fixed, per-tile offset scalar)
-    const uint32_t t0 = (uint32_t)tile_start(k);
+  // tile at t0: HBM -> LDS slot k % NS (per-lane offsets fixed, tile offset scalar), from the
+  // given buffer resources
+  auto issue_from = [&](int k, uint32_t t0, const __amdgpu_buffer_rsrc_t& RK, const __amdgpu_buffer_rsrc_t& RV,
+                        const __amdgpu_buffer_rsrc_t& RKS, const __amdgpu_buffer_rsrc_t& RKZ,
+                        const __amdgpu_buffer_rsrc_t& RVS, const __amdgpu_buffer_rsrc_t& RVZ) {
     unsigned char* st = ring + (k % NS) * ST::BYTES;
     // scale blocks first, in layout order (see Stage), then K rows and V words
     if constexpr (!KCH) {
 #pragma unroll
-      for (int m = 0; m < ST::KSL; ++m) dma4(rks, 4 * lane + 256 * m, t0 * NGK * 2, st + ST::SOFF + m * 256);
+      for (int m = 0; m < ST::KSL; ++m) dma4(RKS, 4 * lane + 256 * m, t0 * NGK * 2, st + ST::SOFF + m * 256);
 #pragma unroll
-      for (int m = 0; m < ST::KSL; ++m) dma4(rkz, 4 * lane + 256 * m, t0 * NGK * 2, st + ST::SOFF + ST::KSB + m * 256);
+      for (int m = 0; m < ST::KSL; ++m) dma4(RKZ, 4 * lane + 256 * m, t0 * NGK * 2, st + ST::SOFF + ST::KSB + m * 256);
     }
     if constexpr (!VCH) {
 #pragma unroll
-      for (int m = 0; m < ST::VSL; ++m) dma4(rvs, 4 * lane + 256 * m, t0 * NGV * 2, st + ST::VSOFF + m * 256);
+      for (int m = 0; m < ST::VSL; ++m) dma4(RVS, 4 * lane + 256 * m, t0 * NGV * 2, st + ST::VSOFF + m * 256);
 #pragma unroll
-      for (int m = 0; m < ST::VSL; ++m) dma4(rvz, 4 * lane + 256 * m, t0 * NGV * 2, st + ST::VSOFF + ST::VSB + m * 256);
+      for (int m = 0; m < ST::VSL; ++m) dma4(RVZ, 4 * lane + 256 * m, t0 * NGV * 2, st + ST::VSOFF + ST::VSB + m * 256);
     }
     if constexpr (KCH) {
 #pragma unroll
-      for (int g2 = 0; g2 < NGT; ++g2) dma4(rks, 4 * lane, (t0 / GRP + g2) * D * 2, st + ST::KCOFF + g2 * 256);
+      for (int g2 = 0; g2 < NGT; ++g2) dma4(RKS, 4 * lane, (t0 / GRP + g2) * D * 2, st + ST::KCOFF + g2 * 256);
 #pragma unroll
       for (int g2 = 0; g2 < NGT; ++g2)
-        dma4(rkz, 4 * lane, (t0 / GRP + g2) * D * 2, st + ST::KCOFF + (NGT + g2) * 256);
+        dma4(RKZ, 4 * lane, (t0 / GRP + g2) * D * 2, st + ST::KCOFF + (NGT + g2) * 256);
     }
     if constexpr (VCH) {
 #pragma unroll
-      for (int g2 = 0; g2 < NGT; ++g2) dma4(rvs, 4 * lane, (t0 / GRP + g2) * D * 2, st + ST::VCOFF + g2 * 256);
+      for (int g2 = 0; g2 < NGT; ++g2) dma4(RVS, 4 * lane, (t0 / GRP + g2) * D * 2, st + ST::VCOFF + g2 * 256);
 #pragma unroll
       for (int g2 = 0; g2 < NGT; ++g2)
-        dma4(rvz, 4 * lane, (t0 / GRP + g2) * D * 2, st + ST::VCOFF + (NGT + g2) * 256);
+        dma4(RVZ, 4 * lane, (t0 / GRP + g2) * D * 2, st + ST::VCOFF + (NGT + g2) * 256);
     }
 #pragma unroll
-    for (int i = 0; i < KW / 4; ++i) dma16(rk, lane * KW * 4 + 16 * i, t0 * KW * 4, st + ST::KOFF + i * 1024);
+    for (int i = 0; i < KW / 4; ++i) dma16(RK, lane * KW * 4 + 16 * i, t0 * KW * 4, st + ST::KOFF + i * 1024);
 #pragma unroll
-    for (int i = 0; i < VW / 2; ++i) dma16(rv, 16 * lane + 1024 * i, (t0 / E) * D * 4, st + ST::VOFF + i * 1024);
+    for (int i = 0; i < VW / 2; ++i) dma16(RV, 16 * lane + 1024 * i, (t0 / E) * D * 4, st + ST::VOFF + i * 1024);
+  };
+  auto issue = [&](int k) { issue_from(k, (uint32_t)tile_start(k), rk, rv, rks, rkz, rvs, rvz); };
+  // the first tiles: tile k, or (a wave with fewer) the same loads on resources of no bytes (out
+  // of range: no memory read, zeros into a slot nobody reads).  The compiler counts loads to the
+  // LDS in its waits only along straight-line code (at a join of branches holding such loads it
+  // waits for all of them), and the query loads are waited for after these.
+  auto issue_first = [&](int k, bool live) {
+    const uint32_t kb = live ? (uint32_t)a.tcap * KW * 4 : 0u, vb = live ? (uint32_t)(a.tcap / E) * D * 4 : 0u;
+    const uint32_t ksz = live ? kscale_bytes : 0u, vsz = live ? vscale_bytes : 0u;  // scalar selects
+    issue_from(k, live ? (uint32_t)tile_start(k) : 0u, rsrc(kbase, kb), rsrc(vbase, vb), rsrc(ksb, ksz),
+               rsrc(kzb, ksz), rsrc(vsb, vsz), rsrc(vzb, vsz));
   };
   auto read = [&](Tile& tl, int k, int ahead) {  // wait for slot k % NS, LDS -> registers
     switch (ahead) {  // loads issued after this tile's that may still be in flight
@@ -1498,16 +1522,19 @@ __device__ __forceinline__ void run_item(const SplitArgs& a, const int b, const 
 
   int nt = 0;  // tiles of this wave
   while (tile_start(nt) < r1) ++nt;
-#pragma unroll
-  for (int k = 0; k < NS - 1; ++k)
-    if (k < nt) issue(k);
-  query_prologue();
   // The SIMD issues from the oldest ready wave first, so the work-groups
   // dispatched first would race ahead and the last ones would finish alone.
   // Each wave lowers its priority at every quarter of its tiles: waves that
-  // are behind win the arbitration and all of them finish together.
+  // are behind win the arbitration and all of them finish together.  The
+  // prologue runs at the top priority: at the default one, a wave still
+  // building its query operand waited behind the loops of the waves around it.
   const int q1 = nt / 4, q2 = nt / 2, q3 = (3 * nt) / 4;
   __builtin_amdgcn_s_setprio(3);
+  query_load();
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int k = 0; k < NS; ++k) issue_first(k, k < nt);
+  query_prologue();
   // Tiles start in increasing order and stop below T, so only the wave's last
   // tile can reach past T.  It is peeled off the loop: a loop body with one
   // instance of the tile code keeps its accumulators in the same registers
@@ -1517,20 +1544,22 @@ __device__ __forceinline__ void run_item(const SplitArgs& a, const int b, const 
     if (k == q1) __builtin_amdgcn_s_setprio(2);
     if (k == q2) __builtin_amdgcn_s_setprio(1);
     if (k == q3) __builtin_amdgcn_s_setprio(0);
-    if (k + NS - 1 < nt) issue(k + NS - 1);
     Tile tl;
     read(tl, k, min(NS - 1, nt - 1 - k));
+    if (k + NS < nt) issue(k + NS);  // the slot just read: NS tiles in flight while this one is processed
     process(tl, tile_start(k), std::false_type{});
   }
   if (nt > 0) {
     __builtin_amdgcn_s_setprio(0);  // q3 <= nt - 1: the last tile always ran at the lowest priority
     Tile tl;
-    read(tl, nt - 1, 0);
+    read(tl, nt - 1, 0);  // (and any loads on no bytes: done before the rings are reused)
     const int t0k = tile_start(nt - 1);
     if (t0k + kTile > T)
       process(tl, t0k, std::true_type{});
     else
       process(tl, t0k, std::false_type{});
+  } else {
+    wait_vmcnt<0>();  // the loads on no bytes write the ring: done before it is reused
   }
 
   __builtin_amdgcn_s_setprio(3);  // the epilogue and the merge are the tail of the launch
@@ -1745,8 +1774,8 @@ __device__ __forceinline__ void window_item(const SplitArgs& a, const int b, con
   if (tid == 0) a.counters[bh] = 0;
 }
 
-// Grids that fit the device in one round: the grid's own map (x = (sequence,
-// KV head) pair, y = range; consecutive work-groups land on different XCDs).
+// Grids that fit the device in one round: the grid's own map (work-group
+// (x, y): window row y of pair x, or range y of pair (x + y) mod pairs).
 // Larger grids (ragged batches of at most kMapMaxB sequences) run persistent:
 // one round of work-groups takes work items from a device-wide counter, longest
 // first (map_select), until the items run out; the last work-group to leave
@@ -1757,13 +1786,19 @@ template <int BITS, bool KCH, bool VCH, int GRP>
 __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(waves_per_simd<BITS, KCH, VCH, GRP>())))
 void split_decode(const SplitArgs a) {
   if (!a.persistent) {
-    const int b = blockIdx.x / a.hkv;
+    // Work-group (x, y) runs pair x's window row y (y < win_wgs), or range
+    // y - win_wgs of pair (x + y) mod B*Hkv: work-groups are dealt to the XCDs
+    // round-robin in launch order, and the rotation spreads each pair's ranges
+    // over all of them (without it, every range of pair x ran on XCD x % 8).
+    const bool win = (int)blockIdx.y < a.win_wgs;
+    const int pair = win ? (int)blockIdx.x : ((int)blockIdx.x + (int)blockIdx.y) % (int)gridDim.x;
+    const int b = pair / a.hkv;
     const int T = min(max(a.seq_lens[b], 0), a.tcap);
-    if ((int)blockIdx.y < a.win_wgs) {  // dispatched first: run beside the ranges, not after them
-      window_item(a, b, blockIdx.x % a.hkv, T, blockIdx.y);
+    if (win) {  // dispatched first: run beside the ranges, not after them
+      window_item(a, b, pair % a.hkv, T, blockIdx.y);
       return;
     }
-    run_item<BITS, KCH, VCH, GRP>(a, b, blockIdx.x % a.hkv, (int)blockIdx.y - a.win_wgs, T, nullptr);
+    run_item<BITS, KCH, VCH, GRP>(a, b, pair % a.hkv, (int)blockIdx.y - a.win_wgs, T, nullptr);
     return;
   }
   // window work-groups take the first blocks (dispatched first) and leave
