@@ -52,9 +52,25 @@ int check_dims(const foscar_dims* d, bool need_heads_ratio) {
   if (d->head_dim != foscar::kHeadDim) return FOSCAR_EUNSUPPORTED;
   if (need_heads_ratio) {
     if (d->num_q_heads % d->num_kv_heads != 0) return FOSCAR_EINVAL;
-    if (d->num_q_heads / d->num_kv_heads > foscar::kMaxG) return FOSCAR_EUNSUPPORTED;
+    if (d->num_q_heads / d->num_kv_heads > foscar::kMaxGqa) return FOSCAR_EUNSUPPORTED;
   }
   return FOSCAR_OK;
+}
+
+// The kernels serve one work pair of at most kMaxG query heads (a wave's rows).
+// A KV head with G query heads is nq pairs of G / nq heads, nq the smallest
+// divisor of G with G / nq <= kMaxG: pair p of a sequence takes query heads
+// p * G / nq .. + G / nq - 1 (rows stay contiguous) and reads KV head p / nq, so
+// that KV head's cache is read nq times.
+int head_groups(int G) {
+  int nq = 1;
+  while (G / nq > foscar::kMaxG || G % nq != 0) ++nq;
+  return nq;
+}
+foscar_dims work_dims(const foscar_dims* d) {
+  foscar_dims w = *d;
+  w.num_kv_heads = d->num_kv_heads * head_groups(d->num_q_heads / d->num_kv_heads);
+  return w;
 }
 
 int check_decode_shape(const foscar_dims* d, int layout, int group) {
@@ -62,8 +78,9 @@ int check_decode_shape(const foscar_dims* d, int layout, int group) {
   if (rc) return rc;
   if (layout < 0 || layout > 3) return FOSCAR_EINVAL;
   if (!valid_group(group)) return FOSCAR_EUNSUPPORTED;
-  // one grid row of work-groups per (sequence, KV head); per-head byte offsets are 32-bit
-  if ((int64_t)d->batch * d->num_kv_heads > (1 << 22) || d->max_seq_len > (1 << 24)) return FOSCAR_EUNSUPPORTED;
+  // one grid row of work-groups per work pair; per-head byte offsets are 32-bit
+  const int64_t pairs = (int64_t)d->batch * d->num_kv_heads * head_groups(d->num_q_heads / d->num_kv_heads);
+  if (pairs > (1 << 22) || d->max_seq_len > (1 << 24)) return FOSCAR_EUNSUPPORTED;
   if (d->max_seq_len % foscar::kTile != 0) return FOSCAR_EUNSUPPORTED;
   if (layout != 0 && d->max_seq_len % group != 0) return FOSCAR_EUNSUPPORTED;
   return FOSCAR_OK;
@@ -223,6 +240,9 @@ int decode_common(int bits, const foscar_dims* d, const void* q, const void* pk,
     return FOSCAR_EINVAL;
   if (windowed && (!aligned(win_k, 16) || !aligned(win_v, 16) || !aligned(win_lens, 4))) return FOSCAR_EINVAL;
 
+  const int kv_group = head_groups(d->num_q_heads / d->num_kv_heads);
+  const foscar_dims wd = work_dims(d);
+  d = &wd;  // from here on: work pairs (KV heads x kv_group)
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return hip_fail(e);
@@ -273,6 +293,7 @@ int decode_common(int bits, const foscar_dims* d, const void* q, const void* pk,
   sa.hq = d->num_q_heads;
   sa.hkv = d->num_kv_heads;
   sa.g_heads = d->num_q_heads / d->num_kv_heads;
+  sa.kv_group = kv_group;
   sa.tcap = d->max_seq_len;
   sa.splits = splits;
   sa.chunk = chunk;
@@ -428,7 +449,8 @@ int foscar_decode_noalloc(int bits, const foscar_dims* dims, const void* q, cons
   if (dims->batch == 0) return FOSCAR_OK;
   // sizes the static scratch cannot hold fail before any HIP call: the counters, and the
   // partials of the smallest plan (one range per pair)
-  if (counter_bytes(dims) > kScratchCounterBytes || partial_bytes(dims, 1) > kScratchBytes - kScratchCounterBytes)
+  const foscar_dims wd = work_dims(dims);
+  if (counter_bytes(&wd) > kScratchCounterBytes || partial_bytes(&wd, 1) > kScratchBytes - kScratchCounterBytes)
     return FOSCAR_ESCRATCH;
   if (!q || !packed_k || !packed_v || !k_scale || !k_zero || !v_scale || !v_zero || !seq_lens || !out)
     return FOSCAR_EINVAL;
@@ -503,7 +525,8 @@ int foscar_split_plan(const foscar_dims* dims, int bits, int layout, int group, 
     cus = compute_units(dev);
     per_cu = resident_per_cu(dev, bits, layout, group);
   }
-  plan(dims, layout, group, cus, per_cu, splits, chunk);
+  const foscar_dims wd = work_dims(dims);
+  plan(&wd, layout, group, cus, per_cu, splits, chunk);
   return FOSCAR_OK;
 }
 
@@ -534,8 +557,9 @@ int foscar_workspace_reserve(const foscar_dims* dims, int bits, int layout, int 
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return hip_fail(e);
   int32_t splits = 1, chunk = 0;
-  plan(dims, layout, group, compute_units(dev), resident_per_cu(dev, bits, layout, group), &splits, &chunk);
-  return get_workspace(counter_bytes(dims), partial_bytes(dims, splits), (hipStream_t)stream, nullptr, nullptr);
+  const foscar_dims wd = work_dims(dims);
+  plan(&wd, layout, group, compute_units(dev), resident_per_cu(dev, bits, layout, group), &splits, &chunk);
+  return get_workspace(counter_bytes(&wd), partial_bytes(&wd, splits), (hipStream_t)stream, nullptr, nullptr);
 }
 
 void foscar_release(void) {

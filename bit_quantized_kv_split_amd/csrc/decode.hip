@@ -1009,14 +1009,15 @@ __device__ __forceinline__ void run_item(const SplitArgs& a, const int b, const 
   const float cv0 = C::bias(2 * (pq % KPW)), cv1 = C::bias(2 * (pq % KPW) + 1);
   const uint32_t cv0h = splat_f16(cv0), cv1h = splat_f16(cv1), oneh = splat_f16(1.f);
 
-  const uint32_t* kbase = a.pk + bh * (size_t)a.tcap * KW;
-  const uint32_t* vbase = a.pv + bh * (size_t)(a.tcap / E) * D;
+  const size_t bkv = bh / a.kv_group;  // the KV head this pair's query heads attend
+  const uint32_t* kbase = a.pk + bkv * (size_t)a.tcap * KW;
+  const uint32_t* vbase = a.pv + bkv * (size_t)(a.tcap / E) * D;
   const __amdgpu_buffer_rsrc_t rk = rsrc(kbase, (uint32_t)a.tcap * KW * 4);
   const __amdgpu_buffer_rsrc_t rv = rsrc(vbase, (uint32_t)(a.tcap / E) * D * 4);
-  const uint16_t* ksb = a.ks + bh * (size_t)(KCH ? (a.tcap / GRP) * D : a.tcap * NGK);
-  const uint16_t* kzb = a.kz + bh * (size_t)(KCH ? (a.tcap / GRP) * D : a.tcap * NGK);
-  const uint16_t* vsb = a.vs + bh * (size_t)(VCH ? (a.tcap / GRP) * D : a.tcap * NGV);
-  const uint16_t* vzb = a.vz + bh * (size_t)(VCH ? (a.tcap / GRP) * D : a.tcap * NGV);
+  const uint16_t* ksb = a.ks + bkv * (size_t)(KCH ? (a.tcap / GRP) * D : a.tcap * NGK);
+  const uint16_t* kzb = a.kz + bkv * (size_t)(KCH ? (a.tcap / GRP) * D : a.tcap * NGK);
+  const uint16_t* vsb = a.vs + bkv * (size_t)(VCH ? (a.tcap / GRP) * D : a.tcap * NGV);
+  const uint16_t* vzb = a.vz + bkv * (size_t)(VCH ? (a.tcap / GRP) * D : a.tcap * NGV);
   const uint32_t kscale_bytes = KCH ? (uint32_t)(a.tcap / GRP) * D * 2 : (uint32_t)a.tcap * NGK * 2;
   const uint32_t vscale_bytes = VCH ? (uint32_t)(a.tcap / GRP) * D * 2 : (uint32_t)a.tcap * NGV * 2;
   const __amdgpu_buffer_rsrc_t rks = rsrc(ksb, kscale_bytes);
@@ -1661,7 +1662,7 @@ __device__ __forceinline__ void window_item(const SplitArgs& a, const int b, con
   const int t0 = wave * chunk, t1 = min(t0 + chunk, W);
   const size_t row0 = (size_t)b * a.hq + (size_t)h * G;
   const size_t bh = (size_t)b * a.hkv + h;
-  const size_t kv0 = (bh * (size_t)a.win_cap + (size_t)j * CW) * D;
+  const size_t kv0 = ((bh / a.kv_group) * (size_t)a.win_cap + (size_t)j * CW) * D;  // the pair's KV head
   // scores on the matrix cores: v_mfma_f32_16x16x32_bf16 with A = 16 window keys (rows = tokens),
   // B = the query rows (columns; G of 16 used), the contraction over channels in 4 steps of 32.
   // Lane l holds token / query row l % 16 and, at step k, channels 32k + 8(l / 16) .. +7 of both

@@ -9,7 +9,8 @@ namespace foscar {
 constexpr int kHeadDim = 128;   // D
 constexpr int kTile = 64;       // tokens per wave tile (16 quads of 4)
 constexpr int kWaves = 4;       // waves per work-group
-constexpr int kMaxG = 4;        // query heads per KV head served by one wave
+constexpr int kMaxG = 4;        // query heads of one work pair (a wave's query rows)
+constexpr int kMaxGqa = 16;     // query heads per KV head the interface takes (served as groups of <= kMaxG)
 constexpr int kMapMaxB = 1024;   // largest batch the device-side work order handles (64 lanes x 16)
 constexpr int kMaxSplits = 512;  // ranges per sequence (bounds the workspace and the merge passes)
 
@@ -28,8 +29,10 @@ struct SplitArgs {
   float* lse;                // fp32 [B][Hq] or null
   float* o_part;             // fp32 [B][Hq][S][D]   normalised partial output of each range
   float* lse_part;           // fp32 [B][Hq][S]      natural-log lse of each range
-  int32_t* counters;         // [B][Hkv] ranges finished; zero between calls
-  int32_t hq, hkv, g_heads;  // Hq, Hkv, G = Hq / Hkv
+  int32_t* counters;         // [B][pairs] ranges finished; zero between calls
+  // Hq; work pairs per sequence (Hkv * kv_group); query heads per pair (Hq / Hkv / kv_group);
+  // pairs per KV head: pair h of a sequence reads KV head h / kv_group
+  int32_t hq, hkv, g_heads, kv_group;
   int32_t tcap;              // Tcap
   int32_t splits;            // S
   int32_t chunk;             // tokens per range (multiple of the wave unit)

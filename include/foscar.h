@@ -53,7 +53,7 @@ extern "C" {
 #define FOSCAR_OK 0
 #define FOSCAR_EINVAL (-1)       /* null or misaligned pointer, negative size, bad layout/side/bits value,
                                     Hq % Hkv != 0 */
-#define FOSCAR_EUNSUPPORTED (-2) /* head_dim != 128, group not in {32,64,128}, Hq/Hkv > 4,
+#define FOSCAR_EUNSUPPORTED (-2) /* head_dim != 128, group not in {32,64,128}, Hq/Hkv > 16,
                                     max_seq_len not a multiple of 64 (and of group for a
                                     channel-wise side), max_seq_len > 2^24,
                                     batch * num_kv_heads > 2^22 */
@@ -77,7 +77,7 @@ extern "C" {
 typedef struct foscar_dims {
   int32_t batch;        /* B >= 0 sequences (B = 0: nothing to do) */
   int32_t num_q_heads;  /* Hq >= 1 */
-  int32_t num_kv_heads; /* Hkv >= 1, Hq % Hkv == 0, Hq / Hkv <= 4 */
+  int32_t num_kv_heads; /* Hkv >= 1, Hq % Hkv == 0, G = Hq / Hkv <= 16 (see foscar_decode_int2) */
   int32_t head_dim;     /* D; must be 128 */
   int32_t max_seq_len;  /* Tcap: tokens allocated per sequence; multiple of 64, and of
                            `group` when a side is channel-wise */
@@ -87,7 +87,9 @@ typedef struct foscar_dims {
 /*
  * Decode step, 2-bit (foscar_decode_int2) or 4-bit (foscar_decode_int4) codes.
  *
- * q         bf16  [B][Hq][D]
+ * q         bf16  [B][Hq][D]; query head i attends KV head i / G, G = Hq / Hkv <= 16.
+ *           A KV head is read once per group of at most 4 of its query heads
+ *           (G = 8: twice, G = 16: four times; G prime above 4: G times).
  * packed_k  u32   [B][Hkv][Tcap][D*bits/32]   keys packed along channels
  * packed_v  u32   [B][Hkv][Tcap*bits/32][D]   values packed along tokens
  *           E = 32/bits codes per word; word holds E consecutive elements of the
@@ -110,9 +112,14 @@ typedef struct foscar_dims {
  *           (may be NULL)
  * stream    hipStream_t
  *
- * Precision: fp16 matrix-core products with fp32 accumulation; query values
- * must lie in the fp16 range; value scales of a token-wise value side must
- * satisfy |s| < 256.  The first call on a (device, stream) pair may allocate the
+ * Precision: token-wise keys: q K^T on the block-scaled matrix cores, the
+ * query as two e4m3 terms (exact for bf16 values) times the key codes (exact),
+ * products summed in the matrix core to about 14 significant bits of each
+ * 16-token block's largest product, fp32 beyond; channel-wise keys: fp16
+ * products (query times scale as an exact fp16 pair), fp32 accumulation.  P V:
+ * fp16 weights (softmax weights, times the value scale for a token-wise value
+ * side) times the value codes, fp32 accumulation.  Query values must lie in the
+ * fp16 range; value scales of a token-wise value side must satisfy |s| < 256.  The first call on a (device, stream) pair may allocate the
  * split workspace (see foscar_workspace_reserve); later calls of the same or
  * smaller size do not allocate.  Calls on different streams do not share
  * workspace.

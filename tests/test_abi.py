@@ -60,7 +60,8 @@ def _decode(lib, dims, layout=0, group=128, ptr=1):
     (dict(max_seq_len=1 << 25), 0, 128, -2),
     (dict(head_dim=64), 0, 128, -2),
     (dict(num_q_heads=6, num_kv_heads=4), 0, 128, -1),
-    (dict(num_q_heads=16, num_kv_heads=2), 0, 128, -2),     # 8 query heads per KV head
+    (dict(num_q_heads=34, num_kv_heads=2), 0, 128, -2),     # 17 query heads per KV head
+    (dict(batch=(1 << 20) + 1, num_q_heads=16, num_kv_heads=2), 0, 128, -2),  # over 2^22 work pairs (G = 8: two per KV head)
     (dict(max_seq_len=1000), 0, 128, -2),                    # not a multiple of 64
     (dict(max_seq_len=192), 2, 128, -2),                     # channel-wise group of 128 does not divide 192
     (dict(batch=-1), 0, 128, -1),

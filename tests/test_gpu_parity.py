@@ -81,8 +81,11 @@ def test_edge_lengths_and_poisoned_padding(bits, kl, vl, g):
     assert np.all(out[0] == 0) and np.all(np.isneginf(lse[0]))
 
 
-@pytest.mark.parametrize("G", [1, 2, 3, 4])
+@pytest.mark.parametrize("G", [1, 2, 3, 4, 5, 6, 8, 12, 16])
 def test_gqa_ratios(G):
+    """G query heads per KV head; above 4 the library serves a KV head as
+    groups of at most 4 query heads (5: five groups of 1, 6: two of 3, 8: two
+    of 4, 12: three of 4, 16: four of 4), each reading the KV head."""
     spec = synth.Spec(f"gqa_{G}", 13, 2, "token", "channel", 64, 2, 3 * G, 3, 128, 512, lens=(512, 300))
     dev, q, lens = stage_spec(spec)
     out, lse = run(spec, dev)
@@ -185,11 +188,12 @@ def test_persistent_work_order_ragged_with_empty_sequences():
         check(out, lse, ro, rl, f"persistent ragged call {k}")
 
 
-@pytest.mark.parametrize("G", [1, 2, 3])
+@pytest.mark.parametrize("G", [1, 2, 3, 8, 16])
 @pytest.mark.parametrize("splits", ["7", "64"])
 def test_gqa_ratios_through_the_merge(G, splits, monkeypatch):
-    """G = 1-3 query heads per KV head with several ranges per sequence: the
-    merge gives each query row its own wave, and waves past G leave early.  64
+    """G = 1-3, 8 and 16 query heads per KV head with several ranges per
+    sequence: the merge gives each query row of a group its own wave, and waves
+    past the group's rows leave early.  64
     forced ranges give 4096 tokens two blocks of 32 ranges and 2500 tokens a
     block plus a masked remainder."""
     spec = synth.Spec(f"gqa_merge_{G}", 14, 2, "token", "channel", 64, 2, 3 * G, 3, 128, 4096, lens=(4096, 2500))

@@ -82,11 +82,12 @@ def test_window_multi_range_and_persistent(name, cap):
     check(out, lse, ro, rl, spec.name)
 
 
-@pytest.mark.parametrize("G", [1, 3])
+@pytest.mark.parametrize("G", [1, 3, 8])
 def test_window_gqa_ratios_through_the_merge(G, monkeypatch):
-    """G = 1 and 3 query heads per KV head, 64 forced ranges and a window:
+    """G = 1, 3 and 8 query heads per KV head, 64 forced ranges and a window:
     window partials fold into the merge of every query row, including the
-    pairs whose sequence has no cache token."""
+    pairs whose sequence has no cache token (G = 8: two groups of 4 query
+    heads read each KV head's cache and window)."""
     spec = synth.Spec(f"win_gqa_{G}", 15, 2, "token", "token", 128, 3, 3 * G, 3, 128, 4096, lens=(4096, 2500, 0))
     monkeypatch.setenv("FOSCAR_SPLITS", "64")
     dev, q, lens = stage_spec(spec)
