@@ -139,15 +139,19 @@ class DecodeCall:
 
 
 def prepare_decode(bits, q, packed_k, packed_v, k_scale, k_zero, v_scale, v_zero, seq_lens, layout, group,
-                   out=None, lse=None, sm_scale=0.0, stream=None, window=None, noalloc=False):
+                   out=None, lse=None, sm_scale=0.0, stream=None, window=None, noalloc=False, paged=None):
     """Check and marshal a decode step (arguments as foscar_decode_int2/4); returns a DecodeCall.
     ``window`` = (win_k, win_v, win_lens) marshals foscar_decode_window_int2/4 instead;
-    ``noalloc`` marshals foscar_decode_noalloc (out and lse must then be given)."""
+    ``noalloc`` marshals foscar_decode_noalloc (out and lse must then be given);
+    ``paged`` = block_table int32 [B, blocks per sequence] marshals foscar_decode_paged_int2/4,
+    with packed_k .. v_zero the block pools (include/foscar.h; block_size = packed_k.shape[2])."""
     import torch
     if bits not in (2, 4):
         raise ValueError(f"bits must be 2 or 4, got {bits}")
     if noalloc and (out is None or lse is None or window is not None):
         raise ValueError("foscar_decode_noalloc takes caller-provided out and lse, and no window")
+    if paged is not None and (noalloc or window is not None):
+        raise ValueError("the paged decode takes no window and allocates its workspace")
     lib = _lib.load()
     dev = q.device
     _require(q, "q", torch.bfloat16, dev)
@@ -159,7 +163,17 @@ def prepare_decode(bits, q, packed_k, packed_v, k_scale, k_zero, v_scale, v_zero
     if q.dim() != 3:
         raise ValueError("q must be [B, Hq, D]")
     B, Hq, D = (int(x) for x in q.shape)
-    Hkv, Tcap = _check_cache(bits, packed_k, packed_v, k_scale, k_zero, v_scale, v_zero, int(layout), group, B, D)
+    if paged is None:
+        Hkv, Tcap = _check_cache(bits, packed_k, packed_v, k_scale, k_zero, v_scale, v_zero, int(layout), group, B, D)
+    else:  # pools: the contiguous layout with (num_blocks, block_size) in place of (B, Tcap)
+        block_table = paged
+        _require(block_table, "block_table", torch.int32, dev)
+        if packed_k.dim() != 4 or block_table.dim() != 2 or int(block_table.shape[0]) != B:
+            raise ValueError("packed_k must be [num_blocks, Hkv, block_size, D*bits/32] and block_table [B, blocks]")
+        num_blocks = int(packed_k.shape[0])
+        Hkv, block_size = _check_cache(bits, packed_k, packed_v, k_scale, k_zero, v_scale, v_zero, int(layout), group,
+                                       num_blocks, D)
+        Tcap = int(block_table.shape[1]) * block_size
     _shape(seq_lens, "seq_lens", (B,))
     if out is None:
         out = torch.empty((B, Hq, D), dtype=torch.bfloat16, device=dev)
@@ -181,9 +195,14 @@ def prepare_decode(bits, q, packed_k, packed_v, k_scale, k_zero, v_scale, v_zero
         call._fn = lib.foscar_decode_noalloc
         call._args = (int(bits),) + call._args
         call._name = "foscar_decode_noalloc"
+    if paged is not None:
+        call._fn = lib.foscar_decode_paged_int2 if bits == 2 else lib.foscar_decode_paged_int4
+        call._args = call._args[:8] + (_ptr(block_table), int(block_size), int(num_blocks)) + call._args[8:]
+        call._name = f"foscar_decode_paged_int{bits}"
     call._dev = dev.index if dev.index is not None else torch.cuda.current_device()
     call.out, call.lse = out, lse
-    call._keep = (dims, q, packed_k, packed_v, k_scale, k_zero, v_scale, v_zero, seq_lens)
+    call._keep = (dims, q, packed_k, packed_v, k_scale, k_zero, v_scale, v_zero, seq_lens,
+                  block_table if paged is not None else None)
     if window is not None:
         win_k, win_v, win_lens = window
         _require(win_k, "win_k", torch.bfloat16, dev)
@@ -245,6 +264,29 @@ def foscar_decode_window_int4(q, packed_k, packed_v, k_scale, k_zero, v_scale, v
     """4-bit decode step plus a bf16 window of recent tokens [B, Hkv, W, D] (include/foscar.h)."""
     return _decode_window(4, q, packed_k, packed_v, k_scale, k_zero, v_scale, v_zero, seq_lens, layout, group, win_k,
                           win_v, win_lens, out, lse, sm_scale, stream)
+
+
+def foscar_decode_paged_int2(q, k_pool, v_pool, k_scale, k_zero, v_scale, v_zero, block_table, seq_lens, layout,
+                             group, out=None, lse=None, sm_scale=0.0, stream=None):
+    """2-bit decode step over a paged cache: block pools [num_blocks, Hkv, block_size, ..] and
+    block_table int32 [B, max_seq_len / block_size] (include/foscar.h). Returns (out, lse)."""
+    return prepare_decode(2, q, k_pool, v_pool, k_scale, k_zero, v_scale, v_zero, seq_lens, layout, group, out, lse,
+                          sm_scale, stream, paged=block_table)()
+
+
+def foscar_decode_paged_int4(q, k_pool, v_pool, k_scale, k_zero, v_scale, v_zero, block_table, seq_lens, layout,
+                             group, out=None, lse=None, sm_scale=0.0, stream=None):
+    """4-bit decode step over a paged cache (see foscar_decode_paged_int2). Returns (out, lse)."""
+    return prepare_decode(4, q, k_pool, v_pool, k_scale, k_zero, v_scale, v_zero, seq_lens, layout, group, out, lse,
+                          sm_scale, stream, paged=block_table)()
+
+
+def decode_paged(q, k_pool, v_pool, k_scale, k_zero, v_scale, v_zero, block_table, seq_lens, *, bits,
+                 k_layout="token", v_layout="token", group=128, sm_scale=0.0, out=None, lse=None, stream=None):
+    """Decode step over a paged cache (pools and block table as foscar_decode_paged_int2)."""
+    fn = foscar_decode_paged_int2 if bits == 2 else foscar_decode_paged_int4
+    return fn(q, k_pool, v_pool, k_scale, k_zero, v_scale, v_zero, block_table, seq_lens,
+              layout_bits(k_layout, v_layout), group, out, lse, sm_scale, stream)
 
 
 def decode(q, packed_k, packed_v, k_scale, k_zero, v_scale, v_zero, seq_lens, *, bits, k_layout="token",

@@ -12,7 +12,7 @@ LIB_PATH = os.path.join(HERE, "libfoscar.so")
 # Names declared in include/foscar.h, in order.
 EXPORTS = [
     "foscar_decode_int2", "foscar_decode_int4", "foscar_decode_noalloc", "foscar_decode_window_int2",
-    "foscar_decode_window_int4",
+    "foscar_decode_window_int4", "foscar_decode_paged_int2", "foscar_decode_paged_int4",
     "foscar_quantize_int2", "foscar_quantize_int4", "foscar_pack", "foscar_unpack", "foscar_packed_bytes",
     "foscar_scale_count", "foscar_workspace_reserve", "foscar_release", "foscar_split_plan", "foscar_occupancy",
     "foscar_record_next_launch",
@@ -47,6 +47,10 @@ def load():
     for name in ("foscar_decode_window_int2", "foscar_decode_window_int4"):
         f = getattr(lib, name)
         f.argtypes = [D, P, P, P, P, P, P, P, P, I, I, P, P, P, ctypes.c_int32, P, P, P]
+        f.restype = I
+    for name in ("foscar_decode_paged_int2", "foscar_decode_paged_int4"):
+        f = getattr(lib, name)
+        f.argtypes = [D, P, P, P, P, P, P, P, P, ctypes.c_int32, ctypes.c_int32, P, I, I, P, P, P]
         f.restype = I
     for name in ("foscar_quantize_int2", "foscar_quantize_int4"):
         f = getattr(lib, name)

@@ -101,15 +101,15 @@ int compute_units(int device) {
 
 // Work-groups of the (bits, layout, group) kernel one CU of `device` holds at
 // once (cached; 4 when the runtime cannot say, e.g. without a GPU).
-int resident_per_cu(int device, int bits, int layout, int group) {
-  const long long key = (((long long)device * 8 + bits) * 4 + layout) * 256 + group;
+int resident_per_cu(int device, int bits, int layout, int group, bool paged = false) {
+  const long long key = ((((long long)device * 8 + bits) * 4 + layout) * 256 + group) * 2 + (paged ? 1 : 0);
   {
     std::lock_guard<std::mutex> lk(g_ws_mutex);
     auto it = g_occ.find(key);
     if (it != g_occ.end()) return it->second;
   }
   int n = 0;
-  if (foscar::decode_occupancy(bits, (layout & FOSCAR_K_CHANNEL) != 0, (layout & FOSCAR_V_CHANNEL) != 0, group, &n) !=
+  if (foscar::decode_occupancy(bits, (layout & FOSCAR_K_CHANNEL) != 0, (layout & FOSCAR_V_CHANNEL) != 0, group, paged, &n) !=
           hipSuccess || n <= 0)
     return 4;
   std::lock_guard<std::mutex> lk(g_ws_mutex);
@@ -122,7 +122,7 @@ int resident_per_cu(int device, int bits, int layout, int group) {
 // at most 4096 tokens so ragged batches balance, every range a multiple of the
 // wave unit.
 void plan(const foscar_dims* d, int layout, int group, int cus, int per_cu, int32_t* splits, int32_t* chunk,
-          int extra_per_pair = 0) {
+          int extra_per_pair = 0, int max_chunk = 0) {
   const int unit = unit_tokens(layout, group);
   const int tcap = d->max_seq_len;
   const int units = tcap / unit;
@@ -149,6 +149,8 @@ void plan(const foscar_dims* d, int layout, int group, int cus, int per_cu, int3
     if (s < by_len) s = by_len;
   }
   if (s > foscar::kMaxSplits) s = foscar::kMaxSplits;
+  // a paged cache: ranges of at most max_chunk tokens (the caller checks that this fits kMaxSplits)
+  if (max_chunk > 0) s = std::max(s, ((long long)units + max_chunk / unit - 1) / (max_chunk / unit));
   if (s > units) s = units;
   if (s < 1) s = 1;
   const long long per = (units + s - 1) / s;
@@ -222,7 +224,8 @@ int decode_common(int bits, const foscar_dims* d, const void* q, const void* pk,
                   const void* kz, const void* vs, const void* vz, const int32_t* seq_lens, int layout, int group,
                   void* out, float* lse, void* stream, bool windowed = false, const void* win_k = nullptr,
                   const void* win_v = nullptr, const int32_t* win_lens = nullptr, int32_t win_cap = 0,
-                  const FixedWorkspace* fixed = nullptr) {
+                  const FixedWorkspace* fixed = nullptr, const int32_t* block_table = nullptr, int32_t block_size = 0,
+                  int32_t num_blocks = 0) {
   const foscar::LaunchEvents ev = g_next_events;  // consumed by this call whether or not it launches
   g_next_events = foscar::LaunchEvents{};
   int rc = check_decode_shape(d, layout, group);
@@ -239,6 +242,7 @@ int decode_common(int bits, const foscar_dims* d, const void* q, const void* pk,
       !aligned(vz, 16) || !aligned(q, 4) || !aligned(seq_lens, 4) || !aligned(out, 4) || !aligned(lse, 4))
     return FOSCAR_EINVAL;
   if (windowed && (!aligned(win_k, 16) || !aligned(win_v, 16) || !aligned(win_lens, 4))) return FOSCAR_EINVAL;
+  const bool paged = block_table != nullptr;
 
   const int kv_group = head_groups(d->num_q_heads / d->num_kv_heads);
   const foscar_dims wd = work_dims(d);
@@ -247,8 +251,9 @@ int decode_common(int bits, const foscar_dims* d, const void* q, const void* pk,
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return hip_fail(e);
   int32_t splits = 1, chunk = foscar::kTile;
-  const int cus = compute_units(dev), per_cu = resident_per_cu(dev, bits, layout, group);
-  plan(d, layout, group, cus, per_cu, &splits, &chunk);
+  const int cus = compute_units(dev), per_cu = resident_per_cu(dev, bits, layout, group, paged);
+  // paged: a range of at most 63 blocks' tokens touches at most 64 blocks (one per lane), aligned or not
+  plan(d, layout, group, cus, per_cu, &splits, &chunk, 0, paged ? 63 * block_size : 0);
   // the window is attended inside the decode launch by win_wgs more work-groups per pair: 1, 2, 4
   // or 8, with chunks of at most 4096 / 8 = 512 = kFusedWindowMax tokens.  A one-round grid has few
   // pairs: its window work-groups take chunks of at most 128 tokens where 8 allow it, beside the
@@ -304,6 +309,9 @@ int decode_common(int bits, const foscar_dims* d, const void* q, const void* pk,
   sa.persistent = ((long long)splits * d->batch * d->num_kv_heads > (long long)sa.grid_wgs &&
                    d->batch <= foscar::kMapMaxB) ? 1 : 0;
   sa.work_ctr = counters + (size_t)d->batch * d->num_kv_heads;
+  sa.block_table = block_table;
+  sa.block_size = block_size;
+  sa.num_blocks = num_blocks;
   sa.win_o = nullptr;
   sa.win_lse = nullptr;
   sa.win_slots = 0;
@@ -465,6 +473,41 @@ int foscar_decode_noalloc(int bits, const foscar_dims* dims, const void* q, cons
                        out, lse, stream, false, nullptr, nullptr, nullptr, 0, &ws);
 }
 
+namespace {
+int decode_paged(int bits, const foscar_dims* dims, const void* q, const void* k_pool, const void* v_pool,
+                 const void* k_scale, const void* k_zero, const void* v_scale, const void* v_zero,
+                 const int32_t* block_table, int32_t block_size, int32_t num_blocks, const int32_t* seq_lens,
+                 int layout, int group, void* out, float* lse, void* stream) {
+  int rc = check_decode_shape(dims, layout, group);
+  if (rc) return rc;
+  if (!block_table || !aligned(block_table, 4) || num_blocks < 1 || block_size < 1) return FOSCAR_EINVAL;
+  // blocks of whole tiles (and whole groups of a channel-wise side); the logical capacity
+  // max_seq_len is a whole number of blocks, in at most kMaxSplits ranges of 63 blocks' tokens
+  if (block_size % foscar::kTile != 0 || block_size > 65536) return FOSCAR_EUNSUPPORTED;
+  if (layout != 0 && block_size % group != 0) return FOSCAR_EUNSUPPORTED;
+  if (dims->max_seq_len % block_size != 0) return FOSCAR_EUNSUPPORTED;
+  if ((int64_t)dims->max_seq_len > (int64_t)foscar::kMaxSplits * 63 * block_size) return FOSCAR_EUNSUPPORTED;
+  return decode_common(bits, dims, q, k_pool, v_pool, k_scale, k_zero, v_scale, v_zero, seq_lens, layout, group, out,
+                       lse, stream, false, nullptr, nullptr, nullptr, 0, nullptr, block_table, block_size, num_blocks);
+}
+}  // namespace
+
+int foscar_decode_paged_int2(const foscar_dims* dims, const void* q, const void* k_pool, const void* v_pool,
+                             const void* k_scale, const void* k_zero, const void* v_scale, const void* v_zero,
+                             const int32_t* block_table, int32_t block_size, int32_t num_blocks,
+                             const int32_t* seq_lens, int layout, int group, void* out, float* lse, void* stream) {
+  return decode_paged(2, dims, q, k_pool, v_pool, k_scale, k_zero, v_scale, v_zero, block_table, block_size,
+                      num_blocks, seq_lens, layout, group, out, lse, stream);
+}
+
+int foscar_decode_paged_int4(const foscar_dims* dims, const void* q, const void* k_pool, const void* v_pool,
+                             const void* k_scale, const void* k_zero, const void* v_scale, const void* v_zero,
+                             const int32_t* block_table, int32_t block_size, int32_t num_blocks,
+                             const int32_t* seq_lens, int layout, int group, void* out, float* lse, void* stream) {
+  return decode_paged(4, dims, q, k_pool, v_pool, k_scale, k_zero, v_scale, v_zero, block_table, block_size,
+                      num_blocks, seq_lens, layout, group, out, lse, stream);
+}
+
 int foscar_quantize_int2(const foscar_dims* dims, const void* k_src, const void* v_src, int32_t src_tokens,
                          const int32_t* start, const int32_t* count, int layout, int group, void* packed_k,
                          void* packed_v, void* k_scale, void* k_zero, void* v_scale, void* v_zero, void* stream) {
@@ -542,7 +585,7 @@ int foscar_occupancy(int bits, int layout, int group, int32_t* wgs_per_cu) {
   if ((bits != 2 && bits != 4) || !valid_group(group)) return FOSCAR_EUNSUPPORTED;
   int n = 0;
   const hipError_t e = foscar::decode_occupancy(bits, (layout & FOSCAR_K_CHANNEL) != 0, (layout & FOSCAR_V_CHANNEL) != 0,
-                                                group, &n);
+                                                group, false, &n);
   if (e != hipSuccess) return hip_fail(e);
   *wgs_per_cu = n;
   return FOSCAR_OK;

@@ -41,6 +41,12 @@ struct SplitArgs {
   int32_t grid_wgs;          // persistent grid size (one round of resident work-groups)
   int32_t batch;             // B
   int32_t* work_ctr;         // [2] items taken, work-groups left; zero between calls
+  // paged cache (block_table != null): pk .. vz are pools of num_blocks blocks of block_size
+  // tokens, [num_blocks][Hkv][block_size][..] in the layouts above with Tcap = block_size, and
+  // logical block j of sequence b (tokens j * block_size ..) is pool block block_table[b][j]
+  const int32_t* block_table;  // [B][Tcap / block_size]
+  int32_t block_size;          // multiple of 64 (and of g for a channel-wise side)
+  int32_t num_blocks;
   float* win_o;              // fp32 [B][Hq][win_slots][D] normalised outputs over a full-precision window, or null
   float* win_lse;            // fp32 [B][Hq][win_slots] their natural-log lse (-inf: no window token)
   int32_t win_slots;         // window partials per row (0: no window)
@@ -65,10 +71,14 @@ struct LaunchEvents {
   hipEvent_t stop = nullptr;
 };
 hipError_t launch_decode(int bits, bool k_channel, bool v_channel, int group, int batch, int hkv,
-                         const SplitArgs& sa, hipStream_t stream, const LaunchEvents& ev);
+                         const SplitArgs& sa, hipStream_t stream, const LaunchEvents& ev);  // paged: sa.block_table
 
 // Work-groups of the decode kernel for (bits, layout sides, group) one CU holds at once.
-hipError_t decode_occupancy(int bits, bool k_channel, bool v_channel, int group, int* per_cu);
+hipError_t decode_occupancy(int bits, bool k_channel, bool v_channel, int group, bool paged, int* per_cu);
+// the paged-cache instances (decode_paged.hip)
+hipError_t launch_decode_paged(int bits, bool k_channel, bool v_channel, int group, int batch, int hkv,
+                               const SplitArgs& sa, hipStream_t stream, const LaunchEvents& ev);
+hipError_t decode_occupancy_paged(int bits, bool k_channel, bool v_channel, int group, int* per_cu);
 // Quantise tokens [start_b, start_b + count_b) of new keys / values into the cache (quant.hip).
 hipError_t launch_quantize(int bits, bool k_channel, bool v_channel, int group, int batch, int hkv, int tcap,
                            int n_src, const void* k_src, const void* v_src, const int32_t* start, const int32_t* count,

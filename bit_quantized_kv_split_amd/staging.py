@@ -39,3 +39,26 @@ def stage(spec_shape, bits, q, seq_lens, head_fn, scale_shapes, device="cuda", s
                 out[f"{key}_{part}"][b].copy_(torch.from_numpy(np.ascontiguousarray(head[f"{key}_{part}"])))
         torch.cuda.synchronize(dev)
     return out
+
+
+def stage_paged(bits, q, seq_lens, pool, block_table, device="cuda"):
+    """Device tensors of a paged decode step: pools (codes packed on the GPU with
+    ``foscar_pack``, one block standing for one sequence of block_size tokens)
+    from ``pool`` (k_codes / v_codes uint8 [NB, Hkv, P, D], scales / offsets
+    fp16), the block table int32 [B, blocks] and the query / lengths.  Keys:
+    q, seq_lens, block_table, k_pool, v_pool, k_scale, k_zero, v_scale, v_zero."""
+    dev = torch.device(device)
+    NB, H, P, D = pool["k_codes"].shape
+    out = {
+        "q": torch.from_numpy(np.ascontiguousarray(q, np.float32)).to(torch.bfloat16).to(dev),
+        "seq_lens": torch.from_numpy(np.ascontiguousarray(seq_lens, np.int32)).to(dev),
+        "block_table": torch.from_numpy(np.ascontiguousarray(block_table, np.int32)).to(dev),
+    }
+    for side, key in ((FOSCAR_SIDE_K, "k"), (FOSCAR_SIDE_V, "v")):
+        codes = torch.from_numpy(np.ascontiguousarray(pool[key + "_codes"], np.uint8)).to(dev)
+        packed = torch.empty(packed_shape(bits, side, NB, H, P, D), dtype=torch.int32, device=dev)
+        out[key + "_pool"] = foscar_pack(bits, side, codes, packed=packed)
+        for part in ("scale", "zero"):
+            out[f"{key}_{part}"] = torch.from_numpy(np.ascontiguousarray(pool[f"{key}_{part}"])).to(dev)
+    torch.cuda.synchronize(dev)
+    return out

@@ -188,6 +188,45 @@ int foscar_decode_window_int4(const foscar_dims* dims, const void* q, const void
                               const int32_t* win_lens, int32_t win_cap, void* out, float* lse, void* stream);
 
 /*
+ * Decode step over a paged cache (2-bit: foscar_decode_paged_int2, 4-bit:
+ * foscar_decode_paged_int4): the cache of every sequence is a list of blocks
+ * of block_size tokens taken from shared pools through a block table, the
+ * layout of serving systems whose prefix cache shares blocks between requests
+ * (the FOSCAR explainer's integration paragraph names SGLang, which keeps its
+ * KV cache this way).  Attention is the same as foscar_decode_int2/int4 over
+ * the sequence's tokens in logical order.
+ *
+ * Arguments as foscar_decode_int2/int4, except:
+ * k_pool, v_pool, k_scale, k_zero, v_scale, v_zero
+ *              pools of num_blocks blocks: each array's layout of
+ *              foscar_decode_int2 with B = num_blocks and Tcap = block_size,
+ *              e.g. k_pool u32 [num_blocks][Hkv][block_size][D*bits/32],
+ *              v_pool u32 [num_blocks][Hkv][block_size*bits/32][D], token-wise
+ *              scales [num_blocks][Hkv][block_size][D/g], channel-wise
+ *              [num_blocks][Hkv][block_size/g][D] (a channel-wise group never
+ *              crosses a block)
+ * block_table  int32 [B][max_seq_len / block_size] (device): logical block j of
+ *              sequence b (tokens j*block_size ..) is pool block
+ *              block_table[b][j]; entries of blocks at or past T_b are not read
+ *              as block ids (they may hold anything); an entry outside
+ *              [0, num_blocks) of a block below T_b reads that block as zeros
+ * block_size   a multiple of 64 (and of g for a channel-wise side), <= 65536;
+ *              max_seq_len is a whole number of blocks, at most
+ *              512 * 63 * block_size tokens
+ * num_blocks   >= 1
+ * Errors: FOSCAR_EINVAL for a null or misaligned block_table, num_blocks < 1;
+ * FOSCAR_EUNSUPPORTED for a block_size or max_seq_len outside the rules above.
+ */
+int foscar_decode_paged_int2(const foscar_dims* dims, const void* q, const void* k_pool, const void* v_pool,
+                             const void* k_scale, const void* k_zero, const void* v_scale, const void* v_zero,
+                             const int32_t* block_table, int32_t block_size, int32_t num_blocks,
+                             const int32_t* seq_lens, int layout, int group, void* out, float* lse, void* stream);
+int foscar_decode_paged_int4(const foscar_dims* dims, const void* q, const void* k_pool, const void* v_pool,
+                             const void* k_scale, const void* k_zero, const void* v_scale, const void* v_zero,
+                             const int32_t* block_table, int32_t block_size, int32_t num_blocks,
+                             const int32_t* seq_lens, int layout, int group, void* out, float* lse, void* stream);
+
+/*
  * Quantise new keys and values into the cache (2-bit: foscar_quantize_int2,
  * 4-bit: foscar_quantize_int4), in the layouts the decode entry points read.
  *

@@ -23,6 +23,11 @@ What it computes (fp64 throughout):
   explainer's accuracy paragraph names: "full-precision windows of recent
   tokens"); attention is over the union of the T_b dequantised cache tokens
   and the window's tokens, computed by ``attend`` on the concatenation.
+* ``gather_paged`` / ``decode_paged_rows``: a paged cache (pools of blocks of
+  P tokens reached through a block table, the KV layout of the serving
+  systems the explainer's integration paragraph names) is first put back in
+  logical token order, then decoded as above: paging is an addressing
+  indirection, not arithmetic.
 * ``pack_k`` / ``pack_v`` / ``unpack_k`` / ``unpack_v``: the packed code layout
   of the C interface, written from its specification (keys packed along
   channels, values packed along tokens; even elements of a word in its low
@@ -156,6 +161,51 @@ def decode_window_rows(w: dict, win: dict, rows, *, k_layout: str, v_layout: str
         v_all = np.concatenate([v_hat, np.asarray(win["v"], np.float64)[b, h, :wl]], axis=0)
         out[n], lse[n] = attend(q[b, i], k_all, v_all, sm_scale)
     return out, lse
+
+
+def gather_paged(pool: dict, block_table, block_size: int, *, k_layout: str, v_layout: str, group: int) -> dict:
+    """The contiguous cache of a paged one.
+
+    ``pool`` holds k_codes / v_codes [NB, Hkv, P, D] and k_scale / k_zero /
+    v_scale / v_zero with P in place of Tcap ([NB, Hkv, P, D/g] token-wise,
+    [NB, Hkv, P/g, D] channel-wise); ``block_table`` [B, nb] maps logical block
+    j of sequence b (tokens j*P .. j*P + P - 1) to pool block block_table[b, j].
+    An entry outside [0, NB) stands for a block of zeros (codes, scales and
+    offsets).  Returns the same keys laid out [B, Hkv, nb*P, ...] (the layout
+    ``decode_rows`` reads), token t of sequence b at position t.
+    """
+    table = np.asarray(block_table)
+    B, nb = table.shape
+    P = int(block_size)
+    out = {}
+    for name in ("k_codes", "v_codes", "k_scale", "k_zero", "v_scale", "v_zero"):
+        src = np.asarray(pool[name])
+        NB, H = src.shape[0], src.shape[1]
+        rows = src.shape[2]            # per block: P token rows, or P/g group rows
+        dst = np.zeros((B, H, nb * rows) + src.shape[3:], src.dtype)
+        for b in range(B):
+            for j in range(nb):
+                blk = int(table[b, j])
+                if 0 <= blk < NB:
+                    dst[b, :, j * rows:(j + 1) * rows] = src[blk]
+        out[name] = dst
+    return out
+
+
+def decode_paged_rows(w_pool: dict, block_table, block_size: int, rows, *, k_layout: str, v_layout: str,
+                      group: int, sm_scale: float):
+    """``decode_rows`` over a paged cache: w_pool holds q, seq_lens and the pools
+    (see ``gather_paged``); only the blocks below each sequence's length are
+    looked up (table entries past it may hold anything)."""
+    table = np.array(block_table, dtype=np.int64)
+    lens = np.asarray(w_pool["seq_lens"])
+    for b in range(table.shape[0]):
+        used = -(-int(max(lens[b], 0)) // block_size)
+        table[b, used:] = -1
+    w = gather_paged(w_pool, table, block_size, k_layout=k_layout, v_layout=v_layout, group=group)
+    w["q"] = w_pool["q"]
+    w["seq_lens"] = w_pool["seq_lens"]
+    return decode_rows(w, rows, k_layout=k_layout, v_layout=v_layout, group=group, sm_scale=sm_scale)
 
 
 # ---------------------------------------------------------------------------

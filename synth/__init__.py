@@ -358,3 +358,63 @@ def make_window(seed: int, batch: int, num_kv_heads: int, cap: int, lens, head_d
     k = bf16_round((rng.standard_normal((batch, num_kv_heads, cap, head_dim)) * std).astype(np.float32))
     v = bf16_round((rng.standard_normal((batch, num_kv_heads, cap, head_dim)) * std).astype(np.float32))
     return {"k": k, "v": v, "lens": np.asarray(lens, np.int32)}
+
+
+def make_block_table(seed: int, lens, blocks_per_seq: int, block_size: int, extra_blocks: int = 3):
+    """A paged layout for sequences of the given lengths: each sequence's blocks
+    below its length get distinct pool blocks in a seeded random order (the
+    pool has ``extra_blocks`` blocks nobody uses); table entries at or past a
+    sequence's length are -1.  Returns (table int32 [B, blocks_per_seq],
+    num_blocks)."""
+    lens = np.asarray(lens)
+    used = [-(-int(t) // block_size) for t in lens]
+    num_blocks = sum(used) + extra_blocks
+    rng = np.random.default_rng([seed, 0x9A6E])
+    perm = rng.permutation(num_blocks)
+    table = np.full((len(lens), blocks_per_seq), -1, np.int32)
+    k = 0
+    for b, n in enumerate(used):
+        table[b, :n] = perm[k:k + n]
+        k += n
+    return table, num_blocks
+
+
+def make_pool(spec: Spec, table, num_blocks: int, block_size: int, poison: bool = True) -> dict:
+    """Pools of a paged cache holding the spec's sequences: block table[b, j] of
+    every array gets sequence b's tokens j*P .. j*P + P - 1 (P = block_size;
+    scale rows P/g per block for a channel-wise side).  Blocks no sequence
+    uses hold random codes and NaN scales/offsets (``poison``).  Keys as
+    ``make_workload`` with num_blocks in place of B and P in place of Tcap."""
+    P, H, D, g = block_size, spec.num_kv_heads, spec.head_dim, spec.group
+    table = np.asarray(table)
+
+    def rows(layout):
+        return P if layout == TOKEN else P // g
+
+    pool = {}
+    for name, layout, cols in (("k", spec.k_layout, None), ("v", spec.v_layout, None)):
+        pool[name + "_codes"] = np.zeros((num_blocks, H, P, D), np.uint8)
+        sc = (num_blocks, H, rows(layout), D // g if layout == TOKEN else D)
+        pool[name + "_scale"] = np.zeros(sc, np.float16)
+        pool[name + "_zero"] = np.zeros(sc, np.float16)
+    used = np.zeros(num_blocks, bool)
+    for b in range(table.shape[0]):
+        seq = make_sequence(spec, b)
+        for j in range(table.shape[1]):
+            blk = int(table[b, j])
+            if blk < 0:
+                continue
+            used[blk] = True
+            for name, layout in (("k", spec.k_layout), ("v", spec.v_layout)):
+                pool[name + "_codes"][blk] = seq[name + "_codes"][:, j * P:(j + 1) * P]
+                r = rows(layout)
+                for part in ("_scale", "_zero"):
+                    pool[name + part][blk] = seq[name + part][:, j * r:(j + 1) * r]
+    if poison:
+        rng = np.random.default_rng([spec.seed, spec.wid, _T_POISON, 0x9A6E])
+        for blk in np.nonzero(~used)[0]:
+            for name in ("k", "v"):
+                pool[name + "_codes"][blk] = rng.integers(0, 1 << spec.bits, size=(H, P, D), dtype=np.uint8)
+                pool[name + "_scale"][blk] = np.float16(np.nan)
+                pool[name + "_zero"][blk] = np.float16(np.nan)
+    return pool

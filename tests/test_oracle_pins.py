@@ -541,3 +541,53 @@ def test_moving_tokens_between_cache_and_window_changes_nothing():
     o3, l3 = oracle.decode_window_rows(dict(w, seq_lens=np.array([0], np.int32)), none, [(0, 0)], k_layout="token",
                                        v_layout="token", group=g, sm_scale=0.25)
     assert not o3.any() and l3[0] == -np.inf
+
+
+# ---------------------------------------------------------------------------
+# Paged cache: gather_paged puts a pool of blocks back in logical order.
+# ---------------------------------------------------------------------------
+
+def test_gather_paged_by_hand():
+    """Three pool blocks of two tokens, one channel, one KV head; sequence 0
+    uses blocks (2, 0), sequence 1 block 1 then an entry outside the pool (a
+    block of zeros); values written out by hand."""
+    codes = np.array([[[[10], [11]]], [[[20], [21]]], [[[30], [31]]]], np.uint8)  # [NB=3][H=1][P=2][D=1]
+    scale = codes.astype(np.float16) / 8          # token-wise, one group of one channel
+    pool = {"k_codes": codes, "v_codes": codes + 1, "k_scale": scale, "k_zero": -scale,
+            "v_scale": scale, "v_zero": scale}
+    table = np.array([[2, 0], [1, 7]], np.int32)
+    w = oracle.gather_paged(pool, table, 2, k_layout="token", v_layout="token", group=1)
+    assert w["k_codes"][:, 0, :, 0].tolist() == [[30, 31, 10, 11], [20, 21, 0, 0]]
+    assert w["v_codes"][:, 0, :, 0].tolist() == [[31, 32, 11, 12], [21, 22, 0, 0]]
+    assert w["k_zero"][0, 0, :, 0].tolist() == [-3.75, -3.875, -1.25, -1.375]
+    assert w["v_scale"][1, 0, :, 0].tolist() == [2.5, 2.625, 0.0, 0.0]
+
+
+def test_gather_paged_channel_wise_scale_rows():
+    """Channel-wise groups of g tokens: each block of P tokens carries P/g scale
+    rows, gathered with the block (P = 4, g = 2: two rows per block)."""
+    nb, P, g = 3, 4, 2
+    s = np.arange(nb * (P // g), dtype=np.float16).reshape(nb, 1, P // g, 1)
+    codes = np.zeros((nb, 1, P, 1), np.uint8)
+    pool = {"k_codes": codes, "v_codes": codes, "k_scale": s, "k_zero": s, "v_scale": s, "v_zero": s}
+    w = oracle.gather_paged(pool, np.array([[1, 2, 0]]), P, k_layout="channel", v_layout="channel", group=g)
+    assert w["k_scale"][0, 0, :, 0].tolist() == [2, 3, 4, 5, 0, 1]
+
+
+@pytest.mark.parametrize("k_layout,v_layout,g,P", [("token", "token", 32, 64), ("token", "channel", 64, 128),
+                                                   ("channel", "token", 32, 128), ("channel", "channel", 64, 64)])
+def test_paged_decode_equals_contiguous_decode(k_layout, v_layout, g, P):
+    """A seeded random block order (unused pool blocks poisoned with NaN scales)
+    gives exactly the contiguous cache's result, ragged lengths with partial
+    last blocks and an empty sequence included."""
+    spec = synth.Spec("paged_pin", 22, 2, k_layout, v_layout, g, 3, 4, 2, 128, 256, lens=(256, 77, 0))
+    table, nb = synth.make_block_table(5, spec.seq_lens(), 256 // P, P)
+    pool = synth.make_pool(spec, table, nb, P)
+    pool["q"] = synth.make_query(spec)
+    pool["seq_lens"] = spec.seq_lens()
+    rows = [(b, i) for b in range(3) for i in range(4)]
+    kw = dict(k_layout=k_layout, v_layout=v_layout, group=g, sm_scale=spec.sm_scale)
+    o_p, l_p = oracle.decode_paged_rows(pool, table, P, rows, **kw)
+    w = synth.make_workload(spec)
+    o_c, l_c = oracle.decode_rows(w, rows, **kw)
+    assert np.array_equal(o_p, o_c) and np.array_equal(l_p, l_c)
