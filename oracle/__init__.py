@@ -23,6 +23,16 @@ What it computes (fp64 throughout):
   explainer's accuracy paragraph names: "full-precision windows of recent
   tokens"); attention is over the union of the T_b dequantised cache tokens
   and the window's tokens, computed by ``attend`` on the concatenation.
+* ``hadamard`` / ``round_bf16`` / ``attend_rotated`` and the ``rotate``
+  argument of the decode functions: a rotated cache, the accuracy recipe the
+  explainer's accuracy paragraph names ("OSCAR's rotations") and its related
+  explainers list (KVarN, a Hadamard-rotated 2-bit KV cache).  The cache holds
+  the quantised rows of K R and/or V R for an orthonormal R (the normalised
+  Sylvester-Hadamard matrix of order D unless given); since R R^T = I the
+  scores are (q R).(k R) and the output is (sum_t p_t v_t R) R^T.  Readings
+  the pages leave open, taken here: the rotated query is held in bf16, the
+  precision of the query itself (round to nearest even); a full-precision
+  window holds the model's own, unrotated rows.
 * ``gather_paged`` / ``decode_paged_rows``: a paged cache (pools of blocks of
   P tokens reached through a block table, the KV layout of the serving
   systems the explainer's integration paragraph names) is first put back in
@@ -91,6 +101,69 @@ def attend(q_row, k_hat, v_hat, sm_scale: float):
     return o, m + math.log(l)
 
 
+def hadamard(n: int) -> np.ndarray:
+    """Orthonormal Sylvester-Hadamard matrix of order n (a power of two):
+    H_1 = [1], H_2m = [[H_m, H_m], [H_m, -H_m]], scaled by 1/sqrt(n), so that
+    entry (i, j) is (-1)^popcount(i & j) / sqrt(n); symmetric and its own
+    inverse."""
+    if n < 1 or n & (n - 1):
+        raise ValueError("order must be a power of two")
+    h = np.ones((1, 1))
+    while h.shape[0] < n:
+        h = np.block([[h, h], [h, -h]])
+    return h / math.sqrt(n)
+
+
+def round_bf16(x) -> np.ndarray:
+    """Nearest bf16 value (8 significant bits), ties to even, for values in
+    bf16's normal range (the query values this is applied to)."""
+    x = np.asarray(x, dtype=np.float64)
+    m, e = np.frexp(x)              # x = m 2^e with 1/2 <= |m| < 1
+    return np.ldexp(np.round(m * 256.0), e - 8)  # np.round: half to even
+
+
+def attend_rotated(q_row, k_hat, v_hat, sm_scale: float, *, rot_k: bool, rot_v: bool, rot=None,
+                   round_query: bool = True, win_k=None, win_v=None):
+    """Softmax attention of one query row over a rotated cache.
+
+    k_hat / v_hat [T, D] are the dequantised cache rows as stored: k R when
+    rot_k, v R when rot_v (R = ``rot``, default ``hadamard(D)``).  The query
+    that meets the stored keys is q R (rounded to bf16 when round_query); the
+    cache's weighted value sum is taken back to the model's basis by R^T.
+    win_k / win_v [W, D] (optional) are full-precision window rows in the
+    model's basis, met by q itself; one softmax runs over the T + W scores.
+    Returns (o [D], lse) like ``attend``.
+    """
+    q = np.asarray(q_row, dtype=np.float64)
+    D = q.shape[0]
+    R = hadamard(D) if rot is None else np.asarray(rot, dtype=np.float64)
+    qk = q @ R if rot_k else q
+    if rot_k and round_query:
+        qk = round_bf16(qk)
+    k_hat = np.asarray(k_hat, dtype=np.float64)
+    v_hat = np.asarray(v_hat, dtype=np.float64)
+    wk = np.zeros((0, D)) if win_k is None else np.asarray(win_k, dtype=np.float64)
+    wv = np.zeros((0, D)) if win_v is None else np.asarray(win_v, dtype=np.float64)
+    T = k_hat.shape[0]
+    scores = np.concatenate([sm_scale * (k_hat @ qk), sm_scale * (wk @ q)])
+    if scores.size == 0:
+        return np.zeros(D), -math.inf
+    m = scores.max()
+    w = np.exp(scores - m)
+    l = w.sum()
+    p = w / l
+    oc = p[:T] @ v_hat
+    if rot_v:
+        oc = oc @ R.T
+    return oc + p[T:] @ wv, m + math.log(l)
+
+
+def _rot_flags(rotate: str):
+    if rotate not in ("", "k", "v", "kv"):
+        raise ValueError(rotate)
+    return "k" in rotate, "v" in rotate
+
+
 def _head(w: dict, b: int, h: int, t: int, k_layout: str, v_layout: str, group: int):
     k_hat = dequantize(w["k_codes"][b, h, :t], _scale_rows(w["k_scale"][b, h], k_layout, group, t),
                        _scale_rows(w["k_zero"][b, h], k_layout, group, t), k_layout, group)
@@ -107,20 +180,24 @@ def _scale_rows(s, layout: str, group: int, t: int):
 
 
 def decode(w: dict, *, k_layout: str, v_layout: str, group: int, sm_scale: float,
-           num_kv_heads: int | None = None):
+           num_kv_heads: int | None = None, rotate: str = ""):
     """Whole decode step.  ``w`` holds q [B,Hq,D], k_codes / v_codes
     [B,Hkv,Tcap,D], k_scale / k_zero / v_scale / v_zero in the layouts of
     ``dequantize`` (with leading [B,Hkv]) and seq_lens [B] (clamped to
-    [0, Tcap]).  Returns (out [B,Hq,D] fp64, lse [B,Hq] fp64)."""
+    [0, Tcap]).  ``rotate`` ("", "k", "v" or "kv") names the sides whose
+    cache holds Hadamard-rotated rows (``attend_rotated``).  Returns
+    (out [B,Hq,D] fp64, lse [B,Hq] fp64)."""
     q = np.asarray(w["q"], dtype=np.float64)
     B, Hq, D = q.shape
     rows = [(b, i) for b in range(B) for i in range(Hq)]
-    o, l = decode_rows(w, rows, k_layout=k_layout, v_layout=v_layout, group=group, sm_scale=sm_scale)
+    o, l = decode_rows(w, rows, k_layout=k_layout, v_layout=v_layout, group=group, sm_scale=sm_scale,
+                       rotate=rotate)
     return o.reshape(B, Hq, D), l.reshape(B, Hq)
 
 
-def decode_rows(w: dict, rows, *, k_layout: str, v_layout: str, group: int, sm_scale: float):
+def decode_rows(w: dict, rows, *, k_layout: str, v_layout: str, group: int, sm_scale: float, rotate: str = ""):
     """Like ``decode`` for a list of (b, query head) pairs only."""
+    rot_k, rot_v = _rot_flags(rotate)
     q = np.asarray(w["q"], dtype=np.float64)
     B, Hq, D = q.shape
     Hkv = w["k_codes"].shape[1]
@@ -135,15 +212,22 @@ def decode_rows(w: dict, rows, *, k_layout: str, v_layout: str, group: int, sm_s
         if (b, h) not in cache:
             cache = {(b, h): _head(w, b, h, t, k_layout, v_layout, group)}
         k_hat, v_hat = cache[(b, h)]
-        out[n], lse[n] = attend(q[b, i], k_hat, v_hat, sm_scale)
+        if rot_k or rot_v:
+            out[n], lse[n] = attend_rotated(q[b, i], k_hat, v_hat, sm_scale, rot_k=rot_k, rot_v=rot_v)
+        else:
+            out[n], lse[n] = attend(q[b, i], k_hat, v_hat, sm_scale)
     return out, lse
 
 
-def decode_window_rows(w: dict, win: dict, rows, *, k_layout: str, v_layout: str, group: int, sm_scale: float):
+def decode_window_rows(w: dict, win: dict, rows, *, k_layout: str, v_layout: str, group: int, sm_scale: float,
+                       rotate: str = ""):
     """``decode_rows`` over the quantised cache of ``w`` plus a full-precision
     window: win["k"], win["v"] [B][Hkv][W][D] (bf16 values, any float dtype),
     win["lens"] [B] (clamped to [0, W]).  Returns (out [n, D], lse [n]) in
-    fp64; a row with no token at all gives out = 0, lse = -inf."""
+    fp64; a row with no token at all gives out = 0, lse = -inf.  With
+    ``rotate``, the cache sides it names hold rotated rows and the window the
+    model's own (``attend_rotated``)."""
+    rot_k, rot_v = _rot_flags(rotate)
     q = np.asarray(w["q"], dtype=np.float64)
     B, Hq, D = q.shape
     Hkv = w["k_codes"].shape[1]
@@ -157,6 +241,11 @@ def decode_window_rows(w: dict, win: dict, rows, *, k_layout: str, v_layout: str
         t = int(min(max(int(w["seq_lens"][b]), 0), Tcap))
         wl = int(min(max(int(win["lens"][b]), 0), W))
         k_hat, v_hat = _head(w, b, h, t, k_layout, v_layout, group)
+        if rot_k or rot_v:
+            out[n], lse[n] = attend_rotated(q[b, i], k_hat, v_hat, sm_scale, rot_k=rot_k, rot_v=rot_v,
+                                            win_k=np.asarray(win["k"], np.float64)[b, h, :wl],
+                                            win_v=np.asarray(win["v"], np.float64)[b, h, :wl])
+            continue
         k_all = np.concatenate([k_hat, np.asarray(win["k"], np.float64)[b, h, :wl]], axis=0)
         v_all = np.concatenate([v_hat, np.asarray(win["v"], np.float64)[b, h, :wl]], axis=0)
         out[n], lse[n] = attend(q[b, i], k_all, v_all, sm_scale)
@@ -193,7 +282,7 @@ def gather_paged(pool: dict, block_table, block_size: int, *, k_layout: str, v_l
 
 
 def decode_paged_rows(w_pool: dict, block_table, block_size: int, rows, *, k_layout: str, v_layout: str,
-                      group: int, sm_scale: float):
+                      group: int, sm_scale: float, rotate: str = ""):
     """``decode_rows`` over a paged cache: w_pool holds q, seq_lens and the pools
     (see ``gather_paged``); only the blocks below each sequence's length are
     looked up (table entries past it may hold anything)."""
@@ -205,7 +294,8 @@ def decode_paged_rows(w_pool: dict, block_table, block_size: int, rows, *, k_lay
     w = gather_paged(w_pool, table, block_size, k_layout=k_layout, v_layout=v_layout, group=group)
     w["q"] = w_pool["q"]
     w["seq_lens"] = w_pool["seq_lens"]
-    return decode_rows(w, rows, k_layout=k_layout, v_layout=v_layout, group=group, sm_scale=sm_scale)
+    return decode_rows(w, rows, k_layout=k_layout, v_layout=v_layout, group=group, sm_scale=sm_scale,
+                       rotate=rotate)
 
 
 # ---------------------------------------------------------------------------

@@ -591,3 +591,133 @@ def test_paged_decode_equals_contiguous_decode(k_layout, v_layout, g, P):
     w = synth.make_workload(spec)
     o_c, l_c = oracle.decode_rows(w, rows, **kw)
     assert np.array_equal(o_p, o_c) and np.array_equal(l_p, l_c)
+
+
+# ---------------------------------------------------------------- rotated cache
+# A cache of Hadamard-rotated rows (explainer, accuracy paragraph: "OSCAR's
+# rotations"; related explainers: KVarN, Hadamard-rotated 2-bit KV).
+
+
+@pytest.mark.parametrize("n", [1, 2, 4, 8, 16, 32, 64, 128])
+def test_hadamard_is_scipys_normalised(n):
+    """The Sylvester construction against scipy's own (a library routine)."""
+    from scipy.linalg import hadamard as scipy_hadamard
+    np.testing.assert_array_equal(oracle.hadamard(n), scipy_hadamard(n) / math.sqrt(n))
+
+
+def test_hadamard_orthonormal_and_symmetric():
+    H = oracle.hadamard(128)
+    np.testing.assert_allclose(H @ H.T, np.eye(128), atol=1e-14)
+    np.testing.assert_array_equal(H, H.T)
+    # entry (i, j) = (-1)^popcount(i & j) / sqrt(128), brute force on a few entries
+    for i, j in ((0, 0), (1, 1), (3, 5), (127, 127), (64, 63), (100, 37)):
+        assert H[i, j] == (-1) ** bin(i & j).count("1") / math.sqrt(128)
+
+
+def test_round_bf16_matches_torch():
+    """Nearest-even bf16 rounding against torch's float32 -> bfloat16 cast, on
+    fp32 values over many binades and on exact ties."""
+    import torch
+    rng = np.random.default_rng(71)
+    x = (rng.standard_normal(4096) * np.exp2(rng.integers(-20, 20, 4096))).astype(np.float32)
+    base = oracle.round_bf16(x.astype(np.float64))
+    ties = (base + np.sign(base) * np.ldexp(1.0, np.frexp(base)[1] - 9)).astype(np.float32)  # + half an ulp
+    assert (oracle.round_bf16(ties.astype(np.float64)) != ties).all()  # every one a tie
+    for v in (x, ties):
+        want = torch.from_numpy(v).to(torch.bfloat16).to(torch.float64).numpy()
+        np.testing.assert_array_equal(oracle.round_bf16(v.astype(np.float64)), want)
+
+
+def test_round_bf16_closed_forms():
+    assert oracle.round_bf16(1 / math.sqrt(128)) == 181 / 2048     # 1.41421356.. * 2^7 = 181.02
+    assert oracle.round_bf16(1 + 2 ** -8) == 1.0                    # tie: to even
+    assert oracle.round_bf16(1 + 3 * 2 ** -8) == 1 + 2 ** -6        # tie: to even
+    assert oracle.round_bf16(-(1 + 3 * 2 ** -8)) == -(1 + 2 ** -6)
+
+
+def _orthogonal(rng, n):
+    """A random orthogonal matrix that is not symmetric (QR of a Gaussian)."""
+    m, r = np.linalg.qr(rng.standard_normal((n, n)))
+    m = m * np.sign(np.diag(r))
+    assert np.abs(m - m.T).max() > 0.1
+    return m
+
+
+@pytest.mark.parametrize("rot_k,rot_v", [(True, True), (True, False), (False, True)])
+def test_rotation_leaves_attention_unchanged(rot_k, rot_v):
+    """R R^T = I: over a cache of K R / V R rows, the rotated query and the
+    un-rotated output give plain attention over K, V exactly (up to fp64
+    rounding).  R is a random non-symmetric orthogonal matrix, so a query
+    rotated by R^T, an output taken back by R, or a dropped step fails."""
+    rng = np.random.default_rng(72)
+    D, T = 16, 23
+    R = _orthogonal(rng, D)
+    q, K, V = rng.standard_normal(D), rng.standard_normal((T, D)), rng.standard_normal((T, D))
+    o_ref, l_ref = oracle.attend(q, K, V, 0.4)
+    o, l = oracle.attend_rotated(q, K @ R if rot_k else K, V @ R if rot_v else V, 0.4, rot_k=rot_k, rot_v=rot_v,
+                                 rot=R, round_query=False)
+    np.testing.assert_allclose(o, o_ref, atol=1e-12)
+    assert abs(l - l_ref) < 1e-12
+    # the same cache read as unrotated differs: the pin can fail
+    o_bad, _ = oracle.attend_rotated(q, K @ R if rot_k else K, V @ R if rot_v else V, 0.4, rot_k=False,
+                                     rot_v=False, rot=R, round_query=False)
+    assert np.abs(o_bad - o_ref).max() > 1e-3
+
+
+def test_rotated_cache_with_unrotated_window():
+    """Cache rows rotated, window rows in the model's basis: one softmax over
+    both equals plain attention over the union."""
+    rng = np.random.default_rng(73)
+    D, T, W = 16, 11, 5
+    R = _orthogonal(rng, D)
+    q = rng.standard_normal(D)
+    K, V = rng.standard_normal((T, D)), rng.standard_normal((T, D))
+    Kw, Vw = rng.standard_normal((W, D)), rng.standard_normal((W, D))
+    o_ref, l_ref = oracle.attend(q, np.concatenate([K, Kw]), np.concatenate([V, Vw]), 0.4)
+    o, l = oracle.attend_rotated(q, K @ R, V @ R, 0.4, rot_k=True, rot_v=True, rot=R, round_query=False,
+                                 win_k=Kw, win_v=Vw)
+    np.testing.assert_allclose(o, o_ref, atol=1e-12)
+    assert abs(l - l_ref) < 1e-12
+    o, l = oracle.attend_rotated(q, np.zeros((0, D)), np.zeros((0, D)), 0.4, rot_k=True, rot_v=True,
+                                 rot=R, win_k=Kw, win_v=Vw)  # window only: the query is not rotated
+    o_ref, l_ref = oracle.attend(q, Kw, Vw, 0.4)
+    np.testing.assert_allclose(o, o_ref, atol=1e-13)
+
+
+def test_rotated_query_is_rounded_to_bf16():
+    """q = c e_0: q H = c / sqrt(128) in every channel, held as bf16.  One
+    token: lse = sm * bf16(c / sqrt(128)) * sum(k) and out = its value (the
+    value side unrotated)."""
+    rng = np.random.default_rng(74)
+    D = 128
+    k, v = rng.standard_normal((1, D)), rng.standard_normal((1, D))
+    for c, qh in ((1.0, 181 / 2048), (2.0, 181 / 1024), (-0.5, -181 / 4096)):
+        q = np.zeros(D)
+        q[0] = c
+        o, l = oracle.attend_rotated(q, k, v, 0.3, rot_k=True, rot_v=False)
+        assert l == pytest.approx(0.3 * qh * k.sum(), rel=1e-14, abs=1e-14)
+        np.testing.assert_array_equal(o, v[0])
+
+
+@pytest.mark.parametrize("k_layout,v_layout", [("token", "token"), ("channel", "channel"), ("token", "channel")])
+def test_decode_rotate_argument(k_layout, v_layout):
+    """``rotate`` routes each side: "k" meets the stored keys with
+    bf16(q H), "v" takes the output back by H (= H^T), "kv" both; lse only
+    depends on the key side."""
+    rng = np.random.default_rng(75)
+    w = _rand_case(rng, k_layout=k_layout, v_layout=v_layout)
+    H = oracle.hadamard(16)
+    kw = dict(k_layout=k_layout, v_layout=v_layout, group=8, sm_scale=0.3)
+    o0, l0 = oracle.decode(w, **kw)
+    wq = dict(w, q=oracle.round_bf16(np.asarray(w["q"], np.float64) @ H))
+    oq, lq = oracle.decode(wq, **kw)
+    ok, lk = oracle.decode(w, rotate="k", **kw)
+    ov, lv = oracle.decode(w, rotate="v", **kw)
+    okv, lkv = oracle.decode(w, rotate="kv", **kw)
+    np.testing.assert_allclose(ok, oq, atol=1e-13)
+    np.testing.assert_allclose(lk, lq, atol=1e-13)
+    np.testing.assert_allclose(ov, o0 @ H, atol=1e-13)
+    np.testing.assert_allclose(lv, l0, atol=1e-13)
+    np.testing.assert_allclose(okv, oq @ H, atol=1e-13)
+    np.testing.assert_allclose(lkv, lq, atol=1e-13)
+    assert np.abs(ok - o0).max() > 1e-3 and np.abs(ov - o0).max() > 1e-3
