@@ -23,6 +23,8 @@ FOSCAR_K_TOKEN = 0
 FOSCAR_K_CHANNEL = 1
 FOSCAR_V_TOKEN = 0
 FOSCAR_V_CHANNEL = 2
+FOSCAR_K_ROTATED = 4
+FOSCAR_V_ROTATED = 8
 FOSCAR_SIDE_K = 0
 FOSCAR_SIDE_V = 1
 
@@ -45,8 +47,13 @@ def _check(rc, where):
         raise FoscarError(rc, where)
 
 
-def layout_bits(k_layout: str, v_layout: str) -> int:
-    return (FOSCAR_K_CHANNEL if k_layout == "channel" else 0) | (FOSCAR_V_CHANNEL if v_layout == "channel" else 0)
+def layout_bits(k_layout: str, v_layout: str, rotate: str = "") -> int:
+    """Layout word of the C interface; ``rotate`` ("", "k", "v", "kv") names the
+    cache sides that hold Hadamard-rotated rows."""
+    if rotate not in ("", "k", "v", "kv"):
+        raise ValueError(f"rotate must be '', 'k', 'v' or 'kv', not {rotate!r}")
+    return ((FOSCAR_K_CHANNEL if k_layout == "channel" else 0) | (FOSCAR_V_CHANNEL if v_layout == "channel" else 0)
+            | (FOSCAR_K_ROTATED if "k" in rotate else 0) | (FOSCAR_V_ROTATED if "v" in rotate else 0))
 
 
 def make_dims(batch, num_q_heads, num_kv_heads, head_dim, max_seq_len, sm_scale=0.0):
@@ -282,17 +289,19 @@ def foscar_decode_paged_int4(q, k_pool, v_pool, k_scale, k_zero, v_scale, v_zero
 
 
 def decode_paged(q, k_pool, v_pool, k_scale, k_zero, v_scale, v_zero, block_table, seq_lens, *, bits,
-                 k_layout="token", v_layout="token", group=128, sm_scale=0.0, out=None, lse=None, stream=None):
+                 k_layout="token", v_layout="token", group=128, sm_scale=0.0, out=None, lse=None, stream=None,
+                 rotate=""):
     """Decode step over a paged cache (pools and block table as foscar_decode_paged_int2)."""
     fn = foscar_decode_paged_int2 if bits == 2 else foscar_decode_paged_int4
     return fn(q, k_pool, v_pool, k_scale, k_zero, v_scale, v_zero, block_table, seq_lens,
-              layout_bits(k_layout, v_layout), group, out, lse, sm_scale, stream)
+              layout_bits(k_layout, v_layout, rotate), group, out, lse, sm_scale, stream)
 
 
 def decode(q, packed_k, packed_v, k_scale, k_zero, v_scale, v_zero, seq_lens, *, bits, k_layout="token",
-           v_layout="token", group=128, sm_scale=0.0, out=None, lse=None, stream=None, window=None):
-    """Decode step; ``window`` = (win_k, win_v, win_lens) adds a bf16 window of recent tokens."""
-    layout = layout_bits(k_layout, v_layout)
+           v_layout="token", group=128, sm_scale=0.0, out=None, lse=None, stream=None, window=None, rotate=""):
+    """Decode step; ``window`` = (win_k, win_v, win_lens) adds a bf16 window of recent tokens;
+    ``rotate`` names the cache sides holding Hadamard-rotated rows ("k", "v", "kv")."""
+    layout = layout_bits(k_layout, v_layout, rotate)
     if window is not None:
         return _decode_window(bits, q, packed_k, packed_v, k_scale, k_zero, v_scale, v_zero, seq_lens, layout, group,
                               *window, out, lse, sm_scale, stream)

@@ -19,7 +19,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libfoscar.so")
-SOURCES = ["api.hip", "decode.hip", "decode_paged.hip", "pack.hip", "quant.hip"]
+SOURCES = ["api.hip", "decode.hip", "decode_paged.hip", "decode_rot.hip", "decode_paged_rot.hip", "pack.hip",
+           "quant.hip"]
 ARCH = os.environ.get("FOSCAR_ARCH", "gfx950")
 
 FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",

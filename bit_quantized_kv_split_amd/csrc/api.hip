@@ -76,13 +76,13 @@ foscar_dims work_dims(const foscar_dims* d) {
 int check_decode_shape(const foscar_dims* d, int layout, int group) {
   int rc = check_dims(d, true);
   if (rc) return rc;
-  if (layout < 0 || layout > 3) return FOSCAR_EINVAL;
+  if (layout < 0 || layout > 15) return FOSCAR_EINVAL;  // K/V group sides and rotation bits
   if (!valid_group(group)) return FOSCAR_EUNSUPPORTED;
   // one grid row of work-groups per work pair; per-head byte offsets are 32-bit
   const int64_t pairs = (int64_t)d->batch * d->num_kv_heads * head_groups(d->num_q_heads / d->num_kv_heads);
   if (pairs > (1 << 22) || d->max_seq_len > (1 << 24)) return FOSCAR_EUNSUPPORTED;
   if (d->max_seq_len % foscar::kTile != 0) return FOSCAR_EUNSUPPORTED;
-  if (layout != 0 && d->max_seq_len % group != 0) return FOSCAR_EUNSUPPORTED;
+  if ((layout & 3) != 0 && d->max_seq_len % group != 0) return FOSCAR_EUNSUPPORTED;
   return FOSCAR_OK;
 }
 
@@ -100,17 +100,19 @@ int compute_units(int device) {
 }
 
 // Work-groups of the (bits, layout, group) kernel one CU of `device` holds at
-// once (cached; 4 when the runtime cannot say, e.g. without a GPU).
+// once (cached; 4 when the runtime cannot say, e.g. without a GPU).  `layout`
+// may carry the rotation bits, which select the rotated variant.
 int resident_per_cu(int device, int bits, int layout, int group, bool paged = false) {
-  const long long key = ((((long long)device * 8 + bits) * 4 + layout) * 256 + group) * 2 + (paged ? 1 : 0);
+  const long long key = ((((long long)device * 8 + bits) * 16 + layout) * 256 + group) * 2 + (paged ? 1 : 0);
   {
     std::lock_guard<std::mutex> lk(g_ws_mutex);
     auto it = g_occ.find(key);
     if (it != g_occ.end()) return it->second;
   }
   int n = 0;
-  if (foscar::decode_occupancy(bits, (layout & FOSCAR_K_CHANNEL) != 0, (layout & FOSCAR_V_CHANNEL) != 0, group, paged, &n) !=
-          hipSuccess || n <= 0)
+  if (foscar::decode_occupancy(bits, (layout & FOSCAR_K_CHANNEL) != 0, (layout & FOSCAR_V_CHANNEL) != 0, group, paged,
+                               (layout >> 2) != 0, &n) != hipSuccess ||
+      n <= 0)
     return 4;
   std::lock_guard<std::mutex> lk(g_ws_mutex);
   g_occ[key] = n;
@@ -230,6 +232,9 @@ int decode_common(int bits, const foscar_dims* d, const void* q, const void* pk,
   g_next_events = foscar::LaunchEvents{};
   int rc = check_decode_shape(d, layout, group);
   if (rc) return rc;
+  const int rot = (layout >> 2) & 3;  // FOSCAR_K_ROTATED, FOSCAR_V_ROTATED
+  const int variant = layout;         // the kernel variant (group sides and rotation)
+  layout &= 3;                        // the group sides
   if (windowed) {
     if (win_cap < 0) return FOSCAR_EINVAL;
     if (win_cap > foscar::kMaxWindow || d->batch > 65535) return FOSCAR_EUNSUPPORTED;
@@ -251,7 +256,7 @@ int decode_common(int bits, const foscar_dims* d, const void* q, const void* pk,
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return hip_fail(e);
   int32_t splits = 1, chunk = foscar::kTile;
-  const int cus = compute_units(dev), per_cu = resident_per_cu(dev, bits, layout, group, paged);
+  const int cus = compute_units(dev), per_cu = resident_per_cu(dev, bits, variant, group, paged);
   // paged: a range of at most 63 blocks' tokens touches at most 64 blocks (one per lane), aligned or not
   plan(d, layout, group, cus, per_cu, &splits, &chunk, 0, paged ? 63 * block_size : 0);
   // the window is attended inside the decode launch by win_wgs more work-groups per pair: 1, 2, 4
@@ -282,7 +287,8 @@ int decode_common(int bits, const foscar_dims* d, const void* q, const void* pk,
 
   const float sm = d->sm_scale > 0.f ? d->sm_scale : 1.0f / sqrtf((float)d->head_dim);
   foscar::SplitArgs sa;
-  sa.q = (const uint16_t*)q;
+  sa.win_q = (const uint16_t*)q;
+  sa.q = (rot & 1) ? (const uint16_t*)out : sa.win_q;  // rotated keys: q H is written to `out` first
   sa.pk = (const uint32_t*)pk;
   sa.pv = (const uint32_t*)pv;
   sa.ks = (const uint16_t*)ks;
@@ -314,18 +320,17 @@ int decode_common(int bits, const foscar_dims* d, const void* q, const void* pk,
   sa.num_blocks = num_blocks;
   sa.win_o = nullptr;
   sa.win_lse = nullptr;
-  sa.win_slots = 0;
   sa.win_wgs = 0;
   sa.win_chunk = 0;
   sa.win_k = sa.win_v = nullptr;
   sa.win_lens = nullptr;
   sa.win_cap = 0;
   sa.win_sm = sm;
+  sa.rot = rot;
   if (windowed) {  // beside the ranges (one round) or before the persistent round in the same grid
     const size_t rows = (size_t)d->batch * d->num_q_heads;
     sa.win_o = sa.lse_part + rows * splits;
     sa.win_lse = sa.win_o + rows * win_wgs * foscar::kHeadDim;
-    sa.win_slots = win_wgs;
     sa.win_wgs = win_wgs;
     sa.win_chunk = win_chunk;
     sa.win_k = (const uint16_t*)win_k;
@@ -334,8 +339,16 @@ int decode_common(int bits, const foscar_dims* d, const void* q, const void* pk,
     sa.win_cap = win_cap;
   }
 
+  foscar::LaunchEvents ev_main = ev;
+  if (rot & 1) {  // the query rotated once per step, into `out` (the decode reads it there before any
+                  // work-group of its work pair writes that row's output)
+    e = foscar::launch_rotate_query(d->batch * d->num_q_heads, sa.win_q, (uint16_t*)out, (hipStream_t)stream,
+                                    ev.start);
+    if (e != hipSuccess) return hip_fail(e);
+    ev_main.start = nullptr;
+  }
   e = foscar::launch_decode(bits, (layout & FOSCAR_K_CHANNEL) != 0, (layout & FOSCAR_V_CHANNEL) != 0, group,
-                            d->batch, d->num_kv_heads, sa, (hipStream_t)stream, ev);
+                            d->batch, d->num_kv_heads, sa, (hipStream_t)stream, ev_main);
   if (e != hipSuccess) return hip_fail(e);
   return FOSCAR_OK;
 }
@@ -484,7 +497,7 @@ int decode_paged(int bits, const foscar_dims* dims, const void* q, const void* k
   // blocks of whole tiles (and whole groups of a channel-wise side); the logical capacity
   // max_seq_len is a whole number of blocks, in at most kMaxSplits ranges of 63 blocks' tokens
   if (block_size % foscar::kTile != 0 || block_size > 65536) return FOSCAR_EUNSUPPORTED;
-  if (layout != 0 && block_size % group != 0) return FOSCAR_EUNSUPPORTED;
+  if ((layout & 3) != 0 && block_size % group != 0) return FOSCAR_EUNSUPPORTED;
   if (dims->max_seq_len % block_size != 0) return FOSCAR_EUNSUPPORTED;
   if ((int64_t)dims->max_seq_len > (int64_t)foscar::kMaxSplits * 63 * block_size) return FOSCAR_EUNSUPPORTED;
   return decode_common(bits, dims, q, k_pool, v_pool, k_scale, k_zero, v_scale, v_zero, seq_lens, layout, group, out,
@@ -569,7 +582,7 @@ int foscar_split_plan(const foscar_dims* dims, int bits, int layout, int group, 
     per_cu = resident_per_cu(dev, bits, layout, group);
   }
   const foscar_dims wd = work_dims(dims);
-  plan(&wd, layout, group, cus, per_cu, splits, chunk);
+  plan(&wd, layout & 3, group, cus, per_cu, splits, chunk);
   return FOSCAR_OK;
 }
 
@@ -581,11 +594,11 @@ int foscar_record_next_launch(void* start_event, void* stop_event) {
 
 int foscar_occupancy(int bits, int layout, int group, int32_t* wgs_per_cu) {
   if (!wgs_per_cu) return FOSCAR_EINVAL;
-  if (layout < 0 || layout > 3) return FOSCAR_EINVAL;
+  if (layout < 0 || layout > 15) return FOSCAR_EINVAL;
   if ((bits != 2 && bits != 4) || !valid_group(group)) return FOSCAR_EUNSUPPORTED;
   int n = 0;
   const hipError_t e = foscar::decode_occupancy(bits, (layout & FOSCAR_K_CHANNEL) != 0, (layout & FOSCAR_V_CHANNEL) != 0,
-                                                group, false, &n);
+                                                group, false, (layout >> 2) != 0, &n);
   if (e != hipSuccess) return hip_fail(e);
   *wgs_per_cu = n;
   return FOSCAR_OK;
@@ -601,7 +614,7 @@ int foscar_workspace_reserve(const foscar_dims* dims, int bits, int layout, int 
   if (e != hipSuccess) return hip_fail(e);
   int32_t splits = 1, chunk = 0;
   const foscar_dims wd = work_dims(dims);
-  plan(&wd, layout, group, compute_units(dev), resident_per_cu(dev, bits, layout, group), &splits, &chunk);
+  plan(&wd, layout & 3, group, compute_units(dev), resident_per_cu(dev, bits, layout, group), &splits, &chunk);
   return get_workspace(counter_bytes(&wd), partial_bytes(&wd, splits), (hipStream_t)stream, nullptr, nullptr);
 }
 

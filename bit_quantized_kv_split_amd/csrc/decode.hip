@@ -45,38 +45,47 @@
 namespace foscar {
 namespace {
 
-template <int BITS, bool KCH, bool VCH>
-hipError_t launch_g(int group, int batch, int hkv, const SplitArgs& sa, hipStream_t stream, int* per_cu,
-                    const LaunchEvents& ev) {
-  return launch_gp<BITS, KCH, VCH, false>(group, batch, hkv, sa, stream, per_cu, ev);
-}
-
-template <int BITS>
-hipError_t launch_bits(bool kch, bool vch, int group, int batch, int hkv, const SplitArgs& sa, hipStream_t stream,
-                       int* per_cu, const LaunchEvents& ev) {
-  if (kch) {
-    return vch ? launch_g<BITS, true, true>(group, batch, hkv, sa, stream, per_cu, ev)
-               : launch_g<BITS, true, false>(group, batch, hkv, sa, stream, per_cu, ev);
-  }
-  return vch ? launch_g<BITS, false, true>(group, batch, hkv, sa, stream, per_cu, ev)
-             : launch_g<BITS, false, false>(group, batch, hkv, sa, stream, per_cu, ev);
+// One wave per query row: lane l rotates channels 2l, 2l + 1 (row r of dst = bf16(q_r H)).
+__global__ __launch_bounds__(kWaves * 64) void rotate_query(const uint16_t* q, uint16_t* dst, int rows) {
+  const int lane = threadIdx.x & 63;
+  const int row = blockIdx.x * kWaves + (threadIdx.x >> 6);
+  if (row >= rows) return;  // whole waves
+  const uint32_t w = reinterpret_cast<const uint32_t*>(q + (size_t)row * kHeadDim)[lane];
+  reinterpret_cast<uint32_t*>(dst + (size_t)row * kHeadDim)[lane] = hadamard_bf16_pair(w, lane);
 }
 
 }  // namespace
 
-hipError_t launch_decode(int bits, bool k_channel, bool v_channel, int group, int batch, int hkv,
-                         const SplitArgs& sa, hipStream_t stream, const LaunchEvents& ev) {
-  if (sa.block_table) return launch_decode_paged(bits, k_channel, v_channel, group, batch, hkv, sa, stream, ev);
-  if (bits == 2) return launch_bits<2>(k_channel, v_channel, group, batch, hkv, sa, stream, nullptr, ev);
-  return launch_bits<4>(k_channel, v_channel, group, batch, hkv, sa, stream, nullptr, ev);
+hipError_t launch_rotate_query(int rows, const uint16_t* q, uint16_t* dst, hipStream_t stream, hipEvent_t start) {
+  if (rows <= 0) return hipSuccess;
+  const dim3 grid((rows + kWaves - 1) / kWaves);
+  if (start)
+    hipExtLaunchKernelGGL(rotate_query, grid, dim3(kWaves * 64), 0, stream, start, nullptr, 0, q, dst, rows);
+  else
+    hipLaunchKernelGGL(rotate_query, grid, dim3(kWaves * 64), 0, stream, q, dst, rows);
+  return hipGetLastError();
 }
 
-hipError_t decode_occupancy(int bits, bool k_channel, bool v_channel, int group, bool paged, int* per_cu) {
-  if (paged) return decode_occupancy_paged(bits, k_channel, v_channel, group, per_cu);
+// the contiguous cache without rotation: instantiated here
+hipError_t launch_split_plain(int bits, bool kch, bool vch, int group, int batch, int hkv, const SplitArgs& sa,
+                              hipStream_t stream, int* per_cu, const LaunchEvents& ev) {
+  return launch_variant<false, false>(bits, kch, vch, group, batch, hkv, sa, stream, per_cu, ev);
+}
+
+hipError_t launch_decode(int bits, bool k_channel, bool v_channel, int group, int batch, int hkv,
+                         const SplitArgs& sa, hipStream_t stream, const LaunchEvents& ev) {
+  const bool paged = sa.block_table != nullptr, rot = sa.rot != 0;
+  auto* fn = paged ? (rot ? launch_split_paged_rot : launch_split_paged)
+                   : (rot ? launch_split_rot : launch_split_plain);
+  return fn(bits, k_channel, v_channel, group, batch, hkv, sa, stream, nullptr, ev);
+}
+
+hipError_t decode_occupancy(int bits, bool k_channel, bool v_channel, int group, bool paged, bool rot, int* per_cu) {
   SplitArgs sa{};
   const LaunchEvents none{};
-  if (bits == 2) return launch_bits<2>(k_channel, v_channel, group, 0, 0, sa, nullptr, per_cu, none);
-  return launch_bits<4>(k_channel, v_channel, group, 0, 0, sa, nullptr, per_cu, none);
+  auto* fn = paged ? (rot ? launch_split_paged_rot : launch_split_paged)
+                   : (rot ? launch_split_rot : launch_split_plain);
+  return fn(bits, k_channel, v_channel, group, 0, 0, sa, nullptr, per_cu, none);
 }
 
 }  // namespace foscar

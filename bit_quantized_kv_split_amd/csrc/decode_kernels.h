@@ -450,6 +450,46 @@ __device__ __forceinline__ void load_u2(uint2 (&dst)[N], const uint16_t* p) {
   for (int i = 0; i < N; ++i) dst[i] = q[i];
 }
 
+// Rotated cache: y = x H for one 128-value row held two values per lane
+// (channel 2 lane + e in x_e), H the orthonormal Sylvester-Hadamard matrix
+// (entry (i, j) = (-1)^popcount(i & j) / sqrt(128); symmetric, its own
+// inverse).  Seven butterfly stages, one per bit of the channel index: bit 0
+// inside the lane, bits 1-6 against the lane whose index differs in bit k - 1
+// (ds_bpermute); the lower channel of each pair keeps the sum, the upper one
+// the difference.  All 64 lanes must run it.
+template <typename T>
+__device__ __forceinline__ void hadamard_row(T& x0, T& x1, int lane) {
+  T s = x0 + x1, d = x0 - x1;
+#pragma unroll
+  for (int k = 0; k < 6; ++k) {
+    const T ps = __shfl_xor(s, 1 << k), pd = __shfl_xor(d, 1 << k);
+    const bool upper = (lane >> k) & 1;
+    s = upper ? ps - s : s + ps;
+    d = upper ? pd - d : d + pd;
+  }
+  const T inv_sqrt128 = (T)0.088388347648318440550;
+  x0 = s * inv_sqrt128;
+  x1 = d * inv_sqrt128;
+}
+// bf16 nearest to x, ties to even, for x in fp32's normal range: the fp64
+// pattern rounded to 7 stored mantissa bits converts to fp32 exactly
+__device__ __forceinline__ uint32_t bf16_rne_f64(double x) {
+  uint64_t u = (uint64_t)__double_as_longlong(x);
+  u += ((uint64_t)1 << 44) - 1 + ((u >> 45) & 1);
+  u &= ~(((uint64_t)1 << 45) - 1);
+  return __float_as_uint((float)__longlong_as_double((long long)u)) >> 16;
+}
+// The rotated query: q H of a bf16 pair row (channels 2 lane, 2 lane + 1),
+// rounded once to bf16.  The butterflies run in fp64, where the sums of bf16
+// values are exact (for rows spanning under 2^38 in magnitude), so the result
+// is the bf16 rounding of the exact product up to the fp64 scaling by
+// 1/sqrt(128).
+__device__ __forceinline__ uint32_t hadamard_bf16_pair(uint32_t w, int lane) {
+  double x0 = (double)__uint_as_float(w << 16), x1 = (double)__uint_as_float(w & 0xFFFF0000u);
+  hadamard_row(x0, x1, lane);
+  return bf16_rne_f64(x0) | (bf16_rne_f64(x1) << 16);
+}
+
 // ---------------------------------------------------------------------------
 // Split kernel.
 // BITS: 2 or 4; KCH / VCH: channel-wise key / value groups; GRP: g.
@@ -515,6 +555,7 @@ __device__ __forceinline__ float wave_max(float v) {
   asm volatile("s_nop 2\n\tv_permlane32_swap_b32 %0, %1" : "+v"(a), "+v"(b));
   return fmaxf(a, b);
 }
+template <bool ROT>
 __device__ __forceinline__ void merge_ranges(const SplitArgs& a, int b, int h, int ns) {
   constexpr int D = kHeadDim, BLK = 32;
   static_assert(kWaves == kMaxG && D == 128, "one wave per query row, two channels per lane");
@@ -556,10 +597,12 @@ __device__ __forceinline__ void merge_ranges(const SplitArgs& a, int b, int h, i
     }
     m = bm;
   }
+  // rotated values: the cache's weighted sum back in the model's basis (the window's rows are in it)
+  if (ROT && (a.rot & 2)) hadamard_row(n0, n1, lane);
   // the full-precision window's partials are further terms of the same merge (1, 2, 4 or 8 slots)
   float m1 = m, d1 = d;
   const int c = 2 * lane;
-  switch (a.win_slots) {
+  switch (a.win_wgs) {
     case 1: fold_window_slots<1>(a, row, c, row, c + 1, m, n0, d, m1, n1, d1); break;
     case 2: fold_window_slots<2>(a, row, c, row, c + 1, m, n0, d, m1, n1, d1); break;
     case 4: fold_window_slots<4>(a, row, c, row, c + 1, m, n0, d, m1, n1, d1); break;
@@ -707,7 +750,7 @@ __device__ __forceinline__ void map_select(const SplitArgs& a, const NextLoad& n
 // writes the final output (the only range) or stores the partial
 // device-coherently and counts its arrival; the last range of the (sequence,
 // KV head) merges them all.  Every return is uniform.
-template <int UNIT>
+template <int UNIT, bool ROT>
 __device__ __forceinline__ void finish_range(const SplitArgs& a, const int b, const int h, const int split,
                                              const int T, float (*s_ml)[2][4], float (*s_o)[4][kHeadDim], int* next,
                                              NextLoad& nx) {
@@ -717,6 +760,31 @@ __device__ __forceinline__ void finish_range(const SplitArgs& a, const int b, co
   const size_t bh = (size_t)b * a.hkv + h;
   const int ns = (T + a.chunk - 1) / a.chunk;  // ranges holding tokens of this sequence
   const bool direct = ns == 1 && !a.win_wgs;  // the only range partial: write the final output
+  if (ROT && direct && (a.rot & 2)) {  // rotated values: wave i takes query row i whole, to rotate it back
+    const int i = wave, lane = tid & 63;
+    if (i < a.g_heads) {
+      float M = -INFINITY;
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) M = fmaxf(M, s_ml[w][0][i]);
+      float n0 = 0.f, n1 = 0.f, den = 0.f;
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) {
+        const float l = s_ml[w][1][i];
+        const float f = (l > 0.f) ? __builtin_amdgcn_exp2f(s_ml[w][0][i] - M) : 0.f;
+        n0 = fmaf(f, s_o[w][i][2 * lane], n0);
+        n1 = fmaf(f, s_o[w][i][2 * lane + 1], n1);
+        den = fmaf(f, l, den);
+      }
+      hadamard_row(n0, n1, lane);
+      const size_t row = (size_t)b * a.hq + h * a.g_heads + i;
+      const float o0 = n0 / den, o1 = n1 / den, l_nat = (M + __log2f(den)) * kLn2;
+      const uint32_t packed = (uint32_t)to_bf16_rne(o0) | ((uint32_t)to_bf16_rne(o1) << 16);
+      reinterpret_cast<uint32_t*>(a.out + row * D)[lane] = packed;
+      if (lane == 0 && a.lse) a.lse[row] = l_nat;
+    }
+    if (next && wave == 0) map_select<UNIT>(a, nx, next);
+    return;
+  }
   for (int idx = (int)tid; idx < 4 * D; idx += blockDim.x) {
     const int i = idx / D, c = idx % D;
     if (i >= a.g_heads) continue;
@@ -771,7 +839,7 @@ __device__ __forceinline__ void finish_range(const SplitArgs& a, const int b, co
   if (tid == 0) s_last = (done == ns - 1 + a.win_wgs);  // fused window work-groups arrive like ranges
   __syncthreads();
   if (!s_last) return;
-  merge_ranges(a, b, h, ns);
+  merge_ranges<ROT>(a, b, h, ns);
   if (tid == 0) a.counters[bh] = 0;  // ready for the next call on this workspace
 }
 
@@ -783,7 +851,7 @@ constexpr int waves_per_simd() {
 // One work item: range `split` of KV head h of sequence b (T = 0 and split = 0:
 // the empty sequence's rows).  Every return is uniform over the work-group.
 // PAGED: the cache is a pool of blocks reached through the block table.
-template <int BITS, bool KCH, bool VCH, int GRP, bool PAGED>
+template <int BITS, bool KCH, bool VCH, int GRP, bool PAGED, bool ROT>
 __device__ __forceinline__ void run_item(const SplitArgs& a, const int b, const int h, const int split, const int T,
                                          int* next) {
   using C = Codec<BITS>;
@@ -953,10 +1021,10 @@ __device__ __forceinline__ void run_item(const SplitArgs& a, const int b, const 
   // ---- running state
   float m_ref = -INFINITY;                 // reference max of this lane's query (log2 units)
   float l_part = 0.f;                      // sum of p over this lane's quad tokens
-  float vz_part[NGV], vb_part[NGV];        // token-wise V: sum p*z, sum P~ * C (per value group)
+  float vz_part[NGV], vb_part[NGV];        // token-wise V: sum p*(z + kMid s), sum P~ * (C + kMid) per value group
 #pragma unroll
   for (int j = 0; j < NGV; ++j) vz_part[j] = vb_part[j] = 0.f;
-  float ps_part = 0.f, pb_part = 0.f;      // channel-wise V: sum P16, sum P16 * C over the current group
+  float ps_part = 0.f, pb_part = 0.f;      // channel-wise V: sum of P (fp32 if CENTER, else fp16), sum P16 * (C + kMid)
   f4 o_acc[2][2];                          // PV accumulators [channel 2l+h][quad parity]: rows = query heads
   f4 o_tot[2];                             // channel-wise V: folded output
 #pragma unroll
@@ -970,7 +1038,14 @@ __device__ __forceinline__ void run_item(const SplitArgs& a, const int b, const 
 
   // value-operand bias of this lane's quad (pairs 2*(qd % KPW), +1)
   const float cv0 = C::bias(2 * (pq % KPW)), cv1 = C::bias(2 * (pq % KPW) + 1);
-  const uint32_t cv0h = splat_f16(cv0), cv1h = splat_f16(cv1), oneh = splat_f16(1.f);
+  // rotated variant: value codes enter P V centred.  Each unit of P removes C + kMid (kMid = half
+  // the code range, C + kMid exact in fp16) from the operand C + q, leaving q - kMid, and kMid * s *
+  // (sum of the fp32 weights) joins the offset term.  The fp16 rounding errors of P then meet codes
+  // of both signs instead of piling up in the same direction on every channel of a row, where the
+  // rotation back by H would gather them into one channel.
+  constexpr bool CENTER = ROT;
+  constexpr float kMid = CENTER ? 0.5f * (float)((1 << BITS) - 1) : 0.f;
+  const uint32_t cv0h = splat_f16(cv0 + kMid), cv1h = splat_f16(cv1 + kMid), oneh = splat_f16(1.f);
 
   const size_t bkv = bh / a.kv_group;  // the KV head this pair's query heads attend
   const uint32_t* kbase = a.pk + bkv * (size_t)a.tcap * KW;
@@ -1063,7 +1138,8 @@ __device__ __forceinline__ void run_item(const SplitArgs& a, const int b, const 
     for (int i = 0; i < 4; ++i) {
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh)
-        o_tot[hh][i] += sv[hh] * (o_acc[hh][0][i] + o_acc[hh][1][i]) + (zv[hh] * psq[i] - sv[hh] * pbq[i]);
+        o_tot[hh][i] += sv[hh] * (o_acc[hh][0][i] + o_acc[hh][1][i]) +
+                        ((CENTER ? fmaf(kMid, sv[hh], zv[hh]) : zv[hh]) * psq[i] - sv[hh] * pbq[i]);
     }
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh) o_acc[hh][0] = o_acc[hh][1] = f4{0.f, 0.f, 0.f, 0.f};
@@ -1441,6 +1517,7 @@ __device__ __forceinline__ void run_item(const SplitArgs& a, const int b, const 
           s[r] = (idx % 2 == 0) ? half_lo(s32) : half_hi(s32);
           z[r] = (idx % 2 == 0) ? half_lo(z32) : half_hi(z32);
           if (tail && (t0 + 4 * pq + r >= T)) s[r] = z[r] = 0.f;  // padding may hold NaN
+          if constexpr (CENTER) z[r] = fmaf(kMid, s[r], z[r]);  // offset of the centred codes
         }
         uint32_t p01, p23;
         if constexpr (tail) {
@@ -1458,7 +1535,10 @@ __device__ __forceinline__ void run_item(const SplitArgs& a, const int b, const 
       const uint32_t p01 = pack_f16(p[0], p[1]);
       const uint32_t p23 = pack_f16(p[2], p[3]);
       s_p[wave][0][KCH ? qn : rh][pq] = make_uint2(p01, p23);
-      ps_part = dot2(p23, oneh, dot2(p01, oneh, ps_part));
+      if constexpr (CENTER)
+        ps_part += (p[0] + p[1]) + (p[2] + p[3]);  // fp32 weights
+      else
+        ps_part = dot2(p23, oneh, dot2(p01, oneh, ps_part));
       pb_part = dot2(p23, cv1h, dot2(p01, cv0h, pb_part));
     }
     __builtin_amdgcn_wave_barrier();
@@ -1616,7 +1696,7 @@ __device__ __forceinline__ void run_item(const SplitArgs& a, const int b, const 
   }
   __syncthreads();
 
-  finish_range<UNIT>(a, b, h, split, T, s_ml, s_o, next, nx);
+  finish_range<UNIT, ROT>(a, b, h, split, T, s_ml, s_o, next, nx);
 }
 
 // A full-precision window of recent tokens attended by S more work-groups of
@@ -1644,6 +1724,7 @@ __device__ __forceinline__ float wg_reduce(float v, float* red, bool is_max) {
   return r;
 }
 
+template <bool ROT>
 __device__ __forceinline__ void window_item(const SplitArgs& a, const int b, const int h, const int T, const int j) {
   constexpr int D = kHeadDim;
   extern __shared__ __align__(16) unsigned char smem[];
@@ -1672,7 +1753,7 @@ __device__ __forceinline__ void window_item(const SplitArgs& a, const int b, con
   const int mr = lane & 15, mg = lane >> 4;
   bf16x8 qb[D / 32];
   {
-    const uint32_t* qr = reinterpret_cast<const uint32_t*>(a.q + (row0 + (size_t)min(mr, G - 1)) * D);
+    const uint32_t* qr = reinterpret_cast<const uint32_t*>((ROT ? a.win_q : a.q) + (row0 + (size_t)min(mr, G - 1)) * D);
 #pragma unroll
     for (int k = 0; k < D / 32; ++k) {
       uint4 w;  // 4-byte loads: the query is only 4-byte aligned
@@ -1769,7 +1850,7 @@ __device__ __forceinline__ void window_item(const SplitArgs& a, const int b, con
   }
   __syncthreads();
   if (!s_wlast) return;
-  merge_ranges(a, b, h, ns);
+  merge_ranges<ROT>(a, b, h, ns);
   if (tid == 0) a.counters[bh] = 0;
 }
 
@@ -1781,7 +1862,7 @@ __device__ __forceinline__ void window_item(const SplitArgs& a, const int b, con
 // resets the counters for the next call.  A window's work-groups come before
 // that round in the grid, one item each; no work-group ever waits for another
 // (every hand-off is an arrival count), so their order cannot stall the grid.
-template <int BITS, bool KCH, bool VCH, int GRP, bool PAGED>
+template <int BITS, bool KCH, bool VCH, int GRP, bool PAGED, bool ROT>
 __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(waves_per_simd<BITS, KCH, VCH, GRP>())))
 void split_decode(const SplitArgs a) {
   if (!a.persistent) {
@@ -1794,10 +1875,10 @@ void split_decode(const SplitArgs a) {
     const int b = pair / a.hkv;
     const int T = min(max(a.seq_lens[b], 0), a.tcap);
     if (win) {  // dispatched first: run beside the ranges, not after them
-      window_item(a, b, pair % a.hkv, T, blockIdx.y);
+      window_item<ROT>(a, b, pair % a.hkv, T, blockIdx.y);
       return;
     }
-    run_item<BITS, KCH, VCH, GRP, PAGED>(a, b, pair % a.hkv, (int)blockIdx.y - a.win_wgs, T, nullptr);
+    run_item<BITS, KCH, VCH, GRP, PAGED, ROT>(a, b, pair % a.hkv, (int)blockIdx.y - a.win_wgs, T, nullptr);
     return;
   }
   // window work-groups take the first blocks (dispatched first) and leave
@@ -1807,7 +1888,7 @@ void split_decode(const SplitArgs a) {
   if ((int)blockIdx.x < nwin) {
     const int pair = (int)blockIdx.x % pairs;  // consecutive blocks: different pairs
     const int b = pair / a.hkv;
-    window_item(a, b, pair % a.hkv, min(max(a.seq_lens[b], 0), a.tcap), (int)blockIdx.x / pairs);
+    window_item<ROT>(a, b, pair % a.hkv, min(max(a.seq_lens[b], 0), a.tcap), (int)blockIdx.x / pairs);
     return;
   }
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -1826,7 +1907,7 @@ void split_decode(const SplitArgs a) {
     const int T = __builtin_amdgcn_readfirstlane(s_item[4]);
     __syncthreads();  // s_item is read before wave 0 maps the item after this one into it
     if (kind == kItemNone) break;
-    run_item<BITS, KCH, VCH, GRP, PAGED>(a, b, h, split, T, s_item);
+    run_item<BITS, KCH, VCH, GRP, PAGED, ROT>(a, b, h, split, T, s_item);
     __syncthreads();  // the item's LDS is free and s_item holds the next item
   }
   if (threadIdx.x == 0) {
@@ -1840,7 +1921,7 @@ void split_decode(const SplitArgs a) {
 
 // Launch the instantiation on `stream`, or (per_cu != nullptr) report how many
 // of its work-groups one CU holds at once instead.
-template <int BITS, bool KCH, bool VCH, int GRP, bool PAGED>
+template <int BITS, bool KCH, bool VCH, int GRP, bool PAGED, bool ROT>
 hipError_t launch_one(int batch, int hkv, const SplitArgs& sa, hipStream_t stream, int* per_cu, const LaunchEvents& ev) {
   using ST = Stage<BITS, KCH, VCH, GRP>;
   constexpr size_t lds = (size_t)kWaves * ST::NS * ST::BYTES;
@@ -1851,7 +1932,7 @@ hipError_t launch_one(int batch, int hkv, const SplitArgs& sa, hipStream_t strea
   if (lds_ok < 0) {
     hipFuncAttributes fa;
     int dev = 0, cu_lds = 0;
-    if (hipFuncGetAttributes(&fa, reinterpret_cast<const void*>(split_decode<BITS, KCH, VCH, GRP, PAGED>)) != hipSuccess ||
+    if (hipFuncGetAttributes(&fa, reinterpret_cast<const void*>(split_decode<BITS, KCH, VCH, GRP, PAGED, ROT>)) != hipSuccess ||
         hipGetDevice(&dev) != hipSuccess ||
         hipDeviceGetAttribute(&cu_lds, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor, dev) != hipSuccess)
       return hipErrorInvalidDeviceFunction;
@@ -1859,27 +1940,44 @@ hipError_t launch_one(int batch, int hkv, const SplitArgs& sa, hipStream_t strea
   }
   if (!lds_ok) return hipErrorInvalidConfiguration;
   if (per_cu)
-    return hipOccupancyMaxActiveBlocksPerMultiprocessor(per_cu, split_decode<BITS, KCH, VCH, GRP, PAGED>, kWaves * 64, lds);
+    return hipOccupancyMaxActiveBlocksPerMultiprocessor(per_cu, split_decode<BITS, KCH, VCH, GRP, PAGED, ROT>, kWaves * 64, lds);
   static_assert(lds >= sizeof(float) * (kMaxG * kHeadDim * (1 + kWaves) + kMaxG * kFusedWindowMax),
                 "rings must hold a fused window's query rows, scores and partial sums");
   const dim3 grid = sa.persistent ? dim3(sa.grid_wgs + batch * hkv * sa.win_wgs) : dim3(batch * hkv, sa.splits + sa.win_wgs);
   if (ev.start || ev.stop)  // timing events recorded by the dispatch itself
-    hipExtLaunchKernelGGL((split_decode<BITS, KCH, VCH, GRP, PAGED>), grid, dim3(kWaves * 64), lds, stream, ev.start, ev.stop,
+    hipExtLaunchKernelGGL((split_decode<BITS, KCH, VCH, GRP, PAGED, ROT>), grid, dim3(kWaves * 64), lds, stream, ev.start, ev.stop,
                           0, sa);
   else
-    hipLaunchKernelGGL((split_decode<BITS, KCH, VCH, GRP, PAGED>), grid, dim3(kWaves * 64), lds, stream, sa);
+    hipLaunchKernelGGL((split_decode<BITS, KCH, VCH, GRP, PAGED, ROT>), grid, dim3(kWaves * 64), lds, stream, sa);
   return hipGetLastError();
 }
 
-template <int BITS, bool KCH, bool VCH, bool PAGED>
+template <int BITS, bool KCH, bool VCH, bool PAGED, bool ROT>
 hipError_t launch_gp(int group, int batch, int hkv, const SplitArgs& sa, hipStream_t stream, int* per_cu,
                      const LaunchEvents& ev) {
   switch (group) {
-    case 32: return launch_one<BITS, KCH, VCH, 32, PAGED>(batch, hkv, sa, stream, per_cu, ev);
-    case 64: return launch_one<BITS, KCH, VCH, 64, PAGED>(batch, hkv, sa, stream, per_cu, ev);
-    case 128: return launch_one<BITS, KCH, VCH, 128, PAGED>(batch, hkv, sa, stream, per_cu, ev);
+    case 32: return launch_one<BITS, KCH, VCH, 32, PAGED, ROT>(batch, hkv, sa, stream, per_cu, ev);
+    case 64: return launch_one<BITS, KCH, VCH, 64, PAGED, ROT>(batch, hkv, sa, stream, per_cu, ev);
+    case 128: return launch_one<BITS, KCH, VCH, 128, PAGED, ROT>(batch, hkv, sa, stream, per_cu, ev);
   }
   return hipErrorInvalidValue;
+}
+
+// Every (bits, layout, group) instance of one (paged, rotated) variant: launch, or with per_cu
+// set, report its occupancy instead.  Each variant is instantiated in a source file of its own.
+template <bool PAGED, bool ROT>
+hipError_t launch_variant(int bits, bool kch, bool vch, int group, int batch, int hkv, const SplitArgs& sa,
+                          hipStream_t stream, int* per_cu, const LaunchEvents& ev) {
+  if (bits == 2) {
+    if (kch) return vch ? launch_gp<2, true, true, PAGED, ROT>(group, batch, hkv, sa, stream, per_cu, ev)
+                        : launch_gp<2, true, false, PAGED, ROT>(group, batch, hkv, sa, stream, per_cu, ev);
+    return vch ? launch_gp<2, false, true, PAGED, ROT>(group, batch, hkv, sa, stream, per_cu, ev)
+               : launch_gp<2, false, false, PAGED, ROT>(group, batch, hkv, sa, stream, per_cu, ev);
+  }
+  if (kch) return vch ? launch_gp<4, true, true, PAGED, ROT>(group, batch, hkv, sa, stream, per_cu, ev)
+                      : launch_gp<4, true, false, PAGED, ROT>(group, batch, hkv, sa, stream, per_cu, ev);
+  return vch ? launch_gp<4, false, true, PAGED, ROT>(group, batch, hkv, sa, stream, per_cu, ev)
+             : launch_gp<4, false, false, PAGED, ROT>(group, batch, hkv, sa, stream, per_cu, ev);
 }
 }  // namespace
 }  // namespace foscar

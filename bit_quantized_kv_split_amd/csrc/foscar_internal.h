@@ -17,7 +17,7 @@ constexpr int kMaxSplits = 512;  // ranges per sequence (bounds the workspace an
 // Arguments of the decode kernel (one work-group per (range, KV head, sequence)).
 // The last work-group to finish the ranges of a (sequence, KV head) merges them.
 struct SplitArgs {
-  const uint16_t* q;         // bf16 [B][Hq][D]
+  const uint16_t* q;         // bf16 [B][Hq][D] the query the cache ranges meet (rotated keys: q H, in `out`)
   const uint32_t* pk;        // [B][Hkv][Tcap][D*bits/32]
   const uint32_t* pv;        // [B][Hkv][Tcap*bits/32][D]
   const uint16_t* ks;        // fp16 key scales   (token-wise [B][Hkv][Tcap][D/g], channel-wise [B][Hkv][Tcap/g][D])
@@ -40,6 +40,10 @@ struct SplitArgs {
   int32_t persistent;        // 1: grid_wgs work-groups take work items from work_ctr (see split_decode)
   int32_t grid_wgs;          // persistent grid size (one round of resident work-groups)
   int32_t batch;             // B
+  // rotated cache, bit 1: the cache values are rows of V H; the cache's weighted value sum is taken
+  // back by H before the window's terms join it (H: orthonormal Sylvester-Hadamard of order 128).
+  // (Rotated keys change only q.)
+  int32_t rot;
   int32_t* work_ctr;         // [2] items taken, work-groups left; zero between calls
   // paged cache (block_table != null): pk .. vz are pools of num_blocks blocks of block_size
   // tokens, [num_blocks][Hkv][block_size][..] in the layouts above with Tcap = block_size, and
@@ -47,12 +51,12 @@ struct SplitArgs {
   const int32_t* block_table;  // [B][Tcap / block_size]
   int32_t block_size;          // multiple of 64 (and of g for a channel-wise side)
   int32_t num_blocks;
-  float* win_o;              // fp32 [B][Hq][win_slots][D] normalised outputs over a full-precision window, or null
-  float* win_lse;            // fp32 [B][Hq][win_slots] their natural-log lse (-inf: no window token)
-  int32_t win_slots;         // window partials per row (0: no window)
-  // window attended inside this launch: win_wgs more work-groups per pair (grid rows 0 .. win_wgs-1
-  // with the ranges in the rows after them, or the first B * Hkv * win_wgs blocks of a persistent
-  // grid), work-group j taking window tokens [j * win_chunk, +win_chunk)
+  float* win_o;              // fp32 [B][Hq][win_wgs][D] normalised outputs over a full-precision window, or null
+  float* win_lse;            // fp32 [B][Hq][win_wgs] their natural-log lse (-inf: no window token)
+  // window attended inside this launch (win_wgs = 0: no window): win_wgs more work-groups per pair
+  // (grid rows 0 .. win_wgs-1 with the ranges in the rows after them, or the first B * Hkv * win_wgs
+  // blocks of a persistent grid), work-group j taking window tokens [j * win_chunk, +win_chunk); each
+  // row gets win_wgs window partials
   int32_t win_wgs;
   int32_t win_chunk;         // <= kFusedWindowMax
   const uint16_t* win_k;     // bf16 [B][Hkv][win_cap][D]
@@ -60,6 +64,7 @@ struct SplitArgs {
   const int32_t* win_lens;   // [B]
   int32_t win_cap;
   float win_sm;              // softmax scale (natural units)
+  const uint16_t* win_q;     // bf16 [B][Hq][D] the query the window meets (the caller's q)
 };
 constexpr int kMaxWindowWgs = 8;      // window work-groups per pair inside the decode launch
 constexpr int kFusedWindowMax = 512;  // window tokens of one work-group inside the decode launch
@@ -71,14 +76,25 @@ struct LaunchEvents {
   hipEvent_t stop = nullptr;
 };
 hipError_t launch_decode(int bits, bool k_channel, bool v_channel, int group, int batch, int hkv,
-                         const SplitArgs& sa, hipStream_t stream, const LaunchEvents& ev);  // paged: sa.block_table
+                         const SplitArgs& sa, hipStream_t stream, const LaunchEvents& ev);  // by sa.block_table, sa.rot
 
-// Work-groups of the decode kernel for (bits, layout sides, group) one CU holds at once.
-hipError_t decode_occupancy(int bits, bool k_channel, bool v_channel, int group, bool paged, int* per_cu);
-// the paged-cache instances (decode_paged.hip)
-hipError_t launch_decode_paged(int bits, bool k_channel, bool v_channel, int group, int batch, int hkv,
-                               const SplitArgs& sa, hipStream_t stream, const LaunchEvents& ev);
-hipError_t decode_occupancy_paged(int bits, bool k_channel, bool v_channel, int group, int* per_cu);
+// Work-groups of the decode kernel for (bits, layout sides, group, paged, rotated) one CU holds at once.
+hipError_t decode_occupancy(int bits, bool k_channel, bool v_channel, int group, bool paged, bool rot, int* per_cu);
+// The four variants of the decode kernel, each instantiated in a source file of its own (decode.hip,
+// decode_paged.hip, decode_rot.hip, decode_paged_rot.hip): launch, or report the occupancy in *per_cu.
+using SplitLauncher = hipError_t (*)(int bits, bool kch, bool vch, int group, int batch, int hkv,
+                                     const SplitArgs& sa, hipStream_t stream, int* per_cu, const LaunchEvents& ev);
+hipError_t launch_split_plain(int bits, bool kch, bool vch, int group, int batch, int hkv, const SplitArgs& sa,
+                              hipStream_t stream, int* per_cu, const LaunchEvents& ev);
+hipError_t launch_split_paged(int bits, bool kch, bool vch, int group, int batch, int hkv, const SplitArgs& sa,
+                              hipStream_t stream, int* per_cu, const LaunchEvents& ev);
+hipError_t launch_split_rot(int bits, bool kch, bool vch, int group, int batch, int hkv, const SplitArgs& sa,
+                            hipStream_t stream, int* per_cu, const LaunchEvents& ev);
+hipError_t launch_split_paged_rot(int bits, bool kch, bool vch, int group, int batch, int hkv, const SplitArgs& sa,
+                                  hipStream_t stream, int* per_cu, const LaunchEvents& ev);
+// dst[r] = bf16(q[r] H) for rows r < rows of 128 bf16 values (rotated keys); `start` (may be null)
+// is recorded by the dispatch before the kernel
+hipError_t launch_rotate_query(int rows, const uint16_t* q, uint16_t* dst, hipStream_t stream, hipEvent_t start);
 // Quantise tokens [start_b, start_b + count_b) of new keys / values into the cache (quant.hip).
 hipError_t launch_quantize(int bits, bool k_channel, bool v_channel, int group, int batch, int hkv, int tcap,
                            int n_src, const void* k_src, const void* v_src, const int32_t* start, const int32_t* count,

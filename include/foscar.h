@@ -69,6 +69,25 @@ extern "C" {
 #define FOSCAR_K_CHANNEL 1
 #define FOSCAR_V_TOKEN 0
 #define FOSCAR_V_CHANNEL 2
+/* Rotated cache (decode entry points only; OR with the bits above).  The
+ * accuracy recipe the explainer's accuracy paragraph names ("OSCAR's
+ * rotations"; its related explainers: KVarN, a Hadamard-rotated 2-bit KV
+ * cache): the cache holds the quantised rows of K H and/or V H, H the
+ * orthonormal Sylvester-Hadamard matrix of order 128 (entry (i, j) =
+ * (-1)^popcount(i & j) / sqrt(128); symmetric, H H = I).
+ *   FOSCAR_K_ROTATED: the keys are rotated; each step rotates the query once
+ *     (q H, rounded once to bf16 from an fp64 transform whose sums are exact)
+ *     before it meets them, so the scores are those of q against K.  A small
+ *     kernel ahead of the decode writes the rotated rows into `out`, where the
+ *     decode reads them before it writes the output over them: `out` must not
+ *     overlap `q`.
+ *   FOSCAR_V_ROTATED: the values are rotated; the cache's weighted value sum is
+ *     taken back by H (fp32) before the final division, so `out` is in the
+ *     model's basis.
+ * A full-precision window (foscar_decode_window_*) holds unrotated rows and
+ * meets the query itself.  The rotated query must lie in the fp16 range. */
+#define FOSCAR_K_ROTATED 4
+#define FOSCAR_V_ROTATED 8
 
 /* Sides for pack / unpack / sizing. */
 #define FOSCAR_SIDE_K 0
@@ -103,7 +122,7 @@ typedef struct foscar_dims {
  *           past T_b (codes, scales, offsets) may hold anything, NaN included,
  *           and do not affect the result.  A channel-wise group that reaches
  *           past T_b covers only its tokens below T_b.
- * layout    FOSCAR_K_* | FOSCAR_V_*
+ * layout    FOSCAR_K_* | FOSCAR_V_* (| FOSCAR_K_ROTATED | FOSCAR_V_ROTATED)
  * group     g in {32, 64, 128} (channels for a token-wise side, tokens for a
  *           channel-wise side; the same g for both sides)
  * out       bf16  [B][Hq][D]  softmax(sm_scale * q K^T) V over the dequantised

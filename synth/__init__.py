@@ -23,7 +23,12 @@ Readings where the pages are silent (each one is listed in the design notes):
     quantised over its valid tokens only;
   * every random stream is ``numpy.random.default_rng([seed, workload id,
     tensor id, b, h])`` so any (sequence, KV head) slice can be regenerated
-    on its own.
+    on its own;
+  * a rotated cache (``Spec.rotate``; the accuracy recipe the explainer's
+    accuracy paragraph names, "OSCAR's rotations", and its related explainer
+    on a Hadamard-rotated 2-bit KV cache) stores the quantised rows of x H,
+    H = scipy.linalg.hadamard(D) / sqrt(D), where x are the drawn rows with
+    their channel scales and outliers: the writer rotates, then quantises.
 """
 from __future__ import annotations
 
@@ -65,6 +70,7 @@ class Spec:
     channel_std_logu: Optional[tuple] = None  # (lo, hi) per-(head, channel) std, log-uniform
     seed: int = 0
     lens: Optional[tuple] = None    # explicit per-sequence lengths (edge-case tests)
+    rotate: str = ""                # cache sides ("k", "v", "kv") stored as rows of x H (Hadamard-rotated)
 
     @property
     def sm_scale(self) -> float:
@@ -164,6 +170,11 @@ def _channel_std(spec: Spec, tensor: int, h: int) -> np.ndarray:
     return np.exp(rng.uniform(math.log(lo), math.log(hi), size=spec.head_dim)).astype(np.float32)
 
 
+def _rotation(d: int) -> np.ndarray:
+    from scipy.linalg import hadamard
+    return hadamard(d) / math.sqrt(d)
+
+
 _CHUNK = 65536  # tokens per generation step (a multiple of every group size)
 
 
@@ -195,6 +206,8 @@ def make_head(spec: Spec, b: int, h: int, seq_len: Optional[int] = None, poison:
                 x *= std[None, :]
             if outl is not None:
                 x[:, outl] *= np.float32(spec.k_outlier_scale)
+            if name in spec.rotate:
+                x = (x.astype(np.float64) @ _rotation(D)).astype(np.float32)
             if layout == TOKEN:
                 qc, sc, zc = quantize_minmax(x.reshape(rows, D // g, g), spec.bits, axis=2)
                 q[c0:c1] = qc.reshape(rows, D)

@@ -26,17 +26,18 @@ def stage_spec(spec, poison=False, q=None):
     return dev, qh, lens
 
 
-def run(spec, dev, sm_scale=0.0):
+def run(spec, dev, sm_scale=0.0, rotate=""):
     import bit_quantized_kv_split_amd as fos
     import torch
     out, lse = fos.decode(dev["q"], dev["packed_k"], dev["packed_v"], dev["k_scale"], dev["k_zero"], dev["v_scale"],
                           dev["v_zero"], dev["seq_lens"], bits=spec.bits, k_layout=spec.k_layout,
-                          v_layout=spec.v_layout, group=spec.group, sm_scale=sm_scale or spec.sm_scale)
+                          v_layout=spec.v_layout, group=spec.group, sm_scale=sm_scale or spec.sm_scale,
+                          rotate=rotate)
     torch.cuda.synchronize()
     return out.float().cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64)
 
 
-def oracle_rows(spec, rows, q, lens, poison=False):
+def oracle_rows(spec, rows, q, lens, poison=False, rotate=""):
     """Oracle output for (b, query head) rows, regenerating only the needed (b, KV head) slices."""
     G = spec.num_q_heads // spec.num_kv_heads
     outs, lses = [], []
@@ -47,16 +48,16 @@ def oracle_rows(spec, rows, q, lens, poison=False):
         w["q"] = q[b:b + 1, i:i + 1]
         w["seq_lens"] = np.array([lens[b]], np.int32)
         o, l = oracle.decode_rows(w, [(0, 0)], k_layout=spec.k_layout, v_layout=spec.v_layout, group=spec.group,
-                                  sm_scale=spec.sm_scale)
+                                  sm_scale=spec.sm_scale, rotate=rotate)
         outs.append(o[0])
         lses.append(l[0])
     return np.array(outs), np.array(lses)
 
 
-def oracle_all(spec, q, lens, poison=False):
+def oracle_all(spec, q, lens, poison=False, rotate=""):
     """(out, lse) for every row: out [B, Hq, D], lse [B, Hq]."""
     rows = [(b, i) for b in range(spec.batch) for i in range(spec.num_q_heads)]
-    o, l = oracle_rows(spec, rows, q, lens, poison)
+    o, l = oracle_rows(spec, rows, q, lens, poison, rotate)
     B, Hq = spec.batch, spec.num_q_heads
     return o.reshape(B, Hq, -1), l.reshape(B, Hq)
 

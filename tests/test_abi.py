@@ -65,7 +65,9 @@ def _decode(lib, dims, layout=0, group=128, ptr=1):
     (dict(max_seq_len=1000), 0, 128, -2),                    # not a multiple of 64
     (dict(max_seq_len=192), 2, 128, -2),                     # channel-wise group of 128 does not divide 192
     (dict(batch=-1), 0, 128, -1),
-    (dict(), 4, 128, -1),                                    # bad layout bits
+    (dict(), 16, 128, -1),                                   # bad layout bits (0-15: sides and rotation)
+    (dict(), -1, 128, -1),
+    (dict(max_seq_len=192), 2 | 4, 128, -2),                 # rotation bits keep the channel-wise check
     (dict(), 0, 48, -2),                                     # bad group
 ])
 def test_invalid_arguments_return_codes_before_any_gpu_call(lib, kw, layout, group, code):
@@ -114,7 +116,7 @@ def test_occupancy_rejects_bad_arguments(lib):
     n = ctypes.c_int32(0)
     assert lib.foscar_occupancy(3, 0, 128, ctypes.byref(n)) == -2
     assert lib.foscar_occupancy(2, 0, 48, ctypes.byref(n)) == -2
-    assert lib.foscar_occupancy(2, 4, 128, ctypes.byref(n)) == -1
+    assert lib.foscar_occupancy(2, 16, 128, ctypes.byref(n)) == -1
     assert lib.foscar_occupancy(2, 0, 128, None) == -1
 
 
@@ -172,7 +174,7 @@ def test_decode_window_rejects_bad_arguments_before_any_gpu_call(lib):
     assert _decode_window(lib, _dims(), win_cap=4097) == -2          # largest window: 4096 tokens
     assert _decode_window(lib, _dims(), win_ptr=0) == -1             # window pointers missing
     assert _decode_window(lib, _dims(head_dim=64)) == -2
-    assert _decode_window(lib, _dims(), layout=4) == -1
+    assert _decode_window(lib, _dims(), layout=16) == -1
     assert _decode_window(lib, None) == -1
     assert _decode_window(lib, _dims(batch=0), ptr=0, win_ptr=0) == 0
 

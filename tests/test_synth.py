@@ -87,3 +87,26 @@ def test_append_case_and_window_generators_are_seeded_and_shaped():
     assert all(np.array_equal(w1[k], w2[k]) for k in w1)
     assert w1["k"].shape == (3, 2, 40, 128) and w1["lens"].dtype == np.int32
     assert np.array_equal(synth.bf16_round(w1["v"]), w1["v"])
+
+
+def test_rotated_cache_holds_rotated_rows():
+    """Spec.rotate: the stored rows dequantise to the drawn rows times the
+    orthonormal Hadamard matrix (within the quantisation step), and the sides
+    it does not name are the unrotated cache, code for code."""
+    import oracle
+    spec = synth.Spec("rot_gen", 40, 4, "token", "channel", 32, 1, 4, 1, 128, 256, channel_std_logu=(0.1, 10.0))
+    plain = synth.make_head(spec, 0, 0)
+    rot = synth.make_head(spec.replace(rotate="k"), 0, 0)
+    for name in ("v_codes", "v_scale", "v_zero"):
+        np.testing.assert_array_equal(rot[name], plain[name])
+    H = oracle.hadamard(128)
+
+    def deq(w):
+        s = np.repeat(w["k_scale"].astype(np.float64), 32, axis=1)
+        return s * w["k_codes"] + np.repeat(w["k_zero"].astype(np.float64), 32, axis=1)
+    kp, kr = deq(plain), deq(rot)
+    step = np.repeat(rot["k_scale"].astype(np.float64), 32, axis=1)
+    # rotating the plain rows back and forth: kr H^T ~ kp, each side within its own quantisation step
+    err = np.abs(kr @ H.T - kp)
+    assert err.mean() < 0.5 * (step.mean() + np.repeat(plain["k_scale"].astype(np.float64), 32, axis=1).mean())
+    assert np.abs(kr - kp).mean() > 10 * err.mean()  # and the stored rows did change
