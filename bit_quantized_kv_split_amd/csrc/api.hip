@@ -401,7 +401,9 @@ int quantize_common(int bits, const foscar_dims* d, const void* k_src, const voi
                     void* kz, void* vs, void* vz, void* stream) {
   int rc = check_dims(d, false);
   if (rc) return rc;
-  if (layout < 0 || layout > 3 || src_tokens < 0) return FOSCAR_EINVAL;
+  if (layout < 0 || layout > 15 || src_tokens < 0) return FOSCAR_EINVAL;
+  const int rot = layout >> 2;  // FOSCAR_K_ROTATED, FOSCAR_V_ROTATED: rotate those rows first
+  layout &= 3;
   if (!valid_group(group)) return FOSCAR_EUNSUPPORTED;
   if (d->max_seq_len % foscar::kTile != 0 || d->max_seq_len > (1 << 24)) return FOSCAR_EUNSUPPORTED;
   if (layout != 0 && d->max_seq_len % group != 0) return FOSCAR_EUNSUPPORTED;
@@ -412,7 +414,7 @@ int quantize_common(int bits, const foscar_dims* d, const void* k_src, const voi
       !aligned(kz, 16) || !aligned(vs, 16) || !aligned(vz, 16) || !aligned(start, 4) || !aligned(count, 4))
     return FOSCAR_EINVAL;
   const hipError_t e = foscar::launch_quantize(bits, (layout & FOSCAR_K_CHANNEL) != 0, (layout & FOSCAR_V_CHANNEL) != 0,
-                                               group, d->batch, d->num_kv_heads, d->max_seq_len, src_tokens, k_src,
+                                               group, rot, d->batch, d->num_kv_heads, d->max_seq_len, src_tokens, k_src,
                                                v_src, start, count, pk, pv, ks, kz, vs, vz, (hipStream_t)stream);
   return e == hipSuccess ? FOSCAR_OK : hip_fail(e);
 }

@@ -95,8 +95,9 @@ hipError_t launch_split_paged_rot(int bits, bool kch, bool vch, int group, int b
 // dst[r] = bf16(q[r] H) for rows r < rows of 128 bf16 values (rotated keys); `start` (may be null)
 // is recorded by the dispatch before the kernel
 hipError_t launch_rotate_query(int rows, const uint16_t* q, uint16_t* dst, hipStream_t stream, hipEvent_t start);
-// Quantise tokens [start_b, start_b + count_b) of new keys / values into the cache (quant.hip).
-hipError_t launch_quantize(int bits, bool k_channel, bool v_channel, int group, int batch, int hkv, int tcap,
+// Quantise tokens [start_b, start_b + count_b) of new keys / values into the cache (quant.hip);
+// rot bit 0 / bit 1: rotate the key / value rows by the orthonormal Hadamard matrix first.
+hipError_t launch_quantize(int bits, bool k_channel, bool v_channel, int group, int rot, int batch, int hkv, int tcap,
                            int n_src, const void* k_src, const void* v_src, const int32_t* start, const int32_t* count,
                            void* pk, void* pv, void* ks, void* kz, void* vs, void* vz, hipStream_t stream);
 hipError_t launch_pack(int bits, int side, int batch, int hkv, int tcap, const uint8_t* codes, uint32_t* packed,

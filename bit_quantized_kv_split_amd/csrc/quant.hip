@@ -96,6 +96,7 @@ struct QuantArgs {
   uint16_t* vs;
   uint16_t* vz;
   int32_t hkv, tcap, n_src;
+  int32_t rot;             // bit 0: rotate the key rows, bit 1: the value rows (rotate_row8)
 };
 
 // Codes of 8 values with scales s[j], offsets z[j] and r[j] = rcp(s[j]) (0
@@ -177,11 +178,47 @@ __device__ __forceinline__ void unpack_bf16x8(const uint4& w, float (&x)[8]) {
   x[4] = bf16_lo(w.z); x[5] = bf16_hi(w.z); x[6] = bf16_lo(w.w); x[7] = bf16_hi(w.w);
 }
 
+// Rotated cache: the 128 channels of one token row, held 8 per lane (channel
+// 8 o + j in x[j], o = lane % 16, the 16 lanes of a token slot), times the
+// orthonormal Sylvester-Hadamard matrix H.  Butterflies on the channel index
+// bits, 0-2 inside the lane and 3-6 against lanes o ^ 1, 2, 4, 8, in fp64,
+// where the sums of bf16 values are exact (rows spanning under 2^38); then
+// one scaling by 1/sqrt(128) in fp64 and one rounding to fp32, the precision
+// the codes are decided in.
+__device__ __forceinline__ void rotate_row8(float (&x)[8], int o) {
+  double v[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) v[j] = (double)x[j];
+#pragma unroll
+  for (int h = 1; h < 8; h <<= 1) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      if (j & h) continue;
+      const double a = v[j], b = v[j | h];
+      v[j] = a + b;
+      v[j | h] = a - b;
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const bool upper = (o >> k) & 1;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const double p = __shfl_xor(v[j], 1 << k);
+      v[j] = upper ? p - v[j] : v[j] + p;
+    }
+  }
+  constexpr double kInvSqrt128 = 0x1.6a09e667f3bcdp-4;  // 1/sqrt(128) = sqrt(2)/16, correctly rounded
+#pragma unroll
+  for (int j = 0; j < 8; ++j) x[j] = (float)(v[j] * kInvSqrt128);
+}
+
 // One side (keys or values) of tokens [t_lo, t_hi) of one (sequence, KV head).
 // Lane l works on token slot r = l / 16 of each step of four tokens and on the
 // channel octet o = l % 16 (channels 8o .. 8o+7): one 16-byte load per lane
-// and row, four consecutive 256-byte rows per wave-instruction.
-template <int BITS, bool CH, int GRP, bool VALUE>
+// and row, four consecutive 256-byte rows per wave-instruction.  ROT: the rows
+// are rotated (rotate_row8) before they are quantised.
+template <int BITS, bool CH, int GRP, bool VALUE, bool ROT>
 __device__ __forceinline__ void quant_side(const uint32_t* src, uint32_t* packed, uint16_t* sc, uint16_t* zr,
                                            size_t bh, int tcap, int n_src, int s0, int t_lo, int t_hi) {
   constexpr int D = kHeadDim, E = 32 / BITS, KW = D / E;
@@ -254,6 +291,7 @@ __device__ __forceinline__ void quant_side(const uint32_t* src, uint32_t* packed
         const bool act = t >= t_lo && t < t_hi;
         float x[8];
         unpack_bf16x8(wb[u], x);
+        if constexpr (ROT) rotate_row8(x, o);
         float mn = fminf(fminf(fminf(x[0], x[1]), fminf(x[2], x[3])), fminf(fminf(x[4], x[5]), fminf(x[6], x[7])));
         float mx = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])), fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
         octet_group_minmax<GRP / 8>(mn, mx);  // the g/8 lanes of this lane's group
@@ -294,6 +332,7 @@ __device__ __forceinline__ void quant_side(const uint32_t* src, uint32_t* packed
           if (tb0 + 4 * u + r >= g1) continue;  // this slot's token is past the group (lane-local)
           float x[8];
           unpack_bf16x8(wb[u], x);
+          if constexpr (ROT) rotate_row8(x, o);  // (the 16 lanes of a slot skip or run together)
 #pragma unroll
           for (int j = 0; j < 8; ++j) {
             mn[j] = fminf(mn[j], x[j]);
@@ -331,6 +370,7 @@ __device__ __forceinline__ void quant_side(const uint32_t* src, uint32_t* packed
           const bool act = t < g1;
           float x[8];
           unpack_bf16x8(wb[u], x);
+          if constexpr (ROT) rotate_row8(x, o);
           uint32_t c[8];
           code8<BITS>(x, gq, rc, c);
           if constexpr (!VALUE) {
@@ -356,8 +396,14 @@ __global__ __launch_bounds__(64) void quant_append(const QuantArgs a) {
   const int t_lo = max(blk, s0), t_hi = min(blk + kQBlock, s0 + n);
   if (t_lo >= t_hi) return;
   const size_t bh = (size_t)b * a.hkv + h;
-  quant_side<BITS, KCH, GRP, false>(a.ksrc, a.pk, a.ks, a.kz, bh, a.tcap, a.n_src, s0, t_lo, t_hi);
-  quant_side<BITS, VCH, GRP, true>(a.vsrc, a.pv, a.vs, a.vz, bh, a.tcap, a.n_src, s0, t_lo, t_hi);
+  if (a.rot & 1)
+    quant_side<BITS, KCH, GRP, false, true>(a.ksrc, a.pk, a.ks, a.kz, bh, a.tcap, a.n_src, s0, t_lo, t_hi);
+  else
+    quant_side<BITS, KCH, GRP, false, false>(a.ksrc, a.pk, a.ks, a.kz, bh, a.tcap, a.n_src, s0, t_lo, t_hi);
+  if (a.rot & 2)
+    quant_side<BITS, VCH, GRP, true, true>(a.vsrc, a.pv, a.vs, a.vz, bh, a.tcap, a.n_src, s0, t_lo, t_hi);
+  else
+    quant_side<BITS, VCH, GRP, true, false>(a.vsrc, a.pv, a.vs, a.vz, bh, a.tcap, a.n_src, s0, t_lo, t_hi);
 }
 
 template <int BITS, bool KCH, bool VCH>
@@ -379,10 +425,11 @@ hipError_t launch_bits(bool kch, bool vch, int group, dim3 grid, const QuantArgs
 
 }  // namespace
 
-hipError_t launch_quantize(int bits, bool k_channel, bool v_channel, int group, int batch, int hkv, int tcap,
+hipError_t launch_quantize(int bits, bool k_channel, bool v_channel, int group, int rot, int batch, int hkv, int tcap,
                            int n_src, const void* k_src, const void* v_src, const int32_t* start, const int32_t* count,
                            void* pk, void* pv, void* ks, void* kz, void* vs, void* vz, hipStream_t stream) {
   QuantArgs a;
+  a.rot = rot;
   a.ksrc = (const uint32_t*)k_src;
   a.vsrc = (const uint32_t*)v_src;
   a.start = start;

@@ -69,7 +69,7 @@ extern "C" {
 #define FOSCAR_K_CHANNEL 1
 #define FOSCAR_V_TOKEN 0
 #define FOSCAR_V_CHANNEL 2
-/* Rotated cache (decode entry points only; OR with the bits above).  The
+/* Rotated cache (OR with the bits above).  The
  * accuracy recipe the explainer's accuracy paragraph names ("OSCAR's
  * rotations"; its related explainers: KVarN, a Hadamard-rotated 2-bit KV
  * cache): the cache holds the quantised rows of K H and/or V H, H the
@@ -86,6 +86,9 @@ extern "C" {
  *     model's basis.
  * A full-precision window (foscar_decode_window_*) holds unrotated rows and
  * meets the query itself.  The rotated query must lie in the fp16 range. */
+/* For foscar_quantize_int2/int4 the same bits rotate the new key / value rows
+ * (x H: fp64 butterflies, exact for bf16 values, one rounding to fp32) before
+ * they are quantised, so that the cache holds the rows the decode expects. */
 #define FOSCAR_K_ROTATED 4
 #define FOSCAR_V_ROTATED 8
 
@@ -262,7 +265,8 @@ int foscar_decode_paged_int4(const foscar_dims* dims, const void* q, const void*
  *               [start[b], start[b] + n_b), n_b = count[b] clamped to
  *               [0, min(src_tokens, Tcap - start[b])]; start[b] outside
  *               [0, Tcap] leaves the sequence untouched
- * layout, group as for decode.  A token-wise side quantises each token's
+ * layout, group as for decode (with FOSCAR_K_ROTATED / FOSCAR_V_ROTATED, the
+ *               rows of that side are rotated first).  A token-wise side quantises each token's
  *               groups of g channels.  A channel-wise side needs start[b] to
  *               be a multiple of g (otherwise sequence b is left untouched);
  *               each group g*tau .. g*tau + g - 1 the range reaches is

@@ -101,17 +101,22 @@ def attend(q_row, k_hat, v_hat, sm_scale: float):
     return o, m + math.log(l)
 
 
-def hadamard(n: int) -> np.ndarray:
-    """Orthonormal Sylvester-Hadamard matrix of order n (a power of two):
-    H_1 = [1], H_2m = [[H_m, H_m], [H_m, -H_m]], scaled by 1/sqrt(n), so that
-    entry (i, j) is (-1)^popcount(i & j) / sqrt(n); symmetric and its own
-    inverse."""
+def sylvester(n: int) -> np.ndarray:
+    """The +-1 Sylvester-Hadamard matrix of order n (a power of two):
+    S_1 = [1], S_2m = [[S_m, S_m], [S_m, -S_m]]; entry (i, j) is
+    (-1)^popcount(i & j)."""
     if n < 1 or n & (n - 1):
         raise ValueError("order must be a power of two")
     h = np.ones((1, 1))
     while h.shape[0] < n:
         h = np.block([[h, h], [h, -h]])
-    return h / math.sqrt(n)
+    return h
+
+
+def hadamard(n: int) -> np.ndarray:
+    """Orthonormal Sylvester-Hadamard matrix of order n: sylvester(n) /
+    sqrt(n), symmetric and its own inverse."""
+    return sylvester(n) / math.sqrt(n)
 
 
 def round_bf16(x) -> np.ndarray:

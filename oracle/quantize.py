@@ -26,13 +26,25 @@ the precision the GPU quantiser decides codes in):
   the range holds; codes and (s, z) of tokens outside the range are left as
   they were.
 
+* ``rotate_rows``: a rotated cache (the accuracy recipe of the explainer's
+  accuracy paragraph, "OSCAR's rotations"; its related explainer on a
+  Hadamard-rotated 2-bit KV cache) stores the codes of x H instead of x, H
+  the orthonormal Sylvester-Hadamard matrix.  Reading: the rotated rows are
+  held in fp32, the precision the quantiser decides in, each the one fp32
+  rounding of (the exact +-1 sum) times (1/sqrt(D) in fp64); ``quantize_append``
+  rotates the sides ``rotate`` names before it quantises them.
+
 Parity pins: ``tests/test_oracle_quant_pins.py`` (exact recovery of values
 on a known grid, constant groups, round-half-even ties, the rounding error
 bound, append order independence).
 """
 from __future__ import annotations
 
+import math
+
 import numpy as np
+
+from . import sylvester
 
 TOKEN = "token"
 CHANNEL = "channel"
@@ -62,8 +74,25 @@ def quantize_group(x, bits: int, axis: int = -1):
     return q.astype(np.uint8), s16, z16
 
 
+def inv_sqrt(d: int) -> float:
+    """1/sqrt(d) for d a power of two, correctly rounded in fp64 (2^-k/2, or
+    sqrt(2) 2^-(k+1)/2 with sqrt correctly rounded and the power exact)."""
+    k = d.bit_length() - 1
+    return math.ldexp(1.0, -k // 2) if k % 2 == 0 else math.ldexp(math.sqrt(2.0), -(k + 1) // 2)
+
+
+def rotate_rows(x) -> np.ndarray:
+    """Rows (last axis, D a power of two) of x -- bf16 values -- times the
+    orthonormal Hadamard matrix, in fp32: the +-1 sums are exact in fp64 (for
+    rows whose values span under 2^38 in magnitude), then scaled by
+    fp64(1/sqrt(D)) and rounded once to fp32."""
+    x = np.asarray(x, dtype=np.float64)
+    D = x.shape[-1]
+    return ((x @ sylvester(D)) * inv_sqrt(D)).astype(np.float32)
+
+
 def quantize_append(cache: dict, k_src, v_src, start, count, *, bits: int, k_layout: str, v_layout: str,
-                    group: int) -> dict:
+                    group: int, rotate: str = "") -> dict:
     """Quantise new tokens into a copy of ``cache`` and return it.
 
     cache: k_codes, v_codes uint8 [B][Hkv][Tcap][D]; k_scale, k_zero,
@@ -73,7 +102,11 @@ def quantize_append(cache: dict, k_src, v_src, start, count, *, bits: int, k_lay
     row r of sequence b is token start[b] + r.
     start, count: int [B].  Per sequence: start outside [0, Tcap] leaves it
     untouched; count is clamped to [0, min(N, Tcap - start)].
+    rotate: "", "k", "v" or "kv" -- the sides whose rows are rotated
+    (``rotate_rows``) before they are quantised.
     """
+    if rotate not in ("", "k", "v", "kv"):
+        raise ValueError(rotate)
     out = {k: np.array(v, copy=True) for k, v in cache.items()}
     B, Hkv, Tcap, D = out["k_codes"].shape
     N = np.asarray(k_src).shape[2]
@@ -89,6 +122,8 @@ def quantize_append(cache: dict, k_src, v_src, start, count, *, bits: int, k_lay
             continue
         for side, src, layout in (("k", k_src, k_layout), ("v", v_src, v_layout)):
             x = np.asarray(src, dtype=np.float32)[b, :, :n, :]          # [Hkv][n][D]
+            if side in rotate:
+                x = rotate_rows(x)
             codes = out[f"{side}_codes"][b]
             sc = out[f"{side}_scale"][b]
             zr = out[f"{side}_zero"][b]

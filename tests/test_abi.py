@@ -146,7 +146,7 @@ def _quantize(lib, dims, layout=0, group=128, src_tokens=16, ptr=1, bits=2):
     (dict(max_seq_len=1000), 0, 128, 16, -2),                 # not a multiple of 64
     (dict(max_seq_len=192), 1, 128, 16, -2),                  # channel-wise group of 128 does not divide 192
     (dict(batch=70000), 0, 128, 16, -2),                      # grid z
-    (dict(), 5, 128, 16, -1),                                 # bad layout bits
+    (dict(), 16, 128, 16, -1),                                # bad layout bits (0-15: sides and rotation)
     (dict(), 0, 16, 16, -2),                                  # bad group
     (dict(), 0, 128, -1, -1),                                 # negative source length
 ])

@@ -4,7 +4,9 @@ word, scale and offset bit-exact, on caches that already hold arbitrary
 content, for every (bits, K layout, V layout, g) instance; ragged starts and
 counts, unaligned channel-wise starts, out-of-range starts, single-token
 appends over several calls, a full-size long-context prefill (sampled
-slices), and quantise-then-decode against the decode oracle.
+slices), and quantise-then-decode against the decode oracle; the same for a
+rotated cache (rows rotated by the Hadamard matrix before they are
+quantised).
 """
 import numpy as np
 import pytest
@@ -33,13 +35,13 @@ def _scales(case, side, layout, g, T):
     return out
 
 
-def _expected(case, bits, kl, vl, g, T):
+def _expected(case, bits, kl, vl, g, T, rotate=""):
     ks, kz = _scales(case, "k", kl, g, T)
     vs, vz = _scales(case, "v", vl, g, T)
     cache = {"k_codes": oracle.unpack_k(case["packed_k"], bits, D), "v_codes": oracle.unpack_v(case["packed_v"], bits),
              "k_scale": ks, "k_zero": kz, "v_scale": vs, "v_zero": vz}
     out = oq.quantize_append(cache, case["k_src"], case["v_src"], case["start"], case["count"], bits=bits,
-                             k_layout=kl, v_layout=vl, group=g)
+                             k_layout=kl, v_layout=vl, group=g, rotate=rotate)
     return {"packed_k": oracle.pack_k(out["k_codes"], bits), "packed_v": oracle.pack_v(out["v_codes"], bits),
             "k_scale": out["k_scale"], "k_zero": out["k_zero"], "v_scale": out["v_scale"], "v_zero": out["v_zero"]}
 
@@ -60,13 +62,13 @@ def _to_device(case, kl, vl, g, T):
     }
 
 
-def _quantize(d, bits, kl, vl, g, k_src=None, v_src=None, start=None, count=None):
+def _quantize(d, bits, kl, vl, g, k_src=None, v_src=None, start=None, count=None, rotate=""):
     fos = _fos()
     fn = fos.foscar_quantize_int2 if bits == 2 else fos.foscar_quantize_int4
     fn(d["k_src"] if k_src is None else k_src, d["v_src"] if v_src is None else v_src,
        d["start"] if start is None else start, d["count"] if count is None else count,
        d["packed_k"], d["packed_v"], d["k_scale"], d["k_zero"], d["v_scale"], d["v_zero"],
-       fos.layout_bits(kl, vl), g)
+       fos.layout_bits(kl, vl, rotate), g)
 
 
 def _compare(d, exp, what):
@@ -189,3 +191,48 @@ def test_quantize_then_decode(bits, kl, vl):
     ro, rl = oracle.decode(w, k_layout=kl, v_layout=vl, group=g, sm_scale=1 / np.sqrt(D))
     check(out.float().cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64), ro, rl,
           f"quantise+decode int{bits} {kl}/{vl}")
+
+
+@pytest.mark.parametrize("rotate", ["k", "v", "kv"])
+@pytest.mark.parametrize("bits,kl,vl,g", [(2, "token", "token", 128), (4, "token", "channel", 32),
+                                          (2, "channel", "token", 64), (4, "channel", "channel", 128)])
+def test_rotated_writer_bit_exact(bits, kl, vl, g, rotate):
+    """Rows rotated by the Hadamard matrix (fp64 butterflies, one rounding to
+    fp32) before they are quantised: every word, scale and offset as the
+    oracle's quantiser over its own rotation of the rows."""
+    T, N = 512, 300
+    if "channel" in (kl, vl):
+        starts, counts = [0, g, 2 * g + 1, 256], [300, 45, 10, 1000]
+    else:
+        starts, counts = [0, 37, 200, 453], [300, 45, 1000, 1000]
+    case = synth.make_append_case(6, len(starts), 2, T, N, bits, starts, counts)
+    d = _to_device(case, kl, vl, g, T)
+    _quantize(d, bits, kl, vl, g, rotate=rotate)
+    _compare(d, _expected(case, bits, kl, vl, g, T, rotate=rotate), f"rotated {rotate} int{bits} {kl}/{vl} g{g}")
+
+
+@pytest.mark.parametrize("bits,kl,vl", [(2, "token", "token"), (4, "channel", "token")])
+def test_rotated_write_then_decode(bits, kl, vl):
+    """A rotated cache written by the GPU quantiser and decoded with the
+    rotation bits, against the decode oracle over the oracle's rotated cache."""
+    import torch
+    fos = _fos()
+    T, N, g, B, H, Hq = 512, 448, 64, 2, 2, 8
+    case = synth.make_append_case(7, B, H, T, N, bits, [0, 0], [N, 301])
+    exp = _expected(case, bits, kl, vl, g, T, rotate="kv")
+    d = _to_device(case, kl, vl, g, T)
+    _quantize(d, bits, kl, vl, g, rotate="kv")
+    _compare(d, exp, "rotated cache")
+    lens = np.array([N, 301], np.int32)
+    rng = np.random.default_rng(8)
+    q = synth.bf16_round(rng.standard_normal((B, Hq, D)).astype(np.float32))
+    out, lse = fos.decode(torch.from_numpy(q).to(torch.bfloat16).cuda(), d["packed_k"], d["packed_v"], d["k_scale"],
+                          d["k_zero"], d["v_scale"], d["v_zero"], torch.from_numpy(lens).cuda(), bits=bits,
+                          k_layout=kl, v_layout=vl, group=g, rotate="kv")
+    torch.cuda.synchronize()
+    w = {"q": q, "k_codes": oracle.unpack_k(exp["packed_k"], bits, D), "v_codes": oracle.unpack_v(exp["packed_v"], bits),
+         "k_scale": exp["k_scale"], "k_zero": exp["k_zero"], "v_scale": exp["v_scale"], "v_zero": exp["v_zero"],
+         "seq_lens": lens}
+    ro, rl = oracle.decode(w, k_layout=kl, v_layout=vl, group=g, sm_scale=1 / np.sqrt(D), rotate="kv")
+    got = out.float().cpu().numpy().astype(np.float64)
+    check(got, lse.cpu().numpy().astype(np.float64), ro, rl, f"rotated write+decode int{bits} {kl}/{vl}")

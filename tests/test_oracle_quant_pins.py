@@ -14,9 +14,12 @@
   writes outside the range, unaligned channel-wise starts and out-of-range
   starts leave the cache as it was.
 """
+import math
+
 import numpy as np
 import pytest
 
+import oracle
 import oracle.quantize as oq
 import synth
 
@@ -155,3 +158,59 @@ def test_out_of_range_writes_nothing():
                              k_layout="token", v_layout="token", group=g)
     assert np.array_equal(out["k_codes"][:, :, :24], cache["k_codes"][:, :, :24])
     assert not np.array_equal(out["k_scale"][:, :, 24:], cache["k_scale"][:, :, 24:])
+
+
+# ---------------------------------------------------------------- rotated writer
+
+def test_inv_sqrt_is_correctly_rounded():
+    """1/sqrt(d) in fp64 within half an ulp of the exact value (50-digit decimal)."""
+    from decimal import Decimal, getcontext
+    getcontext().prec = 50
+    for k in range(0, 12):
+        d = 1 << k
+        c = oq.inv_sqrt(d)
+        exact = 1 / Decimal(d).sqrt()
+        assert abs(Decimal(c) - exact) <= Decimal(math.ulp(c)) / 2, d
+
+
+def test_rotate_rows_unit_vectors_and_fp64_product():
+    """e_j H is row j of the +-1 matrix times 1/sqrt(D) (held in fp32);
+    random bf16 rows agree with the fp64 product by the orthonormal matrix to
+    fp32 rounding."""
+    S = oracle.sylvester(128)
+    c32 = np.float32(oq.inv_sqrt(128))
+    for j in (0, 1, 77, 127):
+        e = np.zeros(128)
+        e[j] = 1.0
+        np.testing.assert_array_equal(oq.rotate_rows(e), (S[j] * c32).astype(np.float32))
+    rng = np.random.default_rng(81)
+    x = synth.bf16_round(rng.standard_normal((64, 128)).astype(np.float32)).astype(np.float64)
+    y = oq.rotate_rows(x).astype(np.float64)
+    ref = x @ oracle.hadamard(128)
+    assert np.abs(y - ref).max() <= 2.0 ** -23 * np.abs(ref).max()
+    np.testing.assert_allclose(oq.rotate_rows(y) , x, atol=1e-5)  # H H = I up to the fp32 roundings
+
+
+@pytest.mark.parametrize("rotate", ["k", "v", "kv"])
+def test_rotated_append_quantises_rotated_rows(rotate):
+    """quantize_append(rotate=...) equals quantize_append of rows rotated
+    beforehand, side by side (the unnamed side untouched)."""
+    rng = np.random.default_rng(82)
+    B, H, T, N, g = 2, 1, 128, 70, 32
+    cache = {"k_codes": np.zeros((B, H, T, 128), np.uint8), "v_codes": np.zeros((B, H, T, 128), np.uint8)}
+    for n in ("k_scale", "k_zero"):
+        cache[n] = np.zeros((B, H, T, 128 // g), np.float16)
+    for n in ("v_scale", "v_zero"):
+        cache[n] = np.zeros((B, H, T // g, 128), np.float16)
+    ks = synth.bf16_round(rng.standard_normal((B, H, N, 128)).astype(np.float32))
+    vs = synth.bf16_round(rng.standard_normal((B, H, N, 128)).astype(np.float32))
+    kw = dict(bits=2, k_layout="token", v_layout="channel", group=g)
+    got = oq.quantize_append(cache, ks, vs, [0, 32], [70, 50], rotate=rotate, **kw)
+    want = oq.quantize_append(cache, oq.rotate_rows(ks) if "k" in rotate else ks,
+                              oq.rotate_rows(vs) if "v" in rotate else vs, [0, 32], [70, 50], **kw)
+    for name in got:
+        np.testing.assert_array_equal(got[name], want[name])
+    plain = oq.quantize_append(cache, ks, vs, [0, 32], [70, 50], **kw)
+    for side in ("k", "v"):
+        same = np.array_equal(got[side + "_codes"], plain[side + "_codes"])
+        assert same == (side not in rotate)
