@@ -20,6 +20,7 @@ import hashlib
 import json
 import math
 import os
+import re
 import sys
 import time
 
@@ -63,12 +64,18 @@ def parse():
 
 
 def kernel_sha():
-    """Hash of the library sources (kernels, launch and split plan)."""
+    """Hash of the library sources (kernels, launch and split plan), with the
+    comments and blank space taken out, so that only a change of code changes
+    it (the sources hold no string with a comment marker)."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "bit_quantized_kv_split_amd", "csrc")
     for name in sorted(os.listdir(csrc)):
-        with open(os.path.join(csrc, name), "rb") as f:
-            h.update(name.encode() + b"\0" + f.read())
+        with open(os.path.join(csrc, name)) as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", "", text)
+        code = " ".join(text.split())
+        h.update(name.encode() + b"\0" + code.encode())
     return h.hexdigest()[:16]
 
 

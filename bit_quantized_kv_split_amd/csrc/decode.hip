@@ -13,33 +13,35 @@
 //
 // Work decomposition (MI355X-native; the pages' Hopper/Blackwell pipelines
 // are not used):
-//   * grid = (ranges S, KV heads, sequences); a work-group of 4 waves owns one
-//     token range of one (sequence, KV head); waves take 64-token tiles (or
-//     g-token units when a channel-wise group is longer than a tile) in turn;
-//   * each wave streams its tiles HBM -> LDS with global_load_lds (dwordx4),
-//     NS tiles deep in a per-wave ring, then reads lane l's data (token l's
-//     packed key row, the value words of channels 2l, 2l+1, the quad's scales)
-//     into registers; no registers are held by loads in flight;
-//   * codes become matrix-core operands by one AND-OR per fp16 pair: a code
-//     dropped into the mantissa under a fixed exponent reads as C + q (C a
-//     power of two), and the C*sum(other operand) it adds is removed once per
-//     row together with the offset correction -- no per-value convert or FMA;
-//   * QK^T: v_mfma_f32_4x4x4_16b_f16, block = 4 tokens x 4 query heads, so
-//     each lane ends with 4 dense scores (4 tokens of its quad, one query head)
-//     and the key-side fold, mask and online softmax run on dense registers;
-//   * P V: the same instruction with blocks over channels; the 4x4 P block of
-//     every quad is shared through LDS (one 8-byte store, eight 16-byte loads
-//     per lane per tile);
-//   * online softmax with the exact running max of each query head (DPP,
-//     ds_swizzle and ds_bpermute reductions across the 16 lanes of a head; the
-//     accumulators are rescaled only when a max rises);
+//   * grid = (work pairs, ranges S); a work pair is (sequence, KV head, group
+//     of at most 4 of the KV head's query heads); a work-group of 4 waves owns
+//     one token range of one pair; waves take 64-token tiles (or g-token units
+//     when a channel-wise group is longer than a tile) in turn;
+//   * each wave streams its tiles HBM -> LDS with buffer loads straight to LDS
+//     (dwordx4), 2 tiles deep in a per-wave ring, then reads lane l's data into
+//     registers; no registers are held by loads in flight;
+//   * token-wise keys: QK^T on the block-scaled matrix cores
+//     (v_mfma_scale_f32_16x16x128_f8f6f4): an INT2 code under one AND is an fp4
+//     operand, an INT4 code an fp8 one, the query two exact e4m3 terms with one
+//     E8M0 scale per row; a 64-token tile is 4 blocks of 16 tokens laid out so
+//     that each lane ends with one query head's scores for the 4 tokens of a quad;
+//   * channel-wise keys and every P V product: v_mfma_f32_4x4x4_16b_f16 with
+//     code operands built by one AND-OR per fp16 pair (a code dropped into the
+//     mantissa under a fixed exponent reads as C + q; the C * sum(other operand)
+//     it adds is removed once per row) -- no per-value convert or FMA anywhere;
+//   * online softmax with the exact running max of each query head (DPP and
+//     permlane reductions; the accumulators are rescaled only when a max rises);
 //   * a range's partial (O, lse) goes to a workspace with device-coherent (sc1)
-//     relaxed stores; after its stores complete (vmcnt(0)) a work-group counts
-//     its arrival on the pair's counter, and the last to arrive merges the
-//     ranges by log-sum-exp, one memory round trip per 32 ranges: one decode
-//     step is one kernel launch;
+//     relaxed stores; after its stores complete a work-group counts its arrival
+//     on the pair's counter, and the last to arrive merges the ranges by
+//     log-sum-exp, one memory round trip per 32 ranges: one decode step is one
+//     kernel launch;
 //   * a full-precision window of recent tokens is attended by extra work-groups
 //     of the same launch (window_item) whose partials join that merge.
+// The kernel templates are in decode_kernels.h.  This file instantiates the
+// contiguous, unrotated variant, holds the rotated-query kernel of a rotated
+// cache, and dispatches a call to one of the four variants (contiguous or
+// paged, unrotated or rotated), each instantiated in a source file of its own.
 #include "decode_kernels.h"
 
 namespace foscar {

@@ -1,6 +1,7 @@
-// Kernel templates of the split decode (see decode.hip for the design); included
-// by decode.hip (contiguous cache) and decode_paged.hip (paged cache), which
-// instantiate the two halves in separate translation units.
+// Kernel templates of the split decode (decode.hip describes the design),
+// included by the four sources that instantiate its variants: decode.hip
+// (contiguous cache), decode_paged.hip (paged cache), decode_rot.hip and
+// decode_paged_rot.hip (rotated caches).
 #pragma once
 #include <math.h>
 
