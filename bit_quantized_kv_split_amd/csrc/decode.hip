@@ -18,8 +18,9 @@
 //     one token range of one pair; waves take 64-token tiles (or g-token units
 //     when a channel-wise group is longer than a tile) in turn;
 //   * each wave streams its tiles HBM -> LDS with buffer loads straight to LDS
-//     (dwordx4), 2 tiles deep in a per-wave ring, then reads lane l's data into
-//     registers; no registers are held by loads in flight;
+//     (dwordx4) into a one-tile slot per wave, copies lane l's data into
+//     registers and refills the slot with the next tile before working on the
+//     copy; no registers are held by loads in flight;
 //   * token-wise keys: QK^T on the block-scaled matrix cores
 //     (v_mfma_scale_f32_16x16x128_f8f6f4): an INT2 code under one AND is an fp4
 //     operand, an INT4 code an fp8 one, the query two exact e4m3 terms with one

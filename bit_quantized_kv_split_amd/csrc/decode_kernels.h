@@ -273,12 +273,17 @@ struct Stage {
   static constexpr int VSL = (VSB + 255) / 256;
   static constexpr int LOADS = KW / 4 + VW / 2 + 2 * KSL + 2 * VSL + (KCB + VCB) / 256;  // loads per tile
   static_assert(KOFF % 16 == 0, "K rows need 16-byte alignment");
-  // ring depth: two tiles in flight per wave; with four waves per work-group
-  // and four work-groups per CU the INT2 rings fit the 160 KB of LDS
+  // ring depth: one staged tile per wave.  A tile is copied into registers
+  // before it is processed and its slot refilled at once, so the next tile's
+  // load still overlaps the current tile's work; a second slot only halved the
+  // work-groups LDS lets a CU hold (the INT4 channel-wise rings took 72 KB: one
+  // work-group per CU).  Measured against two slots: INT4 channel-wise
+  // 100 -> 66 us per step, long-context INT2 64.0 -> 62.0, the others equal or
+  // a few percent faster.
 #ifdef FOSCAR_RING_DEPTH
   static constexpr int NS = FOSCAR_RING_DEPTH;
 #else
-  static constexpr int NS = 2;
+  static constexpr int NS = 1;
 #endif
 };
 
@@ -844,9 +849,16 @@ __device__ __forceinline__ void finish_range(const SplitArgs& a, const int b, co
   if (tid == 0) a.counters[bh] = 0;  // ready for the next call on this workspace
 }
 
+// Waves per SIMD the register allocation aims at (the LDS of a one-tile ring
+// never limits below it).  INT2 token-wise K and V, g = 128: 4 (128 VGPRs).
+// Other INT2 instances: 3 (168 VGPRs): left to themselves they took 180-190
+// (2 waves), and 3 waves ran the ragged token-K / channel-V batches 8-11%
+// faster and the channel-wise ones 2% faster; token-wise g = 32 would spill.
+// INT4: unconstrained; 3 waves made the ragged INT4 batches 2-6% slower.
 template <int BITS, bool KCH, bool VCH, int GRP>
 constexpr int waves_per_simd() {
-  return (BITS == 2 && !KCH && !VCH && GRP == 128) ? 4 : 1;
+  if (BITS == 2 && !KCH && !VCH) return GRP == 128 ? 4 : (GRP == 64 ? 3 : 1);
+  return BITS == 2 ? 3 : 1;
 }
 
 // One work item: range `split` of KV head h of sequence b (T = 0 and split = 0:
