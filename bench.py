@@ -58,6 +58,9 @@ def parse():
                     help="decode with a bf16 window of this many recent tokens per sequence beside the cache")
     ap.add_argument("--op", choices=["decode", "quantize"], default="decode",
                     help="decode: the decode step (default); quantize: quantise-and-append of the workload's cache")
+    ap.add_argument("--gqa", type=int, default=0,
+                    help="query heads per KV head (overrides the workload's; 1-16; the break-even sweep)")
+    ap.add_argument("--group", type=int, default=0, help="group size g (overrides the workload's: 32, 64 or 128)")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="run one plain device copy of this many MiB before warm-up (counter calibration)")
     return ap.parse_args()
@@ -156,7 +159,7 @@ def _init_worker(barrier):
     _BARRIER[0] = barrier
 
 
-def cpu_baseline(spec, q, lens, target_s, max_workers=16):
+def cpu_baseline(spec, q, lens, target_s, max_workers=16, spec_kw=None):
     """The fp64 oracle (numpy, one BLAS thread per process) timed on the host
     cores: one worker process per core (at most the box's 16-CPU share of one
     GPU), the same workload's (sequence, KV head) slices dealt round-robin, all
@@ -182,7 +185,7 @@ def cpu_baseline(spec, q, lens, target_s, max_workers=16):
     barrier = ctx.Barrier(workers, timeout=600)
     chunks = [take[i::workers] for i in range(workers)]
     with ctx.Pool(workers, initializer=_init_worker, initargs=(barrier,)) as pool:
-        res = pool.map(_oracle_worker, [(spec.name, None, q, lens, c) for c in chunks], chunksize=1)
+        res = pool.map(_oracle_worker, [(spec.name, spec_kw, q, lens, c) for c in chunks], chunksize=1)
     t0 = min(r[0] for r in res)
     t1 = max(r[1] for r in res)
     done = sum(r[2] for r in res)
@@ -270,7 +273,12 @@ def main():
     import bit_quantized_kv_split_amd.staging as staging
     import synth
 
-    spec = synth.SPECS[args.workload]
+    spec_kw = {}
+    if args.gqa:
+        spec_kw["num_q_heads"] = args.gqa * synth.SPECS[args.workload].num_kv_heads
+    if args.group:
+        spec_kw["group"] = args.group
+    spec = synth.SPECS[args.workload].replace(**spec_kw)
     dev_name = "cuda:0"
     torch.cuda.set_device(0)
     if args.op == "quantize":
@@ -385,7 +393,8 @@ def main():
                    "splits": splits, "chunk": chunk, "cache_copies": n_copies, "window_tokens": args.window,
                    "algorithmic_bytes_per_step": alg},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                     "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic_per_launch(spec.name),
+                     "frac": round(achieved / PEAK_HBM_GBS, 4),
+                     "traffic": None if spec_kw else traffic_per_launch(spec.name),
                      "kernel": "split_decode (one launch per step)", "kernel_us_avg": round(k_avg * 1e3, 2),
                      "kernel_us_p10": round(pct(kernel_ms, 10) * 1e3, 2),
                      "kernel_us_p50": round(pct(kernel_ms, 50) * 1e3, 2),
@@ -407,7 +416,7 @@ def main():
                              "kernel_us_p90": round(pct(sus_ms, 90) * 1e3, 2),
                              "ratio_to_reported": round(sus_ms_step / ms_per_step, 4)}
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(spec, q, lens, args.cpu_seconds)
+        line["cpu_baseline"] = cpu_baseline(spec, q, lens, args.cpu_seconds, spec_kw=spec_kw or None)
     print(json.dumps(line), flush=True)
 
 
