@@ -1,6 +1,7 @@
 """Build libfoscar.so (HIP, gfx950) in-tree with hipcc.
 
-    python -m bit_quantized_kv_split_amd.build        # or build() from Python
+    python -m bit_quantized_kv_split_amd.build             # or build() from Python
+    python -m bit_quantized_kv_split_amd.build --timeline  # libfoscar_timeline.so (see timeline.py)
 
 Every source is compiled with packed fp32 arithmetic disabled
 (-Xclang -target-feature -Xclang -packed-fp32-ops) and without the compiler's
@@ -19,6 +20,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libfoscar.so")
+LIB_TIMELINE = os.path.join(HERE, "libfoscar_timeline.so")
 SOURCES = ["api.hip", "decode.hip", "decode_paged.hip", "decode_rot.hip", "decode_paged_rot.hip", "pack.hip",
            "quant.hip"]
 ARCH = os.environ.get("FOSCAR_ARCH", "gfx950")
@@ -36,13 +38,19 @@ def _hipcc():
     raise RuntimeError("hipcc not found")
 
 
-def build(verbose: bool = False) -> str:
+def build(verbose: bool = False, timeline: bool = False) -> str:
+    """Compile every source and link the library.  timeline: the same kernels
+    with the per-work-group timeline marks compiled in (-DFOSCAR_TIMELINE),
+    linked as libfoscar_timeline.so; the default library has none."""
     hipcc = _hipcc()
-    os.makedirs(BUILD, exist_ok=True)
+    bdir = BUILD + ("_timeline" if timeline else "")
+    lib = LIB_TIMELINE if timeline else LIB
+    extra = ["-DFOSCAR_TIMELINE"] if timeline else []
+    os.makedirs(bdir, exist_ok=True)
 
     def compile_one(src):
-        obj = os.path.join(BUILD, src + ".o")
-        cmd = [hipcc, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+        obj = os.path.join(bdir, src + ".o")
+        cmd = [hipcc, *FLAGS, *extra, "-c", os.path.join(CSRC, src), "-o", obj]
         r = subprocess.run(cmd, capture_output=True, text=True)
         if r.returncode != 0:
             raise RuntimeError(f"hipcc failed for {src}:\n{r.stderr}")
@@ -52,14 +60,14 @@ def build(verbose: bool = False) -> str:
 
     with ThreadPoolExecutor(len(SOURCES)) as ex:
         objs = list(ex.map(compile_one, SOURCES))
-    tmp = LIB + ".tmp"
+    tmp = lib + ".tmp"
     cmd = [hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, lib)
+    return lib
 
 
 if __name__ == "__main__":
-    print(build(verbose=True))
+    print(build(verbose=True, timeline="--timeline" in sys.argv[1:]))

@@ -83,6 +83,21 @@ hipError_t launch_decode(int bits, bool k_channel, bool v_channel, int group, in
   return fn(bits, k_channel, v_channel, group, batch, hkv, sa, stream, nullptr, ev);
 }
 
+#ifdef FOSCAR_TIMELINE
+// the timeline of the contiguous, unrotated instances (libfoscar_timeline.so only)
+extern "C" int foscar_timeline_clear(void* stream) {  // asynchronous on `stream`: no gap before the next launch
+  void* t = nullptr;
+  hipError_t e = hipGetSymbolAddress(&t, HIP_SYMBOL(g_timeline));
+  if (e == hipSuccess) e = hipMemsetAsync(t, 0, sizeof(g_timeline), (hipStream_t)stream);
+  return (int)e;
+}
+extern "C" int foscar_timeline_read(void* host, int wgs) {  // host: u64 [wgs][8][8], wgs <= 8192
+  if (wgs < 0 || wgs > kTimelineWgs) return -1;
+  return (int)hipMemcpyFromSymbol(host, HIP_SYMBOL(g_timeline), (size_t)wgs * kTimelineItems * 8 * 8, 0,
+                                  hipMemcpyDeviceToHost);
+}
+#endif
+
 hipError_t decode_occupancy(int bits, bool k_channel, bool v_channel, int group, bool paged, bool rot, int* per_cu) {
   SplitArgs sa{};
   const LaunchEvents none{};

@@ -20,6 +20,40 @@ typedef float f4 __attribute__((ext_vector_type(4)));
 
 constexpr float kLn2 = 0.69314718055994530942f;
 
+// Optional per-work-group timeline, compiled in only with -DFOSCAR_TIMELINE
+// (a separate library, libfoscar_timeline.so, built by `build --timeline`;
+// the default build compiles every mark to nothing).  Thread 0 of a
+// work-group records s_memrealtime (100 MHz) per work item: 0 item start,
+// 1 query prologue done, 2 tile loop done, 3 hand-off done, 4 item end; slot
+// 5 holds the item (b << 40 | pair << 20 | range), 6 is 1 for the work-group
+// that merged, 7 the hardware id (XCC id << 32 | HW_ID).
+#ifdef FOSCAR_TIMELINE
+constexpr int kTimelineWgs = 8192, kTimelineItems = 8;
+__device__ unsigned long long g_timeline[kTimelineWgs][kTimelineItems][8];
+__shared__ int s_timeline_item;  // the work-group's item number: an LDS read never waits for loads in flight
+__device__ __forceinline__ unsigned timeline_wg() { return blockIdx.x + gridDim.x * blockIdx.y; }
+__device__ __forceinline__ void timeline_item(int it) {
+  if (threadIdx.x == 0) s_timeline_item = it;
+}
+__device__ __forceinline__ void timeline_set(int k, unsigned long long v) {
+  const unsigned wg = timeline_wg();
+  if (threadIdx.x == 0 && wg < kTimelineWgs) {
+    const int it = s_timeline_item;
+    if (it >= 0 && it < kTimelineItems) g_timeline[wg][it][k] = v;
+  }
+}
+__device__ __forceinline__ void timeline_mark(int k) { timeline_set(k, __builtin_amdgcn_s_memrealtime()); }
+__device__ __forceinline__ void timeline_hw() {
+  timeline_set(7, (unsigned long long)__builtin_amdgcn_s_getreg((20 << 0) | (0 << 6) | (15 << 11)) << 32 |
+                      __builtin_amdgcn_s_getreg((4 << 0) | (0 << 6) | (31 << 11)));
+}
+#else
+__device__ __forceinline__ void timeline_item(int) {}
+__device__ __forceinline__ void timeline_set(int, unsigned long long) {}
+__device__ __forceinline__ void timeline_mark(int) {}
+__device__ __forceinline__ void timeline_hw() {}
+#endif
+
 __device__ __forceinline__ uint32_t and_or(uint32_t x, uint32_t m, uint32_t e) { return (x & m) | e; }
 __device__ __forceinline__ h4 cat4(uint32_t lo, uint32_t hi) {
   return __builtin_bit_cast(h4, (unsigned long long)lo | ((unsigned long long)hi << 32));
@@ -844,8 +878,10 @@ __device__ __forceinline__ void finish_range(const SplitArgs& a, const int b, co
   if (next && wave == 0) map_select<UNIT>(a, nx, next);  // while the count is in flight
   if (tid == 0) s_last = (done == ns - 1 + a.win_wgs);  // fused window work-groups arrive like ranges
   __syncthreads();
+  timeline_mark(3);
   if (!s_last) return;
   merge_ranges<ROT>(a, b, h, ns);
+  timeline_set(6, 1);
   if (tid == 0) a.counters[bh] = 0;  // ready for the next call on this workspace
 }
 
@@ -1627,6 +1663,7 @@ __device__ __forceinline__ void run_item(const SplitArgs& a, const int b, const 
 #pragma unroll
   for (int k = 0; k < NS; ++k) issue_first(k, k < nt);
   query_prologue();
+  timeline_mark(1);
   // Tiles start in increasing order and stop below T, so only the wave's last
   // tile can reach past T.  It is peeled off the loop: a loop body with one
   // instance of the tile code keeps its accumulators in the same registers
@@ -1654,6 +1691,7 @@ __device__ __forceinline__ void run_item(const SplitArgs& a, const int b, const 
     wait_vmcnt<0>();  // the loads on no bytes write the ring: done before it is reused
   }
 
+  timeline_mark(2);
   __builtin_amdgcn_s_setprio(3);  // the epilogue and the merge are the tail of the launch
   // persistent work-groups: the next item's index and lengths load during the epilogue
   NextLoad nx;
@@ -1891,7 +1929,12 @@ void split_decode(const SplitArgs a) {
       window_item<ROT>(a, b, pair % a.hkv, T, blockIdx.y);
       return;
     }
+    timeline_item(0);
+    timeline_mark(0);
+    timeline_hw();
+    timeline_set(5, (unsigned long long)b << 40 | (unsigned long long)pair << 20 | (blockIdx.y - a.win_wgs));
     run_item<BITS, KCH, VCH, GRP, PAGED, ROT>(a, b, pair % a.hkv, (int)blockIdx.y - a.win_wgs, T, nullptr);
+    timeline_mark(4);
     return;
   }
   // window work-groups take the first blocks (dispatched first) and leave
@@ -1912,6 +1955,7 @@ void split_decode(const SplitArgs a) {
     map_select<work_unit<KCH, VCH, GRP>()>(a, nx, s_item);
   }
   __syncthreads();
+  int item_no = 0;  // (the timeline's item number)
   for (;;) {
     const int kind = __builtin_amdgcn_readfirstlane(s_item[3]);
     const int b = __builtin_amdgcn_readfirstlane(s_item[0]);
@@ -1920,7 +1964,12 @@ void split_decode(const SplitArgs a) {
     const int T = __builtin_amdgcn_readfirstlane(s_item[4]);
     __syncthreads();  // s_item is read before wave 0 maps the item after this one into it
     if (kind == kItemNone) break;
+    timeline_item(item_no++);
+    timeline_mark(0);
+    timeline_hw();
+    timeline_set(5, (unsigned long long)b << 40 | (unsigned long long)(b * a.hkv + h) << 20 | (unsigned)split);
     run_item<BITS, KCH, VCH, GRP, PAGED, ROT>(a, b, h, split, T, s_item);
+    timeline_mark(4);
     __syncthreads();  // the item's LDS is free and s_item holds the next item
   }
   if (threadIdx.x == 0) {
