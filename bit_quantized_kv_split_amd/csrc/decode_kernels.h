@@ -1817,12 +1817,17 @@ __device__ __forceinline__ void window_item(const SplitArgs& a, const int b, con
     }
   }
   const uint4* wk = reinterpret_cast<const uint4*>(a.win_k + kv0);
-  for (int tb = t0; tb < t1; tb += 16) {  // wave-uniform: the matrix instructions run with every lane
-    const int t = tb + mr;
-    const uint4* kr = wk + (size_t)min(t, t1 - 1) * (D / 8) + mg;  // rows past t1 re-read row t1 - 1
-    uint4 kw[D / 32];
+  // key rows of block tb (rows past t1 re-read row t1 - 1); the next block's rows load while this
+  // block's scores are formed, so a wave keeps two blocks in flight instead of one
+  auto load_keys = [&](uint4 (&kw)[D / 32], int tb) {
+    const uint4* kr = wk + (size_t)min(tb + mr, t1 - 1) * (D / 8) + mg;
 #pragma unroll
     for (int k = 0; k < D / 32; ++k) kw[k] = kr[4 * k];
+  };
+  uint4 kw[D / 32], kn[D / 32] = {};
+  if (t0 < t1) load_keys(kw, t0);
+  for (int tb = t0; tb < t1; tb += 16) {  // wave-uniform: the matrix instructions run with every lane
+    if (tb + 16 < t1) load_keys(kn, tb + 16);
     f32x4 c = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int k = 0; k < D / 32; ++k)
@@ -1832,6 +1837,8 @@ __device__ __forceinline__ void window_item(const SplitArgs& a, const int b, con
       const int tr = tb + 4 * mg + r;
       if (mr < G && tr < t1) s_p[mr * CW + tr] = c[r] * a.win_sm;
     }
+#pragma unroll
+    for (int k = 0; k < D / 32; ++k) kw[k] = kn[k];
   }
   __syncthreads();
   float m[kMaxG], l[kMaxG];
@@ -1851,10 +1858,15 @@ __device__ __forceinline__ void window_item(const SplitArgs& a, const int b, con
   __syncthreads();
   const uint32_t* wv = reinterpret_cast<const uint32_t*>(a.win_v + kv0) + lane;
   float o[kMaxG][2] = {{0.f, 0.f}, {0.f, 0.f}, {0.f, 0.f}, {0.f, 0.f}};
-  for (int tb = t0; tb < t1; tb += 16) {
-    uint32_t vr[16];
+  // value rows of tokens tb .. tb + 15 (zeros past t1), one block ahead as for the keys
+  auto load_values = [&](uint32_t (&vr)[16], int tb) {
 #pragma unroll
     for (int u = 0; u < 16; ++u) vr[u] = (tb + u < t1) ? wv[(size_t)(tb + u) * (D / 2)] : 0u;
+  };
+  uint32_t vr[16], vn[16] = {};
+  if (t0 < t1) load_values(vr, t0);
+  for (int tb = t0; tb < t1; tb += 16) {
+    if (tb + 16 < t1) load_values(vn, tb + 16);
 #pragma unroll
     for (int u = 0; u < 16; ++u) {
       if (tb + u >= t1) break;
@@ -1866,6 +1878,8 @@ __device__ __forceinline__ void window_item(const SplitArgs& a, const int b, con
         o[i][1] = fmaf(p, v1, o[i][1]);
       }
     }
+#pragma unroll
+    for (int u = 0; u < 16; ++u) vr[u] = vn[u];
   }
 #pragma unroll
   for (int i = 0; i < kMaxG; ++i) {
