@@ -81,7 +81,9 @@ int check_decode_shape(const foscar_dims* d, int layout, int group) {
   // one grid row of work-groups per work pair; per-head byte offsets are 32-bit
   const int64_t pairs = (int64_t)d->batch * d->num_kv_heads * head_groups(d->num_q_heads / d->num_kv_heads);
   if (pairs > (1 << 22) || d->max_seq_len > (1 << 24)) return FOSCAR_EUNSUPPORTED;
-  if (d->max_seq_len % foscar::kTile != 0) return FOSCAR_EUNSUPPORTED;
+  // a multiple of 32: a wave's last tile may then reach 32 tokens past Tcap, where every load reads
+  // zero (each buffer resource ends at the KV head's last token) and the tokens are masked (t >= T)
+  if (d->max_seq_len % 32 != 0) return FOSCAR_EUNSUPPORTED;
   if ((layout & 3) != 0 && d->max_seq_len % group != 0) return FOSCAR_EUNSUPPORTED;
   return FOSCAR_OK;
 }
@@ -127,7 +129,7 @@ void plan(const foscar_dims* d, int layout, int group, int cus, int per_cu, int3
           int extra_per_pair = 0, int max_chunk = 0) {
   const int unit = unit_tokens(layout, group);
   const int tcap = d->max_seq_len;
-  const int units = tcap / unit;
+  const int units = (tcap + unit - 1) / unit;  // the last unit may reach past Tcap (by 32 tokens)
   if (units == 0) {
     *splits = 1;
     *chunk = unit;
@@ -405,7 +407,7 @@ int quantize_common(int bits, const foscar_dims* d, const void* k_src, const voi
   const int rot = layout >> 2;  // FOSCAR_K_ROTATED, FOSCAR_V_ROTATED: rotate those rows first
   layout &= 3;
   if (!valid_group(group)) return FOSCAR_EUNSUPPORTED;
-  if (d->max_seq_len % foscar::kTile != 0 || d->max_seq_len > (1 << 24)) return FOSCAR_EUNSUPPORTED;
+  if (d->max_seq_len % 32 != 0 || d->max_seq_len > (1 << 24)) return FOSCAR_EUNSUPPORTED;
   if (layout != 0 && d->max_seq_len % group != 0) return FOSCAR_EUNSUPPORTED;
   if (d->batch > 65535 || d->num_kv_heads > 65535) return FOSCAR_EUNSUPPORTED;  // grid z / y
   if (d->batch == 0 || src_tokens == 0) return FOSCAR_OK;

@@ -54,7 +54,7 @@ extern "C" {
 #define FOSCAR_EINVAL (-1)       /* null or misaligned pointer, negative size, bad layout/side/bits value,
                                     Hq % Hkv != 0 */
 #define FOSCAR_EUNSUPPORTED (-2) /* head_dim != 128, group not in {32,64,128}, Hq/Hkv > 16,
-                                    max_seq_len not a multiple of 64 (and of group for a
+                                    max_seq_len not a multiple of 32 (and of group for a
                                     channel-wise side), max_seq_len > 2^24,
                                     batch * num_kv_heads > 2^22 */
 #define FOSCAR_EHIP (-3)         /* a HIP call failed; foscar_last_hip_error() has its code */
@@ -101,7 +101,7 @@ typedef struct foscar_dims {
   int32_t num_q_heads;  /* Hq >= 1 */
   int32_t num_kv_heads; /* Hkv >= 1, Hq % Hkv == 0, G = Hq / Hkv <= 16 (see foscar_decode_int2) */
   int32_t head_dim;     /* D; must be 128 */
-  int32_t max_seq_len;  /* Tcap: tokens allocated per sequence; multiple of 64, and of
+  int32_t max_seq_len;  /* Tcap: tokens allocated per sequence; multiple of 32, and of
                            `group` when a side is channel-wise */
   float sm_scale;       /* softmax scale applied to q.k; <= 0 selects 1/sqrt(head_dim) */
 } foscar_dims;
@@ -278,7 +278,7 @@ int foscar_decode_paged_int4(const foscar_dims* dims, const void* q, const void*
  *               the written tokens' codes and their groups' (s, z) change:
  *               codes of other tokens in a shared value word are kept.
  * Only batch, num_kv_heads, head_dim and max_seq_len of dims are used
- * (head_dim 128; max_seq_len a multiple of 64, and of g for a channel-wise
+ * (head_dim 128; max_seq_len a multiple of 32, and of g for a channel-wise
  * side; batch and num_kv_heads at most 65535).
  * Asynchronous on `stream`; the caller keeps the buffers alive.  Calls that
  * write the same sequences must be ordered on one stream.

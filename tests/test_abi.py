@@ -62,7 +62,7 @@ def _decode(lib, dims, layout=0, group=128, ptr=1):
     (dict(num_q_heads=6, num_kv_heads=4), 0, 128, -1),
     (dict(num_q_heads=34, num_kv_heads=2), 0, 128, -2),     # 17 query heads per KV head
     (dict(batch=(1 << 20) + 1, num_q_heads=16, num_kv_heads=2), 0, 128, -2),  # over 2^22 work pairs (G = 8: two per KV head)
-    (dict(max_seq_len=1000), 0, 128, -2),                    # not a multiple of 64
+    (dict(max_seq_len=1000), 0, 128, -2),                    # not a multiple of 32
     (dict(max_seq_len=192), 2, 128, -2),                     # channel-wise group of 128 does not divide 192
     (dict(batch=-1), 0, 128, -1),
     (dict(), 16, 128, -1),                                   # bad layout bits (0-15: sides and rotation)
@@ -102,7 +102,8 @@ def test_split_plan_covers_the_cache(lib, monkeypatch):
     for kw, layout, g in [(dict(batch=4, num_q_heads=32, num_kv_heads=8, max_seq_len=131072), 0, 128),
                           (dict(batch=64, num_q_heads=32, num_kv_heads=8, max_seq_len=65536), 2, 32),
                           (dict(batch=8, num_q_heads=32, num_kv_heads=8, max_seq_len=32768), 3, 128),
-                          (dict(), 0, 128)]:
+                          (dict(max_seq_len=96), 0, 128), (dict(max_seq_len=160), 3, 32),
+                          (dict(max_seq_len=4128), 0, 64), (dict(), 0, 128)]:
         d = _dims(**kw)
         s, c = fos.foscar_split_plan(d, 2, layout, g)
         unit = g if (layout and g > 64) else 64
@@ -143,7 +144,7 @@ def _quantize(lib, dims, layout=0, group=128, src_tokens=16, ptr=1, bits=2):
 
 @pytest.mark.parametrize("kw,layout,group,src,code", [
     (dict(head_dim=64), 0, 128, 16, -2),
-    (dict(max_seq_len=1000), 0, 128, 16, -2),                 # not a multiple of 64
+    (dict(max_seq_len=1000), 0, 128, 16, -2),                 # not a multiple of 32
     (dict(max_seq_len=192), 1, 128, 16, -2),                  # channel-wise group of 128 does not divide 192
     (dict(batch=70000), 0, 128, 16, -2),                      # grid z
     (dict(), 16, 128, 16, -1),                                # bad layout bits (0-15: sides and rotation)

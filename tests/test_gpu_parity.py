@@ -81,6 +81,23 @@ def test_edge_lengths_and_poisoned_padding(bits, kl, vl, g):
     assert np.all(out[0] == 0) and np.all(np.isneginf(lse[0]))
 
 
+@pytest.mark.parametrize("bits", [2, 4])
+@pytest.mark.parametrize("kl,vl,g,tcap", [("token", "token", 128, 96), ("token", "channel", 32, 96),
+                                          ("channel", "channel", 32, 160), ("channel", "token", 32, 96),
+                                          ("token", "token", 64, 4128)])
+def test_capacity_a_multiple_of_32(bits, kl, vl, g, tcap):
+    """A cache capacity of 32 (mod 64) tokens: a wave's last tile reaches past
+    the allocation, where its loads read zero and its tokens are masked.
+    Lengths at the capacity, just under it, at tile and group boundaries and
+    0; 4128 tokens take two ranges, the second ending past the capacity."""
+    lens = (tcap, tcap - 1, tcap - 32, 65, 64, 33, 1, 0)
+    spec = synth.Spec(f"tcap{tcap}_{bits}_{kl}_{vl}_{g}", 13, bits, kl, vl, g, len(lens), 4, 1, 128, tcap, lens=lens)
+    dev, q, lens_np = stage_spec(spec, poison=True)
+    out, lse = run(spec, dev)
+    ro, rl = oracle_all(spec, q, lens_np, poison=True)
+    check(out, lse, ro, rl, spec.name)
+
+
 @pytest.mark.parametrize("G", [1, 2, 3, 4, 5, 6, 8, 12, 16])
 def test_gqa_ratios(G):
     """G query heads per KV head; above 4 the library serves a KV head as
@@ -165,10 +182,20 @@ def test_persistent_work_order_ragged_with_empty_sequences():
     """A batch whose plan needs more work-groups than one round runs the
     persistent, longest-first path: every row (including empty sequences and
     sequences of a few tokens) must match the oracle, on two calls in a row."""
-    import bit_quantized_kv_split_amd as fos
+    _check_persistent(persistent_spec(), "persistent ragged")
+
+
+def test_persistent_work_order_capacity_a_multiple_of_32():
+    """The persistent path over a 32800-token capacity (32 mod 64; value groups
+    of 32 tokens, which divide it), with one sequence that fills it: its last
+    range ends past the allocation."""
+    base = persistent_spec()
+    lens = (32800,) + tuple(base.lens[1:])
+    _check_persistent(base.replace(max_seq_len=32800, group=32, lens=lens), "persistent capacity 32800")
+
+
+def _check_persistent(spec, what):
     import oracle
-    import torch
-    spec = persistent_spec()
     assert_persistent(spec)
     dev, q, lens_np = stage_spec(spec, poison=True)
     G = spec.num_q_heads // spec.num_kv_heads
@@ -185,7 +212,7 @@ def test_persistent_work_order_ragged_with_empty_sequences():
             ro[b, h * G:(h + 1) * G], rl[b, h * G:(h + 1) * G] = o, l
     for k in range(2):
         out, lse = run(spec, dev)
-        check(out, lse, ro, rl, f"persistent ragged call {k}")
+        check(out, lse, ro, rl, f"{what} call {k}")
 
 
 @pytest.mark.parametrize("G", [1, 2, 3, 8, 16])

@@ -193,6 +193,34 @@ def test_quantize_then_decode(bits, kl, vl):
           f"quantise+decode int{bits} {kl}/{vl}")
 
 
+@pytest.mark.parametrize("bits,kl,vl,g", [(2, "token", "token", 32), (4, "token", "channel", 32),
+                                        (2, "channel", "channel", 32)])
+def test_capacity_a_multiple_of_32_write_then_decode(bits, kl, vl, g):
+    """A 96-token capacity (32 mod 64): the writer's 128-token block ends at
+    the capacity and the decode's last tile reaches past it."""
+    import torch
+    fos = _fos()
+    T, N, B, H, Hq = 96, 96, 2, 2, 8
+    case = synth.make_append_case(6, B, H, T, N, bits, [0, 0], [N, 61])
+    exp = _expected(case, bits, kl, vl, g, T)
+    d = _to_device(case, kl, vl, g, T)
+    _quantize(d, bits, kl, vl, g)
+    _compare(d, exp, "quantised cache, capacity 96")
+    lens = np.array([N, 61], np.int32)
+    rng = np.random.default_rng(7)
+    q = synth.bf16_round(rng.standard_normal((B, Hq, D)).astype(np.float32))
+    out, lse = fos.decode(torch.from_numpy(q).to(torch.bfloat16).cuda(), d["packed_k"], d["packed_v"], d["k_scale"],
+                          d["k_zero"], d["v_scale"], d["v_zero"], torch.from_numpy(lens).cuda(), bits=bits,
+                          k_layout=kl, v_layout=vl, group=g)
+    torch.cuda.synchronize()
+    w = {"q": q, "k_codes": oracle.unpack_k(exp["packed_k"], bits, D), "v_codes": oracle.unpack_v(exp["packed_v"], bits),
+         "k_scale": exp["k_scale"], "k_zero": exp["k_zero"], "v_scale": exp["v_scale"], "v_zero": exp["v_zero"],
+         "seq_lens": lens}
+    ro, rl = oracle.decode(w, k_layout=kl, v_layout=vl, group=g, sm_scale=1 / np.sqrt(D))
+    check(out.float().cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64), ro, rl,
+          f"capacity 96 int{bits} {kl}/{vl}")
+
+
 @pytest.mark.parametrize("rotate", ["k", "v", "kv"])
 @pytest.mark.parametrize("bits,kl,vl,g", [(2, "token", "token", 128), (4, "token", "channel", 32),
                                           (2, "channel", "token", 64), (4, "channel", "channel", 128)])
