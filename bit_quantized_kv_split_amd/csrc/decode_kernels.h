@@ -427,7 +427,10 @@ __device__ __forceinline__ float wave_max_same_query(float v) {
 }
 // reductions over a row of 16 lanes (the lanes of one query head in the
 // block-scaled score layout), with the DPP rotations fused into the operation
-__device__ __forceinline__ float row_max16(float v) {
+// max over the 16 lanes of a row (DPP row rotations), then with m, in one asm block (an fmaxf of
+// an asm result and a loop-carried value makes the compiler canonicalise both first: two more
+// instructions per tile)
+__device__ __forceinline__ float row_max16_and(float v, float m) {
   asm volatile(
       "s_nop 2\n\t"
       "v_max_f32_dpp %0, %0, %0 row_ror:8 row_mask:0xf bank_mask:0xf\n\t"
@@ -436,8 +439,10 @@ __device__ __forceinline__ float row_max16(float v) {
       "s_nop 1\n\t"
       "v_max_f32_dpp %0, %0, %0 row_ror:2 row_mask:0xf bank_mask:0xf\n\t"
       "s_nop 1\n\t"
-      "v_max_f32_dpp %0, %0, %0 row_ror:1 row_mask:0xf bank_mask:0xf"
-      : "+v"(v));
+      "v_max_f32_dpp %0, %0, %0 row_ror:1 row_mask:0xf bank_mask:0xf\n\t"
+      "v_max_f32 %0, %0, %1"
+      : "+v"(v)
+      : "v"(m));
   return v;
 }
 __device__ __forceinline__ float row_sum16(float v) {
@@ -1538,7 +1543,7 @@ __device__ __forceinline__ void run_item(const SplitArgs& a, const int b, const 
     // largest weight seen so far is exactly 1, so the operand-folded weight of
     // the dominant token (p * s) is its fp16 scale itself, with no rounding.
     const float mt = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
-    const float m_new = KCH ? wave_max_same_query_and(mt, m_ref) : fmaxf(m_ref, row_max16(mt));
+    const float m_new = KCH ? wave_max_same_query_and(mt, m_ref) : row_max16_and(mt, m_ref);
     if (__any(m_new > m_ref)) {
       const float alpha = __builtin_amdgcn_exp2f(m_ref - m_new);  // 0 on the first tile
       m_ref = m_new;

@@ -42,8 +42,10 @@ namespace {
 
 constexpr int kQBlock = 128;  // tokens per work-group
 
-__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
-__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+// bf16 -> fp32 as a conversion, not a bit cast: the compiler then knows the values are canonical
+// and takes their min / max without canonicalising each one first (same bits, same shift)
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return (float)__builtin_bit_cast(__bf16, (uint16_t)(w & 0xFFFFu)); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return (float)__builtin_bit_cast(__bf16, (uint16_t)(w >> 16)); }
 __device__ __forceinline__ uint16_t h_bits(_Float16 h) { return __builtin_bit_cast(uint16_t, h); }
 
 // bit offset of element e inside its packed word (even elements in the low
@@ -51,14 +53,26 @@ __device__ __forceinline__ uint16_t h_bits(_Float16 h) { return __builtin_bit_ca
 template <int BITS>
 __device__ __forceinline__ int elem_shift(int e) { return BITS * (e >> 1) + 16 * (e & 1); }
 
+// RN(x / L) for L = 2^BITS - 1 (3 or 15) and x >= 0: q = RN(x * c) with c = RN(1 / L), then one
+// correction with the exact remainder, r = fma(-q, L, x), q' = fma(r, c, q) (division by a constant
+// with a fused multiply-add, after Markstein).  Checked against the correctly rounded quotient for
+// every non-negative finite fp32 x, for both L; x = +inf keeps q (= inf), where r is NaN.
+template <int BITS>
+__device__ __forceinline__ float div_range(float x) {
+  constexpr float L = (float)((1 << BITS) - 1);
+  constexpr float c = 1.0f / L;
+  const float q = x * c;
+  const float q2 = __builtin_fmaf(__builtin_fmaf(-q, L, x), c, q);
+  return x == INFINITY ? q : q2;
+}
+
 template <int BITS>
 struct GroupQ {
   _Float16 s16, z16;
   float s, z;  // fp32 values of s16, z16
   GroupQ() = default;
   __device__ __forceinline__ GroupQ(float mn, float mx) {
-    constexpr float L = (float)((1 << BITS) - 1);
-    s16 = (_Float16)__fdiv_rn(mx - mn, L);  // fp32 quotient rounded once, then to fp16 (RNE)
+    s16 = (_Float16)div_range<BITS>(mx - mn);  // fp32 quotient rounded once, then to fp16 (RNE)
     z16 = (_Float16)mn;
     s = (float)s16;
     z = (float)z16;
