@@ -56,6 +56,11 @@ def parse():
     ap.add_argument("--dump-steps", action="store_true", help="print each step's kernel microseconds to stderr")
     ap.add_argument("--window", type=int, default=0,
                     help="decode with a bf16 window of this many recent tokens per sequence beside the cache")
+    ap.add_argument("--paged", type=int, default=0,
+                    help="decode over pools of blocks of this many tokens through a shuffled block table")
+    ap.add_argument("--rotate", default="", choices=["", "k", "v", "kv"],
+                    help="decode with the rotated-cache layout bits (the query rotated per step, the output "
+                         "taken back for a rotated value side); the same synthetic cache, for timing")
     ap.add_argument("--op", choices=["decode", "quantize"], default="decode",
                     help="decode: the decode step (default); quantize: quantise-and-append of the workload's cache")
     ap.add_argument("--gqa", type=int, default=0,
@@ -80,6 +85,25 @@ def kernel_sha():
         code = " ".join(text.split())
         h.update(name.encode() + b"\0" + code.encode())
     return h.hexdigest()[:16]
+
+
+def to_pool(c, spec, P, seed):
+    """The staged contiguous cache `c` as pools of P-token blocks (include/foscar.h: the
+    contiguous layouts with [num_blocks] for B and P for Tcap), logical block j of sequence b at
+    pool block perm[b * (Tcap / P) + j] for a seeded random permutation; returns (pools, block
+    table int32 [B, Tcap / P]).  Plumbing on the GPU: reshapes and one scatter per array."""
+    import torch
+    nb = spec.max_seq_len // P
+    perm = torch.randperm(spec.batch * nb, generator=torch.Generator().manual_seed(1000 + seed))
+    out = dict(c)
+    for name in ("packed_k", "packed_v", "k_scale", "k_zero", "v_scale", "v_zero"):
+        t = c[name]
+        B, H, R, W = t.shape  # R rows per sequence: tokens, value words or channel-wise group rows
+        x = t.reshape(B, H, nb, R // nb, W).permute(0, 2, 1, 3, 4).reshape(B * nb, H, R // nb, W)
+        pool = torch.empty_like(x)
+        pool[perm.to(x.device)] = x
+        out[name] = pool
+    return out, perm.reshape(spec.batch, nb).to(torch.int32).to(c["q"].device)
 
 
 def traffic_per_launch(workload):
@@ -295,6 +319,9 @@ def main():
     cache_bytes = sum(v.numel() * v.element_size() for v in base.values())
     n_copies = args.copies if args.copies > 0 else max(2, -(-(1 << 30) // cache_bytes))
     copies = [base] + [{k: v.clone() for k, v in base.items()} for _ in range(n_copies - 1)]
+    tables = [None] * len(copies)
+    if args.paged > 0:  # each copy regrouped on the GPU into a pool of blocks in a seeded random order
+        copies, tables = (list(x) for x in zip(*[to_pool(c, spec, args.paged, i) for i, c in enumerate(copies)]))
     torch.cuda.synchronize()
     stage_s = time.perf_counter() - t_stage
     layout = fos.layout_bits(spec.k_layout, spec.v_layout)
@@ -311,9 +338,11 @@ def main():
         window = [(torch.from_numpy(win["k"]).to(torch.bfloat16).to(dev_name),
                    torch.from_numpy(win["v"]).to(torch.bfloat16).to(dev_name),
                    torch.from_numpy(win["lens"]).to(dev_name)) for _ in copies]
+    call_layout = fos.layout_bits(spec.k_layout, spec.v_layout, args.rotate)
     calls = [fos.prepare_decode(spec.bits, c["q"], c["packed_k"], c["packed_v"], c["k_scale"], c["k_zero"],
-                                c["v_scale"], c["v_zero"], c["seq_lens"], layout, spec.group, out=o, lse=l, window=w)
-             for c, (o, l), w in zip(copies, outs, window)]
+                                c["v_scale"], c["v_zero"], c["seq_lens"], call_layout, spec.group, out=o, lse=l,
+                                window=w, paged=t)
+             for c, (o, l), w, t in zip(copies, outs, window, tables)]
 
     if args.calibrate_copy_mib > 0:  # a plain copy of known size, for HBM byte counters
         n = args.calibrate_copy_mib << 20
@@ -391,10 +420,12 @@ def main():
                    "global_batch": spec.batch, "seq_len": spec.max_seq_len, "bits": spec.bits,
                    "k_layout": spec.k_layout, "v_layout": spec.v_layout, "group": spec.group,
                    "splits": splits, "chunk": chunk, "cache_copies": n_copies, "window_tokens": args.window,
+                   "paged_block_tokens": args.paged, "rotated_sides": args.rotate,
                    "algorithmic_bytes_per_step": alg},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_HBM_GBS, 4),
-                     "traffic": None if spec_kw else traffic_per_launch(spec.name),
+                     "traffic": None if (spec_kw or args.paged or args.rotate or args.window)
+                     else traffic_per_launch(spec.name),
                      "kernel": "split_decode (one launch per step)", "kernel_us_avg": round(k_avg * 1e3, 2),
                      "kernel_us_p10": round(pct(kernel_ms, 10) * 1e3, 2),
                      "kernel_us_p50": round(pct(kernel_ms, 50) * 1e3, 2),

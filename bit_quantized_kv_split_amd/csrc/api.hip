@@ -259,8 +259,12 @@ int decode_common(int bits, const foscar_dims* d, const void* q, const void* pk,
   if (e != hipSuccess) return hip_fail(e);
   int32_t splits = 1, chunk = foscar::kTile;
   const int cus = compute_units(dev), per_cu = resident_per_cu(dev, bits, variant, group, paged);
-  // paged: a range of at most 63 blocks' tokens touches at most 64 blocks (one per lane), aligned or not
-  plan(d, layout, group, cus, per_cu, &splits, &chunk, 0, paged ? 63 * block_size : 0);
+  // paged: the kernel's lanes hold one block each.  A range of at most 63 blocks' tokens touches at
+  // most 64 blocks, aligned or not; when a block is the wave unit, every range starts on a block and
+  // 64 blocks' tokens touch 64 (at P = 64, 4096-token ranges: one round of work-groups for a long
+  // cache, where 4032-token ranges needed a second, nearly empty round)
+  const int paged_blocks = block_size == unit_tokens(layout, group) ? 64 : 63;
+  plan(d, layout, group, cus, per_cu, &splits, &chunk, 0, paged ? paged_blocks * block_size : 0);
   // the window is attended inside the decode launch by win_wgs more work-groups per pair: 1, 2, 4
   // or 8, with chunks of at most 4096 / 8 = 512 = kFusedWindowMax tokens.  A one-round grid has few
   // pairs: its window work-groups take chunks of at most 128 tokens where 8 allow it, beside the

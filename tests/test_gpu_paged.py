@@ -66,6 +66,19 @@ def test_paged_ranges_through_the_merge(splits, monkeypatch):
     check(out, lse, ro, rl, f"paged splits={splits}")
 
 
+@pytest.mark.parametrize("splits", [1, 2, None])
+@pytest.mark.parametrize("bits", [2, 4])
+def test_paged_block_of_one_unit_takes_64_blocks_per_range(bits, splits, monkeypatch):
+    """Blocks of 64 tokens (the wave unit): every range starts on a block, so a
+    range may hold 64 blocks (one per lane of the table row).  One range asked
+    for over 8192 tokens gets two of 64 blocks; lengths at the range boundary,
+    one block short of it and one token past it."""
+    spec = synth.Spec(f"paged_unit_{bits}", 26, bits, "token", "token", 128, 4, 4, 1, 128, 8192,
+                      lens=(8192, 4096, 4032, 4097))
+    out, lse, ro, rl = _run_paged(spec, 64, splits=splits, monkeypatch=monkeypatch)
+    check(out, lse, ro, rl, f"paged P=64 splits={splits}")
+
+
 def test_paged_gqa_and_persistent_order():
     """16 query heads per KV head (four groups reading each block) on a ragged
     batch large enough for the persistent work order."""
