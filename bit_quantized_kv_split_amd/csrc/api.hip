@@ -293,8 +293,7 @@ int decode_common(int bits, const foscar_dims* d, const void* q, const void* pk,
 
   const float sm = d->sm_scale > 0.f ? d->sm_scale : 1.0f / sqrtf((float)d->head_dim);
   foscar::SplitArgs sa;
-  sa.win_q = (const uint16_t*)q;
-  sa.q = (rot & 1) ? (const uint16_t*)out : sa.win_q;  // rotated keys: q H is written to `out` first
+  sa.q = (const uint16_t*)q;  // rotated keys: each work-group rotates its query rows (q H) itself
   sa.pk = (const uint32_t*)pk;
   sa.pv = (const uint32_t*)pv;
   sa.ks = (const uint16_t*)ks;
@@ -345,16 +344,8 @@ int decode_common(int bits, const foscar_dims* d, const void* q, const void* pk,
     sa.win_cap = win_cap;
   }
 
-  foscar::LaunchEvents ev_main = ev;
-  if (rot & 1) {  // the query rotated once per step, into `out` (the decode reads it there before any
-                  // work-group of its work pair writes that row's output)
-    e = foscar::launch_rotate_query(d->batch * d->num_q_heads, sa.win_q, (uint16_t*)out, (hipStream_t)stream,
-                                    ev.start);
-    if (e != hipSuccess) return hip_fail(e);
-    ev_main.start = nullptr;
-  }
   e = foscar::launch_decode(bits, (layout & FOSCAR_K_CHANNEL) != 0, (layout & FOSCAR_V_CHANNEL) != 0, group,
-                            d->batch, d->num_kv_heads, sa, (hipStream_t)stream, ev_main);
+                            d->batch, d->num_kv_heads, sa, (hipStream_t)stream, ev);
   if (e != hipSuccess) return hip_fail(e);
   return FOSCAR_OK;
 }

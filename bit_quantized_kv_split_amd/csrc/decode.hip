@@ -40,34 +40,12 @@
 //   * a full-precision window of recent tokens is attended by extra work-groups
 //     of the same launch (window_item) whose partials join that merge.
 // The kernel templates are in decode_kernels.h.  This file instantiates the
-// contiguous, unrotated variant, holds the rotated-query kernel of a rotated
-// cache, and dispatches a call to one of the four variants (contiguous or
-// paged, unrotated or rotated), each instantiated in a source file of its own.
+// contiguous, unrotated variant and dispatches a call to one of the four
+// variants (contiguous or paged, unrotated or rotated), each instantiated in a
+// source file of its own.
 #include "decode_kernels.h"
 
 namespace foscar {
-namespace {
-
-// One wave per query row: lane l rotates channels 2l, 2l + 1 (row r of dst = bf16(q_r H)).
-__global__ __launch_bounds__(kWaves * 64) void rotate_query(const uint16_t* q, uint16_t* dst, int rows) {
-  const int lane = threadIdx.x & 63;
-  const int row = blockIdx.x * kWaves + (threadIdx.x >> 6);
-  if (row >= rows) return;  // whole waves
-  const uint32_t w = reinterpret_cast<const uint32_t*>(q + (size_t)row * kHeadDim)[lane];
-  reinterpret_cast<uint32_t*>(dst + (size_t)row * kHeadDim)[lane] = hadamard_bf16_pair(w, lane);
-}
-
-}  // namespace
-
-hipError_t launch_rotate_query(int rows, const uint16_t* q, uint16_t* dst, hipStream_t stream, hipEvent_t start) {
-  if (rows <= 0) return hipSuccess;
-  const dim3 grid((rows + kWaves - 1) / kWaves);
-  if (start)
-    hipExtLaunchKernelGGL(rotate_query, grid, dim3(kWaves * 64), 0, stream, start, nullptr, 0, q, dst, rows);
-  else
-    hipLaunchKernelGGL(rotate_query, grid, dim3(kWaves * 64), 0, stream, q, dst, rows);
-  return hipGetLastError();
-}
 
 // the contiguous cache without rotation: instantiated here
 hipError_t launch_split_plain(int bits, bool kch, bool vch, int group, int batch, int hkv, const SplitArgs& sa,

@@ -980,7 +980,17 @@ __device__ __forceinline__ void run_item(const SplitArgs& a, const int b, const 
   // issue order, so query loads behind a tile's would wait for the whole tile
   uint32_t qw[KCH ? 1 : 16];  // token-wise keys: the lane's 32 query values (MxKey::local order)
   uint32_t qgw[KCH ? 1 : 4];  // token-wise keys: head rh's channels 8 rq .. 8 rq + 7
+  // rotated keys (ROT instances, rot bit 0): the query rows meet the keys as bf16(q H).  Wave w
+  // loads row w (lane l: channels 2l, 2l + 1; channel-wise keys load it so anyway) and rotates it
+  // once the first tiles are in flight; token-wise keys then take their operand words from the
+  // rotated rows in LDS as they would from q.
+  uint32_t qrow = 0u;
   auto query_load = [&]() {
+   if (!KCH && ROT && (a.rot & 1)) {
+    qrow = (wave < a.g_heads)
+        ? reinterpret_cast<const uint32_t*>(a.q + ((size_t)b * a.hq + h * a.g_heads + wave) * D)[lane] : 0u;
+    return;
+   }
    if constexpr (KCH) {
     qw[0] = (wave < a.g_heads)
         ? reinterpret_cast<const uint32_t*>(a.q + ((size_t)b * a.hq + h * a.g_heads + wave) * D)[lane] : 0u;
@@ -1000,6 +1010,32 @@ __device__ __forceinline__ void run_item(const SplitArgs& a, const int b, const 
         a.q + ((size_t)b * a.hq + (size_t)h * a.g_heads + (rh < a.g_heads ? rh : 0)) * D);
 #pragma unroll
     for (int i = 0; i < 4; ++i) qgw[i] = qg[4 * rq + i];
+   }
+  };
+  auto query_rotate = [&]() {  // (the query loads' wait falls after the first tiles' issue)
+   if constexpr (ROT) {
+    if (a.rot & 1) {
+     if constexpr (KCH) {
+      qw[0] = hadamard_bf16_pair(qw[0], lane);
+     } else {
+      __shared__ __align__(16) uint32_t s_qrot[kWaves][64];
+      s_qrot[wave][lane] = hadamard_bf16_pair(qrow, lane);  // rows past G: zeros, never read
+      __syncthreads();
+      const int hq = (lane & 15) >> 2, Gq = lane >> 4;
+      const uint4* qr = reinterpret_cast<const uint4*>(&s_qrot[hq < a.g_heads ? hq : 0][0]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint4 u = qr[MK::quad_index(Gq, i)];
+        qw[4 * i] = u.x;
+        qw[4 * i + 1] = u.y;
+        qw[4 * i + 2] = u.z;
+        qw[4 * i + 3] = u.w;
+      }
+      const uint32_t* qg = &s_qrot[rh < a.g_heads ? rh : 0][0];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) qgw[i] = qg[4 * rq + i];
+     }
+    }
    }
   };
   auto query_prologue = [&]() {  // run after the first tiles are in flight, so the two HBM latencies overlap
@@ -1667,6 +1703,7 @@ __device__ __forceinline__ void run_item(const SplitArgs& a, const int b, const 
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int k = 0; k < NS; ++k) issue_first(k, k < nt);
+  query_rotate();
   query_prologue();
   timeline_mark(1);
   // Tiles start in increasing order and stop below T, so only the wave's last
@@ -1809,7 +1846,7 @@ __device__ __forceinline__ void window_item(const SplitArgs& a, const int b, con
   const int mr = lane & 15, mg = lane >> 4;
   bf16x8 qb[D / 32];
   {
-    const uint32_t* qr = reinterpret_cast<const uint32_t*>((ROT ? a.win_q : a.q) + (row0 + (size_t)min(mr, G - 1)) * D);
+    const uint32_t* qr = reinterpret_cast<const uint32_t*>(a.q + (row0 + (size_t)min(mr, G - 1)) * D);
 #pragma unroll
     for (int k = 0; k < D / 32; ++k) {
       uint4 w;  // 4-byte loads: the query is only 4-byte aligned

@@ -17,7 +17,7 @@ constexpr int kMaxSplits = 512;  // ranges per sequence (bounds the workspace an
 // Arguments of the decode kernel (one work-group per (range, KV head, sequence)).
 // The last work-group to finish the ranges of a (sequence, KV head) merges them.
 struct SplitArgs {
-  const uint16_t* q;         // bf16 [B][Hq][D] the query the cache ranges meet (rotated keys: q H, in `out`)
+  const uint16_t* q;         // bf16 [B][Hq][D] the caller's query (rotated keys: each work-group rotates its rows)
   const uint32_t* pk;        // [B][Hkv][Tcap][D*bits/32]
   const uint32_t* pv;        // [B][Hkv][Tcap*bits/32][D]
   const uint16_t* ks;        // fp16 key scales   (token-wise [B][Hkv][Tcap][D/g], channel-wise [B][Hkv][Tcap/g][D])
@@ -40,9 +40,10 @@ struct SplitArgs {
   int32_t persistent;        // 1: grid_wgs work-groups take work items from work_ctr (see split_decode)
   int32_t grid_wgs;          // persistent grid size (one round of resident work-groups)
   int32_t batch;             // B
-  // rotated cache, bit 1: the cache values are rows of V H; the cache's weighted value sum is taken
-  // back by H before the window's terms join it (H: orthonormal Sylvester-Hadamard of order 128).
-  // (Rotated keys change only q.)
+  // rotated cache (H: orthonormal Sylvester-Hadamard of order 128), bit 0: the cache keys are rows
+  // of K H, and each work-group meets them with its query rows rotated (bf16(q H)); bit 1: the
+  // cache values are rows of V H, and the cache's weighted value sum is taken back by H before the
+  // window's terms join it.
   int32_t rot;
   int32_t* work_ctr;         // [2] items taken, work-groups left; zero between calls
   // paged cache (block_table != null): pk .. vz are pools of num_blocks blocks of block_size
@@ -64,7 +65,6 @@ struct SplitArgs {
   const int32_t* win_lens;   // [B]
   int32_t win_cap;
   float win_sm;              // softmax scale (natural units)
-  const uint16_t* win_q;     // bf16 [B][Hq][D] the query the window meets (the caller's q)
 };
 constexpr int kMaxWindowWgs = 8;      // window work-groups per pair inside the decode launch
 constexpr int kFusedWindowMax = 512;  // window tokens of one work-group inside the decode launch
@@ -92,9 +92,6 @@ hipError_t launch_split_rot(int bits, bool kch, bool vch, int group, int batch, 
                             hipStream_t stream, int* per_cu, const LaunchEvents& ev);
 hipError_t launch_split_paged_rot(int bits, bool kch, bool vch, int group, int batch, int hkv, const SplitArgs& sa,
                                   hipStream_t stream, int* per_cu, const LaunchEvents& ev);
-// dst[r] = bf16(q[r] H) for rows r < rows of 128 bf16 values (rotated keys); `start` (may be null)
-// is recorded by the dispatch before the kernel
-hipError_t launch_rotate_query(int rows, const uint16_t* q, uint16_t* dst, hipStream_t stream, hipEvent_t start);
 // Quantise tokens [start_b, start_b + count_b) of new keys / values into the cache (quant.hip);
 // rot bit 0 / bit 1: rotate the key / value rows by the orthonormal Hadamard matrix first.
 hipError_t launch_quantize(int bits, bool k_channel, bool v_channel, int group, int rot, int batch, int hkv, int tcap,

@@ -75,12 +75,10 @@ extern "C" {
  * cache): the cache holds the quantised rows of K H and/or V H, H the
  * orthonormal Sylvester-Hadamard matrix of order 128 (entry (i, j) =
  * (-1)^popcount(i & j) / sqrt(128); symmetric, H H = I).
- *   FOSCAR_K_ROTATED: the keys are rotated; each step rotates the query once
- *     (q H, rounded once to bf16 from an fp64 transform whose sums are exact)
- *     before it meets them, so the scores are those of q against K.  A small
- *     kernel ahead of the decode writes the rotated rows into `out`, where the
- *     decode reads them before it writes the output over them: `out` must not
- *     overlap `q`.
+ *   FOSCAR_K_ROTATED: the keys are rotated; each work-group rotates the query
+ *     rows it attends with (q H, rounded once to bf16 from an fp64 transform
+ *     whose sums are exact) before they meet the keys, so the scores are those
+ *     of q against K.
  *   FOSCAR_V_ROTATED: the values are rotated; the cache's weighted value sum is
  *     taken back by H (fp32) before the final division, so `out` is in the
  *     model's basis.
