@@ -13,7 +13,8 @@ Infinity Cache.
 Prints one JSON line: metric/value (achieved HBM GB/s of algorithmic bytes per
 step), ms_per_step, a roofline object for the decode kernel (HIP events on
 the launch stream; rocprofv3 summaries of the same command are committed
-under profiles/), and the CPU oracle timed on a bounded sample.
+under profiles/), the CPU oracle timed on a bounded sample, and (default run)
+"int4": the paper-shaped INT4 step, timed the same way by a child run.
 """
 import argparse
 import hashlib
@@ -21,6 +22,7 @@ import json
 import math
 import os
 import re
+import subprocess
 import sys
 import time
 
@@ -56,6 +58,8 @@ def parse():
     ap.add_argument("--dump-steps", action="store_true", help="print each step's kernel microseconds to stderr")
     ap.add_argument("--window", type=int, default=0,
                     help="decode with a bf16 window of this many recent tokens per sequence beside the cache")
+    ap.add_argument("--no-int4", action="store_true",
+                    help="skip the INT4 companion (the paper-shaped INT4 step) of the default run")
     ap.add_argument("--paged", type=int, default=0,
                     help="decode over pools of blocks of this many tokens through a shuffled block table")
     ap.add_argument("--rotate", default="", choices=["", "k", "v", "kv"],
@@ -85,6 +89,26 @@ def kernel_sha():
         code = " ".join(text.split())
         h.update(name.encode() + b"\0" + code.encode())
     return h.hexdigest()[:16]
+
+
+def int4_companion():
+    """The paper-shaped INT4 step (c2_paper_int4: 16 sequences x 8192 tokens, 32 / 8 heads, INT4
+    token-wise, g = 128), timed by a child run of this script; a summary of its JSON line."""
+    cmd = [sys.executable, os.path.abspath(__file__), "--workload", "c2_paper_int4", "--steps", "50", "--warmup",
+           "10", "--sustain", "1000", "--no-cpu-baseline", "--no-int4"]
+    try:
+        r = subprocess.run(cmd, capture_output=True, text=True, timeout=600)
+        d = json.loads([x for x in r.stdout.splitlines() if x.startswith("{")][-1])
+    except (subprocess.SubprocessError, IndexError, ValueError) as e:
+        return {"workload": "c2_paper_int4", "error": f"{type(e).__name__}: {e}"}
+    ro, su = d["roofline"], d.get("sustained", {})
+    return {"workload": d["config"]["workload"], "value": d["value"], "unit": d["unit"],
+            "us_per_step": d["us_per_step"], "pct_of_peak_hbm": d["pct_of_peak_hbm"],
+            "kernel_us_avg": ro["kernel_us_avg"], "kernel_us_p50": ro["kernel_us_p50"], "frac": ro["frac"],
+            "sustained_us_per_step": round(su["ms_per_step"] * 1e3, 2) if su else None,
+            "sustained_kernel_us_avg": su.get("kernel_us_avg"), "cache": d["cache"],
+            "algorithmic_bytes_per_step": d["config"]["algorithmic_bytes_per_step"],
+            "kernel_source_sha": d["kernel_source_sha"]}
 
 
 def to_pool(c, spec, P, seed):
@@ -290,6 +314,12 @@ def main():
         print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for --gpus {args.gpus}).",
               file=sys.stderr)
         sys.exit(2)
+    # the metric names INT2 and INT4: the default run also times the paper-shaped INT4 step, in a
+    # child process started before this one touches the GPU, and reports it beside its own line
+    int4 = None
+    if (args.op == "decode" and args.workload == "c3_long_int2" and not args.no_int4 and not args.window
+            and not args.paged and not args.rotate and not args.gqa and not args.group and not args.copies):
+        int4 = int4_companion()
     import numpy as np
     import torch
 
@@ -446,6 +476,8 @@ def main():
                              "kernel_us_p50": round(pct(sus_ms, 50) * 1e3, 2),
                              "kernel_us_p90": round(pct(sus_ms, 90) * 1e3, 2),
                              "ratio_to_reported": round(sus_ms_step / ms_per_step, 4)}
+    if int4 is not None:
+        line["int4"] = int4
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(spec, q, lens, args.cpu_seconds, spec_kw=spec_kw or None)
     print(json.dumps(line), flush=True)
