@@ -70,6 +70,9 @@ def parse():
     ap.add_argument("--gqa", type=int, default=0,
                     help="query heads per KV head (overrides the workload's; 1-16; the break-even sweep)")
     ap.add_argument("--group", type=int, default=0, help="group size g (overrides the workload's: 32, 64 or 128)")
+    ap.add_argument("--head-dim", type=int, default=0,
+                    help="head dimension (overrides the workload's 128: a multiple of 32 up to 256, the "
+                         "head-dim-generic kernels)")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="run one plain device copy of this many MiB before warm-up (counter calibration)")
     return ap.parse_args()
@@ -318,7 +321,8 @@ def main():
     # child process started before this one touches the GPU, and reports it beside its own line
     int4 = None
     if (args.op == "decode" and args.workload == "c3_long_int2" and not args.no_int4 and not args.window
-            and not args.paged and not args.rotate and not args.gqa and not args.group and not args.copies):
+            and not args.paged and not args.rotate and not args.gqa and not args.group and not args.copies
+            and not args.head_dim):
         int4 = int4_companion()
     import numpy as np
     import torch
@@ -332,7 +336,13 @@ def main():
         spec_kw["num_q_heads"] = args.gqa * synth.SPECS[args.workload].num_kv_heads
     if args.group:
         spec_kw["group"] = args.group
+    if args.head_dim:
+        spec_kw["head_dim"] = args.head_dim
     spec = synth.SPECS[args.workload].replace(**spec_kw)
+    if synth.TOKEN in (spec.k_layout, spec.v_layout) and spec.head_dim % spec.group:
+        print(f"bench.py: a token-wise group of {spec.group} channels does not divide head_dim {spec.head_dim}; "
+              "pass --group", file=sys.stderr)
+        sys.exit(2)
     dev_name = "cuda:0"
     torch.cuda.set_device(0)
     if args.op == "quantize":
@@ -456,7 +466,9 @@ def main():
                      "frac": round(achieved / PEAK_HBM_GBS, 4),
                      "traffic": None if (spec_kw or args.paged or args.rotate or args.window)
                      else traffic_per_launch(spec.name),
-                     "kernel": "split_decode (one launch per step)", "kernel_us_avg": round(k_avg * 1e3, 2),
+                     "kernel": ("split_decode (one launch per step)" if spec.head_dim == 128 else
+                                "gd_split + gd_merge (the head-dim-generic pair of launches per step)"),
+                     "kernel_us_avg": round(k_avg * 1e3, 2),
                      "kernel_us_p10": round(pct(kernel_ms, 10) * 1e3, 2),
                      "kernel_us_p50": round(pct(kernel_ms, 50) * 1e3, 2),
                      "kernel_us_p90": round(pct(kernel_ms, 90) * 1e3, 2),

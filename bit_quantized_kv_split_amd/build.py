@@ -21,8 +21,8 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libfoscar.so")
 LIB_TIMELINE = os.path.join(HERE, "libfoscar_timeline.so")
-SOURCES = ["api.hip", "decode.hip", "decode_paged.hip", "decode_rot.hip", "decode_paged_rot.hip", "pack.hip",
-           "quant.hip"]
+SOURCES = ["api.hip", "decode.hip", "decode_paged.hip", "decode_rot.hip", "decode_paged_rot.hip", "decode_generic.hip",
+           "pack.hip", "quant.hip"]
 ARCH = os.environ.get("FOSCAR_ARCH", "gfx950")
 
 FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",

@@ -49,7 +49,9 @@ int check_dims(const foscar_dims* d, bool need_heads_ratio) {
   if (!d) return FOSCAR_EINVAL;
   if (d->batch < 0 || d->num_q_heads < 1 || d->num_kv_heads < 1 || d->head_dim < 1 || d->max_seq_len < 0)
     return FOSCAR_EINVAL;
-  if (d->head_dim != foscar::kHeadDim) return FOSCAR_EUNSUPPORTED;
+  // 128 on every entry point; other multiples of 32 up to kGdMaxD: plain decode, pack and sizes
+  if (d->head_dim != foscar::kHeadDim && (d->head_dim % 32 != 0 || d->head_dim > foscar::kGdMaxD))
+    return FOSCAR_EUNSUPPORTED;
   if (need_heads_ratio) {
     if (d->num_q_heads % d->num_kv_heads != 0) return FOSCAR_EINVAL;
     if (d->num_q_heads / d->num_kv_heads > foscar::kMaxGqa) return FOSCAR_EUNSUPPORTED;
@@ -85,6 +87,10 @@ int check_decode_shape(const foscar_dims* d, int layout, int group) {
   // zero (each buffer resource ends at the KV head's last token) and the tokens are masked (t >= T)
   if (d->max_seq_len % 32 != 0) return FOSCAR_EUNSUPPORTED;
   if ((layout & 3) != 0 && d->max_seq_len % group != 0) return FOSCAR_EUNSUPPORTED;
+  // a token-wise side groups g channels of a token
+  if ((layout & 3) != (FOSCAR_K_CHANNEL | FOSCAR_V_CHANNEL) && d->head_dim % group != 0) return FOSCAR_EUNSUPPORTED;
+  // rotated caches need head_dim 128 (Hadamard order of the kernels)
+  if ((layout >> 2) != 0 && d->head_dim != foscar::kHeadDim) return FOSCAR_EUNSUPPORTED;
   return FOSCAR_OK;
 }
 
@@ -104,18 +110,19 @@ int compute_units(int device) {
 // Work-groups of the (bits, layout, group) kernel one CU of `device` holds at
 // once (cached; 4 when the runtime cannot say, e.g. without a GPU).  `layout`
 // may carry the rotation bits, which select the rotated variant.
-int resident_per_cu(int device, int bits, int layout, int group, bool paged = false) {
-  const long long key = ((((long long)device * 8 + bits) * 16 + layout) * 256 + group) * 2 + (paged ? 1 : 0);
+int resident_per_cu(int device, int bits, int layout, int group, bool paged = false, bool generic = false) {
+  const long long key =
+      (((((long long)device * 8 + bits) * 16 + layout) * 256 + group) * 2 + (paged ? 1 : 0)) * 2 + (generic ? 1 : 0);
   {
     std::lock_guard<std::mutex> lk(g_ws_mutex);
     auto it = g_occ.find(key);
     if (it != g_occ.end()) return it->second;
   }
   int n = 0;
-  if (foscar::decode_occupancy(bits, (layout & FOSCAR_K_CHANNEL) != 0, (layout & FOSCAR_V_CHANNEL) != 0, group, paged,
-                               (layout >> 2) != 0, &n) != hipSuccess ||
-      n <= 0)
-    return 4;
+  const bool kch = (layout & FOSCAR_K_CHANNEL) != 0, vch = (layout & FOSCAR_V_CHANNEL) != 0;
+  const hipError_t e = generic ? foscar::generic_occupancy(bits, kch, vch, &n)
+                               : foscar::decode_occupancy(bits, kch, vch, group, paged, (layout >> 2) != 0, &n);
+  if (e != hipSuccess || n <= 0) return 4;
   std::lock_guard<std::mutex> lk(g_ws_mutex);
   g_occ[key] = n;
   return n;
@@ -169,7 +176,7 @@ size_t counter_bytes(const foscar_dims* d) {  // B*Hkv range counters, then the 
 }
 size_t partial_bytes(const foscar_dims* d, int32_t splits) {  // range partials, then the window partials of each row
   const size_t rows = (size_t)d->batch * d->num_q_heads * (splits + foscar::kMaxWindowWgs);
-  return rows * (foscar::kHeadDim + 1) * sizeof(float);
+  return rows * (d->head_dim + 1) * sizeof(float);
 }
 
 // Grow-only workspace of (current device, stream).  Growing frees the old
@@ -234,6 +241,8 @@ int decode_common(int bits, const foscar_dims* d, const void* q, const void* pk,
   g_next_events = foscar::LaunchEvents{};
   int rc = check_decode_shape(d, layout, group);
   if (rc) return rc;
+  const bool generic = d->head_dim != foscar::kHeadDim;  // the head-dim-generic kernels: plain caches only
+  if (generic && (windowed || block_table)) return FOSCAR_EUNSUPPORTED;
   const int rot = (layout >> 2) & 3;  // FOSCAR_K_ROTATED, FOSCAR_V_ROTATED
   const int variant = layout;         // the kernel variant (group sides and rotation)
   layout &= 3;                        // the group sides
@@ -250,6 +259,7 @@ int decode_common(int bits, const foscar_dims* d, const void* q, const void* pk,
     return FOSCAR_EINVAL;
   if (windowed && (!aligned(win_k, 16) || !aligned(win_v, 16) || !aligned(win_lens, 4))) return FOSCAR_EINVAL;
   const bool paged = block_table != nullptr;
+  const int hkv = d->num_kv_heads;
 
   const int kv_group = head_groups(d->num_q_heads / d->num_kv_heads);
   const foscar_dims wd = work_dims(d);
@@ -258,7 +268,7 @@ int decode_common(int bits, const foscar_dims* d, const void* q, const void* pk,
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return hip_fail(e);
   int32_t splits = 1, chunk = foscar::kTile;
-  const int cus = compute_units(dev), per_cu = resident_per_cu(dev, bits, variant, group, paged);
+  const int cus = compute_units(dev), per_cu = resident_per_cu(dev, bits, variant, group, paged, generic);
   // paged: the kernel's lanes hold one block each.  A range of at most 63 blocks' tokens touches at
   // most 64 blocks, aligned or not; when a block is the wave unit, every range starts on a block and
   // 64 blocks' tokens touch 64 (at P = 64, 4096-token ranges: one round of work-groups for a long
@@ -292,6 +302,36 @@ int decode_common(int bits, const foscar_dims* d, const void* q, const void* pk,
   }
 
   const float sm = d->sm_scale > 0.f ? d->sm_scale : 1.0f / sqrtf((float)d->head_dim);
+  if (generic) {
+    foscar::GenericArgs ga;
+    ga.q = (const uint16_t*)q;
+    ga.pk = (const uint32_t*)pk;
+    ga.pv = (const uint32_t*)pv;
+    ga.ks = (const uint16_t*)ks;
+    ga.kz = (const uint16_t*)kz;
+    ga.vs = (const uint16_t*)vs;
+    ga.vz = (const uint16_t*)vz;
+    ga.seq_lens = seq_lens;
+    ga.out = (uint16_t*)out;
+    ga.lse = lse;
+    ga.o_part = partials;
+    ga.lse_part = partials + (size_t)d->batch * d->num_q_heads * splits * d->head_dim;
+    ga.batch = d->batch;
+    ga.hq = d->num_q_heads;
+    ga.hkv = hkv;
+    ga.pairs = d->num_kv_heads;  // work pairs per sequence
+    ga.kv_group = kv_group;
+    ga.g_heads = d->num_q_heads / d->num_kv_heads;
+    ga.d = d->head_dim;
+    ga.tcap = d->max_seq_len;
+    ga.group = group;
+    ga.splits = splits;
+    ga.chunk = chunk;
+    ga.sm_log2 = sm * 1.4426950408889634f;
+    e = foscar::launch_decode_generic(bits, (layout & FOSCAR_K_CHANNEL) != 0, (layout & FOSCAR_V_CHANNEL) != 0, ga,
+                                      (hipStream_t)stream, ev);
+    return e == hipSuccess ? FOSCAR_OK : hip_fail(e);
+  }
   foscar::SplitArgs sa;
   sa.q = (const uint16_t*)q;  // rotated keys: each work-group rotates its query rows (q H) itself
   sa.pk = (const uint32_t*)pk;
@@ -398,6 +438,7 @@ int quantize_common(int bits, const foscar_dims* d, const void* k_src, const voi
                     void* kz, void* vs, void* vz, void* stream) {
   int rc = check_dims(d, false);
   if (rc) return rc;
+  if (d->head_dim != foscar::kHeadDim) return FOSCAR_EUNSUPPORTED;
   if (layout < 0 || layout > 15 || src_tokens < 0) return FOSCAR_EINVAL;
   const int rot = layout >> 2;  // FOSCAR_K_ROTATED, FOSCAR_V_ROTATED: rotate those rows first
   layout &= 3;
@@ -492,6 +533,7 @@ int decode_paged(int bits, const foscar_dims* dims, const void* q, const void* k
                  int layout, int group, void* out, float* lse, void* stream) {
   int rc = check_decode_shape(dims, layout, group);
   if (rc) return rc;
+  if (dims->head_dim != foscar::kHeadDim) return FOSCAR_EUNSUPPORTED;
   if (!block_table || !aligned(block_table, 4) || num_blocks < 1 || block_size < 1) return FOSCAR_EINVAL;
   // blocks of whole tiles (and whole groups of a channel-wise side); the logical capacity
   // max_seq_len is a whole number of blocks, in at most kMaxSplits ranges of 63 blocks' tokens
@@ -539,8 +581,8 @@ int foscar_pack(int bits, int side, const foscar_dims* dims, const uint8_t* code
   if (rc) return rc;
   if ((size_t)dims->batch * dims->num_kv_heads * dims->max_seq_len == 0) return FOSCAR_OK;
   if (!codes || !packed) return FOSCAR_EINVAL;
-  hipError_t e = foscar::launch_pack(bits, side, dims->batch, dims->num_kv_heads, dims->max_seq_len, codes,
-                                     (uint32_t*)packed, (hipStream_t)stream);
+  hipError_t e = foscar::launch_pack(bits, side, dims->batch, dims->num_kv_heads, dims->max_seq_len, dims->head_dim,
+                                     codes, (uint32_t*)packed, (hipStream_t)stream);
   return e == hipSuccess ? FOSCAR_OK : hip_fail(e);
 }
 
@@ -549,7 +591,7 @@ int foscar_unpack(int bits, int side, const foscar_dims* dims, const void* packe
   if (rc) return rc;
   if ((size_t)dims->batch * dims->num_kv_heads * dims->max_seq_len == 0) return FOSCAR_OK;
   if (!codes || !packed) return FOSCAR_EINVAL;
-  hipError_t e = foscar::launch_unpack(bits, side, dims->batch, dims->num_kv_heads, dims->max_seq_len,
+  hipError_t e = foscar::launch_unpack(bits, side, dims->batch, dims->num_kv_heads, dims->max_seq_len, dims->head_dim,
                                        (const uint32_t*)packed, codes, (hipStream_t)stream);
   return e == hipSuccess ? FOSCAR_OK : hip_fail(e);
 }
@@ -578,7 +620,7 @@ int foscar_split_plan(const foscar_dims* dims, int bits, int layout, int group, 
   int dev = 0, cus = 256, per_cu = 4;
   if (hipGetDevice(&dev) == hipSuccess) {
     cus = compute_units(dev);
-    per_cu = resident_per_cu(dev, bits, layout, group);
+    per_cu = resident_per_cu(dev, bits, layout, group, false, dims->head_dim != foscar::kHeadDim);
   }
   const foscar_dims wd = work_dims(dims);
   plan(&wd, layout & 3, group, cus, per_cu, splits, chunk);
@@ -613,7 +655,8 @@ int foscar_workspace_reserve(const foscar_dims* dims, int bits, int layout, int 
   if (e != hipSuccess) return hip_fail(e);
   int32_t splits = 1, chunk = 0;
   const foscar_dims wd = work_dims(dims);
-  plan(&wd, layout & 3, group, compute_units(dev), resident_per_cu(dev, bits, layout, group), &splits, &chunk);
+  plan(&wd, layout & 3, group, compute_units(dev),
+       resident_per_cu(dev, bits, layout, group, false, dims->head_dim != foscar::kHeadDim), &splits, &chunk);
   return get_workspace(counter_bytes(&wd), partial_bytes(&wd, splits), (hipStream_t)stream, nullptr, nullptr);
 }
 

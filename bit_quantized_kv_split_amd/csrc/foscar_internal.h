@@ -92,14 +92,44 @@ hipError_t launch_split_rot(int bits, bool kch, bool vch, int group, int batch, 
                             hipStream_t stream, int* per_cu, const LaunchEvents& ev);
 hipError_t launch_split_paged_rot(int bits, bool kch, bool vch, int group, int batch, int hkv, const SplitArgs& sa,
                                   hipStream_t stream, int* per_cu, const LaunchEvents& ev);
+// Decode for head dimensions other than kHeadDim (decode_generic.hip): a multiple of 32 up to
+// kGdMaxD, plain caches (no window, paging or rotation).  One work-group per (work pair, range)
+// writes the range's partial; a second launch merges the ranges of each query row.
+constexpr int kGdMaxD = 256;
+struct GenericArgs {
+  const uint16_t* q;          // bf16 [B][Hq][D]
+  const uint32_t* pk;         // [B][Hkv][Tcap][D*bits/32]
+  const uint32_t* pv;         // [B][Hkv][Tcap*bits/32][D]
+  const uint16_t* ks;         // fp16 scales / offsets in the layouts of SplitArgs
+  const uint16_t* kz;
+  const uint16_t* vs;
+  const uint16_t* vz;
+  const int32_t* seq_lens;    // [B]
+  uint16_t* out;              // bf16 [B][Hq][D]
+  float* lse;                 // fp32 [B][Hq] or null
+  float* o_part;              // fp32 [B][Hq][S][D]
+  float* lse_part;            // fp32 [B][Hq][S]
+  // B; Hq; Hkv; work pairs per sequence (Hkv * kv_group); pairs per KV head; query heads per pair
+  int32_t batch, hq, hkv, pairs, kv_group, g_heads;
+  int32_t d;                  // D
+  int32_t tcap;               // Tcap
+  int32_t group;              // g
+  int32_t splits;             // S
+  int32_t chunk;              // tokens per range (a multiple of 64, and of g for a channel-wise side)
+  float sm_log2;              // sm_scale * log2(e)
+};
+hipError_t launch_decode_generic(int bits, bool k_channel, bool v_channel, const GenericArgs& a, hipStream_t stream,
+                                 const LaunchEvents& ev);
+hipError_t generic_occupancy(int bits, bool k_channel, bool v_channel, int* per_cu);
+
 // Quantise tokens [start_b, start_b + count_b) of new keys / values into the cache (quant.hip);
 // rot bit 0 / bit 1: rotate the key / value rows by the orthonormal Hadamard matrix first.
 hipError_t launch_quantize(int bits, bool k_channel, bool v_channel, int group, int rot, int batch, int hkv, int tcap,
                            int n_src, const void* k_src, const void* v_src, const int32_t* start, const int32_t* count,
                            void* pk, void* pv, void* ks, void* kz, void* vs, void* vz, hipStream_t stream);
-hipError_t launch_pack(int bits, int side, int batch, int hkv, int tcap, const uint8_t* codes, uint32_t* packed,
+hipError_t launch_pack(int bits, int side, int batch, int hkv, int tcap, int d, const uint8_t* codes, uint32_t* packed,
                        hipStream_t stream);
-hipError_t launch_unpack(int bits, int side, int batch, int hkv, int tcap, const uint32_t* packed, uint8_t* codes,
-                         hipStream_t stream);
+hipError_t launch_unpack(int bits, int side, int batch, int hkv, int tcap, int d, const uint32_t* packed,
+                         uint8_t* codes, hipStream_t stream);
 
 }  // namespace foscar

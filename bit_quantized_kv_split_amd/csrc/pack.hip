@@ -31,60 +31,60 @@ __global__ void unpack_keys(int bits, const uint32_t* __restrict__ packed, uint8
 }
 
 // values: word [bh][tw][c] covers codes [bh][tw*E + e][c], e < E
-__global__ void pack_values(int bits, int tcap, const uint8_t* __restrict__ codes, uint32_t* __restrict__ packed,
-                            size_t nwords) {
+__global__ void pack_values(int bits, int tcap, int d, const uint8_t* __restrict__ codes,
+                            uint32_t* __restrict__ packed, size_t nwords) {
   const size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x;
   if (i >= nwords) return;
   const int E = 32 / bits;
   const uint32_t mask = (1u << bits) - 1u;
-  const int c = (int)(i % kHeadDim);
-  const size_t rest = i / kHeadDim;
+  const int c = (int)(i % d);
+  const size_t rest = i / d;
   const size_t tw = rest % (size_t)(tcap / E);
   const size_t bh = rest / (size_t)(tcap / E);
-  const uint8_t* src = codes + (bh * tcap + tw * E) * kHeadDim + c;
+  const uint8_t* src = codes + (bh * tcap + tw * E) * d + c;
   uint32_t w = 0;
-  for (int e = 0; e < E; ++e) w |= ((uint32_t)src[(size_t)e * kHeadDim] & mask) << elem_shift(bits, e);
+  for (int e = 0; e < E; ++e) w |= ((uint32_t)src[(size_t)e * d] & mask) << elem_shift(bits, e);
   packed[i] = w;
 }
 
-__global__ void unpack_values(int bits, int tcap, const uint32_t* __restrict__ packed, uint8_t* __restrict__ codes,
-                              size_t nwords) {
+__global__ void unpack_values(int bits, int tcap, int d, const uint32_t* __restrict__ packed,
+                              uint8_t* __restrict__ codes, size_t nwords) {
   const size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x;
   if (i >= nwords) return;
   const int E = 32 / bits;
   const uint32_t mask = (1u << bits) - 1u;
-  const int c = (int)(i % kHeadDim);
-  const size_t rest = i / kHeadDim;
+  const int c = (int)(i % d);
+  const size_t rest = i / d;
   const size_t tw = rest % (size_t)(tcap / E);
   const size_t bh = rest / (size_t)(tcap / E);
-  uint8_t* dst = codes + (bh * tcap + tw * E) * kHeadDim + c;
+  uint8_t* dst = codes + (bh * tcap + tw * E) * d + c;
   const uint32_t w = packed[i];
-  for (int e = 0; e < E; ++e) dst[(size_t)e * kHeadDim] = (uint8_t)((w >> elem_shift(bits, e)) & mask);
+  for (int e = 0; e < E; ++e) dst[(size_t)e * d] = (uint8_t)((w >> elem_shift(bits, e)) & mask);
 }
 
 }  // namespace
 
-hipError_t launch_pack(int bits, int side, int batch, int hkv, int tcap, const uint8_t* codes, uint32_t* packed,
+hipError_t launch_pack(int bits, int side, int batch, int hkv, int tcap, int d, const uint8_t* codes, uint32_t* packed,
                        hipStream_t stream) {
-  const size_t nwords = (size_t)batch * hkv * tcap * kHeadDim * bits / 32;
+  const size_t nwords = (size_t)batch * hkv * tcap * d * bits / 32;
   if (nwords == 0) return hipSuccess;
   const unsigned blocks = (unsigned)((nwords + 255) / 256);
   if (side == 0)
     hipLaunchKernelGGL(pack_keys, dim3(blocks), dim3(256), 0, stream, bits, codes, packed, nwords);
   else
-    hipLaunchKernelGGL(pack_values, dim3(blocks), dim3(256), 0, stream, bits, tcap, codes, packed, nwords);
+    hipLaunchKernelGGL(pack_values, dim3(blocks), dim3(256), 0, stream, bits, tcap, d, codes, packed, nwords);
   return hipGetLastError();
 }
 
-hipError_t launch_unpack(int bits, int side, int batch, int hkv, int tcap, const uint32_t* packed, uint8_t* codes,
-                         hipStream_t stream) {
-  const size_t nwords = (size_t)batch * hkv * tcap * kHeadDim * bits / 32;
+hipError_t launch_unpack(int bits, int side, int batch, int hkv, int tcap, int d, const uint32_t* packed,
+                         uint8_t* codes, hipStream_t stream) {
+  const size_t nwords = (size_t)batch * hkv * tcap * d * bits / 32;
   if (nwords == 0) return hipSuccess;
   const unsigned blocks = (unsigned)((nwords + 255) / 256);
   if (side == 0)
     hipLaunchKernelGGL(unpack_keys, dim3(blocks), dim3(256), 0, stream, bits, packed, codes, nwords);
   else
-    hipLaunchKernelGGL(unpack_values, dim3(blocks), dim3(256), 0, stream, bits, tcap, packed, codes, nwords);
+    hipLaunchKernelGGL(unpack_values, dim3(blocks), dim3(256), 0, stream, bits, tcap, d, packed, codes, nwords);
   return hipGetLastError();
 }
 

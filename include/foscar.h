@@ -53,7 +53,10 @@ extern "C" {
 #define FOSCAR_OK 0
 #define FOSCAR_EINVAL (-1)       /* null or misaligned pointer, negative size, bad layout/side/bits value,
                                     Hq % Hkv != 0 */
-#define FOSCAR_EUNSUPPORTED (-2) /* head_dim != 128, group not in {32,64,128}, Hq/Hkv > 16,
+#define FOSCAR_EUNSUPPORTED (-2) /* head_dim not 128 where 128 is required (window, paged, rotated,
+                                    quantise) or not a multiple of 32 up to 256, a token-wise
+                                    group that does not divide head_dim,
+                                    group not in {32,64,128}, Hq/Hkv > 16,
                                     max_seq_len not a multiple of 32 (and of group for a
                                     channel-wise side), max_seq_len > 2^24,
                                     batch * num_kv_heads > 2^22 */
@@ -98,7 +101,8 @@ typedef struct foscar_dims {
   int32_t batch;        /* B >= 0 sequences (B = 0: nothing to do) */
   int32_t num_q_heads;  /* Hq >= 1 */
   int32_t num_kv_heads; /* Hkv >= 1, Hq % Hkv == 0, G = Hq / Hkv <= 16 (see foscar_decode_int2) */
-  int32_t head_dim;     /* D; must be 128 */
+  int32_t head_dim;     /* D: 128 for every entry point; foscar_decode_int2/int4, foscar_decode_noalloc,
+                           pack/unpack and the sizes also take a multiple of 32 up to 256 */
   int32_t max_seq_len;  /* Tcap: tokens allocated per sequence; multiple of 32, and of
                            `group` when a side is channel-wise */
   float sm_scale;       /* softmax scale applied to q.k; <= 0 selects 1/sqrt(head_dim) */
@@ -132,7 +136,16 @@ typedef struct foscar_dims {
  *           (may be NULL)
  * stream    hipStream_t
  *
- * Precision: token-wise keys: q K^T on the block-scaled matrix cores, the
+ * Head dims other than 128 (a multiple of 32 up to 256; plain layouts, no
+ * rotation bits; a token-wise side's g must divide D) run on a second pair of
+ * kernels with the same folds (fold-placement table of the FOSCAR explainer)
+ * on the vector ALUs: fp32 products of the bf16 query (times the key scale for
+ * channel-wise keys) and the codes, fp32 softmax weights, fp32 accumulation;
+ * one launch writes each range's partial, a second merges them.  Their
+ * results meet the same error bound; their speed is not that of the D = 128
+ * kernels.
+ *
+ * Precision (D = 128): token-wise keys: q K^T on the block-scaled matrix cores, the
  * query as two e4m3 terms (exact for bf16 values) times the key codes (exact),
  * products summed in the matrix core to about 14 significant bits of each
  * 16-token block's largest product, fp32 beyond; channel-wise keys: fp16
@@ -161,7 +174,7 @@ int foscar_decode_int4(const foscar_dims* dims, const void* q, const void* packe
  * The split workspace (range counters and partial results) is a static device
  * array of 32 MiB inside the library, one copy per GPU, held until the process
  * ends: 64 KiB of counters (batch * num_kv_heads + 2 of them) and the rest for
- * partials, batch * num_q_heads * (splits + 8) * 129 floats.  A call that needs
+ * partials, batch * num_q_heads * (splits + 8) * (head_dim + 1) floats.  A call that needs
  * more returns FOSCAR_ESCRATCH: before any HIP call when even one range per
  * (sequence, KV head) does not fit, otherwise after planning, still before
  * any launch.  No call here allocates or frees device memory; the first call
@@ -295,7 +308,7 @@ int foscar_quantize_int4(const foscar_dims* dims, const void* k_src, const void*
  * packed  u32, FOSCAR_SIDE_K: [B][Hkv][Tcap][D*bits/32]; FOSCAR_SIDE_V: [B][Hkv][Tcap*bits/32][D]
  * bits    2 or 4;  side  FOSCAR_SIDE_K or FOSCAR_SIDE_V
  * Only batch, num_kv_heads, head_dim and max_seq_len of dims are used
- * (head_dim must be 128, max_seq_len a multiple of 32/bits for FOSCAR_SIDE_V).
+ * (head_dim 128 or a multiple of 32 up to 256, max_seq_len a multiple of 32/bits for FOSCAR_SIDE_V).
  */
 int foscar_pack(int bits, int side, const foscar_dims* dims, const uint8_t* codes, void* packed, void* stream);
 int foscar_unpack(int bits, int side, const foscar_dims* dims, const void* packed, uint8_t* codes, void* stream);

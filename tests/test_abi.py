@@ -58,7 +58,11 @@ def _decode(lib, dims, layout=0, group=128, ptr=1):
 @pytest.mark.parametrize("kw,layout,group,code", [
     (dict(batch=1 << 20, num_q_heads=8, num_kv_heads=8), 0, 128, -2),
     (dict(max_seq_len=1 << 25), 0, 128, -2),
-    (dict(head_dim=64), 0, 128, -2),
+    (dict(head_dim=80), 0, 64, -2),                          # head dims: 128, or a multiple of 32 up to 256
+    (dict(head_dim=288), 0, 32, -2),
+    (dict(head_dim=64), 0, 128, -2),                         # a token-wise group of 128 channels in 64
+    (dict(head_dim=64), 1, 128, -2),
+    (dict(head_dim=64), 3 | 4, 64, -2),                      # rotated caches: head_dim 128 only
     (dict(num_q_heads=6, num_kv_heads=4), 0, 128, -1),
     (dict(num_q_heads=34, num_kv_heads=2), 0, 128, -2),     # 17 query heads per KV head
     (dict(batch=(1 << 20) + 1, num_q_heads=16, num_kv_heads=2), 0, 128, -2),  # over 2^22 work pairs (G = 8: two per KV head)
@@ -72,6 +76,21 @@ def _decode(lib, dims, layout=0, group=128, ptr=1):
 ])
 def test_invalid_arguments_return_codes_before_any_gpu_call(lib, kw, layout, group, code):
     assert _decode(lib, _dims(**kw), layout, group) == code
+
+
+@pytest.mark.parametrize("D,layout,group", [(32, 0, 32), (64, 0, 64), (96, 2, 32), (192, 1, 64), (256, 0, 128),
+                                             (64, 3, 128), (256, 3, 32)])
+def test_other_head_dims_pass_the_shape_checks(lib, D, layout, group):
+    """Head dims other than 128 (multiples of 32 up to 256) reach the plain decode: with null
+    pointers the call fails on them, after every shape check, before any HIP call."""
+    import bit_quantized_kv_split_amd as fos
+    d = _dims(head_dim=D)
+    assert _decode(lib, d, layout, group, ptr=0) == -1
+    assert _noalloc(lib, d, layout=layout, group=group, ptr=0) == -1
+    s, c = fos.foscar_split_plan(d, 2, layout, group)
+    assert s * c >= d.max_seq_len and c % 64 == 0
+    assert fos.foscar_packed_bytes(2, fos.FOSCAR_SIDE_K, d) == 1024 * D * 2 // 8
+    assert _quantize(lib, d, layout, group) == -2                    # the quantiser: head_dim 128 only
 
 
 def test_null_pointers_and_dims(lib):
@@ -93,7 +112,7 @@ def test_sizes_and_strings(lib):
     for c, s in [(0, "ok"), (-1, "invalid argument"), (-2, "unsupported"), (-3, "HIP"), (-4, "memory")]:
         assert s in fos.foscar_strerror(c)
     with pytest.raises(ValueError):
-        fos.foscar_split_plan(_dims(head_dim=96), 2, 0, 128)
+        fos.foscar_split_plan(_dims(head_dim=80), 2, 0, 64)
 
 
 def test_split_plan_covers_the_cache(lib, monkeypatch):
@@ -175,6 +194,7 @@ def test_decode_window_rejects_bad_arguments_before_any_gpu_call(lib):
     assert _decode_window(lib, _dims(), win_cap=4097) == -2          # largest window: 4096 tokens
     assert _decode_window(lib, _dims(), win_ptr=0) == -1             # window pointers missing
     assert _decode_window(lib, _dims(head_dim=64)) == -2
+    assert _decode_window(lib, _dims(head_dim=64), group=64) == -2   # other head dims: plain caches only
     assert _decode_window(lib, _dims(), layout=16) == -1
     assert _decode_window(lib, None) == -1
     assert _decode_window(lib, _dims(batch=0), ptr=0, win_ptr=0) == 0
@@ -204,7 +224,7 @@ def test_noalloc_rejects_before_any_gpu_call(lib):
     rejects, before any HIP call, what its static scratch cannot hold."""
     assert _noalloc(lib, _dims(), bits=3) == -1
     assert _noalloc(lib, None) == -1
-    assert _noalloc(lib, _dims(head_dim=64)) == -2
+    assert _noalloc(lib, _dims(head_dim=80)) == -2
     assert _noalloc(lib, _dims(batch=0), ptr=0) == 0
     assert _noalloc(lib, _dims(batch=20000, num_q_heads=1, num_kv_heads=1)) == -5   # range counters
     assert _noalloc(lib, _dims(batch=1024, num_q_heads=32, num_kv_heads=8)) == -5   # partials of one range
