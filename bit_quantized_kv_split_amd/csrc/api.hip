@@ -120,7 +120,7 @@ int resident_per_cu(int device, int bits, int layout, int group, bool paged = fa
   }
   int n = 0;
   const bool kch = (layout & FOSCAR_K_CHANNEL) != 0, vch = (layout & FOSCAR_V_CHANNEL) != 0;
-  const hipError_t e = generic ? foscar::generic_occupancy(bits, kch, vch, &n)
+  const hipError_t e = generic ? foscar::generic_occupancy(bits, kch, vch, group, &n)
                                : foscar::decode_occupancy(bits, kch, vch, group, paged, (layout >> 2) != 0, &n);
   if (e != hipSuccess || n <= 0) return 4;
   std::lock_guard<std::mutex> lk(g_ws_mutex);

@@ -19,12 +19,14 @@
 //
 // Layout of the work: the 4 waves of a work-group take the range's 64-token
 // blocks in turn.  Scores have lane = token (the lane walks its token's key
-// words; the query operand is an LDS broadcast), the online softmax reduces
-// over the wave, and the weighted values have lane = channel (64 consecutive
-// channels per pass, so each value-word load is one coalesced row segment).
-// Every step runs on the vector ALUs: at these head dimensions a 64-token
-// block is too small a contraction per wave for the matrix cores to repay the
-// operand shuffles.  Tokens at or past the sequence length are never loaded.
+// words a channel group at a time, the next group's words in flight; the
+// query operand is an LDS broadcast), the online softmax reduces over the
+// wave, and the weighted values have lane = channel (64 consecutive channels
+// per pass, so each value-word load is one coalesced row segment; a block's
+// word rows one at a time, every pass's word of a row loaded together, the
+// next row in flight).  Every step runs on the vector ALUs (fp16 dot products
+// of code pairs where the operand allows, fp32 FMAs for q * s of channel-wise
+// keys).  Tokens at or past the sequence length are never loaded.
 #include "foscar_internal.h"
 
 namespace foscar {
@@ -68,11 +70,26 @@ struct alignas(16) F4 {
   float v[kMaxG];
 };
 
-template <int BITS, bool KCH, bool VCH>
+// Code pairs as fp16 operands: the two codes of elements 2k and 2k+1 of a word
+// sit at bits bits*k and 16 + bits*k, so one shift and one AND give them as the
+// bit patterns of two fp16 subnormals, exactly code * 2^-24 each (no bias to
+// take back).  v_dot2_f32_f16 multiplies them with a pair of fp16 operands
+// (query channels, or softmax weights) and accumulates in fp32; the sum is
+// scaled by 2^24 once per group.
+typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
+constexpr float kCodeScale = 16777216.0f;  // 2^24
+__device__ __forceinline__ float dot2(uint32_t a, uint32_t codes, float c) {
+  return __builtin_amdgcn_fdot2(__builtin_bit_cast(h2_t, a), __builtin_bit_cast(h2_t, codes), c, false);
+}
+__device__ __forceinline__ uint16_t f16_bits(float x) { return __builtin_bit_cast(uint16_t, (_Float16)x); }
+
+template <int BITS, bool KCH, bool VCH, int GRP>
 __global__ __launch_bounds__(kGdThreads) void gd_split(const GenericArgs a) {
   constexpr int E = 32 / BITS;
+  constexpr int g = GRP;
   constexpr uint32_t MASK = (1u << BITS) - 1u;
-  const int D = a.d, g = a.group, G = a.g_heads, S = a.splits;
+  constexpr uint32_t PMASK = MASK | (MASK << 16);  // a code pair
+  const int D = a.d, G = a.g_heads, S = a.splits;
   const int pair = blockIdx.x, s = blockIdx.y;
   const int b = pair / a.pairs, pp = pair - b * a.pairs;
   const int kvh = pp / a.kv_group;  // KV head; query heads h0 .. h0 + G - 1
@@ -85,12 +102,15 @@ __global__ __launch_bounds__(kGdThreads) void gd_split(const GenericArgs a) {
   const int NJ = D / g;  // channel groups of a token (token-wise sides)
 
   __shared__ F4 s_q[kGdMaxD];                                   // q[h][c] as [c][h]
+  __shared__ uint4 s_q2[kGdMaxD / 2];                           // fp16 pairs (q[h][2i], q[h][2i+1]), h = x, y, z, w
   __shared__ float s_qsum[kGdMaxD / 32][kMaxG];                 // token-wise K: sum of q over channel group j
   __shared__ F4 s_qt[KCH ? kGdWaves * 2 * kGdMaxD : 1];        // channel-wise K: q~ of a block's (<= 2) token groups
   __shared__ float s_bias[kGdWaves][2][kMaxG];                  // channel-wise K: sum_c q z of those groups
-  constexpr int kWSize = VCH ? kGdWaves * 64 : kGdWaves * (kGdMaxD / 32) * 64;
-  constexpr int kOSize = kGdWaves * kGdMaxD;                     // combine: o[w][c] (heads in F4)
-  __shared__ F4 s_w[kWSize > kOSize ? kWSize : kOSize];         // weights of a block; after the loop, the combine
+  // fp16 weight pairs of a block (per token pair: 4 heads x (even token, odd token)), per channel
+  // group for a token-wise value side; after the loop, the combine o[w][c] (heads in F4)
+  constexpr int kWSize = VCH ? kGdWaves * 32 : kGdWaves * (kGdMaxD / 32) * 32;
+  constexpr int kOSize = kGdWaves * kGdMaxD;
+  __shared__ uint4 s_buf[kWSize > kOSize ? kWSize : kOSize];
   __shared__ float s_zs[kGdWaves][kGdMaxD / 32][kMaxG];         // token-wise V: sum_t p z per channel group
   __shared__ float s_m[kGdWaves][kMaxG], s_l[kGdWaves][kMaxG];
 
@@ -99,6 +119,16 @@ __global__ __launch_bounds__(kGdThreads) void gd_split(const GenericArgs a) {
 #pragma unroll
     for (int h = 0; h < kMaxG; ++h) f.v[h] = h < G ? bf16_to_float(a.q[((size_t)b * a.hq + h0 + h) * D + i]) : 0.f;
     s_q[i] = f;
+  }
+  for (int i = tid; i < D / 2; i += kGdThreads) {
+    uint32_t v[kMaxG];
+#pragma unroll
+    for (int h = 0; h < kMaxG; ++h) {
+      const size_t r = ((size_t)b * a.hq + h0 + h) * D + 2 * i;
+      v[h] = h < G ? (uint32_t)f16_bits(bf16_to_float(a.q[r])) | (uint32_t)f16_bits(bf16_to_float(a.q[r + 1])) << 16
+                   : 0u;
+    }
+    s_q2[i] = make_uint4(v[0], v[1], v[2], v[3]);
   }
   __syncthreads();
   if (!KCH && tid < NJ * kMaxG) {
@@ -122,7 +152,10 @@ __global__ __launch_bounds__(kGdThreads) void gd_split(const GenericArgs a) {
     const int t = blk + lane;
     const bool valid = t < r1;
     const int tau0 = blk / g;
-    const int ntau = (KCH || VCH) && g < 64 ? 2 : 1;  // token groups a 64-token block meets (blocks start at multiples of 64)
+    constexpr int ntau = (KCH || VCH) && GRP < 64 ? 2 : 1;  // token groups a 64-token block meets (blocks start at
+                                                          // multiples of 64)
+    constexpr int VW = 64 / E;  // value word rows of a block
+    const int tw0 = blk / E, tw1 = min(blk + 64, r1);  // rows tw0 + k hold tokens below tw1 while (tw0 + k) * E < tw1
 
     // ---- channel-wise K: q~ and the bias of the block's token groups
     if (KCH) {
@@ -163,38 +196,64 @@ __global__ __launch_bounds__(kGdThreads) void gd_split(const GenericArgs a) {
       if (KCH) {
         const int u = t / g - tau0;
         const F4* qt = s_qt + (wave * 2 + u) * kGdMaxD;
-        for (int w = 0; w < W; ++w) {
-          const uint32_t word = krow[w];
+        uint2 nxt = *reinterpret_cast<const uint2*>(krow);  // W is even: word pairs, the next one in flight
+        for (int w = 0; w < W; w += 2) {
+          const uint2 cur = nxt;
+          if (w + 2 < W) nxt = *reinterpret_cast<const uint2*>(krow + w + 2);
 #pragma unroll
-          for (int e = 0; e < E; ++e) {
-            const float cf = (float)((word >> elem_shift(BITS, e)) & MASK);
-            const F4 qv = qt[w * E + e];
+          for (int half = 0; half < 2; ++half) {
+            const uint32_t word = half ? cur.y : cur.x;
 #pragma unroll
-            for (int h = 0; h < kMaxG; ++h) sc[h] = __builtin_fmaf(qv.v[h], cf, sc[h]);
+            for (int e = 0; e < E; ++e) {
+              const float cf = (float)((word >> elem_shift(BITS, e)) & MASK);
+              const F4 qv = qt[(w + half) * E + e];
+#pragma unroll
+              for (int h = 0; h < kMaxG; ++h) sc[h] = __builtin_fmaf(qv.v[h], cf, sc[h]);
+            }
           }
         }
 #pragma unroll
         for (int h = 0; h < kMaxG; ++h) sc[h] += s_bias[wave][u][h];
       } else {
-        const int wpg = g / E;  // words of a channel group
+        constexpr int WPG = GRP / E;  // words of a channel group (even)
+        uint32_t nxt[WPG];            // the next group's words, in flight while this group is summed
+#pragma unroll
+        for (int w = 0; w < WPG; w += 2) {
+          const uint2 v = *reinterpret_cast<const uint2*>(krow + w);
+          nxt[w] = v.x;
+          nxt[w + 1] = v.y;
+        }
         for (int j = 0; j < NJ; ++j) {
-          float acc[kMaxG];
+          uint32_t cur[WPG];
 #pragma unroll
-          for (int h = 0; h < kMaxG; ++h) acc[h] = 0.f;
-          for (int w = j * wpg; w < j * wpg + wpg; ++w) {
-            const uint32_t word = krow[w];
+          for (int w = 0; w < WPG; ++w) cur[w] = nxt[w];
+          if (j + 1 < NJ) {
 #pragma unroll
-            for (int e = 0; e < E; ++e) {
-              const float cf = (float)((word >> elem_shift(BITS, e)) & MASK);
-              const F4 qv = s_q[w * E + e];
-#pragma unroll
-              for (int h = 0; h < kMaxG; ++h) acc[h] = __builtin_fmaf(qv.v[h], cf, acc[h]);
+            for (int w = 0; w < WPG; w += 2) {
+              const uint2 v = *reinterpret_cast<const uint2*>(krow + (j + 1) * WPG + w);
+              nxt[w] = v.x;
+              nxt[w + 1] = v.y;
             }
           }
           const size_t si = (bh * a.tcap + t) * (size_t)NJ + j;
           const float sk = half_to_float(a.ks[si]), zk = half_to_float(a.kz[si]);
+          float acc[kMaxG];
 #pragma unroll
-          for (int h = 0; h < kMaxG; ++h) sc[h] += sk * acc[h] + zk * s_qsum[j][h];
+          for (int h = 0; h < kMaxG; ++h) acc[h] = 0.f;
+#pragma unroll
+          for (int w = 0; w < WPG; ++w) {
+#pragma unroll
+            for (int k = 0; k < E / 2; ++k) {
+              const uint32_t cp = (cur[w] >> (BITS * k)) & PMASK;
+              const uint4 q4 = s_q2[(j * WPG + w) * (E / 2) + k];
+              acc[0] = dot2(q4.x, cp, acc[0]);
+              acc[1] = dot2(q4.y, cp, acc[1]);
+              acc[2] = dot2(q4.z, cp, acc[2]);
+              acc[3] = dot2(q4.w, cp, acc[3]);
+            }
+          }
+#pragma unroll
+          for (int h = 0; h < kMaxG; ++h) sc[h] += sk * (acc[h] * kCodeScale) + zk * s_qsum[j][h];
         }
       }
     }
@@ -219,10 +278,9 @@ __global__ __launch_bounds__(kGdThreads) void gd_split(const GenericArgs a) {
     // ---- weights of the block into LDS, lane = token
     float psum[2][kMaxG];
     if (VCH) {
-      F4 pw;
+      uint16_t* w16 = reinterpret_cast<uint16_t*>(s_buf + wave * 32) + (lane >> 1) * 8 + (lane & 1);
 #pragma unroll
-      for (int h = 0; h < kMaxG; ++h) pw.v[h] = p[h];
-      s_w[wave * 64 + lane] = pw;
+      for (int h = 0; h < kMaxG; ++h) w16[2 * h] = f16_bits(p[h]);
       const int u = ntau == 2 ? (lane >> 5) : 0;
 #pragma unroll
       for (int h = 0; h < kMaxG; ++h) {
@@ -237,65 +295,88 @@ __global__ __launch_bounds__(kGdThreads) void gd_split(const GenericArgs a) {
           sv = half_to_float(a.vs[si]);
           zv = half_to_float(a.vz[si]);
         }
-        F4 pw;
+        uint16_t* w16 =
+            reinterpret_cast<uint16_t*>(s_buf + (wave * (kGdMaxD / 32) + j) * 32) + (lane >> 1) * 8 + (lane & 1);
 #pragma unroll
         for (int h = 0; h < kMaxG; ++h) {
-          pw.v[h] = p[h] * sv;
+          w16[2 * h] = f16_bits(p[h] * sv);
           const float zs = wave_sum(p[h] * zv);
           if (lane == 0) s_zs[wave][j][h] = zs;
         }
-        s_w[(wave * (kGdMaxD / 32) + j) * 64 + lane] = pw;
       }
     }
     wave_lds_sync();
 
-    // ---- weighted values, lane = channel
-    const int tw0 = blk / E, tw1 = min(blk + 64, r1);  // word rows tw0 .. while tw * E < tw1
+    // ---- weighted values, lane = channel (channels lane + 64 i): one word row of the block at a
+    // time, the row's words of every pass loaded together and the next row in flight
+    float accv[kGdPass][kMaxG], part1[kGdPass][kMaxG];  // (channel-wise V, g = 32: tokens 0-31, 32-63)
 #pragma unroll
-    for (int i = 0; i < kGdPass; ++i) {
-      const int c = lane + 64 * i;
-      if (c >= D) break;
+    for (int i = 0; i < kGdPass; ++i)
 #pragma unroll
-      for (int h = 0; h < kMaxG; ++h) o[i][h] *= alpha[h];
-      float part[2][kMaxG];
+      for (int h = 0; h < kMaxG; ++h) {
+        o[i][h] *= alpha[h];
+        accv[i][h] = part1[i][h] = 0.f;
+      }
+    const uint32_t* vbase = a.pv + (bh * (size_t)(a.tcap / E) + tw0) * D + lane;
+    uint32_t nv[kGdPass];
 #pragma unroll
-      for (int h = 0; h < kMaxG; ++h) part[0][h] = part[1][h] = 0.f;
-      const int j = c / g;
-      for (int tw = tw0; tw * E < tw1; ++tw) {
-        const uint32_t word = a.pv[(bh * (size_t)(a.tcap / E) + tw) * D + c];
+    for (int i = 0; i < kGdPass; ++i) nv[i] = lane + 64 * i < D ? vbase[64 * i] : 0u;  // row tw0 holds token blk < tw1
+    for (int k = 0; k < VW; ++k) {
+      if ((tw0 + k) * E >= tw1) break;  // rows past the length
+      uint32_t cv[kGdPass];
 #pragma unroll
-        for (int e = 0; e < E; ++e) {
-          const int local = tw * E + e - blk;  // 0 .. 63; weights past the length are zero
-          const float cf = (float)((word >> elem_shift(BITS, e)) & MASK);
-          if (VCH) {
-            const F4 pw = s_w[wave * 64 + local];
-            const int u = local >> 5;
-            if (ntau == 2 && u == 1) {
+      for (int i = 0; i < kGdPass; ++i) cv[i] = nv[i];
+      if ((tw0 + k + 1) * E < tw1 && k + 1 < VW) {
 #pragma unroll
-              for (int h = 0; h < kMaxG; ++h) part[1][h] = __builtin_fmaf(pw.v[h], cf, part[1][h]);
-            } else {
+        for (int i = 0; i < kGdPass; ++i) nv[i] = lane + 64 * i < D ? vbase[(size_t)(k + 1) * D + 64 * i] : 0u;
+      }
+      const int lp = k * (E / 2);  // token pair of the row's first two tokens (0 .. 31)
 #pragma unroll
-              for (int h = 0; h < kMaxG; ++h) part[0][h] = __builtin_fmaf(pw.v[h], cf, part[0][h]);
-            }
+      for (int i = 0; i < kGdPass; ++i) {
+        const int c = lane + 64 * i;
+        if (c < D) {
+          const uint4* wp = VCH ? s_buf + wave * 32 + lp : s_buf + (wave * (kGdMaxD / 32) + c / g) * 32 + lp;
+          float a4[kMaxG];
+#pragma unroll
+          for (int h = 0; h < kMaxG; ++h) a4[h] = 0.f;
+#pragma unroll
+          for (int kk = 0; kk < E / 2; ++kk) {
+            const uint32_t cp = (cv[i] >> (BITS * kk)) & PMASK;
+            const uint4 w4 = wp[kk];  // weights past the length are zero
+            a4[0] = dot2(w4.x, cp, a4[0]);
+            a4[1] = dot2(w4.y, cp, a4[1]);
+            a4[2] = dot2(w4.z, cp, a4[2]);
+            a4[3] = dot2(w4.w, cp, a4[3]);
+          }
+          if (VCH && ntau == 2 && lp >= 16) {
+#pragma unroll
+            for (int h = 0; h < kMaxG; ++h) part1[i][h] += a4[h];
           } else {
-            const F4 pw = s_w[(wave * (kGdMaxD / 32) + j) * 64 + local];
 #pragma unroll
-            for (int h = 0; h < kMaxG; ++h) o[i][h] = __builtin_fmaf(pw.v[h], cf, o[i][h]);
+            for (int h = 0; h < kMaxG; ++h) accv[i][h] += a4[h];
           }
         }
       }
+    }
+#pragma unroll
+    for (int i = 0; i < kGdPass; ++i) {
+      const int c = lane + 64 * i;
+      if (c >= D) continue;
       if (VCH) {
+#pragma unroll
         for (int u = 0; u < ntau; ++u) {
           const int tau = tau0 + u;
           if (tau * g >= r1) break;
           const size_t si = (bh * (size_t)(a.tcap / g) + tau) * D + c;
           const float sv = half_to_float(a.vs[si]), zv = half_to_float(a.vz[si]);
 #pragma unroll
-          for (int h = 0; h < kMaxG; ++h) o[i][h] += sv * part[u][h] + zv * psum[u][h];
+          for (int h = 0; h < kMaxG; ++h)
+            o[i][h] += sv * ((u ? part1[i][h] : accv[i][h]) * kCodeScale) + zv * psum[u][h];
         }
       } else {
+        const int j = c / g;
 #pragma unroll
-        for (int h = 0; h < kMaxG; ++h) o[i][h] += s_zs[wave][j][h];
+        for (int h = 0; h < kMaxG; ++h) o[i][h] += accv[i][h] * kCodeScale + s_zs[wave][j][h];
       }
     }
     wave_lds_sync();  // the next block's weights overwrite this block's
@@ -303,7 +384,7 @@ __global__ __launch_bounds__(kGdThreads) void gd_split(const GenericArgs a) {
 
   // ---- combine the waves, write the range's partial
   __syncthreads();
-  F4* s_o = s_w;  // [wave][c], heads in F4
+  F4* s_o = reinterpret_cast<F4*>(s_buf);  // [wave][c], heads in F4
 #pragma unroll
   for (int i = 0; i < kGdPass; ++i) {
     const int c = lane + 64 * i;
@@ -370,23 +451,25 @@ __global__ __launch_bounds__(kGdThreads) void gd_merge(const GenericArgs a) {
 }
 
 template <int BITS, bool KCH, bool VCH>
-const void* split_kernel() {
-  return (const void*)gd_split<BITS, KCH, VCH>;
+const void* split_kernel(int group) {
+  if (group == 32) return (const void*)gd_split<BITS, KCH, VCH, 32>;
+  if (group == 64) return (const void*)gd_split<BITS, KCH, VCH, 64>;
+  return (const void*)gd_split<BITS, KCH, VCH, 128>;
 }
 
-const void* pick(int bits, bool kch, bool vch) {
+const void* pick(int bits, bool kch, bool vch, int group) {
   if (bits == 2) {
-    if (kch) return vch ? split_kernel<2, true, true>() : split_kernel<2, true, false>();
-    return vch ? split_kernel<2, false, true>() : split_kernel<2, false, false>();
+    if (kch) return vch ? split_kernel<2, true, true>(group) : split_kernel<2, true, false>(group);
+    return vch ? split_kernel<2, false, true>(group) : split_kernel<2, false, false>(group);
   }
-  if (kch) return vch ? split_kernel<4, true, true>() : split_kernel<4, true, false>();
-  return vch ? split_kernel<4, false, true>() : split_kernel<4, false, false>();
+  if (kch) return vch ? split_kernel<4, true, true>(group) : split_kernel<4, true, false>(group);
+  return vch ? split_kernel<4, false, true>(group) : split_kernel<4, false, false>(group);
 }
 
 }  // namespace
 
-hipError_t generic_occupancy(int bits, bool kch, bool vch, int* per_cu) {
-  return hipOccupancyMaxActiveBlocksPerMultiprocessor(per_cu, pick(bits, kch, vch), kGdThreads, 0);
+hipError_t generic_occupancy(int bits, bool kch, bool vch, int group, int* per_cu) {
+  return hipOccupancyMaxActiveBlocksPerMultiprocessor(per_cu, pick(bits, kch, vch, group), kGdThreads, 0);
 }
 
 hipError_t launch_decode_generic(int bits, bool kch, bool vch, const GenericArgs& a, hipStream_t stream,
@@ -395,7 +478,7 @@ hipError_t launch_decode_generic(int bits, bool kch, bool vch, const GenericArgs
   if (ev.start) e = hipEventRecord(ev.start, stream);
   if (e != hipSuccess) return e;
   void* args[] = {(void*)&a};
-  e = hipLaunchKernel(pick(bits, kch, vch), dim3(a.batch * a.pairs, a.splits), dim3(kGdThreads), args, 0, stream);
+  e = hipLaunchKernel(pick(bits, kch, vch, a.group), dim3(a.batch * a.pairs, a.splits), dim3(kGdThreads), args, 0, stream);
   if (e != hipSuccess) return e;
   e = hipLaunchKernel((const void*)gd_merge, dim3(a.batch * a.hq), dim3(kGdThreads), args, 0, stream);
   if (e != hipSuccess) return e;

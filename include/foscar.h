@@ -139,11 +139,13 @@ typedef struct foscar_dims {
  * Head dims other than 128 (a multiple of 32 up to 256; plain layouts, no
  * rotation bits; a token-wise side's g must divide D) run on a second pair of
  * kernels with the same folds (fold-placement table of the FOSCAR explainer)
- * on the vector ALUs: fp32 products of the bf16 query (times the key scale for
- * channel-wise keys) and the codes, fp32 softmax weights, fp32 accumulation;
- * one launch writes each range's partial, a second merges them.  Their
- * results meet the same error bound; their speed is not that of the D = 128
- * kernels.
+ * on the vector ALUs: token-wise keys as fp16 dot products of the query
+ * (exact for bf16 values in the fp16 range) and the codes, channel-wise keys
+ * as fp32 products of q * s and the codes, value sums as fp16 dot products of
+ * the weights (p, or p * s for a token-wise value side) and the codes, all
+ * accumulated in fp32; one launch writes each range's partial, a second merges
+ * them.  Their results meet the same error bound; their speed is not that of
+ * the D = 128 kernels.
  *
  * Precision (D = 128): token-wise keys: q K^T on the block-scaled matrix cores, the
  * query as two e4m3 terms (exact for bf16 values) times the key codes (exact),
