@@ -428,26 +428,42 @@ __global__ __launch_bounds__(kGdThreads) void gd_split(const GenericArgs a) {
 
 // One work-group per query row: out = sum_s w_s O_s / sum_s w_s with
 // w_s = e^(lse_s - max lse), lse = max + ln sum_s w_s; a row with no token
-// gives out = 0 and lse = -inf.
+// gives out = 0 and lse = -inf.  The weights are computed once per row into
+// LDS; each thread then sums its channels over the ranges.
 __global__ __launch_bounds__(kGdThreads) void gd_merge(const GenericArgs a) {
+  __shared__ float s_wt[kMaxSplits];
+  __shared__ float s_red[2][kGdWaves];
   const size_t row = blockIdx.x;
-  const int S = a.splits, D = a.d;
+  const int S = a.splits, D = a.d, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const float* lp = a.lse_part + row * S;
-  float M = -INFINITY;
-  for (int s = 0; s < S; ++s) M = fmaxf(M, lp[s]);
+  float mx = -INFINITY;
+  for (int s = tid; s < S; s += kGdThreads) mx = fmaxf(mx, lp[s]);
+  mx = wave_max(mx);
+  if (lane == 0) s_red[0][wave] = mx;
+  __syncthreads();
+  float M = s_red[0][0];
+#pragma unroll
+  for (int w = 1; w < kGdWaves; ++w) M = fmaxf(M, s_red[0][w]);
   float den = 0.f;
-  if (M != -INFINITY)
-    for (int s = 0; s < S; ++s) den += expf(lp[s] - M);
-  for (int c = threadIdx.x; c < D; c += kGdThreads) {
+  for (int s = tid; s < S; s += kGdThreads) {
+    const float w = M != -INFINITY ? expf(lp[s] - M) : 0.f;
+    s_wt[s] = w;
+    den += w;
+  }
+  den = wave_sum(den);
+  if (lane == 0) s_red[1][wave] = den;
+  __syncthreads();
+  den = 0.f;
+#pragma unroll
+  for (int w = 0; w < kGdWaves; ++w) den += s_red[1][w];
+  const float* op = a.o_part + row * S * (size_t)D;
+  for (int c = tid; c < D; c += kGdThreads) {
     float num = 0.f;
-    if (M != -INFINITY)
-      for (int s = 0; s < S; ++s) {
-        const float w = expf(lp[s] - M);
-        if (w != 0.f) num += w * a.o_part[(row * S + s) * D + c];
-      }
+#pragma unroll 8
+    for (int s = 0; s < S; ++s) num += s_wt[s] * op[(size_t)s * D + c];  // empty ranges: weight 0, partial 0
     a.out[row * D + c] = float_to_bf16(M != -INFINITY ? num / den : 0.f);
   }
-  if (threadIdx.x == 0 && a.lse) a.lse[row] = M != -INFINITY ? M + logf(den) : -INFINITY;
+  if (tid == 0 && a.lse) a.lse[row] = M != -INFINITY ? M + logf(den) : -INFINITY;
 }
 
 template <int BITS, bool KCH, bool VCH>
