@@ -63,3 +63,9 @@ def test_pools_for_the_paged_timing_hold_every_block_once():
     assert np.array_equal(got["v_codes"], oracle.unpack_v(c["packed_v"].numpy().view(np.uint32), spec.bits))
     for n in ("k_scale", "k_zero", "v_scale", "v_zero"):
         assert np.array_equal(got[n], c[n].numpy()), n
+
+
+def test_a_token_wise_group_that_does_not_divide_the_head_dim_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--head-dim", "64", "--group", "128",
+                        "--no-cpu-baseline"], capture_output=True, text=True, timeout=300)
+    assert r.returncode == 2 and "does not divide head_dim 64" in r.stderr

@@ -2,7 +2,7 @@
 up to 256: the head-dim-generic kernels) against the fp64 oracle, through the C
 interface: the four fold cases at both bit widths, ragged and edge lengths with
 NaN-poisoned padding, GQA ratios, forced range counts, the no-allocation entry
-point and a larger shape."""
+point, a larger shape and HIP-graph replay."""
 import numpy as np
 import pytest
 
@@ -94,3 +94,45 @@ def test_head_dim_256_larger_shape(bits):
     out, lse = run(spec, dev)
     ro, rl = oracle_all(spec, q, lens)
     check(out, lse, ro, rl, spec.name)
+
+
+@pytest.mark.parametrize("D,kl,vl,g", [(64, TOK, CH, 64), (256, CH, TOK, 32)])
+def test_head_dim_graph_capture_replays_match_eager(D, kl, vl, g):
+    """The two launches of a step captured in a HIP graph (workspace reserved on the capture
+    stream first, so a call allocates nothing and records no memset): every replay, with eager
+    work and synchronisation between replays, equals the eager result bit for bit."""
+    import torch
+    import bit_quantized_kv_split_amd as fos
+    spec = synth.Spec(f"hd{D}_graph", 26, 2, kl, vl, g, 3, 8, 2, D, 2048, ragged=True, ragged_lo=100)
+    dev, q, lens = stage_spec(spec)
+    layout = fos.layout_bits(spec.k_layout, spec.v_layout)
+    args = (dev["q"], dev["packed_k"], dev["packed_v"], dev["k_scale"], dev["k_zero"], dev["v_scale"], dev["v_zero"],
+            dev["seq_lens"], layout, spec.group)
+    ref_out, ref_lse = fos.prepare_decode(spec.bits, *args, sm_scale=spec.sm_scale)()
+    torch.cuda.synchronize()
+    ref_out, ref_lse = ref_out.clone(), ref_lse.clone()
+    ro, rl = oracle_all(spec, q, lens)
+    check(ref_out.float().cpu().numpy().astype(np.float64), ref_lse.cpu().numpy().astype(np.float64), ro, rl,
+          spec.name)
+    dims = fos.make_dims(spec.batch, spec.num_q_heads, spec.num_kv_heads, D, spec.max_seq_len)
+    side = torch.cuda.Stream()
+    fos.foscar_workspace_reserve(dims, spec.bits, layout, spec.group, stream=side)
+    out = torch.empty_like(ref_out)
+    lse = torch.empty_like(ref_lse)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(side):
+        call = fos.prepare_decode(spec.bits, *args, out=out, lse=lse, sm_scale=spec.sm_scale, stream=side)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(graph, stream=side):
+            for _ in range(2):
+                call()
+    for k in range(3):
+        out.fill_(float("nan"))
+        lse.fill_(0.0)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref_out) and torch.equal(lse, ref_lse), f"replay {k}"
+        eager_out, eager_lse = fos.prepare_decode(spec.bits, *args, sm_scale=spec.sm_scale)()
+        torch.cuda.synchronize()
+        assert torch.equal(eager_out, ref_out) and torch.equal(eager_lse, ref_lse), f"eager after replay {k}"
