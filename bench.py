@@ -47,7 +47,9 @@ def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=200,
+                    help="untimed steps first (default 200: about 13 ms of the long-context step, so that clocks "
+                         "and power have settled under HBM load before the timed pass)")
     ap.add_argument("--workload", default="c3_long_int2")
     ap.add_argument("--copies", type=int, default=0,
                     help="cache copies rotated over the steps (default: enough for at least 1 GiB)")
@@ -98,7 +100,7 @@ def int4_companion():
     """The paper-shaped INT4 step (c2_paper_int4: 16 sequences x 8192 tokens, 32 / 8 heads, INT4
     token-wise, g = 128), timed by a child run of this script; a summary of its JSON line."""
     cmd = [sys.executable, os.path.abspath(__file__), "--workload", "c2_paper_int4", "--steps", "50", "--warmup",
-           "10", "--sustain", "1000", "--no-cpu-baseline", "--no-int4"]
+           "200", "--sustain", "1000", "--no-cpu-baseline", "--no-int4"]
     try:
         r = subprocess.run(cmd, capture_output=True, text=True, timeout=600)
         d = json.loads([x for x in r.stdout.splitlines() if x.startswith("{")][-1])
