@@ -110,9 +110,10 @@ int compute_units(int device) {
 // Work-groups of the (bits, layout, group) kernel one CU of `device` holds at
 // once (cached; 4 when the runtime cannot say, e.g. without a GPU).  `layout`
 // may carry the rotation bits, which select the rotated variant.
-int resident_per_cu(int device, int bits, int layout, int group, bool paged = false, bool generic = false) {
+int resident_per_cu(int device, int bits, int layout, int group, bool paged = false, int head_dim = foscar::kHeadDim) {
+  const bool generic = head_dim != foscar::kHeadDim;  // the head-dim-generic kernels (their LDS depends on D)
   const long long key =
-      (((((long long)device * 8 + bits) * 16 + layout) * 256 + group) * 2 + (paged ? 1 : 0)) * 2 + (generic ? 1 : 0);
+      (((((long long)device * 8 + bits) * 16 + layout) * 256 + group) * 2 + (paged ? 1 : 0)) * 512 + head_dim;
   {
     std::lock_guard<std::mutex> lk(g_ws_mutex);
     auto it = g_occ.find(key);
@@ -120,7 +121,7 @@ int resident_per_cu(int device, int bits, int layout, int group, bool paged = fa
   }
   int n = 0;
   const bool kch = (layout & FOSCAR_K_CHANNEL) != 0, vch = (layout & FOSCAR_V_CHANNEL) != 0;
-  const hipError_t e = generic ? foscar::generic_occupancy(bits, kch, vch, group, &n)
+  const hipError_t e = generic ? foscar::generic_occupancy(bits, kch, vch, group, head_dim, &n)
                                : foscar::decode_occupancy(bits, kch, vch, group, paged, (layout >> 2) != 0, &n);
   if (e != hipSuccess || n <= 0) return 4;
   std::lock_guard<std::mutex> lk(g_ws_mutex);
@@ -268,7 +269,7 @@ int decode_common(int bits, const foscar_dims* d, const void* q, const void* pk,
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return hip_fail(e);
   int32_t splits = 1, chunk = foscar::kTile;
-  const int cus = compute_units(dev), per_cu = resident_per_cu(dev, bits, variant, group, paged, generic);
+  const int cus = compute_units(dev), per_cu = resident_per_cu(dev, bits, variant, group, paged, d->head_dim);
   // paged: the kernel's lanes hold one block each.  A range of at most 63 blocks' tokens touches at
   // most 64 blocks, aligned or not; when a block is the wave unit, every range starts on a block and
   // 64 blocks' tokens touch 64 (at P = 64, 4096-token ranges: one round of work-groups for a long
@@ -620,7 +621,7 @@ int foscar_split_plan(const foscar_dims* dims, int bits, int layout, int group, 
   int dev = 0, cus = 256, per_cu = 4;
   if (hipGetDevice(&dev) == hipSuccess) {
     cus = compute_units(dev);
-    per_cu = resident_per_cu(dev, bits, layout, group, false, dims->head_dim != foscar::kHeadDim);
+    per_cu = resident_per_cu(dev, bits, layout, group, false, dims->head_dim);
   }
   const foscar_dims wd = work_dims(dims);
   plan(&wd, layout & 3, group, cus, per_cu, splits, chunk);
@@ -656,7 +657,7 @@ int foscar_workspace_reserve(const foscar_dims* dims, int bits, int layout, int 
   int32_t splits = 1, chunk = 0;
   const foscar_dims wd = work_dims(dims);
   plan(&wd, layout & 3, group, compute_units(dev),
-       resident_per_cu(dev, bits, layout, group, false, dims->head_dim != foscar::kHeadDim), &splits, &chunk);
+       resident_per_cu(dev, bits, layout, group, false, dims->head_dim), &splits, &chunk);
   return get_workspace(counter_bytes(&wd), partial_bytes(&wd, splits), (hipStream_t)stream, nullptr, nullptr);
 }
 

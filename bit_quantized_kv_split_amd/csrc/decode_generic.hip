@@ -98,6 +98,8 @@ __device__ __forceinline__ float dot2(uint32_t a, uint32_t codes, float c) {
 }
 __device__ __forceinline__ uint16_t f16_bits(float x) { return __builtin_bit_cast(uint16_t, (_Float16)x); }
 
+extern __shared__ F4 s_dyn[];  // launch-sized LDS: kGdWaves * 2 * D entries for channel-wise keys, else none
+
 template <int BITS, bool KCH, bool VCH, int GRP>
 __global__ __launch_bounds__(kGdThreads) void gd_split(const GenericArgs a) {
   constexpr int E = 32 / BITS;
@@ -119,7 +121,7 @@ __global__ __launch_bounds__(kGdThreads) void gd_split(const GenericArgs a) {
   __shared__ F4 s_q[kGdMaxD];                                   // q[h][c] as [c][h]
   __shared__ uint4 s_q2[kGdMaxD / 2];                           // fp16 pairs (q[h][2i], q[h][2i+1]), h = x, y, z, w
   __shared__ float s_qsum[kGdMaxD / 32][kMaxG];                 // token-wise K: sum of q over channel group j
-  __shared__ F4 s_qt[KCH ? kGdWaves * 2 * kGdMaxD : 1];        // channel-wise K: q~ of a block's (<= 2) token groups
+  F4* const s_qt = s_dyn;  // channel-wise K: q~ of a block's (<= 2) token groups, [wave][2][D] (dynamic LDS)
   __shared__ float s_bias[kGdWaves][2][kMaxG];                  // channel-wise K: sum_c q z of those groups
   // fp16 weight pairs of a block (per token pair: 4 heads x (even token, odd token)), per channel
   // group for a token-wise value side; after the loop, the combine o[w][c] (heads in F4)
@@ -190,7 +192,7 @@ __global__ __launch_bounds__(kGdThreads) void gd_split(const GenericArgs a) {
               qt.v[h] = qc.v[h] * sk;
               bias.v[h] += qc.v[h] * zk;
             }
-            s_qt[(wave * 2 + u) * kGdMaxD + c] = qt;
+            s_qt[(wave * 2 + u) * D + c] = qt;
           }
         }
 #pragma unroll
@@ -210,7 +212,7 @@ __global__ __launch_bounds__(kGdThreads) void gd_split(const GenericArgs a) {
       const uint32_t* krow = a.pk + (bh * a.tcap + t) * (size_t)W;
       if (KCH) {
         const int u = t / g - tau0;
-        const F4* qt = s_qt + (wave * 2 + u) * kGdMaxD;
+        const F4* qt = s_qt + (wave * 2 + u) * D;
         uint2 nxt = *reinterpret_cast<const uint2*>(krow);  // W is even: word pairs, the next one in flight
         for (int w = 0; w < W; w += 2) {
           const uint2 cur = nxt;
@@ -497,10 +499,13 @@ const void* pick(int bits, bool kch, bool vch, int group) {
   return vch ? split_kernel<4, false, true>(group) : split_kernel<4, false, false>(group);
 }
 
+size_t dyn_lds(bool kch, int d) { return kch ? (size_t)kGdWaves * 2 * d * sizeof(F4) : 0; }
+
 }  // namespace
 
-hipError_t generic_occupancy(int bits, bool kch, bool vch, int group, int* per_cu) {
-  return hipOccupancyMaxActiveBlocksPerMultiprocessor(per_cu, pick(bits, kch, vch, group), kGdThreads, 0);
+hipError_t generic_occupancy(int bits, bool kch, bool vch, int group, int d, int* per_cu) {
+  return hipOccupancyMaxActiveBlocksPerMultiprocessor(per_cu, pick(bits, kch, vch, group), kGdThreads,
+                                                      dyn_lds(kch, d));
 }
 
 hipError_t launch_decode_generic(int bits, bool kch, bool vch, const GenericArgs& a, hipStream_t stream,
@@ -509,7 +514,8 @@ hipError_t launch_decode_generic(int bits, bool kch, bool vch, const GenericArgs
   if (ev.start) e = hipEventRecord(ev.start, stream);
   if (e != hipSuccess) return e;
   void* args[] = {(void*)&a};
-  e = hipLaunchKernel(pick(bits, kch, vch, a.group), dim3(a.batch * a.pairs, a.splits), dim3(kGdThreads), args, 0, stream);
+  e = hipLaunchKernel(pick(bits, kch, vch, a.group), dim3(a.batch * a.pairs, a.splits), dim3(kGdThreads), args,
+                     dyn_lds(kch, a.d), stream);
   if (e != hipSuccess) return e;
   e = hipLaunchKernel((const void*)gd_merge, dim3(a.batch * a.hq), dim3(kGdThreads), args, 0, stream);
   if (e != hipSuccess) return e;

@@ -120,7 +120,7 @@ struct GenericArgs {
 };
 hipError_t launch_decode_generic(int bits, bool k_channel, bool v_channel, const GenericArgs& a, hipStream_t stream,
                                  const LaunchEvents& ev);
-hipError_t generic_occupancy(int bits, bool k_channel, bool v_channel, int group, int* per_cu);
+hipError_t generic_occupancy(int bits, bool k_channel, bool v_channel, int group, int d, int* per_cu);
 
 // Quantise tokens [start_b, start_b + count_b) of new keys / values into the cache (quant.hip);
 // rot bit 0 / bit 1: rotate the key / value rows by the orthonormal Hadamard matrix first.
